@@ -1,0 +1,36 @@
+"""Host checks of the seeded input generator (no operator arithmetic involved)."""
+import numpy as np
+import torch
+
+from gated_deltanet_chunked_prefill_amd import inputs
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(100000) * 10.0 ** rng.uniform(-5, 5, 100000)).astype(np.float32)
+    ours = inputs.round_to_bf16(x.copy())
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_distributions_and_determinism():
+    a = inputs.generate(B=2, T=130, H=5, dk=128, dv=64, dtype="bf16", gate="softplus_head",
+                        h0_std=0.02, dout=True, seed=7)
+    b = inputs.generate(B=2, T=130, H=5, dk=128, dv=64, dtype="bf16", gate="softplus_head",
+                        h0_std=0.02, dout=True, seed=7)
+    for n in ("q", "k", "v", "g", "beta", "h0", "dout"):
+        np.testing.assert_array_equal(getattr(a, n), getattr(b, n))
+    nrm = np.linalg.norm(a.k.astype(np.float64), axis=-1)
+    assert np.all(np.abs(nrm - 1) < 1e-2)
+    assert np.all(a.g <= 0) and np.all((a.beta > 0) & (a.beta < 1))
+    # values are exactly representable in bf16
+    np.testing.assert_array_equal(inputs.round_to_bf16(a.v.copy()), a.v)
+    assert abs(float(a.h0.std()) - 0.02) < 2e-3
+
+
+def test_mixed_gate_heads():
+    x = inputs.generate(B=1, T=256, H=16, gate="mixed", seed=3)
+    strong = x.meta["strong_heads"]
+    assert strong.sum() == 11
+    assert np.all(x.g[..., strong] <= -0.05) and np.all(x.g[..., strong] >= -0.5)
+    assert np.all(x.g[..., ~strong] >= -1e-3) and np.all(x.g[..., ~strong] <= -1e-5)
