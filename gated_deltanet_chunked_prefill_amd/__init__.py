@@ -1,2 +1,181 @@
-"""MI355X-native Gated DeltaNet chunked-prefill operator (placeholder; the
-binding is added with the C-ABI library)."""
+"""MI355X-native Gated DeltaNet chunked-prefill operator.
+
+A thin Python binding over the C ABI in include/gdn.h (libgdn.so, built for
+gfx950).  These functions only marshal arguments: they check tensors, allocate
+outputs and the workspace with torch, and pass raw device pointers plus the
+current HIP stream to the library.  Every step of the computation runs in the
+library's HIP kernels; there is no fallback path.
+
+    gdn_chunk_fwd(q, k, v, g, beta, h0=None, scale=1.0, ...) -> (o, ht)
+    gdn_chunk_bwd(q, k, v, g, beta, dout, h0=None, dht=None, scale=1.0) -> dict
+    gdn_gate_scan(g, window_chunks=8, log_eps=log(2^-24)) -> (flags, max_window_logdecay)
+
+Layouts: q, k [B,T,H,128]; v [B,T,H,128]; g = log(alpha) and beta [B,T,H]
+float32; h0 / ht [B,H,128,128] float32; q, k, v in bfloat16 or float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+from . import _lib
+
+DEFAULT_LOG_EPS = math.log(2.0 ** -24)
+
+__all__ = ["gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_gate_scan", "gdn_plan_segments",
+           "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd_workspace_size", "options"]
+
+
+def options(split_mode=0, n_segments=1, use_window=True, window_chunks=8,
+            log_eps=DEFAULT_LOG_EPS) -> _lib.Options:
+    """Build a gdn_options struct (split_mode 0 auto, 1 off, 2 forced n_segments)."""
+    return _lib.Options(int(split_mode), int(n_segments), int(bool(use_window)),
+                        int(window_chunks), float(log_eps))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return _lib.GDN_BF16
+    if t.dtype == torch.float32:
+        return _lib.GDN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _dev(t, name, dtype=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def gdn_plan_segments(B, T, H, num_cus, **opts) -> int:
+    """Segments per head the forward uses for these shapes on num_cus compute units."""
+    o = options(**opts)
+    return _lib.load().gdn_plan_segments(int(B), int(T), int(H), int(num_cus), ctypes.byref(o))
+
+
+def gdn_chunk_fwd_workspace_size(B, T, H, dk=128, dv=128, bf16=True, **opts) -> int:
+    o = options(**opts)
+    n = _lib.load().gdn_chunk_fwd_workspace_size(int(B), int(T), int(H), int(dk), int(dv),
+                                                 _lib.GDN_BF16 if bf16 else _lib.GDN_F32,
+                                                 ctypes.byref(o))
+    if n == ctypes.c_size_t(-1).value:
+        raise _lib.GDNError(_lib.GDN_ERR_INVALID_ARG, _lib.last_error())
+    return int(n)
+
+
+def gdn_chunk_bwd_workspace_size(B, T, H, dk=128, dv=128, bf16=True) -> int:
+    n = _lib.load().gdn_chunk_bwd_workspace_size(int(B), int(T), int(H), int(dk), int(dv),
+                                                 _lib.GDN_BF16 if bf16 else _lib.GDN_F32)
+    if n == ctypes.c_size_t(-1).value:
+        raise _lib.GDNError(_lib.GDN_ERR_INVALID_ARG, _lib.last_error())
+    return int(n)
+
+
+def _workspace(nbytes, device):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, h0=None, scale=1.0, *, output_final_state=True, out=None,
+                  workspace=None, **opts):
+    """Fused chunked forward.  Returns (o, ht) (ht is None when not requested).
+    ``opts`` are the gdn_options fields (split_mode, n_segments, use_window,
+    window_chunks, log_eps).  ``out`` may supply a preallocated o and
+    ``workspace`` a preallocated uint8 workspace."""
+    torch = _torch()
+    lib = _lib.load()
+    _dev(q, "q")
+    dt = q.dtype
+    _dev(k, "k", dt), _dev(v, "v", dt)
+    _dev(g, "g", torch.float32), _dev(beta, "beta", torch.float32)
+    _dev(h0, "h0", torch.float32)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=dt, device=q.device)
+    _dev(o, "o", dt)
+    ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if output_final_state else None
+    opt = options(**opts)
+    code = _dtype_code(q)
+    if workspace is None:
+        n = lib.gdn_chunk_fwd_workspace_size(B, T, H, dk, dv, code, ctypes.byref(opt))
+        if n == ctypes.c_size_t(-1).value:
+            raise _lib.GDNError(_lib.GDN_ERR_INVALID_ARG, _lib.last_error())
+        workspace = _workspace(int(n), q.device)
+    wsz = 0 if workspace is None else workspace.numel()
+    _lib.check(lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                                 _ptr(o), _ptr(ht), B, T, H, dk, dv, code, float(scale),
+                                 ctypes.byref(opt), _ptr(workspace), wsz, _stream(q.device)))
+    return o, ht
+
+
+def gdn_chunk_bwd(q, k, v, g, beta, dout, h0=None, dht=None, scale=1.0, *, workspace=None,
+                  need_dh0=True):
+    """Fused chunked backward.  Returns a dict with dq, dk, dv (I/O dtype), dg, dbeta
+    (float32) and dh0 (float32, or None when need_dh0 is False)."""
+    torch = _torch()
+    lib = _lib.load()
+    _dev(q, "q")
+    dt = q.dtype
+    _dev(k, "k", dt), _dev(v, "v", dt), _dev(dout, "dout", dt)
+    _dev(g, "g", torch.float32), _dev(beta, "beta", torch.float32)
+    _dev(h0, "h0", torch.float32), _dev(dht, "dht", torch.float32)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dq = torch.empty_like(q)
+    dkk = torch.empty_like(k)
+    dvv = torch.empty_like(v)
+    dg = torch.empty_like(g)
+    db = torch.empty_like(beta)
+    dh0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if need_dh0 else None
+    code = _dtype_code(q)
+    if workspace is None:
+        n = lib.gdn_chunk_bwd_workspace_size(B, T, H, dk, dv, code)
+        if n == ctypes.c_size_t(-1).value:
+            raise _lib.GDNError(_lib.GDN_ERR_INVALID_ARG, _lib.last_error())
+        workspace = _workspace(int(n), q.device)
+    wsz = 0 if workspace is None else workspace.numel()
+    _lib.check(lib.gdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                                 _ptr(dout), _ptr(dht), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dg),
+                                 _ptr(db), _ptr(dh0), B, T, H, dk, dv, code, float(scale),
+                                 _ptr(workspace), wsz, _stream(q.device)))
+    return {"dq": dq, "dk": dkk, "dv": dvv, "dg": dg, "dbeta": db, "dh0": dh0}
+
+
+def gdn_gate_scan(g, window_chunks=8, log_eps=DEFAULT_LOG_EPS):
+    """Gate scan over g [B,T,H] float32.  Returns (flags [B,H] int32, max window
+    log-decay [B,H] float32)."""
+    torch = _torch()
+    lib = _lib.load()
+    _dev(g, "g", torch.float32)
+    B, T, H = g.shape
+    flags = torch.empty((B, H), dtype=torch.int32, device=g.device)
+    mx = torch.empty((B, H), dtype=torch.float32, device=g.device)
+    n = lib.gdn_gate_scan_workspace_size(B, T, H)
+    ws = _workspace(int(n), g.device)
+    _lib.check(lib.gdn_gate_scan(_ptr(g), B, T, H, int(window_chunks), float(log_eps), _ptr(flags),
+                                 _ptr(mx), _ptr(ws), int(n), _stream(g.device)))
+    return flags, mx

@@ -1,0 +1,85 @@
+"""ctypes loader for libgdn.so (the C ABI declared in include/gdn.h).
+
+The library is built in-tree by ``gated_deltanet_chunked_prefill_amd.build``.
+There is no fallback: if it is missing or cannot be loaded, every entry point
+raises immediately.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+
+GDN_OK = 0
+GDN_ERR_INVALID_ARG = 1
+GDN_ERR_UNSUPPORTED = 2
+GDN_ERR_WORKSPACE = 3
+GDN_ERR_HIP = 4
+GDN_F32 = 0
+GDN_BF16 = 1
+
+#: every function include/gdn.h declares
+EXPORTS = ("gdn_default_options", "gdn_plan_segments", "gdn_chunk_fwd_workspace_size",
+           "gdn_chunk_fwd", "gdn_chunk_bwd_workspace_size", "gdn_chunk_bwd",
+           "gdn_gate_scan_workspace_size", "gdn_gate_scan", "gdn_last_error")
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("split_mode", ctypes.c_int), ("n_segments", ctypes.c_int),
+                ("use_window", ctypes.c_int), ("window_chunks", ctypes.c_int),
+                ("log_eps", ctypes.c_float)]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+
+def load():
+    """Load libgdn.so once and declare the signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with gated_deltanet_chunked_prefill_amd.build.build() "
+            "(hipcc --offload-arch=gfx950); there is no CPU fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    op = ctypes.POINTER(Options)
+    lib.gdn_default_options.argtypes = [op]
+    lib.gdn_default_options.restype = None
+    lib.gdn_plan_segments.argtypes = [_i, _i, _i, _i, op]
+    lib.gdn_plan_segments.restype = _i
+    lib.gdn_chunk_fwd_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, op]
+    lib.gdn_chunk_fwd_workspace_size.restype = _sz
+    lib.gdn_chunk_fwd.argtypes = [_vp] * 8 + [_i] * 6 + [ctypes.c_float, op, _vp, _sz, _vp]
+    lib.gdn_chunk_fwd.restype = _i
+    lib.gdn_chunk_bwd_workspace_size.argtypes = [_i] * 6
+    lib.gdn_chunk_bwd_workspace_size.restype = _sz
+    lib.gdn_chunk_bwd.argtypes = [_vp] * 14 + [_i] * 6 + [ctypes.c_float, _vp, _sz, _vp]
+    lib.gdn_chunk_bwd.restype = _i
+    lib.gdn_gate_scan_workspace_size.argtypes = [_i, _i, _i]
+    lib.gdn_gate_scan_workspace_size.restype = _sz
+    lib.gdn_gate_scan.argtypes = [_vp, _i, _i, _i, _i, ctypes.c_float, _vp, _vp, _vp, _sz, _vp]
+    lib.gdn_gate_scan.restype = _i
+    lib.gdn_last_error.argtypes = []
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().gdn_last_error().decode()
+
+
+class GDNError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"gdn status {status}: {msg}")
+        self.status = status
+
+
+def check(status: int) -> None:
+    if status != GDN_OK:
+        raise GDNError(status, last_error())

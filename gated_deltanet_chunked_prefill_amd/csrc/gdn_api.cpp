@@ -1,0 +1,258 @@
+// C ABI of the gfx950 Gated DeltaNet chunked-prefill library: argument
+// validation, the launch planner, the workspace carve-up and the launches.
+// Declarations and the contract of every entry point are in include/gdn.h.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+gdn_status fail(gdn_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+gdn_status hip_fail(hipError_t e, const char* what) {
+    return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kChunk = 64;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+gdn_options resolve(const gdn_options* opt) {
+    gdn_options o;
+    gdn_default_options(&o);
+    if (opt) o = *opt;
+    return o;
+}
+
+gdn_status check_options(const gdn_options& o, int N) {
+    if (o.split_mode < 0 || o.split_mode > 2)
+        return fail(GDN_ERR_INVALID_ARG, "split_mode must be 0, 1 or 2 (got %d)", o.split_mode);
+    if (o.split_mode == 2 && (o.n_segments < 1 || o.n_segments > N))
+        return fail(GDN_ERR_INVALID_ARG, "n_segments must be in [1, %d] (got %d)", N, o.n_segments);
+    if (o.window_chunks < 1) return fail(GDN_ERR_INVALID_ARG, "window_chunks must be >= 1");
+    if (!(o.log_eps < 0.f)) return fail(GDN_ERR_INVALID_ARG, "log_eps must be negative");
+    return GDN_OK;
+}
+
+gdn_status check_shapes(int B, int T, int H, int dk, int dv, gdn_dtype dt) {
+    if (B <= 0 || T <= 0 || H <= 0)
+        return fail(GDN_ERR_INVALID_ARG, "B, T, H must be positive (got %d, %d, %d)", B, T, H);
+    if (dk != 128 || dv != 128)
+        return fail(GDN_ERR_UNSUPPORTED, "only dk = dv = 128 is supported (got %d, %d)", dk, dv);
+    if (dt != GDN_F32 && dt != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+    if ((long long)B * T * H * 128 > (1LL << 40))
+        return fail(GDN_ERR_INVALID_ARG, "tensor too large");
+    return GDN_OK;
+}
+
+int num_chunks(int T) { return (T + kChunk - 1) / kChunk; }
+
+int plan(int B, int T, int H, int num_cus, const gdn_options& o) {
+    const int N = num_chunks(T);
+    if (o.split_mode == 1) return 1;
+    if (o.split_mode == 2) return o.n_segments < N ? o.n_segments : N;
+    // automatic (talk summary, paragraph 8: a square-root rule on the chunk count)
+    const long long heads = (long long)B * H;
+    if (heads * 2 >= num_cus || N < 2 * o.window_chunks) return 1;
+    long long p = (num_cus + heads - 1) / heads;
+    long long r = (long long)std::floor(std::sqrt((double)N));
+    long long c = N / (2 * o.window_chunks);
+    if (r < p) p = r;
+    if (c < p) p = c;
+    return p < 1 ? 1 : (int)p;
+}
+
+struct FwdLayout {
+    size_t chunk_sums, flags, maxwin, hs, bz, mt, gsum, total;
+};
+
+FwdLayout fwd_layout(int B, int T, int H, int P) {
+    FwdLayout L{};
+    if (P <= 1) return L;
+    const size_t N = num_chunks(T), bh = (size_t)B * H, SS = 128 * 128;
+    size_t off = 0;
+    L.chunk_sums = off; off += align_up((size_t)B * N * H * sizeof(float));
+    L.flags = off;      off += align_up(bh * sizeof(int32_t));
+    L.maxwin = off;     off += align_up(bh * sizeof(float));
+    L.hs = off;         off += align_up(bh * P * SS * sizeof(float));
+    L.bz = off;         off += align_up(bh * P * SS * sizeof(float));
+    L.mt = off;         off += align_up(bh * P * SS * sizeof(float));
+    L.gsum = off;       off += align_up(bh * P * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+gdn_status device_cus(int* cus) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void gdn_default_options(gdn_options* opt) {
+    if (!opt) return;
+    opt->split_mode = 0;
+    opt->n_segments = 1;
+    opt->use_window = 1;
+    opt->window_chunks = 8;
+    opt->log_eps = std::log(std::ldexp(1.0f, -24));
+}
+
+const char* gdn_last_error(void) { return g_err; }
+
+int gdn_plan_segments(int B, int T, int H, int num_cus, const gdn_options* opt) {
+    if (B <= 0 || T <= 0 || H <= 0 || num_cus <= 0) return 0;
+    gdn_options o = resolve(opt);
+    if (check_options(o, num_chunks(T)) != GDN_OK) return 0;
+    return plan(B, T, H, num_cus, o);
+}
+
+size_t gdn_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, gdn_dtype dtype,
+                                    const gdn_options* opt) {
+    if (check_shapes(B, T, H, dk, dv, dtype) != GDN_OK) return (size_t)-1;
+    gdn_options o = resolve(opt);
+    if (check_options(o, num_chunks(T)) != GDN_OK) return (size_t)-1;
+    int cus = 0;
+    if (device_cus(&cus) != GDN_OK) return (size_t)-1;
+    return fwd_layout(B, T, H, plan(B, T, H, cus, o)).total;
+}
+
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* h0, void* o, float* ht, int B, int T,
+                         int H, int dk, int dv, gdn_dtype dtype, float scale,
+                         const gdn_options* opt, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    g_err[0] = 0;
+    if (!q || !k || !v || !g || !beta || !o)
+        return fail(GDN_ERR_INVALID_ARG, "q, k, v, g, beta and o are required");
+    gdn_status st = check_shapes(B, T, H, dk, dv, dtype);
+    if (st != GDN_OK) return st;
+    const void* vec_ptrs[] = {q, k, v, o};
+    for (const void* p : vec_ptrs)
+        if (!aligned16(p)) return fail(GDN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+    const void* f32_ptrs[] = {g, beta, h0, ht};
+    for (const void* p : f32_ptrs)
+        if (p && !aligned4(p)) return fail(GDN_ERR_INVALID_ARG, "g, beta, h0 and ht must be 4-byte aligned");
+    if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite");
+    gdn_options op = resolve(opt);
+    const int N = num_chunks(T);
+    st = check_options(op, N);
+    if (st != GDN_OK) return st;
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != GDN_OK) return st;
+    const int P = plan(B, T, H, cus, op);
+    const FwdLayout L = fwd_layout(B, T, H, P);
+    if (L.total > 0) {
+        if (!workspace) return fail(GDN_ERR_WORKSPACE, "a workspace of %zu bytes is required", L.total);
+        if (workspace_bytes < L.total)
+            return fail(GDN_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
+        if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+            return fail(GDN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    }
+
+    hipStream_t s = (hipStream_t)stream;
+    gdn::FwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.o = o; p.ht = ht;
+    p.B = B; p.T = T; p.H = H; p.N = N; p.P = P; p.w = op.window_chunks; p.scale = scale;
+    p.flags = nullptr;
+    const bool bf16 = dtype == GDN_BF16;
+    hipError_t e;
+    if (P == 1) {
+        e = gdn::launch_fwd(p, gdn::PHASE_SINGLE, bf16, s);
+        if (e != hipSuccess) return hip_fail(e, "forward launch");
+        return GDN_OK;
+    }
+    char* ws = (char*)workspace;
+    p.hs = (float*)(ws + L.hs);
+    p.bz = (float*)(ws + L.bz);
+    p.mt = (float*)(ws + L.mt);
+    p.gsum = (float*)(ws + L.gsum);
+    if (op.use_window) {
+        int32_t* flags = (int32_t*)(ws + L.flags);
+        e = gdn::launch_gate_scan(g, B, T, H, op.window_chunks, op.log_eps,
+                                  (float*)(ws + L.chunk_sums), flags, (float*)(ws + L.maxwin), s);
+        if (e != hipSuccess) return hip_fail(e, "gate scan launch");
+        p.flags = flags;
+    }
+    e = gdn::launch_fwd(p, gdn::PHASE_A, bf16, s);
+    if (e != hipSuccess) return hip_fail(e, "forward pass-1 launch");
+    if (P >= 3) {
+        e = gdn::launch_combine(p, s);
+        if (e != hipSuccess) return hip_fail(e, "combine launch");
+    }
+    e = gdn::launch_fwd(p, gdn::PHASE_C, bf16, s);
+    if (e != hipSuccess) return hip_fail(e, "forward pass-3 launch");
+    return GDN_OK;
+}
+
+size_t gdn_gate_scan_workspace_size(int B, int T, int H) {
+    if (B <= 0 || T <= 0 || H <= 0) return (size_t)-1;
+    return align_up((size_t)B * num_chunks(T) * H * sizeof(float));
+}
+
+gdn_status gdn_gate_scan(const float* g, int B, int T, int H, int window_chunks, float log_eps,
+                         int32_t* flags, float* max_window_logdecay, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!g || !flags || !workspace) return fail(GDN_ERR_INVALID_ARG, "g, flags and workspace are required");
+    if (B <= 0 || T <= 0 || H <= 0)
+        return fail(GDN_ERR_INVALID_ARG, "B, T, H must be positive (got %d, %d, %d)", B, T, H);
+    if (window_chunks < 1) return fail(GDN_ERR_INVALID_ARG, "window_chunks must be >= 1");
+    if (!aligned4(g) || !aligned4(flags) || (max_window_logdecay && !aligned4(max_window_logdecay)))
+        return fail(GDN_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
+    if (((uintptr_t)workspace & 3u) != 0) return fail(GDN_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
+    const size_t need = gdn_gate_scan_workspace_size(B, T, H);
+    if (workspace_bytes < need)
+        return fail(GDN_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    hipError_t e = gdn::launch_gate_scan(g, B, T, H, window_chunks, log_eps, (float*)workspace, flags,
+                                         max_window_logdecay, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "gate scan launch");
+    return GDN_OK;
+}
+
+size_t gdn_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, gdn_dtype dtype) {
+    if (check_shapes(B, T, H, dk, dv, dtype) != GDN_OK) return (size_t)-1;
+    return align_up((size_t)B * H * num_chunks(T) * 128 * 128 * sizeof(float));
+}
+
+gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* h0, const void* dout, const float* dht,
+                         void* grad_q, void* grad_k, void* grad_v, float* grad_g,
+                         float* grad_beta, float* grad_h0, int B, int T, int H, int dk, int dv,
+                         gdn_dtype dtype, float scale, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    (void)q; (void)k; (void)v; (void)g; (void)beta; (void)h0; (void)dout; (void)dht;
+    (void)grad_q; (void)grad_k; (void)grad_v; (void)grad_g; (void)grad_beta; (void)grad_h0;
+    (void)B; (void)T; (void)H; (void)dk; (void)dv; (void)dtype; (void)scale; (void)workspace;
+    (void)workspace_bytes; (void)stream;
+    g_err[0] = 0;
+    return fail(GDN_ERR_UNSUPPORTED, "backward not built yet");
+}
+
+}  // extern "C"

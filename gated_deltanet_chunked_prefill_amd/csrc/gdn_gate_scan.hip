@@ -1,0 +1,69 @@
+// Gate scan for gfx950 (FlashQLA talk summary, onedev.kr, paragraph 5: one
+// light kernel scans the gate distribution and marks the heads whose
+// alpha-powers fall below a threshold within a window, so those heads can skip
+// the sequence-split correction and warm up over one window instead).
+//
+// Two small launches, both bound by one read of g:
+//   1. chunk sums s[b][c][h] = sum of g over the (up to) 64 tokens of chunk c;
+//      consecutive threads take consecutive heads, so each token row of g
+//      ([B,T,H], H contiguous) is read with coalesced accesses;
+//   2. per head: W_c = s_{c-w+1} + ... + s_c for c >= w-1 (each window summed
+//      directly), its maximum over c, and flag = N >= w && max <= log_eps.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kChunksPerBlock = 8;
+
+__global__ __launch_bounds__(256) void chunk_sums_kernel(const float* __restrict__ g, int T, int H,
+                                                         int N, float* __restrict__ sums) {
+    const int b = blockIdx.y;
+    const int c0 = blockIdx.x * kChunksPerBlock;
+    const int pairs = kChunksPerBlock * H;
+    for (int i = threadIdx.x; i < pairs; i += blockDim.x) {
+        const int c = c0 + i / H, h = i % H;
+        if (c >= N) continue;
+        const int t0 = c * kChunk;
+        const int t1 = t0 + kChunk < T ? t0 + kChunk : T;
+        float acc = 0.f;
+        for (int t = t0; t < t1; ++t) acc += g[((size_t)b * T + t) * H + h];
+        sums[((size_t)b * N + c) * H + h] = acc;
+    }
+}
+
+__global__ __launch_bounds__(256) void window_flags_kernel(const float* __restrict__ sums, int B,
+                                                           int H, int N, int w, float log_eps,
+                                                           int32_t* __restrict__ flags,
+                                                           float* __restrict__ maxwin) {
+    const int bh = blockIdx.x * blockDim.x + threadIdx.x;
+    if (bh >= B * H) return;
+    const int b = bh / H, h = bh % H;
+    float best = -INFINITY;
+    for (int c = w - 1; c < N; ++c) {
+        float acc = 0.f;
+        for (int j = c - w + 1; j <= c; ++j) acc += sums[((size_t)b * N + j) * H + h];
+        best = acc > best ? acc : best;
+    }
+    flags[bh] = (N >= w && best <= log_eps) ? 1 : 0;
+    if (maxwin) maxwin[bh] = best;
+}
+
+}  // namespace
+
+hipError_t launch_gate_scan(const float* g, int B, int T, int H, int w, float log_eps,
+                            float* chunk_sums, int32_t* flags, float* maxwin, hipStream_t s) {
+    const int N = (T + kChunk - 1) / kChunk;
+    dim3 grid1((N + kChunksPerBlock - 1) / kChunksPerBlock, B);
+    hipLaunchKernelGGL(chunk_sums_kernel, grid1, dim3(256), 0, s, g, T, H, N, chunk_sums);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 grid2((B * H + 255) / 256);
+    hipLaunchKernelGGL(window_flags_kernel, grid2, dim3(256), 0, s, chunk_sums, B, H, N, w,
+                       log_eps, flags, maxwin);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,155 @@
+/*
+ * gdn.h - C ABI of the MI355X (gfx950) Gated DeltaNet chunked-prefill library.
+ *
+ * The operator (per batch b and head h, tokens t = 0..T-1):
+ *     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = scale * S_t^T q_t,         alpha_t = exp(g_t),
+ * the gated delta rule of Gated DeltaNet.  The FlashQLA pages describe it as
+ * linear attention with a d x d state updated token by token (talk summary,
+ * onedev.kr, paragraph 2), a forget gate alpha in (0,1) and L2-normalised keys
+ * (paragraph 5), evaluated chunk-wise in WY form (paragraph 3).  The state S is
+ * stored as a dk x dv matrix ("h"), so o_t[j] = scale * sum_i q_t[i] h_t[i][j].
+ *
+ * Conventions for every entry point below
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays;
+ *     q, k, v, o, dout, dq, dk, dv must be 16-byte aligned, the float32 tensors
+ *     4-byte aligned:
+ *         q, k, dq, dk          [B, T, H, dk]   in the I/O dtype
+ *         v, o, dout, dv        [B, T, H, dv]   in the I/O dtype
+ *         g, beta, dg, dbeta    [B, T, H]       float32 (g = log alpha <= 0)
+ *         h0, ht, dht, dh0      [B, H, dk, dv]  float32
+ *   - Only dk = dv = 128 is supported (GDN_ERR_UNSUPPORTED otherwise).  T >= 1 is
+ *     arbitrary: the last 64-token chunk may be short.
+ *   - The op neither normalises q, k nor squashes beta.  The sliding-window
+ *     shortcut assumes ||k_t|| <= 1 and 0 <= beta_t <= 2 (then each per-token map
+ *     I - beta k k^T has spectral norm <= 1).
+ *   - Ownership: the caller owns every buffer, including the workspace.  The
+ *     library allocates no device memory and keeps no pointer after returning.
+ *   - Asynchrony: all work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     default stream) and the call returns without synchronising.  The launch
+ *     plan depends on the shapes only; per-head choices read device data.
+ *   - Errors: arguments are validated before anything is launched; a non-OK
+ *     status means nothing was enqueued, except GDN_ERR_HIP, which reports a
+ *     failed launch (hipGetLastError) after earlier launches of the same call
+ *     may have been enqueued.  gdn_last_error() returns a thread-local message
+ *     for the last non-OK status on the calling thread.  No C++ exception
+ *     crosses this boundary.
+ *   - Calls that share a workspace or outputs must be ordered by the caller
+ *     (e.g. the same stream).
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1, /* null required pointer, non-positive size, misalignment, bad option */
+    GDN_ERR_UNSUPPORTED = 2, /* dk or dv != 128, unknown dtype                                       */
+    GDN_ERR_WORKSPACE = 3,   /* workspace smaller than the matching *_workspace_size() query         */
+    GDN_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed                           */
+} gdn_status;
+
+typedef enum {
+    GDN_F32 = 0,  /* q, k, v, o (and dout, dq, dk, dv) in float32  */
+    GDN_BF16 = 1  /* the same tensors in bfloat16                   */
+} gdn_dtype;
+
+/* Forward options.  Pass NULL for the defaults (gdn_default_options). */
+typedef struct {
+    /* Intra-GPU sequence split (talk summary, paragraph 4: split the sequence
+     * so that few heads still fill the GPU; each segment recurs from a zero
+     * state and a dk x dk correction is composed associatively).
+     *   0 = automatic segment count from the shapes (paragraph 8: a square-root
+     *       rule on the chunk count; see gdn_plan_segments),
+     *   1 = off (one segment per head),
+     *   2 = use n_segments. */
+    int split_mode;
+    int n_segments;     /* used when split_mode == 2; 1 <= n_segments <= number of chunks      */
+    /* Sliding-window heads (paragraph 5): when 1 and the sequence is split, heads
+     * whose every window of window_chunks chunks decays by at least exp(log_eps)
+     * skip the correction and warm up from a zero state over the previous
+     * window_chunks chunks.  0 = always exact. */
+    int use_window;
+    int window_chunks;  /* w >= 1, default 8 (the page 1 commentary quotes a 6-8 chunk warm-up) */
+    float log_eps;      /* default log(2^-24)                                                    */
+} gdn_options;
+
+/* Fill *opt with the defaults: automatic split, window shortcut on, w = 8,
+ * log_eps = log(2^-24). */
+void gdn_default_options(gdn_options* opt);
+
+/* Number of sequence segments per head the forward will use for these shapes on
+ * a device with num_cus compute units (the host-side planner; no device access).
+ * Returns 1 when no split is made, or 0 for invalid arguments. */
+int gdn_plan_segments(int B, int T, int H, int num_cus, const gdn_options* opt);
+
+/* Workspace bytes gdn_chunk_fwd needs for these shapes on the current device
+ * (0 when the sequence is not split).  Returns (size_t)-1 for invalid arguments. */
+size_t gdn_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, gdn_dtype dtype,
+                                    const gdn_options* opt);
+
+/* Fused chunked forward (talk summary, paragraph 3: per 64-token chunk, the
+ * K K^T inverse, W and U, the state pass and the output, fused so that W, U and
+ * the state never reach HBM; paragraphs 4-6: sequence split, window heads and
+ * gate scaling pulled outside the inverse).
+ *   q, k, v, g, beta  inputs (required)
+ *   h0                initial state or NULL (zero state)
+ *   o                 output [B,T,H,dv] (required)
+ *   ht                final state or NULL (not written)
+ *   scale             multiplies every output (1.0 for the plain operator)
+ *   opt               NULL for defaults
+ *   workspace         device memory of at least gdn_chunk_fwd_workspace_size()
+ *                     bytes, 256-byte aligned (may be NULL when that size is 0)
+ * Returns GDN_OK or an error status (see the conventions above). */
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* h0, void* o, float* ht, int B, int T,
+                         int H, int dk, int dv, gdn_dtype dtype, float scale,
+                         const gdn_options* opt, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Workspace bytes for gdn_chunk_bwd ((size_t)-1 for invalid arguments). */
+size_t gdn_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, gdn_dtype dtype);
+
+/* Fused chunked backward (page 1 lede and talk summary paragraph 6: the
+ * backward of GDN chunked prefill; the gradient of the K K^T term is formed as
+ * (dA + dA^T) K in one product).  Gradients of L given dL/do = dout and
+ * dL/dht = dht (NULL = 0):
+ *   grad_q, grad_k, grad_v  [.., dk|dv] in the I/O dtype (required)
+ *   grad_g, grad_beta       [B,T,H] float32 (required); grad_g is dL/d(log alpha)
+ *   grad_h0                 [B,H,dk,dv] float32 or NULL
+ * The forward inputs (q, k, v, g, beta, h0) must be the ones of the forward. */
+gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* h0, const void* dout, const float* dht,
+                         void* grad_q, void* grad_k, void* grad_v, float* grad_g,
+                         float* grad_beta, float* grad_h0, int B, int T, int H, int dk, int dv,
+                         gdn_dtype dtype, float scale, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Workspace bytes for gdn_gate_scan ((size_t)-1 for invalid arguments). */
+size_t gdn_gate_scan_workspace_size(int B, int T, int H);
+
+/* Gate scan (talk summary, paragraph 5: one light kernel scans the gate
+ * distribution to find the heads with an effective sliding window).  With
+ * chunks of 64 tokens (the last may be short), s_c = sum of g over chunk c and
+ * W_c = s_{c-w+1} + ... + s_c for c >= w-1:
+ *   flags[b*H+h]               = 1 if N >= w and max_c W_c <= log_eps, else 0
+ *   max_window_logdecay[b*H+h] = max_c W_c (-inf when N < w); may be NULL.
+ * g is a device pointer [B,T,H] float32; flags / max are device pointers. */
+gdn_status gdn_gate_scan(const float* g, int B, int T, int H, int window_chunks, float log_eps,
+                         int32_t* flags, float* max_window_logdecay, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Thread-local text describing the last non-OK status on this thread ("" if none). */
+const char* gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

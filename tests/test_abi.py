@@ -1,0 +1,93 @@
+"""Host-side checks of the C ABI (no GPU needed): every symbol include/gdn.h
+declares is exported, the planner follows its rule, and invalid arguments are
+rejected before anything touches the device."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from gated_deltanet_chunked_prefill_amd import _lib
+import gated_deltanet_chunked_prefill_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_exports_match_header():
+    lib = _lib.load()
+    names = _declared()
+    assert sorted(_lib.EXPORTS) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_default_options():
+    o = _lib.Options()
+    _lib.load().gdn_default_options(ctypes.byref(o))
+    assert (o.split_mode, o.use_window, o.window_chunks) == (0, 1, 8)
+    assert abs(o.log_eps - math.log(2.0 ** -24)) < 1e-5
+
+
+@pytest.mark.parametrize("B,T,H,cus,expect", [
+    (1, 32768, 32, 256, 8),     # min(ceil(256/32)=8, floor(sqrt(512))=22, 512/16=32)
+    (1, 262144, 16, 256, 16),   # min(16, 64, 256)
+    (1, 4096, 16, 256, 4),      # min(16, 8, 64/16=4)
+    (4, 8192, 32, 256, 1),      # 128 heads >= 256/2: no split
+    (1, 128, 1, 256, 1),        # 2 chunks < 2w
+    (1, 1000, 1, 256, 1),       # 16 chunks: min(256, 4, 1) = 1
+    (1, 64 * 100, 2, 256, 6),   # min(128, 10, 6)
+])
+def test_planner_rule(B, T, H, cus, expect):
+    assert gdn.gdn_plan_segments(B, T, H, cus) == expect
+
+
+def test_planner_modes():
+    assert gdn.gdn_plan_segments(1, 32768, 32, 256, split_mode=1) == 1
+    assert gdn.gdn_plan_segments(1, 32768, 32, 256, split_mode=2, n_segments=5) == 5
+    assert gdn.gdn_plan_segments(1, 32768, 32, 256, split_mode=2, n_segments=0) == 0
+    assert gdn.gdn_plan_segments(1, 32768, 32, 256, split_mode=3) == 0
+    assert gdn.gdn_plan_segments(0, 32768, 32, 256) == 0
+
+
+def _fwd(lib, q=8, k=8, v=8, g=16, beta=16, o=16, B=1, T=64, H=1, dk=128, dv=128, dt=1,
+         opt=None, ws=None, wsz=0):
+    P = ctypes.c_void_p
+    return lib.gdn_chunk_fwd(P(q) if q else None, P(k) if k else None, P(v) if v else None,
+                             P(g) if g else None, P(beta) if beta else None, None,
+                             P(o) if o else None, None, B, T, H, dk, dv, dt, 1.0,
+                             ctypes.byref(opt) if opt else None, P(ws) if ws else None, wsz, None)
+
+
+def test_validation_before_launch():
+    lib = _lib.load()
+    A = 1 << 20   # a fake, aligned address: validation must fail before any use
+    assert _fwd(lib, q=0) == _lib.GDN_ERR_INVALID_ARG
+    assert "required" in _lib.last_error()
+    assert _fwd(lib, q=A, k=A, v=A, g=A, beta=A, o=A, dk=64) == _lib.GDN_ERR_UNSUPPORTED
+    assert _fwd(lib, q=A, k=A, v=A, g=A, beta=A, o=A, dt=7) == _lib.GDN_ERR_UNSUPPORTED
+    assert _fwd(lib, q=A, k=A, v=A, g=A, beta=A, o=A, T=0) == _lib.GDN_ERR_INVALID_ARG
+    assert _fwd(lib, q=A + 2, k=A, v=A, g=A, beta=A, o=A) == _lib.GDN_ERR_INVALID_ARG
+    assert "aligned" in _lib.last_error()
+    assert _fwd(lib, q=A, k=A, v=A, g=A + 2, beta=A, o=A) == _lib.GDN_ERR_INVALID_ARG
+    bad = gdn.options(split_mode=2, n_segments=5)   # T=64 has one chunk
+    assert _fwd(lib, q=A, k=A, v=A, g=A, beta=A, o=A, opt=bad) == _lib.GDN_ERR_INVALID_ARG
+    bad = gdn.options(window_chunks=0)
+    assert _fwd(lib, q=A, k=A, v=A, g=A, beta=A, o=A, opt=bad) == _lib.GDN_ERR_INVALID_ARG
+
+
+def test_gate_scan_and_bwd_validation():
+    lib = _lib.load()
+    A = ctypes.c_void_p(1 << 20)
+    st = lib.gdn_gate_scan(None, 1, 64, 1, 8, -16.0, A, None, A, 1 << 20, None)
+    assert st == _lib.GDN_ERR_INVALID_ARG
+    st = lib.gdn_gate_scan(A, 1, 64 * 10, 4, 8, -16.0, A, None, A, 4, None)
+    assert st == _lib.GDN_ERR_WORKSPACE
+    assert lib.gdn_gate_scan_workspace_size(1, 64 * 10, 4) == 256
+    assert lib.gdn_chunk_bwd_workspace_size(1, 64, 1, 64, 128, 1) == ctypes.c_size_t(-1).value

@@ -1,0 +1,190 @@
+"""GPU parity of the fused forward and the gate scan against the fp64 oracle.
+
+Every case draws seeded inputs, runs the HIP path through the C ABI and the
+oracle on the same values, and checks max|X - X_ref| <= tol * max|X_ref| for
+the output o and the final state ht (tol = 2e-2 for bf16 I/O, 1e-4 for fp32).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gated_deltanet_chunked_prefill_amd import inputs
+from helpers import TOL_BF16, TOL_F32, rel_err, say, to_gpu, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import torch
+    assert torch.cuda.is_available()
+    import gated_deltanet_chunked_prefill_amd as m
+    return m
+
+
+def _run(gdn, x, heads=None, scale=1.0, **opts):
+    t = to_gpu(x)
+    o, ht = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], scale=scale,
+                              **opts)
+    import torch
+    torch.cuda.synchronize()
+    oref, href = oracle.fwd(x.q, x.k, x.v, x.g, x.beta, x.h0, scale=scale, heads=heads)
+    return to_np(o), to_np(ht), oref, href
+
+
+def _check(o, ht, oref, href, tol, heads=None, H=None, label=""):
+    if heads is not None:
+        sel = [(bh // H, bh % H) for bh in heads]
+        eo = max(rel_err(o[b, :, h], oref[b, :, h]) for b, h in sel)
+        eh = max(rel_err(ht[b, h], href[b, h]) for b, h in sel)
+    else:
+        eo, eh = rel_err(o, oref), rel_err(ht, href)
+    say(f"  {label}: o err {eo:.3e}  ht err {eh:.3e}  (tol {tol})")
+    assert eo <= tol and eh <= tol, (eo, eh)
+
+
+def test_fp32_tiny(gdn):
+    say("case fp32_t128_h1")
+    x = inputs.workload("fp32_t128_h1")
+    _check(*_run(gdn, x), TOL_F32, label="fp32 tiny")
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 100, 200])
+def test_bf16_ragged_lengths(gdn, T):
+    say(f"case bf16 ragged T={T}")
+    x = inputs.generate(B=2, T=T, H=3, h0_std=0.02, seed=100 + T)
+    _check(*_run(gdn, x), TOL_BF16, label=f"T={T}")
+
+
+def test_fp32_ragged_with_state(gdn):
+    say("case fp32 ragged T=150 with h0, scale 0.5")
+    x = inputs.generate(B=1, T=150, H=2, dtype="f32", gate="uniform", gate_lo=-0.3,
+                        gate_hi=-0.01, h0_std=0.1, seed=7)
+    _check(*_run(gdn, x, scale=0.5), TOL_F32, label="fp32 ragged")
+
+
+@pytest.mark.parametrize("P,window", [(1, 0), (2, 0), (3, 0), (5, 1), (8, 1), (8, 0)])
+def test_forced_split(gdn, P, window):
+    """Any segment count gives the same result within tolerance; with the window
+    shortcut on, fast-decaying heads take the window path."""
+    say(f"case forced split P={P} window={window}")
+    x = inputs.generate(B=1, T=64 * 24 + 17, H=4, h0_std=0.02, seed=11)
+    _check(*_run(gdn, x, split_mode=2, n_segments=P, use_window=window), TOL_BF16,
+           label=f"P={P} w={window}")
+
+
+def test_split_mixed_heads_window(gdn):
+    say("case mixed heads split with window, w=2")
+    x = inputs.generate(B=2, T=64 * 40, H=4, gate="mixed", strong_frac=0.5, seed=12)
+    flags, _ = oracle.gate_scan(x.g, window_chunks=2)
+    assert flags.sum() >= 2 and flags.sum() < flags.size
+    _check(*_run(gdn, x, split_mode=2, n_segments=10, window_chunks=2), TOL_BF16,
+           label="mixed P=10 w=2")
+
+
+def test_strong_decay_pairwise_fallback(gdn):
+    """Chunks whose total decay exceeds the factored-exponential range use
+    pairwise exponentials; results stay finite and correct."""
+    say("case strong decay (|gamma_C| > 160)")
+    x = inputs.generate(B=1, T=300, H=2, gate="uniform", gate_lo=-4.0, gate_hi=-2.0,
+                        h0_std=0.02, seed=13)
+    o, ht, oref, href = _run(gdn, x, split_mode=1)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(ht))
+    _check(o, ht, oref, href, TOL_BF16, label="strong decay")
+
+
+def test_bf16_t4096_h16(gdn):
+    say("case bf16_t4096_h16 (auto split)")
+    x = inputs.workload("bf16_t4096_h16")
+    _check(*_run(gdn, x), TOL_BF16, label="t4096 h16")
+
+
+def test_call_splitting(gdn):
+    """Chunked prefill: running T1 then T2 from the carried state equals one call."""
+    import torch
+    say("case call splitting")
+    x = inputs.generate(B=1, T=64 * 10 + 30, H=2, h0_std=0.02, seed=14)
+    t = to_gpu(x)
+    o, ht = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"])
+    s = 64 * 4 + 7
+    sl = lambda a: a[:, :s].contiguous()
+    sr = lambda a: a[:, s:].contiguous()
+    oa, ha = gdn.gdn_chunk_fwd(sl(t["q"]), sl(t["k"]), sl(t["v"]), sl(t["g"]), sl(t["beta"]), t["h0"])
+    ob, hb = gdn.gdn_chunk_fwd(sr(t["q"]), sr(t["k"]), sr(t["v"]), sr(t["g"]), sr(t["beta"]), ha)
+    torch.cuda.synchronize()
+    oc = torch.cat([oa, ob], 1)
+    assert rel_err(to_np(oc), to_np(o)) < TOL_BF16
+    assert rel_err(to_np(hb), to_np(ht)) < TOL_BF16
+
+
+def test_causality_bitwise(gdn):
+    """Changing keys and values at and after token t leaves every earlier output
+    bit-identical (the split and window choices do not depend on k or v)."""
+    import torch
+    say("case causality")
+    x = inputs.generate(B=1, T=64 * 20, H=2, seed=15)
+    t = to_gpu(x)
+    o1, _ = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], split_mode=2, n_segments=4)
+    cut = 64 * 9 + 5
+    k2, v2 = t["k"].clone(), t["v"].clone()
+    k2[:, cut:] = -k2[:, cut:]
+    v2[:, cut:] += 1.0
+    o2, _ = gdn.gdn_chunk_fwd(t["q"], k2, v2, t["g"], t["beta"], split_mode=2, n_segments=4)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, :cut], o2[:, :cut])
+    assert not torch.equal(o1[:, cut:], o2[:, cut:])
+
+
+def test_gate_scan_flags(gdn):
+    import torch
+    say("case gate scan")
+    x = inputs.generate(B=2, T=64 * 50 + 9, H=16, gate="softplus_head", seed=16)
+    g = torch.from_numpy(x.g).cuda()
+    flags, mx = gdn.gdn_gate_scan(g, window_chunks=8)
+    torch.cuda.synchronize()
+    fref, mref = oracle.gate_scan(x.g, window_chunks=8)
+    mx = mx.cpu().numpy()
+    np.testing.assert_allclose(mx, mref, rtol=1e-4, atol=1e-3)
+    margin = np.abs(mref - np.log(2.0 ** -24)) > 1e-3
+    np.testing.assert_array_equal(flags.cpu().numpy()[margin], fref[margin])
+    assert 0 < fref.sum() < fref.size
+    # fewer chunks than the window: never flagged
+    f2, m2 = gdn.gdn_gate_scan(g[:, :64 * 7].contiguous(), window_chunks=8)
+    torch.cuda.synchronize()
+    assert int(f2.sum()) == 0 and bool(torch.all(torch.isinf(m2)))
+
+
+def test_workspace_too_small(gdn):
+    import torch
+    from gated_deltanet_chunked_prefill_amd import _lib
+    x = inputs.generate(B=1, T=64 * 40, H=2, seed=17)
+    t = to_gpu(x)
+    ws = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(_lib.GDNError) as ei:
+        gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], split_mode=2, n_segments=4,
+                          workspace=ws)
+    assert ei.value.status == _lib.GDN_ERR_WORKSPACE
+
+
+@pytest.mark.slow
+def test_bf16_t32768_h32_sampled_heads(gdn):
+    """The throughput workload at full size, in the launch configuration the
+    benchmark times; the oracle runs on a sample of heads of both kinds."""
+    say("case bf16_t32768_h32 (full size, sampled heads)")
+    x = inputs.workload("bf16_t32768_h32")
+    flags, _ = oracle.gate_scan(x.g, window_chunks=8)
+    win = [i for i in range(32) if flags[0, i]][:3]
+    ex = [i for i in range(32) if not flags[0, i]][:3]
+    heads = win + ex
+    o, ht, oref, href = _run(gdn, x, heads=heads)
+    _check(o, ht, oref, href, TOL_BF16, heads=heads, H=32, label="t32768 h32")
+
+
+@pytest.mark.slow
+def test_bf16_t262144_h16_sampled_heads(gdn):
+    say("case bf16_t262144_h16_mixed (full size, sampled heads)")
+    x = inputs.workload("bf16_t262144_h16_mixed")
+    strong = x.meta["strong_heads"]
+    heads = [int(np.flatnonzero(strong)[0]), int(np.flatnonzero(~strong)[0])]
+    o, ht, oref, href = _run(gdn, x, heads=heads)
+    _check(o, ht, oref, href, TOL_BF16, heads=heads, H=16, label="t262144 h16")
