@@ -1,0 +1,176 @@
+#!/usr/bin/env python
+"""Throughput benchmark of the fused GDN chunked-prefill forward on one MI355X.
+
+Workload: B=1, T=32768, H=32, dk=dv=128, bf16 q/k/v/o, fp32 g and beta,
+zero initial state, final state returned (seeded synthetic inputs, resident in
+HBM before the timed region).  One step = one gdn_chunk_fwd call (gate scan,
+every forward launch and the segment combine).
+
+Prints one JSON line with tokens/s, the roofline of the fused forward kernel
+(algorithmic bytes over its HIP-event-timed launch durations, against the
+8 TB/s HBM peak) and the fp64 CPU oracle timed on the host as a reference.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+METRIC = "GDN chunked-prefill fwd tokens/s (T=32K,H=32,d=128 bf16); % HBM roofline"
+WORKLOAD = "bf16_t32768_h32"
+# algorithmic bytes per token-head: q, k, v (bf16, 3 x 256 B) and g, beta (2 x 4 B)
+# read, o (bf16, 256 B) written; per head the final state (64 KiB fp32) is written
+# and the initial state (64 KiB) read when given.
+BYTES_PER_TOKEN_HEAD = 3 * 256 + 8 + 256
+STATE_BYTES = 128 * 128 * 4
+
+
+def algorithmic_bytes(B, T, H, has_h0, has_ht):
+    return B * T * H * BYTES_PER_TOKEN_HEAD + B * H * STATE_BYTES * (int(has_h0) + int(has_ht))
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+            self.arr[i] = ev
+        self.n = n
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        st = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[a], self.arr[b])
+        assert st == 0, st
+        return ms.value
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(self.arr[i])
+
+
+def cpu_baseline(x, tokens):
+    """The fp64 oracle, as it stands, on the first `tokens` tokens of every head."""
+    import oracle
+    threads = min(x.q.shape[0] * x.q.shape[2], oracle.default_threads())
+    sl = lambda a: np.ascontiguousarray(a[:, :tokens])
+    q, k, v, g, b = map(sl, (x.q, x.k, x.v, x.g, x.beta))
+    t0 = time.perf_counter()
+    oracle.fwd(q, k, v, g, b, None, nthreads=threads)
+    dt = time.perf_counter() - t0
+    B, _, H, _ = x.q.shape
+    return {"value": B * tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {tokens} of {x.q.shape[1]} tokens, all {B * H} heads, fp64, "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-tokens", type=int, default=32768,
+                    help="tokens per head of the CPU oracle sample (0 to skip)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this operator runs on one GPU (no sharding or collectives are built); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_deltanet_chunked_prefill_amd as gdn
+    from gated_deltanet_chunked_prefill_amd import _lib, inputs
+
+    x = inputs.workload(WORKLOAD)
+    B, T, H, dk, dv = x.shape
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q = torch.from_numpy(x.q).to(dev).to(torch.bfloat16)
+    k = torch.from_numpy(x.k).to(dev).to(torch.bfloat16)
+    v = torch.from_numpy(x.v).to(dev).to(torch.bfloat16)
+    g = torch.from_numpy(x.g).to(dev)
+    beta = torch.from_numpy(x.beta).to(dev)
+    o = torch.empty_like(v)
+    ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, gdn.gdn_chunk_fwd_workspace_size(B, T, H)), dtype=torch.uint8, device=dev)
+    P = gdn.gdn_plan_segments(B, T, H, torch.cuda.get_device_properties(dev).multi_processor_count)
+
+    def step():
+        gdn.gdn_chunk_fwd(q, k, v, g, beta, None, out=o, out_ht=ht, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    lib = _lib.load()
+    cap = 8 * args.steps
+    ev = HipEvents(2 * cap)
+    labels = (ctypes.c_int * cap)()
+    lib.gdn_profile_events(ctypes.cast(ev.arr, ctypes.c_void_p), ctypes.cast(labels, ctypes.c_void_p), cap)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n = lib.gdn_profile_events(None, None, 0)
+    per_kind = {}
+    for i in range(n):
+        per_kind.setdefault(_lib.LAUNCH_KINDS[labels[i]], []).append(ev.elapsed_ms(2 * i, 2 * i + 1))
+    ev.close()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tokens_per_s = B * T / (ms_per_step * 1e-3)
+    nbytes = algorithmic_bytes(B, T, H, False, True)
+    # the fused forward kernel: its launches of one call together read every input
+    # and write every output (the combine and gate scan move only workspace data)
+    fwd_kinds = [kd for kd in ("fwd_single", "fwd_pass_a", "fwd_pass_c") if kd in per_kind]
+    fwd_ms = sum(float(np.mean(per_kind[kd])) for kd in fwd_kinds)
+    achieved = nbytes / (fwd_ms * 1e-3) / 1e9
+    kernel_ms = {kd: round(float(np.mean(t)), 4) for kd, t in per_kind.items()}
+
+    res = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
+                   "segments_per_head": P, "h0": False, "ht": True},
+        "roofline": {"bound": "hbm", "kernel": "gdn_fwd_kernel (" + "+".join(fwd_kinds) + ")",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": nbytes, "kernel_ms": kernel_ms,
+                     "call_frac": nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+    }
+    if args.cpu_tokens > 0:
+        res["cpu_baseline"] = cpu_baseline(x, min(args.cpu_tokens, T))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

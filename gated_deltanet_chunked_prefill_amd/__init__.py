@@ -101,11 +101,11 @@ def _workspace(nbytes, device):
 
 
 def gdn_chunk_fwd(q, k, v, g, beta, h0=None, scale=1.0, *, output_final_state=True, out=None,
-                  workspace=None, **opts):
+                  out_ht=None, workspace=None, **opts):
     """Fused chunked forward.  Returns (o, ht) (ht is None when not requested).
     ``opts`` are the gdn_options fields (split_mode, n_segments, use_window,
-    window_chunks, log_eps).  ``out`` may supply a preallocated o and
-    ``workspace`` a preallocated uint8 workspace."""
+    window_chunks, log_eps).  ``out`` / ``out_ht`` may supply preallocated
+    outputs and ``workspace`` a preallocated uint8 workspace."""
     torch = _torch()
     lib = _lib.load()
     _dev(q, "q")
@@ -117,7 +117,10 @@ def gdn_chunk_fwd(q, k, v, g, beta, h0=None, scale=1.0, *, output_final_state=Tr
     dv = v.shape[-1]
     o = out if out is not None else torch.empty((B, T, H, dv), dtype=dt, device=q.device)
     _dev(o, "o", dt)
-    ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if output_final_state else None
+    if out_ht is not None:
+        ht = _dev(out_ht, "out_ht", torch.float32)
+    else:
+        ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if output_final_state else None
     opt = options(**opts)
     code = _dtype_code(q)
     if workspace is None:

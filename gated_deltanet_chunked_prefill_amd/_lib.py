@@ -22,7 +22,11 @@ GDN_BF16 = 1
 #: every function include/gdn.h declares
 EXPORTS = ("gdn_default_options", "gdn_plan_segments", "gdn_chunk_fwd_workspace_size",
            "gdn_chunk_fwd", "gdn_chunk_bwd_workspace_size", "gdn_chunk_bwd",
-           "gdn_gate_scan_workspace_size", "gdn_gate_scan", "gdn_last_error")
+           "gdn_gate_scan_workspace_size", "gdn_gate_scan", "gdn_profile_events",
+           "gdn_last_error")
+
+LAUNCH_KINDS = {0: "gate_sums", 1: "gate_flags", 2: "fwd_single", 3: "fwd_pass_a",
+                4: "combine", 5: "fwd_pass_c", 6: "bwd_states", 7: "bwd"}
 
 
 class Options(ctypes.Structure):
@@ -64,6 +68,8 @@ def load():
     lib.gdn_gate_scan_workspace_size.restype = _sz
     lib.gdn_gate_scan.argtypes = [_vp, _i, _i, _i, _i, ctypes.c_float, _vp, _vp, _vp, _sz, _vp]
     lib.gdn_gate_scan.restype = _i
+    lib.gdn_profile_events.argtypes = [_vp, _vp, _i]
+    lib.gdn_profile_events.restype = _i
     lib.gdn_last_error.argtypes = []
     lib.gdn_last_error.restype = ctypes.c_char_p
     _lib = lib

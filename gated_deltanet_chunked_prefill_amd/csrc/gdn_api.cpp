@@ -16,6 +16,35 @@ namespace {
 
 thread_local char g_err[512];
 
+// Launch-event profiling hook (gdn_profile_events).
+struct Profile {
+    hipEvent_t* events = nullptr;
+    int* labels = nullptr;
+    int capacity = 0;
+    int used = 0;
+};
+thread_local Profile g_prof;
+
+// Run one launcher, bracketed by profiling events when the hook is set.
+template <typename F>
+hipError_t recorded(int label, hipStream_t s, F&& launch) {
+    Profile& p = g_prof;
+    const bool rec = p.events && p.used < p.capacity;
+    if (rec) {
+        hipError_t e = hipEventRecord(p.events[2 * p.used], s);
+        if (e != hipSuccess) return e;
+    }
+    hipError_t e = launch();
+    if (e != hipSuccess) return e;
+    if (rec) {
+        e = hipEventRecord(p.events[2 * p.used + 1], s);
+        if (e != hipSuccess) return e;
+        p.labels[p.used] = label;
+        ++p.used;
+    }
+    return hipSuccess;
+}
+
 gdn_status fail(gdn_status st, const char* fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
@@ -125,6 +154,19 @@ void gdn_default_options(gdn_options* opt) {
 
 const char* gdn_last_error(void) { return g_err; }
 
+int gdn_profile_events(void** events, int* labels, int capacity) {
+    const int used = g_prof.used;
+    if (!events || !labels || capacity <= 0) {
+        g_prof = Profile{};
+    } else {
+        g_prof.events = (hipEvent_t*)events;
+        g_prof.labels = labels;
+        g_prof.capacity = capacity;
+        g_prof.used = 0;
+    }
+    return used;
+}
+
 int gdn_plan_segments(int B, int T, int H, int num_cus, const gdn_options* opt) {
     if (B <= 0 || T <= 0 || H <= 0 || num_cus <= 0) return 0;
     gdn_options o = resolve(opt);
@@ -184,7 +226,7 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
     const bool bf16 = dtype == GDN_BF16;
     hipError_t e;
     if (P == 1) {
-        e = gdn::launch_fwd(p, gdn::PHASE_SINGLE, bf16, s);
+        e = recorded(GDN_LAUNCH_FWD_SINGLE, s, [&] { return gdn::launch_fwd(p, gdn::PHASE_SINGLE, bf16, s); });
         if (e != hipSuccess) return hip_fail(e, "forward launch");
         return GDN_OK;
     }
@@ -195,18 +237,23 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
     p.gsum = (float*)(ws + L.gsum);
     if (op.use_window) {
         int32_t* flags = (int32_t*)(ws + L.flags);
-        e = gdn::launch_gate_scan(g, B, T, H, op.window_chunks, op.log_eps,
-                                  (float*)(ws + L.chunk_sums), flags, (float*)(ws + L.maxwin), s);
+        float* sums = (float*)(ws + L.chunk_sums);
+        e = recorded(GDN_LAUNCH_GATE_SUMS, s, [&] { return gdn::launch_chunk_sums(g, B, T, H, sums, s); });
+        if (e != hipSuccess) return hip_fail(e, "gate scan launch");
+        e = recorded(GDN_LAUNCH_GATE_FLAGS, s, [&] {
+            return gdn::launch_window_flags(sums, B, T, H, op.window_chunks, op.log_eps, flags,
+                                            (float*)(ws + L.maxwin), s);
+        });
         if (e != hipSuccess) return hip_fail(e, "gate scan launch");
         p.flags = flags;
     }
-    e = gdn::launch_fwd(p, gdn::PHASE_A, bf16, s);
+    e = recorded(GDN_LAUNCH_FWD_PASS_A, s, [&] { return gdn::launch_fwd(p, gdn::PHASE_A, bf16, s); });
     if (e != hipSuccess) return hip_fail(e, "forward pass-1 launch");
     if (P >= 3) {
-        e = gdn::launch_combine(p, s);
+        e = recorded(GDN_LAUNCH_COMBINE, s, [&] { return gdn::launch_combine(p, s); });
         if (e != hipSuccess) return hip_fail(e, "combine launch");
     }
-    e = gdn::launch_fwd(p, gdn::PHASE_C, bf16, s);
+    e = recorded(GDN_LAUNCH_FWD_PASS_C, s, [&] { return gdn::launch_fwd(p, gdn::PHASE_C, bf16, s); });
     if (e != hipSuccess) return hip_fail(e, "forward pass-3 launch");
     return GDN_OK;
 }
@@ -230,8 +277,14 @@ gdn_status gdn_gate_scan(const float* g, int B, int T, int H, int window_chunks,
     const size_t need = gdn_gate_scan_workspace_size(B, T, H);
     if (workspace_bytes < need)
         return fail(GDN_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
-    hipError_t e = gdn::launch_gate_scan(g, B, T, H, window_chunks, log_eps, (float*)workspace, flags,
-                                         max_window_logdecay, (hipStream_t)stream);
+    hipStream_t s = (hipStream_t)stream;
+    float* sums = (float*)workspace;
+    hipError_t e = recorded(GDN_LAUNCH_GATE_SUMS, s, [&] { return gdn::launch_chunk_sums(g, B, T, H, sums, s); });
+    if (e != hipSuccess) return hip_fail(e, "gate scan launch");
+    e = recorded(GDN_LAUNCH_GATE_FLAGS, s, [&] {
+        return gdn::launch_window_flags(sums, B, T, H, window_chunks, log_eps, flags,
+                                        max_window_logdecay, s);
+    });
     if (e != hipSuccess) return hip_fail(e, "gate scan launch");
     return GDN_OK;
 }

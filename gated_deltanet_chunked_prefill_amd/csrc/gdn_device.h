@@ -16,11 +16,9 @@
 // of products in the kernels is arranged that way, so results never leave
 // registers between dependent products.
 //
-// LDS operand layout ("A layout"): a matrix with rows m and Kc contraction
-// columns is stored row-major in fragments of 8 elements; fragment f = 2*ks + g
-// of row m holds the elements kappa(ks, g, 0..7), and sits at slot
-// f ^ swz(m) of the row so that 8 consecutive rows read by one instruction hit
-// distinct bank groups.  One A (or B) fragment is then a single 16-byte read.
+// LDS tiles are natural row-major (see toff); A fragments are two 4-element
+// reads, and fragments of a transposed tile come from the gfx950 transposing
+// LDS read (tfrag), so no transposed copy of any tile is ever stored.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -79,26 +77,73 @@ __device__ __forceinline__ typename FragOf<T>::type acc_frag_scaled(const f32x16
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// Element offset of (row, col) in an A-layout matrix with Kc contraction columns.
-__device__ __forceinline__ int lds_elem(int row, int col, int Kc) {
-    int f = ((col >> 4) << 1) | ((col >> 2) & 1);
-    int j = (((col >> 3) & 1) << 2) | (col & 3);
-    return row * Kc + ((f ^ swz(row)) << 3) + j;
-}
-// Element offset of fragment (row, ks, g).
-__device__ __forceinline__ int lds_frag(int row, int ks, int g, int Kc) {
-    return row * Kc + (((2 * ks + g) ^ swz(row)) << 3);
+// Natural row-major tiles in LDS: a row of `Cols` elements is stored as 16-byte
+// chunks, chunk c of row r at slot c ^ swz(r) (8 consecutive rows read at the
+// same column land in distinct bank groups).  Element offset of (row, col):
+template <typename T, int Cols>
+__device__ __forceinline__ int toff(int row, int col) {
+    constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
+    return row * Cols + ((((col / EPC) ^ swz(row))) * EPC) + (col % EPC);
 }
 
-template <typename T>
-__device__ __forceinline__ typename FragOf<T>::type ld_frag(const T* base, int row, int ks, int g,
-                                                            int Kc) {
-    return *reinterpret_cast<const typename FragOf<T>::type*>(base + lds_frag(row, ks, g, Kc));
+template <typename T> struct Quad;
+template <> struct Quad<__bf16> { typedef __bf16 type __attribute__((ext_vector_type(4))); };
+template <> struct Quad<float> { typedef float type __attribute__((ext_vector_type(4))); };
+
+// A fragment of a row-major tile: lane (m, g) gets A[m][kappa(ks, g, 0..7)], i.e.
+// columns 16ks+4g..+3 and 16ks+8+4g..+3 of row m (two 4-element reads).
+template <typename T, int Cols>
+__device__ __forceinline__ typename FragOf<T>::type afrag(const T* tile, int row, int ks, int g) {
+    typedef typename Quad<T>::type Q4;
+    Q4 lo = *reinterpret_cast<const Q4*>(tile + toff<T, Cols>(row, 16 * ks + 4 * g));
+    Q4 hi = *reinterpret_cast<const Q4*>(tile + toff<T, Cols>(row, 16 * ks + 8 + 4 * g));
+    typename FragOf<T>::type f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { f[j] = lo[j]; f[4 + j] = hi[j]; }
+    return f;
 }
-template <typename T>
-__device__ __forceinline__ void st_frag(T* base, int row, int ks, int g, int Kc,
-                                        const typename FragOf<T>::type& f) {
-    *reinterpret_cast<typename FragOf<T>::type*>(base + lds_frag(row, ks, g, Kc)) = f;
+template <typename T, int Cols>
+__device__ __forceinline__ void st_afrag(T* tile, int row, int ks, int g,
+                                         const typename FragOf<T>::type& f) {
+    typedef typename Quad<T>::type Q4;
+    Q4 lo, hi;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { lo[j] = f[j]; hi[j] = f[4 + j]; }
+    *reinterpret_cast<Q4*>(tile + toff<T, Cols>(row, 16 * ks + 4 * g)) = lo;
+    *reinterpret_cast<Q4*>(tile + toff<T, Cols>(row, 16 * ks + 8 + 4 * g)) = hi;
+}
+
+// Transposed fragment of a row-major tile M[k][n]: lane (m, g), m = lane & 31,
+// gets M[kappa(ks, g, 0..7)][nbase + m].  For bf16 this is two ds_read_b64_tr_b16:
+// within each 16-lane group, lane L points at row k0 + L/4, columns
+// n0 + 4(L%4)..+3, and lane i then holds M[k0 + j][n0 + i] for j = 0..3
+// (verified on gfx950).  The float32 build reads the eight elements one by one.
+template <typename T, int Cols>
+__device__ __forceinline__ typename FragOf<T>::type tfrag(const T* tile, int nbase, int ks, int lane) {
+    const int g = lane >> 5;
+    typename FragOf<T>::type f;
+    if constexpr (sizeof(T) == 2) {
+        typedef short s4 __attribute__((ext_vector_type(4)));
+        const int i = lane & 15;
+        const int n0 = nbase + (lane & 16);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k0 = 16 * ks + 8 * h + 4 * g;
+            const T* p = tile + toff<T, Cols>(k0 + (i >> 2), n0 + 4 * (i & 3));
+            s4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s4*)(__attribute__((address_space(3))) void*)p);
+            // reinterpret the whole vector (per-element casts of the result were
+            // miscompiled into a splat of element 0 by this toolchain)
+            typename Quad<T>::type q = __builtin_bit_cast(typename Quad<T>::type, r);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) f[4 * h + j] = q[j];
+        }
+    } else {
+        const int n = nbase + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = tile[toff<T, Cols>(16 * ks + 8 * (j >> 2) + 4 * g + (j & 3), n)];
+    }
+    return f;
 }
 
 // Inclusive prefix sum across the 64 lanes of a wave.

@@ -3,16 +3,17 @@
 // One workgroup of four wave64s runs one (batch, head, segment) task over a
 // run of 64-token chunks.  Wave w owns dv columns [32w, 32w+32) of the 128x128
 // float32 state, which lives in MFMA accumulators for the whole task: the state,
-// W/U-type intermediates and the per-chunk inverse never reach HBM (FlashQLA
+// the W/U-type intermediates and the per-chunk inverse never reach HBM (FlashQLA
 // talk summary, onedev.kr, paragraph 3 names the per-chunk steps and criticises
 // writing W, U and S to HBM and reading them back).
 //
 // Per chunk (gamma = in-chunk cumulative sum of g, Gamma = exp(gamma)):
 //   prep (chunk-independent, paragraph 3 steps 1-2 and paragraph 6):
 //     A0 = diag(beta) strict_lower(K K^T) and T0 = (I + A0)^-1 are gate-free;
-//     the gated inverse is T = diag(Gamma) T0 diag(1/Gamma), formed from the
-//     2C+1 exponentials exp(gamma_r - gamma_C/2), exp(gamma_C/2 - gamma_r) and
-//     exp(gamma_C/2) (the diagonal scaling pulled outside the inverse);
+//     the gated inverse is T = diag(Gamma) T0 diag(1/Gamma), whose entries
+//     T0_rs Gamma_r/Gamma_s come from the 2C+1 exponentials
+//     exp(gamma_r - gamma_C/2), exp(gamma_C/2 - gamma_r) and exp(gamma_C/2)
+//     (the diagonal scaling pulled outside the inverse);
 //     Tt = T diag(beta) and P = (Q K^T) o Mask, Mask_rs = Gamma_r/Gamma_s for s <= r.
 //     T0 is built per 32x32 diagonal block as the product series
 //     (I+M)(I+M^2)(I+M^4)(I+M^8)(I+M^16), M = -A0_block (exact: M^32 = 0), then
@@ -25,6 +26,11 @@
 // state without Q or O and also carries the gate-free segment transition
 //     Mt <- (I - K^T T0 diag(beta) K) Mt,
 // i.e. the same step on 128 extra columns with V = 0 and Gamma = 1.
+//
+// Memory path: the K, Q and V tiles of a chunk are copied from HBM straight
+// into LDS (global_load_lds, 16 bytes per lane, double-buffered so the next
+// chunk streams in under the current one); K^T and V in accumulator layout are
+// read from the same row-major tiles with the transposing LDS read.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -103,131 +109,80 @@ __device__ bool decode_task(const FwdParams& prm, int phase, Task& t) {
     return true;
 }
 
-// V goes through LDS (transposed, read back as accumulator-layout fragments)
-// for bf16; the float32 build keeps V in registers so that its tiles fit in LDS.
-template <typename T> struct VInLds { static constexpr bool value = sizeof(T) == 2; };
+// bf16 tiles are double-buffered; the float32 build (used for the small float32
+// workloads only) single-buffers to fit in LDS.
+template <typename T> struct NBuf { static constexpr int value = sizeof(T) == 2 ? 2 : 1; };
 
 template <typename T>
 struct Smem {
-    T krm[kChunk * kDk];   // K, A layout, rows = position, contraction = dk
-    T qrm[kChunk * kDk];   // Q, same layout
-    T ktr[kDk * kChunk];   // K^T, A layout, rows = dk, contraction = position
-    T vtr[VInLds<T>::value ? kDv * kChunk : 8];  // V^T, A layout, rows = dv, contraction = position
-    T tt[kChunk * kChunk];   // Tt = T diag(beta), rows r, contraction s
-    // P = (Q K^T) o Mask in full mode; T0 diag(beta) (gate-free) in pass-1
-    T pm[kChunk * kChunk];
-    float exch[64 * 16];     // accumulator hand-over between waves
-    float gam[kChunk];       // gamma_r
-    float gp[kChunk];        // exp(gamma_r - gamma_C/2)
-    float gn[kChunk];        // exp(gamma_C/2 - gamma_r)
-    float Gam[kChunk];       // Gamma_r
-    float E[kChunk];         // Gamma_C / Gamma_r
+    static constexpr int NB = NBuf<T>::value;
+    T kt[NB][kChunk * kDk];   // K, row-major [position][dk]
+    T qt[NB][kChunk * kDk];   // Q
+    T vt[NB][kChunk * kDv];   // V, row-major [position][dv]
+    T tt[kChunk * kChunk];    // Tt = T diag(beta), row-major [r][s]
+    T pm[kChunk * kChunk];    // P = (Q K^T) o Mask (full mode) / T0 diag(beta) (pass-1)
+    float exch[64 * 16];      // accumulator hand-over between waves 0 and 1
+    float gam[kChunk];        // gamma_r
+    float gp[kChunk];         // exp(gamma_r - gamma_C/2)
+    float gn[kChunk];         // exp(gamma_C/2 - gamma_r)
+    float Gam[kChunk];        // Gamma_r
+    float E[kChunk];          // Gamma_C / Gamma_r
     float beta[kChunk];
-    float scal[4];           // [0] Gamma_C, [1] pairwise-exp flag
+    float scal[4];            // [0] Gamma_C, [1] pairwise-exp flag
 };
 
-// Chunk staging registers: one 16-byte vector per thread and row group.
-template <typename T> struct Vec;
-template <> struct Vec<__bf16> {
-    typedef __bf16 v16 __attribute__((ext_vector_type(8)));
-    typedef __bf16 v4 __attribute__((ext_vector_type(4)));
-};
-template <> struct Vec<float> {
-    typedef float v16 __attribute__((ext_vector_type(4)));
-    typedef float v4 __attribute__((ext_vector_type(4)));
-};
-
-template <typename T>
-struct Stage {
-    static constexpr int VE = 16 / (int)sizeof(T);          // elements per vector
-    static constexpr int VPR = kDk / VE;                     // vectors per row
-    static constexpr int NV = kChunk * VPR / 256;            // vectors per thread
-    typename Vec<T>::v16 kv[NV];
-    typename Vec<T>::v16 qv[NV];
-    typename Vec<T>::v16 vv[VInLds<T>::value ? NV : 1];
-    float gb;     // g (wave 0) or beta (wave 1) of position (tid & 63)
-};
-
-// Read the V values this lane needs for the state step, in accumulator layout.
-template <typename T>
-__device__ __forceinline__ void load_v(const T* v, int b, int h, int H, int T_, int t0, int nvalid,
-                                       int col, int g, float* out /*32*/) {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            int pos = 32 * rt + rho(g, r);
-            float x = 0.f;
-            if (pos < nvalid) x = (float)v[(((size_t)b * T_ + t0 + pos) * H + h) * kDv + col];
-            out[16 * rt + r] = x;
-        }
+__device__ __forceinline__ void wait_all_loads() {
+    // vmcnt(0) and lgkmcnt(0): this wave's global->LDS copies and LDS writes are done
+    __builtin_amdgcn_s_waitcnt(0x0070);
 }
 
+// Copy one 64 x 128 tile of chunk rows [t0, t0 + nvalid) of head (b, h) into a
+// swizzled row-major LDS tile.  Full chunks go HBM -> LDS directly (each lane's 16
+// bytes land at slot base + 16*lane, so the lane fetches the chunk that belongs
+// there); a short last chunk goes through registers and is zero-filled.
 template <typename T>
-__device__ __forceinline__ void load_stage(const FwdParams& prm, int b, int h, int t0, int nvalid,
-                                           bool need_q, Stage<T>& st) {
-    const int tid = threadIdx.x;
-    const T* k = (const T*)prm.k;
-    const T* q = (const T*)prm.q;
+__device__ __forceinline__ void load_tile(T* tile, const T* src, int b, int h, int T_, int H, int t0,
+                                          int nvalid) {
+    constexpr int EPC = 16 / (int)sizeof(T);
+    constexpr int CPR = kDk / EPC;                 // 16-byte chunks per row
+    constexpr int ROUNDS = kChunk * CPR / 256;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const size_t rowstride = (size_t)H * kDk;
+    const T* base = src + (((size_t)b * T_ + t0) * H + h) * kDk;
+    if (nvalid == kChunk) {
 #pragma unroll
-    for (int i = 0; i < Stage<T>::NV; ++i) {
-        int vi = tid + 256 * i;
-        int row = vi / Stage<T>::VPR, cv = vi % Stage<T>::VPR;
-        size_t off = (((size_t)b * prm.T + t0 + row) * prm.H + h) * kDk + cv * Stage<T>::VE;
-        typedef typename Vec<T>::v16 V16;
-        V16 z;
+        for (int i = 0; i < ROUNDS; ++i) {
+            const int L = (i * 4 + w) * 64 + lane;     // slot index in the tile
+            const int row = L / CPR, slot = L % CPR;
+            const int c = slot ^ swz(row);
+            const T* gp = base + row * rowstride + c * EPC;
+            T* lbase = tile + (i * 4 + w) * 64 * EPC;
+            __builtin_amdgcn_global_load_lds((const void*)gp,
+                                             (__attribute__((address_space(3))) void*)lbase, 16, 0, 0);
+        }
+    } else {
+        typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-        for (int e = 0; e < Stage<T>::VE; ++e) z[e] = (T)0.f;
-        st.kv[i] = row < nvalid ? *(const V16*)(k + off) : z;
-        st.qv[i] = (need_q && row < nvalid) ? *(const V16*)(q + off) : z;
-        if (VInLds<T>::value) st.vv[i] = row < nvalid ? *(const V16*)((const T*)prm.v + off) : z;
+        for (int i = 0; i < ROUNDS; ++i) {
+            const int L = (i * 4 + w) * 64 + lane;
+            const int row = L / CPR, slot = L % CPR;
+            const int c = slot ^ swz(row);
+            u4 v = {0u, 0u, 0u, 0u};
+            if (row < nvalid) v = *(const u4*)(base + row * rowstride + c * EPC);
+            *(u4*)(tile + L * EPC) = v;
+        }
     }
-    const int pos = tid & 63;
-    float x = 0.f;
-    if (tid < 128 && pos < nvalid) {
-        size_t go = ((size_t)b * prm.T + t0 + pos) * prm.H + h;
-        x = tid < 64 ? prm.g[go] : prm.beta[go];
-    }
-    st.gb = x;
 }
 
-// Write staged K/Q into the A-layout tiles, K^T into its own tile, and the
-// per-position gate vectors (wave 0 does the in-chunk scan).
+// Gate vectors of one chunk from g (wave 0) and beta (wave 1): the in-chunk scan
+// and the 2C+1 exponentials of the factored gate (paragraph 6), re-centred at
+// gamma_C/2 so both factors stay within exp(|gamma_C|/2).  Chunks whose decay
+// exceeds that safe range use pairwise exponentials exp(gamma_r - gamma_s).
 template <typename T>
-__device__ __forceinline__ void store_stage(Smem<T>& sm, const Stage<T>& st, bool need_q,
-                                            float& gsum_acc) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < Stage<T>::NV; ++i) {
-        int vi = tid + 256 * i;
-        int row = vi / Stage<T>::VPR, cv = vi % Stage<T>::VPR;
-        typedef typename Vec<T>::v4 V4;
-        const auto& ke = st.kv[i];
-        const auto& qe = st.qv[i];
-#pragma unroll
-        for (int c4 = 0; c4 < Stage<T>::VE; c4 += 4) {
-            int col = cv * Stage<T>::VE + c4;
-            int off = lds_elem(row, col, kDk);
-            V4 kk, qq;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { kk[e] = ke[c4 + e]; qq[e] = qe[c4 + e]; }
-            *(V4*)(sm.krm + off) = kk;
-            if (need_q) *(V4*)(sm.qrm + off) = qq;
-        }
-#pragma unroll
-        for (int e = 0; e < Stage<T>::VE; ++e) {
-            int col = cv * Stage<T>::VE + e;
-            sm.ktr[lds_elem(col, row, kChunk)] = ke[e];
-            if (VInLds<T>::value) sm.vtr[lds_elem(col, row, kChunk)] = st.vv[i][e];
-        }
-    }
-    const int lane = tid & 63;
+__device__ __forceinline__ void gate_vectors(Smem<T>& sm, float gb, float& gsum_acc) {
+    const int tid = threadIdx.x, lane = tid & 63;
     if (tid < 64) {
-        // gate prep with the diagonal scaling pulled outside the inverse (paragraph 6):
-        // 2C+1 exponentials per chunk, re-centred at gamma_C/2 so that both
-        // factors stay within exp(|gamma_C|/2).  Chunks whose decay exceeds the
-        // safe range fall back to pairwise exponentials exp(gamma_r - gamma_s).
-        float gam = wave_inclusive_scan(st.gb);
+        float gam = wave_inclusive_scan(gb);
         float gC = __shfl(gam, 63, 64);
         float half = 0.5f * gC;
         bool pairwise = gC < -160.f;
@@ -245,8 +200,28 @@ __device__ __forceinline__ void store_stage(Smem<T>& sm, const Stage<T>& st, boo
         }
         gsum_acc += gC;
     } else if (tid < 128) {
-        sm.beta[lane] = st.gb;
+        sm.beta[lane] = gb;
     }
+}
+
+__device__ __forceinline__ float load_gb(const FwdParams& prm, int b, int h, int t0, int nvalid) {
+    const int tid = threadIdx.x, pos = tid & 63;
+    float x = 0.f;
+    if (tid < 128 && pos < nvalid) {
+        size_t go = ((size_t)b * prm.T + t0 + pos) * prm.H + h;
+        x = tid < 64 ? prm.g[go] : prm.beta[go];
+    }
+    return x;
+}
+
+// threadIdx.x hidden from loop-invariant code motion: the swizzled LDS addresses
+// derived from it are then recomputed in each chunk step instead of being
+// hoisted out of the chunk loop, where ~200 precomputed addresses would stay
+// live and push the state and operands into scratch.
+__device__ __forceinline__ int opaque_tid() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
 }
 
 // Per-position vector values for the 16 accumulator rows of row tile rt.
@@ -267,7 +242,7 @@ __device__ __forceinline__ float mask_factor(const Smem<T>& sm, int r, int s, bo
     return pairwise ? __expf(sm.gam[r] - sm.gam[s]) : sm.gp[r] * sm.gn[s];
 }
 
-// 32x32 product of two accumulator-form operands: returns acc(X Y) given
+// 32x32 product of two accumulator-form operands: returns c + X Y given
 // xt = acc(X^T) (its fragments are the A fragments of X) and y = acc(Y).
 template <typename T>
 __device__ __forceinline__ f32x16 mm_acc(const f32x16& xt, const f32x16& y, f32x16 c) {
@@ -276,8 +251,8 @@ __device__ __forceinline__ f32x16 mm_acc(const f32x16& xt, const f32x16& y, f32x
     return c;
 }
 
-// Inverse of (I + Nd) for one 32x32 diagonal block from S = K_p K_p^T (acc form).
-// Returns acc(T0_pp) in z and acc(T0_pp^T) in zt.
+// Inverse of (I + Nd) for one 32x32 diagonal block, Nd = diag(beta) strict_lower(S),
+// from S = K_p K_p^T (acc form).  Returns acc(T0_pp) in z and acc(T0_pp^T) in zt.
 template <typename T>
 __device__ __forceinline__ void diag_inverse(const f32x16& S, const float* beta_blk, int n, int g,
                                              f32x16& z, f32x16& zt) {
@@ -286,50 +261,46 @@ __device__ __forceinline__ void diag_inverse(const f32x16& S, const float* beta_
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         int row = rho(g, r);
-        m[r] = (n < row) ? -beta_blk[row] * S[r] : 0.f;   // M = -diag(beta) strict_lower(S)
-        mt[r] = (row < n) ? -bn * S[r] : 0.f;             // M^T
+        m[r] = (n < row) ? -beta_blk[row] * S[r] : 0.f;   // M = -Nd
+        mt[r] = (row < n) ? -bn * S[r] : 0.f;             // M^T (S is symmetric)
         float id = (row == n) ? 1.f : 0.f;
         z[r] = id + m[r];
         zt[r] = id + mt[r];
     }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-        f32x16 m2 = mm_acc<T>(mt, m, zero16());    // M^2
-        f32x16 m2t = mm_acc<T>(m, mt, zero16());   // (M^2)^T = M^T M^T
+        f32x16 m2 = mm_acc<T>(mt, m, zero16());    // M^(2^(it+1))
+        f32x16 m2t = mm_acc<T>(m, mt, zero16());   // its transpose
         m = m2;
         mt = m2t;
-        f32x16 zn = mm_acc<T>(zt, m, z);           // Z + Z M^(2^k)
-        f32x16 ztn = mm_acc<T>(m, zt, zt);         // Z^T + (M^(2^k))^T Z^T
+        f32x16 zn = mm_acc<T>(zt, m, z);           // Z (I + M^(2^(it+1)))
+        f32x16 ztn = mm_acc<T>(m, zt, zt);         // transpose of the same
         z = zn;
         zt = ztn;
     }
 }
 
+// Chunk-independent prep of one chunk: Tt (and T0 diag(beta) in pass-1) and P.
 template <typename T, int MODE>
-__device__ __forceinline__ void chunk_step(const FwdParams& prm, Smem<T>& sm, const Task& tk,
-                                           int b, int h, int c, bool emit, const float* vreg,
-                                           f32x16* Hs, f32x16* Ms) {
-    const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, n = lane & 31, g = lane >> 5;
+__device__ __forceinline__ void chunk_prep(Smem<T>& sm, int buf, bool emit, bool pairwise) {
     using F = typename FragOf<T>::type;
-    const int t0 = c * kChunk;
-    const int nvalid = prm.T - t0 < kChunk ? prm.T - t0 : kChunk;
-    const bool pairwise = sm.scal[1] != 0.f;
-
-    // ---------------- prep: inverse (waves 0, 1) and P tiles (waves 2, 3) ----------------
-    f32x16 w1_W;  // wave 1: W = A0_10^T T0_11^T
+    const int tid = opaque_tid(), w = tid >> 6, lane = tid & 63, n = lane & 31, g = lane >> 5;
+    const T* kt = sm.kt[buf];
+    const T* qt = sm.qt[buf];
+    f32x16 w1_W;
     if (w < 2) {
         const int p = w;
-        F kf[8];
+        f32x16 S = zero16(), x = zero16();
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) kf[ks] = ld_frag<T>(sm.krm, 32 * p + n, ks, g, kDk);
-        f32x16 S = zero16();
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) S = mma(kf[ks], kf[ks], S);
+        for (int ks = 0; ks < 8; ++ks) {
+            F kf = afrag<T, kDk>(kt, 32 * p + n, ks, g);
+            S = mma(kf, kf, S);
+            // wave 1 also needs K_1 K_0^T: A = K_1 rows, B = K_0^T (its fragment is a K_0 row read)
+            if (p == 1) x = mma(kf, afrag<T, kDk>(kt, n, ks, g), x);
+        }
         f32x16 z, zt;
         diag_inverse<T>(S, sm.beta + 32 * p, n, g, z, zt);
-        // A-layout fragments of the diagonal block of Tt (and T0 diag(beta)):
-        // acc(T0^T) lane n holds row 32p+n of T0, registers = columns.
+        // acc(T0^T): lane n holds row 32p+n of T0, registers = columns 32p + rho
         const int row = 32 * p + n;
 #pragma unroll
         for (int ksl = 0; ksl < 2; ++ksl) {
@@ -341,34 +312,29 @@ __device__ __forceinline__ void chunk_step(const FwdParams& prm, Smem<T>& sm, co
                 f[j] = (T)(col <= row ? t0v * mask_factor(sm, row, col, pairwise) : 0.f);
                 f0[j] = (T)t0v;
             }
-            st_frag<T>(sm.tt, row, 2 * p + ksl, g, kChunk, f);
-            if (MODE == MODE_PASS1) st_frag<T>(sm.pm, row, 2 * p + ksl, g, kChunk, f0);
+            st_afrag<T, kChunk>(sm.tt, row, 2 * p + ksl, g, f);
+            if (MODE == MODE_PASS1) st_afrag<T, kChunk>(sm.pm, row, 2 * p + ksl, g, f0);
         }
         if (p == 0) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) sm.exch[lane * 16 + r] = z[r];
         } else {
             // acc(A0_10) = diag(beta_1) K_1 K_0^T, then W = A0_10^T T0_11^T
-            f32x16 x = zero16();
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) x = mma(kf[ks], ld_frag<T>(sm.krm, n, ks, g, kDk), x);
             f32x16 a10;
 #pragma unroll
             for (int r = 0; r < 16; ++r) a10[r] = sm.beta[32 + rho(g, r)] * x[r];
-            // NOTE: x = acc(K_1 K_0^T) has lane n = column (block-0 position), rows = block-1 positions.
             w1_W = mm_acc<T>(a10, zt, zero16());
         }
-    } else if (emit) {
-        // P^T tiles: acc(K_j Q_i^T) lane n holds row 32i+n of Q K^T, registers = columns 32j+rho
+    } else if (MODE == MODE_FULL && emit) {
+        // acc(K_j Q_i^T): lane n holds row 32i+n of Q K^T, registers = columns 32j+rho
         const int ntile = (w == 2) ? 2 : 1;
         for (int tix = 0; tix < ntile; ++tix) {
-            int i, j;
-            if (w == 2) { i = tix; j = tix; } else { i = 1; j = 0; }
+            const int i = (w == 2) ? tix : 1;
+            const int j = (w == 2) ? tix : 0;
             f32x16 x = zero16();
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks)
-                x = mma(ld_frag<T>(sm.krm, 32 * j + n, ks, g, kDk),
-                        ld_frag<T>(sm.qrm, 32 * i + n, ks, g, kDk), x);
+                x = mma(afrag<T, kDk>(kt, 32 * j + n, ks, g), afrag<T, kDk>(qt, 32 * i + n, ks, g), x);
             const int row = 32 * i + n;
 #pragma unroll
             for (int ksl = 0; ksl < 2; ++ksl) {
@@ -376,16 +342,15 @@ __device__ __forceinline__ void chunk_step(const FwdParams& prm, Smem<T>& sm, co
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) {
                     int col = 32 * j + rho(g, 8 * ksl + jj);
-                    f[jj] = (T)(col <= row ? x[8 * ksl + jj] * mask_factor(sm, row, col, pairwise)
-                                           : 0.f);
+                    f[jj] = (T)(col <= row ? x[8 * ksl + jj] * mask_factor(sm, row, col, pairwise) : 0.f);
                 }
-                st_frag<T>(sm.pm, row, 2 * j + ksl, g, kChunk, f);
+                st_afrag<T, kChunk>(sm.pm, row, 2 * j + ksl, g, f);
             }
         }
     }
     __syncthreads();
     if (w == 1) {
-        // T0_10^T = -T0_00^T (A0_10^T T0_11^T): A fragments of T0_00^T are acc(T0_00)
+        // T0_10^T = -T0_00^T (A0_10^T T0_11^T); the A fragments of T0_00^T are acc(T0_00)
         f32x16 t00;
 #pragma unroll
         for (int r = 0; r < 16; ++r) t00[r] = sm.exch[lane * 16 + r];
@@ -401,92 +366,97 @@ __device__ __forceinline__ void chunk_step(const FwdParams& prm, Smem<T>& sm, co
                 f[j] = (T)(t0v * mask_factor(sm, row, col, pairwise));
                 f0[j] = (T)t0v;
             }
-            st_frag<T>(sm.tt, row, ksl, g, kChunk, f);
-            if (MODE == MODE_PASS1) st_frag<T>(sm.pm, row, ksl, g, kChunk, f0);
+            st_afrag<T, kChunk>(sm.tt, row, ksl, g, f);
+            if (MODE == MODE_PASS1) st_afrag<T, kChunk>(sm.pm, row, ksl, g, f0);
         }
     }
     __syncthreads();
+}
 
-    // ---------------- state step (every wave, its 32 columns) ----------------
-    F hf[8];
+// H <- a H + K^T B with B given as four fragments over the chunk positions.
+template <typename T>
+__device__ __forceinline__ void state_update(const T* kt, f32x16* Hs, float a,
+                                             const typename FragOf<T>::type* bf, int lane) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) hf[ks] = acc_frag<T>(Hs[ks >> 1], ks & 1);
-    f32x16 X[2] = {zero16(), zero16()};
-    f32x16 QH[2] = {zero16(), zero16()};
-    f32x16 XM[2] = {zero16(), zero16()};
-    F mf[8];
-    if (MODE == MODE_PASS1) {
+    for (int ht = 0; ht < 4; ++ht) {
+        f32x16 acc = Hs[ht] * a;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) mf[ks] = acc_frag<T>(Ms[ks >> 1], ks & 1);
+        for (int ks = 0; ks < 4; ++ks) acc = mma(tfrag<T, kDk>(kt, 32 * ht, ks, lane), bf[ks], acc);
+        Hs[ht] = acc;
     }
+}
+
+// X = K Hm for the two 32-row position tiles (Hm: the four dk tiles of a state).
+template <typename T>
+__device__ __forceinline__ void k_times_state(const T* kt, const f32x16* Hm, int n, int g, f32x16* X) {
+    using F = typename FragOf<T>::type;
+    X[0] = zero16();
+    X[1] = zero16();
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
+        F hf = acc_frag<T>(Hm[ks >> 1], ks & 1);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            F a = ld_frag<T>(sm.krm, 32 * rt + n, ks, g, kDk);
-            X[rt] = mma(a, hf[ks], X[rt]);
-            if (MODE == MODE_PASS1) XM[rt] = mma(a, mf[ks], XM[rt]);
-        }
+        for (int rt = 0; rt < 2; ++rt) X[rt] = mma(afrag<T, kDk>(kt, 32 * rt + n, ks, g), hf, X[rt]);
     }
-    if (MODE == MODE_FULL && emit) {
+}
+
+// Lower-triangular 64x64 (row-major tile) times the 64x32 operand given as fragments.
+template <typename T>
+__device__ __forceinline__ void tri_times(const T* tile, const typename FragOf<T>::type* yf, int n,
+                                          int g, f32x16* out) {
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
+    for (int ks = 0; ks < 2; ++ks) out[0] = mma(afrag<T, kChunk>(tile, n, ks, g), yf[ks], out[0]);
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-                QH[rt] = mma(ld_frag<T>(sm.qrm, 32 * rt + n, ks, g, kDk), hf[ks], QH[rt]);
-    }
-    // Y = V - diag(Gamma) X
-    f32x16 Y[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        f32x16 gr = rows_of(sm.Gam, rt, g);
-        f32x16 vr;
-        if constexpr (VInLds<T>::value) {
-            F v0 = ld_frag<T>(sm.vtr, 32 * w + n, 2 * rt, g, kChunk);
-            F v1 = ld_frag<T>(sm.vtr, 32 * w + n, 2 * rt + 1, g, kChunk);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) { vr[j] = (float)v0[j]; vr[8 + j] = (float)v1[j]; }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) vr[r] = vreg[16 * rt + r];
-        }
-        Y[rt] = vr - gr * X[rt];
-    }
+    for (int ks = 0; ks < 4; ++ks) out[1] = mma(afrag<T, kChunk>(tile, 32 + n, ks, g), yf[ks], out[1]);
+}
+
+// The serial state step of one chunk for this wave's 32 state columns.
+template <typename T, int MODE>
+__device__ __forceinline__ void chunk_state(const FwdParams& prm, Smem<T>& sm, int buf, int b, int h,
+                                            int t0, int nvalid, bool emit, f32x16* Hs, f32x16* Ms) {
+    using F = typename FragOf<T>::type;
+    const int tid = opaque_tid(), w = tid >> 6, lane = tid & 63, n = lane & 31, g = lane >> 5;
+    const T* kt = sm.kt[buf];
+    const T* qt = sm.qt[buf];
+    const T* vt = sm.vt[buf];
+
+    f32x16 X[2];
+    k_times_state<T>(kt, Hs, n, g, X);
+    // Y = V - diag(Gamma) X (V in accumulator layout via the transposing read)
     F yf[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) yf[ks] = acc_frag<T>(Y[ks >> 1], ks & 1);
-    // V' = Tt Y (Tt lower triangular: row tile 0 needs k-steps 0-1 only)
-    f32x16 Vp[2] = {zero16(), zero16()};
+    for (int rt = 0; rt < 2; ++rt) {
+        F v0 = tfrag<T, kDv>(vt, 32 * w, 2 * rt, lane);
+        F v1 = tfrag<T, kDv>(vt, 32 * w, 2 * rt + 1, lane);
+        f32x16 gr = rows_of(sm.Gam, rt, g);
+        f32x16 y;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) Vp[0] = mma(ld_frag<T>(sm.tt, n, ks, g, kChunk), yf[ks], Vp[0]);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) Vp[1] = mma(ld_frag<T>(sm.tt, 32 + n, ks, g, kChunk), yf[ks], Vp[1]);
-    f32x16 VpM[2] = {zero16(), zero16()};
-    if (MODE == MODE_PASS1) {
-        F ymf[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            f32x16 t = XM[ks >> 1];
-            ymf[ks] = acc_frag<T>(-t, ks & 1);
+        for (int j = 0; j < 8; ++j) {
+            y[j] = (float)v0[j] - gr[j] * X[rt][j];
+            y[8 + j] = (float)v1[j] - gr[8 + j] * X[rt][8 + j];
         }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            VpM[0] = mma(ld_frag<T>(sm.pm, n, ks, g, kChunk), ymf[ks], VpM[0]);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            VpM[1] = mma(ld_frag<T>(sm.pm, 32 + n, ks, g, kChunk), ymf[ks], VpM[1]);
+        yf[2 * rt] = acc_frag<T>(y, 0);
+        yf[2 * rt + 1] = acc_frag<T>(y, 1);
     }
+    f32x16 Vp[2] = {zero16(), zero16()};
+    tri_times<T>(sm.tt, yf, n, g, Vp);
+
     if (MODE == MODE_FULL && emit) {
+        // O = scale (diag(Gamma) Q H + P V')
+        f32x16 QH[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            F hf = acc_frag<T>(Hs[ks >> 1], ks & 1);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) QH[rt] = mma(afrag<T, kDk>(qt, 32 * rt + n, ks, g), hf, QH[rt]);
+        }
         F vf[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) vf[ks] = acc_frag<T>(Vp[ks >> 1], ks & 1);
         f32x16 O[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) O[rt] = rows_of(sm.Gam, rt, g) * QH[rt];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) O[0] = mma(ld_frag<T>(sm.pm, n, ks, g, kChunk), vf[ks], O[0]);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) O[1] = mma(ld_frag<T>(sm.pm, 32 + n, ks, g, kChunk), vf[ks], O[1]);
+        tri_times<T>(sm.pm, vf, n, g, O);
         T* o = (T*)prm.o;
         const int col = 32 * w + n;
 #pragma unroll
@@ -499,7 +469,6 @@ __device__ __forceinline__ void chunk_step(const FwdParams& prm, Smem<T>& sm, co
             }
     }
     // H <- Gamma_C H + K^T diag(E) V'
-    const float GC = sm.scal[0];
     F ef[4];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
@@ -507,24 +476,19 @@ __device__ __forceinline__ void chunk_step(const FwdParams& prm, Smem<T>& sm, co
         ef[2 * rt] = acc_frag<T>(ev, 0);
         ef[2 * rt + 1] = acc_frag<T>(ev, 1);
     }
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-        f32x16 acc = Hs[ht] * GC;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mma(ld_frag<T>(sm.ktr, 32 * ht + n, ks, g, kChunk), ef[ks], acc);
-        Hs[ht] = acc;
-    }
+    state_update<T>(kt, Hs, sm.scal[0], ef, lane);
+
     if (MODE == MODE_PASS1) {
-        F mvf[4];
+        // Mt <- Mt - K^T T0 diag(beta) K Mt  (V = 0, no gates)
+        k_times_state<T>(kt, Ms, n, g, X);
+        F mf[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) mvf[ks] = acc_frag<T>(VpM[ks >> 1], ks & 1);
+        for (int ks = 0; ks < 4; ++ks) mf[ks] = acc_frag<T>(-X[ks >> 1], ks & 1);
+        f32x16 VpM[2] = {zero16(), zero16()};
+        tri_times<T>(sm.pm, mf, n, g, VpM);
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) {
-            f32x16 acc = Ms[ht];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) acc = mma(ld_frag<T>(sm.ktr, 32 * ht + n, ks, g, kChunk), mvf[ks], acc);
-            Ms[ht] = acc;
-        }
+        for (int ks = 0; ks < 4; ++ks) mf[ks] = acc_frag<T>(VpM[ks >> 1], ks & 1);
+        state_update<T>(kt, Ms, 1.f, mf, lane);
     }
 }
 
@@ -545,10 +509,21 @@ __device__ __forceinline__ void store_state(float* dst, int w, int lane, const f
             dst[(32 * ht + rho(g, r)) * kDv + 32 * w + n] = Hs[ht][r];
 }
 
+template <typename T>
+__device__ __forceinline__ void load_chunk_tiles(const FwdParams& prm, Smem<T>& sm, int buf, int b,
+                                                 int h, int c, bool need_q) {
+    const int t0 = c * kChunk;
+    const int nvalid = prm.T - t0 < kChunk ? prm.T - t0 : kChunk;
+    load_tile<T>(sm.kt[buf], (const T*)prm.k, b, h, prm.T, prm.H, t0, nvalid);
+    load_tile<T>(sm.vt[buf], (const T*)prm.v, b, h, prm.T, prm.H, t0, nvalid);
+    if (need_q) load_tile<T>(sm.qt[buf], (const T*)prm.q, b, h, prm.T, prm.H, t0, nvalid);
+}
+
 template <typename T, int MODE>
 __device__ void run_task(const FwdParams& prm, Smem<T>& sm, const Task& tk) {
+    constexpr int NB = NBuf<T>::value;
     const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, n = lane & 31, g = lane >> 5;
+    const int w = tid >> 6, lane = tid & 63, g = lane >> 5, n = lane & 31;
     const int b = tk.bh / prm.H, h = tk.bh % prm.H;
     const size_t SS = (size_t)kDk * kDv;
 
@@ -569,36 +544,29 @@ __device__ void run_task(const FwdParams& prm, Smem<T>& sm, const Task& tk) {
     }
     float gsum = 0.f;
 
-    Stage<T> st;
-    constexpr int NVR = VInLds<T>::value ? 1 : 32;
-    float vcur[NVR], vnext[NVR];
-    {
-        const int c = tk.c_begin;
-        const int t0 = c * kChunk;
-        const int nvalid = prm.T - t0 < kChunk ? prm.T - t0 : kChunk;
-        const bool need_q = MODE == MODE_FULL && c >= tk.c_out;
-        load_stage<T>(prm, b, h, t0, nvalid, need_q, st);
-        if constexpr (!VInLds<T>::value)
-            load_v<T>((const T*)prm.v, b, h, prm.H, prm.T, t0, nvalid, 32 * w + n, g, vnext);
-    }
+    auto nvalid_of = [&](int c) { return prm.T - c * kChunk < kChunk ? prm.T - c * kChunk : kChunk; };
+    float gb = load_gb(prm, b, h, tk.c_begin * kChunk, nvalid_of(tk.c_begin));
+    if (NB == 2)
+        load_chunk_tiles<T>(prm, sm, 0, b, h, tk.c_begin, MODE == MODE_FULL && tk.c_begin >= tk.c_out);
+
     for (int c = tk.c_begin; c < tk.c_end; ++c) {
         const bool emit = MODE == MODE_FULL && c >= tk.c_out;
-        __syncthreads();  // the previous chunk's state step is done with the tiles
-        store_stage<T>(sm, st, emit, gsum);
-        if constexpr (!VInLds<T>::value) {
-#pragma unroll
-            for (int i = 0; i < NVR; ++i) vcur[i] = vnext[i];
+        const int buf = NB == 2 ? ((c - tk.c_begin) & 1) : 0;
+        const int t0 = c * kChunk, nvalid = nvalid_of(c);
+        if (NB == 1) {
+            __syncthreads();   // the previous chunk is done with the single buffer
+            load_chunk_tiles<T>(prm, sm, 0, b, h, c, emit);
         }
+        wait_all_loads();
+        __syncthreads();       // chunk c is in LDS; the previous chunk is done with buffer buf^1
+        if (NB == 2 && c + 1 < tk.c_end)
+            load_chunk_tiles<T>(prm, sm, buf ^ 1, b, h, c + 1, MODE == MODE_FULL && c + 1 >= tk.c_out);
+        gate_vectors<T>(sm, gb, gsum);
+        if (c + 1 < tk.c_end) gb = load_gb(prm, b, h, t0 + kChunk, nvalid_of(c + 1));
         __syncthreads();
-        if (c + 1 < tk.c_end) {
-            const int t0 = (c + 1) * kChunk;
-            const int nvalid = prm.T - t0 < kChunk ? prm.T - t0 : kChunk;
-            const bool need_q = MODE == MODE_FULL && c + 1 >= tk.c_out;
-            load_stage<T>(prm, b, h, t0, nvalid, need_q, st);
-            if constexpr (!VInLds<T>::value)
-                load_v<T>((const T*)prm.v, b, h, prm.H, prm.T, t0, nvalid, 32 * w + n, g, vnext);
-        }
-        chunk_step<T, MODE>(prm, sm, tk, b, h, c, emit, vcur, Hs, Ms);
+        const bool pairwise = sm.scal[1] != 0.f;
+        chunk_prep<T, MODE>(sm, buf, emit, pairwise);
+        chunk_state<T, MODE>(prm, sm, buf, b, h, t0, nvalid, emit, Hs, Ms);
     }
 
     if (tk.dst == DST_HT) {
@@ -615,7 +583,8 @@ __device__ void run_task(const FwdParams& prm, Smem<T>& sm, const Task& tk) {
 
 template <typename T, int PHASE>
 __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(FwdParams prm) {
-    __shared__ __attribute__((aligned(16))) Smem<T> sm;
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    Smem<T>& sm = *reinterpret_cast<Smem<T>*>(smem_raw);
     Task tk;
     if (!decode_task(prm, PHASE, tk)) return;
     // only the first launch of a split forward has pass-1 tasks
@@ -625,17 +594,25 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(FwdParams prm) {
         run_task<T, MODE_FULL>(prm, sm, tk);
 }
 
+template <typename T, int PHASE>
+hipError_t launch_phase(const FwdParams& p, int grid, hipStream_t s) {
+    const size_t lds = sizeof(Smem<T>);
+    static bool configured = false;
+    if (!configured) {
+        hipError_t e = hipFuncSetAttribute((const void*)gdn_fwd_kernel<T, PHASE>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        configured = true;
+    }
+    hipLaunchKernelGGL((gdn_fwd_kernel<T, PHASE>), dim3(grid), dim3(256), lds, s, p);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_fwd_t(const FwdParams& p, int phase, hipStream_t s) {
-    dim3 block(256);
-    if (phase == PHASE_SINGLE) {
-        hipLaunchKernelGGL((gdn_fwd_kernel<T, PHASE_SINGLE>), dim3(p.B * p.H), block, 0, s, p);
-    } else if (phase == PHASE_A) {
-        hipLaunchKernelGGL((gdn_fwd_kernel<T, PHASE_A>), dim3(p.B * p.H * p.P), block, 0, s, p);
-    } else {
-        hipLaunchKernelGGL((gdn_fwd_kernel<T, PHASE_C>), dim3(p.B * p.H * (p.P - 1)), block, 0, s, p);
-    }
-    return hipGetLastError();
+    if (phase == PHASE_SINGLE) return launch_phase<T, PHASE_SINGLE>(p, p.B * p.H, s);
+    if (phase == PHASE_A) return launch_phase<T, PHASE_A>(p, p.B * p.H * p.P, s);
+    return launch_phase<T, PHASE_C>(p, p.B * p.H * (p.P - 1), s);
 }
 
 }  // namespace

@@ -7,8 +7,8 @@
 //   1. chunk sums s[b][c][h] = sum of g over the (up to) 64 tokens of chunk c;
 //      consecutive threads take consecutive heads, so each token row of g
 //      ([B,T,H], H contiguous) is read with coalesced accesses;
-//   2. per head: W_c = s_{c-w+1} + ... + s_c for c >= w-1 (each window summed
-//      directly), its maximum over c, and flag = N >= w && max <= log_eps.
+//   2. per head (one workgroup): W_c = s_{c-w+1} + ... + s_c for c >= w-1 (each
+//      window summed directly), its maximum over c, and flag = N >= w && max <= log_eps.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -34,34 +34,48 @@ __global__ __launch_bounds__(256) void chunk_sums_kernel(const float* __restrict
     }
 }
 
+// One workgroup per head: each thread sums the windows ending at its chunks,
+// then the workgroup takes the maximum.
 __global__ __launch_bounds__(256) void window_flags_kernel(const float* __restrict__ sums, int B,
                                                            int H, int N, int w, float log_eps,
                                                            int32_t* __restrict__ flags,
                                                            float* __restrict__ maxwin) {
-    const int bh = blockIdx.x * blockDim.x + threadIdx.x;
-    if (bh >= B * H) return;
+    __shared__ float red[256];
+    const int bh = blockIdx.x;
     const int b = bh / H, h = bh % H;
     float best = -INFINITY;
-    for (int c = w - 1; c < N; ++c) {
+    for (int c = w - 1 + (int)threadIdx.x; c < N; c += blockDim.x) {
         float acc = 0.f;
         for (int j = c - w + 1; j <= c; ++j) acc += sums[((size_t)b * N + j) * H + h];
         best = acc > best ? acc : best;
     }
-    flags[bh] = (N >= w && best <= log_eps) ? 1 : 0;
-    if (maxwin) maxwin[bh] = best;
+    red[threadIdx.x] = best;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if ((int)threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        best = red[0];
+        flags[bh] = (N >= w && best <= log_eps) ? 1 : 0;
+        if (maxwin) maxwin[bh] = best;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_gate_scan(const float* g, int B, int T, int H, int w, float log_eps,
-                            float* chunk_sums, int32_t* flags, float* maxwin, hipStream_t s) {
+hipError_t launch_chunk_sums(const float* g, int B, int T, int H, float* chunk_sums, hipStream_t s) {
     const int N = (T + kChunk - 1) / kChunk;
-    dim3 grid1((N + kChunksPerBlock - 1) / kChunksPerBlock, B);
-    hipLaunchKernelGGL(chunk_sums_kernel, grid1, dim3(256), 0, s, g, T, H, N, chunk_sums);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    dim3 grid2((B * H + 255) / 256);
-    hipLaunchKernelGGL(window_flags_kernel, grid2, dim3(256), 0, s, chunk_sums, B, H, N, w,
+    dim3 grid((N + kChunksPerBlock - 1) / kChunksPerBlock, B);
+    hipLaunchKernelGGL(chunk_sums_kernel, grid, dim3(256), 0, s, g, T, H, N, chunk_sums);
+    return hipGetLastError();
+}
+
+hipError_t launch_window_flags(const float* chunk_sums, int B, int T, int H, int w, float log_eps,
+                               int32_t* flags, float* maxwin, hipStream_t s) {
+    const int N = (T + kChunk - 1) / kChunk;
+    dim3 grid(B * H);
+    hipLaunchKernelGGL(window_flags_kernel, grid, dim3(256), 0, s, chunk_sums, B, H, N, w,
                        log_eps, flags, maxwin);
     return hipGetLastError();
 }

@@ -39,8 +39,9 @@ enum FwdPhase { PHASE_SINGLE = 0, PHASE_A = 1, PHASE_C = 2 };
 
 hipError_t launch_fwd(const FwdParams& p, int phase, bool bf16, hipStream_t s);
 hipError_t launch_combine(const FwdParams& p, hipStream_t s);
-hipError_t launch_gate_scan(const float* g, int B, int T, int H, int w, float log_eps,
-                            float* chunk_sums, int32_t* flags, float* maxwin, hipStream_t s);
+hipError_t launch_chunk_sums(const float* g, int B, int T, int H, float* chunk_sums, hipStream_t s);
+hipError_t launch_window_flags(const float* chunk_sums, int B, int T, int H, int w, float log_eps,
+                               int32_t* flags, float* maxwin, hipStream_t s);
 
 struct BwdParams {
     const void* q;

@@ -145,6 +145,29 @@ gdn_status gdn_gate_scan(const float* g, int B, int T, int H, int window_chunks,
                          int32_t* flags, float* max_window_logdecay, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Kinds of kernel launch reported by gdn_profile_events. */
+typedef enum {
+    GDN_LAUNCH_GATE_SUMS = 0,   /* gate scan: per-chunk sums of g                     */
+    GDN_LAUNCH_GATE_FLAGS = 1,  /* gate scan: window maxima and flags                 */
+    GDN_LAUNCH_FWD_SINGLE = 2,  /* fused forward, unsplit                             */
+    GDN_LAUNCH_FWD_PASS_A = 3,  /* fused forward: window heads, segment 0, pass-1     */
+    GDN_LAUNCH_COMBINE = 4,     /* segment combine                                    */
+    GDN_LAUNCH_FWD_PASS_C = 5,  /* fused forward: exact heads from corrected states   */
+    GDN_LAUNCH_BWD_STATES = 6,  /* backward: chunk-boundary state recompute           */
+    GDN_LAUNCH_BWD = 7          /* backward: reverse sweep and local gradients        */
+} gdn_launch_kind;
+
+/* Measurement hook (the talk summary, paragraph 7, argues the fused operator
+ * stays memory-bound; timing each launch is how that is checked).  While set,
+ * every kernel launch the library makes from this thread is bracketed by
+ * hipEventRecord(events[2i]) and hipEventRecord(events[2i+1]) on the launch
+ * stream, and labels[i] receives its gdn_launch_kind, for i = 0..capacity-1;
+ * later launches are not recorded.  events holds 2*capacity hipEvent_t created
+ * by the caller.  Passing events == NULL clears the hook.  Returns the number of
+ * launches recorded since the hook was last set.  Host-only bookkeeping: no
+ * device memory is touched. */
+int gdn_profile_events(void** events, int* labels, int capacity);
+
 /* Thread-local text describing the last non-OK status on this thread ("" if none). */
 const char* gdn_last_error(void);
 
