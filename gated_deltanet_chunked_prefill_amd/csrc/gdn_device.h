@@ -76,14 +76,18 @@ __device__ __forceinline__ typename FragOf<T>::type acc_frag_scaled(const f32x16
 }
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int swz4(int row) { return (row ^ (row >> 2)) & 3; }
 
 // Natural row-major tiles in LDS: a row of `Cols` elements is stored as 16-byte
-// chunks, chunk c of row r at slot c ^ swz(r) (8 consecutive rows read at the
-// same column land in distinct bank groups).  Element offset of (row, col):
+// chunks; chunk c of row r sits at slot c ^ s(r), with s = swz(r) for rows of
+// eight or more chunks and swz4(r) for rows of four, so rows read together at
+// the same column land in different bank groups.  Element offset of (row, col):
 template <typename T, int Cols>
 __device__ __forceinline__ int toff(int row, int col) {
     constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
-    return row * Cols + ((((col / EPC) ^ swz(row))) * EPC) + (col % EPC);
+    constexpr int CPR = Cols / EPC;             // chunks per row
+    const int s = CPR >= 8 ? swz(row) : swz4(row);
+    return row * Cols + (((col / EPC) ^ s) * EPC) + (col % EPC);
 }
 
 template <typename T> struct Quad;
