@@ -166,6 +166,11 @@ __device__ __forceinline__ int opaque_tid() {
     return t;
 }
 
+// Index of this thread's wave in the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 typedef __attribute__((address_space(3))) char lds_t;
 __device__ __forceinline__ const lds_t* as_lds(const void* p) { return (const lds_t*)p; }
 
@@ -399,6 +404,41 @@ __device__ __forceinline__ float gate_factor(float fr, float fc, bool pairwise) 
     return pairwise ? __expf(fr - fc) : fr * fc;
 }
 
+// Diagonal block p of the chunk: S = K_p K_p^T, T0_pp by the series, then the
+// gated Tt_pp (and the gate-free T0_pp diag(beta) in pass-1).  p is a template
+// parameter so that every per-lane address-table index is a compile-time constant.
+template <typename T, int MODE, int p>
+__device__ __forceinline__ void diag_block(const Lane<T>& L, const T* kt, T (*t32)[kT32],
+                                           const float* s_row, const float* s_col,
+                                           const float* s_beta, bool pairwise) {
+    using F = typename FragOf<T>::type;
+    const int n = L.n, g = L.g;
+    f32x16 S = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        F kf = L.f128(kt, p, ks);
+        S = mma(kf, kf, S);
+    }
+    const f32x16 brow = rows_of(s_beta, p, g);
+    f32x16 zt = diag_inverse_t<T>(S, brow, s_beta[32 * p + n], n, g);
+    // acc(T0^T): lane n holds row 32p+n of T0_pp, registers = columns 32p + rho
+    const float fr = s_row[32 * p + n];
+    const f32x16 fc = rows_of(s_col, p, g);
+#pragma unroll
+    for (int ksl = 0; ksl < 2; ++ksl) {
+        F f, f0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = 8 * ksl + j;
+            const float t0v = zt[r] * brow[r];
+            f[j] = (T)(rho(g, r) <= n ? t0v * gate_factor(fr, fc[r], pairwise) : 0.f);
+            f0[j] = (T)t0v;
+        }
+        L.st32(t32[p], ksl, f);
+        if (MODE == MODE_PASS1) L.st32(t32[p == 0 ? 3 : 5], ksl, f0);
+    }
+}
+
 // Chunk-independent prep of one chunk by prep wave pw.
 template <typename T, int MODE>
 __device__ __forceinline__ void chunk_prep(Smem<T>& sm, const Lane<T>& L, int pw, const T* kt,
@@ -412,7 +452,8 @@ __device__ __forceinline__ void chunk_prep(Smem<T>& sm, const Lane<T>& L, int pw
     // re-centred at gamma_C/2 so both factors stay within exp(|gamma_C|/2); chunks
     // whose decay exceeds that safe range use pairwise exponentials.
     const float gam = wave_inclusive_scan(gv);
-    const float gC = __shfl(gam, 63, 64);
+    const float gC = __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, __shfl(gam, 63, 64))));  // wave-uniform
     const float half = 0.5f * gC;
     const bool pairwise = gC < -160.f;
     const float gp = __expf(gam - half);
@@ -433,33 +474,10 @@ __device__ __forceinline__ void chunk_prep(Smem<T>& sm, const Lane<T>& L, int pw
     const float* s_col = scr + (pairwise ? 0 : 2) * kChunk;   // gamma or exp(gC/2 - gamma)
     const float* s_beta = scr + 3 * kChunk;
 
-    if (pw < 2) {
-        // diagonal block p: S = K_p K_p^T, T0_pp by the series, then Tt_pp
-        const int p = pw;
-        f32x16 S = zero16();
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            F kf = L.f128(kt, p, ks);
-            S = mma(kf, kf, S);
-        }
-        const f32x16 brow = rows_of(s_beta, p, g);
-        f32x16 zt = diag_inverse_t<T>(S, brow, s_beta[32 * p + n], n, g);
-        // acc(T0^T): lane n holds row 32p+n of T0_pp, registers = columns 32p + rho
-        const float fr = s_row[32 * p + n];
-        const f32x16 fc = rows_of(s_col, p, g);
-#pragma unroll
-        for (int ksl = 0; ksl < 2; ++ksl) {
-            F f, f0;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int r = 8 * ksl + j;
-                const float t0v = zt[r] * brow[r];
-                f[j] = (T)(rho(g, r) <= n ? t0v * gate_factor(fr, fc[r], pairwise) : 0.f);
-                f0[j] = (T)t0v;
-            }
-            L.st32(t32[p], ksl, f);
-            if (MODE == MODE_PASS1) L.st32(t32[p == 0 ? 3 : 5], ksl, f0);
-        }
+    if (pw == 0) {
+        diag_block<T, MODE, 0>(L, kt, t32, s_row, s_col, s_beta, pairwise);
+    } else if (pw == 1) {
+        diag_block<T, MODE, 1>(L, kt, t32, s_row, s_col, s_beta, pairwise);
     } else if (pw == 2) {
         // off-diagonal block: acc(K_0 K_1^T) has lane n = row 32+n, registers = columns rho
         f32x16 x = zero16();
@@ -518,16 +536,16 @@ __device__ __forceinline__ void chunk_prep(Smem<T>& sm, const Lane<T>& L, int pw
     }
 }
 
-// X = K Hm for the two 32-row position tiles (hf: fragments of the state).
+// X = K Hm for the two 32-row position tiles (Hm: the four dk tiles of a state).
 template <typename T>
-__device__ __forceinline__ void k_times(const Lane<T>& L, const T* kt,
-                                        const typename FragOf<T>::type* hf, f32x16* X) {
+__device__ __forceinline__ void k_times(const Lane<T>& L, const T* kt, const f32x16* Hm, f32x16* X) {
     X[0] = zero16();
     X[1] = zero16();
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-        X[0] = mma(L.f128(kt, 0, ks), hf[ks], X[0]);
-        X[1] = mma(L.f128(kt, 1, ks), hf[ks], X[1]);
+        const typename FragOf<T>::type hf = acc_frag<T>(Hm[ks >> 1], ks & 1);
+        X[0] = mma(L.f128(kt, 0, ks), hf, X[0]);
+        X[1] = mma(L.f128(kt, 1, ks), hf, X[1]);
     }
 }
 
@@ -570,21 +588,20 @@ __device__ __forceinline__ void chunk_state(const FwdParams& prm, const Lane<T>&
                                             f32x16* Hs, f32x16* Ms) {
     using F = typename FragOf<T>::type;
     const int n = L.n, g = L.g, w = L.w;
-    F hf[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) hf[ks] = acc_frag<T>(Hs[ks >> 1], ks & 1);
-
     f32x16 X[2];
     f32x16 OT[2] = {zero16(), zero16()};   // (Q H)^T: lane = position, registers = dv
     X[0] = zero16();
     X[1] = zero16();
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-        X[0] = mma(L.f128(kt, 0, ks), hf[ks], X[0]);
-        X[1] = mma(L.f128(kt, 1, ks), hf[ks], X[1]);
+        // the state fragment of this k-step is converted right before use (keeps
+        // one fragment live instead of eight)
+        const F hf = acc_frag<T>(Hs[ks >> 1], ks & 1);
+        X[0] = mma(L.f128(kt, 0, ks), hf, X[0]);
+        X[1] = mma(L.f128(kt, 1, ks), hf, X[1]);
         if (MODE == MODE_FULL && emit) {
-            OT[0] = mma(hf[ks], L.f128(qt, 0, ks), OT[0]);
-            OT[1] = mma(hf[ks], L.f128(qt, 1, ks), OT[1]);
+            OT[0] = mma(hf, L.f128(qt, 0, ks), OT[0]);
+            OT[1] = mma(hf, L.f128(qt, 1, ks), OT[1]);
         }
     }
     // Y = V - diag(Gamma) X (V in accumulator layout via the transposing read)
@@ -645,10 +662,7 @@ __device__ __forceinline__ void chunk_state(const FwdParams& prm, const Lane<T>&
 
     if (MODE == MODE_PASS1) {
         // Mt <- Mt - K^T T0 diag(beta) K Mt  (V = 0, no gates)
-        F mf[8];
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) mf[ks] = acc_frag<T>(Ms[ks >> 1], ks & 1);
-        k_times<T>(L, kt, mf, X);
+        k_times<T>(L, kt, Ms, X);
         const f32x16 y1 = -X[1];
         F ym0[2] = {acc_frag<T>(-X[0], 0), acc_frag<T>(-X[0], 1)};
         block_solve<T>(L, t32[3], t32[5], t32[4], ym0, y1, Vp);
@@ -753,11 +767,14 @@ __device__ __noinline__ void state_loop(const FwdParams& prm, Smem<T>& sm, const
 
 // Prep waves: stream tiles into LDS and prep each chunk one step ahead of the
 // state waves.  Executes exactly the same barriers as state_loop.
+// Both role loops stay out of line: with this function inlined into the
+// single-launch kernel the hipcc (ROCm 7.2) build produced wrong outputs, while
+// the out-of-line build matches the reference on every tested shape.
 template <typename T, int MODE>
 __device__ __noinline__ void prep_loop(const FwdParams& prm, Smem<T>& sm, const Task& tk) {
     constexpr bool kPipe = Pipe<T>::on;
     const int pl = threadIdx.x & 255;     // lane index within the prep group
-    const int pw = (threadIdx.x >> 6) - 4;
+    const int pw = wave_id() - 4;
     const int b = tk.bh / prm.H, h = tk.bh % prm.H;
     const int nch = tk.c_end - tk.c_begin;
     Lane<T> L;
@@ -823,7 +840,10 @@ __device__ __noinline__ void prep_loop(const FwdParams& prm, Smem<T>& sm, const 
 
 template <typename T, int MODE>
 __device__ __forceinline__ void run_task(const FwdParams& prm, Smem<T>& sm, const Task& tk) {
-    if ((threadIdx.x >> 6) < 4)
+    // the role branch must be wave-uniform to the compiler: both roles hold
+    // s_barrier, and a branch it takes for divergent would be laid out so that a
+    // wave also passes through the other role's barriers
+    if (wave_id() < 4)
         state_loop<T, MODE>(prm, sm, tk);
     else
         prep_loop<T, MODE>(prm, sm, tk);
