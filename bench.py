@@ -13,7 +13,9 @@ Prints one JSON line with tokens/s, the roofline of the fused forward kernel
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +34,15 @@ WORKLOAD = "bf16_t32768_h32"
 # and the initial state (64 KiB) read when given.
 BYTES_PER_TOKEN_HEAD = 3 * 256 + 8 + 256
 STATE_BYTES = 128 * 128 * 4
+# measured HBM traffic of the forward kernel (FETCH_SIZE / WRITE_SIZE counter runs,
+# calibrated against a plain streaming copy); valid only for the kernel source it
+# was taken from
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gdn_fwd_kernel_bf16_t32768_h32_traffic.txt")
+KERNEL_SOURCES = ["gated_deltanet_chunked_prefill_amd/csrc/gdn_fwd.hip",
+                  "gated_deltanet_chunked_prefill_amd/csrc/gdn_device.h",
+                  "gated_deltanet_chunked_prefill_amd/csrc/gdn_internal.h"]
+FWD_KERNEL = "gdn_fwd_kernel"
+CALIB_KERNEL = "neg_kernel"
 
 
 def algorithmic_bytes(B, T, H, has_h0, has_ht):
@@ -65,6 +76,66 @@ class HipEvents:
             self.hip.hipEventDestroy(self.arr[i])
 
 
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_counter_csv(path, counter):
+    """Per-kernel-name list of one counter's per-dispatch values (rocprofv3 --pmc csv)."""
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter:
+                out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def traffic_summary(fetch_csv, write_csv, calib_mib):
+    """Per-call HBM bytes of the forward kernel's launches from a FETCH_SIZE and a
+    WRITE_SIZE run (KiB per dispatch), each scaled by the factor that makes the
+    same counter read the known size of the calibration copy."""
+    fetch = read_counter_csv(fetch_csv, "FETCH_SIZE")
+    write = read_counter_csv(write_csv, "WRITE_SIZE")
+    nbytes = calib_mib * 2 ** 20
+
+    def calib(d):
+        vals = [v for name, vs in d.items() if CALIB_KERNEL in name for v in vs]
+        if not vals:
+            raise SystemExit(f"no {CALIB_KERNEL} dispatch in the counter file")
+        return nbytes / (float(np.median(vals)) * 1024.0)
+
+    def per_call(d, factor):
+        # each forward launch kind runs once per call: sum of the per-kind means
+        kinds = {name: float(np.mean(vs)) for name, vs in d.items() if FWD_KERNEL in name}
+        return sum(kinds.values()) * 1024.0 * factor, kinds
+
+    ff, wf = calib(fetch), calib(write)
+    fb, fk = per_call(fetch, ff)
+    wb, wk = per_call(write, wf)
+    return {"source_sha256": kernel_source_hash(), "workload": WORKLOAD,
+            "fetch_factor": ff, "write_factor": wf, "fetch_bytes": fb, "write_bytes": wb,
+            "traffic_bytes": fb + wb, "fetch_kib_per_kind": fk, "write_kib_per_kind": wk,
+            "calib_mib": calib_mib}
+
+
+def load_traffic():
+    """Measured bytes per call, or None when absent or taken from other kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        lines = [ln for ln in f if ln.startswith("{")]
+    if not lines:
+        return None
+    rec = json.loads(lines[-1])
+    if rec.get("source_sha256") != kernel_source_hash() or rec.get("workload") != WORKLOAD:
+        return None
+    return rec
+
+
 def cpu_baseline(x, tokens):
     """The fp64 oracle, as it stands, on the first `tokens` tokens of every head."""
     import oracle
@@ -87,7 +158,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens per head of the CPU oracle sample (0 to skip)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed steps, stream-copy this many MiB three times "
+                         "(the calibration kernel of the HBM counter runs)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: turn two rocprofv3 --pmc counter files (FETCH_SIZE, "
+                         "WRITE_SIZE) into the traffic summary under profiles/")
     args = ap.parse_args()
+    if args.traffic_from:
+        rec = traffic_summary(args.traffic_from[0], args.traffic_from[1], args.calib_copy_mib)
+        print(json.dumps(rec))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this operator runs on one GPU (no sharding or collectives are built); "
@@ -145,6 +226,8 @@ def main():
     fwd_ms = sum(float(np.mean(per_kind[kd])) for kd in fwd_kinds)
     achieved = nbytes / (fwd_ms * 1e-3) / 1e9
     kernel_ms = {kd: round(float(np.mean(t)), 4) for kd, t in per_kind.items()}
+    tr = load_traffic()
+    traffic = None if tr is None else tr["traffic_bytes"]
 
     res = {
         "metric": METRIC,
@@ -163,10 +246,18 @@ def main():
                    "segments_per_head": P, "h0": False, "ht": True},
         "roofline": {"bound": "hbm", "kernel": "gdn_fwd_kernel (" + "+".join(fwd_kinds) + ")",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "algorithmic_bytes": nbytes, "kernel_ms": kernel_ms,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": nbytes,
+                     "traffic_gbs": None if tr is None else traffic / (fwd_ms * 1e-3) / 1e9, "kernel_ms": kernel_ms,
                      "call_frac": nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
     }
+    if args.calib_copy_mib > 0:
+        src = torch.randn(args.calib_copy_mib * 2 ** 18, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if args.cpu_tokens > 0:
         res["cpu_baseline"] = cpu_baseline(x, min(args.cpu_tokens, T))
     print(json.dumps(res), flush=True)
