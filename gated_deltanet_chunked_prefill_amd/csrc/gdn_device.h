@@ -30,7 +30,7 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kChunk = 64;   // tokens per chunk (talk summary, paragraph 3: "usually 64")
+constexpr int kChunk = 64;   // tokens per chunk (talk summary, paragraph 3, gives 64 as the usual length)
 constexpr int kDk = 128;
 constexpr int kDv = 128;
 
