@@ -153,3 +153,81 @@ def window_head(q, k, v, g, beta, h0, bounds, w, C=64, scale=1.0):
         oo, H = chunked_head(q[ws:e], k[ws:e], v[ws:e], g[ws:e], beta[ws:e], Hs, C, scale)
         o[s:e] = oo[s - ws:]
     return o, H
+
+
+def chunk_backward_local(qc, kc, vc, gc, bc, doc, H, dHn, Hn, scale=1.0):
+    """Local gradients of one chunk given its entering state H, the gradient dHn
+    that reaches the chunk's final state from the right, and that final state Hn.
+
+    Forward in gated-matrix form (Sg_rs = Gamma_r / Gamma_s for s <= r):
+      Pm = tril(Q K^T) o Sg (with diagonal), Mg = strict_lower(K K^T) o Sg,
+      T = (I + diag(beta) Mg)^-1, Y = V - diag(Gamma) K H, V' = T diag(beta) Y,
+      O = scale (diag(Gamma) Q H + Pm V'), Hn = Gamma_C H + K^T diag(E) V',
+      E_r = Gamma_C / Gamma_r.
+    Reverse mode of exactly these lines; the gate gradient arrives per position as
+    d(gamma_r) and becomes d(g_t) by a reverse cumulative sum inside the chunk.
+    Returns (dq, dk, dv, dg, dbeta, dH) where dH is the gradient reaching H."""
+    C = kc.shape[0]
+    gam = np.cumsum(gc)
+    Gam = np.exp(gam)
+    GC = Gam[-1]
+    E = np.exp(gam[-1] - gam)
+    Sg = np.tril(np.exp(gam[:, None] - gam[None, :]))
+    Sqk = qc @ kc.T
+    Skk = kc @ kc.T
+    Pm = np.tril(Sqk) * Sg
+    Mg = np.tril(Skk, -1) * Sg
+    T = np.linalg.inv(np.eye(C) + bc[:, None] * Mg)
+    Y = vc - Gam[:, None] * (kc @ H)
+    Z = bc[:, None] * Y
+    Vp = T @ Z
+    # reverse
+    dVp = scale * Pm.T @ doc + E[:, None] * (kc @ dHn)
+    dZ = T.T @ dVp
+    dY = bc[:, None] * dZ
+    dA = -np.tril(dZ @ Vp.T, -1)
+    dMg = bc[:, None] * dA
+    dPm = scale * np.tril(doc @ Vp.T)
+    dPg = dPm * Sg                      # gradient w.r.t. the raw entries of Q K^T
+    dMgg = dMg * Sg                     # gradient w.r.t. the raw entries of K K^T (strict lower)
+    dq2 = scale * Gam[:, None] * (doc @ H.T)
+    dq = dPg @ kc + dq2
+    dk3 = -Gam[:, None] * (dY @ H.T)
+    dk4 = E[:, None] * (Vp @ dHn.T)
+    dk = dPg.T @ qc + (dMgg + dMgg.T) @ kc + dk3 + dk4
+    dv = dY
+    dbeta = np.sum(Y * dZ, axis=1) + np.sum(dA * Mg, axis=1)
+    X = dPm * Pm + dMg * Mg
+    dgam = X.sum(axis=1) - X.sum(axis=0)
+    dgam += np.sum(qc * dq2, axis=1) + np.sum(kc * dk3, axis=1) - np.sum(kc * dk4, axis=1)
+    dgam[-1] += np.sum(dHn * Hn)
+    dg = np.cumsum(dgam[::-1])[::-1]
+    dH = scale * qc.T @ (Gam[:, None] * doc) + GC * dHn - kc.T @ (Gam[:, None] * dY)
+    return dq, dk, dv, dg, dbeta, dH
+
+
+def chunked_backward_head(q, k, v, g, beta, h0, dout, dht=None, C=64, scale=1.0):
+    """Backward of one head in three sweeps: the chunk-entry states forward, the
+    state gradient backward over chunks, then every chunk's local gradients from
+    its entering state and the gradient reaching its end."""
+    T = q.shape[0]
+    starts = list(range(0, T, C))
+    Hs = [h0.copy()]
+    for s in starts:
+        e = min(s + C, T)
+        _, Hn = chunk_step(q[s:e], k[s:e], v[s:e], g[s:e], beta[s:e], Hs[-1], scale)
+        Hs.append(Hn)
+    dHs = [None] * (len(starts) + 1)
+    dHs[-1] = np.zeros_like(h0) if dht is None else dht.copy()
+    out = {n: np.zeros_like(a) for n, a in (("dq", q), ("dk", k), ("dv", v), ("dg", g),
+                                            ("dbeta", beta))}
+    for i in range(len(starts) - 1, -1, -1):
+        s = starts[i]
+        e = min(s + C, T)
+        dq, dk, dv, dg, db, dH = chunk_backward_local(q[s:e], k[s:e], v[s:e], g[s:e], beta[s:e],
+                                                      dout[s:e], Hs[i], dHs[i + 1], Hs[i + 1], scale)
+        out["dq"][s:e], out["dk"][s:e], out["dv"][s:e] = dq, dk, dv
+        out["dg"][s:e], out["dbeta"][s:e] = dg, db
+        dHs[i] = dH
+    out["dh0"] = dHs[0]
+    return out

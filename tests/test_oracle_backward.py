@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import oracle
+import mirrors
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -124,3 +125,33 @@ def test_beta_zero_no_key_value_gradient():
     gr = oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], dout, h0=x["h0"], dht=dht)
     assert np.all(gr["dk"] == 0) and np.all(gr["dv"] == 0)
     assert np.max(np.abs(gr["dbeta"])) > 1e-3
+
+
+@pytest.mark.parametrize("C", [64, 16, 7])
+def test_chunked_backward_mirror_matches_oracle(C):
+    """The chunk-wise backward (entry states forward, state gradient backward over
+    chunks, local gradients per chunk with the gate gradient as a reverse
+    cumulative sum) reaches the token-by-token BPTT gradients (talk summary,
+    paragraph 3: the four chunk steps; paragraph 6: the K K^T gradient bundled as
+    (dA + dA^T) K)."""
+    rng = np.random.default_rng(11)
+    B, T, H, dk, dv = 1, 150, 2, 16, 12
+    q = rng.standard_normal((B, T, H, dk))
+    k = rng.standard_normal((B, T, H, dk))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, dv))
+    g = -rng.uniform(0.01, 0.5, (B, T, H))
+    beta = rng.uniform(0.0, 1.0, (B, T, H))
+    h0 = rng.standard_normal((B, H, dk, dv))
+    do = rng.standard_normal((B, T, H, dv))
+    dht = rng.standard_normal((B, H, dk, dv))
+    ref = oracle.bwd(q, k, v, g, beta, do, h0, dht, scale=0.7)
+    for h in range(H):
+        m = mirrors.chunked_backward_head(q[0, :, h], k[0, :, h], v[0, :, h], g[0, :, h],
+                                          beta[0, :, h], h0[0, h], do[0, :, h], dht[0, h],
+                                          C=C, scale=0.7)
+        for name in ("dq", "dk", "dv", "dg", "dbeta"):
+            r = ref[name][0, :, h]
+            assert np.abs(m[name] - r).max() <= 1e-10 * np.abs(r).max(), name
+        assert np.abs(m["dh0"] - ref["dh0"][0, h]).max() <= 1e-10 * np.abs(ref["dh0"][0, h]).max()
