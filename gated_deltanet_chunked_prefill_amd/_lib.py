@@ -26,7 +26,7 @@ EXPORTS = ("gdn_default_options", "gdn_plan_segments", "gdn_chunk_fwd_workspace_
            "gdn_last_error")
 
 LAUNCH_KINDS = {0: "gate_sums", 1: "gate_flags", 2: "fwd_single", 3: "fwd_pass_a",
-                4: "combine", 5: "fwd_pass_c", 6: "bwd_states", 7: "bwd"}
+                4: "combine", 5: "fwd_pass_c", 6: "bwd_states", 7: "bwd_dh", 8: "bwd_local"}
 
 
 class Options(ctypes.Structure):

@@ -130,6 +130,20 @@ FwdLayout fwd_layout(int B, int T, int H, int P) {
     return L;
 }
 
+struct BwdLayout {
+    size_t hstore, dhstore, total;
+};
+
+BwdLayout bwd_layout(int B, int T, int H) {
+    BwdLayout L{};
+    const size_t N = num_chunks(T), bh = (size_t)B * H, SS = 128 * 128;
+    size_t off = 0;
+    L.hstore = off;  off += align_up(bh * (N + 1) * SS * sizeof(float));
+    L.dhstore = off; off += align_up(bh * N * SS * sizeof(float));
+    L.total = off;
+    return L;
+}
+
 gdn_status device_cus(int* cus) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -291,7 +305,7 @@ gdn_status gdn_gate_scan(const float* g, int B, int T, int H, int window_chunks,
 
 size_t gdn_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, gdn_dtype dtype) {
     if (check_shapes(B, T, H, dk, dv, dtype) != GDN_OK) return (size_t)-1;
-    return align_up((size_t)B * H * num_chunks(T) * 128 * 128 * sizeof(float));
+    return bwd_layout(B, T, H).total;
 }
 
 gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
@@ -300,12 +314,54 @@ gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const floa
                          float* grad_beta, float* grad_h0, int B, int T, int H, int dk, int dv,
                          gdn_dtype dtype, float scale, void* workspace, size_t workspace_bytes,
                          void* stream) {
-    (void)q; (void)k; (void)v; (void)g; (void)beta; (void)h0; (void)dout; (void)dht;
-    (void)grad_q; (void)grad_k; (void)grad_v; (void)grad_g; (void)grad_beta; (void)grad_h0;
-    (void)B; (void)T; (void)H; (void)dk; (void)dv; (void)dtype; (void)scale; (void)workspace;
-    (void)workspace_bytes; (void)stream;
     g_err[0] = 0;
-    return fail(GDN_ERR_UNSUPPORTED, "backward not built yet");
+    if (!q || !k || !v || !g || !beta || !dout || !grad_q || !grad_k || !grad_v || !grad_g || !grad_beta)
+        return fail(GDN_ERR_INVALID_ARG,
+                    "q, k, v, g, beta, dout, grad_q, grad_k, grad_v, grad_g and grad_beta are required");
+    gdn_status st = check_shapes(B, T, H, dk, dv, dtype);
+    if (st != GDN_OK) return st;
+    if (dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "the backward supports bf16 I/O only");
+    const void* vec_ptrs[] = {q, k, v, dout, grad_q, grad_k, grad_v};
+    for (const void* p : vec_ptrs)
+        if (!aligned16(p))
+            return fail(GDN_ERR_INVALID_ARG, "q, k, v, dout and their gradients must be 16-byte aligned");
+    const void* f32_ptrs[] = {g, beta, h0, dht, grad_g, grad_beta, grad_h0};
+    for (const void* p : f32_ptrs)
+        if (p && !aligned4(p))
+            return fail(GDN_ERR_INVALID_ARG, "float32 tensors must be 4-byte aligned");
+    if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite");
+    const BwdLayout L = bwd_layout(B, T, H);
+    if (!workspace) return fail(GDN_ERR_WORKSPACE, "a workspace of %zu bytes is required", L.total);
+    if (workspace_bytes < L.total)
+        return fail(GDN_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
+    if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+        return fail(GDN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+    hipStream_t s = (hipStream_t)stream;
+    const int N = num_chunks(T);
+    char* ws = (char*)workspace;
+    float* hstore = (float*)(ws + L.hstore);
+    float* dhstore = (float*)(ws + L.dhstore);
+    // 1. the state entering every chunk (the forward kernel, no outputs)
+    gdn::FwdParams f{};
+    f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.h0 = h0; f.o = nullptr; f.ht = nullptr;
+    f.B = B; f.T = T; f.H = H; f.N = N; f.P = 1; f.w = 1; f.scale = scale;
+    f.hstore = hstore;
+    hipError_t e = recorded(GDN_LAUNCH_BWD_STATES, s, [&] { return gdn::launch_fwd(f, gdn::PHASE_SINGLE, true, s); });
+    if (e != hipSuccess) return hip_fail(e, "backward state launch");
+    gdn::BwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.dout = dout; p.dht = dht;
+    p.dq = grad_q; p.dk = grad_k; p.dv = grad_v; p.dg = grad_g; p.dbeta = grad_beta; p.dh0 = grad_h0;
+    p.B = B; p.T = T; p.H = H; p.N = N; p.scale = scale;
+    p.hstore = hstore;
+    p.dhstore = dhstore;
+    // 2. the state gradient, end to start
+    e = recorded(GDN_LAUNCH_BWD_DH, s, [&] { return gdn::launch_bwd_dh(p, true, s); });
+    if (e != hipSuccess) return hip_fail(e, "backward state-gradient launch");
+    // 3. local gradients of every chunk
+    e = recorded(GDN_LAUNCH_BWD_LOCAL, s, [&] { return gdn::launch_bwd_local(p, true, s); });
+    if (e != hipSuccess) return hip_fail(e, "backward local-gradient launch");
+    return GDN_OK;
 }
 
 }  // extern "C"

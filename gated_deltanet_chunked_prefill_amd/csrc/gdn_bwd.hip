@@ -1,0 +1,668 @@
+// Chunked backward of the gated delta rule for gfx950.
+//
+// Three launches (the first is the forward kernel storing the state entering
+// every chunk, see gdn_fwd.hip):
+//
+//   1. state gradient sweep, one workgroup per head, chunks in reverse order.
+//      With dHn the gradient reaching the end of chunk c, the chunk's state step
+//      H' = Gamma_C H + K^T diag(E) V' (E_r = Gamma_C / Gamma_r) and output
+//      O = scale (diag(Gamma) Q H + P V') give the gradient reaching its start:
+//        dV' = scale P^T dO + diag(E) K dHn
+//        dY  = Tt^T dV'        (Tt = T diag(beta), transposed block substitution:
+//                               dY_1 = Tt_11^T dV'_1, dY_0 = Tt_00^T (dV'_0 - Ah_10^T dY_1))
+//        dH  = Gamma_C dHn + scale Q^T diag(Gamma) dO - K^T diag(Gamma) dY
+//      The chunk prep (gate scan, inverse blocks, masked Q K^T blocks) is the
+//      forward's, run by four prep waves one chunk ahead of the four waves that
+//      carry dH in MFMA accumulators.  dHn of every chunk is stored for launch 2.
+//
+//   2. local gradients, one workgroup per (head, chunk), all chunks at once.
+//      From the chunk's entering state H, its final state Hn and dHn it recomputes
+//      the chunk's forward in gated-matrix form (Sg_rs = Gamma_r / Gamma_s, s <= r;
+//      Pm = tril(Q K^T) o Sg, Mg = strict_lower(K K^T) o Sg, T = (I + diag(beta) Mg)^-1,
+//      Y = V - diag(Gamma) K H, V' = T diag(beta) Y) and runs reverse mode:
+//        dY, dZ as above (dZ = dY / beta before the beta scaling)
+//        dPm = scale tril(dO V'^T),  dMg = -strict_lower(dY V'^T)
+//        dq  = (dPm o Sg) K + scale diag(Gamma) dO H^T
+//        dk  = (dPm o Sg)^T Q + (dMg o Sg + (dMg o Sg)^T) K - diag(Gamma) dY H^T
+//              + diag(E) V' dHn^T
+//        dv  = dY
+//        dbeta_r = dZ_r . (Y - Mg V')_r
+//        dgamma_r = sum_s X_rs - sum_s X_sr + q_r . dq2_r + k_r . dk3_r - k_r . dk4_r
+//                   (+ <dHn, Hn> for the last position),  X = dPm o Pm + dMg o Mg,
+//        dg = reverse cumulative sum of dgamma inside the chunk.
+//      The K K^T gradient is bundled as (dA + dA^T) K (FlashQLA talk summary,
+//      onedev.kr, paragraph 6); the four chunk steps being inverted are those of
+//      paragraph 3.  Exponentials of gamma differences are taken pairwise here
+//      (each Sg entry is at most 1), which keeps every factor bounded.
+#include "gdn_chunk.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kDhThreads = 512;     // 4 gradient waves + 4 prep waves
+// The reverse sweep runs prep and gradient step back to back (three barriers per
+// chunk).  Its pipelined schedule (prep one chunk ahead, as in the forward) gave
+// run-to-run different state gradients from the second chunk on, and is off.
+constexpr bool kDhPipelined = false;
+constexpr int kLocalThreads = 256;  // 4 waves
+
+// ---------------------------------------------------------------------------
+// Launch 1: reverse sweep of the state gradient.
+
+// One chunk for gradient wave w (its 32 dv columns of dH).
+template <typename T>
+__device__ __forceinline__ void dh_chunk_step(const Lane<T>& L, const T* kt, const T* qt, const T* dot,
+                                              const T (*t32)[kT32], const float* gam_vec,
+                                              const float* e_vec, float GC, float scale, f32x16* dH) {
+    using F = typename FragOf<T>::type;
+    const int g = L.g, lane = L.lane;
+    f32x16 X[2];
+    k_times<T>(L, kt, dH, X);   // K dHn
+    // P^T dO: (P^T)_00 = P_00^T, (P^T)_01 = P_10^T, (P^T)_11 = P_11^T
+    f32x16 pd0 = zero16(), pd1 = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const F d_lo = L.trV(dot, ks), d_hi = L.trV(dot, 2 + ks);
+        pd0 = mma(tfrag<T, 32>(t32[3], 0, ks, lane), d_lo, pd0);
+        pd0 = mma(tfrag<T, 32>(t32[4], 0, ks, lane), d_hi, pd0);
+        pd1 = mma(tfrag<T, 32>(t32[5], 0, ks, lane), d_hi, pd1);
+    }
+    const f32x16 e0 = rows_of(e_vec, 0, g), e1 = rows_of(e_vec, 1, g);
+    f32x16 dvp0, dvp1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        dvp0[r] = scale * pd0[r] + e0[r] * X[0][r];
+        dvp1[r] = scale * pd1[r] + e1[r] * X[1][r];
+    }
+    // transposed block substitution through Tt = T diag(beta)
+    f32x16 dy1 = zero16();
+    dy1 = mma(tfrag<T, 32>(t32[1], 0, 0, lane), acc_frag<T>(dvp1, 0), dy1);
+    dy1 = mma(tfrag<T, 32>(t32[1], 0, 1, lane), acc_frag<T>(dvp1, 1), dy1);
+    f32x16 z0 = dvp0;   // + (-Ah_10)^T dY_1
+    z0 = mma(tfrag<T, 32>(t32[2], 0, 0, lane), acc_frag<T>(dy1, 0), z0);
+    z0 = mma(tfrag<T, 32>(t32[2], 0, 1, lane), acc_frag<T>(dy1, 1), z0);
+    f32x16 dy0 = zero16();
+    dy0 = mma(tfrag<T, 32>(t32[0], 0, 0, lane), acc_frag<T>(z0, 0), dy0);
+    dy0 = mma(tfrag<T, 32>(t32[0], 0, 1, lane), acc_frag<T>(z0, 1), dy0);
+    // dH <- Gamma_C dH - K^T diag(Gamma) dY + scale Q^T diag(Gamma) dO
+    F bk[4], bq[4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const f32x16 gr = rows_of(gam_vec, rt, g);
+        const f32x16& dy = rt ? dy1 : dy0;
+        const F d0 = L.trV(dot, 2 * rt), d1 = L.trV(dot, 2 * rt + 1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            bk[2 * rt][j] = (T)(-gr[j] * dy[j]);
+            bk[2 * rt + 1][j] = (T)(-gr[8 + j] * dy[8 + j]);
+            bq[2 * rt][j] = (T)(scale * gr[j] * (float)d0[j]);
+            bq[2 * rt + 1][j] = (T)(scale * gr[8 + j] * (float)d1[j]);
+        }
+    }
+    kt_update<T>(L, kt, dH, GC, bk);
+    kt_update<T>(L, qt, dH, 1.f, bq);
+}
+
+// Gradient waves: carry dH from the end of the sequence to its start.  Executes
+// exactly the same barriers as dh_prep_loop.
+template <typename T>
+__device__ __noinline__ void dh_state_loop(const BwdParams& prm, Smem<T>& sm, int bh) {
+    constexpr bool kPipe = kDhPipelined;
+    const size_t SS = (size_t)kDk * kDv;
+    const int N = prm.N;
+    const float scale = prm.scale;
+    float* const dst = prm.dhstore + (size_t)bh * N * SS;
+    Lane<T> L;
+    L.init(threadIdx.x);
+    f32x16 dH[4];
+    if (prm.dht) {
+        load_state(prm.dht + (size_t)bh * SS, L.w, L.lane, dH);
+    } else {
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) dH[ht] = zero16();
+    }
+    if constexpr (kPipe) {
+        lds_barrier();
+        lds_barrier();
+        for (int i = 0; i < N; ++i) {
+            const int c = N - 1 - i;
+            const int slot = i % 3, vb = i & 1;
+            store_state(dst + (size_t)c * SS, L.w, L.lane, dH);
+            dh_chunk_step<T>(L, sm.kt[slot], sm.qt[slot], sm.vt[vb], sm.t32[vb], sm.gam_vec[vb],
+                             sm.e_vec[vb], sm.gc[vb][0], scale, dH);
+            lds_barrier();
+        }
+    } else {
+        for (int i = 0; i < N; ++i) {
+            const int c = N - 1 - i;
+            lds_barrier();
+            lds_barrier();
+            lds_barrier();
+            store_state(dst + (size_t)c * SS, L.w, L.lane, dH);
+            dh_chunk_step<T>(L, sm.kt[0], sm.qt[0], sm.vt[0], sm.t32[0], sm.gam_vec[0], sm.e_vec[0],
+                             sm.gc[0][0], scale, dH);
+        }
+    }
+    if (prm.dh0) store_state(prm.dh0 + (size_t)bh * SS, L.w, L.lane, dH);
+}
+
+// Prep waves: stream K, Q, dO of the chunks in reverse order and prep each one a
+// step ahead of the gradient waves.  Executes exactly the same barriers as
+// dh_state_loop.
+template <typename T>
+__device__ __noinline__ void dh_prep_loop(const BwdParams& prm, Smem<T>& sm, int bh) {
+    constexpr bool kPipe = kDhPipelined;
+    const int pl = threadIdx.x & 255;
+    const int pw = wave_id() - 4;
+    const int H = prm.H, Tn = prm.T, N = prm.N;
+    const int b = bh / H, h = bh % H;
+    const T* const q = (const T*)prm.q;
+    const T* const k = (const T*)prm.k;
+    const T* const dout = (const T*)prm.dout;
+    const float* const gp = prm.g;
+    const float* const bp = prm.beta;
+    Lane<T> L;
+    L.init(threadIdx.x);
+    float gsum = 0.f;
+    float g_cur = 0.f, b_cur = 0.f, g_nxt = 0.f, b_nxt = 0.f;
+    auto cidx = [&](int i) { return N - 1 - i; };
+    auto load_kq = [&](int c, int slot) {
+        const int t0 = c * kChunk, nv = chunk_len(Tn, c);
+        load_tile<T>(sm.kt[slot], k, b, h, Tn, H, t0, nv, pl);
+        load_tile<T>(sm.qt[slot], q, b, h, Tn, H, t0, nv, pl);
+    };
+    auto load_do = [&](int c, int slot) {
+        load_tile<T>(sm.vt[slot], dout, b, h, Tn, H, c * kChunk, chunk_len(Tn, c), pl);
+    };
+    if constexpr (kPipe) {
+        load_kq(cidx(0), 0);
+        load_do(cidx(0), 0);
+        if (N > 1) load_kq(cidx(1), 1);
+        load_gate_beta(gp, bp, Tn, H, b, h, cidx(0), L.lane, g_cur, b_cur);
+        if (N > 1) load_gate_beta(gp, bp, Tn, H, b, h, cidx(1), L.lane, g_nxt, b_nxt);
+        wait_vm();
+        lds_barrier();
+        chunk_prep<T, MODE_FULL>(sm, L, pw, sm.kt[0], sm.qt[0], sm.t32[0], sm.gam_vec[0], sm.e_vec[0],
+                                 sm.gc[0], g_cur, b_cur, true, gsum);
+        g_cur = g_nxt;
+        b_cur = b_nxt;
+        lds_barrier();
+        for (int i = 0; i < N; ++i) {
+            if (i + 1 < N) {
+                if (i + 2 < N) {
+                    load_kq(cidx(i + 2), (i + 2) % 3);
+                    load_gate_beta(gp, bp, Tn, H, b, h, cidx(i + 2), L.lane, g_nxt, b_nxt);
+                }
+                load_do(cidx(i + 1), (i + 1) & 1);
+                const int slot = (i + 1) % 3, pb = (i + 1) & 1;
+                chunk_prep<T, MODE_FULL>(sm, L, pw, sm.kt[slot], sm.qt[slot], sm.t32[pb],
+                                         sm.gam_vec[pb], sm.e_vec[pb], sm.gc[pb], g_cur, b_cur, true,
+                                         gsum);
+                g_cur = g_nxt;
+                b_cur = b_nxt;
+                wait_vm();
+            }
+            lds_barrier();
+        }
+    } else {
+        for (int i = 0; i < N; ++i) {
+            const int c = cidx(i);
+            lds_barrier();
+            load_kq(c, 0);
+            load_do(c, 0);
+            load_gate_beta(gp, bp, Tn, H, b, h, c, L.lane, g_cur, b_cur);
+            wait_vm();
+            lds_barrier();
+            chunk_prep<T, MODE_FULL>(sm, L, pw, sm.kt[0], sm.qt[0], sm.t32[0], sm.gam_vec[0],
+                                     sm.e_vec[0], sm.gc[0], g_cur, b_cur, true, gsum);
+            lds_barrier();
+        }
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kDhThreads, 1) void gdn_bwd_dh_kernel(BwdParams prm) {
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    Smem<T>& sm = *reinterpret_cast<Smem<T>*>(smem_raw);
+    const int bh = blockIdx.x;
+    // wave-uniform role branch: both roles hold barriers
+    if (wave_id() < 4)
+        dh_state_loop<T>(prm, sm, bh);
+    else
+        dh_prep_loop<T>(prm, sm, bh);
+}
+
+// ---------------------------------------------------------------------------
+// Launch 2: local gradients of every chunk.
+
+constexpr int kT64 = 64 * 64;
+
+template <typename T>
+struct LocalSmem {
+    T qt[kChunk * kDk];     // 64 x 128 tiles (swizzled row-major, as in the forward)
+    T kt[kChunk * kDk];
+    T vt[kChunk * kDv];     // V, then V'
+    T dot[kChunk * kDv];    // dO
+    T dyt[kChunk * kDv];    // dY
+    T pm[kT64];             // 64 x 64 tiles (toff<T, 64> layout)
+    T mg[kT64];
+    T tg[kT64];             // diagonal blocks of the gated inverse T (beta-free)
+    T dpg[kT64];            // dPm o Sg
+    T dmg[kT64];            // dMg o Sg
+    float xs[kChunk][kChunk + 1];   // X = dPm o Pm + dMg o Mg
+    float gam[kChunk];
+    float Gam[kChunk];
+    float E[kChunk];
+    float beta[kChunk];
+    float part[4][4][kChunk];       // per wave: dbeta, q.dq2, k.dk3, k.dk4 partial row sums
+    float red[4];
+};
+
+// B fragment of a 128 x 128 float32 state in HBM, contraction over its rows:
+// lane (n, g) gets S[kappa(ks, g, j)][col].
+template <typename T>
+__device__ __forceinline__ typename FragOf<T>::type state_colfrag(const float* S, int ks, int g, int col) {
+    typename FragOf<T>::type f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = (T)S[(16 * ks + 8 * (j >> 2) + 4 * g + (j & 3)) * kDv + col];
+    return f;
+}
+// B fragment of the transposed state (contraction over its columns): lane (n, g)
+// gets S[row][kappa(ks, g, j)].
+template <typename T>
+__device__ __forceinline__ typename FragOf<T>::type state_rowfrag(const float* S, int row, int ks, int g) {
+    const f32x4 lo = *(const f32x4*)(S + (size_t)row * kDv + 16 * ks + 4 * g);
+    const f32x4 hi = *(const f32x4*)(S + (size_t)row * kDv + 16 * ks + 8 + 4 * g);
+    typename FragOf<T>::type f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[j] = (T)lo[j];
+        f[4 + j] = (T)hi[j];
+    }
+    return f;
+}
+
+// Sum of each accumulator row over the 32 lanes of its half-wave; lane n == 0 of
+// each half writes dst[32 rt + rho(g, r)].
+__device__ __forceinline__ void row_sums(float* dst, f32x16 v, int rt, int g, int n) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float x = v[r];
+#pragma unroll
+        for (int d = 1; d < 32; d <<= 1) x += __shfl_xor(x, d, 64);
+        v[r] = x;
+    }
+    if (n == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dst[32 * rt + rho(g, r)] = v[r];
+    }
+}
+
+// Store an accumulator tile (rows 32 ti + rho, column 32 tj + n) into a 64 x 64 tile.
+template <typename T>
+__device__ __forceinline__ void st_tile64(T* tile, const f32x16& v, int ti, int tj, int g, int n) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tile[toff<T, 64>(32 * ti + rho(g, r), 32 * tj + n)] = (T)v[r];
+}
+
+// Store accumulator tile rt of a 64 x 128 result (this wave's 32 columns) to HBM rows.
+template <typename T>
+__device__ __forceinline__ void st_rows_hbm(T* dst, const f32x16& v, int rt, int g, int n, int w, int H,
+                                           int nvalid) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = 32 * rt + rho(g, r);
+        if (row < nvalid) dst[(size_t)row * H * kDk + 32 * w + n] = (T)v[r];
+    }
+}
+// ... and into a swizzled 64 x 128 LDS tile.
+template <typename T>
+__device__ __forceinline__ void st_rows_lds(T* tile, const f32x16& v, int rt, int g, int n, int w) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tile[toff<T, kDv>(32 * rt + rho(g, r), 32 * w + n)] = (T)v[r];
+}
+
+template <typename T>
+__global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_kernel(BwdParams prm) {
+    using F = typename FragOf<T>::type;
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    LocalSmem<T>& sm = *reinterpret_cast<LocalSmem<T>*>(smem_raw);
+    const int H = prm.H, Tn = prm.T, N = prm.N;
+    const int bh = blockIdx.x / N, c = blockIdx.x % N;
+    const int b = bh / H, h = bh % H;
+    const int t0 = c * kChunk, nv = chunk_len(Tn, c);
+    const int tid = threadIdx.x;
+    const int w = wave_id();
+    Lane<T> L;
+    L.init(tid);
+    const int lane = L.lane, n = L.n, g = L.g;
+    const float scale = prm.scale;
+    const size_t SS = (size_t)kDk * kDv;
+    const float* const Hc = prm.hstore + ((size_t)bh * (N + 1) + c) * SS;
+    const float* const Hn = Hc + SS;
+    const float* const dHn = prm.dhstore + ((size_t)bh * N + c) * SS;
+
+    // ---- phase 0: tiles, gates
+    load_tile<T>(sm.qt, (const T*)prm.q, b, h, Tn, H, t0, nv, tid);
+    load_tile<T>(sm.kt, (const T*)prm.k, b, h, Tn, H, t0, nv, tid);
+    load_tile<T>(sm.vt, (const T*)prm.v, b, h, Tn, H, t0, nv, tid);
+    load_tile<T>(sm.dot, (const T*)prm.dout, b, h, Tn, H, t0, nv, tid);
+    if (w == 0) {
+        float gv, bv;
+        load_gate_beta(prm.g, prm.beta, Tn, H, b, h, c, lane, gv, bv);
+        const float gam = wave_inclusive_scan(gv);
+        const float gC = __shfl(gam, 63, 64);
+        sm.gam[lane] = gam;
+        sm.Gam[lane] = __expf(gam);
+        sm.E[lane] = __expf(gC - gam);
+        sm.beta[lane] = bv;
+    }
+    wait_vm();
+    lds_barrier();
+
+    // ---- phase 1: 64 x 64 tile (ti, tj) of the score matrices
+    const int ti = w >> 1, tj = w & 1;
+    f32x16 Pm = zero16(), Mg = zero16(), SG = zero16();
+    if (ti >= tj) {
+        f32x16 sqk = zero16(), skk = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const F kf = L.f128(sm.kt, tj, ks);
+            sqk = mma(L.f128(sm.qt, ti, ks), kf, sqk);
+            skk = mma(L.f128(sm.kt, ti, ks), kf, skk);
+        }
+        const f32x16 gr = rows_of(sm.gam, ti, g);
+        const float gs = sm.gam[32 * tj + n];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int R = 32 * ti + rho(g, r), S = 32 * tj + n;
+            const float sg = R >= S ? __expf(gr[r] - gs) : 0.f;
+            SG[r] = sg;
+            Pm[r] = sqk[r] * sg;
+            Mg[r] = R > S ? skk[r] * sg : 0.f;
+        }
+        if (ti == tj) {
+            // diagonal block p: T_pp = diag(Gamma) T0_pp diag(1/Gamma), T0_pp gate-free
+            const int p = ti;
+            const f32x16 brow = rows_of(sm.beta, p, g);
+            const f32x16 zt = diag_inverse_t<T>(skk, brow, sm.beta[32 * p + n], n, g);
+            // zt = acc(T0_pp^T): lane n holds row 32p + n, registers columns 32p + rho
+            const float gn = sm.gam[32 * p + n];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int col = rho(g, r);
+                const float t = col <= n ? zt[r] * __expf(gn - gr[r]) : 0.f;
+                sm.tg[toff<T, 64>(32 * p + n, 32 * p + col)] = (T)t;
+            }
+        }
+    }
+    st_tile64<T>(sm.pm, Pm, ti, tj, g, n);
+    st_tile64<T>(sm.mg, Mg, ti, tj, g, n);
+    lds_barrier();
+
+    // ---- phase 2: this wave's 32 dv columns of Y, V', dV', dY
+    f32x16 Y[2], Vp[2], dZ[2], dY[2];
+    {
+        f32x16 KH[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const F hf = state_colfrag<T>(Hc, ks, g, 32 * w + n);
+            KH[0] = mma(L.f128(sm.kt, 0, ks), hf, KH[0]);
+            KH[1] = mma(L.f128(sm.kt, 1, ks), hf, KH[1]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const F v0 = L.trV(sm.vt, 2 * rt), v1 = L.trV(sm.vt, 2 * rt + 1);
+            const f32x16 G = rows_of(sm.Gam, rt, g);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                Y[rt][j] = (float)v0[j] - G[j] * KH[rt][j];
+                Y[rt][8 + j] = (float)v1[j] - G[8 + j] * KH[rt][8 + j];
+            }
+        }
+    }
+    const f32x16 be0 = rows_of(sm.beta, 0, g), be1 = rows_of(sm.beta, 1, g);
+    f32x16 MgV0 = zero16(), MgV1 = zero16();
+    {
+        // V'_0 = T_00 diag(beta_0) Y_0 ; V'_1 = T_11 diag(beta_1) (Y_1 - Mg_10 V'_0)
+        const f32x16 z0 = Y[0] * be0;
+        Vp[0] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) Vp[0] = mma(afrag<T, 64>(sm.tg, n, ks, g), acc_frag<T>(z0, ks), Vp[0]);
+        f32x16 w10 = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const F vf = acc_frag<T>(Vp[0], ks);
+            w10 = mma(afrag<T, 64>(sm.mg, 32 + n, ks, g), vf, w10);
+            MgV0 = mma(afrag<T, 64>(sm.mg, n, ks, g), vf, MgV0);
+        }
+        const f32x16 z1 = (Y[1] - w10) * be1;
+        Vp[1] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            Vp[1] = mma(afrag<T, 64>(sm.tg, 32 + n, 2 + ks, g), acc_frag<T>(z1, ks), Vp[1]);
+        MgV1 = w10;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            MgV1 = mma(afrag<T, 64>(sm.mg, 32 + n, 2 + ks, g), acc_frag<T>(Vp[1], ks), MgV1);
+    }
+    {
+        // dV' = scale Pm^T dO + diag(E) K dHn
+        f32x16 KdH[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const F hf = state_colfrag<T>(dHn, ks, g, 32 * w + n);
+            KdH[0] = mma(L.f128(sm.kt, 0, ks), hf, KdH[0]);
+            KdH[1] = mma(L.f128(sm.kt, 1, ks), hf, KdH[1]);
+        }
+        f32x16 PdO[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const F df = L.trV(sm.dot, ks);
+            PdO[0] = mma(tfrag<T, 64>(sm.pm, 0, ks, lane), df, PdO[0]);
+            if (ks >= 2) PdO[1] = mma(tfrag<T, 64>(sm.pm, 32, ks, lane), df, PdO[1]);
+        }
+        f32x16 dVp[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const f32x16 e = rows_of(sm.E, rt, g);
+            dVp[rt] = PdO[rt] * scale + e * KdH[rt];
+        }
+        // dZ_1 = T_11^T dV'_1 ; dZ_0 = T_00^T (dV'_0 - Mg_10^T diag(beta_1) dZ_1)
+        dZ[1] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            dZ[1] = mma(tfrag<T, 64>(sm.tg, 32, 2 + ks, lane), acc_frag<T>(dVp[1], ks), dZ[1]);
+        dY[1] = dZ[1] * be1;
+        f32x16 u = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) u = mma(tfrag<T, 64>(sm.mg, 0, 2 + ks, lane), acc_frag<T>(dY[1], ks), u);
+        const f32x16 t0v = dVp[0] - u;
+        dZ[0] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) dZ[0] = mma(tfrag<T, 64>(sm.tg, 0, ks, lane), acc_frag<T>(t0v, ks), dZ[0]);
+        dY[0] = dZ[0] * be0;
+    }
+    // dbeta partial over this wave's columns; V' and dY to LDS; dv to HBM
+    {
+        const f32x16 r0 = dZ[0] * (Y[0] - MgV0), r1 = dZ[1] * (Y[1] - MgV1);
+        row_sums(sm.part[w][0], r0, 0, g, n);
+        row_sums(sm.part[w][0], r1, 1, g, n);
+        T* dvout = (T*)prm.dv + (((size_t)b * Tn + t0) * H + h) * kDv;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            st_rows_lds<T>(sm.vt, Vp[rt], rt, g, n, w);
+            st_rows_lds<T>(sm.dyt, dY[rt], rt, g, n, w);
+            st_rows_hbm<T>(dvout, dY[rt], rt, g, n, w, H, nv);
+        }
+    }
+    lds_barrier();
+
+    // ---- phase 3: 64 x 64 gradient tiles
+    {
+        f32x16 dPm = zero16(), dMg = zero16();
+        if (ti >= tj) {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const F vf = L.f128(sm.vt, tj, ks);
+                dPm = mma(L.f128(sm.dot, ti, ks), vf, dPm);
+                dMg = mma(L.f128(sm.dyt, ti, ks), vf, dMg);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int R = 32 * ti + rho(g, r), S = 32 * tj + n;
+                dPm[r] = R >= S ? scale * dPm[r] : 0.f;
+                dMg[r] = R > S ? -dMg[r] : 0.f;
+            }
+        }
+        const f32x16 X = dPm * Pm + dMg * Mg;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm.xs[32 * ti + rho(g, r)][32 * tj + n] = X[r];
+        st_tile64<T>(sm.dpg, dPm * SG, ti, tj, g, n);
+        st_tile64<T>(sm.dmg, dMg * SG, ti, tj, g, n);
+    }
+    lds_barrier();
+
+    // ---- phase 4: this wave's 32 dk columns of dq and dk
+    {
+        f32x16 dq[2], dk[2];
+        f32x16 a2[2] = {zero16(), zero16()}, a3[2] = {zero16(), zero16()}, a4[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const F hr = state_rowfrag<T>(Hc, 32 * w + n, ks, g);
+            const F dr = state_rowfrag<T>(dHn, 32 * w + n, ks, g);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                a2[rt] = mma(L.f128(sm.dot, rt, ks), hr, a2[rt]);
+                a3[rt] = mma(L.f128(sm.dyt, rt, ks), hr, a3[rt]);
+                a4[rt] = mma(L.f128(sm.vt, rt, ks), dr, a4[rt]);
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            dq[rt] = zero16();
+            dk[rt] = zero16();
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const F kf = L.trK(sm.kt, w, ks);
+                const F qf = L.trK(sm.qt, w, ks);
+                dq[rt] = mma(afrag<T, 64>(sm.dpg, 32 * rt + n, ks, g), kf, dq[rt]);
+                dk[rt] = mma(tfrag<T, 64>(sm.dpg, 32 * rt, ks, lane), qf, dk[rt]);
+                dk[rt] = mma(afrag<T, 64>(sm.dmg, 32 * rt + n, ks, g), kf, dk[rt]);
+                dk[rt] = mma(tfrag<T, 64>(sm.dmg, 32 * rt, ks, lane), kf, dk[rt]);
+            }
+            const f32x16 G = rows_of(sm.Gam, rt, g), E = rows_of(sm.E, rt, g);
+            const f32x16 dq2 = a2[rt] * G * scale;
+            const f32x16 dk3 = -(a3[rt] * G);
+            const f32x16 dk4 = a4[rt] * E;
+            dq[rt] = dq[rt] + dq2;
+            dk[rt] = dk[rt] + dk3 + dk4;
+            // q and k of this wave's columns in accumulator layout
+            const F q0 = L.trK(sm.qt, w, 2 * rt), q1 = L.trK(sm.qt, w, 2 * rt + 1);
+            const F k0 = L.trK(sm.kt, w, 2 * rt), k1 = L.trK(sm.kt, w, 2 * rt + 1);
+            f32x16 pq, pk3, pk4;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                pq[j] = (float)q0[j] * dq2[j];
+                pq[8 + j] = (float)q1[j] * dq2[8 + j];
+                pk3[j] = (float)k0[j] * dk3[j];
+                pk3[8 + j] = (float)k1[j] * dk3[8 + j];
+                pk4[j] = (float)k0[j] * dk4[j];
+                pk4[8 + j] = (float)k1[j] * dk4[8 + j];
+            }
+            row_sums(sm.part[w][1], pq, rt, g, n);
+            row_sums(sm.part[w][2], pk3, rt, g, n);
+            row_sums(sm.part[w][3], pk4, rt, g, n);
+        }
+        T* dqout = (T*)prm.dq + (((size_t)b * Tn + t0) * H + h) * kDk;
+        T* dkout = (T*)prm.dk + (((size_t)b * Tn + t0) * H + h) * kDk;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            st_rows_hbm<T>(dqout, dq[rt], rt, g, n, w, H, nv);
+            st_rows_hbm<T>(dkout, dk[rt], rt, g, n, w, H, nv);
+        }
+    }
+    // ---- phase 5: <dHn, Hn> for the gradient of gamma_C
+    {
+        float acc = 0.f;
+        for (int i = tid; i < kDk * kDv / 4; i += kLocalThreads) {
+            const f32x4 a = ((const f32x4*)dHn)[i], s = ((const f32x4*)Hn)[i];
+            acc += a[0] * s[0] + a[1] * s[1] + a[2] * s[2] + a[3] * s[3];
+        }
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) acc += __shfl_xor(acc, d, 64);
+        if (lane == 0) sm.red[w] = acc;
+    }
+    lds_barrier();
+
+    // ---- phase 6: dgamma, reverse cumulative sum, dbeta
+    if (w == 0) {
+        const int r = lane;
+        float rs = 0.f, cs = 0.f;
+        for (int s = 0; s < kChunk; ++s) {
+            rs += sm.xs[r][s];
+            cs += sm.xs[s][r];
+        }
+        float dgam = rs - cs, db = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+            dgam += sm.part[ww][1][r] + sm.part[ww][2][r] - sm.part[ww][3][r];
+            db += sm.part[ww][0][r];
+        }
+        if (r == kChunk - 1) dgam += sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
+        // suffix sum over positions r..63
+        const float rev = __shfl(dgam, kChunk - 1 - r, 64);
+        const float sc = wave_inclusive_scan(rev);
+        const float dgv = __shfl(sc, kChunk - 1 - r, 64);
+        if (r < nv) {
+            const size_t go = ((size_t)b * Tn + t0 + r) * H + h;
+            prm.dg[go] = dgv;
+            prm.dbeta[go] = db;
+        }
+    }
+}
+
+template <typename K>
+hipError_t set_lds(K kernel, size_t bytes) {
+    return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <typename T>
+hipError_t launch_dh_t(const BwdParams& p, hipStream_t s) {
+    static bool configured = false;
+    const size_t lds = sizeof(Smem<T>);
+    if (!configured) {
+        hipError_t e = set_lds(gdn_bwd_dh_kernel<T>, lds);
+        if (e != hipSuccess) return e;
+        configured = true;
+    }
+    hipLaunchKernelGGL((gdn_bwd_dh_kernel<T>), dim3(p.B * p.H), dim3(kDhThreads), lds, s, p);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_local_t(const BwdParams& p, hipStream_t s) {
+    static bool configured = false;
+    const size_t lds = sizeof(LocalSmem<T>);
+    if (!configured) {
+        hipError_t e = set_lds(gdn_bwd_local_kernel<T>, lds);
+        if (e != hipSuccess) return e;
+        configured = true;
+    }
+    hipLaunchKernelGGL((gdn_bwd_local_kernel<T>), dim3(p.B * p.H * p.N), dim3(kLocalThreads), lds, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dh(const BwdParams& p, bool bf16, hipStream_t s) {
+    return bf16 ? launch_dh_t<__bf16>(p, s) : hipErrorNotSupported;
+}
+
+hipError_t launch_bwd_local(const BwdParams& p, bool bf16, hipStream_t s) {
+    return bf16 ? launch_local_t<__bf16>(p, s) : hipErrorNotSupported;
+}
+
+}  // namespace gdn

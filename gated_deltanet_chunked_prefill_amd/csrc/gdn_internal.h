@@ -33,6 +33,7 @@ struct FwdParams {
     float* bz;
     float* mt;
     float* gsum;
+    float* hstore;     // nullable: [B*H, N+1, dk, dv] state entering each chunk, then the final state
 };
 
 enum FwdPhase { PHASE_SINGLE = 0, PHASE_A = 1, PHASE_C = 2 };
@@ -51,17 +52,19 @@ struct BwdParams {
     const float* beta;
     const float* h0;
     const void* dout;
-    const float* dht;
+    const float* dht;     // nullable: no gradient on the final state
     void* dq;
     void* dk;
     void* dv;
     float* dg;
     float* dbeta;
-    float* dh0;
+    float* dh0;           // nullable
     int B, T, H, N;
     float scale;
-    float* hstates;   // [B*H, N, dk, dv] state entering each chunk
+    const float* hstore;  // [B*H, N+1, dk, dv] state entering each chunk, then the final state
+    float* dhstore;       // [B*H, N, dk, dv] gradient reaching the end of each chunk
 };
-hipError_t launch_bwd(const BwdParams& p, bool bf16, hipStream_t s);
+hipError_t launch_bwd_dh(const BwdParams& p, bool bf16, hipStream_t s);
+hipError_t launch_bwd_local(const BwdParams& p, bool bf16, hipStream_t s);
 
 }  // namespace gdn

@@ -113,7 +113,10 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          const gdn_options* opt, void* workspace, size_t workspace_bytes,
                          void* stream);
 
-/* Workspace bytes for gdn_chunk_bwd ((size_t)-1 for invalid arguments). */
+/* Workspace bytes for gdn_chunk_bwd ((size_t)-1 for invalid arguments):
+ * B*H*(2N+1) float32 128 x 128 matrices (N = number of 64-token chunks), the
+ * state entering every chunk plus the final state, and the state gradient
+ * reaching the end of every chunk. */
 size_t gdn_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, gdn_dtype dtype);
 
 /* Fused chunked backward (page 1 lede and talk summary paragraph 6: the
@@ -123,7 +126,12 @@ size_t gdn_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, gdn_dty
  *   grad_q, grad_k, grad_v  [.., dk|dv] in the I/O dtype (required)
  *   grad_g, grad_beta       [B,T,H] float32 (required); grad_g is dL/d(log alpha)
  *   grad_h0                 [B,H,dk,dv] float32 or NULL
- * The forward inputs (q, k, v, g, beta, h0) must be the ones of the forward. */
+ * The forward inputs (q, k, v, g, beta, h0) must be the ones of the forward.
+ * Only bf16 I/O is supported (GDN_ERR_UNSUPPORTED for float32).  workspace:
+ * at least gdn_chunk_bwd_workspace_size() bytes, 256-byte aligned (required).
+ * Runs three launches on `stream`: the forward kernel storing the state
+ * entering every chunk, the state gradient from the last chunk to the first,
+ * and the local gradients of all chunks in parallel. */
 gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const float* h0, const void* dout, const float* dht,
                          void* grad_q, void* grad_k, void* grad_v, float* grad_g,
@@ -153,8 +161,9 @@ typedef enum {
     GDN_LAUNCH_FWD_PASS_A = 3,  /* fused forward: window heads, segment 0, pass-1     */
     GDN_LAUNCH_COMBINE = 4,     /* segment combine                                    */
     GDN_LAUNCH_FWD_PASS_C = 5,  /* fused forward: exact heads from corrected states   */
-    GDN_LAUNCH_BWD_STATES = 6,  /* backward: chunk-boundary state recompute           */
-    GDN_LAUNCH_BWD = 7          /* backward: reverse sweep and local gradients        */
+    GDN_LAUNCH_BWD_STATES = 6,  /* backward: state entering every chunk (forward kernel) */
+    GDN_LAUNCH_BWD_DH = 7,      /* backward: state gradient, end to start             */
+    GDN_LAUNCH_BWD_LOCAL = 8    /* backward: local gradients of every chunk           */
 } gdn_launch_kind;
 
 /* Measurement hook (the talk summary, paragraph 7, argues the fused operator

@@ -91,3 +91,29 @@ def test_gate_scan_and_bwd_validation():
     assert st == _lib.GDN_ERR_WORKSPACE
     assert lib.gdn_gate_scan_workspace_size(1, 64 * 10, 4) == 256
     assert lib.gdn_chunk_bwd_workspace_size(1, 64, 1, 64, 128, 1) == ctypes.c_size_t(-1).value
+
+
+def _bwd(lib, ptrs, B=1, T=64, H=1, dt=1, ws=None, wsz=0):
+    P = lambda a: ctypes.c_void_p(a) if a else None
+    q, k, v, g, beta, dout, dq, dk, dv, dg, db = ptrs
+    return lib.gdn_chunk_bwd(P(q), P(k), P(v), P(g), P(beta), None, P(dout), None, P(dq), P(dk),
+                             P(dv), P(dg), P(db), None, B, T, H, 128, 128, dt, 1.0, P(ws), wsz,
+                             None)
+
+
+def test_bwd_validation_before_launch():
+    lib = _lib.load()
+    A = 1 << 20
+    full = [A] * 11
+    SS = 128 * 128 * 4
+    # two chunks: 3 entry/final states + 2 state gradients per head
+    assert lib.gdn_chunk_bwd_workspace_size(1, 128, 1, 128, 128, 1) == 5 * SS
+    assert lib.gdn_chunk_bwd_workspace_size(2, 100, 3, 128, 128, 1) == 6 * 5 * SS
+    assert _bwd(lib, [0] + full[1:]) == _lib.GDN_ERR_INVALID_ARG
+    assert _bwd(lib, full[:10] + [0]) == _lib.GDN_ERR_INVALID_ARG
+    assert _bwd(lib, full, dt=0, ws=A, wsz=1 << 30) == _lib.GDN_ERR_UNSUPPORTED
+    assert "bf16" in _lib.last_error()
+    assert _bwd(lib, full) == _lib.GDN_ERR_WORKSPACE
+    assert _bwd(lib, full, ws=A, wsz=3 * SS - 1) == _lib.GDN_ERR_WORKSPACE
+    assert _bwd(lib, full, ws=A + 16, wsz=1 << 30) == _lib.GDN_ERR_INVALID_ARG
+    assert _bwd(lib, [A + 2] + full[1:], ws=A, wsz=1 << 30) == _lib.GDN_ERR_INVALID_ARG
