@@ -9,6 +9,8 @@ every forward launch and the segment combine).
 Prints one JSON line with tokens/s, the roofline of the fused forward kernel
 (algorithmic bytes over its HIP-event-timed launch durations, against the
 8 TB/s HBM peak) and the fp64 CPU oracle timed on the host as a reference.
+A secondary "backward" object times whole gdn_chunk_bwd calls on the training
+shape (B=4, T=8192, H=32, bf16) with per-launch event times.
 """
 from __future__ import annotations
 
@@ -136,6 +138,56 @@ def load_traffic():
     return rec
 
 
+BWD_WORKLOAD = "bf16_b4_t8192_h32_train"
+# backward algorithmic bytes per token-head: q, k, v, dO read (4 x 256 B), g, beta
+# read (8 B), dq, dk, dv written (3 x 256 B), dg, dbeta written (8 B); per head h0
+# read and dh0 written (2 x 64 KiB)
+BWD_BYTES_PER_TOKEN_HEAD = 4 * 256 + 8 + 3 * 256 + 8
+
+
+def bench_backward(torch, gdn, _lib, inputs, steps, warmup):
+    """Whole gdn_chunk_bwd calls on the training shape, with per-launch event times."""
+    x = inputs.workload(BWD_WORKLOAD)
+    B, T, H, dk, dv = x.shape
+    dev = torch.device("cuda:0")
+    bf = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)
+    q, k, v, do = bf(x.q), bf(x.k), bf(x.v), bf(x.dout)
+    g = torch.from_numpy(x.g).to(dev)
+    beta = torch.from_numpy(x.beta).to(dev)
+    h0 = torch.from_numpy(x.h0).to(dev)
+    del x
+    ws = torch.empty(gdn.gdn_chunk_bwd_workspace_size(B, T, H), dtype=torch.uint8, device=dev)
+
+    def step():
+        gdn.gdn_chunk_bwd(q, k, v, g, beta, do, h0=h0, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    lib = _lib.load()
+    cap = 4 * steps
+    ev = HipEvents(2 * cap)
+    labels = (ctypes.c_int * cap)()
+    lib.gdn_profile_events(ctypes.cast(ev.arr, ctypes.c_void_p), ctypes.cast(labels, ctypes.c_void_p), cap)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n = lib.gdn_profile_events(None, None, 0)
+    per_kind = {}
+    for i in range(n):
+        per_kind.setdefault(_lib.LAUNCH_KINDS[labels[i]], []).append(ev.elapsed_ms(2 * i, 2 * i + 1))
+    ev.close()
+    ms = (t1 - t0) * 1e3 / steps
+    nbytes = B * T * H * BWD_BYTES_PER_TOKEN_HEAD + B * H * STATE_BYTES * 2
+    return {"workload": BWD_WORKLOAD, "B": B, "T": T, "H": H, "steps": steps, "warmup": warmup,
+            "ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kernel_ms": {kd: round(float(np.mean(t)), 4) for kd, t in per_kind.items()}}
+
+
 def cpu_baseline(x, tokens):
     """The fp64 oracle, as it stands, on the first `tokens` tokens of every head."""
     import oracle
@@ -158,6 +210,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens per head of the CPU oracle sample (0 to skip)")
+    ap.add_argument("--bwd-steps", type=int, default=5,
+                    help="timed backward calls on the training shape (0 to skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, stream-copy this many MiB three times "
                          "(the calibration kernel of the HBM counter runs)")
@@ -251,6 +305,10 @@ def main():
                      "traffic_gbs": None if tr is None else traffic / (fwd_ms * 1e-3) / 1e9, "kernel_ms": kernel_ms,
                      "call_frac": nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
     }
+    if args.bwd_steps > 0:
+        del q, k, v, g, beta, o, ht, ws
+        torch.cuda.empty_cache()
+        res["backward"] = bench_backward(torch, gdn, _lib, inputs, args.bwd_steps, 2)
     if args.calib_copy_mib > 0:
         src = torch.randn(args.calib_copy_mib * 2 ** 18, device=dev)
         dst = torch.empty_like(src)
