@@ -347,7 +347,7 @@ gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const floa
     f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.h0 = h0; f.o = nullptr; f.ht = nullptr;
     f.B = B; f.T = T; f.H = H; f.N = N; f.P = 1; f.w = 1; f.scale = scale;
     f.hstore = hstore;
-    hipError_t e = recorded(GDN_LAUNCH_BWD_STATES, s, [&] { return gdn::launch_fwd(f, gdn::PHASE_SINGLE, true, s); });
+    hipError_t e = recorded(GDN_LAUNCH_BWD_STATES, s, [&] { return gdn::launch_fwd(f, gdn::PHASE_STATES, true, s); });
     if (e != hipSuccess) return hip_fail(e, "backward state launch");
     gdn::BwdParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.dout = dout; p.dht = dht;

@@ -111,14 +111,16 @@ template <typename T>
 __device__ __noinline__ void dh_state_loop(const BwdParams& prm, Smem<T>& sm, int bh) {
     constexpr bool kPipe = kDhPipelined;
     const size_t SS = (size_t)kDk * kDv;
-    const int N = prm.N;
-    const float scale = prm.scale;
-    float* const dst = prm.dhstore + (size_t)bh * N * SS;
+    const int N = uni(prm.N);
+    const float scale = uni(prm.scale);
+    float* const dst = uni(prm.dhstore) + (size_t)bh * N * SS;
+    const float* const dht = uni(prm.dht);
+    float* const dh0 = uni(prm.dh0);
     Lane<T> L;
     L.init(threadIdx.x);
     f32x16 dH[4];
-    if (prm.dht) {
-        load_state(prm.dht + (size_t)bh * SS, L.w, L.lane, dH);
+    if (dht) {
+        load_state(dht + (size_t)bh * SS, L.w, L.lane, dH);
     } else {
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) dH[ht] = zero16();
@@ -145,7 +147,7 @@ __device__ __noinline__ void dh_state_loop(const BwdParams& prm, Smem<T>& sm, in
                              sm.gc[0][0], scale, dH);
         }
     }
-    if (prm.dh0) store_state(prm.dh0 + (size_t)bh * SS, L.w, L.lane, dH);
+    if (dh0) store_state(dh0 + (size_t)bh * SS, L.w, L.lane, dH);
 }
 
 // Prep waves: stream K, Q, dO of the chunks in reverse order and prep each one a
@@ -156,13 +158,13 @@ __device__ __noinline__ void dh_prep_loop(const BwdParams& prm, Smem<T>& sm, int
     constexpr bool kPipe = kDhPipelined;
     const int pl = threadIdx.x & 255;
     const int pw = wave_id() - 4;
-    const int H = prm.H, Tn = prm.T, N = prm.N;
+    const int H = uni(prm.H), Tn = uni(prm.T), N = uni(prm.N);
     const int b = bh / H, h = bh % H;
-    const T* const q = (const T*)prm.q;
-    const T* const k = (const T*)prm.k;
-    const T* const dout = (const T*)prm.dout;
-    const float* const gp = prm.g;
-    const float* const bp = prm.beta;
+    const T* const q = uni((const T*)prm.q);
+    const T* const k = uni((const T*)prm.k);
+    const T* const dout = uni((const T*)prm.dout);
+    const float* const gp = uni(prm.g);
+    const float* const bp = uni(prm.beta);
     Lane<T> L;
     L.init(threadIdx.x);
     float gsum = 0.f;

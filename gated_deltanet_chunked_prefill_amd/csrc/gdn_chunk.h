@@ -234,7 +234,7 @@ __device__ __forceinline__ void load_tile(T* tile, const T* src, int b, int h, i
             const int row = L / CPR, slot = L % CPR;
             const int c = slot ^ swz(row);
             u4 v = {0u, 0u, 0u, 0u};
-            if (row < nvalid) v = *(const u4*)(base + row * rowstride + c * EPC);
+            if (row < nvalid) v = *(const __attribute__((address_space(1))) u4*)(base + row * rowstride + c * EPC);
             *(u4*)(tile + L * EPC) = v;
         }
     }
@@ -488,6 +488,22 @@ __device__ __forceinline__ void store_state(float* dst, int w, int lane, const f
             dst[(32 * ht + rho(g, r)) * kDv + 32 * w + n] = Hs[ht][r];
 }
 
+// Wave-uniform copies of values every lane holds alike: the compiler keeps them
+// in scalar registers, so loops bounded by them are scalar loops and values read
+// once through a generic pointer are not re-read (each such read would wait for
+// every outstanding memory operation of the wave).
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uni(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+template <typename P>
+__device__ __forceinline__ P* uni(P* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (P*)(((uint64_t)hi << 32) | lo);
+}
+
 // Number of valid tokens in chunk c of a sequence of T tokens.
 __device__ __forceinline__ int chunk_len(int T, int c) {
     return T - c * kChunk < kChunk ? T - c * kChunk : kChunk;
@@ -500,9 +516,10 @@ __device__ __forceinline__ void load_gate_beta(const float* g, const float* beta
     gv = 0.f;
     bv = 0.f;
     if (lane < chunk_len(T, c)) {
+        typedef __attribute__((address_space(1))) const float gfloat;
         const size_t go = ((size_t)b * T + c * kChunk + lane) * H + h;
-        gv = g[go];
-        bv = beta[go];
+        gv = ((gfloat*)g)[go];
+        bv = ((gfloat*)beta)[go];
     }
 }
 

@@ -63,7 +63,7 @@ __device__ __forceinline__ int seg_start(int p, int N, int P) { return (int)(((l
 // Decode the task of this workgroup.  Returns false when it has nothing to do.
 __device__ bool decode_task(const FwdParams& prm, int phase, Task& t) {
     const int P = prm.P;
-    if (phase == PHASE_SINGLE) {
+    if (phase == PHASE_SINGLE || phase == PHASE_STATES) {
         t.bh = blockIdx.x;
         t.seg = 0;
         t.c_begin = 0;
@@ -121,11 +121,11 @@ __device__ bool decode_task(const FwdParams& prm, int phase, Task& t) {
 
 // The serial state step of one chunk for state wave w (its 32 state columns).
 template <typename T, int MODE>
-__device__ __forceinline__ void chunk_state(const FwdParams& prm, const Lane<T>& L, const T* kt,
+__device__ __forceinline__ void chunk_state(T* o, int Tn, int H, float scale, const Lane<T>& L, const T* kt,
                                             const T* qt, const T* vt, const T (*t32)[kT32],
                                             const float* gam_vec, const float* e_vec, float GC,
                                             int b, int h, int t0, int nvalid, bool emit,
-                                            f32x16* Hs, f32x16* Ms) {
+                                            f32x16* Hs) {
     using F = typename FragOf<T>::type;
     const int n = L.n, g = L.g, w = L.w;
     f32x16 X[2];
@@ -174,18 +174,19 @@ __device__ __forceinline__ void chunk_state(const FwdParams& prm, const Lane<T>&
         OT[1] = mma(vf[2], L.f32(t32[5], 0), OT[1]);
         OT[1] = mma(vf[3], L.f32(t32[5], 1), OT[1]);
         typedef T t4 __attribute__((ext_vector_type(4)));
-        T* o = (T*)prm.o;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             const int pos = 32 * rt + n;
             if (pos < nvalid) {
-                T* orow = o + (((size_t)b * prm.T + t0 + pos) * prm.H + h) * kDv + 32 * w + 4 * g;
+                // global address space: plain vector stores, counted by vmcnt only
+                typedef __attribute__((address_space(1))) t4 gt4;
+                gt4* orow = (gt4*)(o + (((size_t)b * Tn + t0 + pos) * H + h) * kDv + 32 * w + 4 * g);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     t4 v;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = (T)(prm.scale * OT[rt][4 * i + e]);
-                    *(t4*)(orow + 8 * i) = v;
+                    for (int e = 0; e < 4; ++e) v[e] = (T)(scale * OT[rt][4 * i + e]);
+                    orow[2 * i] = v;
                 }
             }
         }
@@ -200,92 +201,89 @@ __device__ __forceinline__ void chunk_state(const FwdParams& prm, const Lane<T>&
     }
     kt_update<T>(L, kt, Hs, GC, ef);
 
-    if (MODE == MODE_PASS1) {
-        // Mt <- Mt - K^T T0 diag(beta) K Mt  (V = 0, no gates)
-        k_times<T>(L, kt, Ms, X);
-        const f32x16 y1 = -X[1];
-        F ym0[2] = {acc_frag<T>(-X[0], 0), acc_frag<T>(-X[0], 1)};
-        block_solve<T>(L, t32[3], t32[5], t32[4], ym0, y1, Vp);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) vf[ks] = acc_frag<T>(Vp[ks >> 1], ks & 1);
-        kt_update<T>(L, kt, Ms, 1.f, vf);
-    }
 }
 
-__device__ __forceinline__ int nvalid_of(const FwdParams& prm, int c) { return chunk_len(prm.T, c); }
-
-__device__ __forceinline__ void load_gb(const FwdParams& prm, int b, int h, int c, int lane, float& gv,
-                                        float& bv) {
-    load_gate_beta(prm.g, prm.beta, prm.T, prm.H, b, h, c, lane, gv, bv);
+// Pass-1 segment transition, carried by the prep waves (prep wave w owns columns
+// [32w, 32w+32) of the 128 x 128 product): Mt <- Mt - K^T T0 diag(beta) K Mt, i.e.
+// the state step with V = 0 and no gates, through the gate-free blocks
+// T0_00 diag(beta), T0_11 diag(beta) and -K_1 K_0^T.
+template <typename T>
+__device__ __forceinline__ void mt_step(const Lane<T>& L, const T* kt, const T (*t32)[kT32], f32x16* Ms) {
+    using F = typename FragOf<T>::type;
+    f32x16 X[2], Vp[2];
+    k_times<T>(L, kt, Ms, X);
+    const f32x16 y1 = -X[1];
+    F ym0[2] = {acc_frag<T>(-X[0], 0), acc_frag<T>(-X[0], 1)};
+    block_solve<T>(L, t32[3], t32[5], t32[4], ym0, y1, Vp);
+    F vf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) vf[ks] = acc_frag<T>(Vp[ks >> 1], ks & 1);
+    kt_update<T>(L, kt, Ms, 1.f, vf);
 }
 
 // State waves: load the entering state, run the serial step of every chunk,
 // store the result.  Executes exactly the same barriers as prep_loop.
-template <typename T, int MODE>
+template <typename T, int MODE, bool KEEP>
 __device__ __noinline__ void state_loop(const FwdParams& prm, Smem<T>& sm, const Task& tk) {
     constexpr bool kPipe = Pipe<T>::on;
-    const int b = tk.bh / prm.H, h = tk.bh % prm.H;
+    // every parameter read once, into scalar registers
+    const int bh = uni(tk.bh), seg = uni(tk.seg), c_begin = uni(tk.c_begin), c_out = uni(tk.c_out);
+    const int c_end = uni(tk.c_end), init = uni(tk.init), dst = uni(tk.dst);
+    const int Tn = uni(prm.T), H = uni(prm.H), N = uni(prm.N), P = uni(prm.P);
+    const float scale = uni(prm.scale);
+    T* const o = uni((T*)prm.o);
+    float* const hst = KEEP ? uni(prm.hstore) : nullptr;
+    const int b = bh / H, h = bh % H;
     const size_t SS = (size_t)kDk * kDv;
-    const int nch = tk.c_end - tk.c_begin;
+    const int nch = c_end - c_begin;
     Lane<T> L;
     L.init(threadIdx.x);
-    f32x16 Hs[4], Ms[4];
-    if (tk.init == INIT_H0) {
-        load_state(prm.h0 + (size_t)tk.bh * SS, L.w, L.lane, Hs);
-    } else if (tk.init == INIT_HS) {
-        load_state(prm.hs + ((size_t)tk.bh * prm.P + tk.seg) * SS, L.w, L.lane, Hs);
+    f32x16 Hs[4];
+    if (init == INIT_H0) {
+        load_state(uni(prm.h0) + (size_t)bh * SS, L.w, L.lane, Hs);
+    } else if (init == INIT_HS) {
+        load_state(uni(prm.hs) + ((size_t)bh * P + seg) * SS, L.w, L.lane, Hs);
     } else {
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) Hs[ht] = zero16();
     }
-    if (MODE == MODE_PASS1) {
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                Ms[ht][r] = (32 * ht + rho(L.g, r) == 32 * L.w + L.n) ? 1.f : 0.f;
-    }
-    const bool has_o = prm.o != nullptr;
-    float* const hst = MODE == MODE_FULL ? prm.hstore : nullptr;
-    const size_t hst_base = (size_t)tk.bh * (prm.N + 1);
-    auto emit = [&](int c) { return MODE == MODE_FULL && has_o && c >= tk.c_out; };
+    const size_t hst_base = (size_t)bh * (N + 1);
+    auto emit = [&](int c) { return MODE == MODE_FULL && o != nullptr && c >= c_out; };
     // the state entering every chunk this task owns (for the backward)
     auto keep = [&](int c) {
-        if (hst && c >= tk.c_out) store_state(hst + (hst_base + c) * SS, L.w, L.lane, Hs);
+        if (KEEP && c >= c_out) store_state(hst + (hst_base + c) * SS, L.w, L.lane, Hs);
     };
     if constexpr (kPipe) {
         lds_barrier();
         lds_barrier();
         for (int i = 0; i < nch; ++i) {
-            const int c = tk.c_begin + i;
+            const int c = c_begin + i;
             const int slot = i % 3, vb = i & 1;
             keep(c);
-            chunk_state<T, MODE>(prm, L, sm.kt[slot], sm.qt[slot], sm.vt[vb], sm.t32[vb],
+            chunk_state<T, MODE>(o, Tn, H, scale, L, sm.kt[slot], sm.qt[slot], sm.vt[vb], sm.t32[vb],
                                  sm.gam_vec[vb], sm.e_vec[vb], sm.gc[vb][0], b, h, c * kChunk,
-                                 nvalid_of(prm, c), emit(c), Hs, Ms);
+                                 chunk_len(Tn, c), emit(c), Hs);
             lds_barrier();
         }
     } else {
         for (int i = 0; i < nch; ++i) {
-            const int c = tk.c_begin + i;
+            const int c = c_begin + i;
             lds_barrier();
             lds_barrier();
             lds_barrier();
             keep(c);
-            chunk_state<T, MODE>(prm, L, sm.kt[0], sm.qt[0], sm.vt[0], sm.t32[0], sm.gam_vec[0],
-                                 sm.e_vec[0], sm.gc[0][0], b, h, c * kChunk, nvalid_of(prm, c),
-                                 emit(c), Hs, Ms);
+            chunk_state<T, MODE>(o, Tn, H, scale, L, sm.kt[0], sm.qt[0], sm.vt[0], sm.t32[0],
+                                 sm.gam_vec[0], sm.e_vec[0], sm.gc[0][0], b, h, c * kChunk,
+                                 chunk_len(Tn, c), emit(c), Hs);
         }
     }
-    if (tk.c_end == prm.N) keep(prm.N);
-    if (tk.dst == DST_HT) {
-        store_state(prm.ht + (size_t)tk.bh * SS, L.w, L.lane, Hs);
-    } else if (tk.dst == DST_HS_NEXT) {
-        store_state(prm.hs + ((size_t)tk.bh * prm.P + tk.seg + 1) * SS, L.w, L.lane, Hs);
-    } else if (tk.dst == DST_PASS1) {
-        const size_t o = ((size_t)tk.bh * prm.P + tk.seg) * SS;
-        store_state(prm.bz + o, L.w, L.lane, Hs);
-        store_state(prm.mt + o, L.w, L.lane, Ms);
+    if (KEEP && c_end == N) keep(N);
+    if (dst == DST_HT) {
+        store_state(uni(prm.ht) + (size_t)bh * SS, L.w, L.lane, Hs);
+    } else if (dst == DST_HS_NEXT) {
+        store_state(uni(prm.hs) + ((size_t)bh * P + seg + 1) * SS, L.w, L.lane, Hs);
+    } else if (dst == DST_PASS1) {
+        store_state(uni(prm.bz) + ((size_t)bh * P + seg) * SS, L.w, L.lane, Hs);
     }
 }
 
@@ -299,42 +297,64 @@ __device__ __noinline__ void prep_loop(const FwdParams& prm, Smem<T>& sm, const 
     constexpr bool kPipe = Pipe<T>::on;
     const int pl = threadIdx.x & 255;     // lane index within the prep group
     const int pw = wave_id() - 4;
-    const int b = tk.bh / prm.H, h = tk.bh % prm.H;
-    const int nch = tk.c_end - tk.c_begin;
+    // every parameter read once, into scalar registers
+    const int bh = uni(tk.bh), seg = uni(tk.seg), c_begin = uni(tk.c_begin), c_out = uni(tk.c_out);
+    const int c_end = uni(tk.c_end), dst = uni(tk.dst);
+    const int Tn = uni(prm.T), H = uni(prm.H), P = uni(prm.P);
+    const T* const kp = uni((const T*)prm.k);
+    const T* const qp = uni((const T*)prm.q);
+    const T* const vp = uni((const T*)prm.v);
+    const float* const gp = uni(prm.g);
+    const float* const bp = uni(prm.beta);
+    const bool has_o = uni(prm.o) != nullptr;
+    const int b = bh / H, h = bh % H;
+    const int nch = c_end - c_begin;
     Lane<T> L;
     L.init(threadIdx.x);
     float gsum = 0.f;
     float g_cur = 0.f, b_cur = 0.f, g_nxt = 0.f, b_nxt = 0.f;
-    const bool has_o = prm.o != nullptr;
-    auto need_q = [&](int c) { return MODE == MODE_FULL && has_o && c >= tk.c_out; };
+    f32x16 Ms[4];
+    if (MODE == MODE_PASS1) {
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                Ms[ht][r] = (32 * ht + rho(L.g, r) == 32 * L.w + L.n) ? 1.f : 0.f;
+    }
+    auto need_q = [&](int c) { return MODE == MODE_FULL && has_o && c >= c_out; };
     auto load_kq = [&](int c, int slot) {
-        const int t0 = c * kChunk, nv = nvalid_of(prm, c);
-        load_tile<T>(sm.kt[slot], (const T*)prm.k, b, h, prm.T, prm.H, t0, nv, pl);
-        if (need_q(c)) load_tile<T>(sm.qt[slot], (const T*)prm.q, b, h, prm.T, prm.H, t0, nv, pl);
+        const int t0 = c * kChunk, nv = chunk_len(Tn, c);
+        load_tile<T>(sm.kt[slot], kp, b, h, Tn, H, t0, nv, pl);
+        if (need_q(c)) load_tile<T>(sm.qt[slot], qp, b, h, Tn, H, t0, nv, pl);
     };
     auto load_v = [&](int c, int slot) {
-        load_tile<T>(sm.vt[slot], (const T*)prm.v, b, h, prm.T, prm.H, c * kChunk, nvalid_of(prm, c), pl);
+        load_tile<T>(sm.vt[slot], vp, b, h, Tn, H, c * kChunk, chunk_len(Tn, c), pl);
+    };
+    auto load_gb = [&](int c, float& gv, float& bv) {
+        load_gate_beta(gp, bp, Tn, H, b, h, c, L.lane, gv, bv);
     };
     if constexpr (kPipe) {
         // prologue: chunk 0 in LDS and prepped; chunk 1's K, Q in flight
-        load_kq(tk.c_begin, 0);
-        load_v(tk.c_begin, 0);
-        if (nch > 1) load_kq(tk.c_begin + 1, 1);
-        load_gb(prm, b, h, tk.c_begin, L.lane, g_cur, b_cur);
-        if (nch > 1) load_gb(prm, b, h, tk.c_begin + 1, L.lane, g_nxt, b_nxt);
+        load_kq(c_begin, 0);
+        load_v(c_begin, 0);
+        if (nch > 1) load_kq(c_begin + 1, 1);
+        load_gb(c_begin, g_cur, b_cur);
+        if (nch > 1) load_gb(c_begin + 1, g_nxt, b_nxt);
         wait_vm();
         lds_barrier();
         chunk_prep<T, MODE>(sm, L, pw, sm.kt[0], sm.qt[0], sm.t32[0], sm.gam_vec[0], sm.e_vec[0],
-                            sm.gc[0], g_cur, b_cur, need_q(tk.c_begin), gsum);
+                            sm.gc[0], g_cur, b_cur, need_q(c_begin), gsum);
         g_cur = g_nxt;
         b_cur = b_nxt;
         lds_barrier();
         for (int i = 0; i < nch; ++i) {
-            const int c = tk.c_begin + i;
+            const int c = c_begin + i;
+            // this chunk's segment transition (its prep outputs are in buffer i & 1)
+            if (MODE == MODE_PASS1) mt_step<T>(L, sm.kt[i % 3], sm.t32[i & 1], Ms);
             if (i + 1 < nch) {
                 if (i + 2 < nch) {
                     load_kq(c + 2, (i + 2) % 3);
-                    load_gb(prm, b, h, c + 2, L.lane, g_nxt, b_nxt);
+                    load_gb(c + 2, g_nxt, b_nxt);
                 }
                 load_v(c + 1, (i + 1) & 1);
                 const int slot = (i + 1) % 3, pb = (i + 1) & 1;
@@ -348,28 +368,32 @@ __device__ __noinline__ void prep_loop(const FwdParams& prm, Smem<T>& sm, const 
         }
     } else {
         for (int i = 0; i < nch; ++i) {
-            const int c = tk.c_begin + i;
+            const int c = c_begin + i;
             lds_barrier();   // the previous chunk is done with the single buffers
             load_kq(c, 0);
             load_v(c, 0);
-            load_gb(prm, b, h, c, L.lane, g_cur, b_cur);
+            load_gb(c, g_cur, b_cur);
             wait_vm();
             lds_barrier();
             chunk_prep<T, MODE>(sm, L, pw, sm.kt[0], sm.qt[0], sm.t32[0], sm.gam_vec[0], sm.e_vec[0],
                                 sm.gc[0], g_cur, b_cur, need_q(c), gsum);
             lds_barrier();
+            if (MODE == MODE_PASS1) mt_step<T>(L, sm.kt[0], sm.t32[0], Ms);
         }
     }
-    if (tk.dst == DST_PASS1 && pw == 3 && L.lane == 0) prm.gsum[(size_t)tk.bh * prm.P + tk.seg] = gsum;
+    if (dst == DST_PASS1) {
+        store_state(uni(prm.mt) + ((size_t)bh * P + seg) * (size_t)(kDk * kDv), L.w, L.lane, Ms);
+        if (pw == 3 && L.lane == 0) uni(prm.gsum)[(size_t)bh * P + seg] = gsum;
+    }
 }
 
-template <typename T, int MODE>
+template <typename T, int MODE, bool KEEP = false>
 __device__ __forceinline__ void run_task(const FwdParams& prm, Smem<T>& sm, const Task& tk) {
     // the role branch must be wave-uniform to the compiler: both roles hold
     // s_barrier, and a branch it takes for divergent would be laid out so that a
     // wave also passes through the other role's barriers
     if (wave_id() < 4)
-        state_loop<T, MODE>(prm, sm, tk);
+        state_loop<T, MODE, KEEP>(prm, sm, tk);
     else
         prep_loop<T, MODE>(prm, sm, tk);
 }
@@ -383,6 +407,8 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_kernel(FwdParams prm) {
     // only the first launch of a split forward has pass-1 tasks
     if (PHASE == PHASE_A && tk.mode == MODE_PASS1)
         run_task<T, MODE_PASS1>(prm, sm, tk);
+    else if (PHASE == PHASE_STATES)
+        run_task<T, MODE_FULL, true>(prm, sm, tk);
     else
         run_task<T, MODE_FULL>(prm, sm, tk);
 }
@@ -404,6 +430,7 @@ hipError_t launch_phase(const FwdParams& p, int grid, hipStream_t s) {
 template <typename T>
 hipError_t launch_fwd_t(const FwdParams& p, int phase, hipStream_t s) {
     if (phase == PHASE_SINGLE) return launch_phase<T, PHASE_SINGLE>(p, p.B * p.H, s);
+    if (phase == PHASE_STATES) return launch_phase<T, PHASE_STATES>(p, p.B * p.H, s);
     if (phase == PHASE_A) return launch_phase<T, PHASE_A>(p, p.B * p.H * p.P, s);
     return launch_phase<T, PHASE_C>(p, p.B * p.H * (p.P - 1), s);
 }

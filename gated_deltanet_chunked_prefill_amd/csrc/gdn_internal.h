@@ -36,7 +36,9 @@ struct FwdParams {
     float* hstore;     // nullable: [B*H, N+1, dk, dv] state entering each chunk, then the final state
 };
 
-enum FwdPhase { PHASE_SINGLE = 0, PHASE_A = 1, PHASE_C = 2 };
+// PHASE_STATES: the unsplit forward that only stores the state entering every
+// chunk (into hstore), for the backward.
+enum FwdPhase { PHASE_SINGLE = 0, PHASE_A = 1, PHASE_C = 2, PHASE_STATES = 3 };
 
 hipError_t launch_fwd(const FwdParams& p, int phase, bool bf16, hipStream_t s);
 hipError_t launch_combine(const FwdParams& p, hipStream_t s);
