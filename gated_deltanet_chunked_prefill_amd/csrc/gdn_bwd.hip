@@ -156,7 +156,6 @@ __device__ __noinline__ void dh_state_loop(const BwdParams& prm, Smem<T>& sm, in
 template <typename T>
 __device__ __noinline__ void dh_prep_loop(const BwdParams& prm, Smem<T>& sm, int bh) {
     constexpr bool kPipe = kDhPipelined;
-    const int pl = threadIdx.x & 255;
     const int pw = wave_id() - 4;
     const int H = uni(prm.H), Tn = uni(prm.T), N = uni(prm.N);
     const int b = bh / H, h = bh % H;
@@ -170,13 +169,16 @@ __device__ __noinline__ void dh_prep_loop(const BwdParams& prm, Smem<T>& sm, int
     float gsum = 0.f;
     float g_cur = 0.f, b_cur = 0.f, g_nxt = 0.f, b_nxt = 0.f;
     auto cidx = [&](int i) { return N - 1 - i; };
+    TileLoader<T> TL;
+    TL.init(pw, L.lane, H);
     auto load_kq = [&](int c, int slot) {
-        const int t0 = c * kChunk, nv = chunk_len(Tn, c);
-        load_tile<T>(sm.kt[slot], k, b, h, Tn, H, t0, nv, pl);
-        load_tile<T>(sm.qt[slot], q, b, h, Tn, H, t0, nv, pl);
+        const size_t cb = chunk_base(b, h, Tn, H, c);
+        const int nv = chunk_len(Tn, c);
+        TL.load(sm.kt[slot], k + cb, nv);
+        TL.load(sm.qt[slot], q + cb, nv);
     };
     auto load_do = [&](int c, int slot) {
-        load_tile<T>(sm.vt[slot], dout, b, h, Tn, H, c * kChunk, chunk_len(Tn, c), pl);
+        TL.load(sm.vt[slot], dout + chunk_base(b, h, Tn, H, c), chunk_len(Tn, c));
     };
     if constexpr (kPipe) {
         load_kq(cidx(0), 0);
@@ -347,10 +349,15 @@ __global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_kernel(BwdPara
     const float* const dHn = prm.dhstore + ((size_t)bh * N + c) * SS;
 
     // ---- phase 0: tiles, gates
-    load_tile<T>(sm.qt, (const T*)prm.q, b, h, Tn, H, t0, nv, tid);
-    load_tile<T>(sm.kt, (const T*)prm.k, b, h, Tn, H, t0, nv, tid);
-    load_tile<T>(sm.vt, (const T*)prm.v, b, h, Tn, H, t0, nv, tid);
-    load_tile<T>(sm.dot, (const T*)prm.dout, b, h, Tn, H, t0, nv, tid);
+    {
+        TileLoader<T> TL;
+        TL.init(w, lane, H);
+        const size_t cb = chunk_base(b, h, Tn, H, c);
+        TL.load(sm.qt, (const T*)prm.q + cb, nv);
+        TL.load(sm.kt, (const T*)prm.k + cb, nv);
+        TL.load(sm.vt, (const T*)prm.v + cb, nv);
+        TL.load(sm.dot, (const T*)prm.dout + cb, nv);
+    }
     if (w == 0) {
         float gv, bv;
         load_gate_beta(prm.g, prm.beta, Tn, H, b, h, c, lane, gv, bv);

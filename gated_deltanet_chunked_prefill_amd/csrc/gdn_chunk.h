@@ -63,6 +63,22 @@ __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
+// Wave-uniform copies of values every lane holds alike: the compiler keeps them
+// in scalar registers, so loops bounded by them are scalar loops and values read
+// once through a generic pointer are not re-read (each such read would wait for
+// every outstanding memory operation of the wave).
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uni(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+template <typename P>
+__device__ __forceinline__ P* uni(P* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (P*)(((uint64_t)hi << 32) | lo);
+}
+
 typedef __attribute__((address_space(3))) char lds_t;
 __device__ __forceinline__ const lds_t* as_lds(const void* p) { return (const lds_t*)p; }
 
@@ -201,43 +217,56 @@ struct Lane {
     }
 };
 
-// Copy one 64 x 128 tile of chunk rows [t0, t0 + nvalid) of head (b, h) into a
-// swizzled row-major LDS tile, spread over the 256 lanes of the prep waves
-// (pl = 0..255).  Full chunks go HBM -> LDS directly (each lane's 16 bytes land
-// at slot base + 16*lane, so the lane fetches the chunk that belongs there); a
-// short last chunk goes through registers and is zero-filled.
+// Copy of one 64 x 128 chunk tile of a head into a swizzled row-major LDS tile,
+// spread over the 256 lanes of four waves.  Full chunks go HBM -> LDS directly
+// (each lane's 16 bytes land at slot base + 16*lane, so the lane fetches the
+// chunk that belongs there); a short last chunk goes through registers and is
+// zero-filled.
 template <typename T>
-__device__ __forceinline__ void load_tile(T* tile, const T* src, int b, int h, int T_, int H, int t0,
-                                          int nvalid, int pl) {
-    constexpr int EPC = 16 / (int)sizeof(T);
-    constexpr int CPR = kDk / EPC;                 // 16-byte chunks per row
-    constexpr int ROUNDS = kChunk * CPR / 256;
-    const int pw = pl >> 6, lane = pl & 63;
-    const size_t rowstride = (size_t)H * kDk;
-    const T* base = src + (((size_t)b * T_ + t0) * H + h) * kDk;
-    if (nvalid == kChunk) {
-#pragma unroll
-        for (int i = 0; i < ROUNDS; ++i) {
-            const int L = (i * 4 + pw) * 64 + lane;     // slot index in the tile
-            const int row = L / CPR, slot = L % CPR;
-            const int c = slot ^ swz(row);
-            const T* gp = base + row * rowstride + c * EPC;
-            T* lbase = tile + (i * 4 + pw) * 64 * EPC;
-            __builtin_amdgcn_global_load_lds((const void*)gp,
-                                             (__attribute__((address_space(3))) void*)lbase, 16, 0, 0);
-        }
-    } else {
-        typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+struct TileLoader {
+    static constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16-byte chunk
+    static constexpr int CPR = kDk / EPC;               // 16-byte chunks per row
+    static constexpr int ROUNDS = kChunk * CPR / 256;
+    uint32_t off[ROUNDS];   // byte offset of this lane's 16 bytes from the chunk's first row
+    int pw, lane;           // loading wave (0..3, wave-uniform) and lane
+
+    // Computed once per task: round i covers tile slots (4i + pw) * 64 + lane.
+    __device__ __forceinline__ void init(int pw_, int lane_, int H) {
+        pw = pw_;
+        lane = lane_;
 #pragma unroll
         for (int i = 0; i < ROUNDS; ++i) {
             const int L = (i * 4 + pw) * 64 + lane;
             const int row = L / CPR, slot = L % CPR;
-            const int c = slot ^ swz(row);
-            u4 v = {0u, 0u, 0u, 0u};
-            if (row < nvalid) v = *(const __attribute__((address_space(1))) u4*)(base + row * rowstride + c * EPC);
-            *(u4*)(tile + L * EPC) = v;
+            off[i] = (uint32_t)((row * H * kDk + (slot ^ swz(row)) * EPC) * (int)sizeof(T));
         }
     }
+    // Copy the chunk whose first row (for this head) is `chunk` into `tile`.
+    __device__ __forceinline__ void load(T* tile, const T* chunk, int nvalid) const {
+        const char* base = (const char*)chunk;
+        if (nvalid == kChunk) {
+#pragma unroll
+            for (int i = 0; i < ROUNDS; ++i) {
+                T* lbase = tile + (i * 4 + pw) * 64 * EPC;   // wave-uniform LDS destination
+                __builtin_amdgcn_global_load_lds((const void*)(base + off[i]),
+                                                 (__attribute__((address_space(3))) void*)lbase, 16, 0, 0);
+            }
+        } else {
+            typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+            for (int i = 0; i < ROUNDS; ++i) {
+                const int L = (i * 4 + pw) * 64 + lane;
+                u4 v = {0u, 0u, 0u, 0u};
+                if (L / CPR < nvalid) v = *(const __attribute__((address_space(1))) u4*)(base + off[i]);
+                *(u4*)(tile + L * EPC) = v;
+            }
+        }
+    }
+};
+
+// Element offset of the first row of chunk c of head (b, h) in a [B, T, H, 128] tensor.
+__device__ __forceinline__ size_t chunk_base(int b, int h, int T, int H, int c) {
+    return (((size_t)b * T + (size_t)c * kChunk) * H + h) * kDk;
 }
 
 // Per-position vector values for the 16 accumulator rows of row tile rt.
@@ -292,17 +321,19 @@ __device__ __forceinline__ f32x16 diag_inverse_t(const f32x16& S, const f32x16& 
 
 // Gate factor Gamma_r / Gamma_s for lane row r and accumulator-row columns s:
 // fr is the row value (gamma_r or exp(gamma_r - gC/2)), fc the column values.
-__device__ __forceinline__ float gate_factor(float fr, float fc, bool pairwise) {
-    return pairwise ? __expf(fr - fc) : fr * fc;
+template <bool PW>
+__device__ __forceinline__ float gate_factor(float fr, float fc) {
+    if constexpr (PW) return __expf(fr - fc);
+    else return fr * fc;
 }
 
 // Diagonal block p of the chunk: S = K_p K_p^T, T0_pp by the series, then the
 // gated Tt_pp (and the gate-free T0_pp diag(beta) in pass-1).  p is a template
 // parameter so that every per-lane address-table index is a compile-time constant.
-template <typename T, int MODE, int p>
+template <typename T, int MODE, int p, bool PW>
 __device__ __forceinline__ void diag_block(const Lane<T>& L, const T* kt, T (*t32)[kT32],
                                            const float* s_row, const float* s_col,
-                                           const float* s_beta, bool pairwise) {
+                                           const float* s_beta) {
     using F = typename FragOf<T>::type;
     const int n = L.n, g = L.g;
     f32x16 S = zero16();
@@ -323,7 +354,7 @@ __device__ __forceinline__ void diag_block(const Lane<T>& L, const T* kt, T (*t3
         for (int j = 0; j < 8; ++j) {
             const int r = 8 * ksl + j;
             const float t0v = zt[r] * brow[r];
-            f[j] = (T)(rho(g, r) <= n ? t0v * gate_factor(fr, fc[r], pairwise) : 0.f);
+            f[j] = (T)(rho(g, r) <= n ? t0v * gate_factor<PW>(fr, fc[r]) : 0.f);
             f0[j] = (T)t0v;
         }
         L.st32(t32[p], ksl, f);
@@ -331,45 +362,20 @@ __device__ __forceinline__ void diag_block(const Lane<T>& L, const T* kt, T (*t3
     }
 }
 
-// Chunk-independent prep of one chunk by prep wave pw.
-template <typename T, int MODE>
-__device__ __forceinline__ void chunk_prep(Smem<T>& sm, const Lane<T>& L, int pw, const T* kt,
-                                           const T* qt, T (*t32)[kT32], float* gam_vec,
-                                           float* e_vec, float* gc, float gv, float bv, bool emit,
-                                           float& gsum) {
+// Matrix part of the chunk prep for prep wave pw, with the gate factor taken as
+// the product of the re-centred exponentials (PW = false) or pairwise (PW = true).
+template <typename T, int MODE, bool PW>
+__device__ __forceinline__ void chunk_prep_mats(const Lane<T>& L, int pw, const T* kt, const T* qt,
+                                                T (*t32)[kT32], const float* scr, bool emit) {
     using F = typename FragOf<T>::type;
-    const int lane = L.lane, n = L.n, g = L.g;
-    float* scr = &sm.pscr[pw][0][0];
-    // in-chunk scan and the 2C+1 exponentials of the factored gate (paragraph 6),
-    // re-centred at gamma_C/2 so both factors stay within exp(|gamma_C|/2); chunks
-    // whose decay exceeds that safe range use pairwise exponentials.
-    const float gam = wave_inclusive_scan(gv);
-    const float gC = __builtin_bit_cast(
-        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, __shfl(gam, 63, 64))));  // wave-uniform
-    const float half = 0.5f * gC;
-    const bool pairwise = gC < -160.f;
-    const float gp = __expf(gam - half);
-    const float gn = __expf(half - gam);
-    const float eh = __expf(half);
-    scr[0 * kChunk + lane] = gam;
-    scr[1 * kChunk + lane] = gp;
-    scr[2 * kChunk + lane] = gn;
-    scr[3 * kChunk + lane] = bv;
-    if (pw == 3) {
-        gam_vec[lane] = pairwise ? __expf(gam) : gp * eh;
-        e_vec[lane] = pairwise ? __expf(gC - gam) : gn * eh;
-        if (lane == 0) gc[0] = pairwise ? __expf(gC) : eh * eh;
-        gsum += gC;
-    }
-    wait_lgkm();
-    const float* s_row = scr + (pairwise ? 0 : 1) * kChunk;   // gamma or exp(gamma - gC/2)
-    const float* s_col = scr + (pairwise ? 0 : 2) * kChunk;   // gamma or exp(gC/2 - gamma)
+    const int n = L.n, g = L.g;
+    const float* s_row = scr + (PW ? 0 : 1) * kChunk;   // gamma or exp(gamma - gC/2)
+    const float* s_col = scr + (PW ? 0 : 2) * kChunk;   // gamma or exp(gC/2 - gamma)
     const float* s_beta = scr + 3 * kChunk;
-
     if (pw == 0) {
-        diag_block<T, MODE, 0>(L, kt, t32, s_row, s_col, s_beta, pairwise);
+        diag_block<T, MODE, 0, PW>(L, kt, t32, s_row, s_col, s_beta);
     } else if (pw == 1) {
-        diag_block<T, MODE, 1>(L, kt, t32, s_row, s_col, s_beta, pairwise);
+        diag_block<T, MODE, 1, PW>(L, kt, t32, s_row, s_col, s_beta);
     } else if (pw == 2) {
         // off-diagonal block: acc(K_0 K_1^T) has lane n = row 32+n, registers = columns rho
         f32x16 x = zero16();
@@ -383,7 +389,7 @@ __device__ __forceinline__ void chunk_prep(Smem<T>& sm, const Lane<T>& L, int pw
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int r = 8 * ksl + j;
-                f[j] = (T)(-x[r] * gate_factor(fr, fc[r], pairwise));
+                f[j] = (T)(-x[r] * gate_factor<PW>(fr, fc[r]));
                 f0[j] = (T)(-x[r]);
             }
             L.st32(t32[2], ksl, f);
@@ -400,7 +406,7 @@ __device__ __forceinline__ void chunk_prep(Smem<T>& sm, const Lane<T>& L, int pw
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int r = 8 * ksl + j;
-                    f[j] = (T)(y[r] * gate_factor(fr, fc[r], pairwise));
+                    f[j] = (T)(y[r] * gate_factor<PW>(fr, fc[r]));
                 }
                 L.st32(t32[4], ksl, f);
             }
@@ -420,12 +426,47 @@ __device__ __forceinline__ void chunk_prep(Smem<T>& sm, const Lane<T>& L, int pw
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int r = 8 * ksl + j;
-                    f[j] = (T)(rho(g, r) <= n ? y[r] * gate_factor(fr, fc[r], pairwise) : 0.f);
+                    f[j] = (T)(rho(g, r) <= n ? y[r] * gate_factor<PW>(fr, fc[r]) : 0.f);
                 }
                 L.st32(t32[j2 == 0 ? 3 : 5], ksl, f);
             }
         }
     }
+}
+
+// Chunk-independent prep of one chunk by prep wave pw.
+template <typename T, int MODE>
+__device__ __forceinline__ void chunk_prep(Smem<T>& sm, const Lane<T>& L, int pw, const T* kt,
+                                           const T* qt, T (*t32)[kT32], float* gam_vec,
+                                           float* e_vec, float* gc, float gv, float bv, bool emit,
+                                           float& gsum) {
+    const int lane = L.lane;
+    float* scr = &sm.pscr[pw][0][0];
+    // in-chunk scan and the 2C+1 exponentials of the factored gate (paragraph 6),
+    // re-centred at gamma_C/2 so both factors stay within exp(|gamma_C|/2); chunks
+    // whose decay exceeds that safe range use pairwise exponentials.
+    const float gam = wave_inclusive_scan(gv);
+    const float gC = uni(__shfl(gam, 63, 64));
+    const float half = 0.5f * gC;
+    const bool pairwise = gC < -160.f;   // wave-uniform
+    const float gp = __expf(gam - half);
+    const float gn = __expf(half - gam);
+    const float eh = __expf(half);
+    scr[0 * kChunk + lane] = gam;
+    scr[1 * kChunk + lane] = gp;
+    scr[2 * kChunk + lane] = gn;
+    scr[3 * kChunk + lane] = bv;
+    if (pw == 3) {
+        gam_vec[lane] = pairwise ? __expf(gam) : gp * eh;
+        e_vec[lane] = pairwise ? __expf(gC - gam) : gn * eh;
+        if (lane == 0) gc[0] = pairwise ? __expf(gC) : eh * eh;
+        gsum += gC;
+    }
+    wait_lgkm();
+    if (pairwise)
+        chunk_prep_mats<T, MODE, true>(L, pw, kt, qt, t32, scr, emit);
+    else
+        chunk_prep_mats<T, MODE, false>(L, pw, kt, qt, t32, scr, emit);
 }
 
 // X = K Hm for the two 32-row position tiles (Hm: the four dk tiles of a state).
@@ -486,22 +527,6 @@ __device__ __forceinline__ void store_state(float* dst, int w, int lane, const f
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             dst[(32 * ht + rho(g, r)) * kDv + 32 * w + n] = Hs[ht][r];
-}
-
-// Wave-uniform copies of values every lane holds alike: the compiler keeps them
-// in scalar registers, so loops bounded by them are scalar loops and values read
-// once through a generic pointer are not re-read (each such read would wait for
-// every outstanding memory operation of the wave).
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ float uni(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
-}
-template <typename P>
-__device__ __forceinline__ P* uni(P* p) {
-    const uint64_t v = (uint64_t)p;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
-    return (P*)(((uint64_t)hi << 32) | lo);
 }
 
 // Number of valid tokens in chunk c of a sequence of T tokens.

@@ -200,7 +200,6 @@ __device__ __forceinline__ void chunk_state(T* o, int Tn, int H, float scale, co
         ef[2 * rt + 1] = acc_frag<T>(ev, 1);
     }
     kt_update<T>(L, kt, Hs, GC, ef);
-
 }
 
 // Pass-1 segment transition, carried by the prep waves (prep wave w owns columns
@@ -295,7 +294,6 @@ __device__ __noinline__ void state_loop(const FwdParams& prm, Smem<T>& sm, const
 template <typename T, int MODE>
 __device__ __noinline__ void prep_loop(const FwdParams& prm, Smem<T>& sm, const Task& tk) {
     constexpr bool kPipe = Pipe<T>::on;
-    const int pl = threadIdx.x & 255;     // lane index within the prep group
     const int pw = wave_id() - 4;
     // every parameter read once, into scalar registers
     const int bh = uni(tk.bh), seg = uni(tk.seg), c_begin = uni(tk.c_begin), c_out = uni(tk.c_out);
@@ -322,13 +320,16 @@ __device__ __noinline__ void prep_loop(const FwdParams& prm, Smem<T>& sm, const 
                 Ms[ht][r] = (32 * ht + rho(L.g, r) == 32 * L.w + L.n) ? 1.f : 0.f;
     }
     auto need_q = [&](int c) { return MODE == MODE_FULL && has_o && c >= c_out; };
+    TileLoader<T> TL;
+    TL.init(pw, L.lane, H);
     auto load_kq = [&](int c, int slot) {
-        const int t0 = c * kChunk, nv = chunk_len(Tn, c);
-        load_tile<T>(sm.kt[slot], kp, b, h, Tn, H, t0, nv, pl);
-        if (need_q(c)) load_tile<T>(sm.qt[slot], qp, b, h, Tn, H, t0, nv, pl);
+        const size_t cb = chunk_base(b, h, Tn, H, c);
+        const int nv = chunk_len(Tn, c);
+        TL.load(sm.kt[slot], kp + cb, nv);
+        if (need_q(c)) TL.load(sm.qt[slot], qp + cb, nv);
     };
     auto load_v = [&](int c, int slot) {
-        load_tile<T>(sm.vt[slot], vp, b, h, Tn, H, c * kChunk, chunk_len(Tn, c), pl);
+        TL.load(sm.vt[slot], vp + chunk_base(b, h, Tn, H, c), chunk_len(Tn, c));
     };
     auto load_gb = [&](int c, float& gv, float& bv) {
         load_gate_beta(gp, bp, Tn, H, b, h, c, L.lane, gv, bv);
