@@ -503,11 +503,21 @@ __device__ __forceinline__ void block_solve(const Lane<T>& L, const T* t00, cons
 template <typename T>
 __device__ __forceinline__ void kt_update(const Lane<T>& L, const T* kt, f32x16* Hm, float a,
                                           const typename FragOf<T>::type* bf) {
+    // software-pipelined over the 16 (ht, ks) steps: the transposed fragment of
+    // the next step is requested before the product of the current one
+    using F = typename FragOf<T>::type;
+    F cur = L.trK(kt, 0, 0);
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
         f32x16 acc = Hm[ht] * a;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mma(L.trK(kt, ht, ks), bf[ks], acc);
+        for (int ks = 0; ks < 4; ++ks) {
+            const int nx = 4 * ht + ks + 1;
+            F nxt;
+            if (nx < 16) nxt = L.trK(kt, nx >> 2, nx & 3);
+            acc = mma(cur, bf[ks], acc);
+            if (nx < 16) cur = nxt;
+        }
         Hm[ht] = acc;
     }
 }

@@ -132,16 +132,41 @@ __device__ __forceinline__ void chunk_state(T* o, int Tn, int H, float scale, co
     f32x16 OT[2] = {zero16(), zero16()};   // (Q H)^T: lane = position, registers = dv
     X[0] = zero16();
     X[1] = zero16();
+    // software-pipelined: the LDS fragments of k-step ks+1 are requested before
+    // the products of k-step ks are issued
+    F ka[2], qa[2];
+    ka[0] = L.f128(kt, 0, 0);
+    ka[1] = L.f128(kt, 1, 0);
+    if (MODE == MODE_FULL && emit) {
+        qa[0] = L.f128(qt, 0, 0);
+        qa[1] = L.f128(qt, 1, 0);
+    }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-        // the state fragment of this k-step is converted right before use (keeps
-        // one fragment live instead of eight)
+        F kn[2], qn[2];
+        if (ks + 1 < 8) {
+            kn[0] = L.f128(kt, 0, ks + 1);
+            kn[1] = L.f128(kt, 1, ks + 1);
+            if (MODE == MODE_FULL && emit) {
+                qn[0] = L.f128(qt, 0, ks + 1);
+                qn[1] = L.f128(qt, 1, ks + 1);
+            }
+        }
+        // the state fragment of this k-step is converted right before use
         const F hf = acc_frag<T>(Hs[ks >> 1], ks & 1);
-        X[0] = mma(L.f128(kt, 0, ks), hf, X[0]);
-        X[1] = mma(L.f128(kt, 1, ks), hf, X[1]);
+        X[0] = mma(ka[0], hf, X[0]);
+        X[1] = mma(ka[1], hf, X[1]);
         if (MODE == MODE_FULL && emit) {
-            OT[0] = mma(hf, L.f128(qt, 0, ks), OT[0]);
-            OT[1] = mma(hf, L.f128(qt, 1, ks), OT[1]);
+            OT[0] = mma(hf, qa[0], OT[0]);
+            OT[1] = mma(hf, qa[1], OT[1]);
+        }
+        if (ks + 1 < 8) {
+            ka[0] = kn[0];
+            ka[1] = kn[1];
+            if (MODE == MODE_FULL && emit) {
+                qa[0] = qn[0];
+                qa[1] = qn[1];
+            }
         }
     }
     // Y = V - diag(Gamma) X (V in accumulator layout via the transposing read)
