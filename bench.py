@@ -4,7 +4,7 @@
 Workload: B=1, T=32768, H=32, dk=dv=128, bf16 q/k/v/o, fp32 g and beta,
 zero initial state, final state returned (seeded synthetic inputs, resident in
 HBM before the timed region).  One step = one gdn_chunk_fwd call (gate scan,
-every forward launch and the segment combine).
+segment planner and the fused forward launch).
 
 Prints one JSON line with tokens/s, the roofline of the fused forward kernel
 (algorithmic bytes over its HIP-event-timed launch durations, against the
@@ -41,9 +41,10 @@ STATE_BYTES = 128 * 128 * 4
 # was taken from
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gdn_fwd_kernel_bf16_t32768_h32_traffic.txt")
 KERNEL_SOURCES = ["gated_deltanet_chunked_prefill_amd/csrc/gdn_fwd.hip",
+                  "gated_deltanet_chunked_prefill_amd/csrc/gdn_chunk.h",
                   "gated_deltanet_chunked_prefill_amd/csrc/gdn_device.h",
                   "gated_deltanet_chunked_prefill_amd/csrc/gdn_internal.h"]
-FWD_KERNEL = "gdn_fwd_kernel"
+FWD_KERNEL = "gdn_fwd_"   # gdn_fwd_kernel (unsplit) and gdn_fwd_queue_kernel (split)
 CALIB_KERNEL = "neg_kernel"
 
 
@@ -245,7 +246,6 @@ def main():
     o = torch.empty_like(v)
     ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     ws = torch.empty(max(1, gdn.gdn_chunk_fwd_workspace_size(B, T, H)), dtype=torch.uint8, device=dev)
-    P = gdn.gdn_plan_segments(B, T, H, torch.cuda.get_device_properties(dev).multi_processor_count)
 
     def step():
         gdn.gdn_chunk_fwd(q, k, v, g, beta, None, out=o, out_ht=ht, workspace=ws)
@@ -253,6 +253,9 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    plan = gdn.gdn_chunk_fwd_plan_info(B, T, H, workspace=ws)
+    if plan["error"]:
+        raise SystemExit("bench.py: the split forward reported a failed wait; outputs are invalid")
 
     lib = _lib.load()
     cap = 8 * args.steps
@@ -274,9 +277,9 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tokens_per_s = B * T / (ms_per_step * 1e-3)
     nbytes = algorithmic_bytes(B, T, H, False, True)
-    # the fused forward kernel: its launches of one call together read every input
-    # and write every output (the combine and gate scan move only workspace data)
-    fwd_kinds = [kd for kd in ("fwd_single", "fwd_pass_a", "fwd_pass_c") if kd in per_kind]
+    # the fused forward kernel reads every input and writes every output (the gate
+    # scan and the planner move only g and workspace data)
+    fwd_kinds = [kd for kd in ("fwd_single", "fwd_queue") if kd in per_kind]
     fwd_ms = sum(float(np.mean(per_kind[kd])) for kd in fwd_kinds)
     achieved = nbytes / (fwd_ms * 1e-3) / 1e9
     kernel_ms = {kd: round(float(np.mean(t)), 4) for kd, t in per_kind.items()}
@@ -297,8 +300,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
-                   "segments_per_head": P, "h0": False, "ht": True},
-        "roofline": {"bound": "hbm", "kernel": "gdn_fwd_kernel (" + "+".join(fwd_kinds) + ")",
+                   "h0": False, "ht": True,
+                   "plan": {k: plan[k] for k in ("P_exact", "P_window", "n_exact", "n_window", "n_jobs")}},
+        "roofline": {"bound": "hbm", "kernel": "+".join(fwd_kinds),
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": nbytes,

@@ -22,7 +22,7 @@ from . import _lib
 
 DEFAULT_LOG_EPS = math.log(2.0 ** -24)
 
-__all__ = ["gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_gate_scan", "gdn_plan_segments",
+__all__ = ["gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_gate_scan", "gdn_plan_segments", "gdn_chunk_fwd_plan_info",
            "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd_workspace_size", "options"]
 
 
@@ -133,6 +133,19 @@ def gdn_chunk_fwd(q, k, v, g, beta, h0=None, scale=1.0, *, output_final_state=Tr
                                  _ptr(o), _ptr(ht), B, T, H, dk, dv, code, float(scale),
                                  ctypes.byref(opt), _ptr(workspace), wsz, _stream(q.device)))
     return o, ht
+
+
+def gdn_chunk_fwd_plan_info(B, T, H, workspace=None, device=None, **opts) -> dict:
+    """The plan the last split forward with these shapes, options and workspace
+    used (synchronises the device's current stream)."""
+    lib = _lib.load()
+    info = (ctypes.c_int32 * 8)()
+    opt = options(**opts)
+    dev = workspace.device if workspace is not None else device
+    _lib.check(lib.gdn_chunk_fwd_plan_info(int(B), int(T), int(H), ctypes.byref(opt), _ptr(workspace),
+                                           info, _stream(dev) if dev is not None else None))
+    keys = ("P_exact", "P_window", "n_exact", "n_window", "n_jobs", "handed_out", "error")
+    return dict(zip(keys, list(info)[:7]))
 
 
 def gdn_chunk_bwd(q, k, v, g, beta, dout, h0=None, dht=None, scale=1.0, *, workspace=None,

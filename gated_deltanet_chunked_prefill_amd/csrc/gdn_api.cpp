@@ -95,23 +95,24 @@ gdn_status check_shapes(int B, int T, int H, int dk, int dv, gdn_dtype dt) {
 
 int num_chunks(int T) { return (T + kChunk - 1) / kChunk; }
 
+// Segment slots per head: 1 = no split.  In the automatic mode this is the
+// most segments the device-side planner may give a head (talk summary,
+// paragraph 8: a square-root rule on the chunk count bounds the split); the
+// planner picks the counts per call from the number of exact and window heads.
 int plan(int B, int T, int H, int num_cus, const gdn_options& o) {
     const int N = num_chunks(T);
     if (o.split_mode == 1) return 1;
     if (o.split_mode == 2) return o.n_segments < N ? o.n_segments : N;
-    // automatic (talk summary, paragraph 8: a square-root rule on the chunk count)
     const long long heads = (long long)B * H;
     if (heads * 2 >= num_cus || N < 2 * o.window_chunks) return 1;
-    long long p = (num_cus + heads - 1) / heads;
-    long long r = (long long)std::floor(std::sqrt((double)N));
-    long long c = N / (2 * o.window_chunks);
-    if (r < p) p = r;
-    if (c < p) p = c;
-    return p < 1 ? 1 : (int)p;
+    long long p = (long long)std::floor(std::sqrt((double)N));
+    if (p > 32) p = 32;
+    if (p > N / 2) p = N / 2;
+    return p < 2 ? 1 : (int)p;
 }
 
 struct FwdLayout {
-    size_t chunk_sums, flags, maxwin, hs, bz, mt, gsum, total;
+    size_t chunk_sums, flags, maxwin, hs, hs_cnt, plan, jobs, total;
 };
 
 FwdLayout fwd_layout(int B, int T, int H, int P) {
@@ -123,9 +124,9 @@ FwdLayout fwd_layout(int B, int T, int H, int P) {
     L.flags = off;      off += align_up(bh * sizeof(int32_t));
     L.maxwin = off;     off += align_up(bh * sizeof(float));
     L.hs = off;         off += align_up(bh * P * SS * sizeof(float));
-    L.bz = off;         off += align_up(bh * P * SS * sizeof(float));
-    L.mt = off;         off += align_up(bh * P * SS * sizeof(float));
-    L.gsum = off;       off += align_up(bh * P * sizeof(float));
+    L.hs_cnt = off;     off += align_up(bh * P * sizeof(int32_t));
+    L.plan = off;       off += align_up(sizeof(gdn::FwdPlan));
+    L.jobs = off;       off += align_up(bh * P * sizeof(gdn::TaskRec));
     L.total = off;
     return L;
 }
@@ -246,9 +247,11 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
     }
     char* ws = (char*)workspace;
     p.hs = (float*)(ws + L.hs);
-    p.bz = (float*)(ws + L.bz);
-    p.mt = (float*)(ws + L.mt);
-    p.gsum = (float*)(ws + L.gsum);
+    p.hs_cnt = (int*)(ws + L.hs_cnt);
+    p.plan = (gdn::FwdPlan*)(ws + L.plan);
+    p.jobs = (gdn::TaskRec*)(ws + L.jobs);
+    p.cus = cus;
+    p.forced = op.split_mode == 2 ? 1 : 0;
     if (op.use_window) {
         int32_t* flags = (int32_t*)(ws + L.flags);
         float* sums = (float*)(ws + L.chunk_sums);
@@ -261,14 +264,39 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
         if (e != hipSuccess) return hip_fail(e, "gate scan launch");
         p.flags = flags;
     }
-    e = recorded(GDN_LAUNCH_FWD_PASS_A, s, [&] { return gdn::launch_fwd(p, gdn::PHASE_A, bf16, s); });
-    if (e != hipSuccess) return hip_fail(e, "forward pass-1 launch");
-    if (P >= 3) {
-        e = recorded(GDN_LAUNCH_COMBINE, s, [&] { return gdn::launch_combine(p, s); });
-        if (e != hipSuccess) return hip_fail(e, "combine launch");
+    e = recorded(GDN_LAUNCH_FWD_PLAN, s, [&] { return gdn::launch_plan(p, s); });
+    if (e != hipSuccess) return hip_fail(e, "forward plan launch");
+    e = recorded(GDN_LAUNCH_FWD_QUEUE, s, [&] { return gdn::launch_fwd(p, gdn::PHASE_QUEUE, bf16, s); });
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+    return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd_plan_info(int B, int T, int H, const gdn_options* opt, const void* workspace,
+                                   int32_t* info, void* stream) {
+    g_err[0] = 0;
+    if (!info) return fail(GDN_ERR_INVALID_ARG, "info is required");
+    if (B <= 0 || T <= 0 || H <= 0)
+        return fail(GDN_ERR_INVALID_ARG, "B, T, H must be positive (got %d, %d, %d)", B, T, H);
+    gdn_options op = resolve(opt);
+    gdn_status st = check_options(op, num_chunks(T));
+    if (st != GDN_OK) return st;
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != GDN_OK) return st;
+    const int P = plan(B, T, H, cus, op);
+    if (P == 1) {
+        const int32_t whole[8] = {1, 1, B * H, 0, B * H, 0, 0, 0};
+        std::memcpy(info, whole, sizeof(whole));
+        return GDN_OK;
     }
-    e = recorded(GDN_LAUNCH_FWD_PASS_C, s, [&] { return gdn::launch_fwd(p, gdn::PHASE_C, bf16, s); });
-    if (e != hipSuccess) return hip_fail(e, "forward pass-3 launch");
+    if (!workspace) return fail(GDN_ERR_WORKSPACE, "the split forward's workspace is required");
+    const FwdLayout L = fwd_layout(B, T, H, P);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(info, (const char*)workspace + L.plan, sizeof(gdn::FwdPlan),
+                                  hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "plan read-back");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "plan read-back");
     return GDN_OK;
 }
 

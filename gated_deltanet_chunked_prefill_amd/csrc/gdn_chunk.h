@@ -36,6 +36,8 @@ struct Smem {
     float e_vec[NP][kChunk];   // Gamma_C / Gamma_r
     float gc[NP][4];           // [0] Gamma_C
     float pscr[4][4][kChunk];  // per prep wave: gamma, exp(gamma - gC/2), exp(gC/2 - gamma), beta
+    int islot[4];              // workgroup-wide scalars: [0] job index
+    float fslot[4];            // [0] exp(sum of g over a segment)
 };
 
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x3f70); }   // vmcnt(0)

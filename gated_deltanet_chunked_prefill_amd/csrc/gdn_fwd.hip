@@ -37,6 +37,22 @@
 //     Mt <- (I - K^T T0 diag(beta) K) Mt,
 // i.e. the same step on 128 extra columns with V = 0 and no gates.
 //
+// Split forward as a work queue.  A one-workgroup plan kernel reads the gate
+// flags, chooses the segment counts of exact and window heads from a cost
+// model and writes the job list; persistent workgroups (one per CU) then take
+// jobs from an atomic counter.  Per exact head with P segments the jobs are
+//   seg 0     full run from h0, publishes the state entering segment 1;
+//   seg p     (0 < p < P-1) pass-1 from zero, then the composition
+//             hs[p+1] = exp(G_p) Mt_p hs[p] + b_p once hs[p] is published, then
+//             the full run of segment p from hs[p];
+//   seg P-1   full run from hs[P-1] (waits for it), writes ht;
+// window heads (paragraph 5) get independent jobs that warm up over the w
+// chunks before their segment.  The list is ordered so that every job waits
+// only for jobs handed out before it (seg 0 jobs, middle segments in
+// increasing p, window jobs, last segments), so the waits end for any number
+// of resident workgroups.  A state crosses workgroups through HBM with an
+// agent-scope release by each producing wave and an acquire by the consumer.
+//
 // K^T and V in accumulator layout are read from the row-major tiles with the
 // transposing LDS read; O is produced transposed (O^T = H^T Q^T + V'^T P^T) so
 // each lane holds a row of O and writes it as 8-byte segments.
@@ -47,10 +63,12 @@ namespace gdn {
 
 namespace {
 
-enum { INIT_ZERO = 0, INIT_H0 = 1, INIT_HS = 2 };
-enum { DST_NONE = 0, DST_HT = 1, DST_HS_NEXT = 2, DST_PASS1 = 3 };
+enum { INIT_ZERO = 0, INIT_H0 = 1, INIT_HS = 2, INIT_HS_WAIT = 3 };
+enum { DST_NONE = 0, DST_HT = 1, DST_HS_NEXT = 2, DST_COMPOSE = 3 };
 
 constexpr int kThreads = 512;   // 4 state waves + 4 prep waves
+constexpr int kMtStride = kDk + 4;   // float row stride of a segment transition staged in LDS
+constexpr int kSpinLimit = 1 << 22;  // polls of about 1 us: seconds, far beyond any real wait
 
 struct Task {
     int bh, seg;
@@ -58,65 +76,95 @@ struct Task {
     int mode, init, dst;
 };
 
-__device__ __forceinline__ int seg_start(int p, int N, int P) { return (int)(((long long)p * N) / P); }
-
-// Decode the task of this workgroup.  Returns false when it has nothing to do.
-__device__ bool decode_task(const FwdParams& prm, int phase, Task& t) {
-    const int P = prm.P;
-    if (phase == PHASE_SINGLE || phase == PHASE_STATES) {
-        t.bh = blockIdx.x;
-        t.seg = 0;
-        t.c_begin = 0;
-        t.c_out = 0;
-        t.c_end = prm.N;
-        t.mode = MODE_FULL;
-        t.init = prm.h0 ? INIT_H0 : INIT_ZERO;
-        t.dst = prm.ht ? DST_HT : DST_NONE;
-        return true;
-    }
-    if (phase == PHASE_A) {
-        t.bh = blockIdx.x / P;
-        t.seg = blockIdx.x % P;
-    } else {
-        t.bh = blockIdx.x / (P - 1);
-        t.seg = 1 + blockIdx.x % (P - 1);
-    }
-    const int p = t.seg;
-    const bool window = prm.flags && prm.flags[t.bh] != 0;
-    const int s = seg_start(p, prm.N, P), e = seg_start(p + 1, prm.N, P);
-    t.c_out = s;
-    t.c_end = e;
-    if (window) {
-        // sliding-window head (paragraph 5): warm up over the w chunks before s
-        if (phase != PHASE_A) return false;
-        t.c_begin = s - prm.w > 0 ? s - prm.w : 0;
-        t.mode = MODE_FULL;
-        t.init = (t.c_begin == 0 && prm.h0) ? INIT_H0 : INIT_ZERO;
-        t.dst = (p == P - 1 && prm.ht) ? DST_HT : DST_NONE;
-        return true;
-    }
-    if (phase == PHASE_A) {
-        if (p == 0) {
-            t.c_begin = 0;
-            t.mode = MODE_FULL;
-            t.init = prm.h0 ? INIT_H0 : INIT_ZERO;
-            t.dst = DST_HS_NEXT;
-            return true;
-        }
-        if (p == P - 1) return false;
-        t.c_begin = s;
-        t.c_out = e;  // no outputs
-        t.mode = MODE_PASS1;
-        t.init = INIT_ZERO;
-        t.dst = DST_PASS1;
-        return true;
-    }
-    // PHASE_C: exact head, segment p >= 1 from its true entering state
-    t.c_begin = s;
+// The unsplit launches: workgroup = head, the whole sequence.
+__device__ void whole_head_task(const FwdParams& prm, Task& t) {
+    t.bh = blockIdx.x;
+    t.seg = 0;
+    t.c_begin = 0;
+    t.c_out = 0;
+    t.c_end = prm.N;
     t.mode = MODE_FULL;
-    t.init = INIT_HS;
-    t.dst = (p == P - 1 && prm.ht) ? DST_HT : DST_NONE;
-    return true;
+    t.init = prm.h0 ? INIT_H0 : INIT_ZERO;
+    t.dst = prm.ht ? DST_HT : DST_NONE;
+}
+
+// Make this wave's global stores visible device-wide, then count the wave in.
+__device__ __forceinline__ void publish(int* cnt) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until `target` waves have published (bounded: on running out the plan's
+// error flag is raised and the wait ends).
+__device__ __forceinline__ void wait_published(const int* cnt, int target, int* error) {
+    for (int spin = 0;; ++spin) {
+        const int v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (uni(v) >= target) break;
+        if (spin >= kSpinLimit) {
+            if ((threadIdx.x & 63) == 0) __hip_atomic_store(error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// acc += a b for float operands: exact float32 products in the float32 build;
+// in the bf16 build three bf16 products of the hi/lo split (a_hi b_hi + a_hi b_lo
+// + a_lo b_hi), close to float32 accuracy.
+template <typename T>
+__device__ __forceinline__ f32x16 mma_f32(const f32x8& a, const f32x8& b, f32x16 acc) {
+    if constexpr (sizeof(T) == 4) {
+        return mma(a, b, acc);
+    } else {
+        bf16x8 ah, al, bh, bl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            ah[j] = (__bf16)a[j];
+            al[j] = (__bf16)(a[j] - (float)ah[j]);
+            bh[j] = (__bf16)b[j];
+            bl[j] = (__bf16)(b[j] - (float)bh[j]);
+        }
+        acc = mma(ah, bh, acc);
+        acc = mma(ah, bl, acc);
+        return mma(al, bh, acc);
+    }
+}
+
+// State wave w's 32 columns of the state entering the next segment (talk
+// summary, paragraph 4: a segment maps its entering state H to
+// exp(G) Mt H + b, with Mt gate-free and b the segment's run from zero):
+//     out = eG * Mt * hin + bz,
+// Mt row-major float in LDS (row stride kMtStride), hin and out in HBM, bz in
+// accumulator layout.
+template <typename T>
+__device__ __forceinline__ void compose_next(const float* mtl, float eG, const float* hin, float* out,
+                                             int w, int lane, const f32x16* bz) {
+    const int n = lane & 31, g = lane >> 5;
+    f32x16 hp[4];
+    load_state(hin, w, lane, hp);
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+        f32x16 acc = zero16();
+        const float* row = mtl + (32 * ht + n) * kMtStride + 4 * g;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(row + 16 * ks);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(row + 16 * ks + 8);
+            f32x8 a, b;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                a[j] = lo[j];
+                a[4 + j] = hi[j];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) b[j] = hp[ks >> 1][8 * (ks & 1) + j];
+            acc = mma_f32<T>(a, b, acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            out[(32 * ht + rho(g, r)) * kDv + 32 * w + n] = eG * acc[r] + bz[ht][r];
+    }
 }
 
 // The serial state step of one chunk for state wave w (its 32 state columns).
@@ -263,10 +311,12 @@ __device__ __noinline__ void state_loop(const FwdParams& prm, Smem<T>& sm, const
     Lane<T> L;
     L.init(threadIdx.x);
     f32x16 Hs[4];
+    const size_t slot = (size_t)bh * P + seg;   // this segment's state slot
     if (init == INIT_H0) {
         load_state(uni(prm.h0) + (size_t)bh * SS, L.w, L.lane, Hs);
-    } else if (init == INIT_HS) {
-        load_state(uni(prm.hs) + ((size_t)bh * P + seg) * SS, L.w, L.lane, Hs);
+    } else if (init == INIT_HS || init == INIT_HS_WAIT) {
+        if (init == INIT_HS_WAIT) wait_published(uni(prm.hs_cnt) + slot, 4, &uni(prm.plan)->error);
+        load_state(uni(prm.hs) + slot * SS, L.w, L.lane, Hs);
     } else {
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) Hs[ht] = zero16();
@@ -305,9 +355,18 @@ __device__ __noinline__ void state_loop(const FwdParams& prm, Smem<T>& sm, const
     if (dst == DST_HT) {
         store_state(uni(prm.ht) + (size_t)bh * SS, L.w, L.lane, Hs);
     } else if (dst == DST_HS_NEXT) {
-        store_state(uni(prm.hs) + ((size_t)bh * P + seg + 1) * SS, L.w, L.lane, Hs);
-    } else if (dst == DST_PASS1) {
-        store_state(uni(prm.bz) + ((size_t)bh * P + seg) * SS, L.w, L.lane, Hs);
+        store_state(uni(prm.hs) + (slot + 1) * SS, L.w, L.lane, Hs);
+        publish(uni(prm.hs_cnt) + slot + 1);
+    } else if (dst == DST_COMPOSE) {
+        // Hs is this segment's run from zero; the prep waves stage Mt and exp(G)
+        lds_barrier();   // done with the chunk tiles
+        lds_barrier();   // Mt in LDS
+        wait_published(uni(prm.hs_cnt) + slot, 4, &uni(prm.plan)->error);
+        float* const hs = uni(prm.hs);
+        compose_next<T>(reinterpret_cast<const float*>(&sm.kt[0][0]), sm.fslot[0], hs + slot * SS,
+                        hs + (slot + 1) * SS, L.w, L.lane, Hs);
+        publish(uni(prm.hs_cnt) + slot + 1);
+        lds_barrier();   // Mt no longer needed
     }
 }
 
@@ -321,9 +380,9 @@ __device__ __noinline__ void prep_loop(const FwdParams& prm, Smem<T>& sm, const 
     constexpr bool kPipe = Pipe<T>::on;
     const int pw = wave_id() - 4;
     // every parameter read once, into scalar registers
-    const int bh = uni(tk.bh), seg = uni(tk.seg), c_begin = uni(tk.c_begin), c_out = uni(tk.c_out);
+    const int bh = uni(tk.bh), c_begin = uni(tk.c_begin), c_out = uni(tk.c_out);
     const int c_end = uni(tk.c_end), dst = uni(tk.dst);
-    const int Tn = uni(prm.T), H = uni(prm.H), P = uni(prm.P);
+    const int Tn = uni(prm.T), H = uni(prm.H);
     const T* const kp = uni((const T*)prm.k);
     const T* const qp = uni((const T*)prm.q);
     const T* const vp = uni((const T*)prm.v);
@@ -407,9 +466,17 @@ __device__ __noinline__ void prep_loop(const FwdParams& prm, Smem<T>& sm, const 
             if (MODE == MODE_PASS1) mt_step<T>(L, sm.kt[0], sm.t32[0], Ms);
         }
     }
-    if (dst == DST_PASS1) {
-        store_state(uni(prm.mt) + ((size_t)bh * P + seg) * (size_t)(kDk * kDv), L.w, L.lane, Ms);
-        if (pw == 3 && L.lane == 0) uni(prm.gsum)[(size_t)bh * P + seg] = gsum;
+    if (dst == DST_COMPOSE) {
+        lds_barrier();   // the state waves are done with the chunk tiles
+        float* const mtl = reinterpret_cast<float*>(&sm.kt[0][0]);
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                mtl[(32 * ht + rho(L.g, r)) * kMtStride + 32 * L.w + L.n] = Ms[ht][r];
+        if (pw == 3 && L.lane == 0) sm.fslot[0] = __expf(gsum);
+        lds_barrier();   // Mt in LDS
+        lds_barrier();   // the state waves have composed
     }
 }
 
@@ -429,42 +496,221 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_kernel(FwdParams prm) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     Smem<T>& sm = *reinterpret_cast<Smem<T>*>(smem_raw);
     Task tk;
-    if (!decode_task(prm, PHASE, tk)) return;
-    // only the first launch of a split forward has pass-1 tasks
-    if (PHASE == PHASE_A && tk.mode == MODE_PASS1)
-        run_task<T, MODE_PASS1>(prm, sm, tk);
-    else if (PHASE == PHASE_STATES)
+    whole_head_task(prm, tk);
+    if (PHASE == PHASE_STATES)
         run_task<T, MODE_FULL, true>(prm, sm, tk);
     else
         run_task<T, MODE_FULL>(prm, sm, tk);
 }
 
+// Persistent workgroups of the split forward: take jobs until the list is empty.
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void gdn_fwd_queue_kernel(FwdParams prm) {
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    Smem<T>& sm = *reinterpret_cast<Smem<T>*>(smem_raw);
+    const int n_jobs = uni(prm.plan->n_jobs);
+    for (;;) {
+        if (threadIdx.x == 0) sm.islot[0] = atomicAdd(&prm.plan->next, 1);
+        __syncthreads();
+        const int j = uni(sm.islot[0]);
+        __syncthreads();
+        if (j >= n_jobs) break;
+        const TaskRec rec = prm.jobs[j];
+        Task tk{rec.bh, rec.seg, rec.c_begin, rec.c_out, rec.c_end, rec.mode, rec.init, rec.dst};
+        if (tk.mode == MODE_PASS1) {
+            // middle segment of an exact head: pass-1 and composition, then the
+            // segment's outputs from its true entering state
+            run_task<T, MODE_PASS1>(prm, sm, tk);
+            tk.mode = MODE_FULL;
+            tk.c_out = tk.c_begin;
+            tk.init = INIT_HS;
+            tk.dst = DST_NONE;
+        }
+        run_task<T, MODE_FULL>(prm, sm, tk);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Planner of the split forward (one workgroup).
+//
+// Cost model, in units of one fused chunk step: a pass-1 step costs kCostPass1,
+// one link of the state chain of an exact head kCostLink.  An exact head with
+// P >= 3 segments keeps P - 1 workgroups busy for about
+//     L (1 + kCostPass1) + (P - 2) kCostLink,   L = 8 N / (kSeg0Weight + 8 (P - 1)),
+// where segment 0 (which only runs full steps and later takes the last
+// segment) is kSeg0Weight / 8 times as long as the others.  The remaining
+// workgroups share the window heads' segments, each costing N / P_w + w.  The
+// planner takes the P (and P_w) with the smallest estimated makespan.
+constexpr float kCostPass1 = 1.4f;
+constexpr float kCostLink = 1.0f;
+constexpr int kSeg0Weight = 11;
+
+__device__ int exact_bound(int p, int P, int N, int w0) {
+    if (p <= 0) return 0;
+    if (p >= P) return N;
+    return (int)(((long long)N * (w0 + 8 * (p - 1))) / (w0 + 8 * (P - 1)));
+}
+
+__device__ void choose_segments(int n_e, int n_w, int N, int w, int cus, int pmax, int& Pe, int& Pw) {
+    float best = 3.0e38f;
+    Pe = 1;
+    Pw = 1;
+    const int pw_cap = N / w > 1 ? N / w : 1;
+    for (int P = 1; P <= (n_e > 0 ? pmax : 1); ++P) {
+        if (P == 2) continue;   // two segments only serialise
+        const int ecus = n_e * (P == 1 ? 1 : P - 1);
+        if (P > 1 && ecus > cus) break;
+        float te = 0.f;
+        if (n_e > 0)
+            te = P == 1 ? (float)N
+                        : 8.f * N * (1.f + kCostPass1) / (kSeg0Weight + 8 * (P - 1)) + (P - 2) * kCostLink;
+        const int free = cus - ecus > 0 ? cus - ecus : 0;
+        int pw = 1;
+        float tw = 0.f;
+        if (n_w > 0) {
+            if (free >= n_w) {
+                pw = free / n_w;
+                if (pw > pmax) pw = pmax;
+                if (pw > pw_cap) pw = pw_cap;
+                tw = (float)N / pw + (pw > 1 ? w : 0);
+            } else if (free > 0) {
+                tw = (float)((n_w + free - 1) / free) * N;
+            } else {
+                tw = te + N;
+            }
+        }
+        const float t = te > tw ? te : tw;
+        if (t < best * 0.999f) {
+            best = t;
+            Pe = P;
+            Pw = pw;
+        }
+    }
+}
+
+__device__ __forceinline__ void put_job(TaskRec* jobs, int j, int bh, int seg, int cb, int co, int ce,
+                                        int mode, int init, int dst) {
+    TaskRec r;
+    r.bh = bh; r.seg = seg; r.c_begin = cb; r.c_out = co; r.c_end = ce;
+    r.mode = mode; r.init = init; r.dst = dst;
+    jobs[j] = r;
+}
+
+__global__ __launch_bounds__(256) void plan_kernel(FwdParams prm) {
+    __shared__ int s_rank[256];
+    __shared__ int s_par[4];
+    const int tid = threadIdx.x;
+    const int nbh = prm.B * prm.H, N = prm.N, pmax = prm.P, w = prm.w;
+    const int per = (nbh + 255) / 256;
+    const int lo = tid * per < nbh ? tid * per : nbh;
+    const int hi = lo + per < nbh ? lo + per : nbh;
+    auto exact = [&](int bh) { return prm.flags == nullptr || prm.flags[bh] == 0; };
+    int ne = 0;
+    for (int bh = lo; bh < hi; ++bh) ne += exact(bh) ? 1 : 0;
+    s_rank[tid] = ne;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int i = 0; i < 256; ++i) {
+            const int c = s_rank[i];
+            s_rank[i] = run;
+            run += c;
+        }
+        const int n_e = run, n_w = nbh - run;
+        int Pe = pmax, Pw = pmax;
+        if (!prm.forced) choose_segments(n_e, n_w, N, w, prm.cus, pmax, Pe, Pw);
+        s_par[0] = n_e;
+        s_par[1] = n_w;
+        s_par[2] = Pe;
+        s_par[3] = Pw;
+        FwdPlan* pl = prm.plan;
+        pl->P_e = Pe;
+        pl->P_w = Pw;
+        pl->n_exact = n_e;
+        pl->n_window = n_w;
+        pl->n_jobs = n_e * Pe + n_w * Pw;
+        pl->next = 0;
+        pl->error = 0;
+    }
+    __syncthreads();
+    const int n_e = s_par[0], n_w = s_par[1], Pe = s_par[2], Pw = s_par[3];
+    // job groups: [seg 0 of exact heads][middle segments, p-major][window jobs][last segments]
+    const int g_mid = n_e, g_win = n_e + n_e * (Pe > 2 ? Pe - 2 : 0), g_last = g_win + n_w * Pw;
+    const int w0 = prm.forced ? 8 : kSeg0Weight;
+    const bool has_h0 = prm.h0 != nullptr, has_ht = prm.ht != nullptr;
+    int re = s_rank[tid], rw = lo - s_rank[tid];
+    for (int bh = lo; bh < hi; ++bh) {
+        if (exact(bh)) {
+            const int init0 = has_h0 ? INIT_H0 : INIT_ZERO;
+            if (Pe == 1) {
+                put_job(prm.jobs, re, bh, 0, 0, 0, N, MODE_FULL, init0, has_ht ? DST_HT : DST_NONE);
+            } else {
+                put_job(prm.jobs, re, bh, 0, 0, 0, exact_bound(1, Pe, N, w0), MODE_FULL, init0, DST_HS_NEXT);
+                for (int p = 1; p + 1 < Pe; ++p) {
+                    const int cb = exact_bound(p, Pe, N, w0), ce = exact_bound(p + 1, Pe, N, w0);
+                    put_job(prm.jobs, g_mid + (p - 1) * n_e + re, bh, p, cb, ce, ce, MODE_PASS1, INIT_ZERO,
+                            DST_COMPOSE);
+                }
+                const int cb = exact_bound(Pe - 1, Pe, N, w0);
+                put_job(prm.jobs, g_last + re, bh, Pe - 1, cb, cb, N, MODE_FULL, INIT_HS_WAIT,
+                        has_ht ? DST_HT : DST_NONE);
+            }
+            ++re;
+        } else {
+            for (int p = 0; p < Pw; ++p) {
+                const int s = (int)(((long long)p * N) / Pw), e = (int)(((long long)(p + 1) * N) / Pw);
+                const int cb = s - w > 0 ? s - w : 0;
+                put_job(prm.jobs, g_win + p * n_w + rw, bh, p, cb, s, e, MODE_FULL,
+                        (cb == 0 && has_h0) ? INIT_H0 : INIT_ZERO,
+                        (p == Pw - 1 && has_ht) ? DST_HT : DST_NONE);
+            }
+            ++rw;
+        }
+    }
+    for (int i = tid; i < nbh * pmax; i += 256) prm.hs_cnt[i] = 0;
+}
+
+template <typename K>
+hipError_t set_lds(K kernel, size_t lds) {
+    return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
 template <typename T, int PHASE>
-hipError_t launch_phase(const FwdParams& p, int grid, hipStream_t s) {
+hipError_t launch_phase(const FwdParams& p, hipStream_t s) {
     const size_t lds = sizeof(Smem<T>);
     static bool configured = false;
     if (!configured) {
-        hipError_t e = hipFuncSetAttribute((const void*)gdn_fwd_kernel<T, PHASE>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e;
+        if constexpr (PHASE == PHASE_QUEUE)
+            e = set_lds(gdn_fwd_queue_kernel<T>, lds);
+        else
+            e = set_lds(gdn_fwd_kernel<T, PHASE>, lds);
         if (e != hipSuccess) return e;
         configured = true;
     }
-    hipLaunchKernelGGL((gdn_fwd_kernel<T, PHASE>), dim3(grid), dim3(kThreads), lds, s, p);
+    if constexpr (PHASE == PHASE_QUEUE)
+        hipLaunchKernelGGL((gdn_fwd_queue_kernel<T>), dim3(p.cus), dim3(kThreads), lds, s, p);
+    else
+        hipLaunchKernelGGL((gdn_fwd_kernel<T, PHASE>), dim3(p.B * p.H), dim3(kThreads), lds, s, p);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_fwd_t(const FwdParams& p, int phase, hipStream_t s) {
-    if (phase == PHASE_SINGLE) return launch_phase<T, PHASE_SINGLE>(p, p.B * p.H, s);
-    if (phase == PHASE_STATES) return launch_phase<T, PHASE_STATES>(p, p.B * p.H, s);
-    if (phase == PHASE_A) return launch_phase<T, PHASE_A>(p, p.B * p.H * p.P, s);
-    return launch_phase<T, PHASE_C>(p, p.B * p.H * (p.P - 1), s);
+    if (phase == PHASE_SINGLE) return launch_phase<T, PHASE_SINGLE>(p, s);
+    if (phase == PHASE_STATES) return launch_phase<T, PHASE_STATES>(p, s);
+    return launch_phase<T, PHASE_QUEUE>(p, s);
 }
 
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p, int phase, bool bf16, hipStream_t s) {
     return bf16 ? launch_fwd_t<__bf16>(p, phase, s) : launch_fwd_t<float>(p, phase, s);
+}
+
+hipError_t launch_plan(const FwdParams& p, hipStream_t s) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p);
+    return hipGetLastError();
 }
 
 }  // namespace gdn

@@ -6,15 +6,32 @@
 
 namespace gdn {
 
-// Workspace of the split forward, per head bh = b*H + h and segment p
-// (all float32, 256-byte aligned sub-buffers):
+// Workspace of the split forward, per head bh = b*H + h and segment slot p < P
+// (P = the largest segment count the call may use; 256-byte aligned sub-buffers):
 //   chunk_sums [B, N, H]          gate scan scratch
 //   flags      [B*H] int32        1 = window head
 //   maxwin     [B*H]              max window log-decay
-//   hs         [B*H, P, dk, dv]   true state entering segment p (p >= 1)
-//   bz         [B*H, P, dk, dv]   final state of segment p run from zero
-//   mt         [B*H, P, dk, dk]   gate-free segment transition (prod of I - K^T T0 diag(beta) K)
-//   gsum       [B*H, P]           sum of g over segment p
+//   hs         [B*H, P, dk, dv]   true state entering segment p (p >= 1) of an exact head
+//   hs_cnt     [B*H, P] int32     number of state waves that have published hs[bh, p]
+//   plan       FwdPlan            segment counts, job count, job counter
+//   jobs       [B*H*P] TaskRec    the work queue of the split forward
+//
+// A job is one run of the fused chunk loop over chunks [c_begin, c_end) of head
+// bh, with outputs from chunk c_out on.  mode = pass-1 marks the middle
+// segments of an exact head: the run from a zero state is followed, in the same
+// job, by the composition of the true state and the run that writes outputs.
+struct TaskRec {
+    int bh, seg, c_begin, c_out, c_end, mode, init, dst;
+};
+struct FwdPlan {
+    int P_e, P_w;      // segments of an exact head / of a window head
+    int n_exact, n_window;
+    int n_jobs;
+    int next;          // next job to hand out (atomic counter)
+    int error;         // set when a wait for another job's state ran out (never expected)
+    int pad;
+};
+
 struct FwdParams {
     const void* q;
     const void* k;
@@ -25,23 +42,27 @@ struct FwdParams {
     void* o;
     float* ht;         // nullable
     int B, T, H, N;    // N = number of 64-token chunks
-    int P;             // segments per head (1 = no split)
+    int P;             // segment slots per head (1 = no split)
     int w;             // window length in chunks
     float scale;
     const int32_t* flags;  // nullable: all heads exact
     float* hs;
-    float* bz;
-    float* mt;
-    float* gsum;
+    int* hs_cnt;
     float* hstore;     // nullable: [B*H, N+1, dk, dv] state entering each chunk, then the final state
+    FwdPlan* plan;     // split forward: written by the plan kernel
+    TaskRec* jobs;
+    int cus;           // compute units of the device
+    int forced;        // 1: every head uses exactly P segments of equal length
 };
 
+// PHASE_SINGLE: one workgroup per head, the whole sequence.
+// PHASE_QUEUE: persistent workgroups running the jobs of the split forward.
 // PHASE_STATES: the unsplit forward that only stores the state entering every
 // chunk (into hstore), for the backward.
-enum FwdPhase { PHASE_SINGLE = 0, PHASE_A = 1, PHASE_C = 2, PHASE_STATES = 3 };
+enum FwdPhase { PHASE_SINGLE = 0, PHASE_QUEUE = 1, PHASE_STATES = 2 };
 
 hipError_t launch_fwd(const FwdParams& p, int phase, bool bf16, hipStream_t s);
-hipError_t launch_combine(const FwdParams& p, hipStream_t s);
+hipError_t launch_plan(const FwdParams& p, hipStream_t s);
 hipError_t launch_chunk_sums(const float* g, int B, int T, int H, float* chunk_sums, hipStream_t s);
 hipError_t launch_window_flags(const float* chunk_sums, int B, int T, int H, int w, float log_eps,
                                int32_t* flags, float* maxwin, hipStream_t s);

@@ -84,10 +84,24 @@ typedef struct {
  * log_eps = log(2^-24). */
 void gdn_default_options(gdn_options* opt);
 
-/* Number of sequence segments per head the forward will use for these shapes on
- * a device with num_cus compute units (the host-side planner; no device access).
- * Returns 1 when no split is made, or 0 for invalid arguments. */
+/* Segment slots per head of the forward for these shapes on a device with
+ * num_cus compute units (the host-side planner; no device access): 1 when the
+ * sequence is not split; n_segments (at most the chunk count) when
+ * split_mode == 2; otherwise the most segments the device-side planner may give
+ * a head, min(32, floor(sqrt(N)), N/2) for N chunks.  That planner reads the
+ * window flags and picks the counts of exact and window heads per call (see
+ * gdn_chunk_fwd_plan_info).  Returns 0 for invalid arguments. */
 int gdn_plan_segments(int B, int T, int H, int num_cus, const gdn_options* opt);
+
+/* Read back the plan the last split forward with these shapes, options and
+ * workspace used (synchronises `stream`).  info[0..7]: segments of an exact
+ * head, segments of a window head, number of exact heads, number of window
+ * heads, number of jobs, jobs handed out (including one empty request per
+ * workgroup), error flag (nonzero: a wait for another job's state ran out; the
+ * outputs are then invalid), 0.  Without a split: {1, 1, B*H, 0, B*H, 0, 0, 0}
+ * and the workspace is not read. */
+gdn_status gdn_chunk_fwd_plan_info(int B, int T, int H, const gdn_options* opt, const void* workspace,
+                                   int32_t* info, void* stream);
 
 /* Workspace bytes gdn_chunk_fwd needs for these shapes on the current device
  * (0 when the sequence is not split).  Returns (size_t)-1 for invalid arguments. */
@@ -158,12 +172,11 @@ typedef enum {
     GDN_LAUNCH_GATE_SUMS = 0,   /* gate scan: per-chunk sums of g                     */
     GDN_LAUNCH_GATE_FLAGS = 1,  /* gate scan: window maxima and flags                 */
     GDN_LAUNCH_FWD_SINGLE = 2,  /* fused forward, unsplit                             */
-    GDN_LAUNCH_FWD_PASS_A = 3,  /* fused forward: window heads, segment 0, pass-1     */
-    GDN_LAUNCH_COMBINE = 4,     /* segment combine                                    */
-    GDN_LAUNCH_FWD_PASS_C = 5,  /* fused forward: exact heads from corrected states   */
-    GDN_LAUNCH_BWD_STATES = 6,  /* backward: state entering every chunk (forward kernel) */
-    GDN_LAUNCH_BWD_DH = 7,      /* backward: state gradient, end to start             */
-    GDN_LAUNCH_BWD_LOCAL = 8    /* backward: local gradients of every chunk           */
+    GDN_LAUNCH_FWD_PLAN = 3,    /* split forward: segment counts and job list         */
+    GDN_LAUNCH_FWD_QUEUE = 4,   /* split forward: persistent workgroups over the jobs */
+    GDN_LAUNCH_BWD_STATES = 5,  /* backward: state entering every chunk (forward kernel) */
+    GDN_LAUNCH_BWD_DH = 6,      /* backward: state gradient, end to start             */
+    GDN_LAUNCH_BWD_LOCAL = 7    /* backward: local gradients of every chunk           */
 } gdn_launch_kind;
 
 /* Measurement hook (the talk summary, paragraph 7, argues the fused operator

@@ -36,13 +36,13 @@ def test_default_options():
 
 
 @pytest.mark.parametrize("B,T,H,cus,expect", [
-    (1, 32768, 32, 256, 8),     # min(ceil(256/32)=8, floor(sqrt(512))=22, 512/16=32)
-    (1, 262144, 16, 256, 16),   # min(16, 64, 256)
-    (1, 4096, 16, 256, 4),      # min(16, 8, 64/16=4)
+    (1, 32768, 32, 256, 22),    # 512 chunks: min(32, floor(sqrt(512)) = 22, 256)
+    (1, 262144, 16, 256, 32),   # min(32, 64, 2048)
+    (1, 4096, 16, 256, 8),      # min(32, 8, 32)
     (4, 8192, 32, 256, 1),      # 128 heads >= 256/2: no split
     (1, 128, 1, 256, 1),        # 2 chunks < 2w
-    (1, 1000, 1, 256, 1),       # 16 chunks: min(256, 4, 1) = 1
-    (1, 64 * 100, 2, 256, 6),   # min(128, 10, 6)
+    (1, 1000, 1, 256, 4),       # 16 chunks: min(32, 4, 8)
+    (1, 64 * 100, 2, 256, 10),  # min(32, 10, 50)
 ])
 def test_planner_rule(B, T, H, cus, expect):
     assert gdn.gdn_plan_segments(B, T, H, cus) == expect

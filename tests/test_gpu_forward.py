@@ -73,6 +73,37 @@ def test_forced_split(gdn, P, window):
            label=f"P={P} w={window}")
 
 
+def test_forced_split_one_chunk_segments(gdn):
+    """As many segments as chunks: every segment is one chunk, every window
+    job warms up from the sequence start or over w earlier chunks."""
+    say("case forced split, one chunk per segment")
+    x = inputs.generate(B=1, T=64 * 9 + 3, H=3, gate="mixed", strong_frac=0.34, h0_std=0.02, seed=18)
+    _check(*_run(gdn, x, split_mode=2, n_segments=10, window_chunks=2), TOL_BF16,
+           label="P = N = 10")
+
+
+def test_forced_split_more_jobs_than_workgroups(gdn):
+    """More jobs than persistent workgroups: workgroups run several jobs and the
+    waits between exact-head segments still resolve."""
+    import torch
+    say("case forced split, 64 heads x 12 segments")
+    x = inputs.generate(B=2, T=64 * 24 + 5, H=32, gate="mixed", strong_frac=0.5, h0_std=0.02, seed=19)
+    t = to_gpu(x)
+    B, T, H = 2, 64 * 24 + 5, 32
+    opts = dict(split_mode=2, n_segments=12, window_chunks=3)
+    ws = torch.zeros(gdn.gdn_chunk_fwd_workspace_size(B, T, H, **opts), dtype=torch.uint8, device="cuda")
+    o, ht = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], workspace=ws, **opts)
+    info = gdn.gdn_chunk_fwd_plan_info(B, T, H, workspace=ws, **opts)
+    say(f"  plan {info}")
+    assert info["error"] == 0
+    assert info["P_exact"] == 12 and info["P_window"] == 12
+    assert info["n_exact"] + info["n_window"] == B * H
+    assert info["n_jobs"] == 12 * B * H > 256
+    assert info["handed_out"] >= info["n_jobs"]
+    oref, href = oracle.fwd(x.q, x.k, x.v, x.g, x.beta, x.h0)
+    _check(to_np(o), to_np(ht), oref, href, TOL_BF16, label="64 heads x 12 segments")
+
+
 def test_split_mixed_heads_window(gdn):
     say("case mixed heads split with window, w=2")
     x = inputs.generate(B=2, T=64 * 40, H=4, gate="mixed", strong_frac=0.5, seed=12)
@@ -171,13 +202,24 @@ def test_bf16_t32768_h32_sampled_heads(gdn):
     """The throughput workload at full size, in the launch configuration the
     benchmark times; the oracle runs on a sample of heads of both kinds."""
     say("case bf16_t32768_h32 (full size, sampled heads)")
+    import torch
     x = inputs.workload("bf16_t32768_h32")
+    B, T, H = 1, 32768, 32
     flags, _ = oracle.gate_scan(x.g, window_chunks=8)
-    win = [i for i in range(32) if flags[0, i]][:3]
-    ex = [i for i in range(32) if not flags[0, i]][:3]
-    heads = win + ex
-    o, ht, oref, href = _run(gdn, x, heads=heads)
-    _check(o, ht, oref, href, TOL_BF16, heads=heads, H=32, label="t32768 h32")
+    win = [i for i in range(H) if flags[0, i]]
+    ex = [i for i in range(H) if not flags[0, i]]
+    # every exact head (their segments hand states to each other), a few window heads
+    heads = win[:3] + ex
+    t = to_gpu(x)
+    ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(B, T, H), dtype=torch.uint8, device="cuda")
+    o, ht = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], workspace=ws)
+    info = gdn.gdn_chunk_fwd_plan_info(B, T, H, workspace=ws)
+    say(f"  plan {info}")
+    assert info["error"] == 0
+    assert (info["n_exact"], info["n_window"]) == (len(ex), len(win))
+    assert info["P_exact"] >= 3
+    oref, href = oracle.fwd(x.q, x.k, x.v, x.g, x.beta, x.h0, heads=heads)
+    _check(to_np(o), to_np(ht), oref, href, TOL_BF16, heads=heads, H=H, label="t32768 h32")
 
 
 @pytest.mark.slow
