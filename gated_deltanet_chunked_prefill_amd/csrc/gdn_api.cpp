@@ -112,7 +112,7 @@ int plan(int B, int T, int H, int num_cus, const gdn_options& o) {
 }
 
 struct FwdLayout {
-    size_t chunk_sums, flags, maxwin, hs, hs_cnt, plan, jobs, total;
+    size_t chunk_sums, flags, maxwin, hs, hs_cnt, bz, mt, eg, tr_cnt, plan, jobs, total;
 };
 
 FwdLayout fwd_layout(int B, int T, int H, int P) {
@@ -125,8 +125,12 @@ FwdLayout fwd_layout(int B, int T, int H, int P) {
     L.maxwin = off;     off += align_up(bh * sizeof(float));
     L.hs = off;         off += align_up(bh * P * SS * sizeof(float));
     L.hs_cnt = off;     off += align_up(bh * P * sizeof(int32_t));
+    L.bz = off;         off += align_up(bh * P * SS * sizeof(float));
+    L.mt = off;         off += align_up(bh * P * 2 * SS * sizeof(uint16_t));
+    L.eg = off;         off += align_up(bh * P * sizeof(float));
+    L.tr_cnt = off;     off += align_up(bh * P * sizeof(int32_t));
     L.plan = off;       off += align_up(sizeof(gdn::FwdPlan));
-    L.jobs = off;       off += align_up(bh * P * sizeof(gdn::TaskRec));
+    L.jobs = off;       off += align_up(bh * (2 * P + 3) * sizeof(gdn::TaskRec));
     L.total = off;
     return L;
 }
@@ -237,7 +241,7 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
     gdn::FwdParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.o = o; p.ht = ht;
     p.B = B; p.T = T; p.H = H; p.N = N; p.P = P; p.w = op.window_chunks; p.scale = scale;
-    p.flags = nullptr;
+    p.sums = nullptr;
     const bool bf16 = dtype == GDN_BF16;
     hipError_t e;
     if (P == 1) {
@@ -248,21 +252,22 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
     char* ws = (char*)workspace;
     p.hs = (float*)(ws + L.hs);
     p.hs_cnt = (int*)(ws + L.hs_cnt);
+    p.bz = (float*)(ws + L.bz);
+    p.mt = (__bf16*)(ws + L.mt);
+    p.eg = (float*)(ws + L.eg);
+    p.tr_cnt = (int*)(ws + L.tr_cnt);
     p.plan = (gdn::FwdPlan*)(ws + L.plan);
     p.jobs = (gdn::TaskRec*)(ws + L.jobs);
     p.cus = cus;
     p.forced = op.split_mode == 2 ? 1 : 0;
+    p.flags = (int32_t*)(ws + L.flags);
+    p.maxwin = (float*)(ws + L.maxwin);
+    p.log_eps = op.log_eps;
     if (op.use_window) {
-        int32_t* flags = (int32_t*)(ws + L.flags);
         float* sums = (float*)(ws + L.chunk_sums);
         e = recorded(GDN_LAUNCH_GATE_SUMS, s, [&] { return gdn::launch_chunk_sums(g, B, T, H, sums, s); });
         if (e != hipSuccess) return hip_fail(e, "gate scan launch");
-        e = recorded(GDN_LAUNCH_GATE_FLAGS, s, [&] {
-            return gdn::launch_window_flags(sums, B, T, H, op.window_chunks, op.log_eps, flags,
-                                            (float*)(ws + L.maxwin), s);
-        });
-        if (e != hipSuccess) return hip_fail(e, "gate scan launch");
-        p.flags = flags;
+        p.sums = sums;   // the plan kernel derives the window flags from these
     }
     e = recorded(GDN_LAUNCH_FWD_PLAN, s, [&] { return gdn::launch_plan(p, s); });
     if (e != hipSuccess) return hip_fail(e, "forward plan launch");

@@ -244,6 +244,9 @@ struct TileLoader {
         }
     }
     // Copy the chunk whose first row (for this head) is `chunk` into `tile`.
+    // CPOL: cache policy of the direct loads (16 = device-coherent, for data
+    // another workgroup published during the same launch).
+    template <int CPOL = 0>
     __device__ __forceinline__ void load(T* tile, const T* chunk, int nvalid) const {
         const char* base = (const char*)chunk;
         if (nvalid == kChunk) {
@@ -251,7 +254,7 @@ struct TileLoader {
             for (int i = 0; i < ROUNDS; ++i) {
                 T* lbase = tile + (i * 4 + pw) * 64 * EPC;   // wave-uniform LDS destination
                 __builtin_amdgcn_global_load_lds((const void*)(base + off[i]),
-                                                 (__attribute__((address_space(3))) void*)lbase, 16, 0, 0);
+                                                 (__attribute__((address_space(3))) void*)lbase, 16, 0, CPOL);
             }
         } else {
             typedef uint32_t u4 __attribute__((ext_vector_type(4)));

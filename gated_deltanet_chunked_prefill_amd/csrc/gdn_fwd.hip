@@ -40,18 +40,13 @@
 // Split forward as a work queue.  A one-workgroup plan kernel reads the gate
 // flags, chooses the segment counts of exact and window heads from a cost
 // model and writes the job list; persistent workgroups (one per CU) then take
-// jobs from an atomic counter.  Per exact head with P segments the jobs are
-//   seg 0     full run from h0, publishes the state entering segment 1;
-//   seg p     (0 < p < P-1) pass-1 from zero, then the composition
-//             hs[p+1] = exp(G_p) Mt_p hs[p] + b_p once hs[p] is published, then
-//             the full run of segment p from hs[p];
-//   seg P-1   full run from hs[P-1] (waits for it), writes ht;
-// window heads (paragraph 5) get independent jobs that warm up over the w
-// chunks before their segment.  The list is ordered so that every job waits
-// only for jobs handed out before it (seg 0 jobs, middle segments in
-// increasing p, window jobs, last segments), so the waits end for any number
-// of resident workgroups.  A state crosses workgroups through HBM with an
-// agent-scope release by each producing wave and an acquire by the consumer.
+// jobs from an atomic counter.  An exact head with P segments gets a full run
+// of segment 0, pass-1 runs of the middle segments (publishing their
+// transitions), one chain job composing the true entering states, and full
+// runs of segments 1 .. P-1 from those states; window heads (paragraph 5) get
+// independent jobs that warm up over the w chunks before their segment.  The
+// list is ordered so that every job waits only for jobs handed out before it,
+// so the waits end for any number of resident workgroups.
 //
 // K^T and V in accumulator layout are read from the row-major tiles with the
 // transposing LDS read; O is produced transposed (O^T = H^T Q^T + V'^T P^T) so
@@ -64,11 +59,13 @@ namespace gdn {
 namespace {
 
 enum { INIT_ZERO = 0, INIT_H0 = 1, INIT_HS = 2, INIT_HS_WAIT = 3 };
-enum { DST_NONE = 0, DST_HT = 1, DST_HS_NEXT = 2, DST_COMPOSE = 3 };
+enum { DST_NONE = 0, DST_HT = 1, DST_HS_NEXT = 2, DST_TRANSITION = 3 };
+enum { MODE_CHAIN = 2 };   // job kind beside MODE_FULL and MODE_PASS1
 
 constexpr int kThreads = 512;   // 4 state waves + 4 prep waves
 constexpr int kMtStride = kDk + 4;   // float row stride of a segment transition staged in LDS
 constexpr int kSpinLimit = 1 << 22;  // polls of about 1 us: seconds, far beyond any real wait
+constexpr size_t kSS = (size_t)kDk * kDv;
 
 struct Task {
     int bh, seg;
@@ -88,12 +85,65 @@ __device__ void whole_head_task(const FwdParams& prm, Task& t) {
     t.dst = prm.ht ? DST_HT : DST_NONE;
 }
 
-// Make this wave's global stores visible device-wide, then count the wave in.
-__device__ __forceinline__ void publish(int* cnt) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// Hand-off of data between workgroups of one launch.  The producer writes with
+// device-coherent stores (the sc1 policy: written through to the level shared
+// by all XCDs), waits until its wave's stores are acknowledged, then adds 1 to
+// a counter; the consumer polls the counter and reads with device-coherent
+// loads.  No cache-wide write-back or invalidation is needed on either side.
+// Bulk data moves as 16-byte buffer accesses; a handed-off state is stored
+// transposed ([dv][dk]) so that each lane's four consecutive accumulator rows
+// are one 16-byte word.
+constexpr int kSC1 = 16;   // cache-policy operand: device scope
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void st_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// byte offset of lane (n, g)'s accumulator rows 32ht + 8q + 4g .. +3 of state
+// column 32w + n in the transposed layout
+__device__ __forceinline__ int state_t_off(int w, int lane, int ht, int q) {
+    return ((32 * w + (lane & 31)) * kDk + 32 * ht + 8 * q + 4 * (lane >> 5)) * 4;
+}
+__device__ __forceinline__ void store_state_t_dev(float* dst, int w, int lane, const f32x16* Hs) {
+    const __amdgpu_buffer_rsrc_t rs = dev_rsrc(dst, (int)(kSS * 4));
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 v = {Hs[ht][4 * q], Hs[ht][4 * q + 1], Hs[ht][4 * q + 2], Hs[ht][4 * q + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, state_t_off(w, lane, ht, q), 0,
+                                                   kSC1);
+        }
+}
+__device__ __forceinline__ void load_state_t_dev(const float* src, int w, int lane, f32x16* Hs) {
+    const __amdgpu_buffer_rsrc_t rs = dev_rsrc(src, (int)(kSS * 4));
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 v = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, state_t_off(w, lane, ht, q), 0, kSC1));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Hs[ht][4 * q + j] = v[j];
+        }
+}
+// Count this wave in (by `amount`) once all its earlier stores are acknowledged.
+__device__ __forceinline__ void publish(int* cnt, int amount = 1) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    wait_vm();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(cnt, amount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A handed-off state is complete when its counter reaches kStateParts: the
+// four state waves of a full run add 4 each, the 16 waves of the four chain
+// jobs (one per 32-column block) 1 each.
+constexpr int kStateParts = 16;
 // Wait until `target` waves have published (bounded: on running out the plan's
 // error flag is raised and the wait ends).
 __device__ __forceinline__ void wait_published(const int* cnt, int target, int* error) {
@@ -106,65 +156,7 @@ __device__ __forceinline__ void wait_published(const int* cnt, int target, int* 
         }
         __builtin_amdgcn_s_sleep(8);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-}
-
-// acc += a b for float operands: exact float32 products in the float32 build;
-// in the bf16 build three bf16 products of the hi/lo split (a_hi b_hi + a_hi b_lo
-// + a_lo b_hi), close to float32 accuracy.
-template <typename T>
-__device__ __forceinline__ f32x16 mma_f32(const f32x8& a, const f32x8& b, f32x16 acc) {
-    if constexpr (sizeof(T) == 4) {
-        return mma(a, b, acc);
-    } else {
-        bf16x8 ah, al, bh, bl;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            ah[j] = (__bf16)a[j];
-            al[j] = (__bf16)(a[j] - (float)ah[j]);
-            bh[j] = (__bf16)b[j];
-            bl[j] = (__bf16)(b[j] - (float)bh[j]);
-        }
-        acc = mma(ah, bh, acc);
-        acc = mma(ah, bl, acc);
-        return mma(al, bh, acc);
-    }
-}
-
-// State wave w's 32 columns of the state entering the next segment (talk
-// summary, paragraph 4: a segment maps its entering state H to
-// exp(G) Mt H + b, with Mt gate-free and b the segment's run from zero):
-//     out = eG * Mt * hin + bz,
-// Mt row-major float in LDS (row stride kMtStride), hin and out in HBM, bz in
-// accumulator layout.
-template <typename T>
-__device__ __forceinline__ void compose_next(const float* mtl, float eG, const float* hin, float* out,
-                                             int w, int lane, const f32x16* bz) {
-    const int n = lane & 31, g = lane >> 5;
-    f32x16 hp[4];
-    load_state(hin, w, lane, hp);
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-        f32x16 acc = zero16();
-        const float* row = mtl + (32 * ht + n) * kMtStride + 4 * g;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(row + 16 * ks);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(row + 16 * ks + 8);
-            f32x8 a, b;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                a[j] = lo[j];
-                a[4 + j] = hi[j];
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) b[j] = hp[ks >> 1][8 * (ks & 1) + j];
-            acc = mma_f32<T>(a, b, acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            out[(32 * ht + rho(g, r)) * kDv + 32 * w + n] = eG * acc[r] + bz[ht][r];
-    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // The serial state step of one chunk for state wave w (its 32 state columns).
@@ -315,8 +307,8 @@ __device__ __noinline__ void state_loop(const FwdParams& prm, Smem<T>& sm, const
     if (init == INIT_H0) {
         load_state(uni(prm.h0) + (size_t)bh * SS, L.w, L.lane, Hs);
     } else if (init == INIT_HS || init == INIT_HS_WAIT) {
-        if (init == INIT_HS_WAIT) wait_published(uni(prm.hs_cnt) + slot, 4, &uni(prm.plan)->error);
-        load_state(uni(prm.hs) + slot * SS, L.w, L.lane, Hs);
+        if (init == INIT_HS_WAIT) wait_published(uni(prm.hs_cnt) + slot, kStateParts, &uni(prm.plan)->error);
+        load_state_t_dev(uni(prm.hs) + slot * SS, L.w, L.lane, Hs);
     } else {
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) Hs[ht] = zero16();
@@ -355,18 +347,14 @@ __device__ __noinline__ void state_loop(const FwdParams& prm, Smem<T>& sm, const
     if (dst == DST_HT) {
         store_state(uni(prm.ht) + (size_t)bh * SS, L.w, L.lane, Hs);
     } else if (dst == DST_HS_NEXT) {
-        store_state(uni(prm.hs) + (slot + 1) * SS, L.w, L.lane, Hs);
-        publish(uni(prm.hs_cnt) + slot + 1);
-    } else if (dst == DST_COMPOSE) {
-        // Hs is this segment's run from zero; the prep waves stage Mt and exp(G)
+        store_state_t_dev(uni(prm.hs) + (slot + 1) * SS, L.w, L.lane, Hs);
+        publish(uni(prm.hs_cnt) + slot + 1, kStateParts / 4);
+    } else if (dst == DST_TRANSITION) {
+        // Hs is this segment's run from a zero state; the prep waves publish Mt
+        store_state_t_dev(uni(prm.bz) + slot * SS, L.w, L.lane, Hs);
+        publish(uni(prm.tr_cnt) + slot);
         lds_barrier();   // done with the chunk tiles
-        lds_barrier();   // Mt in LDS
-        wait_published(uni(prm.hs_cnt) + slot, 4, &uni(prm.plan)->error);
-        float* const hs = uni(prm.hs);
-        compose_next<T>(reinterpret_cast<const float*>(&sm.kt[0][0]), sm.fslot[0], hs + slot * SS,
-                        hs + (slot + 1) * SS, L.w, L.lane, Hs);
-        publish(uni(prm.hs_cnt) + slot + 1);
-        lds_barrier();   // Mt no longer needed
+        lds_barrier();   // Mt staged in LDS
     }
 }
 
@@ -466,7 +454,9 @@ __device__ __noinline__ void prep_loop(const FwdParams& prm, Smem<T>& sm, const 
             if (MODE == MODE_PASS1) mt_step<T>(L, sm.kt[0], sm.t32[0], Ms);
         }
     }
-    if (dst == DST_COMPOSE) {
+    if (dst == DST_TRANSITION) {
+        // publish the segment's gate-free transition Mt as bf16 hi and lo parts
+        // (row-major [128][128] each) and exp(G), staged through LDS as floats
         lds_barrier();   // the state waves are done with the chunk tiles
         float* const mtl = reinterpret_cast<float*>(&sm.kt[0][0]);
 #pragma unroll
@@ -474,9 +464,28 @@ __device__ __noinline__ void prep_loop(const FwdParams& prm, Smem<T>& sm, const 
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 mtl[(32 * ht + rho(L.g, r)) * kMtStride + 32 * L.w + L.n] = Ms[ht][r];
-        if (pw == 3 && L.lane == 0) sm.fslot[0] = __expf(gsum);
-        lds_barrier();   // Mt in LDS
-        lds_barrier();   // the state waves have composed
+        lds_barrier();   // Mt staged
+        const size_t slot = (size_t)bh * uni(prm.P) + uni(tk.seg);
+        const __amdgpu_buffer_rsrc_t rs = dev_rsrc(uni(prm.mt) + slot * 2 * kSS, (int)(2 * kSS * 2));
+        const int row = 32 * pw + (L.lane >> 1), c0 = 64 * (L.lane & 1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float* src = mtl + row * kMtStride + c0 + 8 * i;
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+            bf16x8 hi, lo;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = j < 4 ? x0[j] : x1[j - 4];
+                hi[j] = (__bf16)x;
+                lo[j] = (__bf16)(x - (float)hi[j]);
+            }
+            const int off = (row * kDk + c0 + 8 * i) * 2;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), rs, off, 0, kSC1);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), rs, off + (int)kSS * 2, 0, kSC1);
+        }
+        if (pw == 3 && L.lane == 0) st_dev(uni(prm.eg) + slot, __expf(gsum));
+        publish(uni(prm.tr_cnt) + slot);
     }
 }
 
@@ -489,6 +498,180 @@ __device__ __forceinline__ void run_task(const FwdParams& prm, Smem<T>& sm, cons
         state_loop<T, MODE, KEEP>(prm, sm, tk);
     else
         prep_loop<T, MODE>(prm, sm, tk);
+}
+
+// Chain jobs of an exact head (talk summary, paragraph 4: segment p maps the
+// state entering it, H, to exp(G_p) Mt_p H + b_p, so the true entering states
+// follow from the first one by one dk x dk product per segment):
+//     hs[p+1] = exp(G_p) Mt_p hs[p] + b_p,   p = seg .. c_end - 1.
+// Columns of the state evolve independently, so four jobs share a head, job c
+// owning state columns [32c, 32c+32); its state wave w forms the 32 x 32 tile
+// of rows [32w, 32w+32) per link (24 split-precision MFMAs: a_hi b_hi + a_hi
+// b_lo + a_lo b_hi), publishes it, and the four tiles are exchanged through LDS
+// for the next link.  The prep waves stream each Mt_p (bf16 hi and lo parts,
+// published by the pass-1 job of segment p) into LDS one link ahead; each
+// wave's part of b_p is loaded one link ahead, and a tile's publication is
+// counted one link late, once the wave's later loads show its stores done.
+template <typename T>
+struct ChainBuf {
+    // Mt double-buffered when both buffers fit in front of the prep outputs
+    static constexpr bool two = 2 * 4 * kChunk * kDk * 2 <= (int)offsetof(Smem<T>, t32);
+    static __device__ __forceinline__ __bf16* tiles(Smem<T>& sm, int buf) {
+        return reinterpret_cast<__bf16*>(&sm) + (two ? buf : 0) * 4 * kChunk * kDk;
+    }
+    // exchange of the four 32 x 32 float tiles of a column block (16 KiB)
+    static __device__ __forceinline__ float* exch(Smem<T>& sm) {
+        return reinterpret_cast<float*>(&sm.t32[0][0][0]);
+    }
+};
+static_assert(sizeof(((Smem<float>*)0)->t32) >= 16384 && sizeof(((Smem<__bf16>*)0)->t32) >= 16384,
+              "the chain's tile exchange lives in the prep-output area");
+
+// byte offset of lane (n, g)'s rows 32ht + 8q + 4g .. +3 of state column 32c + n
+// (transposed layout), as in state_t_off
+__device__ __forceinline__ void load_tile_t_dev(const float* src, int c, int ht, int lane, f32x16& t) {
+    const __amdgpu_buffer_rsrc_t rs = dev_rsrc(src, (int)(kSS * 4));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f32x4 v = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, state_t_off(c, lane, ht, q), 0, kSC1));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t[4 * q + j] = v[j];
+    }
+}
+__device__ __forceinline__ void store_tile_t_dev(float* dst, int c, int ht, int lane, const f32x16& t) {
+    const __amdgpu_buffer_rsrc_t rs = dev_rsrc(dst, (int)(kSS * 4));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, state_t_off(c, lane, ht, q), 0,
+                                               kSC1);
+    }
+}
+
+template <typename T>
+__device__ __noinline__ void chain_state(const FwdParams& prm, Smem<T>& sm, const Task& tk) {
+    using CB = ChainBuf<T>;
+    const int bh = uni(tk.bh), p0 = uni(tk.seg), p_end = uni(tk.c_end), c = uni(tk.c_begin);
+    const int P = uni(prm.P);
+    float* const hs = uni(prm.hs);
+    const float* const bz = uni(prm.bz);
+    const float* const eg = uni(prm.eg);
+    int* const hs_cnt = uni(prm.hs_cnt);
+    int* const err = &uni(prm.plan)->error;
+    Lane<__bf16> L;
+    L.init(threadIdx.x);
+    const int w = L.w, lane = L.lane;
+    const size_t base = (size_t)bh * P;
+    float* const ex = CB::exch(sm);
+    // the column block of the first state, all four row tiles
+    f32x16 Hc[4];
+    wait_published(hs_cnt + base + p0, kStateParts, err);
+    load_state_t_dev(hs + (base + p0) * kSS, c, lane, Hc);
+    // this wave's tile of b_p and exp(G_p): read after a barrier behind which the
+    // prep waves have seen transition p published (one link ahead when
+    // double-buffered)
+    f32x16 Bt;
+    float e = 0.f;
+    if (CB::two) {
+        lds_barrier();   // X: Mt_p0 in LDS
+        load_tile_t_dev(bz + (base + p0) * kSS, c, w, lane, Bt);
+        e = ld_dev(eg + base + p0);
+    }
+    for (int p = p0; p < p_end; ++p) {
+        if (!CB::two) {
+            lds_barrier();   // A: Mt_p in LDS
+            load_tile_t_dev(bz + (base + p) * kSS, c, w, lane, Bt);
+            e = ld_dev(eg + base + p);
+        }
+        // H column block split into bf16 hi and lo parts (the B operands)
+        bf16x8 hh[8], hl[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = Hc[ks >> 1][8 * (ks & 1) + j];
+                hh[ks][j] = (__bf16)x;
+                hl[ks][j] = (__bf16)(x - (float)hh[ks][j]);
+            }
+        if (CB::two) lds_barrier();   // Y: the exchange has been read; Mt_p+1 in LDS
+        const __bf16* const thi = CB::tiles(sm, (p - p0) & 1) + (w >> 1) * kChunk * kDk;
+        const __bf16* const tlo = thi + 2 * kChunk * kDk;
+        f32x16 acc0 = zero16(), acc1 = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 8; ks += 2) {
+            const bf16x8 ah0 = L.f128(thi, w & 1, ks), al0 = L.f128(tlo, w & 1, ks);
+            const bf16x8 ah1 = L.f128(thi, w & 1, ks + 1), al1 = L.f128(tlo, w & 1, ks + 1);
+            acc0 = mma(ah0, hh[ks], acc0);
+            acc1 = mma(ah1, hh[ks + 1], acc1);
+            acc0 = mma(ah0, hl[ks], acc0);
+            acc1 = mma(ah1, hl[ks + 1], acc1);
+            acc0 = mma(al0, hh[ks], acc0);
+            acc1 = mma(al1, hh[ks + 1], acc1);
+            __builtin_amdgcn_sched_barrier(0);   // bound the LDS reads in flight (registers)
+        }
+        // b_p arrived (and, memory operations of a wave completing in order, the
+        // previous link's tile stores with it): count that tile in
+        wait_vm();
+        if (p > p0) publish(hs_cnt + base + p);
+        f32x16 Hn;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Hn[r] = e * (acc0[r] + acc1[r]) + Bt[r];
+        store_tile_t_dev(hs + (base + p + 1) * kSS, c, w, lane, Hn);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ex[(w * 16 + r) * 64 + lane] = Hn[r];
+        if (CB::two && p + 1 < p_end) {
+            // the prep waves saw transition p+1 published before barrier Y
+            load_tile_t_dev(bz + (base + p + 1) * kSS, c, w, lane, Bt);
+            e = ld_dev(eg + base + p + 1);
+        }
+        lds_barrier();   // X (two) / B: the exchange is written, Mt_p is done with
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Hc[ht][r] = ex[(ht * 16 + r) * 64 + lane];
+        if (!CB::two) lds_barrier();   // C: the exchange has been read
+    }
+    publish(hs_cnt + base + p_end);
+}
+
+template <typename T>
+__device__ __noinline__ void chain_prep(const FwdParams& prm, Smem<T>& sm, const Task& tk) {
+    using CB = ChainBuf<T>;
+    const int pw = wave_id() - 4, lane = threadIdx.x & 63;
+    const int bh = uni(tk.bh), p0 = uni(tk.seg), p_end = uni(tk.c_end), P = uni(prm.P);
+    const __bf16* const mt = uni(prm.mt);
+    const int* const tr_cnt = uni(prm.tr_cnt);
+    int* const err = &uni(prm.plan)->error;
+    const size_t base = (size_t)bh * P;
+    TileLoader<__bf16> TL;
+    TL.init(pw, lane, 1);
+    auto load = [&](int p) {
+        wait_published(tr_cnt + base + p, 8, err);
+        const __bf16* const src = mt + (base + p) * 2 * kSS;
+        __bf16* const dst = CB::tiles(sm, (p - p0) & 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) TL.template load<16>(dst + q * kChunk * kDk, src + q * kChunk * kDk, kChunk);
+        wait_vm();
+    };
+    if (CB::two) {
+        // Mt_p+1 goes into the buffer link p-1 used; its readers finished before
+        // the X barrier that ends link p-1
+        load(p0);
+        lds_barrier();   // X
+        for (int p = p0; p < p_end; ++p) {
+            if (p + 1 < p_end) load(p + 1);
+            lds_barrier();   // Y
+            lds_barrier();   // X
+        }
+    } else {
+        for (int p = p0; p < p_end; ++p) {
+            load(p);
+            lds_barrier();   // A
+            lds_barrier();   // B
+            lds_barrier();   // C
+        }
+    }
 }
 
 template <typename T, int PHASE>
@@ -516,40 +699,48 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_queue_kernel(FwdParams pr
         __syncthreads();
         if (j >= n_jobs) break;
         const TaskRec rec = prm.jobs[j];
-        Task tk{rec.bh, rec.seg, rec.c_begin, rec.c_out, rec.c_end, rec.mode, rec.init, rec.dst};
-        if (tk.mode == MODE_PASS1) {
-            // middle segment of an exact head: pass-1 and composition, then the
-            // segment's outputs from its true entering state
+        const Task tk{rec.bh, rec.seg, rec.c_begin, rec.c_out, rec.c_end, rec.mode, rec.init, rec.dst};
+        if (tk.mode == MODE_CHAIN) {
+            if (wave_id() < 4)
+                chain_state<T>(prm, sm, tk);
+            else
+                chain_prep<T>(prm, sm, tk);
+        } else if (tk.mode == MODE_PASS1) {
             run_task<T, MODE_PASS1>(prm, sm, tk);
-            tk.mode = MODE_FULL;
-            tk.c_out = tk.c_begin;
-            tk.init = INIT_HS;
-            tk.dst = DST_NONE;
+        } else {
+            run_task<T, MODE_FULL>(prm, sm, tk);
         }
-        run_task<T, MODE_FULL>(prm, sm, tk);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Planner of the split forward (one workgroup).
 //
-// Cost model, in units of one fused chunk step: a pass-1 step costs kCostPass1,
-// one link of the state chain of an exact head kCostLink.  An exact head with
-// P >= 3 segments keeps P - 1 workgroups busy for about
+// Jobs of an exact head split into P >= 3 segments (chunk bounds b_0 = 0 <
+// b_1 < ... < b_P = N):
+//   seg 0           full run of [0, b_1) from h0, publishes hs[1];
+//   pass-1 p        run of [b_p, b_p+1) from a zero state (p = 1 .. P-2),
+//                   publishes b_p, Mt_p and exp(G_p);
+//   chain           hs[p+1] = exp(G_p) Mt_p hs[p] + b_p for p = 1 .. P-2;
+//   pass-3 p        full run of [b_p, b_p+1) from hs[p] (p = 1 .. P-1), the
+//                   last one writes ht.
+// With P = 2 only seg 0 and one pass-3 job remain, with P = 1 one full run.
+// Window heads get P_w independent jobs, each warming up over the w chunks
+// before its segment.  Queue order: seg 0 jobs, pass-1 jobs, window jobs,
+// chain jobs, pass-3 jobs (segment-major), so that every job waits only for
+// jobs handed out before it.
+//
+// Cost model, in units of one full chunk step under load: a pass-1 step costs
+// kCostPass1, one link of the chain kCostLink.  An exact head keeps P - 1
+// workgroups busy for about
 //     L (1 + kCostPass1) + (P - 2) kCostLink,   L = 8 N / (kSeg0Weight + 8 (P - 1)),
-// where segment 0 (which only runs full steps and later takes the last
-// segment) is kSeg0Weight / 8 times as long as the others.  The remaining
-// workgroups share the window heads' segments, each costing N / P_w + w.  The
-// planner takes the P (and P_w) with the smallest estimated makespan.
-constexpr float kCostPass1 = 1.4f;
-constexpr float kCostLink = 1.0f;
+// segment 0 being kSeg0Weight / 8 times as long as the others so that it ends
+// with the pass-1 jobs.  The remaining workgroups share the window heads'
+// segments, each costing N / P_w + w.  The planner takes the P (and P_w) with
+// the smallest estimated makespan.
+constexpr float kCostPass1 = 1.35f;
+constexpr float kCostLink = 0.8f;
 constexpr int kSeg0Weight = 11;
-
-__device__ int exact_bound(int p, int P, int N, int w0) {
-    if (p <= 0) return 0;
-    if (p >= P) return N;
-    return (int)(((long long)N * (w0 + 8 * (p - 1))) / (w0 + 8 * (P - 1)));
-}
 
 __device__ void choose_segments(int n_e, int n_w, int N, int w, int cus, int pmax, int& Pe, int& Pw) {
     float best = 3.0e38f;
@@ -596,64 +787,138 @@ __device__ __forceinline__ void put_job(TaskRec* jobs, int j, int bh, int seg, i
     jobs[j] = r;
 }
 
-__global__ __launch_bounds__(256) void plan_kernel(FwdParams prm) {
-    __shared__ int s_rank[256];
-    __shared__ int s_par[4];
-    const int tid = threadIdx.x;
+constexpr int kPlanThreads = 1024;
+
+// Exclusive prefix sum over the threads of the workgroup (kPlanThreads).
+__device__ int block_exclusive_scan(int x, int* s_wave, int& total) {
+    constexpr int NW = kPlanThreads / 64;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int incl = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += y;
+    }
+    if (lane == 63) s_wave[wv] = incl;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        before += i < wv ? s_wave[i] : 0;
+        total += s_wave[i];
+    }
+    return before + incl - x;
+}
+
+__device__ int seg_bound(long long num, long long den, int N) {
+    return (int)(((double)N * (double)num) / (double)den);
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(FwdParams prm) {
+    __shared__ int s_wave[kPlanThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nbh = prm.B * prm.H, N = prm.N, pmax = prm.P, w = prm.w;
-    const int per = (nbh + 255) / 256;
+    // 1. window flags (talk summary, paragraph 5): per head the largest sum of g
+    //    over w consecutive chunks; a wave per head, each lane a contiguous run of
+    //    chunk windows summed with a running window sum
+    if (prm.sums) {
+        const int R = (N + 63) / 64;
+        for (int bh = wv; bh < nbh; bh += kPlanThreads / 64) {
+            const int b = bh / prm.H, h = bh % prm.H;
+            const float* s = prm.sums + (size_t)b * N * prm.H + h;
+            float best = -INFINITY;
+            const int ca = lane * R < w - 1 ? w - 1 : lane * R;
+            const int cb = (lane + 1) * R < N ? (lane + 1) * R : N;
+            if (ca < cb) {
+                // loads in batches of eight so that each batch is in flight at once
+                float acc = 0.f;
+                for (int j0 = ca - w + 1; j0 <= ca; j0 += 8) {
+                    float v[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) v[u] = j0 + u <= ca ? s[(size_t)(j0 + u) * prm.H] : 0.f;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) acc += v[u];
+                }
+                best = acc;
+                for (int c0 = ca + 1; c0 < cb; c0 += 8) {
+                    float a[8], d[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const bool in = c0 + u < cb;
+                        a[u] = in ? s[(size_t)(c0 + u) * prm.H] : 0.f;
+                        d[u] = in ? s[(size_t)(c0 + u - w) * prm.H] : 0.f;
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        if (c0 + u < cb) {
+                            acc += a[u] - d[u];
+                            best = acc > best ? acc : best;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int d = 32; d > 0; d >>= 1) {
+                const float o = __shfl_xor(best, d, 64);
+                best = o > best ? o : best;
+            }
+            if (lane == 0) {
+                prm.flags[bh] = (N >= w && best <= prm.log_eps) ? 1 : 0;
+                if (prm.maxwin) prm.maxwin[bh] = best;
+            }
+        }
+        __syncthreads();
+    }
+    // 2. rank the exact and the window heads, choose the segment counts
+    const int per = (nbh + kPlanThreads - 1) / kPlanThreads;
     const int lo = tid * per < nbh ? tid * per : nbh;
     const int hi = lo + per < nbh ? lo + per : nbh;
-    auto exact = [&](int bh) { return prm.flags == nullptr || prm.flags[bh] == 0; };
+    auto exact = [&](int bh) { return prm.sums == nullptr || prm.flags[bh] == 0; };
     int ne = 0;
     for (int bh = lo; bh < hi; ++bh) ne += exact(bh) ? 1 : 0;
-    s_rank[tid] = ne;
-    __syncthreads();
+    int n_e = 0;
+    int re = block_exclusive_scan(ne, s_wave, n_e);   // exact rank of this thread's first head
+    int rw = lo - re;                                  // window rank
+    const int n_w = nbh - n_e;
+    int Pe = pmax, Pw = pmax;
+    if (!prm.forced) choose_segments(n_e, n_w, N, w, prm.cus, pmax, Pe, Pw);
+    const int g_win = n_e + (Pe >= 3 ? n_e * (Pe - 2) : 0);
+    const int g_chain = g_win + n_w * Pw;
+    const int g_p3 = g_chain + (Pe >= 3 ? 4 * n_e : 0);
+    const int n_jobs = g_p3 + (Pe >= 2 ? n_e * (Pe - 1) : 0);
     if (tid == 0) {
-        int run = 0;
-        for (int i = 0; i < 256; ++i) {
-            const int c = s_rank[i];
-            s_rank[i] = run;
-            run += c;
-        }
-        const int n_e = run, n_w = nbh - run;
-        int Pe = pmax, Pw = pmax;
-        if (!prm.forced) choose_segments(n_e, n_w, N, w, prm.cus, pmax, Pe, Pw);
-        s_par[0] = n_e;
-        s_par[1] = n_w;
-        s_par[2] = Pe;
-        s_par[3] = Pw;
         FwdPlan* pl = prm.plan;
         pl->P_e = Pe;
         pl->P_w = Pw;
         pl->n_exact = n_e;
         pl->n_window = n_w;
-        pl->n_jobs = n_e * Pe + n_w * Pw;
+        pl->n_jobs = n_jobs;
         pl->next = 0;
         pl->error = 0;
     }
-    __syncthreads();
-    const int n_e = s_par[0], n_w = s_par[1], Pe = s_par[2], Pw = s_par[3];
-    // job groups: [seg 0 of exact heads][middle segments, p-major][window jobs][last segments]
-    const int g_mid = n_e, g_win = n_e + n_e * (Pe > 2 ? Pe - 2 : 0), g_last = g_win + n_w * Pw;
+    // 3. the job list
     const int w0 = prm.forced ? 8 : kSeg0Weight;
+    const long long den = w0 + 8 * (Pe - 1);
+    auto bound = [&](int p) { return p <= 0 ? 0 : p >= Pe ? N : seg_bound(w0 + 8 * (p - 1), den, N); };
     const bool has_h0 = prm.h0 != nullptr, has_ht = prm.ht != nullptr;
-    int re = s_rank[tid], rw = lo - s_rank[tid];
+    const int dst_last = has_ht ? DST_HT : DST_NONE;
     for (int bh = lo; bh < hi; ++bh) {
         if (exact(bh)) {
             const int init0 = has_h0 ? INIT_H0 : INIT_ZERO;
             if (Pe == 1) {
-                put_job(prm.jobs, re, bh, 0, 0, 0, N, MODE_FULL, init0, has_ht ? DST_HT : DST_NONE);
+                put_job(prm.jobs, re, bh, 0, 0, 0, N, MODE_FULL, init0, dst_last);
             } else {
-                put_job(prm.jobs, re, bh, 0, 0, 0, exact_bound(1, Pe, N, w0), MODE_FULL, init0, DST_HS_NEXT);
-                for (int p = 1; p + 1 < Pe; ++p) {
-                    const int cb = exact_bound(p, Pe, N, w0), ce = exact_bound(p + 1, Pe, N, w0);
-                    put_job(prm.jobs, g_mid + (p - 1) * n_e + re, bh, p, cb, ce, ce, MODE_PASS1, INIT_ZERO,
-                            DST_COMPOSE);
-                }
-                const int cb = exact_bound(Pe - 1, Pe, N, w0);
-                put_job(prm.jobs, g_last + re, bh, Pe - 1, cb, cb, N, MODE_FULL, INIT_HS_WAIT,
-                        has_ht ? DST_HT : DST_NONE);
+                put_job(prm.jobs, re, bh, 0, 0, 0, bound(1), MODE_FULL, init0, DST_HS_NEXT);
+                for (int p = 1; p + 1 < Pe; ++p)
+                    put_job(prm.jobs, n_e + (p - 1) * n_e + re, bh, p, bound(p), bound(p + 1), bound(p + 1),
+                            MODE_PASS1, INIT_ZERO, DST_TRANSITION);
+                if (Pe >= 3)
+                    for (int cb = 0; cb < 4; ++cb)   // one chain job per 32-column block
+                        put_job(prm.jobs, g_chain + 4 * re + cb, bh, 1, cb, 0, Pe - 1, MODE_CHAIN, 0, 0);
+                for (int p = 1; p < Pe; ++p)
+                    put_job(prm.jobs, g_p3 + (p - 1) * n_e + re, bh, p, bound(p), bound(p), bound(p + 1),
+                            MODE_FULL, INIT_HS_WAIT, p == Pe - 1 ? dst_last : DST_NONE);
             }
             ++re;
         } else {
@@ -661,13 +926,15 @@ __global__ __launch_bounds__(256) void plan_kernel(FwdParams prm) {
                 const int s = (int)(((long long)p * N) / Pw), e = (int)(((long long)(p + 1) * N) / Pw);
                 const int cb = s - w > 0 ? s - w : 0;
                 put_job(prm.jobs, g_win + p * n_w + rw, bh, p, cb, s, e, MODE_FULL,
-                        (cb == 0 && has_h0) ? INIT_H0 : INIT_ZERO,
-                        (p == Pw - 1 && has_ht) ? DST_HT : DST_NONE);
+                        (cb == 0 && has_h0) ? INIT_H0 : INIT_ZERO, p == Pw - 1 ? dst_last : DST_NONE);
             }
             ++rw;
         }
     }
-    for (int i = tid; i < nbh * pmax; i += 256) prm.hs_cnt[i] = 0;
+    for (int i = tid; i < nbh * pmax; i += kPlanThreads) {
+        prm.hs_cnt[i] = 0;
+        prm.tr_cnt[i] = 0;
+    }
 }
 
 template <typename K>
@@ -709,7 +976,7 @@ hipError_t launch_fwd(const FwdParams& p, int phase, bool bf16, hipStream_t s) {
 }
 
 hipError_t launch_plan(const FwdParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, p);
     return hipGetLastError();
 }
 

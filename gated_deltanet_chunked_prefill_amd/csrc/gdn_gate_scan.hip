@@ -5,8 +5,6 @@
 //
 // Two small launches, both bound by one read of g:
 //   1. chunk sums s[b][c][h] = sum of g over the (up to) 64 tokens of chunk c;
-//      consecutive threads take consecutive heads, so each token row of g
-//      ([B,T,H], H contiguous) is read with coalesced accesses;
 //   2. per head (one workgroup): W_c = s_{c-w+1} + ... + s_c for c >= w-1 (each
 //      window summed directly), its maximum over c, and flag = N >= w && max <= log_eps.
 #include "gdn_device.h"
@@ -16,21 +14,33 @@ namespace gdn {
 
 namespace {
 
-constexpr int kChunksPerBlock = 8;
-
+// One workgroup per (chunk, batch).  The chunk's g values are one contiguous
+// block of 64 x H floats; thread t reads the elements of head t % H in token
+// order (group t / H takes every G-th token, G = 256 / H), so loads are
+// coalesced, and the G partial sums of a head are added in a fixed order
+// (results do not depend on scheduling).
 __global__ __launch_bounds__(256) void chunk_sums_kernel(const float* __restrict__ g, int T, int H,
                                                          int N, float* __restrict__ sums) {
-    const int b = blockIdx.y;
-    const int c0 = blockIdx.x * kChunksPerBlock;
-    const int pairs = kChunksPerBlock * H;
-    for (int i = threadIdx.x; i < pairs; i += blockDim.x) {
-        const int c = c0 + i / H, h = i % H;
-        if (c >= N) continue;
-        const int t0 = c * kChunk;
-        const int t1 = t0 + kChunk < T ? t0 + kChunk : T;
+    __shared__ float part[256];
+    const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int t0 = c * kChunk;
+    const int nt = T - t0 < kChunk ? T - t0 : kChunk;
+    const float* src = g + ((size_t)b * T + t0) * H;
+    for (int h0 = 0; h0 < H; h0 += 256) {
+        const int hw = H - h0 < 256 ? H - h0 : 256;   // heads in this pass
+        const int G = 256 / hw;                        // token groups
+        const int h = h0 + tid % hw, grp = tid / hw;
         float acc = 0.f;
-        for (int t = t0; t < t1; ++t) acc += g[((size_t)b * T + t) * H + h];
-        sums[((size_t)b * N + c) * H + h] = acc;
+        if (grp < G)
+            for (int t = grp; t < nt; t += G) acc += src[(size_t)t * H + h];
+        part[tid] = acc;
+        __syncthreads();
+        if (tid < hw) {
+            float s = 0.f;
+            for (int q = 0; q < G; ++q) s += part[q * hw + tid];
+            sums[((size_t)b * N + c) * H + h0 + tid] = s;
+        }
+        __syncthreads();
     }
 }
 
@@ -66,7 +76,7 @@ __global__ __launch_bounds__(256) void window_flags_kernel(const float* __restri
 
 hipError_t launch_chunk_sums(const float* g, int B, int T, int H, float* chunk_sums, hipStream_t s) {
     const int N = (T + kChunk - 1) / kChunk;
-    dim3 grid((N + kChunksPerBlock - 1) / kChunksPerBlock, B);
+    dim3 grid(N, B);
     hipLaunchKernelGGL(chunk_sums_kernel, grid, dim3(256), 0, s, g, T, H, N, chunk_sums);
     return hipGetLastError();
 }

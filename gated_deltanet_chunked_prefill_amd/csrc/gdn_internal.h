@@ -12,14 +12,17 @@ namespace gdn {
 //   flags      [B*H] int32        1 = window head
 //   maxwin     [B*H]              max window log-decay
 //   hs         [B*H, P, dk, dv]   true state entering segment p (p >= 1) of an exact head
-//   hs_cnt     [B*H, P] int32     number of state waves that have published hs[bh, p]
+//   hs_cnt     [B*H, P] int32     parts of hs[bh, p] published (complete at 16)
+//   bz         [B*H, P, dk, dv]   final state of segment p run from a zero state
+//   mt         [B*H, P, 2, dk, dk] bf16  gate-free transition of segment p, as hi and lo parts
+//   eg         [B*H, P]           exp(sum of g over segment p)
+//   tr_cnt     [B*H, P] int32     number of waves that have published bz, mt, eg of segment p
 //   plan       FwdPlan            segment counts, job count, job counter
-//   jobs       [B*H*P] TaskRec    the work queue of the split forward
+//   jobs       [B*H*(2P+3)] TaskRec  the work queue of the split forward
 //
 // A job is one run of the fused chunk loop over chunks [c_begin, c_end) of head
-// bh, with outputs from chunk c_out on.  mode = pass-1 marks the middle
-// segments of an exact head: the run from a zero state is followed, in the same
-// job, by the composition of the true state and the run that writes outputs.
+// bh, with outputs from chunk c_out on, or (mode = chain) the composition of
+// the states entering segments seg+1 .. c_end of head bh.
 struct TaskRec {
     int bh, seg, c_begin, c_out, c_end, mode, init, dst;
 };
@@ -45,9 +48,16 @@ struct FwdParams {
     int P;             // segment slots per head (1 = no split)
     int w;             // window length in chunks
     float scale;
-    const int32_t* flags;  // nullable: all heads exact
+    const float* sums;     // split forward with window heads: chunk sums of g (null: all heads exact)
+    int32_t* flags;        // written by the plan kernel when sums is set: 1 = window head
+    float* maxwin;         // its window maxima
+    float log_eps;
     float* hs;
     int* hs_cnt;
+    float* bz;
+    __bf16* mt;
+    float* eg;
+    int* tr_cnt;
     float* hstore;     // nullable: [B*H, N+1, dk, dv] state entering each chunk, then the final state
     FwdPlan* plan;     // split forward: written by the plan kernel
     TaskRec* jobs;
