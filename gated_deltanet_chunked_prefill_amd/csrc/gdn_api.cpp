@@ -75,8 +75,9 @@ gdn_options resolve(const gdn_options* opt) {
 gdn_status check_options(const gdn_options& o, int N) {
     if (o.split_mode < 0 || o.split_mode > 2)
         return fail(GDN_ERR_INVALID_ARG, "split_mode must be 0, 1 or 2 (got %d)", o.split_mode);
-    if (o.split_mode == 2 && (o.n_segments < 1 || o.n_segments > N))
-        return fail(GDN_ERR_INVALID_ARG, "n_segments must be in [1, %d] (got %d)", N, o.n_segments);
+    const int pmax = N < gdn::kMaxSegments ? N : gdn::kMaxSegments;
+    if (o.split_mode == 2 && (o.n_segments < 1 || o.n_segments > pmax))
+        return fail(GDN_ERR_INVALID_ARG, "n_segments must be in [1, %d] (got %d)", pmax, o.n_segments);
     if (o.window_chunks < 1) return fail(GDN_ERR_INVALID_ARG, "window_chunks must be >= 1");
     if (!(o.log_eps < 0.f)) return fail(GDN_ERR_INVALID_ARG, "log_eps must be negative");
     return GDN_OK;
@@ -112,7 +113,7 @@ int plan(int B, int T, int H, int num_cus, const gdn_options& o) {
 }
 
 struct FwdLayout {
-    size_t chunk_sums, flags, maxwin, hs, hs_cnt, bz, mt, eg, tr_cnt, plan, jobs, total;
+    size_t wpart, flags, maxwin, head_map, hs, counters, bz, mt, eg, plan, jobs, total;
 };
 
 FwdLayout fwd_layout(int B, int T, int H, int P) {
@@ -120,15 +121,15 @@ FwdLayout fwd_layout(int B, int T, int H, int P) {
     if (P <= 1) return L;
     const size_t N = num_chunks(T), bh = (size_t)B * H, SS = 128 * 128;
     size_t off = 0;
-    L.chunk_sums = off; off += align_up((size_t)B * N * H * sizeof(float));
+    L.wpart = off;      off += align_up((size_t)B * gdn::window_groups(T) * H * sizeof(float));
     L.flags = off;      off += align_up(bh * sizeof(int32_t));
     L.maxwin = off;     off += align_up(bh * sizeof(float));
+    L.head_map = off;   off += align_up(2 * bh * sizeof(int32_t));
     L.hs = off;         off += align_up(bh * P * SS * sizeof(float));
-    L.hs_cnt = off;     off += align_up(bh * P * sizeof(int32_t));
+    L.counters = off;   off += align_up(2 * bh * P * sizeof(int32_t));   // hs_cnt, then tr_cnt
     L.bz = off;         off += align_up(bh * P * SS * sizeof(float));
     L.mt = off;         off += align_up(bh * P * 2 * SS * sizeof(uint16_t));
     L.eg = off;         off += align_up(bh * P * sizeof(float));
-    L.tr_cnt = off;     off += align_up(bh * P * sizeof(int32_t));
     L.plan = off;       off += align_up(sizeof(gdn::FwdPlan));
     L.jobs = off;       off += align_up(bh * (2 * P + 3) * sizeof(gdn::TaskRec));
     L.total = off;
@@ -241,7 +242,7 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
     gdn::FwdParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.o = o; p.ht = ht;
     p.B = B; p.T = T; p.H = H; p.N = N; p.P = P; p.w = op.window_chunks; p.scale = scale;
-    p.sums = nullptr;
+    p.wpart = nullptr;
     const bool bf16 = dtype == GDN_BF16;
     hipError_t e;
     if (P == 1) {
@@ -250,27 +251,31 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
         return GDN_OK;
     }
     char* ws = (char*)workspace;
+    const int nbh = B * H;
     p.hs = (float*)(ws + L.hs);
-    p.hs_cnt = (int*)(ws + L.hs_cnt);
+    p.hs_cnt = (int*)(ws + L.counters);
+    p.tr_cnt = p.hs_cnt + (size_t)nbh * P;
     p.bz = (float*)(ws + L.bz);
     p.mt = (__bf16*)(ws + L.mt);
     p.eg = (float*)(ws + L.eg);
-    p.tr_cnt = (int*)(ws + L.tr_cnt);
     p.plan = (gdn::FwdPlan*)(ws + L.plan);
     p.jobs = (gdn::TaskRec*)(ws + L.jobs);
     p.cus = cus;
     p.forced = op.split_mode == 2 ? 1 : 0;
     p.flags = (int32_t*)(ws + L.flags);
     p.maxwin = (float*)(ws + L.maxwin);
+    p.head_map = (int*)(ws + L.head_map);
     p.log_eps = op.log_eps;
-    if (op.use_window) {
-        float* sums = (float*)(ws + L.chunk_sums);
-        e = recorded(GDN_LAUNCH_GATE_SUMS, s, [&] { return gdn::launch_chunk_sums(g, B, T, H, sums, s); });
-        if (e != hipSuccess) return hip_fail(e, "gate scan launch");
-        p.sums = sums;   // the plan kernel derives the window flags from these
-    }
-    e = recorded(GDN_LAUNCH_FWD_PLAN, s, [&] { return gdn::launch_plan(p, s); });
-    if (e != hipSuccess) return hip_fail(e, "forward plan launch");
+    p.n_groups = gdn::window_groups(T);
+    // window heads only when a window fits the sequence (no head qualifies
+    // otherwise) and the first launch can stage it
+    if (op.use_window && op.window_chunks <= N && op.window_chunks <= gdn::max_window_chunks())
+        p.wpart = (float*)(ws + L.wpart);
+    e = recorded(GDN_LAUNCH_FWD_PLAN, s, [&] {
+        return gdn::launch_fwd_prep(g, B, T, H, op.window_chunks, const_cast<float*>(p.wpart), p.hs_cnt,
+                                    2 * nbh * P, (int*)p.plan, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "forward preparation launch");
     e = recorded(GDN_LAUNCH_FWD_QUEUE, s, [&] { return gdn::launch_fwd(p, gdn::PHASE_QUEUE, bf16, s); });
     if (e != hipSuccess) return hip_fail(e, "forward launch");
     return GDN_OK;

@@ -686,20 +686,42 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_kernel(FwdParams prm) {
         run_task<T, MODE_FULL>(prm, sm, tk);
 }
 
+template <typename T>
+__device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm);
+
 // Persistent workgroups of the split forward: take jobs until the list is empty.
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_queue_kernel(FwdParams prm) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     Smem<T>& sm = *reinterpret_cast<Smem<T>*>(smem_raw);
-    const int n_jobs = uni(prm.plan->n_jobs);
-    for (;;) {
-        if (threadIdx.x == 0) sm.islot[0] = atomicAdd(&prm.plan->next, 1);
+    // workgroup 0 writes the plan and the job list, then releases the others
+    // (the ready word was cleared by the preceding launch)
+    // (the ready word, cleared by the preceding launch, becomes n_jobs + 1; the
+    // job records are written back before it and read with device-coherent loads)
+    int* const ready = &prm.plan->ready;
+    if (blockIdx.x == 0) {
+        plan_wg<T>(prm, sm);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         __syncthreads();
-        const int j = uni(sm.islot[0]);
-        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_store(ready, prm.plan->n_jobs + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (threadIdx.x < 64) {
+        wait_published(ready, 1, &prm.plan->error);
+    }
+    if (threadIdx.x == 0)
+        sm.islot[1] = __hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - 1;
+    __syncthreads();
+    const int n_jobs = uni(sm.islot[1]);
+    // the first job of every workgroup is its index; later ones come from the counter
+    int j = blockIdx.x;
+    for (;; ) {
         if (j >= n_jobs) break;
-        const TaskRec rec = prm.jobs[j];
-        const Task tk{rec.bh, rec.seg, rec.c_begin, rec.c_out, rec.c_end, rec.mode, rec.init, rec.dst};
+        // job records read with device-coherent vector loads (written this launch)
+        const int* const jr = reinterpret_cast<const int*>(prm.jobs + j);
+        int f[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = uni(__hip_atomic_load(jr + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        const Task tk{f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]};
         if (tk.mode == MODE_CHAIN) {
             if (wave_id() < 4)
                 chain_state<T>(prm, sm, tk);
@@ -710,6 +732,10 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_queue_kernel(FwdParams pr
         } else {
             run_task<T, MODE_FULL>(prm, sm, tk);
         }
+        if (threadIdx.x == 0) sm.islot[0] = (int)gridDim.x + atomicAdd(&prm.plan->next, 1);
+        __syncthreads();
+        j = uni(sm.islot[0]);
+        __syncthreads();
     }
 }
 
@@ -742,41 +768,30 @@ constexpr float kCostPass1 = 1.35f;
 constexpr float kCostLink = 0.8f;
 constexpr int kSeg0Weight = 11;
 
-__device__ void choose_segments(int n_e, int n_w, int N, int w, int cus, int pmax, int& Pe, int& Pw) {
-    float best = 3.0e38f;
-    Pe = 1;
-    Pw = 1;
+// Estimated makespan (in full chunk steps) of P segments per exact head; also
+// returns the window heads' segment count.
+__device__ float plan_cost(int P, int n_e, int n_w, int N, int w, int cus, int pmax, int& Pw) {
     const int pw_cap = N / w > 1 ? N / w : 1;
-    for (int P = 1; P <= (n_e > 0 ? pmax : 1); ++P) {
-        if (P == 2) continue;   // two segments only serialise
-        const int ecus = n_e * (P == 1 ? 1 : P - 1);
-        if (P > 1 && ecus > cus) break;
-        float te = 0.f;
-        if (n_e > 0)
-            te = P == 1 ? (float)N
-                        : 8.f * N * (1.f + kCostPass1) / (kSeg0Weight + 8 * (P - 1)) + (P - 2) * kCostLink;
-        const int free = cus - ecus > 0 ? cus - ecus : 0;
-        int pw = 1;
-        float tw = 0.f;
-        if (n_w > 0) {
-            if (free >= n_w) {
-                pw = free / n_w;
-                if (pw > pmax) pw = pmax;
-                if (pw > pw_cap) pw = pw_cap;
-                tw = (float)N / pw + (pw > 1 ? w : 0);
-            } else if (free > 0) {
-                tw = (float)((n_w + free - 1) / free) * N;
-            } else {
-                tw = te + N;
-            }
-        }
-        const float t = te > tw ? te : tw;
-        if (t < best * 0.999f) {
-            best = t;
-            Pe = P;
-            Pw = pw;
+    const int ecus = n_e * (P == 1 ? 1 : P - 1);
+    float te = 0.f;
+    if (n_e > 0)
+        te = P == 1 ? (float)N : 8.f * N * (1.f + kCostPass1) / (kSeg0Weight + 8 * (P - 1)) + (P - 2) * kCostLink;
+    const int free = cus - ecus > 0 ? cus - ecus : 0;
+    Pw = 1;
+    float tw = 0.f;
+    if (n_w > 0) {
+        if (free >= n_w) {
+            Pw = free / n_w;
+            if (Pw > pmax) Pw = pmax;
+            if (Pw > pw_cap) Pw = pw_cap;
+            tw = (float)N / Pw + (Pw > 1 ? w : 0);
+        } else if (free > 0) {
+            tw = (float)((n_w + free - 1) / free) * N;
+        } else {
+            tw = te + N;
         }
     }
+    return te > tw ? te : tw;
 }
 
 __device__ __forceinline__ void put_job(TaskRec* jobs, int j, int bh, int seg, int cb, int co, int ce,
@@ -787,11 +802,9 @@ __device__ __forceinline__ void put_job(TaskRec* jobs, int j, int bh, int seg, i
     jobs[j] = r;
 }
 
-constexpr int kPlanThreads = 1024;
-
-// Exclusive prefix sum over the threads of the workgroup (kPlanThreads).
+// Exclusive prefix sum over the kThreads threads of the workgroup.
 __device__ int block_exclusive_scan(int x, int* s_wave, int& total) {
-    constexpr int NW = kPlanThreads / 64;
+    constexpr int NW = kThreads / 64;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     int incl = x;
 #pragma unroll
@@ -808,6 +821,7 @@ __device__ int block_exclusive_scan(int x, int* s_wave, int& total) {
         before += i < wv ? s_wave[i] : 0;
         total += s_wave[i];
     }
+    __syncthreads();
     return before + incl - x;
 }
 
@@ -815,125 +829,163 @@ __device__ int seg_bound(long long num, long long den, int N) {
     return (int)(((double)N * (double)num) / (double)den);
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(FwdParams prm) {
-    __shared__ int s_wave[kPlanThreads / 64];
+// Planner scratch in the workgroup's LDS (used before any job runs).
+struct PlanLds {
+    int bound[kMaxSegments + 1];
+    int wave[kThreads / 64];
+    int par[2];
+};
+
+// The planner, run by workgroup 0 of the persistent launch before the jobs.
+template <typename T>
+__device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
+    static_assert(sizeof(PlanLds) <= sizeof(Smem<T>), "planner scratch exceeds the LDS");
+    PlanLds& pl = *reinterpret_cast<PlanLds*>(&sm);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int nbh = prm.B * prm.H, N = prm.N, pmax = prm.P, w = prm.w;
-    // 1. window flags (talk summary, paragraph 5): per head the largest sum of g
-    //    over w consecutive chunks; a wave per head, each lane a contiguous run of
-    //    chunk windows summed with a running window sum
-    if (prm.sums) {
-        const int R = (N + 63) / 64;
-        for (int bh = wv; bh < nbh; bh += kPlanThreads / 64) {
-            const int b = bh / prm.H, h = bh % prm.H;
-            const float* s = prm.sums + (size_t)b * N * prm.H + h;
+    const int B = uni(prm.B), H = uni(prm.H), nbh = B * H, N = uni(prm.N), pmax = uni(prm.P), w = uni(prm.w);
+    const float* const wpart = uni(prm.wpart);
+    int* const flags = uni(prm.flags);
+    // 1. window flags (talk summary, paragraph 5): a head is a window head when
+    //    its largest sum of g over w consecutive chunks is at most log_eps; the
+    //    first launch left the maxima per group of chunks, a wave reduces a head
+    if (wpart) {
+        // a run of tph threads per head (a power of two up to 64), all of a
+        // thread's loads issued at once
+        const int NG = uni(prm.n_groups);
+        int tph = 64;
+        while (tph > 1 && tph * nbh > kThreads) tph >>= 1;
+        const int hpr = kThreads / tph;   // heads per round
+        for (int h0 = 0; h0 < nbh; h0 += hpr) {
+            const int bh = h0 + tid / tph, k = tid % tph;
             float best = -INFINITY;
-            const int ca = lane * R < w - 1 ? w - 1 : lane * R;
-            const int cb = (lane + 1) * R < N ? (lane + 1) * R : N;
-            if (ca < cb) {
-                // loads in batches of eight so that each batch is in flight at once
-                float acc = 0.f;
-                for (int j0 = ca - w + 1; j0 <= ca; j0 += 8) {
+            if (bh < nbh) {
+                const int b = bh / H, h = bh % H;
+                for (int q0 = k; q0 < NG; q0 += 8 * tph) {
                     float v[8];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) v[u] = j0 + u <= ca ? s[(size_t)(j0 + u) * prm.H] : 0.f;
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) acc += v[u];
-                }
-                best = acc;
-                for (int c0 = ca + 1; c0 < cb; c0 += 8) {
-                    float a[8], d[8];
-#pragma unroll
                     for (int u = 0; u < 8; ++u) {
-                        const bool in = c0 + u < cb;
-                        a[u] = in ? s[(size_t)(c0 + u) * prm.H] : 0.f;
-                        d[u] = in ? s[(size_t)(c0 + u - w) * prm.H] : 0.f;
+                        const int q = q0 + u * tph;
+                        v[u] = wpart[((size_t)b * NG + (q < NG ? q : NG - 1)) * H + h];
                     }
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        if (c0 + u < cb) {
-                            acc += a[u] - d[u];
-                            best = acc > best ? acc : best;
-                        }
-                    }
+                    for (int u = 0; u < 8; ++u) best = v[u] > best ? v[u] : best;
                 }
             }
-#pragma unroll
-            for (int d = 32; d > 0; d >>= 1) {
+            for (int d = tph >> 1; d > 0; d >>= 1) {
                 const float o = __shfl_xor(best, d, 64);
                 best = o > best ? o : best;
             }
-            if (lane == 0) {
-                prm.flags[bh] = (N >= w && best <= prm.log_eps) ? 1 : 0;
+            if (bh < nbh && k == 0) {
+                flags[bh] = (N >= w && best <= prm.log_eps) ? 1 : 0;
                 if (prm.maxwin) prm.maxwin[bh] = best;
             }
         }
         __syncthreads();
     }
-    // 2. rank the exact and the window heads, choose the segment counts
-    const int per = (nbh + kPlanThreads - 1) / kPlanThreads;
+    // 2. rank the exact and the window heads (head_map: exact heads by rank,
+    //    then window heads by rank) and choose the segment counts
+    const int per = (nbh + kThreads - 1) / kThreads;
     const int lo = tid * per < nbh ? tid * per : nbh;
     const int hi = lo + per < nbh ? lo + per : nbh;
-    auto exact = [&](int bh) { return prm.sums == nullptr || prm.flags[bh] == 0; };
+    auto exact = [&](int bh) { return wpart == nullptr || flags[bh] == 0; };
     int ne = 0;
     for (int bh = lo; bh < hi; ++bh) ne += exact(bh) ? 1 : 0;
     int n_e = 0;
-    int re = block_exclusive_scan(ne, s_wave, n_e);   // exact rank of this thread's first head
-    int rw = lo - re;                                  // window rank
+    int re = block_exclusive_scan(ne, pl.wave, n_e);
+    int rw = lo - re;
     const int n_w = nbh - n_e;
-    int Pe = pmax, Pw = pmax;
-    if (!prm.forced) choose_segments(n_e, n_w, N, w, prm.cus, pmax, Pe, Pw);
+    int* const head_map = uni(prm.head_map);
+    for (int bh = lo; bh < hi; ++bh) {
+        if (exact(bh))
+            head_map[re++] = bh;
+        else
+            head_map[n_e + rw++] = bh;
+    }
+    if (wv == 0) {
+        // candidate segment counts one per lane, the cheapest wins (ties: fewer)
+        int Pe = pmax, Pw = pmax;
+        if (!prm.forced) {
+            float best = 3.0e38f;
+            int bP = 1, bPw = 1;
+            const int pcap = n_e > 0 ? pmax : 1;
+            for (int P0 = 1; P0 <= pcap; P0 += 64) {
+                int P = P0 + lane, pw = 1;
+                float t = 3.0e38f;
+                const bool ok = P <= pcap && P != 2 && (P == 1 || n_e * (P - 1) <= prm.cus);
+                if (ok) t = plan_cost(P, n_e, n_w, N, w, prm.cus, pmax, pw);
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const float ot = __shfl_xor(t, d, 64);
+                    const int oP = __shfl_xor(P, d, 64), opw = __shfl_xor(pw, d, 64);
+                    if (ot < t || (ot == t && oP < P)) {
+                        t = ot;
+                        P = oP;
+                        pw = opw;
+                    }
+                }
+                if (t < best * 0.999f) {
+                    best = t;
+                    bP = P;
+                    bPw = pw;
+                }
+            }
+            Pe = bP;
+            Pw = bPw;
+        }
+        if (lane == 0) {
+            pl.par[0] = Pe;
+            pl.par[1] = Pw;
+        }
+    }
+    __syncthreads();
+    const int Pe = pl.par[0], Pw = pl.par[1];
     const int g_win = n_e + (Pe >= 3 ? n_e * (Pe - 2) : 0);
     const int g_chain = g_win + n_w * Pw;
     const int g_p3 = g_chain + (Pe >= 3 ? 4 * n_e : 0);
     const int n_jobs = g_p3 + (Pe >= 2 ? n_e * (Pe - 1) : 0);
     if (tid == 0) {
-        FwdPlan* pl = prm.plan;
-        pl->P_e = Pe;
-        pl->P_w = Pw;
-        pl->n_exact = n_e;
-        pl->n_window = n_w;
-        pl->n_jobs = n_jobs;
-        pl->next = 0;
-        pl->error = 0;
+        FwdPlan* const fp = uni(prm.plan);
+        fp->P_e = Pe;
+        fp->P_w = Pw;
+        fp->n_exact = n_e;
+        fp->n_window = n_w;
+        fp->n_jobs = n_jobs;
     }
-    // 3. the job list
+    // 3. the job list, one job per thread (segment bounds of exact heads once)
     const int w0 = prm.forced ? 8 : kSeg0Weight;
     const long long den = w0 + 8 * (Pe - 1);
-    auto bound = [&](int p) { return p <= 0 ? 0 : p >= Pe ? N : seg_bound(w0 + 8 * (p - 1), den, N); };
+    for (int p = tid; p <= Pe; p += kThreads)
+        pl.bound[p] = p <= 0 ? 0 : p >= Pe ? N : seg_bound(w0 + 8 * (p - 1), den, N);
+    __syncthreads();
     const bool has_h0 = prm.h0 != nullptr, has_ht = prm.ht != nullptr;
     const int dst_last = has_ht ? DST_HT : DST_NONE;
-    for (int bh = lo; bh < hi; ++bh) {
-        if (exact(bh)) {
-            const int init0 = has_h0 ? INIT_H0 : INIT_ZERO;
-            if (Pe == 1) {
-                put_job(prm.jobs, re, bh, 0, 0, 0, N, MODE_FULL, init0, dst_last);
-            } else {
-                put_job(prm.jobs, re, bh, 0, 0, 0, bound(1), MODE_FULL, init0, DST_HS_NEXT);
-                for (int p = 1; p + 1 < Pe; ++p)
-                    put_job(prm.jobs, n_e + (p - 1) * n_e + re, bh, p, bound(p), bound(p + 1), bound(p + 1),
-                            MODE_PASS1, INIT_ZERO, DST_TRANSITION);
-                if (Pe >= 3)
-                    for (int cb = 0; cb < 4; ++cb)   // one chain job per 32-column block
-                        put_job(prm.jobs, g_chain + 4 * re + cb, bh, 1, cb, 0, Pe - 1, MODE_CHAIN, 0, 0);
-                for (int p = 1; p < Pe; ++p)
-                    put_job(prm.jobs, g_p3 + (p - 1) * n_e + re, bh, p, bound(p), bound(p), bound(p + 1),
-                            MODE_FULL, INIT_HS_WAIT, p == Pe - 1 ? dst_last : DST_NONE);
-            }
-            ++re;
-        } else {
-            for (int p = 0; p < Pw; ++p) {
-                const int s = (int)(((long long)p * N) / Pw), e = (int)(((long long)(p + 1) * N) / Pw);
-                const int cb = s - w > 0 ? s - w : 0;
-                put_job(prm.jobs, g_win + p * n_w + rw, bh, p, cb, s, e, MODE_FULL,
-                        (cb == 0 && has_h0) ? INIT_H0 : INIT_ZERO, p == Pw - 1 ? dst_last : DST_NONE);
-            }
-            ++rw;
+    const int init0 = has_h0 ? INIT_H0 : INIT_ZERO;
+    TaskRec* const jobs = uni(prm.jobs);
+    for (int j = tid; j < n_jobs; j += kThreads) {
+        if (j < n_e) {   // segment 0 (or the whole sequence)
+            const int bh = head_map[j];
+            if (Pe == 1)
+                put_job(jobs, j, bh, 0, 0, 0, N, MODE_FULL, init0, dst_last);
+            else
+                put_job(jobs, j, bh, 0, 0, 0, pl.bound[1], MODE_FULL, init0, DST_HS_NEXT);
+        } else if (j < g_win) {   // pass-1 of segment p, segment-major
+            const int p = 1 + (j - n_e) / n_e, e = (j - n_e) % n_e;
+            put_job(jobs, j, head_map[e], p, pl.bound[p], pl.bound[p + 1], pl.bound[p + 1], MODE_PASS1,
+                    INIT_ZERO, DST_TRANSITION);
+        } else if (j < g_chain) {   // window head segment p, segment-major
+            const int p = (j - g_win) / n_w, r = (j - g_win) % n_w;
+            const int sb = (int)(((long long)p * N) / Pw), e = (int)(((long long)(p + 1) * N) / Pw);
+            const int cb = sb - w > 0 ? sb - w : 0;
+            put_job(jobs, j, head_map[n_e + r], p, cb, sb, e, MODE_FULL,
+                    (cb == 0 && has_h0) ? INIT_H0 : INIT_ZERO, p == Pw - 1 ? dst_last : DST_NONE);
+        } else if (j < g_p3) {   // chain, one job per 32-column block
+            const int e = (j - g_chain) / 4, cb = (j - g_chain) % 4;
+            put_job(jobs, j, head_map[e], 1, cb, 0, Pe - 1, MODE_CHAIN, 0, 0);
+        } else {   // pass-3 of segment p, segment-major
+            const int p = 1 + (j - g_p3) / n_e, e = (j - g_p3) % n_e;
+            put_job(jobs, j, head_map[e], p, pl.bound[p], pl.bound[p], pl.bound[p + 1], MODE_FULL,
+                    INIT_HS_WAIT, p == Pe - 1 ? dst_last : DST_NONE);
         }
-    }
-    for (int i = tid; i < nbh * pmax; i += kPlanThreads) {
-        prm.hs_cnt[i] = 0;
-        prm.tr_cnt[i] = 0;
     }
 }
 
@@ -975,9 +1027,6 @@ hipError_t launch_fwd(const FwdParams& p, int phase, bool bf16, hipStream_t s) {
     return bf16 ? launch_fwd_t<__bf16>(p, phase, s) : launch_fwd_t<float>(p, phase, s);
 }
 
-hipError_t launch_plan(const FwdParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, p);
-    return hipGetLastError();
-}
+
 
 }  // namespace gdn

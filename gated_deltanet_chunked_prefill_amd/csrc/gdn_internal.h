@@ -8,21 +8,25 @@ namespace gdn {
 
 // Workspace of the split forward, per head bh = b*H + h and segment slot p < P
 // (P = the largest segment count the call may use; 256-byte aligned sub-buffers):
-//   chunk_sums [B, N, H]          gate scan scratch
+//   wpart      [B, NG, H]         window maxima per group of chunks (gate scan)
 //   flags      [B*H] int32        1 = window head
 //   maxwin     [B*H]              max window log-decay
 //   hs         [B*H, P, dk, dv]   true state entering segment p (p >= 1) of an exact head
 //   hs_cnt     [B*H, P] int32     parts of hs[bh, p] published (complete at 16)
+//              (hs_cnt and tr_cnt are one block, reset by the first launch)
 //   bz         [B*H, P, dk, dv]   final state of segment p run from a zero state
 //   mt         [B*H, P, 2, dk, dk] bf16  gate-free transition of segment p, as hi and lo parts
 //   eg         [B*H, P]           exp(sum of g over segment p)
 //   tr_cnt     [B*H, P] int32     number of waves that have published bz, mt, eg of segment p
+//   head_map   [2*B*H] int32      heads by exact rank, then by window rank
 //   plan       FwdPlan            segment counts, job count, job counter
 //   jobs       [B*H*(2P+3)] TaskRec  the work queue of the split forward
 //
 // A job is one run of the fused chunk loop over chunks [c_begin, c_end) of head
 // bh, with outputs from chunk c_out on, or (mode = chain) the composition of
 // the states entering segments seg+1 .. c_end of head bh.
+constexpr int kMaxSegments = 1024;   // the device planner's limit on segments per head
+
 struct TaskRec {
     int bh, seg, c_begin, c_out, c_end, mode, init, dst;
 };
@@ -32,7 +36,7 @@ struct FwdPlan {
     int n_jobs;
     int next;          // next job to hand out (atomic counter)
     int error;         // set when a wait for another job's state ran out (never expected)
-    int pad;
+    int ready;         // 1 once the plan and the job list are written
 };
 
 struct FwdParams {
@@ -48,7 +52,10 @@ struct FwdParams {
     int P;             // segment slots per head (1 = no split)
     int w;             // window length in chunks
     float scale;
-    const float* sums;     // split forward with window heads: chunk sums of g (null: all heads exact)
+    const float* wpart;    // split forward with window heads: window maxima per group of chunks
+                           // (null: all heads exact)
+    int n_groups;          // groups of chunks in wpart
+    int* head_map;         // [2*B*H] planner scratch: heads by exact rank, then by window rank
     int32_t* flags;        // written by the plan kernel when sums is set: 1 = window head
     float* maxwin;         // its window maxima
     float log_eps;
@@ -72,8 +79,11 @@ struct FwdParams {
 enum FwdPhase { PHASE_SINGLE = 0, PHASE_QUEUE = 1, PHASE_STATES = 2 };
 
 hipError_t launch_fwd(const FwdParams& p, int phase, bool bf16, hipStream_t s);
-hipError_t launch_plan(const FwdParams& p, hipStream_t s);
 hipError_t launch_chunk_sums(const float* g, int B, int T, int H, float* chunk_sums, hipStream_t s);
+int window_groups(int T);
+int max_window_chunks();
+hipError_t launch_fwd_prep(const float* g, int B, int T, int H, int w, float* part, int* zero, int nzero,
+                           int* plan_words, hipStream_t s);
 hipError_t launch_window_flags(const float* chunk_sums, int B, int T, int H, int w, float log_eps,
                                int32_t* flags, float* maxwin, hipStream_t s);
 

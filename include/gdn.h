@@ -70,7 +70,7 @@ typedef struct {
      *   1 = off (one segment per head),
      *   2 = use n_segments. */
     int split_mode;
-    int n_segments;     /* used when split_mode == 2; 1 <= n_segments <= number of chunks      */
+    int n_segments;     /* used when split_mode == 2; 1 <= n_segments <= min(number of chunks, 1024) */
     /* Sliding-window heads (paragraph 5): when 1 and the sequence is split, heads
      * whose every window of window_chunks chunks decays by at least exp(log_eps)
      * skip the correction and warm up from a zero state over the previous
@@ -96,10 +96,12 @@ int gdn_plan_segments(int B, int T, int H, int num_cus, const gdn_options* opt);
 /* Read back the plan the last split forward with these shapes, options and
  * workspace used (synchronises `stream`).  info[0..7]: segments of an exact
  * head, segments of a window head, number of exact heads, number of window
- * heads, number of jobs, jobs handed out (including one empty request per
- * workgroup), error flag (nonzero: a wait for another job's state ran out; the
- * outputs are then invalid), 0.  Without a split: {1, 1, B*H, 0, B*H, 0, 0, 0}
- * and the workspace is not read. */
+ * heads, number of jobs, requests made to the job counter (a workgroup's first
+ * job is its index; each later request, including one final empty request per
+ * workgroup that ran a job, goes through the counter), error flag (nonzero: a
+ * wait for another job's state ran out; the outputs are then invalid), and the
+ * number of jobs + 1 once the plan was written.  Without a split:
+ * {1, 1, B*H, 0, B*H, 0, 0, 0}; the workspace is not read then. */
 gdn_status gdn_chunk_fwd_plan_info(int B, int T, int H, const gdn_options* opt, const void* workspace,
                                    int32_t* info, void* stream);
 
@@ -172,8 +174,8 @@ typedef enum {
     GDN_LAUNCH_GATE_SUMS = 0,   /* gate scan: per-chunk sums of g                     */
     GDN_LAUNCH_GATE_FLAGS = 1,  /* gate scan: window maxima and flags                 */
     GDN_LAUNCH_FWD_SINGLE = 2,  /* fused forward, unsplit                             */
-    GDN_LAUNCH_FWD_PLAN = 3,    /* split forward: segment counts and job list         */
-    GDN_LAUNCH_FWD_QUEUE = 4,   /* split forward: persistent workgroups over the jobs */
+    GDN_LAUNCH_FWD_PLAN = 3,    /* split forward: chunk sums of g, planner reset      */
+    GDN_LAUNCH_FWD_QUEUE = 4,   /* split forward: planner, then persistent workgroups over the jobs */
     GDN_LAUNCH_BWD_STATES = 5,  /* backward: state entering every chunk (forward kernel) */
     GDN_LAUNCH_BWD_DH = 6,      /* backward: state gradient, end to start             */
     GDN_LAUNCH_BWD_LOCAL = 7    /* backward: local gradients of every chunk           */
