@@ -39,7 +39,7 @@ STATE_BYTES = 128 * 128 * 4
 # measured HBM traffic of the forward kernel (FETCH_SIZE / WRITE_SIZE counter runs,
 # calibrated against a plain streaming copy); valid only for the kernel source it
 # was taken from
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gdn_fwd_kernel_bf16_t32768_h32_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gdn_fwd_queue_kernel_bf16_t32768_h32_traffic.txt")
 KERNEL_SOURCES = ["gated_deltanet_chunked_prefill_amd/csrc/gdn_fwd.hip",
                   "gated_deltanet_chunked_prefill_amd/csrc/gdn_chunk.h",
                   "gated_deltanet_chunked_prefill_amd/csrc/gdn_device.h",
