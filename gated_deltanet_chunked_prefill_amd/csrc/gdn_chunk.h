@@ -535,13 +535,19 @@ __device__ __forceinline__ void load_state(const float* src, int w, int lane, f3
         for (int r = 0; r < 16; ++r)
             Hs[ht][r] = src[(32 * ht + rho(g, r)) * kDv + 32 * w + n];
 }
+// Buffer stores: one lane offset register, the row offsets as constants
+// (keeps the 64 stores from holding 64 address registers).
 __device__ __forceinline__ void store_state(float* dst, int w, int lane, const f32x16* Hs) {
     const int n = lane & 31, g = lane >> 5;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, (int)(kDk * kDv * 4), 0x00020000);
+    const int voff = ((4 * g) * kDv + 32 * w + n) * 4;
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            dst[(32 * ht + rho(g, r)) * kDv + 32 * w + n] = Hs[ht][r];
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Hs[ht][r]), rs, voff,
+                                                  (32 * ht + 8 * (r >> 2) + (r & 3)) * kDv * 4, 0);
 }
 
 // Number of valid tokens in chunk c of a sequence of T tokens.
