@@ -131,7 +131,7 @@ __device__ __noinline__ void dh_state_loop(const BwdParams& prm, Smem<T>& sm, in
         for (int i = 0; i < N; ++i) {
             const int c = N - 1 - i;
             const int slot = i % 3, vb = i & 1;
-            store_state(dst + (size_t)c * SS, L.w, L.lane, dH);
+            store_state(uni(dst + (size_t)c * SS), L.w, L.lane, dH);
             dh_chunk_step<T>(L, sm.kt[slot], sm.qt[slot], sm.vt[vb], sm.t32[vb], sm.gam_vec[vb],
                              sm.e_vec[vb], sm.gc[vb][0], scale, dH);
             lds_barrier();
@@ -142,12 +142,12 @@ __device__ __noinline__ void dh_state_loop(const BwdParams& prm, Smem<T>& sm, in
             lds_barrier();
             lds_barrier();
             lds_barrier();
-            store_state(dst + (size_t)c * SS, L.w, L.lane, dH);
+            store_state(uni(dst + (size_t)c * SS), L.w, L.lane, dH);
             dh_chunk_step<T>(L, sm.kt[0], sm.qt[0], sm.vt[0], sm.t32[0], sm.gam_vec[0], sm.e_vec[0],
                              sm.gc[0][0], scale, dH);
         }
     }
-    if (dh0) store_state(dh0 + (size_t)bh * SS, L.w, L.lane, dH);
+    if (dh0) store_state(uni(dh0 + (size_t)bh * SS), L.w, L.lane, dH);
 }
 
 // Prep waves: stream K, Q, dO of the chunks in reverse order and prep each one a
