@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_kernel(BwdPara
         float gv, bv;
         load_gate_beta(prm.g, prm.beta, Tn, H, b, h, c, lane, gv, bv);
         const float gam = wave_inclusive_scan(gv);
-        const float gC = __shfl(gam, 63, 64);
+        const float gC = lane_value(gam, 63);
         sm.gam[lane] = gam;
         sm.Gam[lane] = __expf(gam);
         sm.E[lane] = __expf(gC - gam);

@@ -96,19 +96,20 @@ __device__ __forceinline__ void lds_st(void* base, uint32_t off, const V& v) {
 // Per-lane LDS addressing.  For bf16 the swizzled byte offsets a lane needs are
 // precomputed once per task into small tables, so every fragment read in the
 // chunk loop is a table register plus an immediate offset:
-//   * rows 32rt + n of a 64 x 128 tile: slot = (2ks + h) ^ 4rt ^ swz(n), whose
-//     low three bits are (c' & 7) ^ swz(n) with c' = (2ks + h) ^ 4rt;
+//   * rows 32rt + n of a 64 x 128 tile: slot = (2ks + h) ^ swz16(n) (swz16 of row
+//     32rt + n equals swz16(n));
 //   * transposing reads of a 64 x 128 tile: lane (i, q, g) of a 16-lane group
-//     reads row 16ks + 8h + a (a = 4g + i/4) and column block 2q + (i/2)%2 of its
-//     32-column window; the slot's low bits are that block ^ a ^ (2ks + h);
+//     reads row r = 16ks + 8h + a (a = 4g + i/4), columns 32ht + 16q + 4(i%4)..+3,
+//     i.e. slot 4ht + x with x = 2q + (i/2)%2; swz16(r) = 4(a%4) + 2h + g, so the
+//     stored slot is 4(ht ^ a%4) + (x ^ (2h + g)) for every ks;
 //   * rows n of a 32 x 32 tile: slot = (2ks + h) ^ swz4(n).
 template <typename T>
 struct Lane {
     int lane, n, g, w;
-    uint32_t a128[8];   // bf16: n*256 + 8g + ((j ^ swz(n)) << 4)
+    uint32_t a128[16];  // bf16: n*256 + 8g + ((j ^ swz16(n)) << 4)
     uint32_t a32[4];    // bf16: n*64 + 8g + ((j ^ swz4(n)) << 4)
-    uint32_t trk[8];    // bf16: transposing-read offsets for column windows 32ht
-    uint32_t trv[8];    // bf16: the same for this wave's V columns 32w
+    uint32_t trk[8];    // bf16: transposing-read offsets, entry 2ht + h (column window 32ht)
+    uint32_t trv[2];    // bf16: the same for this wave's V columns 32w, entry h
 
     __device__ void init(int tid) {
         lane = tid & 63;
@@ -116,18 +117,21 @@ struct Lane {
         g = lane >> 5;
         w = (tid >> 6) & 3;
         if constexpr (sizeof(T) == 2) {
-            const int s = swz(n), s4 = swz4(n);
+            const int s = swz16(n), s4 = swz4(n);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) a128[j] = n * 256 + 8 * g + ((j ^ s) << 4);
+            for (int j = 0; j < 16; ++j) a128[j] = n * 256 + 8 * g + ((j ^ s) << 4);
 #pragma unroll
             for (int j = 0; j < 4; ++j) a32[j] = n * 64 + 8 * g + ((j ^ s4) << 4);
             const int i = lane & 15, q = (lane >> 4) & 1;
             const int a = 4 * g + (i >> 2);
-            const int lam = (2 * q + ((i >> 1) & 1)) ^ a;
+            const int x = 2 * q + ((i >> 1) & 1);
+            const uint32_t base = a * 256 + 8 * (i & 1);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                trk[j] = a * 256 + 8 * (i & 1) + ((j ^ lam) << 4);
-                trv[j] = a * 256 + 8 * (i & 1) + ((j ^ lam ^ (4 * (w & 1))) << 4) + 128 * (w >> 1);
+            for (int h = 0; h < 2; ++h) {
+                const int lo = x ^ (2 * h + g);
+#pragma unroll
+                for (int ht = 0; ht < 4; ++ht) trk[2 * ht + h] = base + ((((ht ^ (a & 3)) << 2) | lo) << 4);
+                trv[h] = base + ((((w ^ (a & 3)) << 2) | lo) << 4);
             }
         }
     }
@@ -136,9 +140,8 @@ struct Lane {
     __device__ __forceinline__ typename FragOf<T>::type f128(const T* tile, int rt, int ks) const {
         if constexpr (sizeof(T) == 2) {
             typedef __bf16 b4 __attribute__((ext_vector_type(4)));
-            const int c0 = (2 * ks) ^ (4 * rt), c1 = (2 * ks + 1) ^ (4 * rt);
-            b4 lo = lds_ld<b4>(tile, a128[c0 & 7] + rt * 8192 + (c0 & 8) * 16);
-            b4 hi = lds_ld<b4>(tile, a128[c1 & 7] + rt * 8192 + (c1 & 8) * 16);
+            b4 lo = lds_ld<b4>(tile, a128[2 * ks] + rt * 8192);
+            b4 hi = lds_ld<b4>(tile, a128[2 * ks + 1] + rt * 8192);
             typename FragOf<T>::type f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) { f[j] = lo[j]; f[4 + j] = hi[j]; }
@@ -177,18 +180,16 @@ struct Lane {
         }
     }
     // Transposed fragment of a 64 x 128 tile: lane (m, g) gets
-    // tile[kappa(ks, g, 0..7)][32*cb + m]; cb = column window (compile-time for
-    // K, the wave's own window for V).
-    __device__ __forceinline__ typename FragOf<T>::type tr(const T* tile, const uint32_t* tab, int cbhi,
-                                                           int kappa_lo, int ks) const {
+    // tile[kappa(ks, g, 0..7)][32*cb + m]; tab2 = the two table entries (h = 0, 1)
+    // of column window cb (compile-time for K, the wave's own window for V).
+    __device__ __forceinline__ typename FragOf<T>::type tr(const T* tile, const uint32_t* tab2, int ks) const {
         if constexpr (sizeof(T) == 2) {
             typedef short s4 __attribute__((ext_vector_type(4)));
             typedef __bf16 b4 __attribute__((ext_vector_type(4)));
             typename FragOf<T>::type f;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int b = (2 * ks + h) & 7;
-                const uint32_t off = tab[(kappa_lo ^ b) & 7] + (16 * ks + 8 * h) * 256 + 128 * cbhi;
+                const uint32_t off = tab2[h] + (16 * ks + 8 * h) * 256;
                 s4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) s4*)(as_lds(tile) + off));
                 b4 q = __builtin_bit_cast(b4, r);
@@ -197,14 +198,14 @@ struct Lane {
             }
             return f;
         } else {
-            (void)tab; (void)cbhi; (void)kappa_lo;
+            (void)tab2;
             return typename FragOf<T>::type{};
         }
     }
     // K^T fragment for dk rows 32ht + m.
     __device__ __forceinline__ typename FragOf<T>::type trK(const T* tile, int ht, int ks) const {
         if constexpr (sizeof(T) == 2) {
-            return tr(tile, trk, ht >> 1, 4 * (ht & 1), ks);
+            return tr(tile, trk + 2 * ht, ks);
         } else {
             return tfrag<T, kDk>(tile, 32 * ht, ks, opaque_tid() & 63);
         }
@@ -212,7 +213,7 @@ struct Lane {
     // V fragment (accumulator layout) for this wave's dv columns.
     __device__ __forceinline__ typename FragOf<T>::type trV(const T* tile, int ks) const {
         if constexpr (sizeof(T) == 2) {
-            return tr(tile, trv, 0, 0, ks);
+            return tr(tile, trv, ks);
         } else {
             return tfrag<T, kDv>(tile, 32 * w, ks, opaque_tid() & 63);
         }
@@ -240,7 +241,7 @@ struct TileLoader {
         for (int i = 0; i < ROUNDS; ++i) {
             const int L = (i * 4 + pw) * 64 + lane;
             const int row = L / CPR, slot = L % CPR;
-            off[i] = (uint32_t)((row * H * kDk + (slot ^ swz(row)) * EPC) * (int)sizeof(T));
+            off[i] = (uint32_t)((row * H * kDk + (slot ^ slot_swz<CPR>(row)) * EPC) * (int)sizeof(T));
         }
     }
     // Copy the chunk whose first row (for this head) is `chunk` into `tile`.
@@ -451,7 +452,7 @@ __device__ __forceinline__ void chunk_prep(Smem<T>& sm, const Lane<T>& L, int pw
     // re-centred at gamma_C/2 so both factors stay within exp(|gamma_C|/2); chunks
     // whose decay exceeds that safe range use pairwise exponentials.
     const float gam = wave_inclusive_scan(gv);
-    const float gC = uni(__shfl(gam, 63, 64));
+    const float gC = lane_value(gam, 63);
     const float half = 0.5f * gC;
     const bool pairwise = gC < -160.f;   // wave-uniform
     const float gp = __expf(gam - half);

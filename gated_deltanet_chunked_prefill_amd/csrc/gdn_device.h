@@ -77,16 +77,28 @@ __device__ __forceinline__ typename FragOf<T>::type acc_frag_scaled(const f32x16
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 __device__ __forceinline__ int swz4(int row) { return (row ^ (row >> 2)) & 3; }
+// Rows of 16 or more slots (a 256-byte bf16 row spans all 64 LDS banks): the
+// slot index is XORed with a 4-bit value that differs for any 16 consecutive
+// rows, and whose top two bits differ for any 4 consecutive rows.  gfx950
+// serves a 64-bit LDS read in two 32-lane halves: 32 rows reading the same
+// 8-byte column then fall on 16 distinct bank pairs (two lanes per bank, the
+// fewest possible), and a transposing read, whose 32 lanes cover 4 rows x 64
+// bytes, touches 4 disjoint 16-bank groups (no conflict).
+__device__ __forceinline__ int swz16(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+template <int CPR>
+__device__ __forceinline__ int slot_swz(int row) {
+    return CPR >= 16 ? swz16(row) : CPR >= 8 ? swz(row) : swz4(row);
+}
 
 // Natural row-major tiles in LDS: a row of `Cols` elements is stored as 16-byte
-// chunks; chunk c of row r sits at slot c ^ s(r), with s = swz(r) for rows of
-// eight or more chunks and swz4(r) for rows of four, so rows read together at
-// the same column land in different bank groups.  Element offset of (row, col):
+// chunks; chunk c of row r sits at slot c ^ slot_swz(r) (swz16 for rows of
+// sixteen or more chunks, swz for eight, swz4 for four), so rows read together
+// at the same column land in different bank groups.  Element offset of (row, col):
 template <typename T, int Cols>
 __device__ __forceinline__ int toff(int row, int col) {
     constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
     constexpr int CPR = Cols / EPC;             // chunks per row
-    const int s = CPR >= 8 ? swz(row) : swz4(row);
+    const int s = slot_swz<CPR>(row);
     return row * Cols + (((col / EPC) ^ s) * EPC) + (col % EPC);
 }
 
@@ -150,14 +162,29 @@ __device__ __forceinline__ typename FragOf<T>::type tfrag(const T* tile, int nba
     return f;
 }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
+// x of lane l, as a wave-uniform value (v_readlane: no LDS round trip).
+__device__ __forceinline__ float lane_value(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+// The value of the lane that DPP control CTRL selects (0 where it selects none
+// or where ROWS masks the row out).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_take(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xf, true));
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave, on the DPP paths alone:
+// shifts by 1, 2, 4 and 8 lanes scan each row of 16, then the last lane of row
+// 0 (and of row 2) is added to row 1 (row 3), and the last lane of row 1 to rows
+// 2 and 3.
 __device__ __forceinline__ float wave_inclusive_scan(float x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        float y = __shfl_up(x, d, 64);
-        if (lane >= d) x += y;
-    }
+    x += dpp_take<0x111, 0xf>(x);   // row_shr:1
+    x += dpp_take<0x112, 0xf>(x);   // row_shr:2
+    x += dpp_take<0x114, 0xf>(x);   // row_shr:4
+    x += dpp_take<0x118, 0xf>(x);   // row_shr:8
+    x += dpp_take<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+    x += dpp_take<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
     return x;
 }
 
