@@ -264,21 +264,24 @@ struct LocalSmem {
     float red[4];
 };
 
-// B fragment of a 128 x 128 float32 state in HBM, contraction over its rows:
-// lane (n, g) gets S[kappa(ks, g, j)][col].
+// B fragment of a 128 x 128 float32 state in HBM, contraction over its rows, in
+// the column order of the 16-byte tile fragments: lane (n, g) gets
+// S[16ks + 8g + j][col], j = 0..7.
 template <typename T>
 __device__ __forceinline__ typename FragOf<T>::type state_colfrag(const float* S, int ks, int g, int col) {
+    static_assert(sizeof(T) == 2, "the backward is built for bf16 only");
     typename FragOf<T>::type f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) f[j] = (T)S[(16 * ks + 8 * (j >> 2) + 4 * g + (j & 3)) * kDv + col];
+    for (int j = 0; j < 8; ++j) f[j] = (T)S[(16 * ks + 8 * g + j) * kDv + col];
     return f;
 }
-// B fragment of the transposed state (contraction over its columns): lane (n, g)
-// gets S[row][kappa(ks, g, j)].
+// B fragment of the transposed state (contraction over its columns), same order:
+// lane (n, g) gets S[row][16ks + 8g + j].
 template <typename T>
 __device__ __forceinline__ typename FragOf<T>::type state_rowfrag(const float* S, int row, int ks, int g) {
-    const f32x4 lo = *(const f32x4*)(S + (size_t)row * kDv + 16 * ks + 4 * g);
-    const f32x4 hi = *(const f32x4*)(S + (size_t)row * kDv + 16 * ks + 8 + 4 * g);
+    static_assert(sizeof(T) == 2, "the backward is built for bf16 only");
+    const f32x4 lo = *(const f32x4*)(S + (size_t)row * kDv + 16 * ks + 8 * g);
+    const f32x4 hi = *(const f32x4*)(S + (size_t)row * kDv + 16 * ks + 8 * g + 4);
     typename FragOf<T>::type f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

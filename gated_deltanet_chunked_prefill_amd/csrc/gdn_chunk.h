@@ -96,8 +96,9 @@ __device__ __forceinline__ void lds_st(void* base, uint32_t off, const V& v) {
 // Per-lane LDS addressing.  For bf16 the swizzled byte offsets a lane needs are
 // precomputed once per task into small tables, so every fragment read in the
 // chunk loop is a table register plus an immediate offset:
-//   * rows 32rt + n of a 64 x 128 tile: slot = (2ks + h) ^ swz16(n) (swz16 of row
-//     32rt + n equals swz16(n));
+//   * rows 32rt + n of a 64 x 128 tile, one 16-byte read of columns 16ks + 8g ..
+//     +7: slot = (2ks + g) ^ swz16(n) (swz16 of row 32rt + n equals swz16(n)); the
+//     16 lanes a 128-bit read serves per cycle hit 16 distinct slots;
 //   * transposing reads of a 64 x 128 tile: lane (i, q, g) of a 16-lane group
 //     reads row r = 16ks + 8h + a (a = 4g + i/4), columns 32ht + 16q + 4(i%4)..+3,
 //     i.e. slot 4ht + x with x = 2q + (i/2)%2; swz16(r) = 4(a%4) + 2h + g, so the
@@ -106,7 +107,7 @@ __device__ __forceinline__ void lds_st(void* base, uint32_t off, const V& v) {
 template <typename T>
 struct Lane {
     int lane, n, g, w;
-    uint32_t a128[16];  // bf16: n*256 + 8g + ((j ^ swz16(n)) << 4)
+    uint32_t a128[8];   // bf16: n*256 + (((2ks + g) ^ swz16(n)) << 4), entry ks
     uint32_t a32[4];    // bf16: n*64 + 8g + ((j ^ swz4(n)) << 4)
     uint32_t trk[8];    // bf16: transposing-read offsets, entry 2ht + h (column window 32ht)
     uint32_t trv[2];    // bf16: the same for this wave's V columns 32w, entry h
@@ -119,7 +120,7 @@ struct Lane {
         if constexpr (sizeof(T) == 2) {
             const int s = swz16(n), s4 = swz4(n);
 #pragma unroll
-            for (int j = 0; j < 16; ++j) a128[j] = n * 256 + 8 * g + ((j ^ s) << 4);
+            for (int ks = 0; ks < 8; ++ks) a128[ks] = n * 256 + (((2 * ks + g) ^ s) << 4);
 #pragma unroll
             for (int j = 0; j < 4; ++j) a32[j] = n * 64 + 8 * g + ((j ^ s4) << 4);
             const int i = lane & 15, q = (lane >> 4) & 1;
@@ -136,16 +137,12 @@ struct Lane {
         }
     }
 
-    // A fragment of rows 32rt + n of a 64 x 128 tile, contraction k-step ks.
+    // A fragment of rows 32rt + n of a 64 x 128 tile, contraction k-step ks.  For
+    // bf16 the lane gets columns 16ks + 8g .. +7 in order (one 16-byte read): a
+    // fragment in accumulator row order meets it only through nat_frag.
     __device__ __forceinline__ typename FragOf<T>::type f128(const T* tile, int rt, int ks) const {
         if constexpr (sizeof(T) == 2) {
-            typedef __bf16 b4 __attribute__((ext_vector_type(4)));
-            b4 lo = lds_ld<b4>(tile, a128[2 * ks] + rt * 8192);
-            b4 hi = lds_ld<b4>(tile, a128[2 * ks + 1] + rt * 8192);
-            typename FragOf<T>::type f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) { f[j] = lo[j]; f[4 + j] = hi[j]; }
-            return f;
+            return lds_ld<typename FragOf<T>::type>(tile, a128[ks] + rt * 8192);
         } else {
             const int nn = opaque_tid() & 31;
             return afrag<T, kDk>(tile, 32 * rt + nn, ks, g);
@@ -476,13 +473,14 @@ __device__ __forceinline__ void chunk_prep(Smem<T>& sm, const Lane<T>& L, int pw
 }
 
 // X = K Hm for the two 32-row position tiles (Hm: the four dk tiles of a state).
+// The K fragments are in column order, so Hm's fragments are reordered to match.
 template <typename T>
 __device__ __forceinline__ void k_times(const Lane<T>& L, const T* kt, const f32x16* Hm, f32x16* X) {
     X[0] = zero16();
     X[1] = zero16();
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-        const typename FragOf<T>::type hf = acc_frag<T>(Hm[ks >> 1], ks & 1);
+        const typename FragOf<T>::type hf = nat_frag<T>(acc_frag<T>(Hm[ks >> 1], ks & 1));
         X[0] = mma(L.f128(kt, 0, ks), hf, X[0]);
         X[1] = mma(L.f128(kt, 1, ks), hf, X[1]);
     }

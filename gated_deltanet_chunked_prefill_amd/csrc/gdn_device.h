@@ -66,6 +66,26 @@ __device__ __forceinline__ typename FragOf<T>::type acc_frag(const f32x16& acc, 
     return f;
 }
 // The same, with a per-register scale.
+// A bf16 fragment taken from accumulator rows carries contraction indices
+// 16h + 8(j>>2) + 4g + (j&3) (the accumulator's row order); a 16-byte tile read
+// carries 16h + 8g + j.  Reordering one into the other moves elements 4..7 of
+// the g = 0 half-wave and elements 0..3 of the g = 1 half-wave across: two
+// v_permlane32_swap, each exchanging the upper half-wave of its first operand
+// with the lower half-wave of its second.  Float32 fragments are unchanged.
+template <typename T>
+__device__ __forceinline__ typename FragOf<T>::type nat_frag(const typename FragOf<T>::type& f) {
+    if constexpr (sizeof(T) == 2) {
+        typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+        const u4 u = __builtin_bit_cast(u4, f);   // u[0], u[1]: elements 0..3; u[2], u[3]: 4..7
+        const auto r0 = __builtin_amdgcn_permlane32_swap(u[0], u[2], false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(u[1], u[3], false, false);
+        const u4 o = {r0[0], r1[0], r0[1], r1[1]};
+        return __builtin_bit_cast(typename FragOf<T>::type, o);
+    } else {
+        return f;
+    }
+}
+
 template <typename T>
 __device__ __forceinline__ typename FragOf<T>::type acc_frag_scaled(const f32x16& acc, int half,
                                                                      const float* s) {

@@ -192,8 +192,9 @@ __device__ __forceinline__ void chunk_state(T* o, int Tn, int H, float scale, co
                 qn[1] = L.f128(qt, 1, ks + 1);
             }
         }
-        // the state fragment of this k-step is converted right before use
-        const F hf = acc_frag<T>(Hs[ks >> 1], ks & 1);
+        // the state fragment of this k-step is converted right before use (into
+        // the column order of the K and Q fragments)
+        const F hf = nat_frag<T>(acc_frag<T>(Hs[ks >> 1], ks & 1));
         X[0] = mma(ka[0], hf, X[0]);
         X[1] = mma(ka[1], hf, X[1]);
         if (MODE == MODE_FULL && emit) {
@@ -584,16 +585,20 @@ __device__ __noinline__ void chain_state(const FwdParams& prm, Smem<T>& sm, cons
             load_tile_t_dev(bz + (base + p) * kSS, c, w, lane, Bt);
             e = ld_dev(eg + base + p);
         }
-        // H column block split into bf16 hi and lo parts (the B operands)
+        // H column block split into bf16 hi and lo parts (the B operands, in the
+        // column order of the Mt fragments)
         bf16x8 hh[8], hl[8];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
+        for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float x = Hc[ks >> 1][8 * (ks & 1) + j];
                 hh[ks][j] = (__bf16)x;
                 hl[ks][j] = (__bf16)(x - (float)hh[ks][j]);
             }
+            hh[ks] = nat_frag<__bf16>(hh[ks]);
+            hl[ks] = nat_frag<__bf16>(hl[ks]);
+        }
         if (CB::two) lds_barrier();   // Y: the exchange has been read; Mt_p+1 in LDS
         const __bf16* const thi = CB::tiles(sm, (p - p0) & 1) + (w >> 1) * kChunk * kDk;
         const __bf16* const tlo = thi + 2 * kChunk * kDk;
