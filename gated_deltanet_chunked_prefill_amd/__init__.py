@@ -27,10 +27,11 @@ __all__ = ["gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_gate_scan", "gdn_plan_segments
 
 
 def options(split_mode=0, n_segments=1, use_window=True, window_chunks=8,
-            log_eps=DEFAULT_LOG_EPS) -> _lib.Options:
-    """Build a gdn_options struct (split_mode 0 auto, 1 off, 2 forced n_segments)."""
+            log_eps=DEFAULT_LOG_EPS, window_levels=4) -> _lib.Options:
+    """Build a gdn_options struct (split_mode 0 auto, 1 off, 2 forced n_segments;
+    window lengths window_chunks * (1 .. window_levels) are tried per head)."""
     return _lib.Options(int(split_mode), int(n_segments), int(bool(use_window)),
-                        int(window_chunks), float(log_eps))
+                        int(window_chunks), float(log_eps), int(window_levels))
 
 
 def _torch():
@@ -104,7 +105,7 @@ def gdn_chunk_fwd(q, k, v, g, beta, h0=None, scale=1.0, *, output_final_state=Tr
                   out_ht=None, workspace=None, **opts):
     """Fused chunked forward.  Returns (o, ht) (ht is None when not requested).
     ``opts`` are the gdn_options fields (split_mode, n_segments, use_window,
-    window_chunks, log_eps).  ``out`` / ``out_ht`` may supply preallocated
+    window_chunks, log_eps, window_levels).  ``out`` / ``out_ht`` may supply preallocated
     outputs and ``workspace`` a preallocated uint8 workspace."""
     torch = _torch()
     lib = _lib.load()

@@ -25,14 +25,14 @@ EXPORTS = ("gdn_default_options", "gdn_plan_segments", "gdn_chunk_fwd_workspace_
            "gdn_gate_scan_workspace_size", "gdn_gate_scan", "gdn_profile_events",
            "gdn_last_error", "gdn_chunk_fwd_plan_info")
 
-LAUNCH_KINDS = {0: "gate_sums", 1: "gate_flags", 2: "fwd_single", 3: "fwd_plan",
-                4: "fwd_queue", 5: "bwd_states", 6: "bwd_dh", 7: "bwd_local"}
+LAUNCH_KINDS = {0: "gate_sums", 1: "gate_flags", 2: "fwd_single", 3: "fwd_windows",
+                4: "fwd_queue", 5: "bwd_states", 6: "bwd_dh", 7: "bwd_local", 8: "fwd_sums"}
 
 
 class Options(ctypes.Structure):
     _fields_ = [("split_mode", ctypes.c_int), ("n_segments", ctypes.c_int),
                 ("use_window", ctypes.c_int), ("window_chunks", ctypes.c_int),
-                ("log_eps", ctypes.c_float)]
+                ("log_eps", ctypes.c_float), ("window_levels", ctypes.c_int)]
 
 
 _lib = None

@@ -80,6 +80,9 @@ gdn_status check_options(const gdn_options& o, int N) {
         return fail(GDN_ERR_INVALID_ARG, "n_segments must be in [1, %d] (got %d)", pmax, o.n_segments);
     if (o.window_chunks < 1) return fail(GDN_ERR_INVALID_ARG, "window_chunks must be >= 1");
     if (!(o.log_eps < 0.f)) return fail(GDN_ERR_INVALID_ARG, "log_eps must be negative");
+    if (o.window_levels < 1 || o.window_levels > gdn::kMaxWindowLevels)
+        return fail(GDN_ERR_INVALID_ARG, "window_levels must be in [1, %d] (got %d)", gdn::kMaxWindowLevels,
+                    o.window_levels);
     return GDN_OK;
 }
 
@@ -113,7 +116,7 @@ int plan(int B, int T, int H, int num_cus, const gdn_options& o) {
 }
 
 struct FwdLayout {
-    size_t wpart, flags, maxwin, head_map, hs, counters, bz, mt, eg, plan, jobs, total;
+    size_t csum, wpart, flags, maxwin, head_map, hs, counters, bz, mt, eg, plan, jobs, total;
 };
 
 FwdLayout fwd_layout(int B, int T, int H, int P) {
@@ -121,7 +124,8 @@ FwdLayout fwd_layout(int B, int T, int H, int P) {
     if (P <= 1) return L;
     const size_t N = num_chunks(T), bh = (size_t)B * H, SS = 128 * 128;
     size_t off = 0;
-    L.wpart = off;      off += align_up((size_t)B * gdn::window_groups(T) * H * sizeof(float));
+    L.csum = off;       off += align_up((size_t)B * N * H * sizeof(float));
+    L.wpart = off;      off += align_up((size_t)gdn::kMaxWindowLevels * B * gdn::window_groups(T) * H * sizeof(float));
     L.flags = off;      off += align_up(bh * sizeof(int32_t));
     L.maxwin = off;     off += align_up(bh * sizeof(float));
     L.head_map = off;   off += align_up(2 * bh * sizeof(int32_t));
@@ -170,6 +174,7 @@ void gdn_default_options(gdn_options* opt) {
     opt->use_window = 1;
     opt->window_chunks = 8;
     opt->log_eps = std::log(std::ldexp(1.0f, -24));
+    opt->window_levels = 4;
 }
 
 const char* gdn_last_error(void) { return g_err; }
@@ -269,13 +274,27 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
     p.n_groups = gdn::window_groups(T);
     // window heads only when a window fits the sequence (no head qualifies
     // otherwise) and the first launch can stage it
-    if (op.use_window && op.window_chunks <= N && op.window_chunks <= gdn::max_window_chunks())
+    // (longer windows are tried only while they fit the sequence and the staging)
+    p.levels = 0;
+    if (op.use_window && op.window_chunks <= N && op.window_chunks <= gdn::max_window_chunks()) {
         p.wpart = (float*)(ws + L.wpart);
-    e = recorded(GDN_LAUNCH_FWD_PLAN, s, [&] {
-        return gdn::launch_fwd_prep(g, B, T, H, op.window_chunks, const_cast<float*>(p.wpart), p.hs_cnt,
-                                    2 * nbh * P, (int*)p.plan, s);
+        p.levels = 1;
+        while (p.levels < op.window_levels && (p.levels + 1) * op.window_chunks <= N &&
+               (p.levels + 1) * op.window_chunks <= gdn::max_window_chunks())
+            ++p.levels;
+    }
+    float* const csum = p.wpart ? (float*)(ws + L.csum) : nullptr;
+    e = recorded(GDN_LAUNCH_FWD_SUMS, s, [&] {
+        return gdn::launch_fwd_sums(g, B, T, H, csum, p.hs_cnt, 2 * nbh * P, (int*)p.plan, s);
     });
     if (e != hipSuccess) return hip_fail(e, "forward preparation launch");
+    if (p.wpart) {
+        e = recorded(GDN_LAUNCH_FWD_WINDOWS, s, [&] {
+            return gdn::launch_fwd_windows(csum, B, T, H, op.window_chunks, p.levels, const_cast<float*>(p.wpart),
+                                           s);
+        });
+        if (e != hipSuccess) return hip_fail(e, "forward window launch");
+    }
     e = recorded(GDN_LAUNCH_FWD_QUEUE, s, [&] { return gdn::launch_fwd(p, gdn::PHASE_QUEUE, bf16, s); });
     if (e != hipSuccess) return hip_fail(e, "forward launch");
     return GDN_OK;

@@ -38,8 +38,9 @@
 // i.e. the same step on 128 extra columns with V = 0 and no gates.
 //
 // Split forward as a work queue.  A one-workgroup plan kernel reads the gate
-// flags, chooses the segment counts of exact and window heads from a cost
-// model and writes the job list; persistent workgroups (one per CU) then take
+// window maxima, gives every head a window length or marks it exact, chooses
+// the segment counts of exact and window heads from a cost model and writes
+// the job list; persistent workgroups (one per CU) then take
 // jobs from an atomic counter.  An exact head with P segments gets a full run
 // of segment 0, pass-1 runs of the middle segments (publishing their
 // transitions), one chain job composing the true entering states, and full
@@ -756,46 +757,91 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_queue_kernel(FwdParams pr
 //   pass-3 p        full run of [b_p, b_p+1) from hs[p] (p = 1 .. P-1), the
 //                   last one writes ht.
 // With P = 2 only seg 0 and one pass-3 job remain, with P = 1 one full run.
-// Window heads get P_w independent jobs, each warming up over the w chunks
-// before its segment.  Queue order: seg 0 jobs, pass-1 jobs, window jobs,
-// chain jobs, pass-3 jobs (segment-major), so that every job waits only for
-// jobs handed out before it.
+// A window head of level m (window of m*w chunks) gets P_m independent jobs,
+// each warming up over the m*w chunks before its segment.  Queue order: seg 0
+// jobs, pass-1 jobs, window jobs (longest windows first), chain jobs, pass-3
+// jobs (segment-major), so that every job waits only for jobs handed out
+// before it.
 //
 // Cost model, in units of one full chunk step under load: a pass-1 step costs
-// kCostPass1, one link of the chain kCostLink.  An exact head keeps P - 1
-// workgroups busy for about
+// kCostPass1, one link of the chain kCostLink, a warm-up step kCostWarm.  An
+// exact head keeps P - 1 workgroups busy for about
 //     L (1 + kCostPass1) + (P - 2) kCostLink,   L = 8 N / (kSeg0Weight + 8 (P - 1)),
 // segment 0 being kSeg0Weight / 8 times as long as the others so that it ends
-// with the pass-1 jobs.  The remaining workgroups share the window heads'
-// segments, each costing N / P_w + w.  The planner takes the P (and P_w) with
-// the smallest estimated makespan.
+// with the pass-1 jobs.  The remaining workgroups share the window heads: a
+// level-m head in P segments costs (N + (P - 1) c_m) / P per job, c_m =
+// kCostWarm m w, when its first segment (which has no warm-up) is longer by
+// c_m; the planner finds the smallest job cost M whose segment counts fit the
+// free workgroups.  It takes the P with the smallest estimated makespan.
 constexpr float kCostPass1 = 1.35f;
 constexpr float kCostLink = 0.8f;
+constexpr float kCostWarm = 0.7f;
 constexpr int kSeg0Weight = 11;
 
+struct WinLevels {
+    int n[kMaxWindowLevels];   // window heads per level (index m - 1)
+    int levels, N, w, pmax;
+};
+
+// Fewest segments for a level-m head so that each job costs at most M (0: none).
+__device__ __forceinline__ int win_segments(const WinLevels& wl, int m, float M) {
+    const float c = kCostWarm * m * wl.w;
+    if (M >= (float)wl.N) return 1;
+    if (M <= c) return 0;
+    int cap = wl.N / (m * wl.w);
+    cap = cap < 1 ? 1 : cap;
+    cap = cap < wl.pmax ? cap : wl.pmax;
+    const float p = ceilf(((float)wl.N - c) / (M - c));
+    return p <= (float)cap ? (int)p : 0;
+}
+
+// Smallest job cost of the window heads on `free` workgroups; Pm[m-1] gets the
+// segment counts.  With fewer workgroups than window heads every head is one job.
+__device__ float window_cost(const WinLevels& wl, int free, int* Pm) {
+    int n_w = 0;
+    for (int m = 1; m <= wl.levels; ++m) n_w += wl.n[m - 1];
+    for (int m = 1; m <= wl.levels; ++m) Pm[m - 1] = 1;
+    if (n_w == 0) return 0.f;
+    if (free < n_w) return free > 0 ? (float)((n_w + free - 1) / free) * wl.N : -1.f;
+    float lo = 0.f, hi = (float)wl.N;   // hi is feasible (one job per head)
+    for (int it = 0; it < 24; ++it) {
+        const float mid = 0.5f * (lo + hi);
+        int need = 0;
+        bool ok = true;
+        for (int m = 1; m <= wl.levels && ok; ++m) {
+            if (wl.n[m - 1] == 0) continue;
+            const int p = win_segments(wl, m, mid);
+            ok = p > 0;
+            need += wl.n[m - 1] * p;
+        }
+        if (ok && need <= free)
+            hi = mid;
+        else
+            lo = mid;
+    }
+    float cost = 0.f;
+    for (int m = 1; m <= wl.levels; ++m) {
+        if (wl.n[m - 1] == 0) continue;
+        const int p = win_segments(wl, m, hi);
+        Pm[m - 1] = p;
+        const float c = kCostWarm * m * wl.w;
+        const float t = ((float)wl.N + (p - 1) * c) / p;
+        cost = t > cost ? t : cost;
+    }
+    return cost;
+}
+
 // Estimated makespan (in full chunk steps) of P segments per exact head; also
-// returns the window heads' segment count.
-__device__ float plan_cost(int P, int n_e, int n_w, int N, int w, int cus, int pmax, int& Pw) {
-    const int pw_cap = N / w > 1 ? N / w : 1;
+// returns the window heads' segment counts per level.
+__device__ float plan_cost(int P, int n_e, const WinLevels& wl, int cus, int* Pm) {
+    const int N = wl.N;
     const int ecus = n_e * (P == 1 ? 1 : P - 1);
     float te = 0.f;
     if (n_e > 0)
         te = P == 1 ? (float)N : 8.f * N * (1.f + kCostPass1) / (kSeg0Weight + 8 * (P - 1)) + (P - 2) * kCostLink;
     const int free = cus - ecus > 0 ? cus - ecus : 0;
-    Pw = 1;
-    float tw = 0.f;
-    if (n_w > 0) {
-        if (free >= n_w) {
-            Pw = free / n_w;
-            if (Pw > pmax) Pw = pmax;
-            if (Pw > pw_cap) Pw = pw_cap;
-            tw = (float)N / Pw + (Pw > 1 ? w : 0);
-        } else if (free > 0) {
-            tw = (float)((n_w + free - 1) / free) * N;
-        } else {
-            tw = te + N;
-        }
-    }
+    float tw = window_cost(wl, free, Pm);
+    if (tw < 0.f) tw = te + N;   // no workgroup left: the window heads run after the exact ones
     return te > tw ? te : tw;
 }
 
@@ -834,11 +880,30 @@ __device__ int seg_bound(long long num, long long den, int N) {
     return (int)(((double)N * (double)num) / (double)den);
 }
 
+// Start of segment p of a level-m window head with P segments: the first
+// segment is longer by c = kCostWarm m w so that every job costs the same.
+// Equal segments when forced, or when the others would be shorter than 1.5
+// chunks (the rounded bounds then still increase strictly).
+__device__ int win_bound(int p, int P, int N, float c, bool forced) {
+    if (p <= 0) return 0;
+    if (p >= P) return N;
+    int s;
+    if (forced || (float)N - c < 1.5f * P) {
+        s = (int)(((long long)p * N) / P);
+    } else {
+        const float L0 = ((float)N + (P - 1) * c) / P;
+        s = (int)floorf(p * L0 - (p - 1) * c + 0.5f);
+    }
+    s = s < p ? p : s;
+    return s > N - (P - p) ? N - (P - p) : s;
+}
+
 // Planner scratch in the workgroup's LDS (used before any job runs).
 struct PlanLds {
     int bound[kMaxSegments + 1];
     int wave[kThreads / 64];
-    int par[2];
+    int par[2 + kMaxWindowLevels];
+    int cls[1 + kMaxWindowLevels];   // heads per class: exact, then window levels L .. 1
 };
 
 // The planner, run by workgroup 0 of the persistent launch before the jobs.
@@ -849,10 +914,12 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int B = uni(prm.B), H = uni(prm.H), nbh = B * H, N = uni(prm.N), pmax = uni(prm.P), w = uni(prm.w);
     const float* const wpart = uni(prm.wpart);
+    const int LV = wpart ? uni(prm.levels) : 0;
     int* const flags = uni(prm.flags);
-    // 1. window flags (talk summary, paragraph 5): a head is a window head when
-    //    its largest sum of g over w consecutive chunks is at most log_eps; the
-    //    first launch left the maxima per group of chunks, a wave reduces a head
+    // 1. window levels (talk summary, paragraph 5): a head is a window head of
+    //    level m when its largest sum of g over m*w consecutive chunks is at
+    //    most log_eps, for the smallest such m; the first launch left the
+    //    maxima per length and group of chunks, a run of threads reduces a head
     if (wpart) {
         // a run of tph threads per head (a power of two up to 64), all of a
         // thread's loads issued at once
@@ -862,96 +929,154 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
         const int hpr = kThreads / tph;   // heads per round
         for (int h0 = 0; h0 < nbh; h0 += hpr) {
             const int bh = h0 + tid / tph, k = tid % tph;
-            float best = -INFINITY;
-            if (bh < nbh) {
-                const int b = bh / H, h = bh % H;
-                for (int q0 = k; q0 < NG; q0 += 8 * tph) {
-                    float v[8];
+            const int b = bh < nbh ? bh / H : 0, h = bh < nbh ? bh % H : 0;
+            int lev = 0;
+            for (int m = LV; m >= 1; --m) {
+                float best = -INFINITY;
+                if (bh < nbh) {
+                    const float* const src = wpart + (size_t)(m - 1) * B * NG * H;
+                    for (int q0 = k; q0 < NG; q0 += 8 * tph) {
+                        float v[8];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const int q = q0 + u * tph;
-                        v[u] = wpart[((size_t)b * NG + (q < NG ? q : NG - 1)) * H + h];
+                        for (int u = 0; u < 8; ++u) {
+                            const int q = q0 + u * tph;
+                            v[u] = src[((size_t)b * NG + (q < NG ? q : NG - 1)) * H + h];
+                        }
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) best = v[u] > best ? v[u] : best;
                     }
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) best = v[u] > best ? v[u] : best;
                 }
+                for (int d = tph >> 1; d > 0; d >>= 1) {
+                    const float o = __shfl_xor(best, d, 64);
+                    best = o > best ? o : best;
+                }
+                if (N >= m * w && best <= prm.log_eps) lev = m;
+                if (m == 1 && bh < nbh && k == 0 && prm.maxwin) prm.maxwin[bh] = best;
             }
-            for (int d = tph >> 1; d > 0; d >>= 1) {
-                const float o = __shfl_xor(best, d, 64);
-                best = o > best ? o : best;
-            }
-            if (bh < nbh && k == 0) {
-                flags[bh] = (N >= w && best <= prm.log_eps) ? 1 : 0;
-                if (prm.maxwin) prm.maxwin[bh] = best;
-            }
+            if (bh < nbh && k == 0) flags[bh] = lev;
         }
         __syncthreads();
     }
-    // 2. rank the exact and the window heads (head_map: exact heads by rank,
-    //    then window heads by rank) and choose the segment counts
+    // 2. choose the segment counts and the longest window kept (heads of a
+    //    higher level are exact: for short sequences the exact split can be
+    //    cheaper than long warm-ups), then rank the heads by class (head_map:
+    //    exact heads, then window heads of level Lc, Lc-1, .., 1, each class in
+    //    head order)
     const int per = (nbh + kThreads - 1) / kThreads;
     const int lo = tid * per < nbh ? tid * per : nbh;
     const int hi = lo + per < nbh ? lo + per : nbh;
-    auto exact = [&](int bh) { return wpart == nullptr || flags[bh] == 0; };
-    int ne = 0;
-    for (int bh = lo; bh < hi; ++bh) ne += exact(bh) ? 1 : 0;
-    int n_e = 0;
-    int re = block_exclusive_scan(ne, pl.wave, n_e);
-    int rw = lo - re;
-    const int n_w = nbh - n_e;
-    int* const head_map = uni(prm.head_map);
-    for (int bh = lo; bh < hi; ++bh) {
-        if (exact(bh))
-            head_map[re++] = bh;
-        else
-            head_map[n_e + rw++] = bh;
+    auto level_of = [&](int bh) { return wpart ? flags[bh] : 0; };
+    for (int m = 0; m <= LV; ++m) {
+        int cnt = 0;
+        for (int bh = lo; bh < hi; ++bh) cnt += level_of(bh) == m ? 1 : 0;
+        int tot = 0;
+        block_exclusive_scan(cnt, pl.wave, tot);
+        if (tid == 0) pl.cls[m] = tot;   // heads per level (0 = exact)
     }
+    __syncthreads();
     if (wv == 0) {
-        // candidate segment counts one per lane, the cheapest wins (ties: fewer)
-        int Pe = pmax, Pw = pmax;
+        // candidates (P, Lc), one per lane and round, ordered by P, then by
+        // decreasing Lc; the cheapest wins, ties go to the earlier candidate
+        int Pe = pmax, Lc = LV;
         if (!prm.forced) {
             float best = 3.0e38f;
-            int bP = 1, bPw = 1;
-            const int pcap = n_e > 0 ? pmax : 1;
-            for (int P0 = 1; P0 <= pcap; P0 += 64) {
-                int P = P0 + lane, pw = 1;
+            int bi = 0;
+            const int ncand = pmax * (LV + 1);
+            for (int i0 = 0; i0 < ncand; i0 += 64) {
+                int i = i0 + lane;
+                const int P = 1 + i / (LV + 1), lc = LV - i % (LV + 1);
+                WinLevels wl;
+                wl.levels = lc;
+                wl.N = N;
+                wl.w = w;
+                wl.pmax = pmax;
+                int n_e = pl.cls[0];
+                for (int m = 1; m <= kMaxWindowLevels; ++m) {
+                    const int c = m <= LV ? pl.cls[m] : 0;
+                    wl.n[m - 1] = m <= lc ? c : 0;
+                    n_e += m > lc ? c : 0;
+                }
                 float t = 3.0e38f;
-                const bool ok = P <= pcap && P != 2 && (P == 1 || n_e * (P - 1) <= prm.cus);
-                if (ok) t = plan_cost(P, n_e, n_w, N, w, prm.cus, pmax, pw);
+                const bool ok = i < ncand && (n_e > 0 || P == 1) && P != 2 && (P == 1 || n_e * (P - 1) <= prm.cus);
+                int pm_unused[kMaxWindowLevels];
+                if (ok) t = plan_cost(P, n_e, wl, prm.cus, pm_unused);
 #pragma unroll
                 for (int d = 1; d < 64; d <<= 1) {
                     const float ot = __shfl_xor(t, d, 64);
-                    const int oP = __shfl_xor(P, d, 64), opw = __shfl_xor(pw, d, 64);
-                    if (ot < t || (ot == t && oP < P)) {
+                    const int oi = __shfl_xor(i, d, 64);
+                    if (ot < t || (ot == t && oi < i)) {
                         t = ot;
-                        P = oP;
-                        pw = opw;
+                        i = oi;
                     }
                 }
                 if (t < best * 0.999f) {
                     best = t;
-                    bP = P;
-                    bPw = pw;
+                    bi = i;
                 }
             }
-            Pe = bP;
-            Pw = bPw;
+            Pe = 1 + bi / (LV + 1);
+            Lc = LV - bi % (LV + 1);
         }
         if (lane == 0) {
             pl.par[0] = Pe;
-            pl.par[1] = Pw;
+            pl.par[1] = Lc;
         }
     }
     __syncthreads();
-    const int Pe = pl.par[0], Pw = pl.par[1];
+    const int Lc = pl.par[1];
+    // window heads above the kept level become exact (flags rewritten)
+    auto cls_of = [&](int bh) { const int m = level_of(bh); return (m == 0 || m > Lc) ? 0 : 1 + (Lc - m); };
+    int start = 0;   // first slot of the current class
+    int* const head_map = uni(prm.head_map);
+    for (int ci = 0; ci <= Lc; ++ci) {
+        int cnt = 0;
+        for (int bh = lo; bh < hi; ++bh) cnt += cls_of(bh) == ci ? 1 : 0;
+        int tot = 0;
+        const int r = block_exclusive_scan(cnt, pl.wave, tot);
+        int slot = start + r;
+        for (int bh = lo; bh < hi; ++bh)
+            if (cls_of(bh) == ci) head_map[slot++] = bh;
+        start += tot;
+        if (tid == 0) pl.cls[ci] = tot;   // heads per class from here on
+    }
+    __syncthreads();
+    if (wpart)
+        for (int bh = lo; bh < hi; ++bh)
+            if (flags[bh] > Lc) flags[bh] = 0;
+    const int n_e = pl.cls[0];
+    const int n_w = nbh - n_e;
+    WinLevels wl;
+    wl.levels = Lc;
+    wl.N = N;
+    wl.w = w;
+    wl.pmax = pmax;
+    for (int m = 1; m <= kMaxWindowLevels; ++m) wl.n[m - 1] = m <= Lc ? pl.cls[1 + Lc - m] : 0;
+    if (wv == 0) {
+        const int Pe = pl.par[0];
+        int Pm[kMaxWindowLevels];
+        for (int m = 0; m < kMaxWindowLevels; ++m) Pm[m] = pmax;
+        if (!prm.forced) plan_cost(Pe, n_e, wl, prm.cus, Pm);
+        if (lane == 0) {
+            int pw_max = 1;
+            for (int m = 0; m < kMaxWindowLevels; ++m) {
+                pl.par[2 + m] = Pm[m];
+                if (m < Lc && wl.n[m] > 0 && Pm[m] > pw_max) pw_max = Pm[m];
+            }
+            pl.par[1] = pw_max;
+        }
+    }
+    __syncthreads();
+    const int Pe = pl.par[0];
+    int n_win_jobs = 0;
+    for (int m = 1; m <= Lc; ++m) n_win_jobs += wl.n[m - 1] * pl.par[1 + m];
     const int g_win = n_e + (Pe >= 3 ? n_e * (Pe - 2) : 0);
-    const int g_chain = g_win + n_w * Pw;
+    const int g_chain = g_win + n_win_jobs;
     const int g_p3 = g_chain + (Pe >= 3 ? 4 * n_e : 0);
     const int n_jobs = g_p3 + (Pe >= 2 ? n_e * (Pe - 1) : 0);
     if (tid == 0) {
         FwdPlan* const fp = uni(prm.plan);
         fp->P_e = Pe;
-        fp->P_w = Pw;
+        fp->P_w = pl.par[1];
         fp->n_exact = n_e;
         fp->n_window = n_w;
         fp->n_jobs = n_jobs;
@@ -977,12 +1102,21 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
             const int p = 1 + (j - n_e) / n_e, e = (j - n_e) % n_e;
             put_job(jobs, j, head_map[e], p, pl.bound[p], pl.bound[p + 1], pl.bound[p + 1], MODE_PASS1,
                     INIT_ZERO, DST_TRANSITION);
-        } else if (j < g_chain) {   // window head segment p, segment-major
-            const int p = (j - g_win) / n_w, r = (j - g_win) % n_w;
-            const int sb = (int)(((long long)p * N) / Pw), e = (int)(((long long)(p + 1) * N) / Pw);
-            const int cb = sb - w > 0 ? sb - w : 0;
-            put_job(jobs, j, head_map[n_e + r], p, cb, sb, e, MODE_FULL,
-                    (cb == 0 && has_h0) ? INIT_H0 : INIT_ZERO, p == Pw - 1 ? dst_last : DST_NONE);
+        } else if (j < g_chain) {   // window segments, level by level (longest first), head-major
+            int jw = j - g_win, hbase = n_e, m = Lc;
+            for (; m > 1; --m) {
+                const int nj = wl.n[m - 1] * pl.par[1 + m];
+                if (jw < nj) break;
+                jw -= nj;
+                hbase += wl.n[m - 1];
+            }
+            const int P = pl.par[1 + m], W = m * w;
+            const int r = jw / P, p = jw % P;
+            const float c = kCostWarm * W;
+            const int sb = win_bound(p, P, N, c, prm.forced != 0), e = win_bound(p + 1, P, N, c, prm.forced != 0);
+            const int cb = sb - W > 0 ? sb - W : 0;
+            put_job(jobs, j, head_map[hbase + r], p, cb, sb, e, MODE_FULL,
+                    (cb == 0 && has_h0) ? INIT_H0 : INIT_ZERO, p == P - 1 ? dst_last : DST_NONE);
         } else if (j < g_p3) {   // chain, one job per 32-column block
             const int e = (j - g_chain) / 4, cb = (j - g_chain) % 4;
             put_job(jobs, j, head_map[e], 1, cb, 0, Pe - 1, MODE_CHAIN, 0, 0);

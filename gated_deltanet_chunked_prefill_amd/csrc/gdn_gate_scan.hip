@@ -7,8 +7,9 @@
 //   1. chunk sums s[b][c][h] = sum of g over the (up to) 64 tokens of chunk c;
 //   2. per head (one workgroup): W_c = s_{c-w+1} + ... + s_c for c >= w-1 (each
 //      window summed directly), its maximum over c, and flag = N >= w && max <= log_eps.
-// The split forward launches fwd_prep_kernel instead, which forms the same
-// window sums per group of chunks for its planner.
+// The split forward forms the same chunk sums (fwd_sums_kernel) and window
+// sums per group of chunks and window length (fwd_window_kernel) for its
+// planner.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -33,8 +34,20 @@ __device__ void chunk_sums_wg(const float* __restrict__ g, int T, int H, int N, 
         const int G = 256 / hw;                        // token groups
         const int h = h0 + tid % hw, grp = tid / hw;
         float acc = 0.f;
-        if (grp < G)
+        if (G >= 4 && grp < G) {
+            // at most 16 tokens per thread: every load issued before the sum
+            // (tokens past the chunk read as zero, which leaves the sum unchanged)
+            float v[16];
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const int t = grp + m * G;
+                v[m] = t < nt ? src[(size_t)t * H + h] : 0.f;
+            }
+#pragma unroll
+            for (int m = 0; m < 16; ++m) acc += v[m];
+        } else if (grp < G) {
             for (int t = grp; t < nt; t += G) acc += src[(size_t)t * H + h];
+        }
         part[tid] = acc;
         __syncthreads();
         if (tid < hw) {
@@ -52,101 +65,64 @@ __global__ __launch_bounds__(256) void chunk_sums_kernel(const float* __restrict
 }
 
 // First launch of the split forward: the reset of the planner's words and
-// hand-off counters, which the persistent launch that follows relies on, and
-// (when window heads are considered) window maxima per group of kWinGroup
-// chunks.  Workgroup (grp, b) forms the chunk sums of its chunks and of the
-// w - 1 chunks before them (same arrangement and summation order as
-// chunk_sums_kernel; a batch of chunks' loads in flight at once), then per head
-// the largest window sum W_c = s_{c-w+1} + ... + s_c (summed in that order)
-// over the windows ending in the group: part[(b*NG + grp)*H + h], -inf when no
-// window ends there.  The planner takes the maximum over the groups.
-constexpr int kWinGroup = 8;
-constexpr int kWinBatch = 4;        // chunks whose loads are in flight together
-constexpr int kWinMaxSums = 8192;   // LDS floats for the group's chunk sums
-
-__global__ __launch_bounds__(256) void fwd_prep_kernel(const float* __restrict__ g, int T, int H, int N, int w,
-                                                       float* __restrict__ part, int* __restrict__ zero,
+// hand-off counters, which the persistent launch relies on, and (when window
+// heads are considered) the chunk sums of g, one workgroup per chunk, in the
+// arrangement and summation order of chunk_sums_kernel.
+__global__ __launch_bounds__(256) void fwd_sums_kernel(const float* __restrict__ g, int T, int H, int N,
+                                                       float* __restrict__ sums, int* __restrict__ zero,
                                                        int nzero, int* __restrict__ plan_words) {
-    __shared__ float s_sum[kWinMaxSums];
-    __shared__ float red[kWinBatch][256];
-    const int grp = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int wg = b * gridDim.x + grp, nwg = gridDim.x * gridDim.y;
+    const int tid = threadIdx.x;
+    const int wg = blockIdx.y * gridDim.x + blockIdx.x, nwg = gridDim.x * gridDim.y;
     for (int i = wg * 256 + tid; i < nzero; i += nwg * 256) zero[i] = 0;
     if (wg == 0 && tid < 8) plan_words[tid] = 0;
-    if (!part) return;
+    if (sums) chunk_sums_wg(g, T, H, N, blockIdx.x, blockIdx.y, sums);
+}
+
+// Second launch (window heads considered): window maxima per group of
+// kWinGroup chunks for the window lengths W = m*w, m = 1 .. levels.  Workgroup
+// (grp, b) stages the chunk sums of its chunks and of the levels*w - 1 chunks
+// before them, then per head and length takes the largest window sum
+// s_{c-W+1} + ... + s_c (summed in that order) over the windows ending in the
+// group: part[(((m-1)*B + b)*NG + grp)*H + h], -inf when no window ends there.
+// The planner takes the maximum over the groups.  At m = 1 the sums are those
+// of window_flags_kernel, term for term.
+constexpr int kWinGroup = 8;
+constexpr int kWinMaxSums = 8192;   // LDS floats for the group's chunk sums
+__global__ __launch_bounds__(256) void fwd_window_kernel(const float* __restrict__ sums, int H, int N, int w,
+                                                         int levels, float* __restrict__ part) {
+    __shared__ float s_sum[kWinMaxSums];
+    const int grp = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int NG = gridDim.x;
     const int c0 = grp * kWinGroup;
     const int c1 = c0 + kWinGroup < N ? c0 + kWinGroup : N;
-    const int cs = c0 - w + 1 > 0 ? c0 - w + 1 : 0;   // first chunk a window needs
+    const int wl = levels * w;                          // longest window
+    const int cs = c0 - wl + 1 > 0 ? c0 - wl + 1 : 0;   // first chunk a window needs
     const int nc = c1 - cs;
     const int hpass = kWinMaxSums / nc < H ? kWinMaxSums / nc : H;   // >= 1: nc <= kWinMaxSums
     for (int h0 = 0; h0 < H; h0 += hpass) {
         const int hn = H - h0 < hpass ? H - h0 : hpass;
-        for (int hb = 0; hb < hn; hb += 256) {
-            const int hw = hn - hb < 256 ? hn - hb : 256;
-            const int G = 256 / hw;
-            const int hh = h0 + hb + tid % hw, q = tid / hw;
-            for (int cb = cs; cb < c1; cb += kWinBatch) {
-                float acc[kWinBatch];
-                if (G >= 8 && q < G) {
-                    // at most eight rows per chunk and thread: all the batch's
-                    // loads are issued before any is summed (rows past the
-                    // sequence or the batch read as zero)
-                    float v[kWinBatch][8];
-#pragma unroll
-                    for (int k = 0; k < kWinBatch; ++k) {
-                        const int c = cb + k < c1 ? cb + k : c1 - 1;
-                        const int t0 = c * kChunk;
-                        const int nt = cb + k < c1 ? (T - t0 < kChunk ? T - t0 : kChunk) : 0;
-                        const float* src = g + ((size_t)b * T + t0) * H;
-#pragma unroll
-                        for (int m = 0; m < 8; ++m) {
-                            const int t = q + m * G;
-                            v[k][m] = t < nt ? src[(size_t)t * H + hh] : 0.f;
-                        }
-                    }
-#pragma unroll
-                    for (int k = 0; k < kWinBatch; ++k) {
-                        acc[k] = 0.f;
-#pragma unroll
-                        for (int m = 0; m < 8; ++m) acc[k] += v[k][m];
-                    }
-                } else {
-#pragma unroll
-                    for (int k = 0; k < kWinBatch; ++k) {
-                        acc[k] = 0.f;
-                        const int c = cb + k;
-                        if (c < c1 && q < G) {
-                            const int t0 = c * kChunk;
-                            const int nt = T - t0 < kChunk ? T - t0 : kChunk;
-                            const float* src = g + ((size_t)b * T + t0) * H;
-                            for (int t = q; t < nt; t += G) acc[k] += src[(size_t)t * H + hh];
-                        }
-                    }
-                }
-#pragma unroll
-                for (int k = 0; k < kWinBatch; ++k) red[k][tid] = acc[k];
-                __syncthreads();
-                if (tid < hw)
-#pragma unroll
-                    for (int k = 0; k < kWinBatch; ++k) {
-                        if (cb + k < c1) {
-                            float v = 0.f;
-                            for (int j = 0; j < G; ++j) v += red[k][j * hw + tid];
-                            s_sum[(cb + k - cs) * hpass + hb + tid] = v;
-                        }
-                    }
-                __syncthreads();
-            }
+        for (int i = tid; i < nc * hn; i += 256) {
+            const int c = cs + i / hn, hl = i % hn;
+            s_sum[(c - cs) * hpass + hl] = sums[((size_t)b * N + c) * H + h0 + hl];
         }
-        for (int hl = tid; hl < hn; hl += 256) {
-            float best = -INFINITY;
-            for (int c = c0 > w - 1 ? c0 : w - 1; c < c1; ++c) {
-                float acc = 0.f;
-                for (int j = c - w + 1; j <= c; ++j) acc += s_sum[(j - cs) * hpass + hl];
-                best = acc > best ? acc : best;
+        __syncthreads();
+        // one thread per (head, length, window end); the kWinGroup ends of a
+        // (head, length) pair sit in adjacent lanes and are reduced by shuffles
+        const int ntask = hn * levels * kWinGroup;
+        for (int x0 = 0; x0 < ntask; x0 += 256) {
+            const int x = x0 + tid, e = x % kWinGroup, pr = x / kWinGroup;
+            const int hl = pr % hn, m = 1 + pr / hn, W = m * w, c = c0 + e;
+            float acc = -INFINITY;
+            if (x < ntask && c < c1 && c >= W - 1) {
+                acc = 0.f;
+                for (int j = c - W + 1; j <= c; ++j) acc += s_sum[(j - cs) * hpass + hl];
             }
-            part[((size_t)b * NG + grp) * H + h0 + hl] = best;
+#pragma unroll
+            for (int d = 1; d < kWinGroup; d <<= 1) {
+                const float o = __shfl_xor(acc, d, 64);
+                acc = o > acc ? o : acc;
+            }
+            if (x < ntask && e == 0) part[(((size_t)(m - 1) * gridDim.y + b) * NG + grp) * H + h0 + hl] = acc;
         }
         __syncthreads();
     }
@@ -192,14 +168,20 @@ hipError_t launch_chunk_sums(const float* g, int B, int T, int H, float* chunk_s
 int window_groups(int T) { return ((T + kChunk - 1) / kChunk + kWinGroup - 1) / kWinGroup; }
 int max_window_chunks() { return kWinMaxSums - kWinGroup + 1; }
 
-hipError_t launch_fwd_prep(const float* g, int B, int T, int H, int w, float* part, int* zero, int nzero,
+hipError_t launch_fwd_sums(const float* g, int B, int T, int H, float* sums, int* zero, int nzero,
                            int* plan_words, hipStream_t s) {
     const int N = (T + kChunk - 1) / kChunk;
-    dim3 grid(part ? window_groups(T) : 1, part ? B : 1);
-    hipLaunchKernelGGL(fwd_prep_kernel, grid, dim3(256), 0, s, g, T, H, N, w, part, zero, nzero, plan_words);
+    dim3 grid(sums ? N : 1, sums ? B : 1);
+    hipLaunchKernelGGL(fwd_sums_kernel, grid, dim3(256), 0, s, g, T, H, N, sums, zero, nzero, plan_words);
     return hipGetLastError();
 }
-
+hipError_t launch_fwd_windows(const float* sums, int B, int T, int H, int w, int levels, float* part,
+                              hipStream_t s) {
+    const int N = (T + kChunk - 1) / kChunk;
+    dim3 grid(window_groups(T), B);
+    hipLaunchKernelGGL(fwd_window_kernel, grid, dim3(256), 0, s, sums, H, N, w, levels, part);
+    return hipGetLastError();
+}
 hipError_t launch_window_flags(const float* chunk_sums, int B, int T, int H, int w, float log_eps,
                                int32_t* flags, float* maxwin, hipStream_t s) {
     const int N = (T + kChunk - 1) / kChunk;

@@ -8,8 +8,10 @@ namespace gdn {
 
 // Workspace of the split forward, per head bh = b*H + h and segment slot p < P
 // (P = the largest segment count the call may use; 256-byte aligned sub-buffers):
-//   wpart      [B, NG, H]         window maxima per group of chunks (gate scan)
-//   flags      [B*H] int32        1 = window head
+//   csum       [B, N, H]          sums of g per chunk (gate scan)
+//   wpart      [LV, B, NG, H]     window maxima per group of chunks (gate scan), per
+//                                 window length level (LV = kMaxWindowLevels slots)
+//   flags      [B*H] int32        0 = exact head, m >= 1 = window head of m*w chunks
 //   maxwin     [B*H]              max window log-decay
 //   hs         [B*H, P, dk, dv]   true state entering segment p (p >= 1) of an exact head
 //   hs_cnt     [B*H, P] int32     parts of hs[bh, p] published (complete at 16)
@@ -26,12 +28,13 @@ namespace gdn {
 // bh, with outputs from chunk c_out on, or (mode = chain) the composition of
 // the states entering segments seg+1 .. c_end of head bh.
 constexpr int kMaxSegments = 1024;   // the device planner's limit on segments per head
+constexpr int kMaxWindowLevels = 8;  // window lengths w, 2w, ..., 8w chunks at most
 
 struct TaskRec {
     int bh, seg, c_begin, c_out, c_end, mode, init, dst;
 };
 struct FwdPlan {
-    int P_e, P_w;      // segments of an exact head / of a window head
+    int P_e, P_w;      // segments of an exact head / the most segments of a window head
     int n_exact, n_window;
     int n_jobs;
     int next;          // next job to hand out (atomic counter)
@@ -50,14 +53,15 @@ struct FwdParams {
     float* ht;         // nullable
     int B, T, H, N;    // N = number of 64-token chunks
     int P;             // segment slots per head (1 = no split)
-    int w;             // window length in chunks
+    int w;             // window length in chunks (level 1)
+    int levels;        // window lengths tried: w, 2w, ..., levels * w (0 with no window heads)
     float scale;
-    const float* wpart;    // split forward with window heads: window maxima per group of chunks
-                           // (null: all heads exact)
+    const float* wpart;    // split forward with window heads: window maxima per level and group
+                           // of chunks (null: all heads exact)
     int n_groups;          // groups of chunks in wpart
     int* head_map;         // [2*B*H] planner scratch: heads by exact rank, then by window rank
-    int32_t* flags;        // written by the plan kernel when sums is set: 1 = window head
-    float* maxwin;         // its window maxima
+    int32_t* flags;        // written by the planner: 0 = exact head, m = window head of m*w chunks
+    float* maxwin;         // the largest window sum at length w
     float log_eps;
     float* hs;
     int* hs_cnt;
@@ -82,8 +86,10 @@ hipError_t launch_fwd(const FwdParams& p, int phase, bool bf16, hipStream_t s);
 hipError_t launch_chunk_sums(const float* g, int B, int T, int H, float* chunk_sums, hipStream_t s);
 int window_groups(int T);
 int max_window_chunks();
-hipError_t launch_fwd_prep(const float* g, int B, int T, int H, int w, float* part, int* zero, int nzero,
+hipError_t launch_fwd_sums(const float* g, int B, int T, int H, float* sums, int* zero, int nzero,
                            int* plan_words, hipStream_t s);
+hipError_t launch_fwd_windows(const float* sums, int B, int T, int H, int w, int levels, float* part,
+                              hipStream_t s);
 hipError_t launch_window_flags(const float* chunk_sums, int B, int T, int H, int w, float log_eps,
                                int32_t* flags, float* maxwin, hipStream_t s);
 

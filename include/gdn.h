@@ -78,10 +78,17 @@ typedef struct {
     int use_window;
     int window_chunks;  /* w >= 1, default 8 (the page 1 commentary quotes a 6-8 chunk warm-up) */
     float log_eps;      /* default log(2^-24)                                                    */
+    /* Per-head window length (talk summary, paragraph 8, lists fixed window
+     * rules as an open problem): the forward tries the lengths w, 2w, ...,
+     * window_levels * w chunks and gives each head the shortest one whose every
+     * window decays by at least exp(log_eps); a head that none satisfies stays
+     * exact.  1 = the single length w.  1 <= window_levels <= 8, default 4;
+     * lengths beyond the first launch's staging limit are not tried. */
+    int window_levels;
 } gdn_options;
 
 /* Fill *opt with the defaults: automatic split, window shortcut on, w = 8,
- * log_eps = log(2^-24). */
+ * log_eps = log(2^-24), window_levels = 4. */
 void gdn_default_options(gdn_options* opt);
 
 /* Segment slots per head of the forward for these shapes on a device with
@@ -174,11 +181,12 @@ typedef enum {
     GDN_LAUNCH_GATE_SUMS = 0,   /* gate scan: per-chunk sums of g                     */
     GDN_LAUNCH_GATE_FLAGS = 1,  /* gate scan: window maxima and flags                 */
     GDN_LAUNCH_FWD_SINGLE = 2,  /* fused forward, unsplit                             */
-    GDN_LAUNCH_FWD_PLAN = 3,    /* split forward: chunk sums of g, planner reset      */
+    GDN_LAUNCH_FWD_WINDOWS = 3, /* split forward: window maxima per group of chunks   */
     GDN_LAUNCH_FWD_QUEUE = 4,   /* split forward: planner, then persistent workgroups over the jobs */
     GDN_LAUNCH_BWD_STATES = 5,  /* backward: state entering every chunk (forward kernel) */
     GDN_LAUNCH_BWD_DH = 6,      /* backward: state gradient, end to start             */
-    GDN_LAUNCH_BWD_LOCAL = 7    /* backward: local gradients of every chunk           */
+    GDN_LAUNCH_BWD_LOCAL = 7,   /* backward: local gradients of every chunk           */
+    GDN_LAUNCH_FWD_SUMS = 8     /* split forward: chunk sums of g, planner reset      */
 } gdn_launch_kind;
 
 /* Measurement hook (the talk summary, paragraph 7, argues the fused operator

@@ -31,7 +31,7 @@ def test_exports_match_header():
 def test_default_options():
     o = _lib.Options()
     _lib.load().gdn_default_options(ctypes.byref(o))
-    assert (o.split_mode, o.use_window, o.window_chunks) == (0, 1, 8)
+    assert (o.split_mode, o.use_window, o.window_chunks, o.window_levels) == (0, 1, 8, 4)
     assert abs(o.log_eps - math.log(2.0 ** -24)) < 1e-5
 
 
@@ -80,6 +80,10 @@ def test_validation_before_launch():
     assert _fwd(lib, q=A, k=A, v=A, g=A, beta=A, o=A, opt=bad) == _lib.GDN_ERR_INVALID_ARG
     bad = gdn.options(window_chunks=0)
     assert _fwd(lib, q=A, k=A, v=A, g=A, beta=A, o=A, opt=bad) == _lib.GDN_ERR_INVALID_ARG
+    for lv in (0, 9):
+        bad = gdn.options(window_levels=lv)
+        assert _fwd(lib, q=A, k=A, v=A, g=A, beta=A, o=A, opt=bad) == _lib.GDN_ERR_INVALID_ARG
+        assert "window_levels" in _lib.last_error()
 
 
 def test_gate_scan_and_bwd_validation():

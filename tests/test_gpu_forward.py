@@ -199,27 +199,69 @@ def test_workspace_too_small(gdn):
     assert ei.value.status == _lib.GDN_ERR_WORKSPACE
 
 
+def _window_levels(g, w=8, levels=4):
+    """Per head the smallest m <= levels whose windows of m*w chunks all decay
+    below the threshold (oracle gate scan), 0 when none does."""
+    lev = np.zeros(g.shape[0] * g.shape[2], np.int64)
+    for m in range(levels, 0, -1):
+        f, _ = oracle.gate_scan(g, window_chunks=m * w)
+        lev[f.reshape(-1) == 1] = m
+    return lev
+
+
+def _check_plan_levels(info, lev, nbh):
+    """The device plan keeps the window heads of levels 1 .. Lc for some Lc (the
+    rest are exact), so the window count is a prefix sum of the oracle's counts."""
+    counts = [int(np.sum(lev == m)) for m in range(1, 9)]
+    prefixes = [sum(counts[:lc]) for lc in range(0, 9)]
+    assert info["error"] == 0
+    assert info["n_exact"] + info["n_window"] == nbh
+    assert info["n_window"] in prefixes, (info, counts)
+
+
+def test_window_levels_mixed(gdn):
+    """Heads with different window lengths (8, 16, 24, 32 chunks) in one call:
+    the automatic plan and the plan with a single window length agree with the
+    oracle, and the levels turn exact heads into window heads."""
+    import torch
+    say("case window levels, B=1 T=64*160+21 H=12")
+    x = inputs.generate(B=1, T=64 * 160 + 21, H=12, gate="softplus_head", h0_std=0.02, seed=24)
+    B, T, H = 1, 64 * 160 + 21, 12
+    lev = _window_levels(x.g)
+    say(f"  oracle levels {lev.tolist()}")
+    assert len(set(lev.tolist())) >= 3
+    t = to_gpu(x)
+    oref, href = oracle.fwd(x.q, x.k, x.v, x.g, x.beta, x.h0)
+    infos = {}
+    for lv in (1, 4):
+        ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(B, T, H), dtype=torch.uint8, device="cuda")
+        o, ht = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], workspace=ws,
+                                  window_levels=lv)
+        infos[lv] = gdn.gdn_chunk_fwd_plan_info(B, T, H, workspace=ws, window_levels=lv)
+        say(f"  levels={lv}: plan {infos[lv]}")
+        _check_plan_levels(infos[lv], np.where(lev <= lv, lev, 0), B * H)
+        _check(to_np(o), to_np(ht), oref, href, TOL_BF16, label=f"window_levels={lv}")
+    assert infos[4]["n_window"] >= infos[1]["n_window"]
+
+
 @pytest.mark.slow
 def test_bf16_t32768_h32_sampled_heads(gdn):
     """The throughput workload at full size, in the launch configuration the
-    benchmark times; the oracle runs on a sample of heads of both kinds."""
+    benchmark times; the oracle runs on every head above the first window
+    level, every exact head and a few first-level window heads."""
     say("case bf16_t32768_h32 (full size, sampled heads)")
     import torch
     x = inputs.workload("bf16_t32768_h32")
     B, T, H = 1, 32768, 32
-    flags, _ = oracle.gate_scan(x.g, window_chunks=8)
-    win = [i for i in range(H) if flags[0, i]]
-    ex = [i for i in range(H) if not flags[0, i]]
-    # every exact head (their segments hand states to each other), a few window heads
-    heads = win[:3] + ex
+    lev = _window_levels(x.g)
+    say(f"  oracle levels {lev.tolist()}")
+    heads = [i for i in range(H) if lev[i] == 1][:3] + [i for i in range(H) if lev[i] != 1]
     t = to_gpu(x)
     ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(B, T, H), dtype=torch.uint8, device="cuda")
     o, ht = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], workspace=ws)
     info = gdn.gdn_chunk_fwd_plan_info(B, T, H, workspace=ws)
     say(f"  plan {info}")
-    assert info["error"] == 0
-    assert (info["n_exact"], info["n_window"]) == (len(ex), len(win))
-    assert info["P_exact"] >= 3
+    _check_plan_levels(info, lev, B * H)
     oref, href = oracle.fwd(x.q, x.k, x.v, x.g, x.beta, x.h0, heads=heads)
     _check(to_np(o), to_np(ht), oref, href, TOL_BF16, heads=heads, H=H, label="t32768 h32")
 
