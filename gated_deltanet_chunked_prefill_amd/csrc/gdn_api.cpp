@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "gdn_internal.h"
 
@@ -55,6 +56,42 @@ gdn_status fail(gdn_status st, const char* fmt, ...) {
 
 gdn_status hip_fail(hipError_t e, const char* what) {
     return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// A side stream per device (default priority, non-blocking), created on first
+// use and kept until the process ends: the backward forks its two independent
+// sweeps onto it and joins them back through events.
+constexpr int kMaxDevices = 64;
+hipStream_t g_side[kMaxDevices];
+std::mutex g_side_mu;
+
+hipError_t side_stream(hipStream_t* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    if (!g_side[dev]) {
+        e = hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking);
+        if (e != hipSuccess) {
+            g_side[dev] = nullptr;
+            return e;
+        }
+    }
+    *out = g_side[dev];
+    return hipSuccess;
+}
+
+// Make `waiter` wait for the work enqueued so far on `producer` (a fresh event
+// per hand-over, released once enqueued).
+hipError_t stream_wait(hipStream_t waiter, hipStream_t producer) {
+    hipEvent_t ev;
+    hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(ev, producer);
+    if (e == hipSuccess) e = hipStreamWaitEvent(waiter, ev, 0);
+    const hipError_t d = hipEventDestroy(ev);
+    return e != hipSuccess ? e : d;
 }
 
 constexpr int kChunk = 64;
@@ -395,26 +432,34 @@ gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const floa
         return fail(GDN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
 
     hipStream_t s = (hipStream_t)stream;
+    hipStream_t s2 = nullptr;
+    hipError_t e = side_stream(&s2);
+    if (e != hipSuccess) return hip_fail(e, "backward side stream");
     const int N = num_chunks(T);
     char* ws = (char*)workspace;
     float* hstore = (float*)(ws + L.hstore);
     float* dhstore = (float*)(ws + L.dhstore);
-    // 1. the state entering every chunk (the forward kernel, no outputs)
     gdn::FwdParams f{};
     f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.h0 = h0; f.o = nullptr; f.ht = nullptr;
     f.B = B; f.T = T; f.H = H; f.N = N; f.P = 1; f.w = 1; f.scale = scale;
     f.hstore = hstore;
-    hipError_t e = recorded(GDN_LAUNCH_BWD_STATES, s, [&] { return gdn::launch_fwd(f, gdn::PHASE_STATES, true, s); });
-    if (e != hipSuccess) return hip_fail(e, "backward state launch");
     gdn::BwdParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.dout = dout; p.dht = dht;
     p.dq = grad_q; p.dk = grad_k; p.dv = grad_v; p.dg = grad_g; p.dbeta = grad_beta; p.dh0 = grad_h0;
     p.B = B; p.T = T; p.H = H; p.N = N; p.scale = scale;
     p.hstore = hstore;
     p.dhstore = dhstore;
-    // 2. the state gradient, end to start
-    e = recorded(GDN_LAUNCH_BWD_DH, s, [&] { return gdn::launch_bwd_dh(p, true, s); });
+    // 1 and 2 are independent (B*H workgroups each) and run side by side: the
+    // state gradient, end to start, on the side stream, and the state entering
+    // every chunk (the forward kernel, no outputs) on the caller's stream
+    e = stream_wait(s2, s);
+    if (e != hipSuccess) return hip_fail(e, "backward fork");
+    e = recorded(GDN_LAUNCH_BWD_DH, s2, [&] { return gdn::launch_bwd_dh(p, true, s2); });
     if (e != hipSuccess) return hip_fail(e, "backward state-gradient launch");
+    e = recorded(GDN_LAUNCH_BWD_STATES, s, [&] { return gdn::launch_fwd(f, gdn::PHASE_STATES, true, s); });
+    if (e != hipSuccess) return hip_fail(e, "backward state launch");
+    e = stream_wait(s, s2);
+    if (e != hipSuccess) return hip_fail(e, "backward join");
     // 3. local gradients of every chunk
     e = recorded(GDN_LAUNCH_BWD_LOCAL, s, [&] { return gdn::launch_bwd_local(p, true, s); });
     if (e != hipSuccess) return hip_fail(e, "backward local-gradient launch");

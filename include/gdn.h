@@ -152,9 +152,13 @@ size_t gdn_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, gdn_dty
  * The forward inputs (q, k, v, g, beta, h0) must be the ones of the forward.
  * Only bf16 I/O is supported (GDN_ERR_UNSUPPORTED for float32).  workspace:
  * at least gdn_chunk_bwd_workspace_size() bytes, 256-byte aligned (required).
- * Runs three launches on `stream`: the forward kernel storing the state
- * entering every chunk, the state gradient from the last chunk to the first,
- * and the local gradients of all chunks in parallel. */
+ * Runs three launches: the forward kernel storing the state entering every
+ * chunk (on `stream`) and, side by side with it, the state gradient from the
+ * last chunk to the first (on a library-owned side stream of the current
+ * device, created on first use with default priority, joined back through an
+ * event); then the local gradients of all chunks in parallel on `stream`.
+ * The call is ordered after earlier work on `stream` and later work on
+ * `stream` is ordered after it, as with a single stream. */
 gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const float* h0, const void* dout, const float* dht,
                          void* grad_q, void* grad_k, void* grad_v, float* grad_g,
