@@ -185,8 +185,8 @@ BwdLayout bwd_layout(int B, int T, int H) {
     BwdLayout L{};
     const size_t N = num_chunks(T), bh = (size_t)B * H, SS = 128 * 128;
     size_t off = 0;
-    L.hstore = off;  off += align_up(bh * (N + 1) * SS * sizeof(float));
-    L.dhstore = off; off += align_up(bh * N * SS * sizeof(float));
+    L.hstore = off;  off += align_up(bh * (N + 1) * SS * sizeof(uint16_t));   // bf16
+    L.dhstore = off; off += align_up(bh * N * SS * sizeof(uint16_t));
     L.total = off;
     return L;
 }
@@ -437,8 +437,8 @@ gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const floa
     if (e != hipSuccess) return hip_fail(e, "backward side stream");
     const int N = num_chunks(T);
     char* ws = (char*)workspace;
-    float* hstore = (float*)(ws + L.hstore);
-    float* dhstore = (float*)(ws + L.dhstore);
+    __bf16* hstore = (__bf16*)(ws + L.hstore);
+    __bf16* dhstore = (__bf16*)(ws + L.dhstore);
     gdn::FwdParams f{};
     f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.h0 = h0; f.o = nullptr; f.ht = nullptr;
     f.B = B; f.T = T; f.H = H; f.N = N; f.P = 1; f.w = 1; f.scale = scale;

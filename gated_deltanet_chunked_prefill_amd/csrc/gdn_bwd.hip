@@ -113,7 +113,7 @@ __device__ __noinline__ void dh_state_loop(const BwdParams& prm, Smem<T>& sm, in
     const size_t SS = (size_t)kDk * kDv;
     const int N = uni(prm.N);
     const float scale = uni(prm.scale);
-    float* const dst = uni(prm.dhstore) + (size_t)bh * N * SS;
+    __bf16* const dst = uni(prm.dhstore) + (size_t)bh * N * SS;
     const float* const dht = uni(prm.dht);
     float* const dh0 = uni(prm.dh0);
     Lane<T> L;
@@ -131,7 +131,7 @@ __device__ __noinline__ void dh_state_loop(const BwdParams& prm, Smem<T>& sm, in
         for (int i = 0; i < N; ++i) {
             const int c = N - 1 - i;
             const int slot = i % 3, vb = i & 1;
-            store_state(uni(dst + (size_t)c * SS), L.w, L.lane, dH);
+            store_state_bf16t(uni(dst + (size_t)c * SS), L.w, L.lane, dH);
             dh_chunk_step<T>(L, sm.kt[slot], sm.qt[slot], sm.vt[vb], sm.t32[vb], sm.gam_vec[vb],
                              sm.e_vec[vb], sm.gc[vb][0], scale, dH);
             lds_barrier();
@@ -142,7 +142,7 @@ __device__ __noinline__ void dh_state_loop(const BwdParams& prm, Smem<T>& sm, in
             lds_barrier();
             lds_barrier();
             lds_barrier();
-            store_state(uni(dst + (size_t)c * SS), L.w, L.lane, dH);
+            store_state_bf16t(uni(dst + (size_t)c * SS), L.w, L.lane, dH);
             dh_chunk_step<T>(L, sm.kt[0], sm.qt[0], sm.vt[0], sm.t32[0], sm.gam_vec[0], sm.e_vec[0],
                              sm.gc[0][0], scale, dH);
         }
@@ -264,30 +264,24 @@ struct LocalSmem {
     float red[4];
 };
 
-// B fragment of a 128 x 128 float32 state in HBM, contraction over its rows, in
-// the column order of the 16-byte tile fragments: lane (n, g) gets
-// S[16ks + 8g + j][col], j = 0..7.
+// B fragment of a stored state (bf16, transposed [dv][dk]), contraction over
+// its dk rows, in the column order of the 16-byte tile fragments: lane (n, g)
+// gets S[16ks + 8g + j][col], j = 0..7, one 16-byte load.
 template <typename T>
-__device__ __forceinline__ typename FragOf<T>::type state_colfrag(const float* S, int ks, int g, int col) {
+__device__ __forceinline__ typename FragOf<T>::type state_colfrag(const __bf16* St, int ks, int g, int col) {
     static_assert(sizeof(T) == 2, "the backward is built for bf16 only");
-    typename FragOf<T>::type f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) f[j] = (T)S[(16 * ks + 8 * g + j) * kDv + col];
-    return f;
+    typedef __attribute__((address_space(1))) const typename FragOf<T>::type gfrag;
+    return *(gfrag*)(St + (size_t)col * kDk + 16 * ks + 8 * g);
 }
-// B fragment of the transposed state (contraction over its columns), same order:
-// lane (n, g) gets S[row][16ks + 8g + j].
+// B fragment of the transposed state (contraction over its dv columns), same
+// order: lane (n, g) gets S[row][16ks + 8g + j] (a column of the stored layout).
 template <typename T>
-__device__ __forceinline__ typename FragOf<T>::type state_rowfrag(const float* S, int row, int ks, int g) {
+__device__ __forceinline__ typename FragOf<T>::type state_rowfrag(const __bf16* St, int row, int ks, int g) {
     static_assert(sizeof(T) == 2, "the backward is built for bf16 only");
-    const f32x4 lo = *(const f32x4*)(S + (size_t)row * kDv + 16 * ks + 8 * g);
-    const f32x4 hi = *(const f32x4*)(S + (size_t)row * kDv + 16 * ks + 8 * g + 4);
+    typedef __attribute__((address_space(1))) const __bf16 gbf;
     typename FragOf<T>::type f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        f[j] = (T)lo[j];
-        f[4 + j] = (T)hi[j];
-    }
+    for (int j = 0; j < 8; ++j) f[j] = ((gbf*)St)[(size_t)(16 * ks + 8 * g + j) * kDk + row];
     return f;
 }
 
@@ -347,9 +341,9 @@ __global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_kernel(BwdPara
     const int lane = L.lane, n = L.n, g = L.g;
     const float scale = prm.scale;
     const size_t SS = (size_t)kDk * kDv;
-    const float* const Hc = prm.hstore + ((size_t)bh * (N + 1) + c) * SS;
-    const float* const Hn = Hc + SS;
-    const float* const dHn = prm.dhstore + ((size_t)bh * N + c) * SS;
+    const __bf16* const Hc = prm.hstore + ((size_t)bh * (N + 1) + c) * SS;
+    const __bf16* const Hn = Hc + SS;
+    const __bf16* const dHn = prm.dhstore + ((size_t)bh * N + c) * SS;
 
     // ---- phase 0: tiles, gates
     {
@@ -599,9 +593,11 @@ __global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_kernel(BwdPara
     // ---- phase 5: <dHn, Hn> for the gradient of gamma_C
     {
         float acc = 0.f;
-        for (int i = tid; i < kDk * kDv / 4; i += kLocalThreads) {
-            const f32x4 a = ((const f32x4*)dHn)[i], s = ((const f32x4*)Hn)[i];
-            acc += a[0] * s[0] + a[1] * s[1] + a[2] * s[2] + a[3] * s[3];
+        typedef __attribute__((address_space(1))) const bf16x8 gb8;
+        for (int i = tid; i < kDk * kDv / 8; i += kLocalThreads) {
+            const bf16x8 a = ((gb8*)dHn)[i], s = ((gb8*)Hn)[i];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc += (float)a[j] * (float)s[j];
         }
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) acc += __shfl_xor(acc, d, 64);

@@ -549,6 +549,28 @@ __device__ __forceinline__ void store_state(float* dst, int w, int lane, const f
                                                   (32 * ht + 8 * (r >> 2) + (r & 3)) * kDv * 4, 0);
 }
 
+// The state as bf16 in the transposed layout [dv][dk]: a lane's four
+// consecutive accumulator rows 32ht + 8q + 4g .. +3 of column 32w + n are one
+// 8-byte word.  Buffer stores with the row offsets as constants.
+__device__ __forceinline__ void store_state_bf16t(__bf16* dst, int w, int lane, const f32x16* Hs) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 b4_t __attribute__((ext_vector_type(4)));
+    const int n = lane & 31, g = lane >> 5;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, (int)(kDk * kDv * 2), 0x00020000);
+    const int voff = ((32 * w + n) * kDk + 4 * g) * 2;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            b4_t v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (__bf16)Hs[ht][4 * q + e];
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), rs, voff,
+                                                  (32 * ht + 8 * q) * 2, 0);
+        }
+}
+
 // Number of valid tokens in chunk c of a sequence of T tokens.
 __device__ __forceinline__ int chunk_len(int T, int c) {
     return T - c * kChunk < kChunk ? T - c * kChunk : kChunk;

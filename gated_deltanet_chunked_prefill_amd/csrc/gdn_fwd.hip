@@ -298,7 +298,7 @@ __device__ __noinline__ void state_loop(const FwdParams& prm, Smem<T>& sm, const
     const int Tn = uni(prm.T), H = uni(prm.H), N = uni(prm.N), P = uni(prm.P);
     const float scale = uni(prm.scale);
     T* const o = uni((T*)prm.o);
-    float* const hst = KEEP ? uni(prm.hstore) : nullptr;
+    __bf16* const hst = KEEP ? uni(prm.hstore) : nullptr;
     const int b = bh / H, h = bh % H;
     const size_t SS = (size_t)kDk * kDv;
     const int nch = c_end - c_begin;
@@ -319,7 +319,7 @@ __device__ __noinline__ void state_loop(const FwdParams& prm, Smem<T>& sm, const
     auto emit = [&](int c) { return MODE == MODE_FULL && o != nullptr && c >= c_out; };
     // the state entering every chunk this task owns (for the backward)
     auto keep = [&](int c) {
-        if (KEEP && c >= c_out) store_state(hst + (hst_base + c) * SS, L.w, L.lane, Hs);
+        if (KEEP && c >= c_out) store_state_bf16t(hst + (hst_base + c) * SS, L.w, L.lane, Hs);
     };
     if constexpr (kPipe) {
         lds_barrier();

@@ -69,7 +69,8 @@ struct FwdParams {
     __bf16* mt;
     float* eg;
     int* tr_cnt;
-    float* hstore;     // nullable: [B*H, N+1, dk, dv] state entering each chunk, then the final state
+    __bf16* hstore;    // nullable: [B*H, N+1, dv, dk] bf16, transposed: state entering each chunk,
+                       // then the final state
     FwdPlan* plan;     // split forward: written by the plan kernel
     TaskRec* jobs;
     int cus;           // compute units of the device
@@ -110,8 +111,9 @@ struct BwdParams {
     float* dh0;           // nullable
     int B, T, H, N;
     float scale;
-    const float* hstore;  // [B*H, N+1, dk, dv] state entering each chunk, then the final state
-    float* dhstore;       // [B*H, N, dk, dv] gradient reaching the end of each chunk
+    const __bf16* hstore;  // [B*H, N+1, dv, dk] bf16, transposed: state entering each chunk, then
+                           // the final state
+    __bf16* dhstore;       // [B*H, N, dv, dk] bf16, transposed: gradient reaching the end of each chunk
 };
 hipError_t launch_bwd_dh(const BwdParams& p, bool bf16, hipStream_t s);
 hipError_t launch_bwd_local(const BwdParams& p, bool bf16, hipStream_t s);

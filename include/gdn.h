@@ -137,7 +137,7 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          void* stream);
 
 /* Workspace bytes for gdn_chunk_bwd ((size_t)-1 for invalid arguments):
- * B*H*(2N+1) float32 128 x 128 matrices (N = number of 64-token chunks), the
+ * B*H*(2N+1) bfloat16 128 x 128 matrices (N = number of 64-token chunks), the
  * state entering every chunk plus the final state, and the state gradient
  * reaching the end of every chunk. */
 size_t gdn_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, gdn_dtype dtype);

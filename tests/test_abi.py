@@ -109,7 +109,7 @@ def test_bwd_validation_before_launch():
     lib = _lib.load()
     A = 1 << 20
     full = [A] * 11
-    SS = 128 * 128 * 4
+    SS = 128 * 128 * 2   # bf16 states
     # two chunks: 3 entry/final states + 2 state gradients per head
     assert lib.gdn_chunk_bwd_workspace_size(1, 128, 1, 128, 128, 1) == 5 * SS
     assert lib.gdn_chunk_bwd_workspace_size(2, 100, 3, 128, 128, 1) == 6 * 5 * SS
