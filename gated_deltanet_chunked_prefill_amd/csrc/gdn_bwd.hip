@@ -16,7 +16,7 @@
 //      carry dH in MFMA accumulators.  dHn of every chunk is stored for launch 2.
 //
 //   2. local gradients, one workgroup per (head, chunk), all chunks at once.
-//      From the chunk's entering state H, its final state Hn and dHn it recomputes
+//      From the chunk's entering state H and dHn it recomputes
 //      the chunk's forward in gated-matrix form (Sg_rs = Gamma_r / Gamma_s, s <= r;
 //      Pm = tril(Q K^T) o Sg, Mg = strict_lower(K K^T) o Sg, T = (I + diag(beta) Mg)^-1,
 //      Y = V - diag(Gamma) K H, V' = T diag(beta) Y) and runs reverse mode:
@@ -29,6 +29,8 @@
 //        dbeta_r = dZ_r . (Y - Mg V')_r
 //        dgamma_r = sum_s X_rs - sum_s X_sr + q_r . dq2_r + k_r . dk3_r - k_r . dk4_r
 //                   (+ <dHn, Hn> for the last position),  X = dPm o Pm + dMg o Mg,
+//                   with Hn = Gamma_C H + K^T diag(E) V' the chunk's final state, so
+//                   <dHn, Hn> = Gamma_C <dHn, H> + sum_r E_r (K dHn)_r . V'_r
 //        dg = reverse cumulative sum of dgamma inside the chunk.
 //      The K K^T gradient is bundled as (dA + dA^T) K (FlashQLA talk summary,
 //      onedev.kr, paragraph 6); the four chunk steps being inverted are those of
@@ -342,7 +344,6 @@ __global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_kernel(BwdPara
     const float scale = prm.scale;
     const size_t SS = (size_t)kDk * kDv;
     const __bf16* const Hc = prm.hstore + ((size_t)bh * (N + 1) + c) * SS;
-    const __bf16* const Hn = Hc + SS;
     const __bf16* const dHn = prm.dhstore + ((size_t)bh * N + c) * SS;
 
     // ---- phase 0: tiles, gates
@@ -410,6 +411,10 @@ __global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_kernel(BwdPara
 
     // ---- phase 2: this wave's 32 dv columns of Y, V', dV', dY
     f32x16 Y[2], Vp[2], dZ[2], dY[2];
+    // this lane's part of <dHn, Hn>, with Hn = Gamma_C Hc + K^T diag(E) V' the
+    // chunk's final state: <dHn, Hn> = Gamma_C <dHn, Hc> + sum_r E_r (K dHn)_r . V'_r,
+    // both terms over this wave's columns
+    float hn_dot = 0.f, hc_dot = 0.f;
     {
         f32x16 KH[2] = {zero16(), zero16()};
 #pragma unroll
@@ -417,6 +422,10 @@ __global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_kernel(BwdPara
             const F hf = state_colfrag<T>(Hc, ks, g, 32 * w + n);
             KH[0] = mma(L.f128(sm.kt, 0, ks), hf, KH[0]);
             KH[1] = mma(L.f128(sm.kt, 1, ks), hf, KH[1]);
+            // <dHn, Hc> over this wave's columns (the same elements of dHn)
+            const F df = state_colfrag<T>(dHn, ks, g, 32 * w + n);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) hc_dot += (float)hf[j] * (float)df[j];
         }
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
@@ -431,6 +440,7 @@ __global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_kernel(BwdPara
     }
     const f32x16 be0 = rows_of(sm.beta, 0, g), be1 = rows_of(sm.beta, 1, g);
     f32x16 MgV0 = zero16(), MgV1 = zero16();
+
     {
         // V'_0 = T_00 diag(beta_0) Y_0 ; V'_1 = T_11 diag(beta_1) (Y_1 - Mg_10 V'_0)
         const f32x16 z0 = Y[0] * be0;
@@ -475,6 +485,8 @@ __global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_kernel(BwdPara
         for (int rt = 0; rt < 2; ++rt) {
             const f32x16 e = rows_of(sm.E, rt, g);
             dVp[rt] = PdO[rt] * scale + e * KdH[rt];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) hn_dot += e[r] * KdH[rt][r] * Vp[rt][r];
         }
         // dZ_1 = T_11^T dV'_1 ; dZ_0 = T_00^T (dV'_0 - Mg_10^T diag(beta_1) dZ_1)
         dZ[1] = zero16();
@@ -539,6 +551,7 @@ __global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_kernel(BwdPara
         for (int ks = 0; ks < 8; ++ks) {
             const F hr = state_rowfrag<T>(Hc, 32 * w + n, ks, g);
             const F dr = state_rowfrag<T>(dHn, 32 * w + n, ks, g);
+
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
                 a2[rt] = mma(L.f128(sm.dot, rt, ks), hr, a2[rt]);
@@ -590,15 +603,9 @@ __global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_kernel(BwdPara
             st_rows_hbm<T>(dkout, dk[rt], rt, g, n, w, H, nv);
         }
     }
-    // ---- phase 5: <dHn, Hn> for the gradient of gamma_C
+    // ---- phase 5: <dHn, Hn> for the gradient of gamma_C, this wave's part
     {
-        float acc = 0.f;
-        typedef __attribute__((address_space(1))) const bf16x8 gb8;
-        for (int i = tid; i < kDk * kDv / 8; i += kLocalThreads) {
-            const bf16x8 a = ((gb8*)dHn)[i], s = ((gb8*)Hn)[i];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc += (float)a[j] * (float)s[j];
-        }
+        float acc = sm.Gam[kChunk - 1] * hc_dot + hn_dot;   // Gamma_{63} = Gamma_C
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) acc += __shfl_xor(acc, d, 64);
         if (lane == 0) sm.red[w] = acc;
