@@ -779,40 +779,58 @@ constexpr float kCostWarm = 0.7f;
 constexpr int kSeg0Weight = 11;
 
 struct WinLevels {
-    int n[kMaxWindowLevels];   // window heads per level (index m - 1)
-    int levels, N, w, pmax;
+    int n[kMaxWindowLevels];     // window heads per level (index m - 1)
+    float c[kMaxWindowLevels];   // warm-up cost kCostWarm m w of a level
+    int cap[kMaxWindowLevels];   // most segments of a level: min(pmax, max(1, N / (m w)))
+    int levels, N;
+    // per-level constants, computed once per plan
+    __device__ void init(int levels_, int N_, int w, int pmax) {
+        levels = levels_;
+        N = N_;
+#pragma unroll
+        for (int m = 1; m <= kMaxWindowLevels; ++m) {
+            c[m - 1] = kCostWarm * m * w;
+            int cp = N / (m * w);
+            cp = cp < 1 ? 1 : cp;
+            cap[m - 1] = cp < pmax ? cp : pmax;
+        }
+    }
 };
 
 // Fewest segments for a level-m head so that each job costs at most M (0: none).
 __device__ __forceinline__ int win_segments(const WinLevels& wl, int m, float M) {
-    const float c = kCostWarm * m * wl.w;
+    const float c = wl.c[m - 1];
     if (M >= (float)wl.N) return 1;
     if (M <= c) return 0;
-    int cap = wl.N / (m * wl.w);
-    cap = cap < 1 ? 1 : cap;
-    cap = cap < wl.pmax ? cap : wl.pmax;
-    const float p = ceilf(((float)wl.N - c) / (M - c));
-    return p <= (float)cap ? (int)p : 0;
+    const float p = ceilf(((float)wl.N - c) * __frcp_rn(M - c));
+    return p <= (float)wl.cap[m - 1] ? (int)p : 0;
 }
 
 // Smallest job cost of the window heads on `free` workgroups; Pm[m-1] gets the
 // segment counts.  With fewer workgroups than window heads every head is one job.
+// Every loop over the levels is unrolled so that the per-level values stay in
+// registers.
 __device__ float window_cost(const WinLevels& wl, int free, int* Pm) {
     int n_w = 0;
-    for (int m = 1; m <= wl.levels; ++m) n_w += wl.n[m - 1];
-    for (int m = 1; m <= wl.levels; ++m) Pm[m - 1] = 1;
+#pragma unroll
+    for (int m = 1; m <= kMaxWindowLevels; ++m) {
+        n_w += m <= wl.levels ? wl.n[m - 1] : 0;
+        Pm[m - 1] = 1;
+    }
     if (n_w == 0) return 0.f;
     if (free < n_w) return free > 0 ? (float)((n_w + free - 1) / free) * wl.N : -1.f;
     float lo = 0.f, hi = (float)wl.N;   // hi is feasible (one job per head)
-    for (int it = 0; it < 24; ++it) {
+    for (int it = 0; it < 16; ++it) {
         const float mid = 0.5f * (lo + hi);
         int need = 0;
         bool ok = true;
-        for (int m = 1; m <= wl.levels && ok; ++m) {
-            if (wl.n[m - 1] == 0) continue;
-            const int p = win_segments(wl, m, mid);
-            ok = p > 0;
-            need += wl.n[m - 1] * p;
+#pragma unroll
+        for (int m = 1; m <= kMaxWindowLevels; ++m) {
+            if (m <= wl.levels && wl.n[m - 1] > 0) {
+                const int p = win_segments(wl, m, mid);
+                ok = ok && p > 0;
+                need += wl.n[m - 1] * p;
+            }
         }
         if (ok && need <= free)
             hi = mid;
@@ -820,13 +838,14 @@ __device__ float window_cost(const WinLevels& wl, int free, int* Pm) {
             lo = mid;
     }
     float cost = 0.f;
-    for (int m = 1; m <= wl.levels; ++m) {
-        if (wl.n[m - 1] == 0) continue;
-        const int p = win_segments(wl, m, hi);
-        Pm[m - 1] = p;
-        const float c = kCostWarm * m * wl.w;
-        const float t = ((float)wl.N + (p - 1) * c) / p;
-        cost = t > cost ? t : cost;
+#pragma unroll
+    for (int m = 1; m <= kMaxWindowLevels; ++m) {
+        if (m <= wl.levels && wl.n[m - 1] > 0) {
+            const int p = win_segments(wl, m, hi);
+            Pm[m - 1] = p;
+            const float t = ((float)wl.N + (p - 1) * wl.c[m - 1]) / p;
+            cost = t > cost ? t : cost;
+        }
     }
     return cost;
 }
@@ -899,11 +918,17 @@ __device__ int win_bound(int p, int P, int N, float c, bool forced) {
 }
 
 // Planner scratch in the workgroup's LDS (used before any job runs).
+// Per-head tables of the planner live in LDS up to this many heads (always, for
+// the automatic split, which needs B*H < CUs/2), in the workspace beyond.
+constexpr int kPlanHeads = 4096;
+
 struct PlanLds {
     int bound[kMaxSegments + 1];
     int wave[kThreads / 64];
     int par[2 + kMaxWindowLevels];
     int cls[1 + kMaxWindowLevels];   // heads per class: exact, then window levels L .. 1
+    int lev[kPlanHeads];             // window level per head (0 = exact)
+    int hmap[kPlanHeads];            // heads by class
 };
 
 // The planner, run by workgroup 0 of the persistent launch before the jobs.
@@ -916,56 +941,67 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
     const float* const wpart = uni(prm.wpart);
     const int LV = wpart ? uni(prm.levels) : 0;
     int* const flags = uni(prm.flags);
+    const bool in_lds = nbh <= kPlanHeads;
+    int* const levp = in_lds ? pl.lev : flags;
+    int* const hm = in_lds ? pl.hmap : uni(prm.head_map);
     // 1. window levels (talk summary, paragraph 5): a head is a window head of
     //    level m when its largest sum of g over m*w consecutive chunks is at
     //    most log_eps, for the smallest such m; the first launch left the
     //    maxima per length and group of chunks, a run of threads reduces a head
+    //    (every level's loads issued together)
     if (wpart) {
-        // a run of tph threads per head (a power of two up to 64), all of a
-        // thread's loads issued at once
         const int NG = uni(prm.n_groups);
         int tph = 64;
         while (tph > 1 && tph * nbh > kThreads) tph >>= 1;
         const int hpr = kThreads / tph;   // heads per round
+        const size_t lstride = (size_t)B * NG * H;
         for (int h0 = 0; h0 < nbh; h0 += hpr) {
             const int bh = h0 + tid / tph, k = tid % tph;
             const int b = bh < nbh ? bh / H : 0, h = bh < nbh ? bh % H : 0;
-            int lev = 0;
-            for (int m = LV; m >= 1; --m) {
-                float best = -INFINITY;
-                if (bh < nbh) {
-                    const float* const src = wpart + (size_t)(m - 1) * B * NG * H;
-                    for (int q0 = k; q0 < NG; q0 += 8 * tph) {
-                        float v[8];
+            float best[kMaxWindowLevels];
 #pragma unroll
-                        for (int u = 0; u < 8; ++u) {
+            for (int m = 0; m < kMaxWindowLevels; ++m) best[m] = -INFINITY;
+            if (bh < nbh) {
+                for (int q0 = k; q0 < NG; q0 += 4 * tph) {
+                    float v[kMaxWindowLevels][4];
+#pragma unroll
+                    for (int m = 0; m < kMaxWindowLevels; ++m)
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
                             const int q = q0 + u * tph;
-                            v[u] = src[((size_t)b * NG + (q < NG ? q : NG - 1)) * H + h];
+                            v[m][u] = m < LV ? wpart[m * lstride + ((size_t)b * NG + (q < NG ? q : NG - 1)) * H + h]
+                                             : -INFINITY;
                         }
 #pragma unroll
-                        for (int u = 0; u < 8; ++u) best = v[u] > best ? v[u] : best;
-                    }
+                    for (int m = 0; m < kMaxWindowLevels; ++m)
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) best[m] = v[m][u] > best[m] ? v[m][u] : best[m];
                 }
-                for (int d = tph >> 1; d > 0; d >>= 1) {
-                    const float o = __shfl_xor(best, d, 64);
-                    best = o > best ? o : best;
-                }
-                if (N >= m * w && best <= prm.log_eps) lev = m;
-                if (m == 1 && bh < nbh && k == 0 && prm.maxwin) prm.maxwin[bh] = best;
             }
-            if (bh < nbh && k == 0) flags[bh] = lev;
+            int lev = 0;
+#pragma unroll
+            for (int m = kMaxWindowLevels; m >= 1; --m) {
+                float x = best[m - 1];
+                for (int d = tph >> 1; d > 0; d >>= 1) {
+                    const float o = __shfl_xor(x, d, 64);
+                    x = o > x ? o : x;
+                }
+                if (m <= LV && N >= m * w && x <= prm.log_eps) lev = m;
+                if (m == 1 && bh < nbh && k == 0 && prm.maxwin) prm.maxwin[bh] = x;
+            }
+            if (bh < nbh && k == 0) levp[bh] = lev;
         }
         __syncthreads();
     }
     // 2. choose the segment counts and the longest window kept (heads of a
     //    higher level are exact: for short sequences the exact split can be
-    //    cheaper than long warm-ups), then rank the heads by class (head_map:
-    //    exact heads, then window heads of level Lc, Lc-1, .., 1, each class in
-    //    head order)
+    //    cheaper than long warm-ups), then rank the heads by class (exact
+    //    heads, then window heads of level Lc, Lc-1, .., 1, each class in head
+    //    order)
     const int per = (nbh + kThreads - 1) / kThreads;
     const int lo = tid * per < nbh ? tid * per : nbh;
     const int hi = lo + per < nbh ? lo + per : nbh;
-    auto level_of = [&](int bh) { return wpart ? flags[bh] : 0; };
+    auto level_of = [&](int bh) { return wpart ? levp[bh] : 0; };
     for (int m = 0; m <= LV; ++m) {
         int cnt = 0;
         for (int bh = lo; bh < hi; ++bh) cnt += level_of(bh) == m ? 1 : 0;
@@ -974,6 +1010,8 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
         if (tid == 0) pl.cls[m] = tot;   // heads per level (0 = exact)
     }
     __syncthreads();
+    WinLevels base;
+    base.init(LV, N, w, pmax);
     if (wv == 0) {
         // candidates (P, Lc), one per lane and round, ordered by P, then by
         // decreasing Lc; the cheapest wins, ties go to the earlier candidate
@@ -985,12 +1023,10 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
             for (int i0 = 0; i0 < ncand; i0 += 64) {
                 int i = i0 + lane;
                 const int P = 1 + i / (LV + 1), lc = LV - i % (LV + 1);
-                WinLevels wl;
+                WinLevels wl = base;
                 wl.levels = lc;
-                wl.N = N;
-                wl.w = w;
-                wl.pmax = pmax;
                 int n_e = pl.cls[0];
+#pragma unroll
                 for (int m = 1; m <= kMaxWindowLevels; ++m) {
                     const int c = m <= LV ? pl.cls[m] : 0;
                     wl.n[m - 1] = m <= lc ? c : 0;
@@ -1024,10 +1060,9 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
     }
     __syncthreads();
     const int Lc = pl.par[1];
-    // window heads above the kept level become exact (flags rewritten)
+    // window heads above the kept level become exact
     auto cls_of = [&](int bh) { const int m = level_of(bh); return (m == 0 || m > Lc) ? 0 : 1 + (Lc - m); };
     int start = 0;   // first slot of the current class
-    int* const head_map = uni(prm.head_map);
     for (int ci = 0; ci <= Lc; ++ci) {
         int cnt = 0;
         for (int bh = lo; bh < hi; ++bh) cnt += cls_of(bh) == ci ? 1 : 0;
@@ -1035,29 +1070,32 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
         const int r = block_exclusive_scan(cnt, pl.wave, tot);
         int slot = start + r;
         for (int bh = lo; bh < hi; ++bh)
-            if (cls_of(bh) == ci) head_map[slot++] = bh;
+            if (cls_of(bh) == ci) hm[slot++] = bh;
         start += tot;
         if (tid == 0) pl.cls[ci] = tot;   // heads per class from here on
     }
-    __syncthreads();
+    // the levels that ran, for the record (0 = exact)
     if (wpart)
-        for (int bh = lo; bh < hi; ++bh)
-            if (flags[bh] > Lc) flags[bh] = 0;
+        for (int bh = lo; bh < hi; ++bh) {
+            const int m = levp[bh];
+            flags[bh] = m > Lc ? 0 : m;
+        }
+    __syncthreads();
     const int n_e = pl.cls[0];
     const int n_w = nbh - n_e;
-    WinLevels wl;
+    WinLevels wl = base;
     wl.levels = Lc;
-    wl.N = N;
-    wl.w = w;
-    wl.pmax = pmax;
+#pragma unroll
     for (int m = 1; m <= kMaxWindowLevels; ++m) wl.n[m - 1] = m <= Lc ? pl.cls[1 + Lc - m] : 0;
     if (wv == 0) {
         const int Pe = pl.par[0];
         int Pm[kMaxWindowLevels];
+#pragma unroll
         for (int m = 0; m < kMaxWindowLevels; ++m) Pm[m] = pmax;
         if (!prm.forced) plan_cost(Pe, n_e, wl, prm.cus, Pm);
         if (lane == 0) {
             int pw_max = 1;
+#pragma unroll
             for (int m = 0; m < kMaxWindowLevels; ++m) {
                 pl.par[2 + m] = Pm[m];
                 if (m < Lc && wl.n[m] > 0 && Pm[m] > pw_max) pw_max = Pm[m];
@@ -1068,7 +1106,7 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
     __syncthreads();
     const int Pe = pl.par[0];
     int n_win_jobs = 0;
-    for (int m = 1; m <= Lc; ++m) n_win_jobs += wl.n[m - 1] * pl.par[1 + m];
+    for (int m = 1; m <= Lc; ++m) n_win_jobs += pl.cls[1 + Lc - m] * pl.par[1 + m];
     const int g_win = n_e + (Pe >= 3 ? n_e * (Pe - 2) : 0);
     const int g_chain = g_win + n_win_jobs;
     const int g_p3 = g_chain + (Pe >= 3 ? 4 * n_e : 0);
@@ -1093,36 +1131,37 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
     TaskRec* const jobs = uni(prm.jobs);
     for (int j = tid; j < n_jobs; j += kThreads) {
         if (j < n_e) {   // segment 0 (or the whole sequence)
-            const int bh = head_map[j];
+            const int bh = hm[j];
             if (Pe == 1)
                 put_job(jobs, j, bh, 0, 0, 0, N, MODE_FULL, init0, dst_last);
             else
                 put_job(jobs, j, bh, 0, 0, 0, pl.bound[1], MODE_FULL, init0, DST_HS_NEXT);
         } else if (j < g_win) {   // pass-1 of segment p, segment-major
             const int p = 1 + (j - n_e) / n_e, e = (j - n_e) % n_e;
-            put_job(jobs, j, head_map[e], p, pl.bound[p], pl.bound[p + 1], pl.bound[p + 1], MODE_PASS1,
+            put_job(jobs, j, hm[e], p, pl.bound[p], pl.bound[p + 1], pl.bound[p + 1], MODE_PASS1,
                     INIT_ZERO, DST_TRANSITION);
         } else if (j < g_chain) {   // window segments, level by level (longest first), head-major
             int jw = j - g_win, hbase = n_e, m = Lc;
             for (; m > 1; --m) {
-                const int nj = wl.n[m - 1] * pl.par[1 + m];
+                const int nm = pl.cls[1 + Lc - m];   // heads of level m
+                const int nj = nm * pl.par[1 + m];
                 if (jw < nj) break;
                 jw -= nj;
-                hbase += wl.n[m - 1];
+                hbase += nm;
             }
             const int P = pl.par[1 + m], W = m * w;
             const int r = jw / P, p = jw % P;
             const float c = kCostWarm * W;
             const int sb = win_bound(p, P, N, c, prm.forced != 0), e = win_bound(p + 1, P, N, c, prm.forced != 0);
             const int cb = sb - W > 0 ? sb - W : 0;
-            put_job(jobs, j, head_map[hbase + r], p, cb, sb, e, MODE_FULL,
+            put_job(jobs, j, hm[hbase + r], p, cb, sb, e, MODE_FULL,
                     (cb == 0 && has_h0) ? INIT_H0 : INIT_ZERO, p == P - 1 ? dst_last : DST_NONE);
         } else if (j < g_p3) {   // chain, one job per 32-column block
             const int e = (j - g_chain) / 4, cb = (j - g_chain) % 4;
-            put_job(jobs, j, head_map[e], 1, cb, 0, Pe - 1, MODE_CHAIN, 0, 0);
+            put_job(jobs, j, hm[e], 1, cb, 0, Pe - 1, MODE_CHAIN, 0, 0);
         } else {   // pass-3 of segment p, segment-major
             const int p = 1 + (j - g_p3) / n_e, e = (j - g_p3) % n_e;
-            put_job(jobs, j, head_map[e], p, pl.bound[p], pl.bound[p], pl.bound[p + 1], MODE_FULL,
+            put_job(jobs, j, hm[e], p, pl.bound[p], pl.bound[p], pl.bound[p + 1], MODE_FULL,
                     INIT_HS_WAIT, p == Pe - 1 ? dst_last : DST_NONE);
         }
     }
