@@ -358,7 +358,9 @@ gdn_status gdn_chunk_fwd_plan_info(int B, int T, int H, const gdn_options* opt, 
     if (!workspace) return fail(GDN_ERR_WORKSPACE, "the split forward's workspace is required");
     const FwdLayout L = fwd_layout(B, T, H, P);
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = hipMemcpyAsync(info, (const char*)workspace + L.plan, sizeof(gdn::FwdPlan),
+    static_assert(sizeof(gdn::FwdPlan) >= 8 * sizeof(int32_t) && sizeof(gdn::FwdPlan) <= 16 * sizeof(int32_t),
+                  "plan words: eight reported, at most sixteen reset");
+    hipError_t e = hipMemcpyAsync(info, (const char*)workspace + L.plan, 8 * sizeof(int32_t),
                                   hipMemcpyDeviceToHost, s);
     if (e != hipSuccess) return hip_fail(e, "plan read-back");
     e = hipStreamSynchronize(s);

@@ -700,12 +700,16 @@ template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_queue_kernel(FwdParams prm) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     Smem<T>& sm = *reinterpret_cast<Smem<T>*>(smem_raw);
-    // workgroup 0 writes the plan and the job list, then releases the others
-    // (the ready word was cleared by the preceding launch)
+    // one workgroup writes the plan and the job list, then releases the others
     // (the ready word, cleared by the preceding launch, becomes n_jobs + 1; the
     // job records are written back before it and read with device-coherent loads)
     int* const ready = &prm.plan->ready;
-    if (blockIdx.x == 0) {
+    // the first workgroup to arrive plans (the dispatch order of workgroups is
+    // not their index order)
+    if (threadIdx.x == 0)
+        sm.islot[2] = __hip_atomic_fetch_add(&prm.plan->ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (uni(sm.islot[2]) == 0) {
         plan_wg<T>(prm, sm);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         __syncthreads();
@@ -802,7 +806,7 @@ __device__ __forceinline__ int win_segments(const WinLevels& wl, int m, float M)
     const float c = wl.c[m - 1];
     if (M >= (float)wl.N) return 1;
     if (M <= c) return 0;
-    const float p = ceilf(((float)wl.N - c) * __frcp_rn(M - c));
+    const float p = ceilf(((float)wl.N - c) * __builtin_amdgcn_rcpf(M - c));
     return p <= (float)wl.cap[m - 1] ? (int)p : 0;
 }
 
@@ -820,7 +824,7 @@ __device__ float window_cost(const WinLevels& wl, int free, int* Pm) {
     if (n_w == 0) return 0.f;
     if (free < n_w) return free > 0 ? (float)((n_w + free - 1) / free) * wl.N : -1.f;
     float lo = 0.f, hi = (float)wl.N;   // hi is feasible (one job per head)
-    for (int it = 0; it < 16; ++it) {
+    for (int it = 0; it < 12; ++it) {   // M to within N / 4096 chunk steps
         const float mid = 0.5f * (lo + hi);
         int need = 0;
         bool ok = true;
@@ -931,7 +935,8 @@ struct PlanLds {
     int hmap[kPlanHeads];            // heads by class
 };
 
-// The planner, run by workgroup 0 of the persistent launch before the jobs.
+// The planner, run by the first workgroup of the persistent launch to arrive,
+// before any job.
 template <typename T>
 __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
     static_assert(sizeof(PlanLds) <= sizeof(Smem<T>), "planner scratch exceeds the LDS");
@@ -1034,8 +1039,9 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
                 }
                 float t = 3.0e38f;
                 const bool ok = i < ncand && (n_e > 0 || P == 1) && P != 2 && (P == 1 || n_e * (P - 1) <= prm.cus);
-                int pm_unused[kMaxWindowLevels];
-                if (ok) t = plan_cost(P, n_e, wl, prm.cus, pm_unused);
+                int pm[kMaxWindowLevels];
+                if (ok) t = plan_cost(P, n_e, wl, prm.cus, pm);
+                const int mine = i;
 #pragma unroll
                 for (int d = 1; d < 64; d <<= 1) {
                     const float ot = __shfl_xor(t, d, 64);
@@ -1048,10 +1054,20 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
                 if (t < best * 0.999f) {
                     best = t;
                     bi = i;
+                    // the winning lane keeps its window segment counts
+                    if (mine == i) {
+#pragma unroll
+                        for (int m = 0; m < kMaxWindowLevels; ++m) pl.par[2 + m] = pm[m];
+                    }
                 }
             }
             Pe = 1 + bi / (LV + 1);
             Lc = LV - bi % (LV + 1);
+        } else {
+            if (lane == 0) {
+#pragma unroll
+                for (int m = 0; m < kMaxWindowLevels; ++m) pl.par[2 + m] = pmax;
+            }
         }
         if (lane == 0) {
             pl.par[0] = Pe;
@@ -1087,21 +1103,14 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
     wl.levels = Lc;
 #pragma unroll
     for (int m = 1; m <= kMaxWindowLevels; ++m) wl.n[m - 1] = m <= Lc ? pl.cls[1 + Lc - m] : 0;
-    if (wv == 0) {
-        const int Pe = pl.par[0];
-        int Pm[kMaxWindowLevels];
+    if (tid == 0) {
+        int pw_max = 1;
 #pragma unroll
-        for (int m = 0; m < kMaxWindowLevels; ++m) Pm[m] = pmax;
-        if (!prm.forced) plan_cost(Pe, n_e, wl, prm.cus, Pm);
-        if (lane == 0) {
-            int pw_max = 1;
-#pragma unroll
-            for (int m = 0; m < kMaxWindowLevels; ++m) {
-                pl.par[2 + m] = Pm[m];
-                if (m < Lc && wl.n[m] > 0 && Pm[m] > pw_max) pw_max = Pm[m];
-            }
-            pl.par[1] = pw_max;
+        for (int m = 0; m < kMaxWindowLevels; ++m) {
+            const int pm = pl.par[2 + m];
+            if (m < Lc && wl.n[m] > 0 && pm > pw_max) pw_max = pm;
         }
+        pl.par[1] = pw_max;
     }
     __syncthreads();
     const int Pe = pl.par[0];

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void fwd_sums_kernel(const float* __restrict__
     const int tid = threadIdx.x;
     const int wg = blockIdx.y * gridDim.x + blockIdx.x, nwg = gridDim.x * gridDim.y;
     for (int i = wg * 256 + tid; i < nzero; i += nwg * 256) zero[i] = 0;
-    if (wg == 0 && tid < 8) plan_words[tid] = 0;
+    if (wg == 0 && tid < 16) plan_words[tid] = 0;   // the planner's words (at most 16)
     if (sums) chunk_sums_wg(g, T, H, N, blockIdx.x, blockIdx.y, sums);
 }
 
