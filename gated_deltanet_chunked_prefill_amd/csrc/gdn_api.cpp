@@ -153,7 +153,7 @@ int plan(int B, int T, int H, int num_cus, const gdn_options& o) {
 }
 
 struct FwdLayout {
-    size_t csum, wpart, flags, maxwin, head_map, hs, counters, bz, mt, eg, plan, jobs, total;
+    size_t csum, wmax, flags, maxwin, head_map, hs, counters, bz, mt, eg, plan, jobs, total;
 };
 
 FwdLayout fwd_layout(int B, int T, int H, int P) {
@@ -162,7 +162,7 @@ FwdLayout fwd_layout(int B, int T, int H, int P) {
     const size_t N = num_chunks(T), bh = (size_t)B * H, SS = 128 * 128;
     size_t off = 0;
     L.csum = off;       off += align_up((size_t)B * N * H * sizeof(float));
-    L.wpart = off;      off += align_up((size_t)gdn::kMaxWindowLevels * B * gdn::window_groups(T) * H * sizeof(float));
+    L.wmax = off;       off += align_up((size_t)gdn::kMaxWindowLevels * bh * sizeof(int32_t));
     L.flags = off;      off += align_up(bh * sizeof(int32_t));
     L.maxwin = off;     off += align_up(bh * sizeof(float));
     L.head_map = off;   off += align_up(2 * bh * sizeof(int32_t));
@@ -284,7 +284,7 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
     gdn::FwdParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.o = o; p.ht = ht;
     p.B = B; p.T = T; p.H = H; p.N = N; p.P = P; p.w = op.window_chunks; p.scale = scale;
-    p.wpart = nullptr;
+    p.wmax = nullptr;
     const bool bf16 = dtype == GDN_BF16;
     hipError_t e;
     if (P == 1) {
@@ -308,27 +308,27 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
     p.maxwin = (float*)(ws + L.maxwin);
     p.head_map = (int*)(ws + L.head_map);
     p.log_eps = op.log_eps;
-    p.n_groups = gdn::window_groups(T);
     // window heads only when a window fits the sequence (no head qualifies
     // otherwise) and the first launch can stage it
     // (longer windows are tried only while they fit the sequence and the staging)
     p.levels = 0;
     if (op.use_window && op.window_chunks <= N && op.window_chunks <= gdn::max_window_chunks()) {
-        p.wpart = (float*)(ws + L.wpart);
+        p.wmax = (const int*)(ws + L.wmax);
         p.levels = 1;
         while (p.levels < op.window_levels && (p.levels + 1) * op.window_chunks <= N &&
                (p.levels + 1) * op.window_chunks <= gdn::max_window_chunks())
             ++p.levels;
     }
-    float* const csum = p.wpart ? (float*)(ws + L.csum) : nullptr;
+    float* const csum = p.wmax ? (float*)(ws + L.csum) : nullptr;
+    int* const wmax = const_cast<int*>(p.wmax);
     e = recorded(GDN_LAUNCH_FWD_SUMS, s, [&] {
-        return gdn::launch_fwd_sums(g, B, T, H, csum, p.hs_cnt, 2 * nbh * P, (int*)p.plan, s);
+        return gdn::launch_fwd_sums(g, B, T, H, csum, p.hs_cnt, 2 * nbh * P, (int*)p.plan, wmax,
+                                    wmax ? p.levels * nbh : 0, s);
     });
     if (e != hipSuccess) return hip_fail(e, "forward preparation launch");
-    if (p.wpart) {
+    if (p.wmax) {
         e = recorded(GDN_LAUNCH_FWD_WINDOWS, s, [&] {
-            return gdn::launch_fwd_windows(csum, B, T, H, op.window_chunks, p.levels, const_cast<float*>(p.wpart),
-                                           s);
+            return gdn::launch_fwd_windows(csum, B, T, H, op.window_chunks, p.levels, wmax, s);
         });
         if (e != hipSuccess) return hip_fail(e, "forward window launch");
     }

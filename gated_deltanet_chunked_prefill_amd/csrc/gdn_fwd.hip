@@ -787,9 +787,11 @@ struct WinLevels {
     float c[kMaxWindowLevels];   // warm-up cost kCostWarm m w of a level
     int cap[kMaxWindowLevels];   // most segments of a level: min(pmax, max(1, N / (m w)))
     int levels, N;
+    int lmax;                    // levels tried (the same for every lane)
     // per-level constants, computed once per plan
     __device__ void init(int levels_, int N_, int w, int pmax) {
         levels = levels_;
+        lmax = levels_;
         N = N_;
 #pragma unroll
         for (int m = 1; m <= kMaxWindowLevels; ++m) {
@@ -801,20 +803,24 @@ struct WinLevels {
     }
 };
 
-// Fewest segments for a level-m head so that each job costs at most M (0: none).
-__device__ __forceinline__ int win_segments(const WinLevels& wl, int m, float M) {
+// Segments of a level-m head so that each job costs at most M: the smallest P
+// with (N + (P - 1) c) / P <= M; `bad` is set when none within the cap exists.
+__device__ __forceinline__ int win_segments(const WinLevels& wl, int m, float M, bool& bad) {
     const float c = wl.c[m - 1];
-    if (M >= (float)wl.N) return 1;
-    if (M <= c) return 0;
-    const float p = ceilf(((float)wl.N - c) * __builtin_amdgcn_rcpf(M - c));
-    return p <= (float)wl.cap[m - 1] ? (int)p : 0;
+    const float q = ((float)wl.N - c) * __builtin_amdgcn_rcpf(M - c);
+    int p = (int)ceilf(q);
+    p = M >= (float)wl.N ? 1 : p;
+    bad = M < (float)wl.N && (M <= c || p > wl.cap[m - 1]);
+    return p;
 }
 
 // Smallest job cost of the window heads on `free` workgroups; Pm[m-1] gets the
 // segment counts.  With fewer workgroups than window heads every head is one job.
-// Every loop over the levels is unrolled so that the per-level values stay in
-// registers.
+// The level loops are unrolled and branch-free (per-level values stay in
+// registers; lanes evaluating different candidates do not diverge), bounded by
+// the wave-uniform level count lmax.
 __device__ float window_cost(const WinLevels& wl, int free, int* Pm) {
+    const int lmax = uni(wl.lmax);
     int n_w = 0;
 #pragma unroll
     for (int m = 1; m <= kMaxWindowLevels; ++m) {
@@ -830,26 +836,27 @@ __device__ float window_cost(const WinLevels& wl, int free, int* Pm) {
         bool ok = true;
 #pragma unroll
         for (int m = 1; m <= kMaxWindowLevels; ++m) {
-            if (m <= wl.levels && wl.n[m - 1] > 0) {
-                const int p = win_segments(wl, m, mid);
-                ok = ok && p > 0;
-                need += wl.n[m - 1] * p;
-            }
+            if (m > lmax) break;
+            const bool act = m <= wl.levels && wl.n[m - 1] > 0;
+            bool bad;
+            const int p = win_segments(wl, m, mid, bad);
+            ok = ok && !(act && bad);
+            need += act ? wl.n[m - 1] * p : 0;
         }
-        if (ok && need <= free)
-            hi = mid;
-        else
-            lo = mid;
+        const bool feas = ok && need <= free;
+        hi = feas ? mid : hi;
+        lo = feas ? lo : mid;
     }
     float cost = 0.f;
 #pragma unroll
     for (int m = 1; m <= kMaxWindowLevels; ++m) {
-        if (m <= wl.levels && wl.n[m - 1] > 0) {
-            const int p = win_segments(wl, m, hi);
-            Pm[m - 1] = p;
-            const float t = ((float)wl.N + (p - 1) * wl.c[m - 1]) / p;
-            cost = t > cost ? t : cost;
-        }
+        if (m > lmax) break;
+        const bool act = m <= wl.levels && wl.n[m - 1] > 0;
+        bool bad;
+        const int p = win_segments(wl, m, hi, bad);
+        Pm[m - 1] = act ? p : 1;
+        const float t = ((float)wl.N + (p - 1) * wl.c[m - 1]) / (float)p;
+        cost = act && t > cost ? t : cost;
     }
     return cost;
 }
@@ -943,58 +950,27 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
     PlanLds& pl = *reinterpret_cast<PlanLds*>(&sm);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int B = uni(prm.B), H = uni(prm.H), nbh = B * H, N = uni(prm.N), pmax = uni(prm.P), w = uni(prm.w);
-    const float* const wpart = uni(prm.wpart);
-    const int LV = wpart ? uni(prm.levels) : 0;
+    const int* const wmax = uni(prm.wmax);
+    const int LV = wmax ? uni(prm.levels) : 0;
     int* const flags = uni(prm.flags);
     const bool in_lds = nbh <= kPlanHeads;
     int* const levp = in_lds ? pl.lev : flags;
     int* const hm = in_lds ? pl.hmap : uni(prm.head_map);
     // 1. window levels (talk summary, paragraph 5): a head is a window head of
     //    level m when its largest sum of g over m*w consecutive chunks is at
-    //    most log_eps, for the smallest such m; the first launch left the
-    //    maxima per length and group of chunks, a run of threads reduces a head
-    //    (every level's loads issued together)
-    if (wpart) {
-        const int NG = uni(prm.n_groups);
-        int tph = 64;
-        while (tph > 1 && tph * nbh > kThreads) tph >>= 1;
-        const int hpr = kThreads / tph;   // heads per round
-        const size_t lstride = (size_t)B * NG * H;
-        for (int h0 = 0; h0 < nbh; h0 += hpr) {
-            const int bh = h0 + tid / tph, k = tid % tph;
-            const int b = bh < nbh ? bh / H : 0, h = bh < nbh ? bh % H : 0;
-            float best[kMaxWindowLevels];
+    //    most log_eps, for the smallest such m; the preceding launch left that
+    //    largest sum per length and head (every level's value loaded together)
+    if (wmax) {
+        for (int bh = tid; bh < nbh; bh += kThreads) {
+            int key[kMaxWindowLevels];
 #pragma unroll
-            for (int m = 0; m < kMaxWindowLevels; ++m) best[m] = -INFINITY;
-            if (bh < nbh) {
-                for (int q0 = k; q0 < NG; q0 += 4 * tph) {
-                    float v[kMaxWindowLevels][4];
-#pragma unroll
-                    for (int m = 0; m < kMaxWindowLevels; ++m)
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const int q = q0 + u * tph;
-                            v[m][u] = m < LV ? wpart[m * lstride + ((size_t)b * NG + (q < NG ? q : NG - 1)) * H + h]
-                                             : -INFINITY;
-                        }
-#pragma unroll
-                    for (int m = 0; m < kMaxWindowLevels; ++m)
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) best[m] = v[m][u] > best[m] ? v[m][u] : best[m];
-                }
-            }
+            for (int m = 0; m < kMaxWindowLevels; ++m) key[m] = m < LV ? wmax[(size_t)m * nbh + bh] : 0;
             int lev = 0;
 #pragma unroll
-            for (int m = kMaxWindowLevels; m >= 1; --m) {
-                float x = best[m - 1];
-                for (int d = tph >> 1; d > 0; d >>= 1) {
-                    const float o = __shfl_xor(x, d, 64);
-                    x = o > x ? o : x;
-                }
-                if (m <= LV && N >= m * w && x <= prm.log_eps) lev = m;
-                if (m == 1 && bh < nbh && k == 0 && prm.maxwin) prm.maxwin[bh] = x;
-            }
-            if (bh < nbh && k == 0) levp[bh] = lev;
+            for (int m = kMaxWindowLevels; m >= 1; --m)
+                if (m <= LV && N >= m * w && key_float(key[m - 1]) <= prm.log_eps) lev = m;
+            if (prm.maxwin) prm.maxwin[bh] = key_float(key[0]);
+            levp[bh] = lev;
         }
         __syncthreads();
     }
@@ -1006,7 +982,7 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
     const int per = (nbh + kThreads - 1) / kThreads;
     const int lo = tid * per < nbh ? tid * per : nbh;
     const int hi = lo + per < nbh ? lo + per : nbh;
-    auto level_of = [&](int bh) { return wpart ? levp[bh] : 0; };
+    auto level_of = [&](int bh) { return wmax ? levp[bh] : 0; };
     for (int m = 0; m <= LV; ++m) {
         int cnt = 0;
         for (int bh = lo; bh < hi; ++bh) cnt += level_of(bh) == m ? 1 : 0;
@@ -1018,29 +994,52 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
     WinLevels base;
     base.init(LV, N, w, pmax);
     if (wv == 0) {
-        // candidates (P, Lc), one per lane and round, ordered by P, then by
-        // decreasing Lc; the cheapest wins, ties go to the earlier candidate
+        // candidates (P, Lc): the distinct cutoffs Lc (Lc differs from Lc + 1
+        // only when level Lc + 1 has heads), from LV down, and for each the
+        // exact segment counts P that fit (P = 1 alone when no head is exact),
+        // one per lane and round; the cheapest wins, ties go to the earlier one
         int Pe = pmax, Lc = LV;
         if (!prm.forced) {
+            int cnt_lc[kMaxWindowLevels + 1], ne_lc[kMaxWindowLevels + 1];
+            int ncand = 0;
+#pragma unroll
+            for (int lc = kMaxWindowLevels; lc >= 0; --lc) {
+                int ne = pl.cls[0];
+#pragma unroll
+                for (int m = 1; m <= kMaxWindowLevels; ++m) ne += (m > lc && m <= LV) ? pl.cls[m] : 0;
+                ne_lc[lc] = ne;
+                const bool distinct = lc <= LV && (lc == LV || pl.cls[lc + 1] > 0);
+                int pok = ne > 0 ? 1 + prm.cus / ne : 1;   // largest P with ne (P - 1) <= cus
+                pok = pok < pmax ? pok : pmax;
+                cnt_lc[lc] = !distinct ? 0 : (ne == 0 ? 1 : 1 + (pok >= 3 ? pok - 2 : 0));
+                ncand += cnt_lc[lc];
+            }
             float best = 3.0e38f;
-            int bi = 0;
-            const int ncand = pmax * (LV + 1);
             for (int i0 = 0; i0 < ncand; i0 += 64) {
                 int i = i0 + lane;
-                const int P = 1 + i / (LV + 1), lc = LV - i % (LV + 1);
+                // candidate i -> (lc, P)
+                int lc = 0, P = 1, rem = i;
+                bool found = false;
+#pragma unroll
+                for (int l = kMaxWindowLevels; l >= 0; --l) {
+                    if (!found && rem < cnt_lc[l]) {
+                        lc = l;
+                        P = rem == 0 ? 1 : rem + 2;
+                        found = true;
+                    } else if (!found) {
+                        rem -= cnt_lc[l];
+                    }
+                }
                 WinLevels wl = base;
                 wl.levels = lc;
-                int n_e = pl.cls[0];
+                int n_e = 0;
 #pragma unroll
-                for (int m = 1; m <= kMaxWindowLevels; ++m) {
-                    const int c = m <= LV ? pl.cls[m] : 0;
-                    wl.n[m - 1] = m <= lc ? c : 0;
-                    n_e += m > lc ? c : 0;
-                }
+                for (int l = 0; l <= kMaxWindowLevels; ++l) n_e = l == lc ? ne_lc[l] : n_e;
+#pragma unroll
+                for (int m = 1; m <= kMaxWindowLevels; ++m) wl.n[m - 1] = (m <= lc && m <= LV) ? pl.cls[m] : 0;
                 float t = 3.0e38f;
-                const bool ok = i < ncand && (n_e > 0 || P == 1) && P != 2 && (P == 1 || n_e * (P - 1) <= prm.cus);
                 int pm[kMaxWindowLevels];
-                if (ok) t = plan_cost(P, n_e, wl, prm.cus, pm);
+                if (found && i < ncand) t = plan_cost(P, n_e, wl, prm.cus, pm);
                 const int mine = i;
 #pragma unroll
                 for (int d = 1; d < 64; d <<= 1) {
@@ -1053,25 +1052,22 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
                 }
                 if (t < best * 0.999f) {
                     best = t;
-                    bi = i;
-                    // the winning lane keeps its window segment counts
+                    // the winning lane records its choice and its window segment counts
                     if (mine == i) {
+                        pl.par[0] = P;
+                        pl.par[1] = lc;
 #pragma unroll
                         for (int m = 0; m < kMaxWindowLevels; ++m) pl.par[2 + m] = pm[m];
                     }
                 }
             }
-            Pe = 1 + bi / (LV + 1);
-            Lc = LV - bi % (LV + 1);
         } else {
             if (lane == 0) {
+                pl.par[0] = Pe;
+                pl.par[1] = Lc;
 #pragma unroll
                 for (int m = 0; m < kMaxWindowLevels; ++m) pl.par[2 + m] = pmax;
             }
-        }
-        if (lane == 0) {
-            pl.par[0] = Pe;
-            pl.par[1] = Lc;
         }
     }
     __syncthreads();
@@ -1091,7 +1087,7 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
         if (tid == 0) pl.cls[ci] = tot;   // heads per class from here on
     }
     // the levels that ran, for the record (0 = exact)
-    if (wpart)
+    if (wmax)
         for (int bh = lo; bh < hi; ++bh) {
             const int m = levp[bh];
             flags[bh] = m > Lc ? 0 : m;

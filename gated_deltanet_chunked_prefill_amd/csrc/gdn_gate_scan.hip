@@ -70,10 +70,12 @@ __global__ __launch_bounds__(256) void chunk_sums_kernel(const float* __restrict
 // arrangement and summation order of chunk_sums_kernel.
 __global__ __launch_bounds__(256) void fwd_sums_kernel(const float* __restrict__ g, int T, int H, int N,
                                                        float* __restrict__ sums, int* __restrict__ zero,
-                                                       int nzero, int* __restrict__ plan_words) {
+                                                       int nzero, int* __restrict__ plan_words,
+                                                       int* __restrict__ wmax, int nwmax) {
     const int tid = threadIdx.x;
     const int wg = blockIdx.y * gridDim.x + blockIdx.x, nwg = gridDim.x * gridDim.y;
     for (int i = wg * 256 + tid; i < nzero; i += nwg * 256) zero[i] = 0;
+    for (int i = wg * 256 + tid; i < nwmax; i += nwg * 256) wmax[i] = float_key(-INFINITY);
     if (wg == 0 && tid < 16) plan_words[tid] = 0;   // the planner's words (at most 16)
     if (sums) chunk_sums_wg(g, T, H, N, blockIdx.x, blockIdx.y, sums);
 }
@@ -83,16 +85,15 @@ __global__ __launch_bounds__(256) void fwd_sums_kernel(const float* __restrict__
 // (grp, b) stages the chunk sums of its chunks and of the levels*w - 1 chunks
 // before them, then per head and length takes the largest window sum
 // s_{c-W+1} + ... + s_c (summed in that order) over the windows ending in the
-// group: part[(((m-1)*B + b)*NG + grp)*H + h], -inf when no window ends there.
-// The planner takes the maximum over the groups.  At m = 1 the sums are those
-// of window_flags_kernel, term for term.
+// group, folded into wmax[(m-1)*B*H + b*H + h] with an atomic maximum of
+// order-preserving integer keys (the first launch set every entry to -inf).  At
+// m = 1 the sums are those of window_flags_kernel, term for term.
 constexpr int kWinGroup = 8;
 constexpr int kWinMaxSums = 8192;   // LDS floats for the group's chunk sums
 __global__ __launch_bounds__(256) void fwd_window_kernel(const float* __restrict__ sums, int H, int N, int w,
-                                                         int levels, float* __restrict__ part) {
+                                                         int levels, int* __restrict__ wmax) {
     __shared__ float s_sum[kWinMaxSums];
     const int grp = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int NG = gridDim.x;
     const int c0 = grp * kWinGroup;
     const int c1 = c0 + kWinGroup < N ? c0 + kWinGroup : N;
     const int wl = levels * w;                          // longest window
@@ -122,7 +123,8 @@ __global__ __launch_bounds__(256) void fwd_window_kernel(const float* __restrict
                 const float o = __shfl_xor(acc, d, 64);
                 acc = o > acc ? o : acc;
             }
-            if (x < ntask && e == 0) part[(((size_t)(m - 1) * gridDim.y + b) * NG + grp) * H + h0 + hl] = acc;
+            if (x < ntask && e == 0 && acc > -INFINITY)
+                atomicMax(&wmax[((size_t)(m - 1) * gridDim.y + b) * H + h0 + hl], float_key(acc));
         }
         __syncthreads();
     }
@@ -169,17 +171,18 @@ int window_groups(int T) { return ((T + kChunk - 1) / kChunk + kWinGroup - 1) / 
 int max_window_chunks() { return kWinMaxSums - kWinGroup + 1; }
 
 hipError_t launch_fwd_sums(const float* g, int B, int T, int H, float* sums, int* zero, int nzero,
-                           int* plan_words, hipStream_t s) {
+                           int* plan_words, int* wmax, int nwmax, hipStream_t s) {
     const int N = (T + kChunk - 1) / kChunk;
     dim3 grid(sums ? N : 1, sums ? B : 1);
-    hipLaunchKernelGGL(fwd_sums_kernel, grid, dim3(256), 0, s, g, T, H, N, sums, zero, nzero, plan_words);
+    hipLaunchKernelGGL(fwd_sums_kernel, grid, dim3(256), 0, s, g, T, H, N, sums, zero, nzero, plan_words, wmax,
+                       nwmax);
     return hipGetLastError();
 }
-hipError_t launch_fwd_windows(const float* sums, int B, int T, int H, int w, int levels, float* part,
+hipError_t launch_fwd_windows(const float* sums, int B, int T, int H, int w, int levels, int* wmax,
                               hipStream_t s) {
     const int N = (T + kChunk - 1) / kChunk;
     dim3 grid(window_groups(T), B);
-    hipLaunchKernelGGL(fwd_window_kernel, grid, dim3(256), 0, s, sums, H, N, w, levels, part);
+    hipLaunchKernelGGL(fwd_window_kernel, grid, dim3(256), 0, s, sums, H, N, w, levels, wmax);
     return hipGetLastError();
 }
 hipError_t launch_window_flags(const float* chunk_sums, int B, int T, int H, int w, float log_eps,

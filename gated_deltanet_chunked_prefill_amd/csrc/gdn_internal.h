@@ -9,8 +9,8 @@ namespace gdn {
 // Workspace of the split forward, per head bh = b*H + h and segment slot p < P
 // (P = the largest segment count the call may use; 256-byte aligned sub-buffers):
 //   csum       [B, N, H]          sums of g per chunk (gate scan)
-//   wpart      [LV, B, NG, H]     window maxima per group of chunks (gate scan), per
-//                                 window length level (LV = kMaxWindowLevels slots)
+//   wmax       [LV, B*H] int32    largest window sum per window length level and head,
+//                                 as order-preserving integer keys (LV = kMaxWindowLevels slots)
 //   flags      [B*H] int32        0 = exact head, m >= 1 = window head of m*w chunks
 //   maxwin     [B*H]              max window log-decay
 //   hs         [B*H, P, dk, dv]   true state entering segment p (p >= 1) of an exact head
@@ -57,9 +57,9 @@ struct FwdParams {
     int w;             // window length in chunks (level 1)
     int levels;        // window lengths tried: w, 2w, ..., levels * w (0 with no window heads)
     float scale;
-    const float* wpart;    // split forward with window heads: window maxima per level and group
-                           // of chunks (null: all heads exact)
-    int n_groups;          // groups of chunks in wpart
+    const int* wmax;       // split forward with window heads: largest window sum per window
+                           // length and head [levels, B*H], as order-preserving integer keys
+                           // (null: all heads exact)
     int* head_map;         // [2*B*H] planner scratch: heads by exact rank, then by window rank
     int32_t* flags;        // written by the planner: 0 = exact head, m = window head of m*w chunks
     float* maxwin;         // the largest window sum at length w
@@ -89,9 +89,18 @@ hipError_t launch_chunk_sums(const float* g, int B, int T, int H, float* chunk_s
 int window_groups(int T);
 int max_window_chunks();
 hipError_t launch_fwd_sums(const float* g, int B, int T, int H, float* sums, int* zero, int nzero,
-                           int* plan_words, hipStream_t s);
-hipError_t launch_fwd_windows(const float* sums, int B, int T, int H, int w, int levels, float* part,
+                           int* plan_words, int* wmax, int nwmax, hipStream_t s);
+hipError_t launch_fwd_windows(const float* sums, int B, int T, int H, int w, int levels, int* wmax,
                               hipStream_t s);
+// Order-preserving integer key of a float (signed comparison of keys = comparison
+// of the floats), and back.
+__host__ __device__ inline int float_key(float x) {
+    const int b = __builtin_bit_cast(int, x);
+    return b >= 0 ? b : b ^ 0x7FFFFFFF;
+}
+__host__ __device__ inline float key_float(int k) {
+    return __builtin_bit_cast(float, k >= 0 ? k : k ^ 0x7FFFFFFF);
+}
 hipError_t launch_window_flags(const float* chunk_sums, int B, int T, int H, int w, float log_eps,
                                int32_t* flags, float* maxwin, hipStream_t s);
 
