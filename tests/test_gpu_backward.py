@@ -82,6 +82,25 @@ def test_bwd_strong_decay(gdn):
     _check(got, ref, "strong decay")
 
 
+@pytest.mark.parametrize("case", ["no_decay", "beta0", "beta1"])
+def test_bwd_degenerate_gates(gdn, case):
+    """alpha = 1 (g = 0), beta = 0 (then dk = dv = 0 exactly: keys and values never
+    reach the state) and beta = 1, against the BPTT oracle."""
+    say(f"case bwd degenerate gates {case}")
+    x = inputs.generate(B=1, T=64 * 3 + 17, H=2, h0_std=0.05, dout=True, seed=33)
+    if case == "no_decay":
+        x.g[...] = 0.0
+    elif case == "beta0":
+        x.beta[...] = 0.0
+    else:
+        x.beta[...] = 1.0
+    got, ref = _bwd(gdn, x)
+    if case == "beta0":
+        assert np.max(np.abs(ref["dk"])) == 0.0 and np.max(np.abs(ref["dv"])) == 0.0
+        assert np.max(np.abs(got["dk"])) < 1e-6 and np.max(np.abs(got["dv"])) < 1e-6
+    _check(got, ref, case)
+
+
 @pytest.mark.slow
 def test_bwd_train_workload_sampled_heads(gdn):
     """The training shape (B=4, T=8192, H=32) at full size; the oracle runs on a

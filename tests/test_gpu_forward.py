@@ -115,6 +115,36 @@ def test_split_mixed_heads_window(gdn):
            label="mixed P=10 w=2")
 
 
+@pytest.mark.parametrize("case", ["no_decay", "beta0", "beta1"])
+@pytest.mark.parametrize("split", [1, 0, 2])
+def test_degenerate_gates(gdn, case, split):
+    """Degenerate gates of the recurrence, against the oracle: alpha = 1 (g = 0,
+    no decay: no head may take the window shortcut, the split must be exact),
+    beta = 0 (the state only decays, o = scale decayed h0^T q) and beta = 1 (each
+    token overwrites the value stored at its key), unsplit (1), automatic (0) and
+    forced into 5 segments (2)."""
+    import torch
+    say(f"case degenerate gates {case} split_mode={split}")
+    B, T, H = 1, 64 * 12 + 9, 3
+    x = inputs.generate(B=B, T=T, H=H, h0_std=0.05, seed=31)
+    if case == "no_decay":
+        x.g[...] = 0.0
+    elif case == "beta0":
+        x.beta[...] = 0.0
+    else:
+        x.beta[...] = 1.0
+    opts = dict(split_mode=split, n_segments=5) if split == 2 else dict(split_mode=split)
+    t = to_gpu(x)
+    ws = torch.empty(max(1, gdn.gdn_chunk_fwd_workspace_size(B, T, H, **opts)), dtype=torch.uint8, device="cuda")
+    o, ht = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], workspace=ws, **opts)
+    torch.cuda.synchronize()
+    if split == 2 and case == "no_decay":
+        info = gdn.gdn_chunk_fwd_plan_info(B, T, H, workspace=ws, **opts)
+        assert info["error"] == 0 and info["n_window"] == 0 and info["n_exact"] == B * H, info
+    oref, href = oracle.fwd(x.q, x.k, x.v, x.g, x.beta, x.h0)
+    _check(to_np(o), to_np(ht), oref, href, TOL_BF16, label=f"{case} split={split}")
+
+
 def test_strong_decay_pairwise_fallback(gdn):
     """Chunks whose total decay exceeds the factored-exponential range use
     pairwise exponentials; results stay finite and correct."""
