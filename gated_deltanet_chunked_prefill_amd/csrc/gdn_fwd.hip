@@ -940,6 +940,7 @@ struct PlanLds {
     int cls[1 + kMaxWindowLevels];   // heads per class: exact, then window levels L .. 1
     int lev[kPlanHeads];             // window level per head (0 = exact)
     int hmap[kPlanHeads];            // heads by class
+    int kb[kMaxWindowLevels];        // heads of a level given one segment more (the first ones)
 };
 
 // The planner, run by the first workgroup of the persistent launch to arrive,
@@ -1100,18 +1101,50 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
 #pragma unroll
     for (int m = 1; m <= kMaxWindowLevels; ++m) wl.n[m - 1] = m <= Lc ? pl.cls[1 + Lc - m] : 0;
     if (tid == 0) {
+        // Workgroups the window heads leave free go, one segment more per head,
+        // to the heads of the levels whose jobs cost most: the makespan estimate
+        // stays, but far fewer jobs run at it (job times vary from workgroup to
+        // workgroup, so the slowest of many such jobs sets the end of the launch).
+        const int Pe0 = pl.par[0];
+        int spare = 0;
+        if (!prm.forced) {
+            spare = prm.cus - (n_e == 0 ? 0 : n_e * (Pe0 == 1 ? 1 : Pe0 - 1));
+            for (int m = 1; m <= Lc; ++m) spare -= pl.cls[1 + Lc - m] * pl.par[1 + m];
+        }
+        for (int m = 0; m < kMaxWindowLevels; ++m) pl.kb[m] = 0;
+        for (int pass = 0; pass < Lc && spare > 0; ++pass) {
+            int bm = 0;
+            float bc = -1.f;
+            for (int m = 1; m <= Lc; ++m) {
+                const int nm = pl.cls[1 + Lc - m];
+                const int P = pl.par[1 + m];
+                int cap = N / (m * w);
+                cap = cap < 1 ? 1 : cap;
+                cap = cap < pmax ? cap : pmax;
+                if (nm == 0 || pl.kb[m - 1] != 0 || P + 1 > cap) continue;
+                const float f = ((float)N + (P - 1) * (kCostWarm * m * w)) / P;
+                if (f > bc) {
+                    bc = f;
+                    bm = m;
+                }
+            }
+            if (bm == 0) break;
+            const int nm = pl.cls[1 + Lc - bm];
+            const int k = nm < spare ? nm : spare;
+            pl.kb[bm - 1] = k;
+            spare -= k;
+        }
         int pw_max = 1;
-#pragma unroll
-        for (int m = 0; m < kMaxWindowLevels; ++m) {
-            const int pm = pl.par[2 + m];
-            if (m < Lc && wl.n[m] > 0 && pm > pw_max) pw_max = pm;
+        for (int m = 1; m <= Lc; ++m) {
+            const int pm = pl.par[1 + m] + (pl.kb[m - 1] > 0 ? 1 : 0);
+            if (pl.cls[1 + Lc - m] > 0 && pm > pw_max) pw_max = pm;
         }
         pl.par[1] = pw_max;
     }
     __syncthreads();
     const int Pe = pl.par[0];
     int n_win_jobs = 0;
-    for (int m = 1; m <= Lc; ++m) n_win_jobs += pl.cls[1 + Lc - m] * pl.par[1 + m];
+    for (int m = 1; m <= Lc; ++m) n_win_jobs += pl.cls[1 + Lc - m] * pl.par[1 + m] + pl.kb[m - 1];
     const int g_win = n_e + (Pe >= 3 ? n_e * (Pe - 2) : 0);
     const int g_chain = g_win + n_win_jobs;
     const int g_p3 = g_chain + (Pe >= 3 ? 4 * n_e : 0);
@@ -1149,13 +1182,23 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
             int jw = j - g_win, hbase = n_e, m = Lc;
             for (; m > 1; --m) {
                 const int nm = pl.cls[1 + Lc - m];   // heads of level m
-                const int nj = nm * pl.par[1 + m];
+                const int nj = nm * pl.par[1 + m] + pl.kb[m - 1];
                 if (jw < nj) break;
                 jw -= nj;
                 hbase += nm;
             }
-            const int P = pl.par[1 + m], W = m * w;
-            const int r = jw / P, p = jw % P;
+            // the first kb heads of the level have one segment more
+            const int Pm = pl.par[1 + m], kb = pl.kb[m - 1], W = m * w;
+            int P, r, p;
+            if (jw < kb * (Pm + 1)) {
+                P = Pm + 1;
+                r = jw / P;
+                p = jw % P;
+            } else {
+                P = Pm;
+                r = kb + (jw - kb * (Pm + 1)) / Pm;
+                p = (jw - kb * (Pm + 1)) % Pm;
+            }
             const float c = kCostWarm * W;
             const int sb = win_bound(p, P, N, c, prm.forced != 0), e = win_bound(p + 1, P, N, c, prm.forced != 0);
             const int cb = sb - W > 0 ? sb - W : 0;
