@@ -310,21 +310,29 @@ __device__ __forceinline__ void st_tile64(T* tile, const f32x16& v, int ti, int 
     for (int r = 0; r < 16; ++r) tile[toff<T, 64>(32 * ti + rho(g, r), 32 * tj + n)] = (T)v[r];
 }
 
-// Store accumulator tile rt of a 64 x 128 result (this wave's 32 columns) to HBM rows.
-template <typename T>
-__device__ __forceinline__ void st_rows_hbm(T* dst, const f32x16& v, int rt, int g, int n, int w, int H,
-                                           int nvalid) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = 32 * rt + rho(g, r);
-        if (row < nvalid) dst[(size_t)row * H * kDk + 32 * w + n] = (T)v[r];
-    }
-}
-// ... and into a swizzled 64 x 128 LDS tile.
+// Store accumulator tile rt of a 64 x 128 result (this wave's 32 columns) into a
+// swizzled 64 x 128 LDS tile.
 template <typename T>
 __device__ __forceinline__ void st_rows_lds(T* tile, const f32x16& v, int rt, int g, int n, int w) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) tile[toff<T, kDv>(32 * rt + rho(g, r), 32 * w + n)] = (T)v[r];
+}
+
+// Copy the first nv rows of a swizzled 64 x 128 LDS tile to the rows of a
+// [.., T, H, 128] tensor (dst = the chunk's first row of this head), as
+// 16-byte row pieces: 1024 pieces over the workgroup's threads.
+template <typename T>
+__device__ __forceinline__ void copy_tile_rows(T* dst, const T* tile, int H, int nv, int tid) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(1))) u4 gu4;
+#pragma unroll
+    for (int i = tid; i < kChunk * 16; i += kLocalThreads) {
+        const int row = i >> 4, ch = i & 15;
+        if (row < nv) {
+            const u4 x = *reinterpret_cast<const u4*>(tile + toff<T, kDv>(row, 8 * ch));
+            *(gu4*)(dst + (size_t)row * H * kDv + 8 * ch) = x;
+        }
+    }
 }
 
 template <typename T>
@@ -503,22 +511,22 @@ __global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_kernel(BwdPara
         for (int ks = 0; ks < 2; ++ks) dZ[0] = mma(tfrag<T, 64>(sm.tg, 0, ks, lane), acc_frag<T>(t0v, ks), dZ[0]);
         dY[0] = dZ[0] * be0;
     }
-    // dbeta partial over this wave's columns; V' and dY to LDS; dv to HBM
+    // dbeta partial over this wave's columns; V' and dY to LDS (dv = dY goes to
+    // HBM from there, as row pieces)
     {
         const f32x16 r0 = dZ[0] * (Y[0] - MgV0), r1 = dZ[1] * (Y[1] - MgV1);
         row_sums(sm.part[w][0], r0, 0, g, n);
         row_sums(sm.part[w][0], r1, 1, g, n);
-        T* dvout = (T*)prm.dv + (((size_t)b * Tn + t0) * H + h) * kDv;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             st_rows_lds<T>(sm.vt, Vp[rt], rt, g, n, w);
             st_rows_lds<T>(sm.dyt, dY[rt], rt, g, n, w);
-            st_rows_hbm<T>(dvout, dY[rt], rt, g, n, w, H, nv);
         }
     }
     lds_barrier();
 
     // ---- phase 3: 64 x 64 gradient tiles
+    copy_tile_rows<T>((T*)prm.dv + (((size_t)b * Tn + t0) * H + h) * kDv, sm.dyt, H, nv, tid);
     {
         f32x16 dPm = zero16(), dMg = zero16();
         if (ti >= tj) {
@@ -595,13 +603,16 @@ __global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_kernel(BwdPara
             row_sums(sm.part[w][2], pk3, rt, g, n);
             row_sums(sm.part[w][3], pk4, rt, g, n);
         }
-        T* dqout = (T*)prm.dq + (((size_t)b * Tn + t0) * H + h) * kDk;
-        T* dkout = (T*)prm.dk + (((size_t)b * Tn + t0) * H + h) * kDk;
+        // dq and dk through the Q and K tiles (no longer read): row pieces to HBM
+        lds_barrier();
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            st_rows_hbm<T>(dqout, dq[rt], rt, g, n, w, H, nv);
-            st_rows_hbm<T>(dkout, dk[rt], rt, g, n, w, H, nv);
+            st_rows_lds<T>(sm.qt, dq[rt], rt, g, n, w);
+            st_rows_lds<T>(sm.kt, dk[rt], rt, g, n, w);
         }
+        lds_barrier();
+        copy_tile_rows<T>((T*)prm.dq + (((size_t)b * Tn + t0) * H + h) * kDk, sm.qt, H, nv, tid);
+        copy_tile_rows<T>((T*)prm.dk + (((size_t)b * Tn + t0) * H + h) * kDk, sm.kt, H, nv, tid);
     }
     // ---- phase 5: <dHn, Hn> for the gradient of gamma_C, this wave's part
     {
