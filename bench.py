@@ -10,7 +10,9 @@ Prints one JSON line with tokens/s, the roofline of the fused forward kernel
 (algorithmic bytes over its HIP-event-timed launch durations, against the
 8 TB/s HBM peak) and the fp64 CPU oracle timed on the host as a reference.
 A secondary "backward" object times whole gdn_chunk_bwd calls on the training
-shape (B=4, T=8192, H=32, bf16) with per-launch event times.
+shape (B=4, T=8192, H=32, bf16) with per-launch event times, and a "varlen"
+object whole gdn_chunk_fwd_varlen calls on a packed batch of 8 prompts of
+mixed lengths (32768 tokens, H=32).
 """
 from __future__ import annotations
 
@@ -113,7 +115,10 @@ def traffic_summary(fetch_csv, write_csv, calib_mib):
 
     def per_call(d, factor):
         # each forward launch kind runs once per call: sum of the per-kind means
-        kinds = {name: float(np.mean(vs)) for name, vs in d.items() if FWD_KERNEL in name}
+        # (the backward's state store and the packed-sequence forward are other
+        # instantiations of gdn_fwd_kernel: PHASE_STATES = 2, PHASE_VARLEN = 3)
+        kinds = {name: float(np.mean(vs)) for name, vs in d.items()
+                 if FWD_KERNEL in name and "Li2E" not in name and "Li3E" not in name}
         return sum(kinds.values()) * 1024.0 * factor, kinds
 
     ff, wf = calib(fetch), calib(write)
@@ -189,6 +194,43 @@ def bench_backward(torch, gdn, _lib, inputs, steps, warmup):
             "kernel_ms": {kd: round(float(np.mean(t)), 4) for kd, t in per_kind.items()}}
 
 
+# packed variable-length batch (serving shape): 8 prompts of mixed lengths, 32768
+# tokens in all, H = 32, bf16, no initial state, final states returned
+VARLEN_WORKLOAD = "bf16_varlen_8seq_t32768_h32"
+VARLEN_LENGTHS = (8192, 6000, 5000, 4096, 3500, 2800, 2000, 1180)
+
+
+def bench_varlen(torch, gdn, inputs, steps, warmup):
+    """Whole gdn_chunk_fwd_varlen calls on the packed batch above."""
+    lens = np.array(VARLEN_LENGTHS, np.int64)
+    T, H, S = int(lens.sum()), 32, len(lens)
+    x = inputs.generate(B=1, T=T, H=H, seed=5)
+    dev = torch.device("cuda:0")
+    bf = lambda a: torch.from_numpy(a[0]).to(dev).to(torch.bfloat16)
+    q, k, v = bf(x.q), bf(x.k), bf(x.v)
+    g = torch.from_numpy(x.g[0]).to(dev)
+    beta = torch.from_numpy(x.beta[0]).to(dev)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+    o = torch.empty_like(v)
+    ht = torch.empty((S, H, 128, 128), dtype=torch.float32, device=dev)
+
+    def step():
+        gdn.gdn_chunk_fwd_varlen(q, k, v, g, beta, cu, out=o, out_ht=ht)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    nbytes = algorithmic_bytes(1, T, H, False, False) + S * H * STATE_BYTES
+    return {"workload": VARLEN_WORKLOAD, "lengths": list(VARLEN_LENGTHS), "H": H, "steps": steps,
+            "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nbytes,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def cpu_baseline(x, tokens):
     """The fp64 oracle, as it stands, on the first `tokens` tokens of every head."""
     import oracle
@@ -213,6 +255,8 @@ def main():
                     help="tokens per head of the CPU oracle sample (0 to skip)")
     ap.add_argument("--bwd-steps", type=int, default=5,
                     help="timed backward calls on the training shape (0 to skip)")
+    ap.add_argument("--varlen-steps", type=int, default=5,
+                    help="timed packed variable-length calls (0 to skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, stream-copy this many MiB three times "
                          "(the calibration kernel of the HBM counter runs)")
@@ -309,10 +353,13 @@ def main():
                      "traffic_gbs": None if tr is None else traffic / (fwd_ms * 1e-3) / 1e9, "kernel_ms": kernel_ms,
                      "call_frac": nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
     }
-    if args.bwd_steps > 0:
+    if args.bwd_steps > 0 or args.varlen_steps > 0:
         del q, k, v, g, beta, o, ht, ws
         torch.cuda.empty_cache()
+    if args.bwd_steps > 0:
         res["backward"] = bench_backward(torch, gdn, _lib, inputs, args.bwd_steps, 2)
+    if args.varlen_steps > 0:
+        res["varlen"] = bench_varlen(torch, gdn, inputs, args.varlen_steps, 2)
     if args.calib_copy_mib > 0:
         src = torch.randn(args.calib_copy_mib * 2 ** 18, device=dev)
         dst = torch.empty_like(src)

@@ -7,6 +7,7 @@ current HIP stream to the library.  Every step of the computation runs in the
 library's HIP kernels; there is no fallback path.
 
     gdn_chunk_fwd(q, k, v, g, beta, h0=None, scale=1.0, ...) -> (o, ht)
+    gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None, ...) -> (o, ht)
     gdn_chunk_bwd(q, k, v, g, beta, dout, h0=None, dht=None, scale=1.0) -> dict
     gdn_gate_scan(g, window_chunks=8, log_eps=log(2^-24)) -> (flags, max_window_logdecay)
 
@@ -22,7 +23,8 @@ from . import _lib
 
 DEFAULT_LOG_EPS = math.log(2.0 ** -24)
 
-__all__ = ["gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_gate_scan", "gdn_plan_segments", "gdn_chunk_fwd_plan_info",
+__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_varlen", "gdn_chunk_bwd", "gdn_gate_scan", "gdn_plan_segments",
+           "gdn_chunk_fwd_plan_info",
            "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd_workspace_size", "options"]
 
 
@@ -133,6 +135,38 @@ def gdn_chunk_fwd(q, k, v, g, beta, h0=None, scale=1.0, *, output_final_state=Tr
     _lib.check(lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
                                  _ptr(o), _ptr(ht), B, T, H, dk, dv, code, float(scale),
                                  ctypes.byref(opt), _ptr(workspace), wsz, _stream(q.device)))
+    return o, ht
+
+
+def gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None, scale=1.0, *,
+                         output_final_state=True, out=None, out_ht=None):
+    """Fused forward over packed variable-length sequences.  q, k, v: [T, H, d]
+    (or [1, T, H, d]) in bf16 or float32, g, beta: [T, H] (or [1, T, H]) float32,
+    cu_seqlens: int32 [S + 1] on the same device (token offsets of the S
+    sequences), h0: [S, H, dk, dv] float32 or None.  Returns (o, ht) with o
+    shaped like v and ht [S, H, dk, dv] (None when not requested)."""
+    torch = _torch()
+    lib = _lib.load()
+    _dev(q, "q")
+    dt = q.dtype
+    _dev(k, "k", dt), _dev(v, "v", dt)
+    _dev(g, "g", torch.float32), _dev(beta, "beta", torch.float32)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    _dev(h0, "h0", torch.float32)
+    T, H, dk = q.shape[-3], q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    S = cu_seqlens.numel() - 1
+    if S < 1:
+        raise ValueError("cu_seqlens needs at least two entries")
+    o = out if out is not None else torch.empty_like(v)
+    _dev(o, "o", dt)
+    if out_ht is not None:
+        ht = _dev(out_ht, "out_ht", torch.float32)
+    else:
+        ht = torch.empty((S, H, dk, dv), dtype=torch.float32, device=q.device) if output_final_state else None
+    _lib.check(lib.gdn_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                                        _ptr(o), _ptr(ht), _ptr(cu_seqlens), S, T, H, dk, dv,
+                                        _dtype_code(q), float(scale), _stream(q.device)))
     return o, ht
 
 

@@ -337,6 +337,37 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
     return GDN_OK;
 }
 
+gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, const float* h0, void* o, float* ht,
+                                const int32_t* cu_seqlens, int n_seqs, int T, int H, int dk, int dv,
+                                gdn_dtype dtype, float scale, void* stream) {
+    g_err[0] = 0;
+    if (!q || !k || !v || !g || !beta || !o || !cu_seqlens)
+        return fail(GDN_ERR_INVALID_ARG, "q, k, v, g, beta, o and cu_seqlens are required");
+    if (n_seqs <= 0) return fail(GDN_ERR_INVALID_ARG, "n_seqs must be positive (got %d)", n_seqs);
+    gdn_status st = check_shapes(1, T, H, dk, dv, dtype);
+    if (st != GDN_OK) return st;
+    if ((long long)n_seqs * H > (1LL << 30)) return fail(GDN_ERR_INVALID_ARG, "too many sequences");
+    const void* vec_ptrs[] = {q, k, v, o};
+    for (const void* p : vec_ptrs)
+        if (!aligned16(p)) return fail(GDN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+    const void* i32_ptrs[] = {g, beta, h0, ht, cu_seqlens};
+    for (const void* p : i32_ptrs)
+        if (p && !aligned4(p))
+            return fail(GDN_ERR_INVALID_ARG, "g, beta, h0, ht and cu_seqlens must be 4-byte aligned");
+    if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite");
+    hipStream_t s = (hipStream_t)stream;
+    gdn::FwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.o = o; p.ht = ht;
+    p.B = n_seqs; p.T = T; p.H = H; p.N = num_chunks(T); p.P = 1; p.w = 1; p.scale = scale;
+    p.cu = cu_seqlens;
+    const hipError_t e = recorded(GDN_LAUNCH_FWD_SINGLE, s, [&] {
+        return gdn::launch_fwd(p, gdn::PHASE_VARLEN, dtype == GDN_BF16, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+    return GDN_OK;
+}
+
 gdn_status gdn_chunk_fwd_plan_info(int B, int T, int H, const gdn_options* opt, const void* workspace,
                                    int32_t* info, void* stream) {
     g_err[0] = 0;

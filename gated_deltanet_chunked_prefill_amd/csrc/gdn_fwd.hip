@@ -685,11 +685,35 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_kernel(FwdParams prm) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     Smem<T>& sm = *reinterpret_cast<Smem<T>*>(smem_raw);
     Task tk;
-    whole_head_task(prm, tk);
-    if (PHASE == PHASE_STATES)
-        run_task<T, MODE_FULL, true>(prm, sm, tk);
-    else
-        run_task<T, MODE_FULL>(prm, sm, tk);
+    if constexpr (PHASE == PHASE_VARLEN) {
+        // Packed sequences: sequence s = blockIdx / H holds tokens [t0, t1).  The
+        // task runs as sequence s of a batch of sequences of length len, with
+        // every token pointer shifted by t0 - s*len, so that the loops' token
+        // index s*len + t addresses token t0 + t.
+        const int s = (int)blockIdx.x / prm.H;
+        int t0 = uni(prm.cu[s]), t1 = uni(prm.cu[s + 1]);
+        t0 = t0 < 0 ? 0 : (t0 > prm.T ? prm.T : t0);
+        t1 = t1 < t0 ? t0 : (t1 > prm.T ? prm.T : t1);
+        const int len = t1 - t0;
+        const long long shift = ((long long)t0 - (long long)s * len) * prm.H;   // in token-head rows
+        FwdParams p = prm;
+        p.q = (const T*)prm.q + shift * kDk;
+        p.k = (const T*)prm.k + shift * kDk;
+        p.v = (const T*)prm.v + shift * kDv;
+        p.o = (T*)prm.o + shift * kDv;
+        p.g = prm.g + shift;
+        p.beta = prm.beta + shift;
+        p.T = len;
+        p.N = (len + kChunk - 1) / kChunk;
+        whole_head_task(p, tk);
+        run_task<T, MODE_FULL>(p, sm, tk);
+    } else {
+        whole_head_task(prm, tk);
+        if (PHASE == PHASE_STATES)
+            run_task<T, MODE_FULL, true>(prm, sm, tk);
+        else
+            run_task<T, MODE_FULL>(prm, sm, tk);
+    }
 }
 
 template <typename T>
@@ -1244,6 +1268,7 @@ template <typename T>
 hipError_t launch_fwd_t(const FwdParams& p, int phase, hipStream_t s) {
     if (phase == PHASE_SINGLE) return launch_phase<T, PHASE_SINGLE>(p, s);
     if (phase == PHASE_STATES) return launch_phase<T, PHASE_STATES>(p, s);
+    if (phase == PHASE_VARLEN) return launch_phase<T, PHASE_VARLEN>(p, s);
     return launch_phase<T, PHASE_QUEUE>(p, s);
 }
 

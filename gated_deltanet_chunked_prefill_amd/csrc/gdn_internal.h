@@ -76,13 +76,16 @@ struct FwdParams {
     TaskRec* jobs;
     int cus;           // compute units of the device
     int forced;        // 1: every head uses exactly P segments of equal length
+    const int* cu;     // packed sequences (PHASE_VARLEN): token offsets [B+1] of the B
+                       // sequences in a [1, T, H, d] batch; null otherwise
 };
 
 // PHASE_SINGLE: one workgroup per head, the whole sequence.
 // PHASE_QUEUE: persistent workgroups running the jobs of the split forward.
 // PHASE_STATES: the unsplit forward that only stores the state entering every
 // chunk (into hstore), for the backward.
-enum FwdPhase { PHASE_SINGLE = 0, PHASE_QUEUE = 1, PHASE_STATES = 2 };
+// PHASE_VARLEN: one workgroup per (sequence, head) of a packed batch (cu).
+enum FwdPhase { PHASE_SINGLE = 0, PHASE_QUEUE = 1, PHASE_STATES = 2, PHASE_VARLEN = 3 };
 
 hipError_t launch_fwd(const FwdParams& p, int phase, bool bf16, hipStream_t s);
 hipError_t launch_chunk_sums(const float* g, int B, int T, int H, float* chunk_sums, hipStream_t s);

@@ -136,6 +136,29 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          const gdn_options* opt, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* Fused chunked forward over a packed batch of variable-length sequences (the
+ * chunked-prefill serving shape: several prompts of different lengths in one
+ * call; the same chunk-wise computation as gdn_chunk_fwd, talk summary
+ * paragraph 3, applied to each sequence on its own).
+ *   q, k, v, o        [T, H, dk|dv] in the I/O dtype: the sequences one after another
+ *   g, beta           [T, H] float32
+ *   cu_seqlens        DEVICE pointer, int32 [n_seqs + 1]: sequence s holds tokens
+ *                     cu_seqlens[s] .. cu_seqlens[s+1] - 1 (non-decreasing,
+ *                     cu_seqlens[0] = 0, cu_seqlens[n_seqs] = T).  The values are read
+ *                     on the device and clamped to [0, T]; an empty sequence leaves
+ *                     its final state equal to its initial state.
+ *   h0                initial states [n_seqs, H, dk, dv] float32, or NULL (zero)
+ *   ht                final states [n_seqs, H, dk, dv] float32, or NULL (not written)
+ *   scale             multiplies every output
+ * Chunks never cross a sequence boundary (each sequence's last chunk may be
+ * short).  One workgroup per (sequence, head); the intra-GPU sequence split and
+ * the window shortcut are not applied here.  No workspace.  Errors as for
+ * gdn_chunk_fwd; tokens outside every sequence are neither read nor written. */
+gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, const float* h0, void* o, float* ht,
+                                const int32_t* cu_seqlens, int n_seqs, int T, int H, int dk, int dv,
+                                gdn_dtype dtype, float scale, void* stream);
+
 /* Workspace bytes for gdn_chunk_bwd ((size_t)-1 for invalid arguments):
  * B*H*(2N+1) bfloat16 128 x 128 matrices (N = number of 64-token chunks), the
  * state entering every chunk plus the final state, and the state gradient

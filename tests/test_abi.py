@@ -121,3 +121,21 @@ def test_bwd_validation_before_launch():
     assert _bwd(lib, full, ws=A, wsz=3 * SS - 1) == _lib.GDN_ERR_WORKSPACE
     assert _bwd(lib, full, ws=A + 16, wsz=1 << 30) == _lib.GDN_ERR_INVALID_ARG
     assert _bwd(lib, [A + 2] + full[1:], ws=A, wsz=1 << 30) == _lib.GDN_ERR_INVALID_ARG
+
+
+def test_varlen_validation_before_launch():
+    """gdn_chunk_fwd_varlen rejects bad arguments before anything is launched."""
+    lib = _lib.load()
+    A = 1 << 20
+    P = lambda a: ctypes.c_void_p(a) if a else None
+
+    def call(q=A, cu=A, n_seqs=2, T=128, H=1, dk=128, dt=1):
+        return lib.gdn_chunk_fwd_varlen(P(q), P(A), P(A), P(A), P(A), None, P(A), None, P(cu), n_seqs, T, H,
+                                        dk, 128, dt, 1.0, None)
+    assert call(cu=0) == _lib.GDN_ERR_INVALID_ARG
+    assert "cu_seqlens" in _lib.last_error()
+    assert call(n_seqs=0) == _lib.GDN_ERR_INVALID_ARG
+    assert call(T=0) == _lib.GDN_ERR_INVALID_ARG
+    assert call(dk=64) == _lib.GDN_ERR_UNSUPPORTED
+    assert call(q=A + 8) == _lib.GDN_ERR_INVALID_ARG
+    assert call(cu=A + 2) == _lib.GDN_ERR_INVALID_ARG

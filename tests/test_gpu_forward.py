@@ -274,6 +274,59 @@ def test_window_levels_mixed(gdn):
     assert infos[4]["n_window"] >= infos[1]["n_window"]
 
 
+def _varlen_case(gdn, lens, H, dtype, seed, tol):
+    import torch
+    T = int(sum(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    S = len(lens)
+    x = inputs.generate(B=1, T=T, H=H, dtype=dtype, seed=seed)
+    h0 = inputs.generate(B=S, T=1, H=H, dtype=dtype, h0_std=0.05, seed=seed + 1).h0
+    t = to_gpu(x)
+    sq = lambda a: a[0]   # [1, T, ...] -> [T, ...]
+    o, ht = gdn.gdn_chunk_fwd_varlen(sq(t["q"]), sq(t["k"]), sq(t["v"]), sq(t["g"]), sq(t["beta"]),
+                                     torch.from_numpy(cu).cuda(), h0=torch.from_numpy(h0).cuda())
+    torch.cuda.synchronize()
+    o, ht = to_np(o), to_np(ht)
+    for s_ in range(S):
+        a, b = int(cu[s_]), int(cu[s_ + 1])
+        if a == b:
+            assert np.array_equal(ht[s_], h0[s_].astype(np.float64)), "empty sequence keeps its state"
+            continue
+        sl = lambda arr: arr[:, a:b]
+        oref, href = oracle.fwd(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), h0[s_:s_ + 1])
+        _check(o[None, a:b], ht[s_:s_ + 1], oref, href, tol, label=f"sequence {s_} ({b - a} tokens)")
+
+
+def test_varlen_packed_bf16(gdn):
+    """Packed sequences of ragged lengths (one empty) against the oracle run on
+    each sequence alone."""
+    say("case varlen bf16 lengths 1, 63, 64, 65, 200, 0, 130")
+    _varlen_case(gdn, [1, 63, 64, 65, 200, 0, 130], H=2, dtype="bf16", seed=41, tol=TOL_BF16)
+
+
+def test_varlen_packed_fp32(gdn):
+    say("case varlen fp32 lengths 5, 64, 70")
+    _varlen_case(gdn, [5, 64, 70], H=2, dtype="f32", seed=43, tol=TOL_F32)
+
+
+def test_varlen_equals_fixed_length(gdn):
+    """Equal-length packed sequences give bit-identical results to the unsplit
+    fixed-length forward on [B, T, H, d] (the same kernel with shifted pointers)."""
+    import torch
+    say("case varlen vs fixed length")
+    B, T, H = 3, 64 * 5 + 7, 2
+    x = inputs.generate(B=B, T=T, H=H, h0_std=0.05, seed=45)
+    t = to_gpu(x)
+    o1, h1 = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], split_mode=1)
+    fl = lambda a: a.reshape((B * T,) + tuple(a.shape[2:])).contiguous()
+    cu = torch.arange(0, B * T + 1, T, dtype=torch.int32, device="cuda")
+    o2, h2 = gdn.gdn_chunk_fwd_varlen(fl(t["q"]), fl(t["k"]), fl(t["v"]), fl(t["g"]), fl(t["beta"]), cu,
+                                      h0=t["h0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1.reshape(o2.shape), o2)
+    assert torch.equal(h1, h2)
+
+
 @pytest.mark.slow
 def test_bf16_t32768_h32_sampled_heads(gdn):
     """The throughput workload at full size, in the launch configuration the
