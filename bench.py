@@ -226,9 +226,28 @@ def bench_varlen(torch, gdn, inputs, steps, warmup):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     nbytes = algorithmic_bytes(1, T, H, False, False) + S * H * STATE_BYTES
-    return {"workload": VARLEN_WORKLOAD, "lengths": list(VARLEN_LENGTHS), "H": H, "steps": steps,
-            "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nbytes,
-            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    res = {"workload": VARLEN_WORKLOAD, "lengths": list(VARLEN_LENGTHS), "H": H, "steps": steps,
+           "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nbytes,
+           "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    # the backward of the same packed batch (dO ~ N(0,1), no initial state)
+    do = torch.from_numpy(inputs.generate(B=1, T=T, H=H, dout=True, seed=6).dout[0]).to(dev).to(torch.bfloat16)
+    ws = torch.empty(gdn.gdn_chunk_bwd_varlen_workspace_size(S, T, H), dtype=torch.uint8, device=dev)
+
+    def bstep():
+        gdn.gdn_chunk_bwd_varlen(q, k, v, g, beta, do, cu, workspace=ws)
+
+    for _ in range(warmup):
+        bstep()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        bstep()
+    torch.cuda.synchronize()
+    bms = (time.perf_counter() - t0) * 1e3 / steps
+    bbytes = T * H * BWD_BYTES_PER_TOKEN_HEAD + S * H * STATE_BYTES
+    res.update({"bwd_ms_per_call": bms, "bwd_tokens_per_s": T / (bms * 1e-3),
+                "bwd_hbm_frac": bbytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+    return res
 
 
 def cpu_baseline(x, tokens):

@@ -9,6 +9,7 @@ library's HIP kernels; there is no fallback path.
     gdn_chunk_fwd(q, k, v, g, beta, h0=None, scale=1.0, ...) -> (o, ht)
     gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None, ...) -> (o, ht)
     gdn_chunk_bwd(q, k, v, g, beta, dout, h0=None, dht=None, scale=1.0) -> dict
+    gdn_chunk_bwd_varlen(q, k, v, g, beta, dout, cu_seqlens, h0=None, ...) -> dict
     gdn_gate_scan(g, window_chunks=8, log_eps=log(2^-24)) -> (flags, max_window_logdecay)
 
 Layouts: q, k [B,T,H,128]; v [B,T,H,128]; g = log(alpha) and beta [B,T,H]
@@ -23,9 +24,10 @@ from . import _lib
 
 DEFAULT_LOG_EPS = math.log(2.0 ** -24)
 
-__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_varlen", "gdn_chunk_bwd", "gdn_gate_scan", "gdn_plan_segments",
-           "gdn_chunk_fwd_plan_info",
-           "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd_workspace_size", "options"]
+__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_varlen", "gdn_chunk_bwd", "gdn_chunk_bwd_varlen", "gdn_gate_scan",
+           "gdn_plan_segments",
+           "gdn_chunk_fwd_plan_info", "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd_workspace_size",
+           "gdn_chunk_bwd_varlen_workspace_size", "options"]
 
 
 def options(split_mode=0, n_segments=1, use_window=True, window_chunks=8,
@@ -83,6 +85,14 @@ def gdn_chunk_fwd_workspace_size(B, T, H, dk=128, dv=128, bf16=True, **opts) -> 
     n = _lib.load().gdn_chunk_fwd_workspace_size(int(B), int(T), int(H), int(dk), int(dv),
                                                  _lib.GDN_BF16 if bf16 else _lib.GDN_F32,
                                                  ctypes.byref(o))
+    if n == ctypes.c_size_t(-1).value:
+        raise _lib.GDNError(_lib.GDN_ERR_INVALID_ARG, _lib.last_error())
+    return int(n)
+
+
+def gdn_chunk_bwd_varlen_workspace_size(n_seqs, T, H, dk=128, dv=128, bf16=True) -> int:
+    n = _lib.load().gdn_chunk_bwd_varlen_workspace_size(n_seqs, T, H, dk, dv,
+                                                        _lib.GDN_BF16 if bf16 else _lib.GDN_F32)
     if n == ctypes.c_size_t(-1).value:
         raise _lib.GDNError(_lib.GDN_ERR_INVALID_ARG, _lib.last_error())
     return int(n)
@@ -213,6 +223,43 @@ def gdn_chunk_bwd(q, k, v, g, beta, dout, h0=None, dht=None, scale=1.0, *, works
                                  _ptr(dout), _ptr(dht), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dg),
                                  _ptr(db), _ptr(dh0), B, T, H, dk, dv, code, float(scale),
                                  _ptr(workspace), wsz, _stream(q.device)))
+    return {"dq": dq, "dk": dkk, "dv": dvv, "dg": dg, "dbeta": db, "dh0": dh0}
+
+
+def gdn_chunk_bwd_varlen(q, k, v, g, beta, dout, cu_seqlens, h0=None, dht=None, scale=1.0, *,
+                         workspace=None, need_dh0=True):
+    """Backward of gdn_chunk_fwd_varlen (packed sequences, tensors [T, H, ..] or
+    [1, T, H, ..], cu_seqlens int32 [S + 1] on the device).  Returns a dict with
+    dq, dk, dv, dg, dbeta shaped like their inputs and dh0 [S, H, dk, dv] (None
+    when need_dh0 is False).  Tokens outside every sequence are not written
+    (their gradients are left as allocated)."""
+    torch = _torch()
+    lib = _lib.load()
+    _dev(q, "q")
+    dt = q.dtype
+    _dev(k, "k", dt), _dev(v, "v", dt), _dev(dout, "dout", dt)
+    _dev(g, "g", torch.float32), _dev(beta, "beta", torch.float32)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    _dev(h0, "h0", torch.float32), _dev(dht, "dht", torch.float32)
+    T, H, dk = q.shape[-3], q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    S = cu_seqlens.numel() - 1
+    if S < 1:
+        raise ValueError("cu_seqlens needs at least two entries")
+    dq, dkk, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg, db = torch.empty_like(g), torch.empty_like(beta)
+    dh0 = torch.empty((S, H, dk, dv), dtype=torch.float32, device=q.device) if need_dh0 else None
+    code = _dtype_code(q)
+    if workspace is None:
+        n = lib.gdn_chunk_bwd_varlen_workspace_size(S, T, H, dk, dv, code)
+        if n == ctypes.c_size_t(-1).value:
+            raise _lib.GDNError(_lib.GDN_ERR_INVALID_ARG, _lib.last_error())
+        workspace = _workspace(int(n), q.device)
+    _lib.check(lib.gdn_chunk_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                                        _ptr(dout), _ptr(dht), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dg),
+                                        _ptr(db), _ptr(dh0), _ptr(cu_seqlens), S, T, H, dk, dv, code,
+                                        float(scale), _ptr(workspace), workspace.numel(),
+                                        _stream(q.device)))
     return {"dq": dq, "dk": dkk, "dv": dvv, "dg": dg, "dbeta": db, "dh0": dh0}
 
 

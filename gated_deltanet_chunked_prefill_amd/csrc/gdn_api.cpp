@@ -191,6 +191,26 @@ BwdLayout bwd_layout(int B, int T, int H) {
     return L;
 }
 
+// Packed-sequence backward workspace: the chunk prefix, then states and state
+// gradients in per-head slots (cmax = ceil(T/64) + S bounds the chunks of all
+// sequences together).
+struct BwdVarlenLayout {
+    size_t cstart, hstore, dhstore, total;
+    int cmax;
+};
+
+BwdVarlenLayout bwd_varlen_layout(int S, int T, int H) {
+    BwdVarlenLayout L{};
+    L.cmax = num_chunks(T) + S;
+    const size_t SS = 128 * 128;
+    size_t off = 0;
+    L.cstart = off;  off += align_up(((size_t)S + 1) * sizeof(int32_t));
+    L.hstore = off;  off += align_up((size_t)H * (L.cmax + S) * SS * sizeof(uint16_t));   // bf16
+    L.dhstore = off; off += align_up((size_t)H * L.cmax * SS * sizeof(uint16_t));
+    L.total = off;
+    return L;
+}
+
 gdn_status device_cus(int* cus) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -365,6 +385,81 @@ gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
         return gdn::launch_fwd(p, gdn::PHASE_VARLEN, dtype == GDN_BF16, s);
     });
     if (e != hipSuccess) return hip_fail(e, "forward launch");
+    return GDN_OK;
+}
+
+size_t gdn_chunk_bwd_varlen_workspace_size(int n_seqs, int T, int H, int dk, int dv, gdn_dtype dtype) {
+    if (n_seqs <= 0 || check_shapes(1, T, H, dk, dv, dtype) != GDN_OK) return (size_t)-1;
+    if ((long long)n_seqs * H > (1LL << 30)) return (size_t)-1;
+    return bwd_varlen_layout(n_seqs, T, H).total;
+}
+
+gdn_status gdn_chunk_bwd_varlen(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, const float* h0, const void* dout, const float* dht,
+                                void* grad_q, void* grad_k, void* grad_v, float* grad_g,
+                                float* grad_beta, float* grad_h0, const int32_t* cu_seqlens, int n_seqs,
+                                int T, int H, int dk, int dv, gdn_dtype dtype, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!q || !k || !v || !g || !beta || !dout || !grad_q || !grad_k || !grad_v || !grad_g || !grad_beta ||
+        !cu_seqlens)
+        return fail(GDN_ERR_INVALID_ARG, "q, k, v, g, beta, dout, the gradients of q, k, v, g, beta and "
+                                         "cu_seqlens are required");
+    if (n_seqs <= 0) return fail(GDN_ERR_INVALID_ARG, "n_seqs must be positive (got %d)", n_seqs);
+    gdn_status st = check_shapes(1, T, H, dk, dv, dtype);
+    if (st != GDN_OK) return st;
+    if ((long long)n_seqs * H > (1LL << 30)) return fail(GDN_ERR_INVALID_ARG, "too many sequences");
+    if (dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "the backward supports bf16 I/O only");
+    const void* vec_ptrs[] = {q, k, v, dout, grad_q, grad_k, grad_v};
+    for (const void* p : vec_ptrs)
+        if (!aligned16(p))
+            return fail(GDN_ERR_INVALID_ARG, "q, k, v, dout and their gradients must be 16-byte aligned");
+    const void* i32_ptrs[] = {g, beta, h0, dht, grad_g, grad_beta, grad_h0, cu_seqlens};
+    for (const void* p : i32_ptrs)
+        if (p && !aligned4(p))
+            return fail(GDN_ERR_INVALID_ARG, "float32 tensors and cu_seqlens must be 4-byte aligned");
+    if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite");
+    const BwdVarlenLayout L = bwd_varlen_layout(n_seqs, T, H);
+    if (!workspace) return fail(GDN_ERR_WORKSPACE, "a workspace of %zu bytes is required", L.total);
+    if (workspace_bytes < L.total)
+        return fail(GDN_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
+    if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+        return fail(GDN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+    hipStream_t s = (hipStream_t)stream;
+    hipStream_t s2 = nullptr;
+    hipError_t e = side_stream(&s2);
+    if (e != hipSuccess) return hip_fail(e, "backward side stream");
+    char* ws = (char*)workspace;
+    int* cstart = (int*)(ws + L.cstart);
+    __bf16* hstore = (__bf16*)(ws + L.hstore);
+    __bf16* dhstore = (__bf16*)(ws + L.dhstore);
+    gdn::FwdParams f{};
+    f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.h0 = h0; f.o = nullptr; f.ht = nullptr;
+    f.B = n_seqs; f.T = T; f.H = H; f.N = num_chunks(T); f.P = 1; f.w = 1; f.scale = scale;
+    f.hstore = hstore;
+    f.cu = cu_seqlens; f.cmax = L.cmax; f.cstart = cstart;
+    gdn::BwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.dout = dout; p.dht = dht;
+    p.dq = grad_q; p.dk = grad_k; p.dv = grad_v; p.dg = grad_g; p.dbeta = grad_beta; p.dh0 = grad_h0;
+    p.B = n_seqs; p.T = T; p.H = H; p.N = num_chunks(T); p.scale = scale;
+    p.hstore = hstore;
+    p.dhstore = dhstore;
+    p.cu = cu_seqlens; p.cmax = L.cmax; p.cstart = cstart;
+    // the chunk prefix, then (as in gdn_chunk_bwd) the state-gradient sweep on the
+    // side stream beside the state store, then the local gradients
+    e = gdn::launch_seq_chunk_prefix(cu_seqlens, n_seqs, T, cstart, s);
+    if (e != hipSuccess) return hip_fail(e, "backward chunk prefix launch");
+    e = stream_wait(s2, s);
+    if (e != hipSuccess) return hip_fail(e, "backward fork");
+    e = recorded(GDN_LAUNCH_BWD_DH, s2, [&] { return gdn::launch_bwd_dh(p, true, s2); });
+    if (e != hipSuccess) return hip_fail(e, "backward state-gradient launch");
+    e = recorded(GDN_LAUNCH_BWD_STATES, s, [&] { return gdn::launch_fwd(f, gdn::PHASE_STATES_VARLEN, true, s); });
+    if (e != hipSuccess) return hip_fail(e, "backward state launch");
+    e = stream_wait(s, s2);
+    if (e != hipSuccess) return hip_fail(e, "backward join");
+    e = recorded(GDN_LAUNCH_BWD_LOCAL, s, [&] { return gdn::launch_bwd_local(p, true, s); });
+    if (e != hipSuccess) return hip_fail(e, "backward local-gradient launch");
     return GDN_OK;
 }
 

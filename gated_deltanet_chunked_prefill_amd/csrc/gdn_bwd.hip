@@ -240,6 +240,76 @@ __global__ __launch_bounds__(kDhThreads, 1) void gdn_bwd_dh_kernel(BwdParams prm
         dh_prep_loop<T>(prm, sm, bh);
 }
 
+// Packed sequences: parameters of sequence s, head h as one sequence of a batch
+// of sequences of its length.  Every token pointer is shifted by t0 - s*len
+// tokens (the kernels' token index s*len + t then addresses token t0 + t), and
+// the stored-state pointers so that slot bh*(nch+1) + c (states) and bh*nch + c
+// (state gradients) address the sequence's own slots.
+__device__ __forceinline__ void varlen_bwd_params(BwdParams& p, int s, int h, size_t elem) {
+    const SeqSpan sp = seq_span(p.cu, p.cstart, p.T, s);
+    const long long rows = ((long long)sp.t0 - (long long)s * sp.len) * p.H;   // token-head rows
+    const long long vb = rows * kDk * (long long)elem;                          // bytes of q, k, v rows
+    p.q = (const char*)p.q + vb;
+    p.k = (const char*)p.k + vb;
+    p.v = (const char*)p.v + vb;
+    p.dout = (const char*)p.dout + vb;
+    p.dq = (char*)p.dq + vb;
+    p.dk = (char*)p.dk + vb;
+    p.dv = (char*)p.dv + vb;
+    p.g += rows;
+    p.beta += rows;
+    p.dg += rows;
+    p.dbeta += rows;
+    const long long bh = (long long)s * p.H + h;
+    const long long SS = (long long)kDk * kDv;
+    p.hstore += ((long long)h * (p.cmax + p.B) + sp.c0 + s - bh * (sp.nch + 1)) * SS;
+    p.dhstore += ((long long)h * p.cmax + sp.c0 - bh * sp.nch) * SS;
+    p.T = sp.len;
+    p.N = sp.nch;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kDhThreads, 1) void gdn_bwd_dh_varlen_kernel(BwdParams prm_in) {
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    Smem<T>& sm = *reinterpret_cast<Smem<T>*>(smem_raw);
+    const int bh = blockIdx.x;
+    BwdParams prm = prm_in;
+    varlen_bwd_params(prm, bh / prm_in.H, bh % prm_in.H, sizeof(T));
+    if (wave_id() < 4)
+        dh_state_loop<T>(prm, sm, bh);
+    else
+        dh_prep_loop<T>(prm, sm, bh);
+}
+
+// Packed sequences: cstart[s] = chunks of sequences 0 .. s-1 (s = 0 .. B), one
+// workgroup, 256 sequences per round with a running carry.
+__global__ __launch_bounds__(256) void seq_chunk_prefix_kernel(const int* __restrict__ cu, int B, int T,
+                                                               int* __restrict__ cstart) {
+    __shared__ int part[256];
+    const int tid = threadIdx.x;
+    int carry = 0;
+    for (int s0 = 0; s0 < B; s0 += 256) {
+        const int s = s0 + tid;
+        int nch = 0;
+        if (s < B) {
+            const int t0 = clamp_tok(cu[s], 0, T);
+            nch = (clamp_tok(cu[s + 1], t0, T) - t0 + 63) / 64;
+        }
+        part[tid] = nch;
+        __syncthreads();
+        for (int d = 1; d < 256; d <<= 1) {   // inclusive scan
+            const int x = tid >= d ? part[tid - d] : 0;
+            __syncthreads();
+            part[tid] += x;
+            __syncthreads();
+        }
+        if (s < B) cstart[s] = carry + part[tid] - nch;
+        carry += part[255];
+        __syncthreads();
+    }
+    if (tid == 0) cstart[B] = carry;
+}
+
 // ---------------------------------------------------------------------------
 // Launch 2: local gradients of every chunk.
 
@@ -335,13 +405,13 @@ __device__ __forceinline__ void copy_tile_rows(T* dst, const T* tile, int H, int
     }
 }
 
+// The local gradients of chunk c of head bh (one workgroup).
 template <typename T>
-__global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_kernel(BwdParams prm) {
+__device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) {
     using F = typename FragOf<T>::type;
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     LocalSmem<T>& sm = *reinterpret_cast<LocalSmem<T>*>(smem_raw);
     const int H = prm.H, Tn = prm.T, N = prm.N;
-    const int bh = blockIdx.x / N, c = blockIdx.x % N;
     const int b = bh / H, h = bh % H;
     const int t0 = c * kChunk, nv = chunk_len(Tn, c);
     const int tid = threadIdx.x;
@@ -650,6 +720,32 @@ __global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_kernel(BwdPara
     }
 }
 
+template <typename T>
+__global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_kernel(BwdParams prm) {
+    local_body<T>(prm, blockIdx.x / prm.N, blockIdx.x % prm.N);
+}
+
+// Packed sequences: workgroup (h, gc) takes chunk gc of all the batch's chunks
+// of head h (none past the last chunk); a binary search of the chunk prefix
+// finds its sequence.
+template <typename T>
+__global__ __launch_bounds__(kLocalThreads, 1) void gdn_bwd_local_varlen_kernel(BwdParams prm_in) {
+    const int h = (int)blockIdx.x / prm_in.cmax, gc = (int)blockIdx.x % prm_in.cmax;
+    const int* const cs = prm_in.cstart;
+    if (gc >= __builtin_amdgcn_readfirstlane(cs[prm_in.B])) return;   // whole workgroup
+    int lo = 0, hi = prm_in.B;   // cs[lo] <= gc < cs[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (__builtin_amdgcn_readfirstlane(cs[mid]) <= gc)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    BwdParams prm = prm_in;
+    varlen_bwd_params(prm, lo, h, sizeof(T));
+    local_body<T>(prm, lo * prm_in.H + h, gc - __builtin_amdgcn_readfirstlane(cs[lo]));
+}
+
 template <typename K>
 hipError_t set_lds(K kernel, size_t bytes) {
     return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
@@ -661,10 +757,14 @@ hipError_t launch_dh_t(const BwdParams& p, hipStream_t s) {
     const size_t lds = sizeof(Smem<T>);
     if (!configured) {
         hipError_t e = set_lds(gdn_bwd_dh_kernel<T>, lds);
+        if (e == hipSuccess) e = set_lds(gdn_bwd_dh_varlen_kernel<T>, lds);
         if (e != hipSuccess) return e;
         configured = true;
     }
-    hipLaunchKernelGGL((gdn_bwd_dh_kernel<T>), dim3(p.B * p.H), dim3(kDhThreads), lds, s, p);
+    if (p.cu)
+        hipLaunchKernelGGL((gdn_bwd_dh_varlen_kernel<T>), dim3(p.B * p.H), dim3(kDhThreads), lds, s, p);
+    else
+        hipLaunchKernelGGL((gdn_bwd_dh_kernel<T>), dim3(p.B * p.H), dim3(kDhThreads), lds, s, p);
     return hipGetLastError();
 }
 
@@ -674,10 +774,15 @@ hipError_t launch_local_t(const BwdParams& p, hipStream_t s) {
     const size_t lds = sizeof(LocalSmem<T>);
     if (!configured) {
         hipError_t e = set_lds(gdn_bwd_local_kernel<T>, lds);
+        if (e == hipSuccess) e = set_lds(gdn_bwd_local_varlen_kernel<T>, lds);
         if (e != hipSuccess) return e;
         configured = true;
     }
-    hipLaunchKernelGGL((gdn_bwd_local_kernel<T>), dim3(p.B * p.H * p.N), dim3(kLocalThreads), lds, s, p);
+    if (p.cu)
+        hipLaunchKernelGGL((gdn_bwd_local_varlen_kernel<T>), dim3(p.H * p.cmax), dim3(kLocalThreads), lds, s,
+                           p);
+    else
+        hipLaunchKernelGGL((gdn_bwd_local_kernel<T>), dim3(p.B * p.H * p.N), dim3(kLocalThreads), lds, s, p);
     return hipGetLastError();
 }
 
@@ -689,6 +794,11 @@ hipError_t launch_bwd_dh(const BwdParams& p, bool bf16, hipStream_t s) {
 
 hipError_t launch_bwd_local(const BwdParams& p, bool bf16, hipStream_t s) {
     return bf16 ? launch_local_t<__bf16>(p, s) : hipErrorNotSupported;
+}
+
+hipError_t launch_seq_chunk_prefix(const int* cu, int B, int T, int* cstart, hipStream_t s) {
+    hipLaunchKernelGGL(seq_chunk_prefix_kernel, dim3(1), dim3(256), 0, s, cu, B, T, cstart);
+    return hipGetLastError();
 }
 
 }  // namespace gdn

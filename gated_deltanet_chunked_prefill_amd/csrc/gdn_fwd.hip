@@ -685,28 +685,31 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_kernel(FwdParams prm) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     Smem<T>& sm = *reinterpret_cast<Smem<T>*>(smem_raw);
     Task tk;
-    if constexpr (PHASE == PHASE_VARLEN) {
-        // Packed sequences: sequence s = blockIdx / H holds tokens [t0, t1).  The
-        // task runs as sequence s of a batch of sequences of length len, with
+    if constexpr (PHASE == PHASE_VARLEN || PHASE == PHASE_STATES_VARLEN) {
+        // Packed sequences: sequence s = blockIdx / H holds tokens [t0, t0 + len).
+        // The task runs as sequence s of a batch of sequences of length len, with
         // every token pointer shifted by t0 - s*len, so that the loops' token
-        // index s*len + t addresses token t0 + t.
-        const int s = (int)blockIdx.x / prm.H;
-        int t0 = uni(prm.cu[s]), t1 = uni(prm.cu[s + 1]);
-        t0 = t0 < 0 ? 0 : (t0 > prm.T ? prm.T : t0);
-        t1 = t1 < t0 ? t0 : (t1 > prm.T ? prm.T : t1);
-        const int len = t1 - t0;
-        const long long shift = ((long long)t0 - (long long)s * len) * prm.H;   // in token-head rows
+        // index s*len + t addresses token t0 + t (and, when the states are kept,
+        // the state slot bh*(nch+1) + c addresses the sequence's own slots).
+        const int s = (int)blockIdx.x / prm.H, h = (int)blockIdx.x % prm.H;
+        const SeqSpan sp = seq_span(prm.cu, prm.cstart, prm.T, s);
+        const long long shift = ((long long)sp.t0 - (long long)s * sp.len) * prm.H;   // token-head rows
         FwdParams p = prm;
         p.q = (const T*)prm.q + shift * kDk;
         p.k = (const T*)prm.k + shift * kDk;
         p.v = (const T*)prm.v + shift * kDv;
-        p.o = (T*)prm.o + shift * kDv;
+        if (prm.o) p.o = (T*)prm.o + shift * kDv;
         p.g = prm.g + shift;
         p.beta = prm.beta + shift;
-        p.T = len;
-        p.N = (len + kChunk - 1) / kChunk;
+        p.T = sp.len;
+        p.N = sp.nch;
+        if constexpr (PHASE == PHASE_STATES_VARLEN) {
+            const long long slot = (long long)h * (prm.cmax + prm.B) + sp.c0 + s -
+                                   (long long)blockIdx.x * (sp.nch + 1);
+            p.hstore = prm.hstore + slot * (long long)(kDk * kDv);
+        }
         whole_head_task(p, tk);
-        run_task<T, MODE_FULL>(p, sm, tk);
+        run_task<T, MODE_FULL, PHASE == PHASE_STATES_VARLEN>(p, sm, tk);
     } else {
         whole_head_task(prm, tk);
         if (PHASE == PHASE_STATES)
@@ -1269,6 +1272,7 @@ hipError_t launch_fwd_t(const FwdParams& p, int phase, hipStream_t s) {
     if (phase == PHASE_SINGLE) return launch_phase<T, PHASE_SINGLE>(p, s);
     if (phase == PHASE_STATES) return launch_phase<T, PHASE_STATES>(p, s);
     if (phase == PHASE_VARLEN) return launch_phase<T, PHASE_VARLEN>(p, s);
+    if (phase == PHASE_STATES_VARLEN) return launch_phase<T, PHASE_STATES_VARLEN>(p, s);
     return launch_phase<T, PHASE_QUEUE>(p, s);
 }
 

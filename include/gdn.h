@@ -159,6 +159,29 @@ gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
                                 const int32_t* cu_seqlens, int n_seqs, int T, int H, int dk, int dv,
                                 gdn_dtype dtype, float scale, void* stream);
 
+/* Workspace bytes for gdn_chunk_bwd_varlen ((size_t)-1 for invalid arguments):
+ * the chunk prefix of the sequences, and per head (ceil(T/64) + 2 n_seqs)
+ * bfloat16 128 x 128 states plus (ceil(T/64) + n_seqs) state gradients. */
+size_t gdn_chunk_bwd_varlen_workspace_size(int n_seqs, int T, int H, int dk, int dv, gdn_dtype dtype);
+
+/* Backward of gdn_chunk_fwd_varlen (packed variable-length sequences, same
+ * layouts): gradients of L given dL/do = dout [T, H, dv] and dL/dht = dht
+ * [n_seqs, H, dk, dv] (NULL = 0), each sequence on its own as in
+ * gdn_chunk_bwd.  grad_q, grad_k, grad_v [T, H, ..] (I/O dtype), grad_g,
+ * grad_beta [T, H] float32, grad_h0 [n_seqs, H, dk, dv] float32 or NULL.
+ * cu_seqlens as for gdn_chunk_fwd_varlen (device, read on the device; tokens
+ * outside every sequence are not written).  bf16 I/O only.  workspace: at
+ * least gdn_chunk_bwd_varlen_workspace_size() bytes, 256-byte aligned.  Runs a
+ * one-workgroup chunk-prefix launch, then the launches of gdn_chunk_bwd (the
+ * state store and the state-gradient sweep side by side on the library's side
+ * stream) with one workgroup per (sequence, head) or per (head, chunk). */
+gdn_status gdn_chunk_bwd_varlen(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, const float* h0, const void* dout, const float* dht,
+                                void* grad_q, void* grad_k, void* grad_v, float* grad_g,
+                                float* grad_beta, float* grad_h0, const int32_t* cu_seqlens, int n_seqs,
+                                int T, int H, int dk, int dv, gdn_dtype dtype, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes for gdn_chunk_bwd ((size_t)-1 for invalid arguments):
  * B*H*(2N+1) bfloat16 128 x 128 matrices (N = number of 64-token chunks), the
  * state entering every chunk plus the final state, and the state gradient

@@ -139,3 +139,23 @@ def test_varlen_validation_before_launch():
     assert call(dk=64) == _lib.GDN_ERR_UNSUPPORTED
     assert call(q=A + 8) == _lib.GDN_ERR_INVALID_ARG
     assert call(cu=A + 2) == _lib.GDN_ERR_INVALID_ARG
+
+
+def test_bwd_varlen_validation_before_launch():
+    lib = _lib.load()
+    A = 1 << 20
+    SS = 128 * 128 * 2
+    # 2 sequences, T = 128: cmax = 2 + 2 chunk slots; per head 6 states and 4 gradients
+    assert lib.gdn_chunk_bwd_varlen_workspace_size(2, 128, 1, 128, 128, 1) == 256 + 6 * SS + 4 * SS
+    assert lib.gdn_chunk_bwd_varlen_workspace_size(0, 128, 1, 128, 128, 1) == ctypes.c_size_t(-1).value
+    P = lambda a: ctypes.c_void_p(a) if a else None
+
+    def call(cu=A, dt=1, ws=A, wsz=1 << 30):
+        # q, k, v, g, beta, h0 = NULL, dout, dht = NULL, five gradients, dh0 = NULL
+        return lib.gdn_chunk_bwd_varlen(*([P(A)] * 5), None, P(A), None, *([P(A)] * 5), None, P(cu), 2, 128,
+                                        1, 128, 128, dt, 1.0, P(ws), wsz, None)
+    assert call(cu=0) == _lib.GDN_ERR_INVALID_ARG
+    assert call(dt=0) == _lib.GDN_ERR_UNSUPPORTED
+    assert call(ws=0) == _lib.GDN_ERR_WORKSPACE
+    assert call(wsz=1024) == _lib.GDN_ERR_WORKSPACE
+    assert call(ws=A + 16) == _lib.GDN_ERR_INVALID_ARG
