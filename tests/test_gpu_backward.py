@@ -159,3 +159,45 @@ def test_bwd_varlen_equals_fixed_length(gdn):
     for n in ("dq", "dk", "dv", "dg", "dbeta"):
         assert torch.equal(a[n].reshape(b[n].shape), b[n]), n
     assert torch.equal(a["dh0"], b["dh0"])
+
+
+def test_varlen_many_sequences(gdn):
+    """300 short packed sequences (more than one 256-sequence round of the chunk
+    prefix; lengths 0 to 70, empty ones included): forward outputs, final states
+    and every gradient of each sequence against the oracle."""
+    import torch
+    say("case varlen 300 sequences, forward and backward")
+    rng = np.random.default_rng(61)
+    lens = rng.integers(0, 71, size=300)
+    lens[[5, 17, 260]] = 0
+    H, S, T = 1, len(lens), int(lens.sum())
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    x = inputs.generate(B=1, T=T, H=H, dout=True, seed=62)
+    h0 = inputs.generate(B=S, T=1, H=H, h0_std=0.05, seed=63).h0
+    t = to_gpu(x)
+    sq = lambda a: a[0]
+    cu_t, h0_t = torch.from_numpy(cu).cuda(), torch.from_numpy(h0).cuda()
+    o, ht = gdn.gdn_chunk_fwd_varlen(sq(t["q"]), sq(t["k"]), sq(t["v"]), sq(t["g"]), sq(t["beta"]), cu_t,
+                                     h0=h0_t)
+    out = gdn.gdn_chunk_bwd_varlen(sq(t["q"]), sq(t["k"]), sq(t["v"]), sq(t["g"]), sq(t["beta"]),
+                                   sq(t["dout"]), cu_t, h0=h0_t)
+    torch.cuda.synchronize()
+    o, ht = to_np(o), to_np(ht)
+    got = {n: to_np(out[n]) for n in NAMES}
+    worst = {}
+    for s_ in range(S):
+        a, b = int(cu[s_]), int(cu[s_ + 1])
+        if a == b:
+            assert np.array_equal(ht[s_], h0[s_].astype(np.float64))
+            assert np.max(np.abs(got["dh0"][s_])) == 0.0
+            continue
+        sl = lambda arr: arr[:, a:b]
+        oref, href = oracle.fwd(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), h0[s_:s_ + 1])
+        ref = oracle.bwd(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), sl(x.dout), h0[s_:s_ + 1])
+        errs = {"o": rel_err(o[None, a:b], oref), "ht": rel_err(ht[s_:s_ + 1], href)}
+        for n in NAMES:
+            errs[n] = rel_err(got[n][None, a:b] if n != "dh0" else got[n][s_:s_ + 1], ref[n])
+        for n, e in errs.items():
+            worst[n] = max(worst.get(n, 0.0), e)
+    say("  worst over sequences: " + "  ".join(f"{n} {e:.2e}" for n, e in worst.items()))
+    assert all(e <= TOL_BF16 for e in worst.values()), worst
