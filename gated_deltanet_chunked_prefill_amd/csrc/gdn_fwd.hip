@@ -720,7 +720,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_kernel(FwdParams prm) {
 }
 
 template <typename T>
-__device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm);
+__device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm);
 
 // Persistent workgroups of the split forward: take jobs until the list is empty.
 template <typename T>
@@ -809,128 +809,42 @@ constexpr float kCostLink = 0.8f;
 constexpr float kCostWarm = 0.7f;
 constexpr int kSeg0Weight = 11;
 
-struct WinLevels {
-    int n[kMaxWindowLevels];     // window heads per level (index m - 1)
-    float c[kMaxWindowLevels];   // warm-up cost kCostWarm m w of a level
-    int cap[kMaxWindowLevels];   // most segments of a level: min(pmax, max(1, N / (m w)))
-    int levels, N;
-    int lmax;                    // levels tried (the same for every lane)
-    // per-level constants, computed once per plan
-    __device__ void init(int levels_, int N_, int w, int pmax) {
-        levels = levels_;
-        lmax = levels_;
-        N = N_;
-#pragma unroll
-        for (int m = 1; m <= kMaxWindowLevels; ++m) {
-            c[m - 1] = kCostWarm * m * w;
-            int cp = N / (m * w);
-            cp = cp < 1 ? 1 : cp;
-            cap[m - 1] = cp < pmax ? cp : pmax;
-        }
-    }
-};
+constexpr int kCandP = 32;   // segment counts tried per kept window level: P = 1, 3, .., 32
+constexpr int kMaxCand = (kMaxWindowLevels + 1) * (kCandP - 1);
 
-// Segments of a level-m head so that each job costs at most M: the smallest P
-// with (N + (P - 1) c) / P <= M; `bad` is set when none within the cap exists.
-__device__ __forceinline__ int win_segments(const WinLevels& wl, int m, float M, bool& bad) {
-    const float c = wl.c[m - 1];
-    const float q = ((float)wl.N - c) * __builtin_amdgcn_rcpf(M - c);
+// Job cost of a head of warm-up cost c in P segments: (N + (P - 1) c) / P.
+__device__ __forceinline__ float win_job_cost(int N, float c, int P) {
+    return ((float)N + (float)(P - 1) * c) / (float)P;
+}
+
+// Segments of a window head of warm-up cost c so that each job costs at most M:
+// the smallest P with (N + (P - 1) c) / P <= M; `bad` is set when none up to
+// `cap` exists.
+__device__ __forceinline__ int win_segments(int N, float c, int cap, float M, bool& bad) {
+    const float q = ((float)N - c) * __builtin_amdgcn_rcpf(M - c);
     int p = (int)ceilf(q);
-    p = M >= (float)wl.N ? 1 : p;
-    bad = M < (float)wl.N && (M <= c || p > wl.cap[m - 1]);
-    return p;
+    p = M >= (float)N ? 1 : p;
+    bad = M < (float)N && (M <= c || p > cap);
+    return bad ? 1 : p;
 }
 
-// Smallest job cost of the window heads on `free` workgroups; Pm[m-1] gets the
-// segment counts.  With fewer workgroups than window heads every head is one job.
-// The level loops are unrolled and branch-free (per-level values stay in
-// registers; lanes evaluating different candidates do not diverge), bounded by
-// the wave-uniform level count lmax.
-__device__ float window_cost(const WinLevels& wl, int free, int* Pm) {
-    const int lmax = uni(wl.lmax);
-    int n_w = 0;
-#pragma unroll
-    for (int m = 1; m <= kMaxWindowLevels; ++m) {
-        n_w += m <= wl.levels ? wl.n[m - 1] : 0;
-        Pm[m - 1] = 1;
-    }
-    if (n_w == 0) return 0.f;
-    if (free < n_w) return free > 0 ? (float)((n_w + free - 1) / free) * wl.N : -1.f;
-    float lo = 0.f, hi = (float)wl.N;   // hi is feasible (one job per head)
-    for (int it = 0; it < 12; ++it) {   // M to within N / 4096 chunk steps
-        const float mid = 0.5f * (lo + hi);
-        int need = 0;
-        bool ok = true;
-#pragma unroll
-        for (int m = 1; m <= kMaxWindowLevels; ++m) {
-            if (m > lmax) break;
-            const bool act = m <= wl.levels && wl.n[m - 1] > 0;
-            bool bad;
-            const int p = win_segments(wl, m, mid, bad);
-            ok = ok && !(act && bad);
-            need += act ? wl.n[m - 1] * p : 0;
-        }
-        const bool feas = ok && need <= free;
-        hi = feas ? mid : hi;
-        lo = feas ? lo : mid;
-    }
-    float cost = 0.f;
-#pragma unroll
-    for (int m = 1; m <= kMaxWindowLevels; ++m) {
-        if (m > lmax) break;
-        const bool act = m <= wl.levels && wl.n[m - 1] > 0;
-        bool bad;
-        const int p = win_segments(wl, m, hi, bad);
-        Pm[m - 1] = act ? p : 1;
-        const float t = ((float)wl.N + (p - 1) * wl.c[m - 1]) / (float)p;
-        cost = act && t > cost ? t : cost;
-    }
-    return cost;
-}
-
-// Estimated makespan (in full chunk steps) of P segments per exact head; also
-// returns the window heads' segment counts per level.
-__device__ float plan_cost(int P, int n_e, const WinLevels& wl, int cus, int* Pm) {
-    const int N = wl.N;
-    const int ecus = n_e * (P == 1 ? 1 : P - 1);
-    float te = 0.f;
-    if (n_e > 0)
-        te = P == 1 ? (float)N : 8.f * N * (1.f + kCostPass1) / (kSeg0Weight + 8 * (P - 1)) + (P - 2) * kCostLink;
-    const int free = cus - ecus > 0 ? cus - ecus : 0;
-    float tw = window_cost(wl, free, Pm);
-    if (tw < 0.f) tw = te + N;   // no workgroup left: the window heads run after the exact ones
-    return te > tw ? te : tw;
+// A store through a global-address-space pointer.  The same store through a
+// generic pointer is a flat store, which the wave also counts as an LDS
+// operation: the next LDS barrier would wait until it reached memory.
+template <typename V>
+__device__ __forceinline__ void gstore(V* p, const V& v) {
+    *(__attribute__((address_space(1))) V*)p = v;
 }
 
 __device__ __forceinline__ void put_job(TaskRec* jobs, int j, int bh, int seg, int cb, int co, int ce,
                                         int mode, int init, int dst) {
-    TaskRec r;
-    r.bh = bh; r.seg = seg; r.c_begin = cb; r.c_out = co; r.c_end = ce;
-    r.mode = mode; r.init = init; r.dst = dst;
-    jobs[j] = r;
-}
-
-// Exclusive prefix sum over the kThreads threads of the workgroup.
-__device__ int block_exclusive_scan(int x, int* s_wave, int& total) {
-    constexpr int NW = kThreads / 64;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int incl = x;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += y;
-    }
-    if (lane == 63) s_wave[wv] = incl;
-    __syncthreads();
-    int before = 0;
-    total = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        before += i < wv ? s_wave[i] : 0;
-        total += s_wave[i];
-    }
-    __syncthreads();
-    return before + incl - x;
+    using i32x4 = int __attribute__((ext_vector_type(4)));
+    static_assert(sizeof(TaskRec) == 2 * sizeof(i32x4), "job record layout");
+    // the record's fields in declaration order, as two 16-byte stores
+    const i32x4 lo = {bh, seg, cb, co}, hi = {ce, mode, init, dst};
+    i32x4* const dst4 = reinterpret_cast<i32x4*>(jobs + j);
+    gstore(dst4, lo);
+    gstore(dst4 + 1, hi);
 }
 
 __device__ int seg_bound(long long num, long long den, int N) {
@@ -959,35 +873,87 @@ __device__ int win_bound(int p, int P, int N, float c, bool forced) {
 // Per-head tables of the planner live in LDS up to this many heads (always, for
 // the automatic split, which needs B*H < CUs/2), in the workspace beyond.
 constexpr int kPlanHeads = 4096;
+constexpr int kMaxBp = kMaxWindowLevels * kCandP;   // job-cost breakpoints: (level, P <= 32)
 
 struct PlanLds {
     int bound[kMaxSegments + 1];
-    int wave[kThreads / 64];
-    int par[2 + kMaxWindowLevels];
-    int cls[1 + kMaxWindowLevels];   // heads per class: exact, then window levels L .. 1
-    int lev[kPlanHeads];             // window level per head (0 = exact)
-    int hmap[kPlanHeads];            // heads by class
-    int kb[kMaxWindowLevels];        // heads of a level given one segment more (the first ones)
+    int lcnt[1 + kMaxWindowLevels];   // heads per window level (0 = exact)
+    float cw[kMaxWindowLevels];       // warm-up cost kCostWarm m w per level
+    int cap[kMaxWindowLevels];        // most segments per level: min(pmax, max(1, N / (m w)))
+    int cum[1 + kMaxWindowLevels];    // window heads of levels 1..m
+    int off[1 + kMaxWindowLevels];    // breakpoints of levels 1..m (level m's start at off[m-1])
+    int cnt[1 + kMaxWindowLevels];    // candidates per cutoff Lc
+    int pm[kMaxWindowLevels];         // chosen segments of a window head per level
+    int kb[kMaxWindowLevels];         // heads of a level given one segment more (the first ones)
+    int pe, lc;                       // chosen exact segment count and longest level kept
+    int tmin, win;                    // smallest estimated makespan (key) and the chosen candidate
+    int rc[kThreads / 64][1 + kMaxWindowLevels];   // heads per wave and class in one round
+    int cand_lc[kMaxCand], cand_p[kMaxCand], cand_fr[kMaxCand];   // candidate: cutoff, P, free workgroups
+    int mkey[kMaxCand];               // per candidate: smallest feasible window job cost (key)
+    int bkey[kMaxBp];                 // breakpoints, level by level (levels with heads): job cost (key)
+    int need[kMaxWindowLevels][kMaxBp];   // [Lc-1][b]: workgroups the window heads need at breakpoint b
+    int lev[kPlanHeads];              // window level per head (0 = exact)
+    int hmap[kPlanHeads];             // heads by class
 };
 
+// q = floor(a / b) for 0 <= a < 2^20 and 1 <= b < 2^12 through the reciprocal:
+// (a + 1/2) / b lies at least 1/(2b) from an integer, and the single-precision
+// product is off by at most (a / b) 2^-22 < 1/(4b).
+__device__ __forceinline__ int small_div(int a, int b) {
+    return (int)(((float)a + 0.5f) * __builtin_amdgcn_rcpf((float)b));
+}
+
 // The planner, run by the first workgroup of the persistent launch to arrive,
-// before any job.
+// before any job.  The other workgroups wait for it, so every step is a short
+// parallel pass with small code (it runs once per launch, from a cold
+// instruction cache).
+//
+// Candidates (Lc, P): window levels above Lc run as exact heads, exact heads
+// take P segments.  Per Lc (from the highest level down, only where level
+// Lc + 1 has heads or Lc is the highest) they are P = 1 and P = 3 .. the
+// largest P whose exact jobs fit the workgroups (P = 1 alone when no head is
+// exact).  The window heads' job cost M of a candidate is the smallest M at
+// which their segment counts fit the free workgroups; a level's count only
+// changes where M equals its job cost at some P, so M is the smallest feasible
+// such breakpoint (each evaluated just above the breakpoint).  The makespan
+// estimate is the larger of the exact heads' time and M; the earliest
+// candidate within 0.1 % of the smallest wins (fewer segments, more window
+// heads on near-ties).
 template <typename T>
-__device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
+__device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
     static_assert(sizeof(PlanLds) <= sizeof(Smem<T>), "planner scratch exceeds the LDS");
     PlanLds& pl = *reinterpret_cast<PlanLds*>(&sm);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int B = uni(prm.B), H = uni(prm.H), nbh = B * H, N = uni(prm.N), pmax = uni(prm.P), w = uni(prm.w);
+    const int cus = uni(prm.cus), forced = uni(prm.forced);
     const int* const wmax = uni(prm.wmax);
     const int LV = wmax ? uni(prm.levels) : 0;
+    const float log_eps = uni(prm.log_eps);
     int* const flags = uni(prm.flags);
+    int* const head_map = uni(prm.head_map);
+    float* const maxwin = uni(prm.maxwin);
+    FwdPlan* const fp = uni(prm.plan);
+    TaskRec* const jobs = uni(prm.jobs);
+    const bool has_h0 = prm.h0 != nullptr, has_ht = prm.ht != nullptr;
     const bool in_lds = nbh <= kPlanHeads;
-    int* const levp = in_lds ? pl.lev : flags;
-    int* const hm = in_lds ? pl.hmap : uni(prm.head_map);
+    if (tid <= kMaxWindowLevels) pl.lcnt[tid] = 0;
+    if (tid < kMaxWindowLevels) {
+        const int m = tid + 1;
+        pl.cw[tid] = kCostWarm * (float)(m * w);
+        int cp = N / (m * w);
+        cp = cp < 1 ? 1 : cp;
+        pl.cap[tid] = cp < pmax ? cp : pmax;
+    }
+    if (tid == 0) {
+        pl.tmin = 0x7FFFFFFF;
+        pl.win = 0x7FFFFFFF;
+    }
+    for (int i = tid; i < kMaxCand; i += kThreads) pl.mkey[i] = 0x7FFFFFFF;
+    lds_barrier();
     // 1. window levels (talk summary, paragraph 5): a head is a window head of
     //    level m when its largest sum of g over m*w consecutive chunks is at
     //    most log_eps, for the smallest such m; the preceding launch left that
-    //    largest sum per length and head (every level's value loaded together)
+    //    largest sum per length and head
     if (wmax) {
         for (int bh = tid; bh < nbh; bh += kThreads) {
             int key[kMaxWindowLevels];
@@ -996,204 +962,289 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
             int lev = 0;
 #pragma unroll
             for (int m = kMaxWindowLevels; m >= 1; --m)
-                if (m <= LV && N >= m * w && key_float(key[m - 1]) <= prm.log_eps) lev = m;
-            if (prm.maxwin) prm.maxwin[bh] = key_float(key[0]);
-            levp[bh] = lev;
+                if (m <= LV && N >= m * w && key_float(key[m - 1]) <= log_eps) lev = m;
+            if (maxwin) gstore(maxwin + bh, key_float(key[0]));
+            if (in_lds)
+                pl.lev[bh] = lev;
+            else
+                gstore(flags + bh, lev);
+            atomicAdd(&pl.lcnt[lev], 1);
         }
-        __syncthreads();
+    } else if (tid == 0) {
+        pl.lcnt[0] = nbh;
     }
-    // 2. choose the segment counts and the longest window kept (heads of a
-    //    higher level are exact: for short sequences the exact split can be
-    //    cheaper than long warm-ups), then rank the heads by class (exact
-    //    heads, then window heads of level Lc, Lc-1, .., 1, each class in head
-    //    order)
-    const int per = (nbh + kThreads - 1) / kThreads;
-    const int lo = tid * per < nbh ? tid * per : nbh;
-    const int hi = lo + per < nbh ? lo + per : nbh;
-    auto level_of = [&](int bh) { return wmax ? levp[bh] : 0; };
-    for (int m = 0; m <= LV; ++m) {
-        int cnt = 0;
-        for (int bh = lo; bh < hi; ++bh) cnt += level_of(bh) == m ? 1 : 0;
-        int tot = 0;
-        block_exclusive_scan(cnt, pl.wave, tot);
-        if (tid == 0) pl.cls[m] = tot;   // heads per level (0 = exact)
+    lds_barrier();
+    // per-level values in registers (loops over the levels are unrolled; a
+    // level picked at run time is read from LDS); cum[m]: window heads of
+    // levels 1..m; off[m]: breakpoints of levels 1..m (cap of each level with
+    // heads), so that level m's breakpoints start at off[m-1]
+    int lcnt[kMaxWindowLevels + 1], cap[kMaxWindowLevels], cum[kMaxWindowLevels + 1], off[kMaxWindowLevels + 1];
+    float cw[kMaxWindowLevels];
+    lcnt[0] = pl.lcnt[0];
+    cum[0] = 0;
+    off[0] = 0;
+#pragma unroll
+    for (int m = 1; m <= kMaxWindowLevels; ++m) {
+        lcnt[m] = pl.lcnt[m];   // zero above LV
+        cap[m - 1] = pl.cap[m - 1];
+        cw[m - 1] = pl.cw[m - 1];
+        cum[m] = cum[m - 1] + lcnt[m];
+        off[m] = off[m - 1] + (lcnt[m] > 0 ? cap[m - 1] : 0);
     }
-    __syncthreads();
-    WinLevels base;
-    base.init(LV, N, w, pmax);
-    if (wv == 0) {
-        // candidates (P, Lc): the distinct cutoffs Lc (Lc differs from Lc + 1
-        // only when level Lc + 1 has heads), from LV down, and for each the
-        // exact segment counts P that fit (P = 1 alone when no head is exact),
-        // one per lane and round; the cheapest wins, ties go to the earlier one
-        int Pe = pmax, Lc = LV;
-        if (!prm.forced) {
-            int cnt_lc[kMaxWindowLevels + 1], ne_lc[kMaxWindowLevels + 1];
-            int ncand = 0;
+    if (tid <= kMaxWindowLevels) {
+        int cv = 0, ov = 0;
 #pragma unroll
-            for (int lc = kMaxWindowLevels; lc >= 0; --lc) {
-                int ne = pl.cls[0];
+        for (int m = 1; m <= kMaxWindowLevels; ++m) {
+            cv = m == tid ? cum[m] : cv;
+            ov = m == tid ? off[m] : ov;
+        }
+        pl.cum[tid] = cv;
+        pl.off[tid] = ov;
+    }
+    lds_barrier();
+    if (!forced) {
+        // 2. candidate counts per cutoff (one thread per Lc) and the breakpoint
+        //    list (one thread per (level, P))
+        if (tid <= kMaxWindowLevels) {
+            const int lc = tid, ne = nbh - pl.cum[lc];
+            const bool distinct = lc <= LV && (lc == LV || pl.lcnt[lc + 1] > 0);
+            int pok = ne > 0 ? 1 + small_div(cus, ne) : 1;   // largest P with ne (P - 1) <= cus
+            pok = pok < pmax ? pok : pmax;
+            pok = pok < kCandP ? pok : kCandP;
+            pl.cnt[lc] = !distinct ? 0 : (ne == 0 ? 1 : 1 + (pok >= 3 ? pok - 2 : 0));
+        }
+        if (tid < kMaxBp) {
+            const int m = 1 + (tid >> 5), p = 1 + (tid & 31);
+            if (m <= LV && pl.lcnt[m] > 0 && p <= pl.cap[m - 1])
+                pl.bkey[pl.off[m - 1] + p - 1] = float_key(win_job_cost(N, pl.cw[m - 1], p) * (1.f + 1e-5f));
+        }
+        lds_barrier();
+        int cbase[kMaxWindowLevels + 1];   // first candidate of each cutoff (cutoffs from high to low)
+        int ncand = 0;
 #pragma unroll
-                for (int m = 1; m <= kMaxWindowLevels; ++m) ne += (m > lc && m <= LV) ? pl.cls[m] : 0;
-                ne_lc[lc] = ne;
-                const bool distinct = lc <= LV && (lc == LV || pl.cls[lc + 1] > 0);
-                int pok = ne > 0 ? 1 + prm.cus / ne : 1;   // largest P with ne (P - 1) <= cus
-                pok = pok < pmax ? pok : pmax;
-                cnt_lc[lc] = !distinct ? 0 : (ne == 0 ? 1 : 1 + (pok >= 3 ? pok - 2 : 0));
-                ncand += cnt_lc[lc];
+        for (int lc = kMaxWindowLevels; lc >= 0; --lc) {
+            cbase[lc] = ncand;
+            ncand += pl.cnt[lc];
+        }
+        const int nbmax = off[kMaxWindowLevels];
+        // 3. candidate i: its cutoff, P and free workgroups (one thread each);
+        //    workgroups the window heads need at each breakpoint, per cutoff
+        if (tid < ncand) {
+            int lc = 0, ci = 0;
+#pragma unroll
+            for (int l = kMaxWindowLevels; l >= 0; --l) {
+                const bool in = tid >= cbase[l] && tid < cbase[l] + pl.cnt[l];
+                lc = in ? l : lc;
+                ci = in ? tid - cbase[l] : ci;
             }
-            float best = 3.0e38f;
-            for (int i0 = 0; i0 < ncand; i0 += 64) {
-                int i = i0 + lane;
-                // candidate i -> (lc, P)
-                int lc = 0, P = 1, rem = i;
-                bool found = false;
+            const int P = ci == 0 ? 1 : ci + 2;
+            const int ne = nbh - pl.cum[lc];
+            const int fr = cus - ne * (P == 1 ? 1 : P - 1);
+            pl.cand_lc[tid] = lc;
+            pl.cand_p[tid] = P;
+            pl.cand_fr[tid] = fr > 0 ? fr : 0;
+        }
+        for (int it = tid; it < LV * kMaxBp; it += kThreads) {
+            const int lc = 1 + it / kMaxBp, b = it % kMaxBp;
+            if (b < pl.off[lc]) {
+                const float M = key_float(pl.bkey[b]);
+                int need = 0;
+                bool ok = true;
 #pragma unroll
-                for (int l = kMaxWindowLevels; l >= 0; --l) {
-                    if (!found && rem < cnt_lc[l]) {
-                        lc = l;
-                        P = rem == 0 ? 1 : rem + 2;
-                        found = true;
-                    } else if (!found) {
-                        rem -= cnt_lc[l];
-                    }
+                for (int m = 1; m <= kMaxWindowLevels; ++m) {
+                    const bool act = m <= lc && lcnt[m] > 0;
+                    bool bad;
+                    const int p = win_segments(N, cw[m - 1], cap[m - 1], M, bad);
+                    ok = ok && !(act && bad);
+                    need += act ? lcnt[m] * p : 0;
                 }
-                WinLevels wl = base;
-                wl.levels = lc;
-                int n_e = 0;
-#pragma unroll
-                for (int l = 0; l <= kMaxWindowLevels; ++l) n_e = l == lc ? ne_lc[l] : n_e;
-#pragma unroll
-                for (int m = 1; m <= kMaxWindowLevels; ++m) wl.n[m - 1] = (m <= lc && m <= LV) ? pl.cls[m] : 0;
-                float t = 3.0e38f;
-                int pm[kMaxWindowLevels];
-                if (found && i < ncand) t = plan_cost(P, n_e, wl, prm.cus, pm);
-                const int mine = i;
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const float ot = __shfl_xor(t, d, 64);
-                    const int oi = __shfl_xor(i, d, 64);
-                    if (ot < t || (ot == t && oi < i)) {
-                        t = ot;
-                        i = oi;
-                    }
-                }
-                if (t < best * 0.999f) {
-                    best = t;
-                    // the winning lane records its choice and its window segment counts
-                    if (mine == i) {
-                        pl.par[0] = P;
-                        pl.par[1] = lc;
-#pragma unroll
-                        for (int m = 0; m < kMaxWindowLevels; ++m) pl.par[2 + m] = pm[m];
-                    }
-                }
-            }
-        } else {
-            if (lane == 0) {
-                pl.par[0] = Pe;
-                pl.par[1] = Lc;
-#pragma unroll
-                for (int m = 0; m < kMaxWindowLevels; ++m) pl.par[2 + m] = pmax;
+                pl.need[lc - 1][b] = ok ? need : 0x7FFFFFFF;
             }
         }
-    }
-    __syncthreads();
-    const int Lc = pl.par[1];
-    // window heads above the kept level become exact
-    auto cls_of = [&](int bh) { const int m = level_of(bh); return (m == 0 || m > Lc) ? 0 : 1 + (Lc - m); };
-    int start = 0;   // first slot of the current class
-    for (int ci = 0; ci <= Lc; ++ci) {
-        int cnt = 0;
-        for (int bh = lo; bh < hi; ++bh) cnt += cls_of(bh) == ci ? 1 : 0;
-        int tot = 0;
-        const int r = block_exclusive_scan(cnt, pl.wave, tot);
-        int slot = start + r;
-        for (int bh = lo; bh < hi; ++bh)
-            if (cls_of(bh) == ci) hm[slot++] = bh;
-        start += tot;
-        if (tid == 0) pl.cls[ci] = tot;   // heads per class from here on
-    }
-    // the levels that ran, for the record (0 = exact)
-    if (wmax)
-        for (int bh = lo; bh < hi; ++bh) {
-            const int m = levp[bh];
-            flags[bh] = m > Lc ? 0 : m;
+        lds_barrier();
+        // 4. per (candidate, breakpoint): the smallest feasible breakpoint
+        if (nbmax > 0) {
+            // consecutive items belong to different candidates (an LDS atomic
+            // of a wave on one address is serialised)
+            for (int it = tid; it < ncand * nbmax; it += kThreads) {
+                const int b = small_div(it, ncand), i = it - b * ncand;
+                const int lc = pl.cand_lc[i];
+                if (lc >= 1 && b < pl.off[lc] && pl.need[lc - 1][b] <= pl.cand_fr[i])
+                    atomicMin(&pl.mkey[i], pl.bkey[b]);
+            }
         }
-    __syncthreads();
-    const int n_e = pl.cls[0];
+        lds_barrier();
+        // 5. the estimated makespan of each candidate, in full chunk steps
+        int lc = 0, P = 1;
+        int pmv[kMaxWindowLevels];
+        float t = 3.0e38f;
+#pragma unroll
+        for (int m = 0; m < kMaxWindowLevels; ++m) pmv[m] = 1;
+        if (tid < ncand) {
+            lc = pl.cand_lc[tid];
+            P = pl.cand_p[tid];
+            const int fr = pl.cand_fr[tid];
+            const int ne = nbh - pl.cum[lc];
+            const int nw = nbh - ne;   // window heads kept
+            float te = 0.f;
+            if (ne > 0)
+                te = P == 1 ? (float)N
+                            : 8.f * N * (1.f + kCostPass1) / (kSeg0Weight + 8 * (P - 1)) + (P - 2) * kCostLink;
+            float tw = 0.f;
+            if (nw > 0 && fr < nw) {
+                // fewer workgroups than window heads: one job per head, in rounds;
+                // with none free the window heads run after the exact ones
+                tw = fr > 0 ? (float)((nw + fr - 1) / fr) * N : te + N;
+            } else if (nw > 0) {
+                const float M = key_float(pl.mkey[tid]);
+#pragma unroll
+                for (int m = 1; m <= kMaxWindowLevels; ++m) {
+                    bool bad;
+                    const int p = win_segments(N, cw[m - 1], cap[m - 1], M, bad);
+                    if (m <= lc && lcnt[m] > 0) {
+                        pmv[m - 1] = p;
+                        const float f = win_job_cost(N, cw[m - 1], p);
+                        tw = f > tw ? f : tw;
+                    }
+                }
+            }
+            t = te > tw ? te : tw;
+            atomicMin(&pl.tmin, float_key(t));
+        }
+        lds_barrier();
+        if (tid < ncand && t <= key_float(pl.tmin) * 1.001f) atomicMin(&pl.win, tid);
+        lds_barrier();
+        if (tid == pl.win) {
+            pl.pe = P;
+            pl.lc = lc;
+#pragma unroll
+            for (int m = 0; m < kMaxWindowLevels; ++m) pl.pm[m] = pmv[m];
+        }
+    } else if (tid == 0) {
+        pl.pe = pmax;
+        pl.lc = LV;
+#pragma unroll
+        for (int m = 0; m < kMaxWindowLevels; ++m) pl.pm[m] = pmax;
+    }
+    lds_barrier();
+    const int Pe = uni(pl.pe), Lc = uni(pl.lc);
+    int pmr[kMaxWindowLevels], nl[kMaxWindowLevels];
+#pragma unroll
+    for (int m = 1; m <= kMaxWindowLevels; ++m) {
+        pmr[m - 1] = pl.pm[m - 1];
+        nl[m - 1] = m <= Lc ? lcnt[m] : 0;
+    }
+    const int n_e = nbh - pl.cum[Lc];
     const int n_w = nbh - n_e;
-    WinLevels wl = base;
-    wl.levels = Lc;
+    // 6. workgroups the window heads leave free go, one segment more per head,
+    //    to the heads of the levels whose jobs cost most (levels by job cost,
+    //    highest first, ties to the lower level; each takes what is left, up to
+    //    its head count): the makespan estimate stays, but far fewer jobs run at
+    //    it (job times vary from workgroup to workgroup, so the slowest of many
+    //    such jobs sets the end of the launch).  One thread per level.
+    if (tid < kMaxWindowLevels) {
+        int spare = cus - (n_e == 0 ? 0 : n_e * (Pe == 1 ? 1 : Pe - 1));
+        float f[kMaxWindowLevels];
+        bool el[kMaxWindowLevels];
 #pragma unroll
-    for (int m = 1; m <= kMaxWindowLevels; ++m) wl.n[m - 1] = m <= Lc ? pl.cls[1 + Lc - m] : 0;
-    if (tid == 0) {
-        // Workgroups the window heads leave free go, one segment more per head,
-        // to the heads of the levels whose jobs cost most: the makespan estimate
-        // stays, but far fewer jobs run at it (job times vary from workgroup to
-        // workgroup, so the slowest of many such jobs sets the end of the launch).
-        const int Pe0 = pl.par[0];
-        int spare = 0;
-        if (!prm.forced) {
-            spare = prm.cus - (n_e == 0 ? 0 : n_e * (Pe0 == 1 ? 1 : Pe0 - 1));
-            for (int m = 1; m <= Lc; ++m) spare -= pl.cls[1 + Lc - m] * pl.par[1 + m];
+        for (int m = 1; m <= kMaxWindowLevels; ++m) {
+            spare -= nl[m - 1] * pmr[m - 1];
+            el[m - 1] = nl[m - 1] > 0 && pmr[m - 1] + 1 <= cap[m - 1];
+            f[m - 1] = win_job_cost(N, cw[m - 1], pmr[m - 1]);
         }
-        for (int m = 0; m < kMaxWindowLevels; ++m) pl.kb[m] = 0;
-        for (int pass = 0; pass < Lc && spare > 0; ++pass) {
-            int bm = 0;
-            float bc = -1.f;
-            for (int m = 1; m <= Lc; ++m) {
-                const int nm = pl.cls[1 + Lc - m];
-                const int P = pl.par[1 + m];
-                int cap = N / (m * w);
-                cap = cap < 1 ? 1 : cap;
-                cap = cap < pmax ? cap : pmax;
-                if (nm == 0 || pl.kb[m - 1] != 0 || P + 1 > cap) continue;
-                const float f = ((float)N + (P - 1) * (kCostWarm * m * w)) / P;
-                if (f > bc) {
-                    bc = f;
-                    bm = m;
-                }
-            }
-            if (bm == 0) break;
-            const int nm = pl.cls[1 + Lc - bm];
-            const int k = nm < spare ? nm : spare;
-            pl.kb[bm - 1] = k;
-            spare -= k;
+        const int m = tid + 1;
+        bool mine = el[0];
+        float fm = f[0];
+#pragma unroll
+        for (int k = 1; k < kMaxWindowLevels; ++k) {
+            mine = k == tid ? el[k] : mine;
+            fm = k == tid ? f[k] : fm;
         }
-        int pw_max = 1;
-        for (int m = 1; m <= Lc; ++m) {
-            const int pm = pl.par[1 + m] + (pl.kb[m - 1] > 0 ? 1 : 0);
-            if (pl.cls[1 + Lc - m] > 0 && pm > pw_max) pw_max = pm;
-        }
-        pl.par[1] = pw_max;
+        int before = 0;
+#pragma unroll
+        for (int k = 1; k <= kMaxWindowLevels; ++k)
+            before += (el[k - 1] && (f[k - 1] > fm || (f[k - 1] == fm && k < m))) ? nl[k - 1] : 0;
+        int k = spare - before;
+        const int nm = m <= Lc ? pl.lcnt[m] : 0;
+        k = k < nm ? k : nm;
+        pl.kb[tid] = (forced || !mine || k < 0) ? 0 : k;
     }
-    __syncthreads();
-    const int Pe = pl.par[0];
-    int n_win_jobs = 0;
-    for (int m = 1; m <= Lc; ++m) n_win_jobs += pl.cls[1 + Lc - m] * pl.par[1 + m] + pl.kb[m - 1];
+    lds_barrier();
+    int kbr[kMaxWindowLevels];
+    int n_win_jobs = 0, pw = 1;
+#pragma unroll
+    for (int m = 1; m <= kMaxWindowLevels; ++m) {
+        kbr[m - 1] = pl.kb[m - 1];
+        n_win_jobs += nl[m - 1] * pmr[m - 1] + kbr[m - 1];
+        const int p = pmr[m - 1] + (kbr[m - 1] > 0 ? 1 : 0);
+        pw = (nl[m - 1] > 0 && p > pw) ? p : pw;
+    }
+    // 7. rank the heads by class (exact heads with the levels above Lc, then
+    //    levels Lc, .., 1), each class in head order: rounds of one head per
+    //    thread, ranks inside a wave from ballots; record the levels that ran
+    //    (0 = exact)
+    int* const hm = in_lds ? pl.hmap : head_map;
+    int cst[kMaxWindowLevels + 1];   // next free slot per class
+    cst[0] = 0;
+#pragma unroll
+    for (int c = 1; c <= kMaxWindowLevels; ++c) cst[c] = n_e + (c <= Lc ? n_w - pl.cum[Lc - c + 1] : 0);
+    for (int r0 = 0; r0 < nbh; r0 += kThreads) {
+        const int bh = r0 + tid;
+        const bool valid = bh < nbh;
+        const int m = (valid && wmax) ? (in_lds ? pl.lev[bh] : flags[bh]) : 0;
+        const int c = (m == 0 || m > Lc) ? 0 : 1 + Lc - m;
+        int rank = 0;
+        for (int cc = 0; cc <= Lc; ++cc) {
+            const unsigned long long mask = __ballot(valid && c == cc);
+            if (lane == 0) pl.rc[wv][cc] = __popcll(mask);
+            if (c == cc)
+                rank = __builtin_amdgcn_mbcnt_hi((unsigned)(mask >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0u));
+        }
+        lds_barrier();
+        int before = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < kThreads / 64; ++w2) before += w2 < wv ? pl.rc[w2][c] : 0;
+        if (valid) {
+            int slot = cst[0];
+#pragma unroll
+            for (int k = 1; k <= kMaxWindowLevels; ++k) slot = k == c ? cst[k] : slot;
+            if (in_lds)
+                pl.hmap[slot + before + rank] = bh;
+            else
+                gstore(head_map + slot + before + rank, bh);
+            if (wmax) gstore(flags + bh, m > Lc ? 0 : m);
+        }
+        if (r0 + kThreads < nbh) {
+            // the next round's heads come after this round's in every class
+            for (int cc = 0; cc <= Lc; ++cc) {
+                int n = 0;
+#pragma unroll
+                for (int w2 = 0; w2 < kThreads / 64; ++w2) n += pl.rc[w2][cc];
+#pragma unroll
+                for (int k = 0; k <= kMaxWindowLevels; ++k) cst[k] += k == cc ? n : 0;
+            }
+        }
+        lds_barrier();
+    }
     const int g_win = n_e + (Pe >= 3 ? n_e * (Pe - 2) : 0);
     const int g_chain = g_win + n_win_jobs;
     const int g_p3 = g_chain + (Pe >= 3 ? 4 * n_e : 0);
     const int n_jobs = g_p3 + (Pe >= 2 ? n_e * (Pe - 1) : 0);
     if (tid == 0) {
-        FwdPlan* const fp = uni(prm.plan);
-        fp->P_e = Pe;
-        fp->P_w = pl.par[1];
-        fp->n_exact = n_e;
-        fp->n_window = n_w;
-        fp->n_jobs = n_jobs;
+        gstore(&fp->P_e, Pe);
+        gstore(&fp->P_w, pw);
+        gstore(&fp->n_exact, n_e);
+        gstore(&fp->n_window, n_w);
+        gstore(&fp->n_jobs, n_jobs);
     }
-    // 3. the job list, one job per thread (segment bounds of exact heads once)
-    const int w0 = prm.forced ? 8 : kSeg0Weight;
+    // 8. the job list, one job per thread (segment bounds of exact heads once)
+    const int w0 = forced ? 8 : kSeg0Weight;
     const long long den = w0 + 8 * (Pe - 1);
     for (int p = tid; p <= Pe; p += kThreads)
         pl.bound[p] = p <= 0 ? 0 : p >= Pe ? N : seg_bound(w0 + 8 * (p - 1), den, N);
     __syncthreads();
-    const bool has_h0 = prm.h0 != nullptr, has_ht = prm.ht != nullptr;
     const int dst_last = has_ht ? DST_HT : DST_NONE;
     const int init0 = has_h0 ? INIT_H0 : INIT_ZERO;
-    TaskRec* const jobs = uni(prm.jobs);
     for (int j = tid; j < n_jobs; j += kThreads) {
         if (j < n_e) {   // segment 0 (or the whole sequence)
             const int bh = hm[j];
@@ -1206,16 +1257,31 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
             put_job(jobs, j, hm[e], p, pl.bound[p], pl.bound[p + 1], pl.bound[p + 1], MODE_PASS1,
                     INIT_ZERO, DST_TRANSITION);
         } else if (j < g_chain) {   // window segments, level by level (longest first), head-major
-            int jw = j - g_win, hbase = n_e, m = Lc;
-            for (; m > 1; --m) {
-                const int nm = pl.cls[1 + Lc - m];   // heads of level m
-                const int nj = nm * pl.par[1 + m] + pl.kb[m - 1];
-                if (jw < nj) break;
-                jw -= nj;
-                hbase += nm;
+            int jw = j - g_win, hbase = n_e, m = 1;
+            bool fnd = false;
+#pragma unroll
+            for (int mm = kMaxWindowLevels; mm >= 2; --mm) {
+                if (mm <= Lc && !fnd) {
+                    const int nj = nl[mm - 1] * pmr[mm - 1] + kbr[mm - 1];
+                    if (jw < nj) {
+                        m = mm;
+                        fnd = true;
+                    } else {
+                        jw -= nj;
+                        hbase += nl[mm - 1];
+                    }
+                }
+            }
+            int Pm = pmr[0], kb = kbr[0];
+            float c = cw[0];
+#pragma unroll
+            for (int mm = 2; mm <= kMaxWindowLevels; ++mm) {
+                Pm = mm == m ? pmr[mm - 1] : Pm;
+                kb = mm == m ? kbr[mm - 1] : kb;
+                c = mm == m ? cw[mm - 1] : c;
             }
             // the first kb heads of the level have one segment more
-            const int Pm = pl.par[1 + m], kb = pl.kb[m - 1], W = m * w;
+            const int W = m * w;
             int P, r, p;
             if (jw < kb * (Pm + 1)) {
                 P = Pm + 1;
@@ -1226,8 +1292,7 @@ __device__ __noinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
                 r = kb + (jw - kb * (Pm + 1)) / Pm;
                 p = (jw - kb * (Pm + 1)) % Pm;
             }
-            const float c = kCostWarm * W;
-            const int sb = win_bound(p, P, N, c, prm.forced != 0), e = win_bound(p + 1, P, N, c, prm.forced != 0);
+            const int sb = win_bound(p, P, N, c, forced != 0), e = win_bound(p + 1, P, N, c, forced != 0);
             const int cb = sb - W > 0 ? sb - W : 0;
             put_job(jobs, j, hm[hbase + r], p, cb, sb, e, MODE_FULL,
                     (cb == 0 && has_h0) ? INIT_H0 : INIT_ZERO, p == P - 1 ? dst_last : DST_NONE);
