@@ -274,6 +274,59 @@ def test_window_levels_mixed(gdn):
     assert infos[4]["n_window"] >= infos[1]["n_window"]
 
 
+def test_planner_eight_levels(gdn):
+    """Window heads of all eight levels (w = 8 chunks) and exact heads in one
+    automatic call with window_levels = 8 and a ragged tail: the plan keeps the
+    levels up to some cutoff, every job is handed out, and the output agrees with
+    the oracle.  Exercises the planner's candidate and breakpoint tables and the
+    spare-workgroup boost across many levels."""
+    import torch
+    say("case planner with eight window levels, B=1 T=64*72+13 H=12")
+    B, T, H = 1, 64 * 72 + 13, 12
+    x = inputs.generate(B=B, T=T, H=H, h0_std=0.02, seed=41)
+    want = [1, 2, 3, 4, 5, 6, 7, 8, 0, 0, 1, 2]
+    for h, m in enumerate(want):
+        # constant gates with a total decay of 18.7 over m windows of 8 chunks:
+        # beyond log(2^-24) = -16.64 over m*8 chunks (also for the windows that
+        # end in the 13-token tail), not over (m-1)*8 chunks
+        x.g[:, :, h] = -18.7 / (m * 8 * 64) if m else -1e-3
+    lev = _window_levels(x.g, levels=8)
+    assert lev.tolist() == want, lev.tolist()
+    t = to_gpu(x)
+    ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(B, T, H), dtype=torch.uint8, device="cuda")
+    o, ht = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], workspace=ws,
+                              window_levels=8)
+    info = gdn.gdn_chunk_fwd_plan_info(B, T, H, workspace=ws, window_levels=8)
+    say(f"  plan {info}")
+    _check_plan_levels(info, lev, B * H)
+    assert info["handed_out"] >= info["n_jobs"]
+    oref, href = oracle.fwd(x.q, x.k, x.v, x.g, x.beta, x.h0)
+    _check(to_np(o), to_np(ht), oref, href, TOL_BF16, label="eight levels")
+
+
+def test_forced_split_600_heads(gdn):
+    """More heads than the planner has threads (600 > 512): the ranking of the
+    heads by class runs in two rounds.  Forced split into 3 segments, exact and
+    window heads mixed, many jobs per workgroup."""
+    import torch
+    say("case forced split, 600 heads x 3 segments")
+    B, T, H = 2, 64 * 4 + 7, 300
+    x = inputs.generate(B=B, T=T, H=H, gate="mixed", strong_frac=0.5, h0_std=0.02, seed=43)
+    opts = dict(split_mode=2, n_segments=3, window_chunks=2)
+    t = to_gpu(x)
+    ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(B, T, H, **opts), dtype=torch.uint8, device="cuda")
+    o, ht = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], workspace=ws, **opts)
+    info = gdn.gdn_chunk_fwd_plan_info(B, T, H, workspace=ws, **opts)
+    say(f"  plan {info}")
+    assert info["error"] == 0 and info["P_exact"] == 3
+    assert info["n_exact"] + info["n_window"] == B * H and info["n_window"] > 0 and info["n_exact"] > 0
+    # exact head: segment 0, one pass-1 run, 4 chain jobs, 2 pass-3 runs; window head: 3 runs
+    assert info["n_jobs"] == info["n_exact"] * 8 + info["n_window"] * 3
+    assert info["handed_out"] >= info["n_jobs"]
+    oref, href = oracle.fwd(x.q, x.k, x.v, x.g, x.beta, x.h0)
+    _check(to_np(o), to_np(ht), oref, href, TOL_BF16, label="600 heads x 3 segments")
+
+
 def _varlen_case(gdn, lens, H, dtype, seed, tol):
     import torch
     T = int(sum(lens))
