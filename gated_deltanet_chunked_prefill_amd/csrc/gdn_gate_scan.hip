@@ -90,7 +90,8 @@ __global__ __launch_bounds__(256) void fwd_sums_kernel(const float* __restrict__
 // m = 1 the sums are those of window_flags_kernel, term for term.
 constexpr int kWinGroup = 8;
 constexpr int kWinMaxSums = 8192;   // LDS floats for the group's chunk sums
-__global__ __launch_bounds__(256) void fwd_window_kernel(const float* __restrict__ sums, int H, int N, int w,
+constexpr int kWinThreads = 512;    // one pass over the (head, length, end) triples of 32 heads
+__global__ __launch_bounds__(kWinThreads) void fwd_window_kernel(const float* __restrict__ sums, int H, int N, int w,
                                                          int levels, int* __restrict__ wmax) {
     __shared__ float s_sum[kWinMaxSums];
     const int grp = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(256) void fwd_window_kernel(const float* __restrict
     const int hpass = kWinMaxSums / nc < H ? kWinMaxSums / nc : H;   // >= 1: nc <= kWinMaxSums
     for (int h0 = 0; h0 < H; h0 += hpass) {
         const int hn = H - h0 < hpass ? H - h0 : hpass;
-        for (int i = tid; i < nc * hn; i += 256) {
+        for (int i = tid; i < nc * hn; i += kWinThreads) {
             const int c = cs + i / hn, hl = i % hn;
             s_sum[(c - cs) * hpass + hl] = sums[((size_t)b * N + c) * H + h0 + hl];
         }
@@ -110,13 +111,17 @@ __global__ __launch_bounds__(256) void fwd_window_kernel(const float* __restrict
         // one thread per (head, length, window end); the kWinGroup ends of a
         // (head, length) pair sit in adjacent lanes and are reduced by shuffles
         const int ntask = hn * levels * kWinGroup;
-        for (int x0 = 0; x0 < ntask; x0 += 256) {
+        for (int x0 = 0; x0 < ntask; x0 += kWinThreads) {
             const int x = x0 + tid, e = x % kWinGroup, pr = x / kWinGroup;
             const int hl = pr % hn, m = 1 + pr / hn, W = m * w, c = c0 + e;
             float acc = -INFINITY;
             if (x < ntask && c < c1 && c >= W - 1) {
+                // summed left to right; the unrolled loop issues the LDS reads
+                // ahead of the dependent additions
                 acc = 0.f;
-                for (int j = c - W + 1; j <= c; ++j) acc += s_sum[(j - cs) * hpass + hl];
+                const float* src = s_sum + (c - W + 1 - cs) * hpass + hl;
+#pragma unroll 8
+                for (int j = 0; j < W; ++j) acc += src[j * hpass];
             }
 #pragma unroll
             for (int d = 1; d < kWinGroup; d <<= 1) {
@@ -182,7 +187,7 @@ hipError_t launch_fwd_windows(const float* sums, int B, int T, int H, int w, int
                               hipStream_t s) {
     const int N = (T + kChunk - 1) / kChunk;
     dim3 grid(window_groups(T), B);
-    hipLaunchKernelGGL(fwd_window_kernel, grid, dim3(256), 0, s, sums, H, N, w, levels, wmax);
+    hipLaunchKernelGGL(fwd_window_kernel, grid, dim3(kWinThreads), 0, s, sums, H, N, w, levels, wmax);
     return hipGetLastError();
 }
 hipError_t launch_window_flags(const float* chunk_sums, int B, int T, int H, int w, float log_eps,
