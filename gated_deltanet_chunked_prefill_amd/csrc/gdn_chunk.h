@@ -36,8 +36,9 @@ struct Smem {
     float e_vec[NP][kChunk];   // Gamma_C / Gamma_r
     float gc[NP][4];           // [0] Gamma_C
     float pscr[4][4][kChunk];  // per prep wave: gamma, exp(gamma - gC/2), exp(gC/2 - gamma), beta
-    int islot[4];              // workgroup-wide scalars: [0] job index
+    int islot[4];              // workgroup-wide scalars: [0] job index, [1] job count
     float fslot[4];            // [0] exp(sum of g over a segment)
+    int jrec[8];               // split forward: the workgroup's first job, planned in the workgroup
 };
 
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x3f70); }   // vmcnt(0)

@@ -719,45 +719,66 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_kernel(FwdParams prm) {
     }
 }
 
+// Per-head tables of the planner live in LDS up to this many heads (always, for
+// the automatic split, which needs B*H < CUs/2), in the workspace beyond.
+constexpr int kPlanHeads = 4096;
+
 template <typename T>
-__device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm);
+__device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm, bool publish);
 
 // Persistent workgroups of the split forward: take jobs until the list is empty.
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_queue_kernel(FwdParams prm) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     Smem<T>& sm = *reinterpret_cast<Smem<T>*>(smem_raw);
-    // one workgroup writes the plan and the job list, then releases the others
-    // (the ready word, cleared by the preceding launch, becomes n_jobs + 1; the
-    // job records are written back before it and read with device-coherent loads)
+    // The plan is a deterministic function of the launch's inputs.  With the
+    // per-head tables in LDS every workgroup plans for itself and starts its
+    // first job (its own index) at once; workgroup 0 also writes the job list
+    // for the jobs handed out later and releases it through the ready word
+    // (cleared by the preceding launch, it becomes n_jobs + 1; the records are
+    // written back before it and read with device-coherent loads).  With more
+    // heads than the LDS tables hold, workgroup 0 plans alone in the workspace
+    // and the others wait for the list.
     int* const ready = &prm.plan->ready;
-    // the first workgroup to arrive plans (the dispatch order of workgroups is
-    // not their index order)
-    if (threadIdx.x == 0)
-        sm.islot[2] = __hip_atomic_fetch_add(&prm.plan->ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (uni(sm.islot[2]) == 0) {
-        plan_wg<T>(prm, sm);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __syncthreads();
-        if (threadIdx.x == 0)
-            __hip_atomic_store(ready, prm.plan->n_jobs + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int* const err = &prm.plan->error;
+    const bool local = uni(prm.B) * uni(prm.H) <= kPlanHeads;
+    const bool publish = blockIdx.x == 0;
+    if (local || publish) {
+        plan_wg<T>(prm, sm, publish);
+        if (publish) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __syncthreads();
+            if (threadIdx.x == 0)
+                __hip_atomic_store(ready, sm.islot[1] + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     } else if (threadIdx.x < 64) {
-        wait_published(ready, 1, &prm.plan->error);
+        wait_published(ready, 1, err);
+        if (threadIdx.x == 0)
+            sm.islot[1] = __hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - 1;
     }
-    if (threadIdx.x == 0)
-        sm.islot[1] = __hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - 1;
     __syncthreads();
     const int n_jobs = uni(sm.islot[1]);
     // the first job of every workgroup is its index; later ones come from the counter
     int j = blockIdx.x;
+    bool first = true, listed = !local || publish;   // listed: the job list is known to be written
     for (;; ) {
         if (j >= n_jobs) break;
-        // job records read with device-coherent vector loads (written this launch)
-        const int* const jr = reinterpret_cast<const int*>(prm.jobs + j);
         int f[8];
+        if (first && local) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = uni(__hip_atomic_load(jr + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            for (int i = 0; i < 8; ++i) f[i] = uni(sm.jrec[i]);
+        } else {
+            if (!listed) {
+                if (threadIdx.x < 64) wait_published(ready, 1, err);
+                __syncthreads();
+                listed = true;
+            }
+            // job records read with device-coherent vector loads (written this launch)
+            const int* const jr = reinterpret_cast<const int*>(prm.jobs + j);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f[i] = uni(__hip_atomic_load(jr + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        }
+        first = false;
         const Task tk{f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]};
         if (tk.mode == MODE_CHAIN) {
             if (wave_id() < 4)
@@ -836,15 +857,26 @@ __device__ __forceinline__ void gstore(V* p, const V& v) {
     *(__attribute__((address_space(1))) V*)p = v;
 }
 
-__device__ __forceinline__ void put_job(TaskRec* jobs, int j, int bh, int seg, int cb, int co, int ce,
-                                        int mode, int init, int dst) {
+// Job j: into the job list when publishing, and into the workgroup's LDS slot
+// when it is the workgroup's first job.
+__device__ __forceinline__ void put_job(TaskRec* jobs, int* jrec, bool publish, int j, int bh, int seg, int cb,
+                                        int co, int ce, int mode, int init, int dst) {
     using i32x4 = int __attribute__((ext_vector_type(4)));
     static_assert(sizeof(TaskRec) == 2 * sizeof(i32x4), "job record layout");
     // the record's fields in declaration order, as two 16-byte stores
     const i32x4 lo = {bh, seg, cb, co}, hi = {ce, mode, init, dst};
-    i32x4* const dst4 = reinterpret_cast<i32x4*>(jobs + j);
-    gstore(dst4, lo);
-    gstore(dst4 + 1, hi);
+    if (publish) {
+        i32x4* const dst4 = reinterpret_cast<i32x4*>(jobs + j);
+        gstore(dst4, lo);
+        gstore(dst4 + 1, hi);
+    }
+    if (j == (int)blockIdx.x) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            jrec[i] = lo[i];
+            jrec[4 + i] = hi[i];
+        }
+    }
 }
 
 __device__ int seg_bound(long long num, long long den, int N) {
@@ -870,9 +902,6 @@ __device__ int win_bound(int p, int P, int N, float c, bool forced) {
 }
 
 // Planner scratch in the workgroup's LDS (used before any job runs).
-// Per-head tables of the planner live in LDS up to this many heads (always, for
-// the automatic split, which needs B*H < CUs/2), in the workspace beyond.
-constexpr int kPlanHeads = 4096;
 constexpr int kMaxBp = kMaxWindowLevels * kCandP;   // job-cost breakpoints: (level, P <= 32)
 
 struct PlanLds {
@@ -903,10 +932,13 @@ __device__ __forceinline__ int small_div(int a, int b) {
     return (int)(((float)a + 0.5f) * __builtin_amdgcn_rcpf((float)b));
 }
 
-// The planner, run by the first workgroup of the persistent launch to arrive,
-// before any job.  The other workgroups wait for it, so every step is a short
-// parallel pass with small code (it runs once per launch, from a cold
-// instruction cache).
+// The planner, run by every workgroup of the persistent launch before its first
+// job (by workgroup 0 alone when the per-head tables exceed the LDS), with the
+// same result in each: it is on every workgroup's path to its first job, so
+// every step is a short parallel pass with small code (it runs once per
+// launch, from a cold instruction cache).  Workgroup 0 (`publish`) also writes
+// the job list, the per-head levels and the plan record; every workgroup keeps
+// its own first job in LDS.
 //
 // Candidates (Lc, P): window levels above Lc run as exact heads, exact heads
 // take P segments.  Per Lc (from the highest level down, only where level
@@ -920,8 +952,8 @@ __device__ __forceinline__ int small_div(int a, int b) {
 // candidate within 0.1 % of the smallest wins (fewer segments, more window
 // heads on near-ties).
 template <typename T>
-__device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
-    static_assert(sizeof(PlanLds) <= sizeof(Smem<T>), "planner scratch exceeds the LDS");
+__device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm, bool publish) {
+    static_assert(sizeof(PlanLds) <= offsetof(Smem<T>, islot), "planner scratch overlaps the job slots");
     PlanLds& pl = *reinterpret_cast<PlanLds*>(&sm);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int B = uni(prm.B), H = uni(prm.H), nbh = B * H, N = uni(prm.N), pmax = uni(prm.P), w = uni(prm.w);
@@ -963,7 +995,7 @@ __device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
 #pragma unroll
             for (int m = kMaxWindowLevels; m >= 1; --m)
                 if (m <= LV && N >= m * w && key_float(key[m - 1]) <= log_eps) lev = m;
-            if (maxwin) gstore(maxwin + bh, key_float(key[0]));
+            if (maxwin && publish) gstore(maxwin + bh, key_float(key[0]));
             if (in_lds)
                 pl.lev[bh] = lev;
             else
@@ -1212,7 +1244,7 @@ __device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
                 pl.hmap[slot + before + rank] = bh;
             else
                 gstore(head_map + slot + before + rank, bh);
-            if (wmax) gstore(flags + bh, m > Lc ? 0 : m);
+            if (wmax && publish) gstore(flags + bh, m > Lc ? 0 : m);
         }
         if (r0 + kThreads < nbh) {
             // the next round's heads come after this round's in every class
@@ -1230,14 +1262,16 @@ __device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
     const int g_chain = g_win + n_win_jobs;
     const int g_p3 = g_chain + (Pe >= 3 ? 4 * n_e : 0);
     const int n_jobs = g_p3 + (Pe >= 2 ? n_e * (Pe - 1) : 0);
-    if (tid == 0) {
+    if (tid == 0) sm.islot[1] = n_jobs;
+    if (tid == 0 && publish) {
         gstore(&fp->P_e, Pe);
         gstore(&fp->P_w, pw);
         gstore(&fp->n_exact, n_e);
         gstore(&fp->n_window, n_w);
         gstore(&fp->n_jobs, n_jobs);
     }
-    // 8. the job list, one job per thread (segment bounds of exact heads once)
+    // 8. the job list, one job per thread (segment bounds of exact heads once);
+    //    a workgroup that does not publish forms only its own first job
     const int w0 = forced ? 8 : kSeg0Weight;
     const long long den = w0 + 8 * (Pe - 1);
     for (int p = tid; p <= Pe; p += kThreads)
@@ -1246,15 +1280,16 @@ __device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
     const int dst_last = has_ht ? DST_HT : DST_NONE;
     const int init0 = has_h0 ? INIT_H0 : INIT_ZERO;
     for (int j = tid; j < n_jobs; j += kThreads) {
+        if (!publish && j != (int)blockIdx.x) continue;   // only the workgroup's own first job
         if (j < n_e) {   // segment 0 (or the whole sequence)
             const int bh = hm[j];
             if (Pe == 1)
-                put_job(jobs, j, bh, 0, 0, 0, N, MODE_FULL, init0, dst_last);
+                put_job(jobs, sm.jrec, publish, j, bh, 0, 0, 0, N, MODE_FULL, init0, dst_last);
             else
-                put_job(jobs, j, bh, 0, 0, 0, pl.bound[1], MODE_FULL, init0, DST_HS_NEXT);
+                put_job(jobs, sm.jrec, publish, j, bh, 0, 0, 0, pl.bound[1], MODE_FULL, init0, DST_HS_NEXT);
         } else if (j < g_win) {   // pass-1 of segment p, segment-major
             const int p = 1 + (j - n_e) / n_e, e = (j - n_e) % n_e;
-            put_job(jobs, j, hm[e], p, pl.bound[p], pl.bound[p + 1], pl.bound[p + 1], MODE_PASS1,
+            put_job(jobs, sm.jrec, publish, j, hm[e], p, pl.bound[p], pl.bound[p + 1], pl.bound[p + 1], MODE_PASS1,
                     INIT_ZERO, DST_TRANSITION);
         } else if (j < g_chain) {   // window segments, level by level (longest first), head-major
             int jw = j - g_win, hbase = n_e, m = 1;
@@ -1294,14 +1329,14 @@ __device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm) {
             }
             const int sb = win_bound(p, P, N, c, forced != 0), e = win_bound(p + 1, P, N, c, forced != 0);
             const int cb = sb - W > 0 ? sb - W : 0;
-            put_job(jobs, j, hm[hbase + r], p, cb, sb, e, MODE_FULL,
+            put_job(jobs, sm.jrec, publish, j, hm[hbase + r], p, cb, sb, e, MODE_FULL,
                     (cb == 0 && has_h0) ? INIT_H0 : INIT_ZERO, p == P - 1 ? dst_last : DST_NONE);
         } else if (j < g_p3) {   // chain, one job per 32-column block
             const int e = (j - g_chain) / 4, cb = (j - g_chain) % 4;
-            put_job(jobs, j, hm[e], 1, cb, 0, Pe - 1, MODE_CHAIN, 0, 0);
+            put_job(jobs, sm.jrec, publish, j, hm[e], 1, cb, 0, Pe - 1, MODE_CHAIN, 0, 0);
         } else {   // pass-3 of segment p, segment-major
             const int p = 1 + (j - g_p3) / n_e, e = (j - g_p3) % n_e;
-            put_job(jobs, j, hm[e], p, pl.bound[p], pl.bound[p], pl.bound[p + 1], MODE_FULL,
+            put_job(jobs, sm.jrec, publish, j, hm[e], p, pl.bound[p], pl.bound[p], pl.bound[p + 1], MODE_FULL,
                     INIT_HS_WAIT, p == Pe - 1 ? dst_last : DST_NONE);
         }
     }

@@ -39,8 +39,7 @@ struct FwdPlan {
     int n_jobs;
     int next;          // next job to hand out (atomic counter)
     int error;         // set when a wait for another job's state ran out (never expected)
-    int ready;         // 1 once the plan and the job list are written
-    int ticket;        // arrival count of the persistent workgroups (the first to arrive plans)
+    int ready;         // job count + 1 once the job list is written
 };
 
 struct FwdParams {
