@@ -918,9 +918,9 @@ struct PlanLds {
     int tmin, win;                    // smallest estimated makespan (key) and the chosen candidate
     int rc[kThreads / 64][1 + kMaxWindowLevels];   // heads per wave and class in one round
     int cand_lc[kMaxCand], cand_p[kMaxCand], cand_fr[kMaxCand];   // candidate: cutoff, P, free workgroups
-    int mkey[kMaxCand];               // per candidate: smallest feasible window job cost (key)
     int bkey[kMaxBp];                 // breakpoints, level by level (levels with heads): job cost (key)
-    int need[kMaxWindowLevels][kMaxBp];   // [Lc-1][b]: workgroups the window heads need at breakpoint b
+    int need[kMaxWindowLevels][kMaxBp + 1];   // [Lc-1][b]: workgroups the window heads need at
+                                              // breakpoint b (rows padded: no bank conflicts)
     int lev[kPlanHeads];              // window level per head (0 = exact)
     int hmap[kPlanHeads];             // heads by class
 };
@@ -980,7 +980,6 @@ __device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm, bool 
         pl.tmin = 0x7FFFFFFF;
         pl.win = 0x7FFFFFFF;
     }
-    for (int i = tid; i < kMaxCand; i += kThreads) pl.mkey[i] = 0x7FFFFFFF;
     lds_barrier();
     // 1. window levels (talk summary, paragraph 5): a head is a window head of
     //    level m when its largest sum of g over m*w consecutive chunks is at
@@ -1058,7 +1057,6 @@ __device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm, bool 
             cbase[lc] = ncand;
             ncand += pl.cnt[lc];
         }
-        const int nbmax = off[kMaxWindowLevels];
         // 3. candidate i: its cutoff, P and free workgroups (one thread each);
         //    workgroups the window heads need at each breakpoint, per cutoff
         if (tid < ncand) {
@@ -1094,19 +1092,8 @@ __device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm, bool 
             }
         }
         lds_barrier();
-        // 4. per (candidate, breakpoint): the smallest feasible breakpoint
-        if (nbmax > 0) {
-            // consecutive items belong to different candidates (an LDS atomic
-            // of a wave on one address is serialised)
-            for (int it = tid; it < ncand * nbmax; it += kThreads) {
-                const int b = small_div(it, ncand), i = it - b * ncand;
-                const int lc = pl.cand_lc[i];
-                if (lc >= 1 && b < pl.off[lc] && pl.need[lc - 1][b] <= pl.cand_fr[i])
-                    atomicMin(&pl.mkey[i], pl.bkey[b]);
-            }
-        }
-        lds_barrier();
-        // 5. the estimated makespan of each candidate, in full chunk steps
+        // 4. per candidate (one thread each): the smallest feasible breakpoint of
+        //    its cutoff and the estimated makespan, in full chunk steps
         int lc = 0, P = 1;
         int pmv[kMaxWindowLevels];
         float t = 3.0e38f;
@@ -1128,7 +1115,17 @@ __device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm, bool 
                 // with none free the window heads run after the exact ones
                 tw = fr > 0 ? (float)((nw + fr - 1) / fr) * N : te + N;
             } else if (nw > 0) {
-                const float M = key_float(pl.mkey[tid]);
+                // the breakpoints of levels 1 .. lc; the one with all heads in
+                // one segment each is always feasible here (fr >= nw)
+                const int* const nd = pl.need[lc - 1];
+                const int nb = pl.off[lc];
+                int best = 0x7FFFFFFF;
+#pragma unroll 8
+                for (int b = 0; b < nb; ++b) {
+                    const int kk = pl.bkey[b];
+                    best = (nd[b] <= fr && kk < best) ? kk : best;
+                }
+                const float M = key_float(best);
 #pragma unroll
                 for (int m = 1; m <= kMaxWindowLevels; ++m) {
                     bool bad;
