@@ -1165,7 +1165,7 @@ __device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm, bool 
     }
     const int n_e = nbh - pl.cum[Lc];
     const int n_w = nbh - n_e;
-    // 6. workgroups the window heads leave free go, one segment more per head,
+    // 5. workgroups the window heads leave free go, one segment more per head,
     //    to the heads of the levels whose jobs cost most (levels by job cost,
     //    highest first, ties to the lower level; each takes what is left, up to
     //    its head count): the makespan estimate stays, but far fewer jobs run at
@@ -1208,7 +1208,7 @@ __device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm, bool 
         const int p = pmr[m - 1] + (kbr[m - 1] > 0 ? 1 : 0);
         pw = (nl[m - 1] > 0 && p > pw) ? p : pw;
     }
-    // 7. rank the heads by class (exact heads with the levels above Lc, then
+    // 6. rank the heads by class (exact heads with the levels above Lc, then
     //    levels Lc, .., 1), each class in head order: rounds of one head per
     //    thread, ranks inside a wave from ballots; record the levels that ran
     //    (0 = exact)
@@ -1267,7 +1267,7 @@ __device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm, bool 
         gstore(&fp->n_window, n_w);
         gstore(&fp->n_jobs, n_jobs);
     }
-    // 8. the job list, one job per thread (segment bounds of exact heads once);
+    // 7. the job list, one job per thread (segment bounds of exact heads once);
     //    a workgroup that does not publish forms only its own first job
     const int w0 = forced ? 8 : kSeg0Weight;
     const long long den = w0 + 8 * (Pe - 1);
