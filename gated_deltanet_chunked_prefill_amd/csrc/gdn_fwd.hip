@@ -723,6 +723,16 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_kernel(FwdParams prm) {
 // the automatic split, which needs B*H < CUs/2), in the workspace beyond.
 constexpr int kPlanHeads = 4096;
 
+// The persistent kernel's parameters read straight from the kernel-argument
+// segment (they are its only argument, at offset 0), with scalar loads.  The
+// kernel's own copy, which the job functions take by reference, sits in scratch
+// memory; reading that back would put a scratch round trip before the
+// planner's first loads.
+using KParams = const __attribute__((address_space(4))) FwdParams;
+__device__ __forceinline__ KParams& launch_params() {
+    return *(KParams*)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
 template <typename T>
 __device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm, bool publish);
 
@@ -741,7 +751,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_queue_kernel(FwdParams pr
     // and the others wait for the list.
     int* const ready = &prm.plan->ready;
     int* const err = &prm.plan->error;
-    const bool local = uni(prm.B) * uni(prm.H) <= kPlanHeads;
+    const bool local = launch_params().B * launch_params().H <= kPlanHeads;
     const bool publish = blockIdx.x == 0;
     if (local || publish) {
         plan_wg<T>(prm, sm, publish);
@@ -952,7 +962,9 @@ __device__ __forceinline__ int small_div(int a, int b) {
 // candidate within 0.1 % of the smallest wins (fewer segments, more window
 // heads on near-ties).
 template <typename T>
-__device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm, bool publish) {
+__device__ __forceinline__ void plan_wg(const FwdParams& prm_copy, Smem<T>& sm, bool publish) {
+    KParams& prm = launch_params();
+    (void)prm_copy;
     static_assert(sizeof(PlanLds) <= offsetof(Smem<T>, islot), "planner scratch overlaps the job slots");
     PlanLds& pl = *reinterpret_cast<PlanLds*>(&sm);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -968,6 +980,11 @@ __device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm, bool 
     TaskRec* const jobs = uni(prm.jobs);
     const bool has_h0 = prm.h0 != nullptr, has_ht = prm.ht != nullptr;
     const bool in_lds = nbh <= kPlanHeads;
+    // the group maxima of the thread's first head, loaded first: their latency
+    // (data another launch wrote) overlaps the set-up below
+    int key0[kMaxWindowLevels];
+#pragma unroll
+    for (int m = 0; m < kMaxWindowLevels; ++m) key0[m] = (wmax && m < LV && tid < nbh) ? wmax[(size_t)m * nbh + tid] : 0;
     if (tid <= kMaxWindowLevels) pl.lcnt[tid] = 0;
     if (tid < kMaxWindowLevels) {
         const int m = tid + 1;
@@ -989,7 +1006,8 @@ __device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm, bool 
         for (int bh = tid; bh < nbh; bh += kThreads) {
             int key[kMaxWindowLevels];
 #pragma unroll
-            for (int m = 0; m < kMaxWindowLevels; ++m) key[m] = m < LV ? wmax[(size_t)m * nbh + bh] : 0;
+            for (int m = 0; m < kMaxWindowLevels; ++m)
+                key[m] = bh == tid ? key0[m] : (m < LV ? wmax[(size_t)m * nbh + bh] : 0);
             int lev = 0;
 #pragma unroll
             for (int m = kMaxWindowLevels; m >= 1; --m)
