@@ -327,6 +327,31 @@ def test_forced_split_600_heads(gdn):
     _check(to_np(o), to_np(ht), oref, href, TOL_BF16, label="600 heads x 3 segments")
 
 
+def test_forced_split_4200_heads_global_tables(gdn):
+    """More heads than the planner's LDS tables hold (4200 > 4096): one
+    workgroup plans with its per-head tables in the workspace and the others
+    wait for the job list; 8400 jobs, nearly all taken from the list."""
+    import torch
+    say("case forced split, 4200 heads x 2 segments (planner tables in the workspace)")
+    B, T, H = 2, 64 * 2 + 48, 2100
+    x = inputs.generate(B=B, T=T, H=H, h0_std=0.02, seed=47)
+    # every other head decays by 25.6 per chunk (19.2 over the 48-token tail): a
+    # window head at w = 1
+    x.g[:, :, 0::2] = -0.4
+    opts = dict(split_mode=2, n_segments=2, window_chunks=1)
+    t = to_gpu(x)
+    ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(B, T, H, **opts), dtype=torch.uint8, device="cuda")
+    o, ht = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], workspace=ws, **opts)
+    info = gdn.gdn_chunk_fwd_plan_info(B, T, H, workspace=ws, **opts)
+    say(f"  plan {info}")
+    assert info["error"] == 0 and info["P_exact"] == 2
+    assert info["n_exact"] + info["n_window"] == B * H and info["n_window"] > 0 and info["n_exact"] > 0
+    # exact head: segment 0 and one pass-3 run; window head: 2 runs
+    assert info["n_jobs"] == 2 * B * H and info["handed_out"] >= info["n_jobs"]
+    oref, href = oracle.fwd(x.q, x.k, x.v, x.g, x.beta, x.h0)
+    _check(to_np(o), to_np(ht), oref, href, TOL_BF16, label="4200 heads x 2 segments")
+
+
 def _varlen_case(gdn, lens, H, dtype, seed, tol):
     import torch
     T = int(sum(lens))
