@@ -9,8 +9,11 @@ The arithmetic lives in ``gdn_oracle.c`` (token-by-token gated delta rule,
 back-propagation through time and a brute-force gate scan, all float64).  This
 module compiles it with gcc (OpenMP over heads) and calls it through ctypes.
 
-Parity pins for every function here are in ``tests/test_oracle_pins.py`` and
-``tests/test_oracle_backward.py``; none is "parity unpinned".
+Parity pins for every function here are in ``tests/test_oracle_pins.py``,
+``tests/test_oracle_backward.py`` and ``tests/test_oracle_kda.py``.  One part is
+"parity unpinned": in :func:`kda_fwd` (a reading; the pages do not print KDA's
+recurrence) the order of the per-channel decay and the delta correction matters only
+for keys that mix channels, and no value independent of the reading fixes it.
 """
 from __future__ import annotations
 
@@ -136,3 +139,37 @@ def gate_scan(g, chunk=64, window_chunks=8, log_eps=float(np.log(2.0 ** -24))):
     _load().gdn_oracle_gate_scan(_ptr(g), B, T, H, int(chunk), int(window_chunks), float(log_eps),
                                  _ptr(flags, _ip), _ptr(mx))
     return flags, mx
+
+
+def kda_fwd(q, k, v, g, beta, h0=None, scale=1.0):
+    """Token-by-token forward of the per-channel-decay variant (KDA), float64 numpy.
+
+    Reading (the pages name KDA as the sibling operator of Kimi's hybrid stack but
+    do not print its recurrence): the scalar decay of the gated delta rule becomes
+    one decay per key channel, applied to the state before the delta correction,
+
+        S_t = (I - beta_t k_t k_t^T) diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T,
+        o_t = scale * S_t^T q_t,
+
+    with S of shape [dk, dv] (rows = key channels), the layout of :func:`fwd`'s
+    states.  With g_t equal in every channel it is :func:`fwd`.
+
+    Shapes: q,k,g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H]; h0 [B,H,dk,dv] or None.
+    Returns (o [B,T,H,dv], ht [B,H,dk,dv]).  The loop over tokens runs in Python
+    (vectorised over batch and heads): for small cases.  Pinned in
+    ``tests/test_oracle_kda.py``."""
+    q, k, v, g, beta, h0 = map(_f64, (q, k, v, g, beta, h0))
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    assert k.shape == q.shape and g.shape == q.shape and v.shape[:3] == (B, T, H)
+    assert beta.shape == (B, T, H)
+    S = np.zeros((B, H, dk, dv)) if h0 is None else h0.copy()
+    o = np.zeros((B, T, H, dv))
+    for t in range(T):
+        kt, vt, bt = k[:, t], v[:, t], beta[:, t]          # [B,H,dk], [B,H,dv], [B,H]
+        S = np.exp(g[:, t])[..., None] * S                  # per-channel decay of the rows
+        kS = np.einsum("bhk,bhkv->bhv", kt, S)              # k_t^T S
+        S = S - bt[..., None, None] * kt[..., :, None] * kS[..., None, :]
+        S = S + bt[..., None, None] * kt[..., :, None] * vt[..., None, :]
+        o[:, t] = scale * np.einsum("bhkv,bhk->bhv", S, q[:, t])
+    return o, S
