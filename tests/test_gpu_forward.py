@@ -352,6 +352,27 @@ def test_forced_split_4200_heads_global_tables(gdn):
     _check(to_np(o), to_np(ht), oref, href, TOL_BF16, label="4200 heads x 2 segments")
 
 
+@pytest.mark.parametrize("opts", [dict(), dict(split_mode=2, n_segments=5)])
+def test_fp32_split(gdn, opts):
+    """fp32 inputs through the split forward (the persistent kernel's fp32
+    instantiation): exact and window heads, a ragged tail and an entering state,
+    automatic plan and a forced split into 5 segments."""
+    import torch
+    say(f"case fp32 split {opts}, B=1 T=64*40+17 H=4")
+    B, T, H = 1, 64 * 40 + 17, 4
+    x = inputs.generate(B=B, T=T, H=H, dtype="f32", gate="mixed", strong_frac=0.5, h0_std=0.05, seed=53)
+    t = to_gpu(x)
+    ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(B, T, H, **opts), dtype=torch.uint8, device="cuda")
+    o, ht = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], workspace=ws, scale=0.5,
+                              **opts)
+    info = gdn.gdn_chunk_fwd_plan_info(B, T, H, workspace=ws, **opts)
+    say(f"  plan {info}")
+    assert info["error"] == 0 and info["n_exact"] + info["n_window"] == B * H
+    assert info["P_exact"] > 1 or info["P_window"] > 1
+    oref, href = oracle.fwd(x.q, x.k, x.v, x.g, x.beta, x.h0, scale=0.5)
+    _check(to_np(o), to_np(ht), oref, href, TOL_F32, label=f"fp32 split {opts}")
+
+
 def _varlen_case(gdn, lens, H, dtype, seed, tol):
     import torch
     T = int(sum(lens))
