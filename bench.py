@@ -188,10 +188,34 @@ def bench_backward(torch, gdn, _lib, inputs, steps, warmup):
     ev.close()
     ms = (t1 - t0) * 1e3 / steps
     nbytes = B * T * H * BWD_BYTES_PER_TOKEN_HEAD + B * H * STATE_BYTES * 2
-    return {"workload": BWD_WORKLOAD, "B": B, "T": T, "H": H, "steps": steps, "warmup": warmup,
-            "ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3),
-            "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "kernel_ms": {kd: round(float(np.mean(t)), 4) for kd, t in per_kind.items()}}
+    res = {"workload": BWD_WORKLOAD, "B": B, "T": T, "H": H, "steps": steps, "warmup": warmup,
+           "ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3),
+           "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "kernel_ms": {kd: round(float(np.mean(t)), 4) for kd, t in per_kind.items()}}
+    # the forward of the same training shape (h0 given, ht returned)
+    o = torch.empty_like(v)
+    ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    fws = torch.empty(max(1, gdn.gdn_chunk_fwd_workspace_size(B, T, H)), dtype=torch.uint8, device=dev)
+
+    def fstep():
+        gdn.gdn_chunk_fwd(q, k, v, g, beta, h0, out=o, out_ht=ht, workspace=fws)
+
+    for _ in range(warmup):
+        fstep()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fstep()
+    torch.cuda.synchronize()
+    fms = (time.perf_counter() - t0) * 1e3 / steps
+    plan = gdn.gdn_chunk_fwd_plan_info(B, T, H, workspace=fws)
+    if plan["error"]:
+        raise SystemExit("bench.py: the split forward reported a failed wait (training shape)")
+    fbytes = algorithmic_bytes(B, T, H, True, True)
+    res["forward"] = {"ms_per_call": fms, "tokens_per_s": B * T / (fms * 1e-3), "algorithmic_bytes": fbytes,
+                      "hbm_frac": fbytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "plan": {k_: plan[k_] for k_ in ("P_exact", "P_window", "n_exact", "n_window", "n_jobs")}}
+    return res
 
 
 # packed variable-length batch (serving shape): 8 prompts of mixed lengths, 32768
@@ -250,6 +274,26 @@ def bench_varlen(torch, gdn, inputs, steps, warmup):
     return res
 
 
+def rep_stats(torch, step, reps, flush_bytes=0):
+    """Median and minimum (ms) of `reps` single calls, each bracketed by events
+    on the current stream (the stream the library launches on); with
+    flush_bytes > 0 a buffer of that size is written between calls (outside the
+    timed region) so that no input stays in the 256 MB MALL."""
+    buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda") if flush_bytes else None
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        if buf is not None:
+            buf.fill_(1.0)
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    del buf
+    return {"reps": reps, "median_ms": float(np.median(t)), "min_ms": float(np.min(t)),
+            "mean_ms": float(np.mean(t))}
+
+
 def cpu_baseline(x, tokens):
     """The fp64 oracle, as it stands, on the first `tokens` tokens of every head."""
     import oracle
@@ -260,9 +304,10 @@ def cpu_baseline(x, tokens):
     oracle.fwd(q, k, v, g, b, None, nthreads=threads)
     dt = time.perf_counter() - t0
     B, _, H, _ = x.q.shape
-    return {"value": B * tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": B * tokens / dt, "unit": "tokens/s", "cores": threads, "threads": threads,
+            "host_cores": oracle.default_threads(), "host_cpus_total": os.cpu_count(), "kind": "oracle",
             "sample": f"first {tokens} of {x.q.shape[1]} tokens, all {B * H} heads, fp64, "
-                      f"{dt:.2f} s wall"}
+                      f"{threads} OpenMP threads (one head each at a time), {dt:.2f} s wall"}
 
 
 def main():
@@ -270,6 +315,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=50,
+                    help="single calls timed one by one for the median and minimum, "
+                         "once plain and once with a 512 MiB write between calls")
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens per head of the CPU oracle sample (0 to skip)")
     ap.add_argument("--bwd-steps", type=int, default=5,
@@ -336,6 +384,12 @@ def main():
     for i in range(n):
         per_kind.setdefault(_lib.LAUNCH_KINDS[labels[i]], []).append(ev.elapsed_ms(2 * i, 2 * i + 1))
     ev.close()
+    # a wait that ran out inside a timed call would leave invalid outputs
+    plan_after = gdn.gdn_chunk_fwd_plan_info(B, T, H, workspace=ws)
+    if plan_after["error"]:
+        raise SystemExit("bench.py: the split forward reported a failed wait in a timed call")
+    timing = {"plain": rep_stats(torch, step, args.reps),
+              "mall_flushed": rep_stats(torch, step, args.reps, flush_bytes=512 * 2 ** 20)}
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tokens_per_s = B * T / (ms_per_step * 1e-3)
@@ -371,6 +425,7 @@ def main():
                      "algorithmic_bytes": nbytes,
                      "traffic_gbs": None if tr is None else traffic / (fwd_ms * 1e-3) / 1e9, "kernel_ms": kernel_ms,
                      "call_frac": nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "timing": timing,
     }
     if args.bwd_steps > 0 or args.varlen_steps > 0:
         del q, k, v, g, beta, o, ht, ws

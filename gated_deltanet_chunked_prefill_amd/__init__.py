@@ -65,6 +65,27 @@ def _dev(t, name, dtype=None):
     return t
 
 
+def _shape(t, name, shape, device):
+    """Raise ValueError unless tensor t (or None) has exactly `shape` and lives on
+    `device`: a tensor the library would index past its end never reaches it."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _workspace_arg(ws, device):
+    torch = _torch()
+    if ws is None:
+        return
+    _dev(ws, "workspace")
+    if ws.dtype != torch.uint8 or ws.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor")
+    _shape(ws, "workspace", ws.shape, device)
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -126,14 +147,25 @@ def gdn_chunk_fwd(q, k, v, g, beta, h0=None, scale=1.0, *, output_final_state=Tr
     _dev(k, "k", dt), _dev(v, "v", dt)
     _dev(g, "g", torch.float32), _dev(beta, "beta", torch.float32)
     _dev(h0, "h0", torch.float32)
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, T, H, d]")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
+    dev = q.device
+    _shape(k, "k", (B, T, H, dk), dev)
+    _shape(v, "v", (B, T, H, dv), dev)
+    _shape(g, "g", (B, T, H), dev)
+    _shape(beta, "beta", (B, T, H), dev)
+    _shape(h0, "h0", (B, H, dk, dv), dev)
     o = out if out is not None else torch.empty((B, T, H, dv), dtype=dt, device=q.device)
     _dev(o, "o", dt)
+    _shape(o, "out", (B, T, H, dv), dev)
     if out_ht is not None:
         ht = _dev(out_ht, "out_ht", torch.float32)
+        _shape(ht, "out_ht", (B, H, dk, dv), dev)
     else:
         ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if output_final_state else None
+    _workspace_arg(workspace, dev)
     opt = options(**opts)
     code = _dtype_code(q)
     if workspace is None:
@@ -146,6 +178,28 @@ def gdn_chunk_fwd(q, k, v, g, beta, h0=None, scale=1.0, *, output_final_state=Tr
                                  _ptr(o), _ptr(ht), B, T, H, dk, dv, code, float(scale),
                                  ctypes.byref(opt), _ptr(workspace), wsz, _stream(q.device)))
     return o, ht
+
+
+def _varlen_shapes(q, k, v, g, beta, cu_seqlens):
+    """Packed-batch shapes: q, k [T, H, dk] or [1, T, H, dk], v like q with dv,
+    g, beta q's shape without the last axis, cu_seqlens 1-D with S + 1 >= 2
+    entries, all on q's device.  Returns (T, H, dk, dv, S)."""
+    if q.dim() not in (3, 4) or (q.dim() == 4 and q.shape[0] != 1):
+        raise ValueError("q, k, v must be [T, H, d] or [1, T, H, d]")
+    T, H, dk = q.shape[-3], q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    dev = q.device
+    _shape(k, "k", q.shape, dev)
+    _shape(v, "v", tuple(q.shape[:-1]) + (dv,), dev)
+    _shape(g, "g", q.shape[:-1], dev)
+    _shape(beta, "beta", q.shape[:-1], dev)
+    if cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be 1-D")
+    _shape(cu_seqlens, "cu_seqlens", cu_seqlens.shape, dev)
+    S = cu_seqlens.numel() - 1
+    if S < 1:
+        raise ValueError("cu_seqlens needs at least two entries")
+    return T, H, dk, dv, S
 
 
 def gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None, scale=1.0, *,
@@ -163,15 +217,15 @@ def gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None, scale=1.0, *,
     _dev(g, "g", torch.float32), _dev(beta, "beta", torch.float32)
     _dev(cu_seqlens, "cu_seqlens", torch.int32)
     _dev(h0, "h0", torch.float32)
-    T, H, dk = q.shape[-3], q.shape[-2], q.shape[-1]
-    dv = v.shape[-1]
-    S = cu_seqlens.numel() - 1
-    if S < 1:
-        raise ValueError("cu_seqlens needs at least two entries")
+    T, H, dk, dv, S = _varlen_shapes(q, k, v, g, beta, cu_seqlens)
+    dev = q.device
+    _shape(h0, "h0", (S, H, dk, dv), dev)
     o = out if out is not None else torch.empty_like(v)
     _dev(o, "o", dt)
+    _shape(o, "out", v.shape, dev)
     if out_ht is not None:
         ht = _dev(out_ht, "out_ht", torch.float32)
+        _shape(ht, "out_ht", (S, H, dk, dv), dev)
     else:
         ht = torch.empty((S, H, dk, dv), dtype=torch.float32, device=q.device) if output_final_state else None
     _lib.check(lib.gdn_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
@@ -204,8 +258,19 @@ def gdn_chunk_bwd(q, k, v, g, beta, dout, h0=None, dht=None, scale=1.0, *, works
     _dev(k, "k", dt), _dev(v, "v", dt), _dev(dout, "dout", dt)
     _dev(g, "g", torch.float32), _dev(beta, "beta", torch.float32)
     _dev(h0, "h0", torch.float32), _dev(dht, "dht", torch.float32)
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, T, H, d]")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
+    dev = q.device
+    _shape(k, "k", (B, T, H, dk), dev)
+    _shape(v, "v", (B, T, H, dv), dev)
+    _shape(dout, "dout", (B, T, H, dv), dev)
+    _shape(g, "g", (B, T, H), dev)
+    _shape(beta, "beta", (B, T, H), dev)
+    _shape(h0, "h0", (B, H, dk, dv), dev)
+    _shape(dht, "dht", (B, H, dk, dv), dev)
+    _workspace_arg(workspace, dev)
     dq = torch.empty_like(q)
     dkk = torch.empty_like(k)
     dvv = torch.empty_like(v)
@@ -241,11 +306,12 @@ def gdn_chunk_bwd_varlen(q, k, v, g, beta, dout, cu_seqlens, h0=None, dht=None, 
     _dev(g, "g", torch.float32), _dev(beta, "beta", torch.float32)
     _dev(cu_seqlens, "cu_seqlens", torch.int32)
     _dev(h0, "h0", torch.float32), _dev(dht, "dht", torch.float32)
-    T, H, dk = q.shape[-3], q.shape[-2], q.shape[-1]
-    dv = v.shape[-1]
-    S = cu_seqlens.numel() - 1
-    if S < 1:
-        raise ValueError("cu_seqlens needs at least two entries")
+    T, H, dk, dv, S = _varlen_shapes(q, k, v, g, beta, cu_seqlens)
+    dev = q.device
+    _shape(dout, "dout", v.shape, dev)
+    _shape(h0, "h0", (S, H, dk, dv), dev)
+    _shape(dht, "dht", (S, H, dk, dv), dev)
+    _workspace_arg(workspace, dev)
     dq, dkk, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dg, db = torch.empty_like(g), torch.empty_like(beta)
     dh0 = torch.empty((S, H, dk, dv), dtype=torch.float32, device=q.device) if need_dh0 else None
@@ -269,6 +335,8 @@ def gdn_gate_scan(g, window_chunks=8, log_eps=DEFAULT_LOG_EPS):
     torch = _torch()
     lib = _lib.load()
     _dev(g, "g", torch.float32)
+    if g.dim() != 3:
+        raise ValueError("g must be [B, T, H]")
     B, T, H = g.shape
     flags = torch.empty((B, H), dtype=torch.int32, device=g.device)
     mx = torch.empty((B, H), dtype=torch.float32, device=g.device)

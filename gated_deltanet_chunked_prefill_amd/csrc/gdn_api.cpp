@@ -123,6 +123,8 @@ gdn_status check_options(const gdn_options& o, int N) {
     return GDN_OK;
 }
 
+constexpr long long kChunkRows = 64;   // tokens per chunk
+
 gdn_status check_shapes(int B, int T, int H, int dk, int dv, gdn_dtype dt) {
     if (B <= 0 || T <= 0 || H <= 0)
         return fail(GDN_ERR_INVALID_ARG, "B, T, H must be positive (got %d, %d, %d)", B, T, H);
@@ -131,6 +133,13 @@ gdn_status check_shapes(int B, int T, int H, int dk, int dv, gdn_dtype dt) {
     if (dt != GDN_F32 && dt != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
     if ((long long)B * T * H * 128 > (1LL << 40))
         return fail(GDN_ERR_INVALID_ARG, "tensor too large");
+    // The tile loaders address the 64 rows of one chunk of one head (stride
+    // H * 128 elements) with 32-bit per-lane byte offsets: reject head counts
+    // whose 64-row span does not fit.
+    const long long elem = dt == GDN_F32 ? 4 : 2;
+    if ((long long)kChunkRows * H * 128 * elem > (long long)INT32_MAX)
+        return fail(GDN_ERR_INVALID_ARG, "H = %d too large for %s I/O (at most %lld heads)", H,
+                    dt == GDN_F32 ? "float32" : "bfloat16", (long long)INT32_MAX / (kChunkRows * 128 * elem));
     return GDN_OK;
 }
 
@@ -191,9 +200,10 @@ BwdLayout bwd_layout(int B, int T, int H) {
     return L;
 }
 
-// Packed-sequence backward workspace: the chunk prefix, then states and state
+// Packed-sequence backward workspace: the chunk prefix and the sequence bounds
+// (cu_seqlens clamped to [0, T] and made non-decreasing), then states and state
 // gradients in per-head slots (cmax = ceil(T/64) + S bounds the chunks of all
-// sequences together).
+// sequences together, which holds because the bounded sequences are disjoint).
 struct BwdVarlenLayout {
     size_t cstart, hstore, dhstore, total;
     int cmax;
@@ -204,7 +214,7 @@ BwdVarlenLayout bwd_varlen_layout(int S, int T, int H) {
     L.cmax = num_chunks(T) + S;
     const size_t SS = 128 * 128;
     size_t off = 0;
-    L.cstart = off;  off += align_up(((size_t)S + 1) * sizeof(int32_t));
+    L.cstart = off;  off += align_up(2 * ((size_t)S + 1) * sizeof(int32_t));   // chunk prefix, then bounds
     L.hstore = off;  off += align_up((size_t)H * (L.cmax + S) * SS * sizeof(uint16_t));   // bf16
     L.dhstore = off; off += align_up((size_t)H * L.cmax * SS * sizeof(uint16_t));
     L.total = off;
@@ -507,6 +517,8 @@ gdn_status gdn_gate_scan(const float* g, int B, int T, int H, int window_chunks,
     if (B <= 0 || T <= 0 || H <= 0)
         return fail(GDN_ERR_INVALID_ARG, "B, T, H must be positive (got %d, %d, %d)", B, T, H);
     if (window_chunks < 1) return fail(GDN_ERR_INVALID_ARG, "window_chunks must be >= 1");
+    if ((long long)B * H > (long long)INT32_MAX || (long long)B * T * H > (1LL << 40))
+        return fail(GDN_ERR_INVALID_ARG, "B * H or B * T * H too large");
     if (!aligned4(g) || !aligned4(flags) || (max_window_logdecay && !aligned4(max_window_logdecay)))
         return fail(GDN_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
     if (((uintptr_t)workspace & 3u) != 0) return fail(GDN_ERR_INVALID_ARG, "workspace must be 4-byte aligned");

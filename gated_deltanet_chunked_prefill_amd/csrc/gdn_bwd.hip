@@ -246,7 +246,7 @@ __global__ __launch_bounds__(kDhThreads, 1) void gdn_bwd_dh_kernel(BwdParams prm
 // the stored-state pointers so that slot bh*(nch+1) + c (states) and bh*nch + c
 // (state gradients) address the sequence's own slots.
 __device__ __forceinline__ void varlen_bwd_params(BwdParams& p, int s, int h, size_t elem) {
-    const SeqSpan sp = seq_span(p.cu, p.cstart, p.T, s);
+    const SeqSpan sp = seq_span(p.cu, p.cstart, p.B, p.T, s);
     const long long rows = ((long long)sp.t0 - (long long)s * sp.len) * p.H;   // token-head rows
     const long long vb = rows * kDk * (long long)elem;                          // bytes of q, k, v rows
     p.q = (const char*)p.q + vb;
@@ -281,20 +281,34 @@ __global__ __launch_bounds__(kDhThreads, 1) void gdn_bwd_dh_varlen_kernel(BwdPar
         dh_prep_loop<T>(prm, sm, bh);
 }
 
-// Packed sequences: cstart[s] = chunks of sequences 0 .. s-1 (s = 0 .. B), one
-// workgroup, 256 sequences per round with a running carry.
+// Packed sequences, one workgroup, 256 bounds per round with running carries:
+// the bounds bnd[s] = max(0, clamp(cu[0]), .., clamp(cu[s])) (s = 0 .. B, a
+// prefix maximum, so sequence s = [bnd[s], bnd[s+1]) never overlaps another)
+// into cstart[B + 1 + s], and the chunk prefix cstart[s] = chunks of sequences
+// 0 .. s-1 (s = 0 .. B).
 __global__ __launch_bounds__(256) void seq_chunk_prefix_kernel(const int* __restrict__ cu, int B, int T,
                                                                int* __restrict__ cstart) {
     __shared__ int part[256];
+    __shared__ int bnd[257];
+    int* const bout = cstart + B + 1;
     const int tid = threadIdx.x;
-    int carry = 0;
-    for (int s0 = 0; s0 < B; s0 += 256) {
-        const int s = s0 + tid;
-        int nch = 0;
-        if (s < B) {
-            const int t0 = clamp_tok(cu[s], 0, T);
-            nch = (clamp_tok(cu[s + 1], t0, T) - t0 + 63) / 64;
+    int carry = 0, lastb = 0;   // chunks before this round; the bound before this round
+    for (int s0 = 0; s0 <= B; s0 += 256) {
+        const int s = s0 + tid;   // bound index; sequence s - 1 ends at bound s
+        part[tid] = s <= B ? clamp_tok(cu[s], 0, T) : 0;
+        __syncthreads();
+        for (int d = 1; d < 256; d <<= 1) {   // inclusive maximum scan
+            const int x = tid >= d ? part[tid - d] : 0;
+            __syncthreads();
+            part[tid] = part[tid] > x ? part[tid] : x;
+            __syncthreads();
         }
+        const int b = part[tid] > lastb ? part[tid] : lastb;
+        if (s <= B) bout[s] = b;
+        bnd[tid + 1] = b;
+        if (tid == 0) bnd[0] = lastb;
+        __syncthreads();
+        const int nch = (s >= 1 && s <= B) ? (bnd[tid + 1] - bnd[tid] + 63) / 64 : 0;
         part[tid] = nch;
         __syncthreads();
         for (int d = 1; d < 256; d <<= 1) {   // inclusive scan
@@ -303,8 +317,9 @@ __global__ __launch_bounds__(256) void seq_chunk_prefix_kernel(const int* __rest
             part[tid] += x;
             __syncthreads();
         }
-        if (s < B) cstart[s] = carry + part[tid] - nch;
+        if (s >= 1 && s <= B) cstart[s - 1] = carry + part[tid] - nch;
         carry += part[255];
+        lastb = bnd[256];
         __syncthreads();
     }
     if (tid == 0) cstart[B] = carry;

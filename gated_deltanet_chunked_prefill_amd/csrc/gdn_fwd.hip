@@ -692,7 +692,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_kernel(FwdParams prm) {
         // index s*len + t addresses token t0 + t (and, when the states are kept,
         // the state slot bh*(nch+1) + c addresses the sequence's own slots).
         const int s = (int)blockIdx.x / prm.H, h = (int)blockIdx.x % prm.H;
-        const SeqSpan sp = seq_span(prm.cu, prm.cstart, prm.T, s);
+        const SeqSpan sp = seq_span(prm.cu, prm.cstart, prm.B, prm.T, s);
         const long long shift = ((long long)sp.t0 - (long long)s * sp.len) * prm.H;   // token-head rows
         FwdParams p = prm;
         p.q = (const T*)prm.q + shift * kDk;

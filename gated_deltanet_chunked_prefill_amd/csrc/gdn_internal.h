@@ -79,24 +79,36 @@ struct FwdParams {
                        // [B+1] of the B sequences in a [1, T, H, d] batch; null otherwise
     int cmax;          // packed sequences: chunk slots per head, ceil(T/64) + B (bounds the
                        // chunks of all sequences together)
-    const int* cstart; // packed sequences with kept states: chunk prefix [B+1] (seq_span)
+    const int* cstart; // packed sequences with kept states: chunk prefix [B+1], then the
+                       // sequence bounds [B+1] (seq_span)
 };
 
-// Packed sequences: sequence s holds tokens [t0, t0 + len), t0 = cu[s] and
-// t0 + len = cu[s+1], both clamped to [0, T] (and the end to at least t0);
-// nch = ceil(len / 64) chunks; c0 = cstart[s], the chunks of the sequences before
-// it (its first chunk in a numbering of all chunks of the batch), when the
-// chunk prefix cstart is given.
+// Packed sequences: sequence s holds tokens [t0, t0 + len).  Without the chunk
+// prefix, t0 = cu[s] and t0 + len = cu[s+1], both clamped to [0, T] (and the end
+// to at least t0).  With it (the backward, cstart != null), the bounds are the
+// ones the prefix launch wrote after the prefix, cstart[nseq + 1 + s] =
+// max(0, clamp(cu[0]), .., clamp(cu[s])): non-decreasing, so the sequences are
+// disjoint and their chunks fit the per-head slots even when cu_seqlens
+// decreases.  nch = ceil(len / 64) chunks; c0 = cstart[s], the chunks of the
+// sequences before it (its first chunk in a numbering of all chunks of the
+// batch).
 struct SeqSpan {
     int t0, len, nch, c0;
 };
 __host__ __device__ inline int clamp_tok(int x, int lo, int T) { return x < lo ? lo : (x > T ? T : x); }
-__device__ inline SeqSpan seq_span(const int* cu, const int* cstart, int T, int s) {
+__device__ inline SeqSpan seq_span(const int* cu, const int* cstart, int nseq, int T, int s) {
     SeqSpan r;
-    r.t0 = clamp_tok(__builtin_amdgcn_readfirstlane(cu[s]), 0, T);
-    r.len = clamp_tok(__builtin_amdgcn_readfirstlane(cu[s + 1]), r.t0, T) - r.t0;
+    if (cstart) {
+        const int* const bnd = cstart + nseq + 1;
+        r.t0 = __builtin_amdgcn_readfirstlane(bnd[s]);
+        r.len = __builtin_amdgcn_readfirstlane(bnd[s + 1]) - r.t0;
+        r.c0 = __builtin_amdgcn_readfirstlane(cstart[s]);
+    } else {
+        r.t0 = clamp_tok(__builtin_amdgcn_readfirstlane(cu[s]), 0, T);
+        r.len = clamp_tok(__builtin_amdgcn_readfirstlane(cu[s + 1]), r.t0, T) - r.t0;
+        r.c0 = 0;
+    }
     r.nch = (r.len + 63) / 64;
-    r.c0 = cstart ? __builtin_amdgcn_readfirstlane(cstart[s]) : 0;
     return r;
 }
 
@@ -150,13 +162,14 @@ struct BwdParams {
     __bf16* dhstore;       // [B*H, N, dv, dk] bf16, transposed: gradient reaching the end of each chunk
     const int* cu;         // packed sequences: token offsets [B+1] (null: B sequences of length T)
     int cmax;              // packed sequences: chunk slots per head (see FwdParams)
-    const int* cstart;     // packed sequences: chunk prefix [B+1]
+    const int* cstart;     // packed sequences: chunk prefix [B+1], then the sequence bounds [B+1]
 };
 // Packed sequences: the stored states of sequence s, head h sit at per-head slots
 // h * (cmax + B) + c0 + s + c (c = 0 .. nch, the last being its final state) and
 // the state gradients at h * cmax + c0 + c (c < nch).
 hipError_t launch_bwd_dh(const BwdParams& p, bool bf16, hipStream_t s);
-// Packed sequences: cstart[s] = chunks of sequences 0 .. s-1, s = 0 .. B.
+// Packed sequences: cstart[s] = chunks of sequences 0 .. s-1, s = 0 .. B, then
+// the bounds cstart[B + 1 + s] = max(0, clamp(cu[0]), .., clamp(cu[s])), s = 0 .. B.
 hipError_t launch_seq_chunk_prefix(const int* cu, int B, int T, int* cstart, hipStream_t s);
 hipError_t launch_bwd_local(const BwdParams& p, bool bf16, hipStream_t s);
 

@@ -19,7 +19,10 @@
  *         g, beta, dg, dbeta    [B, T, H]       float32 (g = log alpha <= 0)
  *         h0, ht, dht, dh0      [B, H, dk, dv]  float32
  *   - Only dk = dv = 128 is supported (GDN_ERR_UNSUPPORTED otherwise).  T >= 1 is
- *     arbitrary: the last 64-token chunk may be short.
+ *     arbitrary: the last 64-token chunk may be short.  B*T*H*128 <= 2^40, and the
+ *     64 rows of one chunk of one head must span less than 2^31 bytes
+ *     (64 * H * 128 * element size < 2^31: H < 131072 for bfloat16, H < 65536 for
+ *     float32); larger shapes are rejected with GDN_ERR_INVALID_ARG.
  *   - The op neither normalises q, k nor squashes beta.  The sliding-window
  *     shortcut assumes ||k_t|| <= 1 and 0 <= beta_t <= 2 (then each per-token map
  *     I - beta k k^T has spectral norm <= 1).
@@ -143,10 +146,14 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
  *   q, k, v, o        [T, H, dk|dv] in the I/O dtype: the sequences one after another
  *   g, beta           [T, H] float32
  *   cu_seqlens        DEVICE pointer, int32 [n_seqs + 1]: sequence s holds tokens
- *                     cu_seqlens[s] .. cu_seqlens[s+1] - 1 (non-decreasing,
+ *                     cu_seqlens[s] .. cu_seqlens[s+1] - 1 (required: non-decreasing,
  *                     cu_seqlens[0] = 0, cu_seqlens[n_seqs] = T).  The values are read
- *                     on the device and clamped to [0, T]; an empty sequence leaves
- *                     its final state equal to its initial state.
+ *                     on the device and clamped to [0, T] (the end of a sequence to at
+ *                     least its start), so no access leaves the tensors whatever they
+ *                     hold; a decreasing cu_seqlens makes sequences overlap, and the
+ *                     output rows they share are then written more than once
+ *                     (unspecified values).  An empty sequence leaves its final state
+ *                     equal to its initial state.
  *   h0                initial states [n_seqs, H, dk, dv] float32, or NULL (zero)
  *   ht                final states [n_seqs, H, dk, dv] float32, or NULL (not written)
  *   scale             multiplies every output
@@ -160,7 +167,7 @@ gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
                                 gdn_dtype dtype, float scale, void* stream);
 
 /* Workspace bytes for gdn_chunk_bwd_varlen ((size_t)-1 for invalid arguments):
- * the chunk prefix of the sequences, and per head (ceil(T/64) + 2 n_seqs)
+ * the chunk prefix and bounds of the sequences, and per head (ceil(T/64) + 2 n_seqs)
  * bfloat16 128 x 128 states plus (ceil(T/64) + n_seqs) state gradients. */
 size_t gdn_chunk_bwd_varlen_workspace_size(int n_seqs, int T, int H, int dk, int dv, gdn_dtype dtype);
 
@@ -170,7 +177,11 @@ size_t gdn_chunk_bwd_varlen_workspace_size(int n_seqs, int T, int H, int dk, int
  * gdn_chunk_bwd.  grad_q, grad_k, grad_v [T, H, ..] (I/O dtype), grad_g,
  * grad_beta [T, H] float32, grad_h0 [n_seqs, H, dk, dv] float32 or NULL.
  * cu_seqlens as for gdn_chunk_fwd_varlen (device, read on the device; tokens
- * outside every sequence are not written).  bf16 I/O only.  workspace: at
+ * outside every sequence are not written).  Here the bounds are made
+ * non-decreasing on the device before use: sequence s runs from
+ * max(cu_seqlens[0..s]) to max(cu_seqlens[0..s+1]) (each value clamped to [0, T]),
+ * which is the given sequence whenever cu_seqlens is valid and keeps every
+ * workspace slot in bounds when it is not.  bf16 I/O only.  workspace: at
  * least gdn_chunk_bwd_varlen_workspace_size() bytes, 256-byte aligned.  Runs a
  * one-workgroup chunk-prefix launch, then the launches of gdn_chunk_bwd (the
  * state store and the state-gradient sweep side by side on the library's side

@@ -159,3 +159,90 @@ def test_bwd_varlen_validation_before_launch():
     assert call(ws=0) == _lib.GDN_ERR_WORKSPACE
     assert call(wsz=1024) == _lib.GDN_ERR_WORKSPACE
     assert call(ws=A + 16) == _lib.GDN_ERR_INVALID_ARG
+
+
+def test_head_count_bound():
+    """Head counts whose 64-row chunk span does not fit the tile loaders' 32-bit
+    offsets (64 * H * 128 * element size >= 2^31) are rejected before anything
+    touches the device, in every entry point that takes them."""
+    lib = _lib.load()
+    A = 1 << 20
+    P = lambda a: ctypes.c_void_p(a) if a else None
+    big = {0: 65536, 1: 131072}   # float32, bfloat16: the first rejected head count
+    for dt, H in big.items():
+        assert _fwd(lib, q=A, k=A, v=A, g=A, beta=A, o=A, H=H, dt=dt) == _lib.GDN_ERR_INVALID_ARG
+        assert "too large" in _lib.last_error()
+        # one head fewer passes validation (it then fails at the device query here)
+        assert _fwd(lib, q=A, k=A, v=A, g=A, beta=A, o=A, H=H - 1, dt=dt) != _lib.GDN_ERR_INVALID_ARG
+        assert lib.gdn_chunk_fwd_workspace_size(1, 64, H, 128, 128, dt, None) == ctypes.c_size_t(-1).value
+        st = lib.gdn_chunk_fwd_varlen(*([P(A)] * 5), None, P(A), None, P(A), 1, 64, H, 128, 128, dt, 1.0, None)
+        assert st == _lib.GDN_ERR_INVALID_ARG
+    assert _bwd(lib, [A] * 11, H=big[1], ws=A, wsz=1 << 40) == _lib.GDN_ERR_INVALID_ARG
+    assert lib.gdn_chunk_bwd_varlen_workspace_size(1, 64, big[1], 128, 128, 1) == ctypes.c_size_t(-1).value
+    st = lib.gdn_chunk_bwd_varlen(*([P(A)] * 5), None, P(A), None, *([P(A)] * 5), None, P(A), 1, 64,
+                                  big[1], 128, 128, 1, 1.0, P(A), 1 << 40, None)
+    assert st == _lib.GDN_ERR_INVALID_ARG
+    # the gate scan bounds B*H by the int range and B*T*H by 2^40
+    st = lib.gdn_gate_scan(P(A), 1 << 16, 64, 1 << 16, 8, -16.0, P(A), None, P(A), 1 << 40, None)
+    assert st == _lib.GDN_ERR_INVALID_ARG
+
+
+def _prefix_model(cu, T):
+    """The packed-sequence prefix launch as the kernel computes it: rounds of 256
+    bound indices, a running prefix maximum of the clamped cu_seqlens and a
+    running chunk count.  Returns (chunk prefix [S+1], bounds [S+1])."""
+    S = len(cu) - 1
+    clamp = lambda x, lo: lo if x < lo else (T if x > T else x)
+    cstart, bnd_out = [0] * (S + 1), [0] * (S + 1)
+    carry, lastb = 0, 0
+    for s0 in range(0, S + 1, 256):
+        part = [clamp(cu[s], 0) if s <= S else 0 for s in range(s0, s0 + 256)]
+        for i in range(1, 256):
+            part[i] = max(part[i], part[i - 1])
+        b = [max(x, lastb) for x in part]
+        bnd = [lastb] + b
+        for i, s in enumerate(range(s0, s0 + 256)):
+            if s <= S:
+                bnd_out[s] = b[i]
+        nch = [(bnd[i + 1] - bnd[i] + 63) // 64 if 1 <= s <= S else 0
+               for i, s in enumerate(range(s0, s0 + 256))]
+        run = 0
+        for i, s in enumerate(range(s0, s0 + 256)):
+            run += nch[i]
+            if 1 <= s <= S:
+                cstart[s - 1] = carry + run - nch[i]
+        carry += run
+        lastb = bnd[256]
+    cstart[S] = carry
+    return cstart, bnd_out
+
+
+@pytest.mark.parametrize("case", ["valid", "decreasing", "repeat_full", "out_of_range", "many"])
+def test_varlen_prefix_spans_stay_in_slots(case):
+    """Packed-sequence backward: whatever cu_seqlens holds, the bounds the prefix
+    launch derives are non-decreasing inside [0, T], every sequence's chunks fit
+    the per-head slots the workspace provides (cmax = ceil(T/64) + S chunk slots,
+    cmax + S state slots), and for a valid cu_seqlens the bounds are cu_seqlens
+    itself."""
+    rng = __import__("numpy").random.default_rng(5)
+    T = 1024
+    cu = {"valid": [0, 100, 100, 640, 1024],
+          "decreasing": [0, 500, 100, 300, 1024],
+          "repeat_full": [0, T, 0, T, 0, T],
+          "out_of_range": [-50, 2000, -7, 5000, 30],
+          "many": list(rng.integers(-100, T + 100, size=601))}[case]
+    S = len(cu) - 1
+    cstart, bnd = _prefix_model(cu, T)
+    assert all(0 <= bnd[s] <= bnd[s + 1] <= T for s in range(S))
+    assert bnd[0] >= 0 and bnd[S] <= T
+    nch = [(bnd[s + 1] - bnd[s] + 63) // 64 for s in range(S)]
+    assert cstart == [sum(nch[:s]) for s in range(S + 1)]
+    cmax = (T + 63) // 64 + S
+    assert cstart[S] <= cmax
+    for s in range(S):
+        # states: slot c0 + s + c for c = 0 .. nch (the last is the final state);
+        # state gradients: slot c0 + c for c < nch
+        assert cstart[s] + s + nch[s] < cmax + S
+        assert nch[s] == 0 or cstart[s] + nch[s] - 1 < cmax
+    if case == "valid":
+        assert bnd == cu
