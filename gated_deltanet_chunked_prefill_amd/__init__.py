@@ -24,7 +24,7 @@ from . import _lib
 
 DEFAULT_LOG_EPS = math.log(2.0 ** -24)
 
-__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_varlen", "gdn_chunk_bwd", "gdn_chunk_bwd_varlen", "gdn_gate_scan",
+__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_varlen", "gdn_chunk_bwd", "gdn_chunk_bwd_varlen", "gdn_gate_scan",
            "gdn_plan_segments",
            "gdn_chunk_fwd_plan_info", "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd_workspace_size",
            "gdn_chunk_bwd_varlen_workspace_size", "options"]
@@ -200,6 +200,41 @@ def _varlen_shapes(q, k, v, g, beta, cu_seqlens):
     if S < 1:
         raise ValueError("cu_seqlens needs at least two entries")
     return T, H, dk, dv, S
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, g, beta, h0=None, scale=1.0, *, out, out_ht=None, **opts):
+    """gdn_chunk_fwd without a workspace: the library's fixed per-GPU scratch
+    array holds the split forward's state (no allocation inside the call, so it
+    can run under graph capture).  ``out`` (and ``out_ht`` when the final state is
+    wanted) must be preallocated; returns (out, out_ht).  Calls that overlap in
+    time on one GPU share the scratch and race."""
+    torch = _torch()
+    lib = _lib.load()
+    _dev(q, "q")
+    dt = q.dtype
+    _dev(k, "k", dt), _dev(v, "v", dt)
+    _dev(g, "g", torch.float32), _dev(beta, "beta", torch.float32)
+    _dev(h0, "h0", torch.float32)
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, T, H, d]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _shape(k, "k", (B, T, H, dk), dev)
+    _shape(v, "v", (B, T, H, dv), dev)
+    _shape(g, "g", (B, T, H), dev)
+    _shape(beta, "beta", (B, T, H), dev)
+    _shape(h0, "h0", (B, H, dk, dv), dev)
+    _dev(out, "out", dt)
+    _shape(out, "out", (B, T, H, dv), dev)
+    if out_ht is not None:
+        _dev(out_ht, "out_ht", torch.float32)
+        _shape(out_ht, "out_ht", (B, H, dk, dv), dev)
+    opt = options(**opts)
+    _lib.check(lib.gdn_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                                         _ptr(out), _ptr(out_ht), B, T, H, dk, dv, _dtype_code(q), float(scale),
+                                         ctypes.byref(opt), _stream(dev)))
+    return out, out_ht
 
 
 def gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None, scale=1.0, *,

@@ -276,12 +276,14 @@ size_t gdn_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, gdn_dty
     return fwd_layout(B, T, H, plan(B, T, H, cus, o)).total;
 }
 
-gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, const float* h0, void* o, float* ht, int B, int T,
-                         int H, int dk, int dv, gdn_dtype dtype, float scale,
-                         const gdn_options* opt, void* workspace, size_t workspace_bytes,
-                         void* stream) {
-    g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+
+// Checks of the forward's tensors and sizes, shared by both forward entry points.
+gdn_status check_fwd_args(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          const float* h0, const void* o, const float* ht, int B, int T, int H, int dk, int dv,
+                          gdn_dtype dtype, float scale) {
     if (!q || !k || !v || !g || !beta || !o)
         return fail(GDN_ERR_INVALID_ARG, "q, k, v, g, beta and o are required");
     gdn_status st = check_shapes(B, T, H, dk, dv, dtype);
@@ -293,24 +295,16 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
     for (const void* p : f32_ptrs)
         if (p && !aligned4(p)) return fail(GDN_ERR_INVALID_ARG, "g, beta, h0 and ht must be 4-byte aligned");
     if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite");
-    gdn_options op = resolve(opt);
-    const int N = num_chunks(T);
-    st = check_options(op, N);
-    if (st != GDN_OK) return st;
-    int cus = 0;
-    st = device_cus(&cus);
-    if (st != GDN_OK) return st;
-    const int P = plan(B, T, H, cus, op);
-    const FwdLayout L = fwd_layout(B, T, H, P);
-    if (L.total > 0) {
-        if (!workspace) return fail(GDN_ERR_WORKSPACE, "a workspace of %zu bytes is required", L.total);
-        if (workspace_bytes < L.total)
-            return fail(GDN_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
-        if (((uintptr_t)workspace & (kAlign - 1)) != 0)
-            return fail(GDN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    }
+    return GDN_OK;
+}
 
-    hipStream_t s = (hipStream_t)stream;
+// The forward's launches with P segment slots per head, in a workspace of at
+// least fwd_layout(B, T, H, P).total bytes (unused when P = 1).
+gdn_status fwd_launch(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                      const float* h0, void* o, float* ht, int B, int T, int H, gdn_dtype dtype, float scale,
+                      const gdn_options& op, int cus, int P, void* workspace, hipStream_t s) {
+    const int N = num_chunks(T);
+    const FwdLayout L = fwd_layout(B, T, H, P);
     gdn::FwdParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.o = o; p.ht = ht;
     p.B = B; p.T = T; p.H = H; p.N = N; p.P = P; p.w = op.window_chunks; p.scale = scale;
@@ -365,6 +359,71 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
     e = recorded(GDN_LAUNCH_FWD_QUEUE, s, [&] { return gdn::launch_fwd(p, gdn::PHASE_QUEUE, bf16, s); });
     if (e != hipSuccess) return hip_fail(e, "forward launch");
     return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* h0, void* o, float* ht, int B, int T,
+                         int H, int dk, int dv, gdn_dtype dtype, float scale,
+                         const gdn_options* opt, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    g_err[0] = 0;
+    gdn_status st = check_fwd_args(q, k, v, g, beta, h0, o, ht, B, T, H, dk, dv, dtype, scale);
+    if (st != GDN_OK) return st;
+    gdn_options op = resolve(opt);
+    st = check_options(op, num_chunks(T));
+    if (st != GDN_OK) return st;
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != GDN_OK) return st;
+    const int P = plan(B, T, H, cus, op);
+    const FwdLayout L = fwd_layout(B, T, H, P);
+    if (L.total > 0) {
+        if (!workspace) return fail(GDN_ERR_WORKSPACE, "a workspace of %zu bytes is required", L.total);
+        if (workspace_bytes < L.total)
+            return fail(GDN_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
+        if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+            return fail(GDN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    }
+    return fwd_launch(q, k, v, g, beta, h0, o, ht, B, T, H, dtype, scale, op, cus, P, workspace,
+                      (hipStream_t)stream);
+}
+
+static_assert(gdn::kFwdScratchBytes == GDN_NOALLOC_SCRATCH_BYTES, "scratch size declared in gdn.h");
+
+gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const float* h0, void* o, float* ht, int B, int T,
+                                 int H, int dk, int dv, gdn_dtype dtype, float scale,
+                                 const gdn_options* opt, void* stream) {
+    g_err[0] = 0;
+    gdn_status st = check_fwd_args(q, k, v, g, beta, h0, o, ht, B, T, H, dk, dv, dtype, scale);
+    if (st != GDN_OK) return st;
+    gdn_options op = resolve(opt);
+    st = check_options(op, num_chunks(T));
+    if (st != GDN_OK) return st;
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != GDN_OK) return st;
+    int P = plan(B, T, H, cus, op);
+    const size_t cap = gdn::kFwdScratchBytes;
+    if (fwd_layout(B, T, H, P).total > cap) {
+        if (op.split_mode == 2)
+            return fail(GDN_ERR_WORKSPACE,
+                        "%d segments per head need %zu bytes of scratch; the fixed scratch holds %zu bytes",
+                        P, fwd_layout(B, T, H, P).total, cap);
+        // automatic split: fewer segment slots, down to none
+        while (P > 1 && fwd_layout(B, T, H, P).total > cap) --P;
+    }
+    void* scratch = nullptr;
+    if (P > 1) {
+        const hipError_t e = gdn::fwd_scratch(&scratch);
+        if (e != hipSuccess) return hip_fail(e, "scratch address lookup");
+    }
+    return fwd_launch(q, k, v, g, beta, h0, o, ht, B, T, H, dtype, scale, op, cus, P, scratch,
+                      (hipStream_t)stream);
 }
 
 gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g,

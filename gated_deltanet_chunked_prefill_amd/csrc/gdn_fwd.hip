@@ -52,6 +52,8 @@
 // K^T and V in accumulator layout are read from the row-major tiles with the
 // transposing LDS read; O is produced transposed (O^T = H^T Q^T + V'^T P^T) so
 // each lane holds a row of O and writes it as 8-byte segments.
+#include <mutex>
+
 #include "gdn_chunk.h"
 #include "gdn_internal.h"
 
@@ -1395,6 +1397,37 @@ hipError_t launch_fwd_t(const FwdParams& p, int phase, hipStream_t s) {
 
 hipError_t launch_fwd(const FwdParams& p, int phase, bool bf16, hipStream_t s) {
     return bf16 ? launch_fwd_t<__bf16>(p, phase, s) : launch_fwd_t<float>(p, phase, s);
+}
+
+// Scratch of the forward entry point that allocates nothing
+// (gdn_chunk_fwd_noalloc): a fixed array in device memory, one copy per GPU,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device array: its device address is looked up once per
+// device (with that device current) and only that address is handed to
+// kernels.
+static __device__ __align__(256) unsigned char scratch[kFwdScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+void* g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t fwd_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr || ((uintptr_t)p & 255u) != 0) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 

@@ -121,6 +121,10 @@ __device__ inline SeqSpan seq_span(const int* cu, const int* cstart, int nseq, i
 enum FwdPhase { PHASE_SINGLE = 0, PHASE_QUEUE = 1, PHASE_STATES = 2, PHASE_VARLEN = 3, PHASE_STATES_VARLEN = 4 };
 
 hipError_t launch_fwd(const FwdParams& p, int phase, bool bf16, hipStream_t s);
+// The forward's fixed scratch array (gdn_chunk_fwd_noalloc): its size, and its
+// device address on the current device (looked up on the first call per device).
+constexpr size_t kFwdScratchBytes = (size_t)64 << 20;
+hipError_t fwd_scratch(void** ptr);
 hipError_t launch_chunk_sums(const float* g, int B, int T, int H, float* chunk_sums, hipStream_t s);
 int window_groups(int T);
 int max_window_chunks();

@@ -139,6 +139,30 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          const gdn_options* opt, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* Bytes of the fixed scratch array gdn_chunk_fwd_noalloc uses on each GPU. */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* gdn_chunk_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments and results without a workspace argument.  The call makes no
+ * hipMalloc, hipFree or other allocating call.  The split forward's scratch
+ * (what gdn_chunk_fwd keeps in its workspace) lives in a fixed device array of
+ * GDN_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs on
+ * until the process ends; its address is looked up once per device, on the
+ * first call with that device current.  Everything the kernels need cleared is
+ * cleared by the call's own first kernel.
+ * Limit: with split_mode == 2, a segment count whose scratch exceeds the array
+ * is rejected with GDN_ERR_WORKSPACE; the automatic plan uses at most as many
+ * segment slots per head as fit (none, i.e. the unsplit forward, if even two do
+ * not), so its results can differ from gdn_chunk_fwd's by rounding only.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * the same GPU (different streams, or threads without ordering) race and give
+ * wrong results; order them (e.g. one stream).  Errors as for gdn_chunk_fwd. */
+gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const float* h0, void* o, float* ht, int B, int T,
+                                 int H, int dk, int dv, gdn_dtype dtype, float scale,
+                                 const gdn_options* opt, void* stream);
+
 /* Fused chunked forward over a packed batch of variable-length sequences (the
  * chunked-prefill serving shape: several prompts of different lengths in one
  * call; the same chunk-wise computation as gdn_chunk_fwd, talk summary
