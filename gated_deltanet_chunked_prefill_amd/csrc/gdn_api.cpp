@@ -148,13 +148,16 @@ int num_chunks(int T) { return (T + kChunk - 1) / kChunk; }
 // Segment slots per head: 1 = no split.  In the automatic mode this is the
 // most segments the device-side planner may give a head (talk summary,
 // paragraph 8: a square-root rule on the chunk count bounds the split); the
-// planner picks the counts per call from the number of exact and window heads.
+// planner picks the counts per call from the number of exact and window heads,
+// with its makespan model deciding between no split (one candidate) and the
+// split ones whenever there are fewer heads than compute units (paragraph 8
+// calls a fixed activation boundary crude).
 int plan(int B, int T, int H, int num_cus, const gdn_options& o) {
     const int N = num_chunks(T);
     if (o.split_mode == 1) return 1;
     if (o.split_mode == 2) return o.n_segments < N ? o.n_segments : N;
     const long long heads = (long long)B * H;
-    if (heads * 2 >= num_cus || N < 2 * o.window_chunks) return 1;
+    if (heads >= num_cus || N < 2 * o.window_chunks) return 1;
     long long p = (long long)std::floor(std::sqrt((double)N));
     if (p > 32) p = 32;
     if (p > N / 2) p = N / 2;

@@ -163,12 +163,16 @@ __device__ __forceinline__ void wait_published(const int* cnt, int target, int* 
 }
 
 // The serial state step of one chunk for state wave w (its 32 state columns).
-template <typename T, int MODE>
+// EMIT (output chunk or not) is a compile-time choice: a run-time flag inside
+// the unrolled product loops made every k-step branch and copy the (Q H)^T
+// accumulators, waiting on each product's result.
+template <typename T, int MODE, bool EMIT>
 __device__ __forceinline__ void chunk_state(T* o, int Tn, int H, float scale, const Lane<T>& L, const T* kt,
                                             const T* qt, const T* vt, const T (*t32)[kT32],
                                             const float* gam_vec, const float* e_vec, float GC,
-                                            int b, int h, int t0, int nvalid, bool emit,
+                                            int b, int h, int t0, int nvalid,
                                             f32x16* Hs) {
+    constexpr bool emit = MODE == MODE_FULL && EMIT;
     using F = typename FragOf<T>::type;
     const int n = L.n, g = L.g, w = L.w;
     f32x16 X[2];
@@ -318,7 +322,9 @@ __device__ __noinline__ void state_loop(const FwdParams& prm, Smem<T>& sm, const
         for (int ht = 0; ht < 4; ++ht) Hs[ht] = zero16();
     }
     const size_t hst_base = (size_t)bh * (N + 1);
-    auto emit = [&](int c) { return MODE == MODE_FULL && o != nullptr && c >= c_out; };
+    // chunks before i_out only warm the state up; from i_out on they emit outputs
+    // (two loops, each with its step compiled for its kind of chunk)
+    const int i_out = (MODE == MODE_FULL && o != nullptr) ? (c_out > c_begin ? c_out - c_begin : 0) : nch;
     // the state entering every chunk this task owns (for the backward)
     auto keep = [&](int c) {
         if (KEEP && c >= c_out) store_state_bf16t(hst + (hst_base + c) * SS, L.w, L.lane, Hs);
@@ -326,13 +332,22 @@ __device__ __noinline__ void state_loop(const FwdParams& prm, Smem<T>& sm, const
     if constexpr (kPipe) {
         lds_barrier();
         lds_barrier();
-        for (int i = 0; i < nch; ++i) {
+        for (int i = 0; i < i_out && i < nch; ++i) {
             const int c = c_begin + i;
             const int slot = i % 3, vb = i & 1;
             keep(c);
-            chunk_state<T, MODE>(o, Tn, H, scale, L, sm.kt[slot], sm.qt[slot], sm.vt[vb], sm.t32[vb],
-                                 sm.gam_vec[vb], sm.e_vec[vb], sm.gc[vb][0], b, h, c * kChunk,
-                                 chunk_len(Tn, c), emit(c), Hs);
+            chunk_state<T, MODE, false>(o, Tn, H, scale, L, sm.kt[slot], sm.qt[slot], sm.vt[vb], sm.t32[vb],
+                                        sm.gam_vec[vb], sm.e_vec[vb], sm.gc[vb][0], b, h, c * kChunk,
+                                        chunk_len(Tn, c), Hs);
+            lds_barrier();
+        }
+        for (int i = i_out; i < nch; ++i) {
+            const int c = c_begin + i;
+            const int slot = i % 3, vb = i & 1;
+            keep(c);
+            chunk_state<T, MODE, true>(o, Tn, H, scale, L, sm.kt[slot], sm.qt[slot], sm.vt[vb], sm.t32[vb],
+                                       sm.gam_vec[vb], sm.e_vec[vb], sm.gc[vb][0], b, h, c * kChunk,
+                                       chunk_len(Tn, c), Hs);
             lds_barrier();
         }
     } else {
@@ -342,9 +357,14 @@ __device__ __noinline__ void state_loop(const FwdParams& prm, Smem<T>& sm, const
             lds_barrier();
             lds_barrier();
             keep(c);
-            chunk_state<T, MODE>(o, Tn, H, scale, L, sm.kt[0], sm.qt[0], sm.vt[0], sm.t32[0],
-                                 sm.gam_vec[0], sm.e_vec[0], sm.gc[0][0], b, h, c * kChunk,
-                                 chunk_len(Tn, c), emit(c), Hs);
+            if (i >= i_out)
+                chunk_state<T, MODE, true>(o, Tn, H, scale, L, sm.kt[0], sm.qt[0], sm.vt[0], sm.t32[0],
+                                           sm.gam_vec[0], sm.e_vec[0], sm.gc[0][0], b, h, c * kChunk,
+                                           chunk_len(Tn, c), Hs);
+            else
+                chunk_state<T, MODE, false>(o, Tn, H, scale, L, sm.kt[0], sm.qt[0], sm.vt[0], sm.t32[0],
+                                            sm.gam_vec[0], sm.e_vec[0], sm.gc[0][0], b, h, c * kChunk,
+                                            chunk_len(Tn, c), Hs);
         }
     }
     if (KEEP && c_end == N) keep(N);
@@ -722,7 +742,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_kernel(FwdParams prm) {
 }
 
 // Per-head tables of the planner live in LDS up to this many heads (always, for
-// the automatic split, which needs B*H < CUs/2), in the workspace beyond.
+// the automatic split, which needs B*H < CUs), in the workspace beyond.
 constexpr int kPlanHeads = 4096;
 
 // The persistent kernel's parameters read straight from the kernel-argument

@@ -97,8 +97,10 @@ void gdn_default_options(gdn_options* opt);
 /* Segment slots per head of the forward for these shapes on a device with
  * num_cus compute units (the host-side planner; no device access): 1 when the
  * sequence is not split; n_segments (at most the chunk count) when
- * split_mode == 2; otherwise the most segments the device-side planner may give
- * a head, min(32, floor(sqrt(N)), N/2) for N chunks.  That planner reads the
+ * split_mode == 2; otherwise 1 when B*H >= num_cus or N < 2 * window_chunks, else
+ * the most segments the device-side planner may give a head,
+ * min(32, floor(sqrt(N)), N/2) for N chunks (its makespan model may still keep
+ * heads unsplit).  That planner reads the
  * window flags and picks the counts of exact and window heads per call (see
  * gdn_chunk_fwd_plan_info).  Returns 0 for invalid arguments. */
 int gdn_plan_segments(int B, int T, int H, int num_cus, const gdn_options* opt);

@@ -39,7 +39,8 @@ def test_default_options():
     (1, 32768, 32, 256, 22),    # 512 chunks: min(32, floor(sqrt(512)) = 22, 256)
     (1, 262144, 16, 256, 32),   # min(32, 64, 2048)
     (1, 4096, 16, 256, 8),      # min(32, 8, 32)
-    (4, 8192, 32, 256, 1),      # 128 heads >= 256/2: no split
+    (4, 8192, 32, 256, 11),     # 128 heads < 256 CUs: min(32, floor(sqrt(128)) = 11, 64)
+    (8, 8192, 32, 256, 1),      # 256 heads >= 256 CUs: no split
     (1, 128, 1, 256, 1),        # 2 chunks < 2w
     (1, 1000, 1, 256, 4),       # 16 chunks: min(32, 4, 8)
     (1, 64 * 100, 2, 256, 10),  # min(32, 10, 50)
