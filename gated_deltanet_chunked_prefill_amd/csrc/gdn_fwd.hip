@@ -246,25 +246,9 @@ __device__ __forceinline__ void chunk_state(T* o, int Tn, int H, float scale, co
         OT[1] = mma(vf[1], L.f32(t32[4], 1), OT[1]);
         OT[1] = mma(vf[2], L.f32(t32[5], 0), OT[1]);
         OT[1] = mma(vf[3], L.f32(t32[5], 1), OT[1]);
-        typedef T t4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const int pos = 32 * rt + n;
-            if (pos < nvalid) {
-                // global address space: plain vector stores, counted by vmcnt only
-                typedef __attribute__((address_space(1))) t4 gt4;
-                gt4* orow = (gt4*)(o + (((size_t)b * Tn + t0 + pos) * H + h) * kDv + 32 * w + 4 * g);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    t4 v;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = (T)(scale * OT[rt][4 * i + e]);
-                    orow[2 * i] = v;
-                }
-            }
-        }
     }
-    // H <- Gamma_C H + K^T diag(E) V'
+    // H <- Gamma_C H + K^T diag(E) V', issued before the output is converted and
+    // stored so that those instructions overlap the update's products
     F ef[4];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
@@ -273,6 +257,55 @@ __device__ __forceinline__ void chunk_state(T* o, int Tn, int H, float scale, co
         ef[2 * rt + 1] = acc_frag<T>(ev, 1);
     }
     kt_update<T>(L, kt, Hs, GC, ef);
+    if (MODE == MODE_FULL && emit) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int pos = 32 * rt + n;
+            // global address space: plain vector stores, counted by vmcnt only
+            T* const orow = o + (((size_t)b * Tn + t0 + pos) * H + h) * kDv + 32 * w;
+            if constexpr (sizeof(T) == 2) {
+                // lane (n, g) holds state columns 8i + 4g .. +3 (i = 0..3) of row pos;
+                // two lane swaps between the half-waves give it columns 8g .. +7 and
+                // 16 + 8g .. +7, two 16-byte pieces
+                uint32_t pk[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+                    const b2 pr = {(__bf16)(scale * OT[rt][2 * k]), (__bf16)(scale * OT[rt][2 * k + 1])};
+                    pk[k] = __builtin_bit_cast(uint32_t, pr);
+                }
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const auto r = __builtin_amdgcn_permlane32_swap(pk[4 * q + e], pk[4 * q + 2 + e], false, false);
+                        pk[4 * q + e] = r[0];
+                        pk[4 * q + 2 + e] = r[1];
+                    }
+                }
+                if (pos < nvalid) {
+                    typedef __attribute__((address_space(1))) u32x4 gu4;
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const u32x4 v = {pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]};
+                        *(gu4*)(orow + 16 * q + 8 * g) = v;
+                    }
+                }
+            } else {
+                if (pos < nvalid) {
+                    typedef T t4 __attribute__((ext_vector_type(4)));
+                    typedef __attribute__((address_space(1))) t4 gt4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        t4 v;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = (T)(scale * OT[rt][4 * i + e]);
+                        *(gt4*)(orow + 8 * i + 4 * g) = v;
+                    }
+                }
+            }
+        }
+    }
 }
 
 // Pass-1 segment transition, carried by the prep waves (prep wave w owns columns
