@@ -36,6 +36,7 @@ struct Smem {
     float e_vec[NP][kChunk];   // Gamma_C / Gamma_r
     float gc[NP][4];           // [0] Gamma_C
     float pscr[4][4][kChunk];  // per prep wave: gamma, exp(gamma - gC/2), exp(gC/2 - gamma), beta
+    float gbt[3][2][kChunk];   // bf16 pipeline: g and beta of a chunk, staged with its K/Q slot
     int islot[4];              // workgroup-wide scalars: [0] job index, [1] job count
     float fslot[4];            // [0] exp(sum of g over a segment)
     int jrec[8];               // split forward: the workgroup's first job, planned in the workgroup
@@ -219,25 +220,25 @@ struct Lane {
 };
 
 // Copy of one 64 x 128 chunk tile of a head into a swizzled row-major LDS tile,
-// spread over the 256 lanes of four waves.  Full chunks go HBM -> LDS directly
-// (each lane's 16 bytes land at slot base + 16*lane, so the lane fetches the
-// chunk that belongs there); a short last chunk goes through registers and is
-// zero-filled.
-template <typename T>
+// spread over the 64 NW lanes of NW loading waves.  Full chunks go HBM -> LDS
+// directly (each lane's 16 bytes land at slot base + 16*lane, so the lane fetches
+// the chunk that belongs there); a short last chunk goes through registers and
+// is zero-filled.
+template <typename T, int NW = 4>
 struct TileLoader {
     static constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16-byte chunk
     static constexpr int CPR = kDk / EPC;               // 16-byte chunks per row
-    static constexpr int ROUNDS = kChunk * CPR / 256;
+    static constexpr int ROUNDS = kChunk * CPR / (64 * NW);
     uint32_t off[ROUNDS];   // byte offset of this lane's 16 bytes from the chunk's first row
-    int pw, lane;           // loading wave (0..3, wave-uniform) and lane
+    int pw, lane;           // loading wave (0..NW-1, wave-uniform) and lane
 
-    // Computed once per task: round i covers tile slots (4i + pw) * 64 + lane.
+    // Computed once per task: round i covers tile slots (NW i + pw) * 64 + lane.
     __device__ __forceinline__ void init(int pw_, int lane_, int H) {
         pw = pw_;
         lane = lane_;
 #pragma unroll
         for (int i = 0; i < ROUNDS; ++i) {
-            const int L = (i * 4 + pw) * 64 + lane;
+            const int L = (i * NW + pw) * 64 + lane;
             const int row = L / CPR, slot = L % CPR;
             off[i] = (uint32_t)((row * H * kDk + (slot ^ slot_swz<CPR>(row)) * EPC) * (int)sizeof(T));
         }
@@ -251,7 +252,7 @@ struct TileLoader {
         if (nvalid == kChunk) {
 #pragma unroll
             for (int i = 0; i < ROUNDS; ++i) {
-                T* lbase = tile + (i * 4 + pw) * 64 * EPC;   // wave-uniform LDS destination
+                T* lbase = tile + (i * NW + pw) * 64 * EPC;   // wave-uniform LDS destination
                 __builtin_amdgcn_global_load_lds((const void*)(base + off[i]),
                                                  (__attribute__((address_space(3))) void*)lbase, 16, 0, CPOL);
             }
@@ -259,7 +260,7 @@ struct TileLoader {
             typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 #pragma unroll
             for (int i = 0; i < ROUNDS; ++i) {
-                const int L = (i * 4 + pw) * 64 + lane;
+                const int L = (i * NW + pw) * 64 + lane;
                 u4 v = {0u, 0u, 0u, 0u};
                 if (L / CPR < nvalid) v = *(const __attribute__((address_space(1))) u4*)(base + off[i]);
                 *(u4*)(tile + L * EPC) = v;

@@ -439,7 +439,7 @@ __device__ __noinline__ void prep_loop(const FwdParams& prm, Smem<T>& sm, const 
     Lane<T> L;
     L.init(threadIdx.x);
     float gsum = 0.f;
-    float g_cur = 0.f, b_cur = 0.f, g_nxt = 0.f, b_nxt = 0.f;
+    float g_cur = 0.f, b_cur = 0.f;
     f32x16 Ms[4];
     if (MODE == MODE_PASS1) {
 #pragma unroll
@@ -449,33 +449,56 @@ __device__ __noinline__ void prep_loop(const FwdParams& prm, Smem<T>& sm, const 
                 Ms[ht][r] = (32 * ht + rho(L.g, r) == 32 * L.w + L.n) ? 1.f : 0.f;
     }
     auto need_q = [&](int c) { return MODE == MODE_FULL && has_o && c >= c_out; };
-    TileLoader<T> TL;
-    TL.init(pw, L.lane, H);
+    // bf16: prep waves 2 and 3 issue every load of the chunk tiles and stage g and
+    // beta in LDS, so waves 0 and 1 (the diagonal inverses, the longest prep work)
+    // never wait on the memory pipeline; float32: all four load their quarter.
+    constexpr int kLoaders = kPipe ? 2 : 4;
+    const bool loader = pw >= 4 - kLoaders;
+    TileLoader<T, kLoaders> TL;
+    if (loader) TL.init(pw - (4 - kLoaders), L.lane, H);
     auto load_kq = [&](int c, int slot) {
+        if (!loader) return;
         const size_t cb = chunk_base(b, h, Tn, H, c);
         const int nv = chunk_len(Tn, c);
         TL.load(sm.kt[slot], kp + cb, nv);
         if (need_q(c)) TL.load(sm.qt[slot], qp + cb, nv);
     };
     auto load_v = [&](int c, int slot) {
+        if (!loader) return;
         TL.load(sm.vt[slot], vp + chunk_base(b, h, Tn, H, c), chunk_len(Tn, c));
     };
     auto load_gb = [&](int c, float& gv, float& bv) {
         load_gate_beta(gp, bp, Tn, H, b, h, c, L.lane, gv, bv);
     };
+    // g (wave 2) and beta (wave 3) of chunk c into LDS slot `slot`, zero past the
+    // end of the sequence (a short chunk goes through registers)
+    auto stage_gb = [&](int c, int slot) {
+        if (pw < 2) return;
+        const float* const src = pw == 2 ? gp : bp;
+        float* const dst = &sm.gbt[slot][pw - 2][0];
+        const size_t e0 = ((size_t)b * Tn + (size_t)c * kChunk) * H + h;
+        const int nv = chunk_len(Tn, c);
+        if (nv == kChunk) {
+            __builtin_amdgcn_global_load_lds((const void*)(src + e0 + (size_t)L.lane * H),
+                                             (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+        } else {
+            typedef __attribute__((address_space(1))) const float gfloat;
+            dst[L.lane] = L.lane < nv ? ((gfloat*)src)[e0 + (size_t)L.lane * H] : 0.f;
+        }
+    };
     if constexpr (kPipe) {
-        // prologue: chunk 0 in LDS and prepped; chunk 1's K, Q in flight
+        // prologue: chunk 0 in LDS and prepped; chunk 1's K, Q, g, beta in flight
         load_kq(c_begin, 0);
         load_v(c_begin, 0);
-        if (nch > 1) load_kq(c_begin + 1, 1);
-        load_gb(c_begin, g_cur, b_cur);
-        if (nch > 1) load_gb(c_begin + 1, g_nxt, b_nxt);
+        stage_gb(c_begin, 0);
+        if (nch > 1) {
+            load_kq(c_begin + 1, 1);
+            stage_gb(c_begin + 1, 1);
+        }
         wait_vm();
         lds_barrier();
         chunk_prep<T, MODE>(sm, L, pw, sm.kt[0], sm.qt[0], sm.t32[0], sm.gam_vec[0], sm.e_vec[0],
-                            sm.gc[0], g_cur, b_cur, need_q(c_begin), gsum);
-        g_cur = g_nxt;
-        b_cur = b_nxt;
+                            sm.gc[0], sm.gbt[0][0][L.lane], sm.gbt[0][1][L.lane], need_q(c_begin), gsum);
         lds_barrier();
         for (int i = 0; i < nch; ++i) {
             const int c = c_begin + i;
@@ -484,14 +507,13 @@ __device__ __noinline__ void prep_loop(const FwdParams& prm, Smem<T>& sm, const 
             if (i + 1 < nch) {
                 if (i + 2 < nch) {
                     load_kq(c + 2, (i + 2) % 3);
-                    load_gb(c + 2, g_nxt, b_nxt);
+                    stage_gb(c + 2, (i + 2) % 3);
                 }
                 load_v(c + 1, (i + 1) & 1);
                 const int slot = (i + 1) % 3, pb = (i + 1) & 1;
                 chunk_prep<T, MODE>(sm, L, pw, sm.kt[slot], sm.qt[slot], sm.t32[pb], sm.gam_vec[pb],
-                                    sm.e_vec[pb], sm.gc[pb], g_cur, b_cur, need_q(c + 1), gsum);
-                g_cur = g_nxt;
-                b_cur = b_nxt;
+                                    sm.e_vec[pb], sm.gc[pb], sm.gbt[slot][0][L.lane], sm.gbt[slot][1][L.lane],
+                                    need_q(c + 1), gsum);
                 wait_vm();
             }
             lds_barrier();
