@@ -12,7 +12,8 @@ Prints one JSON line with tokens/s, the roofline of the fused forward kernel
 A secondary "backward" object times whole gdn_chunk_bwd calls on the training
 shape (B=4, T=8192, H=32, bf16) with per-launch event times, and a "varlen"
 object whole gdn_chunk_fwd_varlen calls on a packed batch of 8 prompts of
-mixed lengths (32768 tokens, H=32).
+mixed lengths (32768 tokens, H=32), and a "kda" object whole gdn_kda_fwd calls
+(per-key-channel decay) at B=1, T=32768, H=32.
 """
 from __future__ import annotations
 
@@ -294,6 +295,42 @@ def rep_stats(torch, step, reps, flush_bytes=0):
             "mean_ms": float(np.mean(t))}
 
 
+KDA_WORKLOAD = "bf16_kda_t32768_h32"
+# KDA algorithmic bytes per token-head: q, k, v, o (bf16, 4 x 256 B), g per key
+# channel (128 x 4 B) and beta (4 B); per head the final state (64 KiB)
+KDA_BYTES_PER_TOKEN_HEAD = 4 * 256 + 128 * 4 + 4
+
+
+def bench_kda(torch, gdn, inputs, steps, warmup):
+    """Whole gdn_kda_fwd calls (per-key-channel decay) on the throughput shape."""
+    x = inputs.kda_workload(KDA_WORKLOAD)
+    B, T, H, dk, dv = x.shape
+    dev = torch.device("cuda:0")
+    bf = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)
+    q, k, v = bf(x.q), bf(x.k), bf(x.v)
+    g = torch.from_numpy(x.g).to(dev)
+    beta = torch.from_numpy(x.beta).to(dev)
+    del x
+    o = torch.empty_like(v)
+    ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+
+    def step():
+        gdn.gdn_kda_fwd(q, k, v, g, beta, None, out=o, out_ht=ht)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    nbytes = B * T * H * KDA_BYTES_PER_TOKEN_HEAD + B * H * STATE_BYTES
+    return {"workload": KDA_WORKLOAD, "B": B, "T": T, "H": H, "steps": steps, "ms_per_call": ms,
+            "tokens_per_s": B * T / (ms * 1e-3), "algorithmic_bytes": nbytes,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def cpu_baseline(x, tokens):
     """The fp64 oracle, as it stands, on the first `tokens` tokens of every head."""
     import oracle
@@ -324,6 +361,8 @@ def main():
                     help="timed backward calls on the training shape (0 to skip)")
     ap.add_argument("--varlen-steps", type=int, default=5,
                     help="timed packed variable-length calls (0 to skip)")
+    ap.add_argument("--kda-steps", type=int, default=3,
+                    help="timed per-key-channel-decay (KDA) forward calls (0 to skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, stream-copy this many MiB three times "
                          "(the calibration kernel of the HBM counter runs)")
@@ -427,13 +466,15 @@ def main():
                      "call_frac": nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "timing": timing,
     }
-    if args.bwd_steps > 0 or args.varlen_steps > 0:
+    if args.bwd_steps > 0 or args.varlen_steps > 0 or args.kda_steps > 0:
         del q, k, v, g, beta, o, ht, ws
         torch.cuda.empty_cache()
     if args.bwd_steps > 0:
         res["backward"] = bench_backward(torch, gdn, _lib, inputs, args.bwd_steps, 2)
     if args.varlen_steps > 0:
         res["varlen"] = bench_varlen(torch, gdn, inputs, args.varlen_steps, 2)
+    if args.kda_steps > 0:
+        res["kda"] = bench_kda(torch, gdn, inputs, args.kda_steps, 1)
     if args.calib_copy_mib > 0:
         src = torch.randn(args.calib_copy_mib * 2 ** 18, device=dev)
         dst = torch.empty_like(src)

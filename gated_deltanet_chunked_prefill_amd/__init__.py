@@ -8,6 +8,7 @@ library's HIP kernels; there is no fallback path.
 
     gdn_chunk_fwd(q, k, v, g, beta, h0=None, scale=1.0, ...) -> (o, ht)
     gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None, ...) -> (o, ht)
+    gdn_kda_fwd(q, k, v, g, beta, h0=None, scale=1.0) -> (o, ht)   (g per key channel)
     gdn_chunk_bwd(q, k, v, g, beta, dout, h0=None, dht=None, scale=1.0) -> dict
     gdn_chunk_bwd_varlen(q, k, v, g, beta, dout, cu_seqlens, h0=None, ...) -> dict
     gdn_gate_scan(g, window_chunks=8, log_eps=log(2^-24)) -> (flags, max_window_logdecay)
@@ -24,7 +25,7 @@ from . import _lib
 
 DEFAULT_LOG_EPS = math.log(2.0 ** -24)
 
-__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_varlen", "gdn_chunk_bwd", "gdn_chunk_bwd_varlen", "gdn_gate_scan",
+__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_kda_fwd", "gdn_chunk_fwd_varlen", "gdn_chunk_bwd", "gdn_chunk_bwd_varlen", "gdn_gate_scan",
            "gdn_plan_segments",
            "gdn_chunk_fwd_plan_info", "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd_workspace_size",
            "gdn_chunk_bwd_varlen_workspace_size", "options"]
@@ -235,6 +236,39 @@ def gdn_chunk_fwd_noalloc(q, k, v, g, beta, h0=None, scale=1.0, *, out, out_ht=N
                                          _ptr(out), _ptr(out_ht), B, T, H, dk, dv, _dtype_code(q), float(scale),
                                          ctypes.byref(opt), _stream(dev)))
     return out, out_ht
+
+
+def gdn_kda_fwd(q, k, v, g, beta, h0=None, scale=1.0, *, output_final_state=True, out=None, out_ht=None):
+    """Chunked forward of the per-key-channel-decay variant (KDA): as
+    gdn_chunk_fwd, with g [B, T, H, dk] float32 (one log-decay per key channel)
+    and bf16 q, k, v.  Returns (o, ht)."""
+    torch = _torch()
+    lib = _lib.load()
+    _dev(q, "q", torch.bfloat16)
+    _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16)
+    _dev(g, "g", torch.float32), _dev(beta, "beta", torch.float32)
+    _dev(h0, "h0", torch.float32)
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, T, H, d]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _shape(k, "k", (B, T, H, dk), dev)
+    _shape(v, "v", (B, T, H, dv), dev)
+    _shape(g, "g", (B, T, H, dk), dev)
+    _shape(beta, "beta", (B, T, H), dev)
+    _shape(h0, "h0", (B, H, dk, dv), dev)
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    _dev(o, "o", torch.bfloat16)
+    _shape(o, "out", (B, T, H, dv), dev)
+    if out_ht is not None:
+        ht = _dev(out_ht, "out_ht", torch.float32)
+        _shape(ht, "out_ht", (B, H, dk, dv), dev)
+    else:
+        ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
+    _lib.check(lib.gdn_kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht),
+                               B, T, H, dk, dv, _lib.GDN_BF16, float(scale), _stream(dev)))
+    return o, ht
 
 
 def gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None, scale=1.0, *,

@@ -429,6 +429,22 @@ gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, co
                       (hipStream_t)stream);
 }
 
+gdn_status gdn_kda_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                       const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, gdn_dtype dtype,
+                       float scale, void* stream) {
+    g_err[0] = 0;
+    gdn_status st = check_fwd_args(q, k, v, g, beta, h0, o, ht, B, T, H, dk, dv, dtype, scale);
+    if (st != GDN_OK) return st;
+    if (dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "the KDA forward supports bf16 I/O only");
+    gdn::KdaParams p{};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.o = o; p.ht = ht;
+    p.B = B; p.T = T; p.H = H; p.N = num_chunks(T); p.scale = scale;
+    hipStream_t s = (hipStream_t)stream;
+    const hipError_t e = recorded(GDN_LAUNCH_KDA_FWD, s, [&] { return gdn::launch_kda_fwd(p, s); });
+    if (e != hipSuccess) return hip_fail(e, "KDA forward launch");
+    return GDN_OK;
+}
+
 gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, const float* h0, void* o, float* ht,
                                 const int32_t* cu_seqlens, int n_seqs, int T, int H, int dk, int dv,

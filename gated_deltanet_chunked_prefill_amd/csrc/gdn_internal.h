@@ -168,6 +168,23 @@ struct BwdParams {
     int cmax;              // packed sequences: chunk slots per head (see FwdParams)
     const int* cstart;     // packed sequences: chunk prefix [B+1], then the sequence bounds [B+1]
 };
+// Per-key-channel-decay variant (KDA): g is [B, T, H, dk] float32 (one log-decay
+// per key channel), q, k, v, o bf16; one workgroup per (batch, head).
+struct KdaParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const float* h0;   // nullable
+    void* o;
+    float* ht;         // nullable
+    int B, T, H, N;
+    float scale;
+};
+hipError_t launch_kda_fwd(const KdaParams& p, hipStream_t s);
+size_t kda_smem_bytes();
+
 // Packed sequences: the stored states of sequence s, head h sit at per-head slots
 // h * (cmax + B) + c0 + s + c (c = 0 .. nch, the last being its final state) and
 // the state gradients at h * cmax + c0 + c (c < nch).

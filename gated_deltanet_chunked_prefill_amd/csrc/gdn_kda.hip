@@ -1,0 +1,369 @@
+// Chunked forward of the per-key-channel-decay variant (KDA) for gfx950.
+//
+// The FlashQLA commentary names GDN and KDA as the sibling operators of the
+// library (its "kernel innovation" section); the pages never print KDA's
+// recurrence.  The reading taken here: one decay per key channel, applied to
+// the state before the delta correction,
+//     S_t = (I - beta_t k_t k_t^T) diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T,
+//     o_t = scale * S_t^T q_t,                 g_t in R^dk,
+// which is the gated delta rule when every channel decays alike.
+//
+// Chunk form (chunks of 64 tokens, G_r = in-chunk cumulative sum of g per key
+// channel, H = the dk x dv state entering the chunk):
+//     U  = (I + strict_lower(diag(beta) Kt Kh^T))^-1 diag(beta) (V - Kt H)
+//     O  = scale (Qt H + lower(Qt Kh^T) U)
+//     H' = diag(exp(G_C)) H + (K o exp(G_C - G))^T U
+// with Kt = K o exp(G), Kh = K o exp(-G), Qt = Q o exp(G) row by row: the
+// scalar gate factors of the GDN chunk step become per-channel factors inside
+// the operands, so they are applied to the K and Q tiles before the products
+// instead of as row and column scalings after them (the talk summary's EXP
+// consolidation, paragraph 6, does not carry over: exp(G_r - G_s) no longer
+// factors into one number per row and column).
+//
+// Range: Kt Kh^T only enters for s <= r, where every factor exp(G_r - G_s) is
+// at most 1, but the two operands carry exp(G) and exp(-G) separately.  Each
+// 32-token half of the chunk is therefore re-centred at the cumulative decay of
+// its middle token (diagonal blocks: factors within exp(|decay over 16
+// tokens|)), and the off-diagonal block (rows in the second half, columns in the
+// first) at the decay of token 31, the boundary, where both factors are at most
+// 1.  The exact products Kt H and Qt H use the re-centred tiles against state
+// rows scaled by exp(centre) (at most 1).  Results are finite whenever no key
+// channel decays by more than exp(-176) over 16 consecutive tokens of a chunk.
+//
+// One workgroup (eight waves) per (batch, head) runs the chunks in order; per
+// chunk: all waves load the K, Q, V tiles and form the re-centred tiles in LDS;
+// waves 4-7 then build the inverse blocks and the masked score blocks while
+// waves 0-3, each owning 32 state columns in MFMA accumulators, form Kt H and
+// Qt H; after a barrier the state waves solve for U by block forward
+// substitution, write the outputs and update the state.
+#include "gdn_chunk.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kKdaThreads = 512;
+
+struct KdaSmem {
+    __bf16 ku[kChunk * kDk];   // raw K, then K o exp(G_C - G)
+    __bf16 qc[kChunk * kDk];   // raw Q, then Q o exp(G - c_half)
+    __bf16 kc[kChunk * kDk];   // K o exp(G - c_half)
+    __bf16 kd[kChunk * kDk];   // K o exp(c_half - G)
+    __bf16 bnd[kChunk * kDk];  // rows 0-31: K o exp(G_31 - G); rows 32-63: K o exp(G - G_31)
+    __bf16 bq[kChunk * kDk];   // rows 0-31: Q of tokens 32-63 o exp(G - G_31)
+    __bf16 vt[kChunk * kDv];   // V
+    __bf16 t32[6][kT32];       // Tt_00, Tt_11, -Ah_10, P_00, P_10, P_11 (A-layout 32 x 32 tiles)
+    float ec0[kDk];            // exp(c_0) per key channel (c_0 = G at token 15)
+    float ec1[kDk];            // exp(c_1) (c_1 = G at token 47)
+    float eC[kDk];             // exp(G_C)
+    float psum[4][kDk];        // per key channel: sums of g over tokens 16p .. 16p + 15
+    float beta[kChunk];
+};
+
+// Inverse of (I + Nd) for one 32 x 32 diagonal block, Nd = diag(beta)
+// strict_lower(S), given acc(S) and acc(S^T) (S is not symmetric here).
+// Returns acc(T0^T): lane n holds row n of T0.  The product series
+// (I + M)(I + M^2)(I + M^4)(I + M^8)(I + M^16), M = -Nd, is exact (M^32 = 0).
+__device__ __forceinline__ f32x16 kda_diag_inverse_t(const f32x16& S, const f32x16& St, const f32x16& beta_rows,
+                                                     float beta_n, int n, int g) {
+    f32x16 m, mt, zt;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = rho(g, r);
+        m[r] = (n < row) ? -beta_rows[r] * S[r] : 0.f;   // M[row][n]
+        mt[r] = (row < n) ? -beta_n * St[r] : 0.f;       // M^T[row][n] = M[n][row]
+        const float id = (row == n) ? 1.f : 0.f;
+        zt[r] = id + mt[r];
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const f32x16 m2 = mm_acc<__bf16>(mt, m, zero16());    // M^(2^(it+1))
+        const f32x16 m2t = mm_acc<__bf16>(m, mt, zero16());   // its transpose
+        m = m2;
+        mt = m2t;
+        zt = mm_acc<__bf16>(m, zt, zt);                       // Z^T (I + M^(2^(it+1)))^T
+    }
+    return zt;
+}
+
+// A 32 x 32 block written as an A-layout tile (lane n = row n): values x[r] at
+// row n, column rho(g, r), times `s` and masked to columns <= n when `lower`.
+__device__ __forceinline__ void put_block(const Lane<__bf16>& L, __bf16* tile, const f32x16& x, float s,
+                                          bool lower) {
+#pragma unroll
+    for (int ksl = 0; ksl < 2; ++ksl) {
+        bf16x8 f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = 8 * ksl + j;
+            f[j] = (__bf16)((!lower || rho(L.g, r) <= L.n) ? s * x[r] : 0.f);
+        }
+        L.st32(tile, ksl, f);
+    }
+}
+
+// acc(X Y^T) for rows 32 xr + (0..31) of tile X and rows 32 yr + (0..31) of tile
+// Y (both 64 x 128 row-major): lane n holds (Y X^T)[n][rho].
+__device__ __forceinline__ f32x16 rows_product(const Lane<__bf16>& L, const __bf16* X, int xr, const __bf16* Y,
+                                               int yr) {
+    f32x16 a = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) a = mma(L.f128(X, xr, ks), L.f128(Y, yr, ks), a);
+    return a;
+}
+
+// Prep wave pw (0..3) of one chunk.
+__device__ __forceinline__ void kda_prep(const Lane<__bf16>& L, KdaSmem& sm, int pw) {
+    const int n = L.n, g = L.g;
+    if (pw < 2) {
+        // diagonal block p: S = Kc_p Kd_p^T, T0_pp by the series, Tt_pp = T0_pp diag(beta)
+        const int p = pw;
+        const f32x16 S = rows_product(L, sm.kc, p, sm.kd, p);    // acc(Kc Kd^T): [rho][n] = kc_rho . kd_n
+        const f32x16 St = rows_product(L, sm.kd, p, sm.kc, p);   // acc(S^T)
+        const f32x16 brow = rows_of(sm.beta, p, g);
+        const f32x16 zt = kda_diag_inverse_t(S, St, brow, sm.beta[32 * p + n], n, g);
+        f32x16 tt;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tt[r] = zt[r] * brow[r];
+        put_block(L, sm.t32[p], tt, 1.f, true);
+    } else if (pw == 2) {
+        // off-diagonal block, rows 32-63 by columns 0-31, centred at token 31:
+        // lane n holds Ah_10[n][rho] = kt_(32+n) . kh_rho
+        const f32x16 x = rows_product(L, sm.bnd, 0, sm.bnd, 1);
+        put_block(L, sm.t32[2], x, -1.f, false);
+    } else {
+        // masked score blocks: P_jj[n][rho] = qt_n . kh_rho (rho <= n), P_10 at the boundary
+        put_block(L, sm.t32[3], rows_product(L, sm.kd, 0, sm.qc, 0), 1.f, true);
+        put_block(L, sm.t32[5], rows_product(L, sm.kd, 1, sm.qc, 1), 1.f, true);
+        put_block(L, sm.t32[4], rows_product(L, sm.bnd, 0, sm.bq, 0), 1.f, false);
+    }
+}
+
+// Steps 1 and 2 of chunk c, run by every wave: the raw K, Q, V tiles (zero past
+// the end of the sequence), beta, the cumulative decays per key channel and the
+// re-centred tiles.  Thread (channel ch, quarter part) owns tokens 16 part ..
+// 16 part + 15 of key channel ch.  Ends with a barrier.
+__device__ __forceinline__ void kda_tiles(const KdaParams& prm, KdaSmem& sm, const TileLoader<__bf16, 8>& TL, int b,
+                                          int h, int c) {
+    const int Tn = uni(prm.T), H = uni(prm.H);
+    const int tid = threadIdx.x;
+    const int ch = tid & (kDk - 1), part = tid >> 7;
+    const int nv = chunk_len(Tn, c);
+    const size_t cb = chunk_base(b, h, Tn, H, c);
+    TL.load(sm.ku, uni((const __bf16*)prm.k) + cb, nv);
+    TL.load(sm.qc, uni((const __bf16*)prm.q) + cb, nv);
+    TL.load(sm.vt, uni((const __bf16*)prm.v) + cb, nv);
+    typedef __attribute__((address_space(1))) const float gfloat;
+    if (tid < kChunk)
+        sm.beta[tid] = tid < nv ? ((gfloat*)uni(prm.beta))[((size_t)b * Tn + (size_t)c * kChunk + tid) * H + h] : 0.f;
+    const float* const gp = uni(prm.g);
+    float gl[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int t = 16 * part + j;
+        gl[j] = t < nv ? ((gfloat*)gp)[(((size_t)b * Tn + (size_t)c * kChunk + t) * H + h) * kDk + ch] : 0.f;
+    }
+    float run = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        run += gl[j];
+        gl[j] = run;
+    }
+    sm.psum[part][ch] = run;
+    wait_vm();
+    __syncthreads();
+    float Gend[4];
+    Gend[0] = sm.psum[0][ch];
+#pragma unroll
+    for (int p = 1; p < 4; ++p) Gend[p] = Gend[p - 1] + sm.psum[p][ch];
+    const float off = part == 0 ? 0.f : Gend[part - 1];
+    const float c0 = Gend[0], gb = Gend[1], c1 = Gend[2], gC = Gend[3];
+    const float centre = part < 2 ? c0 : c1;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int t = 16 * part + j;
+        const float G = off + gl[j];
+        const int e = toff<__bf16, kDk>(t, ch);
+        const float kv = (float)sm.ku[e], qv = (float)sm.qc[e];
+        const float ec = __expf(G - centre), ed = __expf(centre - G);
+        sm.kc[e] = (__bf16)(kv * ec);
+        sm.kd[e] = (__bf16)(kv * ed);
+        sm.qc[e] = (__bf16)(qv * ec);
+        sm.ku[e] = (__bf16)(kv * __expf(gC - G));
+        if (part < 2) {
+            sm.bnd[e] = (__bf16)(kv * __expf(gb - G));
+        } else {
+            const float eb = __expf(G - gb);
+            sm.bnd[e] = (__bf16)(kv * eb);
+            sm.bq[toff<__bf16, kDk>(t - 32, ch)] = (__bf16)(qv * eb);
+        }
+    }
+    if (part == 0) {
+        sm.ec0[ch] = __expf(c0);
+        sm.ec1[ch] = __expf(c1);
+        sm.eC[ch] = __expf(gC);
+    }
+    __syncthreads();
+}
+
+// Waves 4-7: per chunk the shared steps, then the inverse and score blocks.
+// Executes exactly the barriers of kda_state_loop.
+__device__ __noinline__ void kda_prep_loop(const KdaParams& prm, KdaSmem& sm) {
+    const int bh = blockIdx.x, H = uni(prm.H), N = uni(prm.N);
+    const int b = bh / H, h = bh % H;
+    Lane<__bf16> L;
+    L.init(threadIdx.x);
+    TileLoader<__bf16, 8> TL;
+    TL.init(wave_id(), threadIdx.x & 63, H);
+    for (int c = 0; c < N; ++c) {
+        kda_tiles(prm, sm, TL, b, h, c);
+        kda_prep(L, sm, wave_id() - 4);
+        __syncthreads();   // blocks written
+        __syncthreads();   // the state step is done with the tiles
+    }
+}
+
+// Waves 0-3: the state (32 columns per wave, in MFMA accumulators) and the
+// serial chunk step.  Executes exactly the barriers of kda_prep_loop.
+__device__ __noinline__ void kda_state_loop(const KdaParams& prm, KdaSmem& sm) {
+    using F = bf16x8;
+    const int bh = blockIdx.x;
+    const int Tn = uni(prm.T), H = uni(prm.H), N = uni(prm.N);
+    const int b = bh / H, h = bh % H;
+    const int lane = threadIdx.x & 63;
+    const float scale = uni(prm.scale);
+    __bf16* const op = uni((__bf16*)prm.o);
+    Lane<__bf16> L;
+    L.init(threadIdx.x);
+    TileLoader<__bf16, 8> TL;
+    TL.init(wave_id(), lane, H);
+    const int n = L.n, gg = L.g, w = L.w;
+    f32x16 Hs[4];
+    if (prm.h0) {
+        load_state(uni(prm.h0) + (size_t)bh * kDk * kDv, w, lane, Hs);
+    } else {
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) Hs[ht] = zero16();
+    }
+    for (int c = 0; c < N; ++c) {
+        const int nv = chunk_len(Tn, c);
+        kda_tiles(prm, sm, TL, b, h, c);
+        // Kt H and (Qt H)^T: state rows of each k-step scaled by each half's exp(centre)
+        f32x16 X[2], OT[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            X[rt] = zero16();
+            OT[rt] = zero16();
+        }
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const f32x16 s0 = rows_of(sm.ec0, ks >> 1, gg), s1 = rows_of(sm.ec1, ks >> 1, gg);
+            F h0f, h1f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int r = 8 * (ks & 1) + j;
+                h0f[j] = (__bf16)(Hs[ks >> 1][r] * s0[r]);
+                h1f[j] = (__bf16)(Hs[ks >> 1][r] * s1[r]);
+            }
+            h0f = nat_frag<__bf16>(h0f);
+            h1f = nat_frag<__bf16>(h1f);
+            X[0] = mma(L.f128(sm.kc, 0, ks), h0f, X[0]);
+            X[1] = mma(L.f128(sm.kc, 1, ks), h1f, X[1]);
+            OT[0] = mma(h0f, L.f128(sm.qc, 0, ks), OT[0]);
+            OT[1] = mma(h1f, L.f128(sm.qc, 1, ks), OT[1]);
+        }
+        __syncthreads();   // blocks written
+        // Y = V - Kt H, U by block substitution
+        f32x16 Y[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const F v0 = L.trV(sm.vt, 2 * rt), v1 = L.trV(sm.vt, 2 * rt + 1);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                Y[rt][j] = (float)v0[j] - X[rt][j];
+                Y[rt][8 + j] = (float)v1[j] - X[rt][8 + j];
+            }
+        }
+        const F y0f[2] = {acc_frag<__bf16>(Y[0], 0), acc_frag<__bf16>(Y[0], 1)};
+        f32x16 Vp[2];
+        block_solve<__bf16>(L, sm.t32[0], sm.t32[1], sm.t32[2], y0f, Y[1], Vp);
+        F vf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) vf[ks] = acc_frag<__bf16>(Vp[ks >> 1], ks & 1);
+        // O^T = (Qt H)^T + U^T P^T; P^T's B fragments are rows of P
+        OT[0] = mma(vf[0], L.f32(sm.t32[3], 0), OT[0]);
+        OT[0] = mma(vf[1], L.f32(sm.t32[3], 1), OT[0]);
+        OT[1] = mma(vf[0], L.f32(sm.t32[4], 0), OT[1]);
+        OT[1] = mma(vf[1], L.f32(sm.t32[4], 1), OT[1]);
+        OT[1] = mma(vf[2], L.f32(sm.t32[5], 0), OT[1]);
+        OT[1] = mma(vf[3], L.f32(sm.t32[5], 1), OT[1]);
+        // H <- diag(exp(G_C)) H + (K o exp(G_C - G))^T U
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) Hs[ht] = Hs[ht] * rows_of(sm.eC, ht, gg);
+        kt_update<__bf16>(L, sm.ku, Hs, 1.f, vf);
+        // outputs: lane (n, g) holds state columns 8i + 4g .. +3 of row 32rt + n;
+        // two half-wave lane swaps give it columns 8g .. +7 and 16 + 8g .. +7
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int pos = 32 * rt + n;
+            uint32_t pk[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+                const b2 pr = {(__bf16)(scale * OT[rt][2 * k]), (__bf16)(scale * OT[rt][2 * k + 1])};
+                pk[k] = __builtin_bit_cast(uint32_t, pr);
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const auto r = __builtin_amdgcn_permlane32_swap(pk[4 * q + e], pk[4 * q + 2 + e], false, false);
+                    pk[4 * q + e] = r[0];
+                    pk[4 * q + 2 + e] = r[1];
+                }
+            }
+            if (pos < nv) {
+                typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+                typedef __attribute__((address_space(1))) u4 gu4;
+                __bf16* const orow = op + (((size_t)b * Tn + (size_t)c * kChunk + pos) * H + h) * kDv + 32 * w;
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const u4 v = {pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]};
+                    *(gu4*)(orow + 16 * q + 8 * gg) = v;
+                }
+            }
+        }
+        __syncthreads();   // the tiles are free for the next chunk
+    }
+    if (prm.ht) store_state(uni(prm.ht) + (size_t)bh * kDk * kDv, w, lane, Hs);
+}
+
+__global__ __launch_bounds__(kKdaThreads, 1) void gdn_kda_fwd_kernel(KdaParams prm) {
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    KdaSmem& sm = *reinterpret_cast<KdaSmem*>(smem_raw);
+    // the role branch is wave-uniform: both roles hold barriers
+    if (wave_id() < 4)
+        kda_state_loop(prm, sm);
+    else
+        kda_prep_loop(prm, sm);
+}
+
+}  // namespace
+
+size_t kda_smem_bytes() { return sizeof(KdaSmem); }
+
+hipError_t launch_kda_fwd(const KdaParams& p, hipStream_t s) {
+    static bool configured = false;
+    const size_t lds = sizeof(KdaSmem);
+    if (!configured) {
+        const hipError_t e = hipFuncSetAttribute((const void*)gdn_kda_fwd_kernel,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        configured = true;
+    }
+    hipLaunchKernelGGL(gdn_kda_fwd_kernel, dim3(p.B * p.H), dim3(kKdaThreads), lds, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

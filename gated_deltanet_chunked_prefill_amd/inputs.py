@@ -134,6 +134,49 @@ def generate(B, T, H, dk=128, dv=128, dtype="bf16", gate="softplus_head", gate_l
     return GDNInputs(q=q, k=k, v=v, g=g, beta=beta, h0=h0, dout=do, dtype=dtype, meta=meta)
 
 
+#: Named workloads of the per-key-channel-decay variant (KDA): g is [B,T,H,dk]
+KDA_WORKLOADS = {
+    # bf16 with an initial state; per-(head, channel) decay rates
+    "bf16_kda_t4096_h16": dict(B=1, T=4096, H=16, h0_std=0.02, seed=7),
+    # the throughput shape of the GDN benchmark, for the KDA kernel
+    "bf16_kda_t32768_h32": dict(B=1, T=32768, H=32, h0_std=None, seed=8),
+}
+
+
+def generate_kda(B, T, H, dk=128, dv=128, gate="softplus_channel", gate_lo=-0.3, gate_hi=-0.01,
+                 h0_std=None, seed=0) -> GDNInputs:
+    """Seeded bf16 inputs of the per-key-channel-decay variant: q, k, v, beta as
+    :func:`generate`; g [B,T,H,dk] float32, either -softplus(x) * A_{h,i} with x ~
+    N(0,1) per element and a decay rate A_{h,i} = exp(U[-4,-1]) drawn once per
+    (head, key channel) ("softplus_channel"), or U[gate_lo, gate_hi] per element
+    ("uniform").  Draw order: q, k, v, beta, gate parts, h0."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _normal_rows(rng, (B, T, H, dk), "bf16")
+    k = _normal_rows(rng, (B, T, H, dk), "bf16")
+    v = _plain_normal(rng, (B, T, H, dv), "bf16")
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32)
+    meta = {"gate": gate}
+    if gate == "softplus_channel":
+        rate = np.exp(rng.uniform(-4.0, -1.0, (H, dk)))
+        x = rng.standard_normal((B, T, H, dk))
+        g = (-np.logaddexp(0.0, x) * rate[None, None]).astype(np.float32)
+        meta["rate"] = rate
+    elif gate == "uniform":
+        g = rng.uniform(gate_lo, gate_hi, (B, T, H, dk)).astype(np.float32)
+    else:
+        raise ValueError(f"unknown gate kind {gate!r}")
+    h0 = None
+    if h0_std is not None:
+        h0 = (rng.standard_normal((B, H, dk, dv), dtype=np.float32) * np.float32(h0_std))
+    return GDNInputs(q=q, k=k, v=v, g=g, beta=beta, h0=h0, dout=None, dtype="bf16", meta=meta)
+
+
+def kda_workload(name: str, **overrides) -> GDNInputs:
+    cfg = dict(KDA_WORKLOADS[name])
+    cfg.update(overrides)
+    return generate_kda(**cfg)
+
+
 def workload(name: str, **overrides) -> GDNInputs:
     """Inputs of a named workload; keyword overrides replace any of its fields
     (e.g. ``T=`` to draw a shorter sample with the same distributions)."""

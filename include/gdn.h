@@ -192,6 +192,26 @@ gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
                                 const int32_t* cu_seqlens, int n_seqs, int T, int H, int dk, int dv,
                                 gdn_dtype dtype, float scale, void* stream);
 
+/* Chunked forward of the per-key-channel-decay variant (KDA; the FlashQLA
+ * commentary names it, in its "kernel innovation" section, as the library's
+ * sibling operator of GDN, without printing its recurrence).  The reading:
+ *     S_t = (I - beta_t k_t k_t^T) diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = scale * S_t^T q_t,
+ * with one log-decay per key channel, g_t in R^dk, applied to the state before
+ * the delta correction; with equal channels it is gdn_chunk_fwd's operator.
+ *   q, k, v, o        as for gdn_chunk_fwd, bfloat16 only (GDN_ERR_UNSUPPORTED otherwise)
+ *   g                 [B, T, H, dk] float32, log-decays (<= 0) per key channel
+ *   beta, h0, ht      as for gdn_chunk_fwd (h0, ht nullable)
+ * The chunk step applies the per-channel decay factors to the K and Q tiles
+ * (re-centred per 32-token half, and at the half boundary for the block that
+ * couples the halves), so results are finite as long as no key channel decays
+ * by more than exp(-176) over 16 consecutive tokens of a 64-token chunk.  One
+ * workgroup per (batch, head), chunks in order; no workspace, no sequence split.
+ * Errors as for gdn_chunk_fwd. */
+gdn_status gdn_kda_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                       const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, gdn_dtype dtype,
+                       float scale, void* stream);
+
 /* Workspace bytes for gdn_chunk_bwd_varlen ((size_t)-1 for invalid arguments):
  * the chunk prefix and bounds of the sequences, and per head (ceil(T/64) + 2 n_seqs)
  * bfloat16 128 x 128 states plus (ceil(T/64) + n_seqs) state gradients. */
@@ -273,7 +293,8 @@ typedef enum {
     GDN_LAUNCH_BWD_STATES = 5,  /* backward: state entering every chunk (forward kernel) */
     GDN_LAUNCH_BWD_DH = 6,      /* backward: state gradient, end to start             */
     GDN_LAUNCH_BWD_LOCAL = 7,   /* backward: local gradients of every chunk           */
-    GDN_LAUNCH_FWD_SUMS = 8     /* split forward: chunk sums of g, planner reset      */
+    GDN_LAUNCH_FWD_SUMS = 8,    /* split forward: chunk sums of g, planner reset      */
+    GDN_LAUNCH_KDA_FWD = 9      /* KDA forward                                        */
 } gdn_launch_kind;
 
 /* Measurement hook (the talk summary, paragraph 7, argues the fused operator

@@ -247,3 +247,20 @@ def test_varlen_prefix_spans_stay_in_slots(case):
         assert nch[s] == 0 or cstart[s] + nch[s] - 1 < cmax
     if case == "valid":
         assert bnd == cu
+
+
+def test_kda_validation_before_launch():
+    """gdn_kda_fwd: bf16 only, the forward's argument checks, nothing launched."""
+    lib = _lib.load()
+    A = 1 << 20
+    P = lambda a: ctypes.c_void_p(a) if a else None
+
+    def call(q=A, g=A, dt=1, T=128, H=1, dk=128):
+        return lib.gdn_kda_fwd(P(q), P(A), P(A), P(g), P(A), None, P(A), None, 1, T, H, dk, 128, dt, 1.0, None)
+    assert call(q=0) == _lib.GDN_ERR_INVALID_ARG
+    assert call(g=0) == _lib.GDN_ERR_INVALID_ARG
+    assert call(dt=0) == _lib.GDN_ERR_UNSUPPORTED
+    assert "bf16" in _lib.last_error()
+    assert call(dk=64) == _lib.GDN_ERR_UNSUPPORTED
+    assert call(T=0) == _lib.GDN_ERR_INVALID_ARG
+    assert call(g=A + 2) == _lib.GDN_ERR_INVALID_ARG
