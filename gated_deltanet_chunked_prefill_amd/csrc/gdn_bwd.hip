@@ -337,18 +337,28 @@ struct LocalSmem {
     T vt[kChunk * kDv];     // V, then V'
     T dot[kChunk * kDv];    // dO
     T dyt[kChunk * kDv];    // dY
-    T pm[kT64];             // 64 x 64 tiles (toff<T, 64> layout)
-    T mg[kT64];
-    T tg[kT64];             // diagonal blocks of the gated inverse T (beta-free)
-    T dpg[kT64];            // dPm o Sg
-    T dmg[kT64];            // dMg o Sg
-    float xs[kChunk][kChunk + 1];   // X = dPm o Pm + dMg o Mg
+    // One region, three lives: the 64 x 64 score tiles Pm, Mg and the diagonal
+    // blocks of the gated inverse (phases 1-2); the chunk's entering state and
+    // its gradient as four 64 x 128 tiles, rows = dv (the state-row products);
+    // the gradient tiles dPm o Sg, dMg o Sg (the dq, dk products).
+    T reg[4 * kChunk * kDk];
     float gam[kChunk];
     float Gam[kChunk];
     float E[kChunk];
     float beta[kChunk];
     float part[4][4][kChunk];       // per wave: dbeta, q.dq2, k.dk3, k.dk4 partial row sums
+    float xrow[4][32];              // per wave: row sums of its 32 x 32 tile of X = dPm o Pm + dMg o Mg
+    float xcol[4][32];              // per wave: column sums of that tile
     float red[4];
+    __device__ T* pm() { return reg; }
+    __device__ T* mg() { return reg + kT64; }
+    __device__ T* tg() { return reg + 2 * kT64; }   // diagonal blocks of the gated inverse T (beta-free)
+    __device__ T* st(int i) { return reg + i * kChunk * kDk; }   // 0, 1: H rows 0-63, 64-127; 2, 3: dHn
+    __device__ T* dpg() { return reg; }             // dPm o Sg
+    __device__ T* dmg() { return reg + kT64; }      // dMg o Sg
+    __device__ const T* pm() const { return reg; }
+    __device__ const T* mg() const { return reg + kT64; }
+    __device__ const T* tg() const { return reg + 2 * kT64; }
 };
 
 // B fragment of a stored state (bf16, transposed [dv][dk]), contraction over
@@ -360,32 +370,77 @@ __device__ __forceinline__ typename FragOf<T>::type state_colfrag(const __bf16* 
     typedef __attribute__((address_space(1))) const typename FragOf<T>::type gfrag;
     return *(gfrag*)(St + (size_t)col * kDk + 16 * ks + 8 * g);
 }
-// B fragment of the transposed state (contraction over its dv columns), same
-// order: lane (n, g) gets S[row][16ks + 8g + j] (a column of the stored layout).
+// Transposed fragment of a 64 x 128 LDS tile in the contraction order of the
+// 16-byte tile fragments: lane (n, g) gets tile[16 ks + 8 g + j][nbase + n],
+// j = 0..7 (two ds_read_b64_tr_b16, each giving four consecutive rows).
 template <typename T>
-__device__ __forceinline__ typename FragOf<T>::type state_rowfrag(const __bf16* St, int row, int ks, int g) {
+__device__ __forceinline__ typename FragOf<T>::type tfrag_nat(const T* tile, int nbase, int ks, int lane) {
     static_assert(sizeof(T) == 2, "the backward is built for bf16 only");
-    typedef __attribute__((address_space(1))) const __bf16 gbf;
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    const int g = lane >> 5, i = lane & 15, n0 = nbase + (lane & 16);
     typename FragOf<T>::type f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) f[j] = ((gbf*)St)[(size_t)(16 * ks + 8 * g + j) * kDk + row];
+    for (int h = 0; h < 2; ++h) {
+        const T* p = tile + toff<T, kDk>(16 * ks + 8 * g + 4 * h + (i >> 2), n0 + 4 * (i & 3));
+        const s4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s4*)(__attribute__((address_space(3))) void*)p);
+        const typename Quad<T>::type q = __builtin_bit_cast(typename Quad<T>::type, r);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[4 * h + j] = q[j];
+    }
     return f;
 }
 
-// Sum of each accumulator row over the 32 lanes of its half-wave; lane n == 0 of
-// each half writes dst[32 rt + rho(g, r)].
-__device__ __forceinline__ void row_sums(float* dst, f32x16 v, int rt, int g, int n) {
+// Sum of each accumulator row over the 32 lanes of its half-wave, written to
+// dst[32 rt + rho(g, r)].  A reduce-scatter: each exchange halves the registers a
+// lane carries (it keeps the half its partner does not), so 16 rows cost 8
+// v_permlane16_swap (lanes n, n ^ 16) and 15 DPP moves (partners n ^ 8, n ^ 7,
+// n ^ 2, n ^ 1) instead of a five-step butterfly per row.  Afterwards lanes
+// n and n ^ 1 hold the sum of register n >> 1; the even lane writes it.
+__device__ __forceinline__ void row_sums(float* dst, const f32x16& v, int rt, int g, int n) {
+    float a[8];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        float x = v[r];
-#pragma unroll
-        for (int d = 1; d < 32; d <<= 1) x += __shfl_xor(x, d, 64);
-        v[r] = x;
+    for (int i = 0; i < 8; ++i) {
+        // even rows of 16 keep registers 0..7, odd rows 8..15: the swap hands the
+        // odd row its partner's register i + 8 and the even row its partner's i
+        // (__builtin_bit_cast of a vector element reads element 0 with this
+        // toolchain; the intrinsic conversions take the element's value)
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 8]),
+                                                        false, false);
+        a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
-    if (n == 0) {
+    const bool b3 = (n >> 3) & 1, b2 = (n >> 2) & 1, b1 = (n >> 1) & 1;
+    float b[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dst[32 * rt + rho(g, r)] = v[r];
+    for (int i = 0; i < 4; ++i) {
+        const float send = b3 ? a[i] : a[i + 4];
+        const float keep = b3 ? a[i + 4] : a[i];
+        b[i] = keep + dpp_take<0x128, 0xf>(send);   // row_ror:8, lane n ^ 8
     }
+    float c[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float send = b2 ? b[i] : b[i + 2];
+        const float keep = b2 ? b[i + 2] : b[i];
+        c[i] = keep + dpp_take<0x141, 0xf>(send);   // row_half_mirror, lane n ^ 7
+    }
+    const float send = b1 ? c[0] : c[1];
+    const float keep = b1 ? c[1] : c[0];
+    float d = keep + dpp_take<0x4e, 0xf>(send);     // quad_perm [2,3,0,1], lane n ^ 2
+    d += dpp_take<0xb1, 0xf>(d);                    // quad_perm [1,0,3,2], lane n ^ 1
+    if ((n & 1) == 0) dst[32 * rt + rho(g, n >> 1)] = d;
+}
+
+// Column sums of an accumulator tile (over its 32 rows, both half-waves):
+// written by the g = 0 half to dst[n].
+__device__ __forceinline__ void col_sums(float* dst, const f32x16& v, int g, int n) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += v[r];
+    const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    // x[0] holds, in the upper half-wave, the lower half's value; x[1] the reverse
+    const float other = __uint_as_float(g ? x[0] : x[1]);
+    if (g == 0) dst[n] = s + other;
 }
 
 // Store an accumulator tile (rows 32 ti + rho, column 32 tj + n) into a 64 x 64 tile.
@@ -420,6 +475,35 @@ __device__ __forceinline__ void copy_tile_rows(T* dst, const T* tile, int H, int
     }
 }
 
+// Tile (ti, tj) of the gated score matrices, ti >= tj: Pm = tril(Q K^T) o Sg and
+// Mg = strict_lower(K K^T) o Sg with Sg_rs = exp(gamma_r - gamma_s) (s <= r), in
+// accumulator form (rows 32 ti + rho, column 32 tj + n); skk returns the raw K K^T
+// tile.  Recomputed where needed rather than carried in registers between phases.
+template <typename T>
+__device__ __forceinline__ void score_tiles(const Lane<T>& L, const LocalSmem<T>& sm, int ti, int tj,
+                                            f32x16& Pm, f32x16& Mg, f32x16& SG, f32x16& skk) {
+    using F = typename FragOf<T>::type;
+    const int n = L.n, g = L.g;
+    f32x16 sqk = zero16();
+    skk = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        const F kf = L.f128(sm.kt, tj, ks);
+        sqk = mma(L.f128(sm.qt, ti, ks), kf, sqk);
+        skk = mma(L.f128(sm.kt, ti, ks), kf, skk);
+    }
+    const f32x16 gr = rows_of(sm.gam, ti, g);
+    const float gs = sm.gam[32 * tj + n];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int R = 32 * ti + rho(g, r), S = 32 * tj + n;
+        const float sg = R >= S ? __expf(gr[r] - gs) : 0.f;
+        SG[r] = sg;
+        Pm[r] = sqk[r] * sg;
+        Mg[r] = R > S ? skk[r] * sg : 0.f;
+    }
+}
+
 // The local gradients of chunk c of head bh (one workgroup).
 template <typename T>
 __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) {
@@ -439,7 +523,14 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
     const __bf16* const Hc = prm.hstore + ((size_t)bh * (N + 1) + c) * SS;
     const __bf16* const dHn = prm.dhstore + ((size_t)bh * N + c) * SS;
 
-    // ---- phase 0: tiles, gates
+    // ---- phase 0: tiles, gates; the state fragments of phase 2 are requested
+    // first, so their latency runs under the tile loads'
+    F hcf[8], dhf[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        hcf[ks] = state_colfrag<T>(Hc, ks, g, 32 * w + n);
+        dhf[ks] = state_colfrag<T>(dHn, ks, g, 32 * w + n);
+    }
     {
         TileLoader<T> TL;
         TL.init(w, lane, H);
@@ -464,25 +555,11 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
 
     // ---- phase 1: 64 x 64 tile (ti, tj) of the score matrices
     const int ti = w >> 1, tj = w & 1;
-    f32x16 Pm = zero16(), Mg = zero16(), SG = zero16();
+    {
+    f32x16 Pm = zero16(), Mg = zero16(), SG, skk;
     if (ti >= tj) {
-        f32x16 sqk = zero16(), skk = zero16();
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const F kf = L.f128(sm.kt, tj, ks);
-            sqk = mma(L.f128(sm.qt, ti, ks), kf, sqk);
-            skk = mma(L.f128(sm.kt, ti, ks), kf, skk);
-        }
+        score_tiles<T>(L, sm, ti, tj, Pm, Mg, SG, skk);
         const f32x16 gr = rows_of(sm.gam, ti, g);
-        const float gs = sm.gam[32 * tj + n];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int R = 32 * ti + rho(g, r), S = 32 * tj + n;
-            const float sg = R >= S ? __expf(gr[r] - gs) : 0.f;
-            SG[r] = sg;
-            Pm[r] = sqk[r] * sg;
-            Mg[r] = R > S ? skk[r] * sg : 0.f;
-        }
         if (ti == tj) {
             // diagonal block p: T_pp = diag(Gamma) T0_pp diag(1/Gamma), T0_pp gate-free
             const int p = ti;
@@ -494,12 +571,13 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
             for (int r = 0; r < 16; ++r) {
                 const int col = rho(g, r);
                 const float t = col <= n ? zt[r] * __expf(gn - gr[r]) : 0.f;
-                sm.tg[toff<T, 64>(32 * p + n, 32 * p + col)] = (T)t;
+                sm.tg()[toff<T, 64>(32 * p + n, 32 * p + col)] = (T)t;
             }
         }
     }
-    st_tile64<T>(sm.pm, Pm, ti, tj, g, n);
-    st_tile64<T>(sm.mg, Mg, ti, tj, g, n);
+    st_tile64<T>(sm.pm(), Pm, ti, tj, g, n);
+    st_tile64<T>(sm.mg(), Mg, ti, tj, g, n);
+    }
     lds_barrier();
 
     // ---- phase 2: this wave's 32 dv columns of Y, V', dV', dY
@@ -512,11 +590,11 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
         f32x16 KH[2] = {zero16(), zero16()};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            const F hf = state_colfrag<T>(Hc, ks, g, 32 * w + n);
+            const F hf = hcf[ks];
             KH[0] = mma(L.f128(sm.kt, 0, ks), hf, KH[0]);
             KH[1] = mma(L.f128(sm.kt, 1, ks), hf, KH[1]);
             // <dHn, Hc> over this wave's columns (the same elements of dHn)
-            const F df = state_colfrag<T>(dHn, ks, g, 32 * w + n);
+            const F df = dhf[ks];
 #pragma unroll
             for (int j = 0; j < 8; ++j) hc_dot += (float)hf[j] * (float)df[j];
         }
@@ -539,30 +617,30 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
         const f32x16 z0 = Y[0] * be0;
         Vp[0] = zero16();
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) Vp[0] = mma(afrag<T, 64>(sm.tg, n, ks, g), acc_frag<T>(z0, ks), Vp[0]);
+        for (int ks = 0; ks < 2; ++ks) Vp[0] = mma(afrag<T, 64>(sm.tg(), n, ks, g), acc_frag<T>(z0, ks), Vp[0]);
         f32x16 w10 = zero16();
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const F vf = acc_frag<T>(Vp[0], ks);
-            w10 = mma(afrag<T, 64>(sm.mg, 32 + n, ks, g), vf, w10);
-            MgV0 = mma(afrag<T, 64>(sm.mg, n, ks, g), vf, MgV0);
+            w10 = mma(afrag<T, 64>(sm.mg(), 32 + n, ks, g), vf, w10);
+            MgV0 = mma(afrag<T, 64>(sm.mg(), n, ks, g), vf, MgV0);
         }
         const f32x16 z1 = (Y[1] - w10) * be1;
         Vp[1] = zero16();
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            Vp[1] = mma(afrag<T, 64>(sm.tg, 32 + n, 2 + ks, g), acc_frag<T>(z1, ks), Vp[1]);
+            Vp[1] = mma(afrag<T, 64>(sm.tg(), 32 + n, 2 + ks, g), acc_frag<T>(z1, ks), Vp[1]);
         MgV1 = w10;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            MgV1 = mma(afrag<T, 64>(sm.mg, 32 + n, 2 + ks, g), acc_frag<T>(Vp[1], ks), MgV1);
+            MgV1 = mma(afrag<T, 64>(sm.mg(), 32 + n, 2 + ks, g), acc_frag<T>(Vp[1], ks), MgV1);
     }
     {
         // dV' = scale Pm^T dO + diag(E) K dHn
         f32x16 KdH[2] = {zero16(), zero16()};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            const F hf = state_colfrag<T>(dHn, ks, g, 32 * w + n);
+            const F hf = dhf[ks];
             KdH[0] = mma(L.f128(sm.kt, 0, ks), hf, KdH[0]);
             KdH[1] = mma(L.f128(sm.kt, 1, ks), hf, KdH[1]);
         }
@@ -570,8 +648,8 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const F df = L.trV(sm.dot, ks);
-            PdO[0] = mma(tfrag<T, 64>(sm.pm, 0, ks, lane), df, PdO[0]);
-            if (ks >= 2) PdO[1] = mma(tfrag<T, 64>(sm.pm, 32, ks, lane), df, PdO[1]);
+            PdO[0] = mma(tfrag<T, 64>(sm.pm(), 0, ks, lane), df, PdO[0]);
+            if (ks >= 2) PdO[1] = mma(tfrag<T, 64>(sm.pm(), 32, ks, lane), df, PdO[1]);
         }
         f32x16 dVp[2];
 #pragma unroll
@@ -585,15 +663,15 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
         dZ[1] = zero16();
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            dZ[1] = mma(tfrag<T, 64>(sm.tg, 32, 2 + ks, lane), acc_frag<T>(dVp[1], ks), dZ[1]);
+            dZ[1] = mma(tfrag<T, 64>(sm.tg(), 32, 2 + ks, lane), acc_frag<T>(dVp[1], ks), dZ[1]);
         dY[1] = dZ[1] * be1;
         f32x16 u = zero16();
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) u = mma(tfrag<T, 64>(sm.mg, 0, 2 + ks, lane), acc_frag<T>(dY[1], ks), u);
+        for (int ks = 0; ks < 2; ++ks) u = mma(tfrag<T, 64>(sm.mg(), 0, 2 + ks, lane), acc_frag<T>(dY[1], ks), u);
         const f32x16 t0v = dVp[0] - u;
         dZ[0] = zero16();
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) dZ[0] = mma(tfrag<T, 64>(sm.tg, 0, ks, lane), acc_frag<T>(t0v, ks), dZ[0]);
+        for (int ks = 0; ks < 2; ++ks) dZ[0] = mma(tfrag<T, 64>(sm.tg(), 0, ks, lane), acc_frag<T>(t0v, ks), dZ[0]);
         dY[0] = dZ[0] * be0;
     }
     // dbeta partial over this wave's columns; V' and dY to LDS (dv = dY goes to
@@ -610,11 +688,24 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
     }
     lds_barrier();
 
-    // ---- phase 3: 64 x 64 gradient tiles
-    copy_tile_rows<T>((T*)prm.dv + (((size_t)b * Tn + t0) * H + h) * kDv, sm.dyt, H, nv, tid);
+    // ---- phase 3: the chunk's entering state and its gradient go to the shared
+    // region (the score tiles are dead) while the 64 x 64 gradient tiles are
+    // formed in registers
     {
-        f32x16 dPm = zero16(), dMg = zero16();
+        TileLoader<T> TL;
+        TL.init(w, lane, 1);   // rows of 128 contiguous elements
+        TL.load(sm.st(0), (const T*)Hc, kChunk);
+        TL.load(sm.st(1), (const T*)Hc + kChunk * kDk, kChunk);
+        TL.load(sm.st(2), (const T*)dHn, kChunk);
+        TL.load(sm.st(3), (const T*)dHn + kChunk * kDk, kChunk);
+    }
+    copy_tile_rows<T>((T*)prm.dv + (((size_t)b * Tn + t0) * H + h) * kDv, sm.dyt, H, nv, tid);
+    f32x16 dpS, dmS;   // dPm o Sg, dMg o Sg
+    {
+        f32x16 dPm = zero16(), dMg = zero16(), Pm = zero16(), Mg = zero16(), SG = zero16();
         if (ti >= tj) {
+            f32x16 skk;
+            score_tiles<T>(L, sm, ti, tj, Pm, Mg, SG, skk);
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
                 const F vf = L.f128(sm.vt, tj, ks);
@@ -629,11 +720,12 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
             }
         }
         const f32x16 X = dPm * Pm + dMg * Mg;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sm.xs[32 * ti + rho(g, r)][32 * tj + n] = X[r];
-        st_tile64<T>(sm.dpg, dPm * SG, ti, tj, g, n);
-        st_tile64<T>(sm.dmg, dMg * SG, ti, tj, g, n);
+        row_sums(sm.xrow[w], X, 0, g, n);
+        col_sums(sm.xcol[w], X, g, n);
+        dpS = dPm * SG;
+        dmS = dMg * SG;
     }
+    wait_vm();
     lds_barrier();
 
     // ---- phase 4: this wave's 32 dk columns of dq and dk
@@ -642,9 +734,9 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
         f32x16 a2[2] = {zero16(), zero16()}, a3[2] = {zero16(), zero16()}, a4[2] = {zero16(), zero16()};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            const F hr = state_rowfrag<T>(Hc, 32 * w + n, ks, g);
-            const F dr = state_rowfrag<T>(dHn, 32 * w + n, ks, g);
-
+            // state rows 32w + n over dv = 16 ks + 8 g + j (the stored layout is [dv][dk])
+            const F hr = tfrag_nat<T>(sm.st(ks >> 2), 32 * w, ks & 3, lane);
+            const F dr = tfrag_nat<T>(sm.st(2 + (ks >> 2)), 32 * w, ks & 3, lane);
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
                 a2[rt] = mma(L.f128(sm.dot, rt, ks), hr, a2[rt]);
@@ -652,6 +744,10 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
                 a4[rt] = mma(L.f128(sm.vt, rt, ks), dr, a4[rt]);
             }
         }
+        lds_barrier();   // the states are dead: the gradient tiles take the region
+        st_tile64<T>(sm.dpg(), dpS, ti, tj, g, n);
+        st_tile64<T>(sm.dmg(), dmS, ti, tj, g, n);
+        lds_barrier();
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             dq[rt] = zero16();
@@ -660,10 +756,10 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
             for (int ks = 0; ks < 4; ++ks) {
                 const F kf = L.trK(sm.kt, w, ks);
                 const F qf = L.trK(sm.qt, w, ks);
-                dq[rt] = mma(afrag<T, 64>(sm.dpg, 32 * rt + n, ks, g), kf, dq[rt]);
-                dk[rt] = mma(tfrag<T, 64>(sm.dpg, 32 * rt, ks, lane), qf, dk[rt]);
-                dk[rt] = mma(afrag<T, 64>(sm.dmg, 32 * rt + n, ks, g), kf, dk[rt]);
-                dk[rt] = mma(tfrag<T, 64>(sm.dmg, 32 * rt, ks, lane), kf, dk[rt]);
+                dq[rt] = mma(afrag<T, 64>(sm.dpg(), 32 * rt + n, ks, g), kf, dq[rt]);
+                dk[rt] = mma(tfrag<T, 64>(sm.dpg(), 32 * rt, ks, lane), qf, dk[rt]);
+                dk[rt] = mma(afrag<T, 64>(sm.dmg(), 32 * rt + n, ks, g), kf, dk[rt]);
+                dk[rt] = mma(tfrag<T, 64>(sm.dmg(), 32 * rt, ks, lane), kf, dk[rt]);
             }
             const f32x16 G = rows_of(sm.Gam, rt, g), E = rows_of(sm.E, rt, g);
             const f32x16 dq2 = a2[rt] * G * scale;
@@ -710,12 +806,11 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
 
     // ---- phase 6: dgamma, reverse cumulative sum, dbeta
     if (w == 0) {
-        const int r = lane;
-        float rs = 0.f, cs = 0.f;
-        for (int s = 0; s < kChunk; ++s) {
-            rs += sm.xs[r][s];
-            cs += sm.xs[s][r];
-        }
+        const int r = lane, rl = r & 31;
+        // wave 2 ti + tj holds the tile (ti, tj): rows of tile ti come from waves
+        // 2 ti and 2 ti + 1, columns of tile tj from waves tj and 2 + tj
+        const float rs = r < 32 ? sm.xrow[0][rl] + sm.xrow[1][rl] : sm.xrow[2][rl] + sm.xrow[3][rl];
+        const float cs = r < 32 ? sm.xcol[0][rl] + sm.xcol[2][rl] : sm.xcol[1][rl] + sm.xcol[3][rl];
         float dgam = rs - cs, db = 0.f;
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
