@@ -49,6 +49,11 @@ constexpr int kDhThreads = 512;     // 4 gradient waves + 4 prep waves
 // run-to-run different state gradients from the second chunk on, and is off.
 constexpr bool kDhPipelined = false;
 constexpr int kLocalThreads = 256;  // 4 waves
+// direct state loads per wave in the local-gradient kernel (four 64 x 128 tiles)
+constexpr int kStateLoads = 16;
+// s_waitcnt immediate for vmcnt(n) alone, n < 64 (vmcnt in bits 3:0 and 15:14;
+// expcnt and lgkmcnt at their maxima, as in vmcnt(0) = 0x3f70)
+constexpr int vmcnt_wait(int n) { return 0x3f70 | (n & 15) | (((n >> 4) & 3) << 14); }
 
 // ---------------------------------------------------------------------------
 // Launch 1: reverse sweep of the state gradient.
@@ -336,12 +341,14 @@ struct LocalSmem {
     T kt[kChunk * kDk];
     T vt[kChunk * kDv];     // V, then V'
     T dot[kChunk * kDv];    // dO
-    T dyt[kChunk * kDv];    // dY
-    // One region, three lives: the 64 x 64 score tiles Pm, Mg and the diagonal
-    // blocks of the gated inverse (phases 1-2); the chunk's entering state and
-    // its gradient as four 64 x 128 tiles, rows = dv (the state-row products);
-    // the gradient tiles dPm o Sg, dMg o Sg (the dq, dk products).
-    T reg[4 * kChunk * kDk];
+    // the 64 x 64 score tiles Pm, Mg and the diagonal blocks of the gated
+    // inverse (phases 1-2), then dY as a 64 x 128 tile
+    T sc[3 * kT64];
+    // the chunk's entering state and its gradient, stored layout [dv][dk], as
+    // four 64 x 128 tiles (rows dv 0-63, 64-127 of each), then the gradient
+    // tiles dPm o Sg, dMg o Sg
+    T stt[4 * kChunk * kDk];
+    float gst[2][kChunk];           // g and beta of the chunk as loaded (zero past the end)
     float gam[kChunk];
     float Gam[kChunk];
     float E[kChunk];
@@ -350,16 +357,18 @@ struct LocalSmem {
     float xrow[4][32];              // per wave: row sums of its 32 x 32 tile of X = dPm o Pm + dMg o Mg
     float xcol[4][32];              // per wave: column sums of that tile
     float red[4];
-    __device__ T* pm() { return reg; }
-    __device__ T* mg() { return reg + kT64; }
-    __device__ T* tg() { return reg + 2 * kT64; }   // diagonal blocks of the gated inverse T (beta-free)
-    __device__ T* st(int i) { return reg + i * kChunk * kDk; }   // 0, 1: H rows 0-63, 64-127; 2, 3: dHn
-    __device__ T* dpg() { return reg; }             // dPm o Sg
-    __device__ T* dmg() { return reg + kT64; }      // dMg o Sg
-    __device__ const T* pm() const { return reg; }
-    __device__ const T* mg() const { return reg + kT64; }
-    __device__ const T* tg() const { return reg + 2 * kT64; }
+    __device__ T* pm() { return sc; }
+    __device__ T* mg() { return sc + kT64; }
+    __device__ T* tg() { return sc + 2 * kT64; }    // diagonal blocks of the gated inverse T (beta-free)
+    __device__ T* dyt() { return sc; }
+    __device__ T* st(int i) { return stt + i * kChunk * kDk; }   // 0, 1: H; 2, 3: dHn
+    __device__ T* dpg() { return stt; }             // dPm o Sg
+    __device__ T* dmg() { return stt + kT64; }      // dMg o Sg
+    __device__ const T* pm() const { return sc; }
+    __device__ const T* mg() const { return sc + kT64; }
+    __device__ const T* tg() const { return sc + 2 * kT64; }
 };
+static_assert(sizeof(LocalSmem<__bf16>) <= 160 * 1024, "local-gradient LDS exceeds a CU's 160 KB");
 
 // B fragment of a stored state (bf16, transposed [dv][dk]), contraction over
 // its dk rows, in the column order of the 16-byte tile fragments: lane (n, g)
@@ -523,13 +532,22 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
     const __bf16* const Hc = prm.hstore + ((size_t)bh * (N + 1) + c) * SS;
     const __bf16* const dHn = prm.dhstore + ((size_t)bh * N + c) * SS;
 
-    // ---- phase 0: tiles, gates; the state fragments of phase 2 are requested
-    // first, so their latency runs under the tile loads'
-    F hcf[8], dhf[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-        hcf[ks] = state_colfrag<T>(Hc, ks, g, 32 * w + n);
-        dhf[ks] = state_colfrag<T>(dHn, ks, g, 32 * w + n);
+    // ---- phase 0: g and beta, the tiles, then the entering state and its
+    // gradient (not read before phase 2: their latency runs under phase 1).
+    // Every full-chunk load goes straight to LDS, so no register waits on them.
+    if (w == 0) {
+        const size_t e0 = ((size_t)b * Tn + t0) * H + h;
+        if (nv == kChunk) {
+            __builtin_amdgcn_global_load_lds((const void*)(prm.g + e0 + (size_t)lane * H),
+                                             (__attribute__((address_space(3))) void*)&sm.gst[0][0], 4, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(prm.beta + e0 + (size_t)lane * H),
+                                             (__attribute__((address_space(3))) void*)&sm.gst[1][0], 4, 0, 0);
+        } else {
+            float gv = 0.f, bv = 0.f;
+            load_gate_beta(prm.g, prm.beta, Tn, H, b, h, c, lane, gv, bv);
+            sm.gst[0][lane] = gv;
+            sm.gst[1][lane] = bv;
+        }
     }
     {
         TileLoader<T> TL;
@@ -539,19 +557,32 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
         TL.load(sm.kt, (const T*)prm.k + cb, nv);
         TL.load(sm.vt, (const T*)prm.v + cb, nv);
         TL.load(sm.dot, (const T*)prm.dout + cb, nv);
+        TileLoader<T> TS;
+        TS.init(w, lane, 1);   // rows of 128 contiguous elements
+        static_assert(4 * TileLoader<T>::ROUNDS == kStateLoads, "state loads per wave");
+        TS.load(sm.st(0), (const T*)Hc, kChunk);
+        TS.load(sm.st(1), (const T*)Hc + kChunk * kDk, kChunk);
+        TS.load(sm.st(2), (const T*)dHn, kChunk);
+        TS.load(sm.st(3), (const T*)dHn + kChunk * kDk, kChunk);
     }
-    if (w == 0) {
-        float gv, bv;
-        load_gate_beta(prm.g, prm.beta, Tn, H, b, h, c, lane, gv, bv);
-        const float gam = wave_inclusive_scan(gv);
+    // Memory operations complete in issue order: all but the last kStateLoads
+    // (this wave's state loads) done means g, beta and the tiles are in LDS.  The
+    // barrier is spelled out: an LDS release fence would also wait for the state
+    // loads (direct loads write LDS).
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(kStateLoads) & ~(0x3f << 8));   // and lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    {
+        // the in-chunk gate scan, by every wave (each writes the same values and
+        // reads back only its own writes)
+        const float gam = wave_inclusive_scan(sm.gst[0][lane]);
         const float gC = lane_value(gam, 63);
         sm.gam[lane] = gam;
         sm.Gam[lane] = __expf(gam);
         sm.E[lane] = __expf(gC - gam);
-        sm.beta[lane] = bv;
+        sm.beta[lane] = sm.gst[1][lane];
     }
-    wait_vm();
-    lds_barrier();
 
     // ---- phase 1: 64 x 64 tile (ti, tj) of the score matrices
     const int ti = w >> 1, tj = w & 1;
@@ -580,6 +611,9 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
     }
     lds_barrier();
 
+    wait_vm();       // the staged states
+    lds_barrier();
+
     // ---- phase 2: this wave's 32 dv columns of Y, V', dV', dY
     f32x16 Y[2], Vp[2], dZ[2], dY[2];
     // this lane's part of <dHn, Hn>, with Hn = Gamma_C Hc + K^T diag(E) V' the
@@ -590,11 +624,11 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
         f32x16 KH[2] = {zero16(), zero16()};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            const F hf = hcf[ks];
+            const F hf = L.f128(sm.st(w >> 1), w & 1, ks);   // H rows 32w + n of [dv][dk]
             KH[0] = mma(L.f128(sm.kt, 0, ks), hf, KH[0]);
             KH[1] = mma(L.f128(sm.kt, 1, ks), hf, KH[1]);
             // <dHn, Hc> over this wave's columns (the same elements of dHn)
-            const F df = dhf[ks];
+            const F df = L.f128(sm.st(2 + (w >> 1)), w & 1, ks);
 #pragma unroll
             for (int j = 0; j < 8; ++j) hc_dot += (float)hf[j] * (float)df[j];
         }
@@ -640,7 +674,7 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
         f32x16 KdH[2] = {zero16(), zero16()};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            const F hf = dhf[ks];
+            const F hf = L.f128(sm.st(2 + (w >> 1)), w & 1, ks);
             KdH[0] = mma(L.f128(sm.kt, 0, ks), hf, KdH[0]);
             KdH[1] = mma(L.f128(sm.kt, 1, ks), hf, KdH[1]);
         }
@@ -681,25 +715,16 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
         row_sums(sm.part[w][0], r0, 0, g, n);
         row_sums(sm.part[w][0], r1, 1, g, n);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            st_rows_lds<T>(sm.vt, Vp[rt], rt, g, n, w);
-            st_rows_lds<T>(sm.dyt, dY[rt], rt, g, n, w);
-        }
+        for (int rt = 0; rt < 2; ++rt) st_rows_lds<T>(sm.vt, Vp[rt], rt, g, n, w);
+        lds_barrier();   // the score tiles are dead: dY takes their place
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) st_rows_lds<T>(sm.dyt(), dY[rt], rt, g, n, w);
     }
     lds_barrier();
 
-    // ---- phase 3: the chunk's entering state and its gradient go to the shared
-    // region (the score tiles are dead) while the 64 x 64 gradient tiles are
-    // formed in registers
-    {
-        TileLoader<T> TL;
-        TL.init(w, lane, 1);   // rows of 128 contiguous elements
-        TL.load(sm.st(0), (const T*)Hc, kChunk);
-        TL.load(sm.st(1), (const T*)Hc + kChunk * kDk, kChunk);
-        TL.load(sm.st(2), (const T*)dHn, kChunk);
-        TL.load(sm.st(3), (const T*)dHn + kChunk * kDk, kChunk);
-    }
-    copy_tile_rows<T>((T*)prm.dv + (((size_t)b * Tn + t0) * H + h) * kDv, sm.dyt, H, nv, tid);
+    // ---- phase 3: 64 x 64 gradient tiles, kept in registers until the staged
+    // states are no longer read
+    copy_tile_rows<T>((T*)prm.dv + (((size_t)b * Tn + t0) * H + h) * kDv, sm.dyt(), H, nv, tid);
     f32x16 dpS, dmS;   // dPm o Sg, dMg o Sg
     {
         f32x16 dPm = zero16(), dMg = zero16(), Pm = zero16(), Mg = zero16(), SG = zero16();
@@ -710,7 +735,7 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
             for (int ks = 0; ks < 8; ++ks) {
                 const F vf = L.f128(sm.vt, tj, ks);
                 dPm = mma(L.f128(sm.dot, ti, ks), vf, dPm);
-                dMg = mma(L.f128(sm.dyt, ti, ks), vf, dMg);
+                dMg = mma(L.f128(sm.dyt(), ti, ks), vf, dMg);
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -725,8 +750,6 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
         dpS = dPm * SG;
         dmS = dMg * SG;
     }
-    wait_vm();
-    lds_barrier();
 
     // ---- phase 4: this wave's 32 dk columns of dq and dk
     {
@@ -740,7 +763,7 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
                 a2[rt] = mma(L.f128(sm.dot, rt, ks), hr, a2[rt]);
-                a3[rt] = mma(L.f128(sm.dyt, rt, ks), hr, a3[rt]);
+                a3[rt] = mma(L.f128(sm.dyt(), rt, ks), hr, a3[rt]);
                 a4[rt] = mma(L.f128(sm.vt, rt, ks), dr, a4[rt]);
             }
         }
