@@ -467,6 +467,40 @@ __device__ __forceinline__ void st_rows_lds(T* tile, const f32x16& v, int rt, in
     for (int r = 0; r < 16; ++r) tile[toff<T, kDv>(32 * rt + rho(g, r), 32 * w + n)] = (T)v[r];
 }
 
+// Store the 32 values of a transposed accumulator tile that belong to one row:
+// lane (n, g) holds columns 8i + 4g .. +3 (i = 0..3) of its row; two lane swaps
+// between the half-waves give it columns 8g .. +7 and 16 + 8g .. +7, stored as
+// two 16-byte pieces at row + 8g and row + 16 + 8g (when valid).
+template <typename T>
+__device__ __forceinline__ void store_row_pieces(T* row, const f32x16& v, int g, bool valid) {
+    static_assert(sizeof(T) == 2, "the backward is built for bf16 only");
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    uint32_t pk[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const b2 pr = {(__bf16)v[2 * k], (__bf16)v[2 * k + 1]};
+        pk[k] = __builtin_bit_cast(uint32_t, pr);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const auto r = __builtin_amdgcn_permlane32_swap(pk[4 * q + e], pk[4 * q + 2 + e], false, false);
+            pk[4 * q + e] = r[0];
+            pk[4 * q + 2 + e] = r[1];
+        }
+    }
+    if (valid) {
+        typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(1))) u4 gu4;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const u4 x = {pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]};
+            *(gu4*)(row + 16 * q + 8 * g) = x;
+        }
+    }
+}
+
 // Copy the first nv rows of a swizzled 64 x 128 LDS tile to the rows of a
 // [.., T, H, 128] tensor (dst = the chunk's first row of this head), as
 // 16-byte row pieces: 1024 pieces over the workgroup's threads.
@@ -751,9 +785,10 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
         dmS = dMg * SG;
     }
 
-    // ---- phase 4: this wave's 32 dk columns of dq and dk
+    // ---- phase 4: this wave's 32 dk columns of dq and dk, accumulated transposed
+    // (swapped MFMA operands: lane n = position 32 rt + n, registers = dk rows
+    // 32 w + rho), so that a lane holds row pieces of its position
     {
-        f32x16 dq[2], dk[2];
         f32x16 a2[2] = {zero16(), zero16()}, a3[2] = {zero16(), zero16()}, a4[2] = {zero16(), zero16()};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
@@ -762,9 +797,9 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
             const F dr = tfrag_nat<T>(sm.st(2 + (ks >> 2)), 32 * w, ks & 3, lane);
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                a2[rt] = mma(L.f128(sm.dot, rt, ks), hr, a2[rt]);
-                a3[rt] = mma(L.f128(sm.dyt(), rt, ks), hr, a3[rt]);
-                a4[rt] = mma(L.f128(sm.vt, rt, ks), dr, a4[rt]);
+                a2[rt] = mma(hr, L.f128(sm.dot, rt, ks), a2[rt]);   // (dO H^T)^T
+                a3[rt] = mma(hr, L.f128(sm.dyt(), rt, ks), a3[rt]); // (dY H^T)^T
+                a4[rt] = mma(dr, L.f128(sm.vt, rt, ks), a4[rt]);    // (V' dHn^T)^T
             }
         }
         lds_barrier();   // the states are dead: the gradient tiles take the region
@@ -773,50 +808,44 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
         lds_barrier();
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            dq[rt] = zero16();
-            dk[rt] = zero16();
+            const int pos = 32 * rt + n;
+            f32x16 dqt = zero16(), dkt = zero16();
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const F kf = L.trK(sm.kt, w, ks);
                 const F qf = L.trK(sm.qt, w, ks);
-                dq[rt] = mma(afrag<T, 64>(sm.dpg(), 32 * rt + n, ks, g), kf, dq[rt]);
-                dk[rt] = mma(tfrag<T, 64>(sm.dpg(), 32 * rt, ks, lane), qf, dk[rt]);
-                dk[rt] = mma(afrag<T, 64>(sm.dmg(), 32 * rt + n, ks, g), kf, dk[rt]);
-                dk[rt] = mma(tfrag<T, 64>(sm.dmg(), 32 * rt, ks, lane), kf, dk[rt]);
+                dqt = mma(kf, afrag<T, 64>(sm.dpg(), pos, ks, g), dqt);        // (dPm o Sg  K)^T
+                dkt = mma(qf, tfrag<T, 64>(sm.dpg(), 32 * rt, ks, lane), dkt); // ((dPm o Sg)^T Q)^T
+                dkt = mma(kf, afrag<T, 64>(sm.dmg(), pos, ks, g), dkt);        // (dMg o Sg  K)^T
+                dkt = mma(kf, tfrag<T, 64>(sm.dmg(), 32 * rt, ks, lane), dkt); // ((dMg o Sg)^T K)^T
             }
-            const f32x16 G = rows_of(sm.Gam, rt, g), E = rows_of(sm.E, rt, g);
-            const f32x16 dq2 = a2[rt] * G * scale;
-            const f32x16 dk3 = -(a3[rt] * G);
+            const float G = sm.Gam[pos], E = sm.E[pos];
+            const f32x16 dq2 = a2[rt] * (G * scale);
+            const f32x16 dk3 = a3[rt] * (-G);
             const f32x16 dk4 = a4[rt] * E;
-            dq[rt] = dq[rt] + dq2;
-            dk[rt] = dk[rt] + dk3 + dk4;
-            // q and k of this wave's columns in accumulator layout
-            const F q0 = L.trK(sm.qt, w, 2 * rt), q1 = L.trK(sm.qt, w, 2 * rt + 1);
-            const F k0 = L.trK(sm.kt, w, 2 * rt), k1 = L.trK(sm.kt, w, 2 * rt + 1);
+            dqt = dqt + dq2;
+            dkt = dkt + dk3 + dk4;
+            // q and k of this position at dk rows 32w + rho(g, r): four 4-element reads
             f32x16 pq, pk3, pk4;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                pq[j] = (float)q0[j] * dq2[j];
-                pq[8 + j] = (float)q1[j] * dq2[8 + j];
-                pk3[j] = (float)k0[j] * dk3[j];
-                pk3[8 + j] = (float)k1[j] * dk3[8 + j];
-                pk4[j] = (float)k0[j] * dk4[j];
-                pk4[8 + j] = (float)k1[j] * dk4[8 + j];
-            }
-            row_sums(sm.part[w][1], pq, rt, g, n);
-            row_sums(sm.part[w][2], pk3, rt, g, n);
-            row_sums(sm.part[w][3], pk4, rt, g, n);
-        }
-        // dq and dk through the Q and K tiles (no longer read): row pieces to HBM
-        lds_barrier();
+            for (int i = 0; i < 4; ++i) {
+                typedef typename Quad<T>::type Q4;
+                const Q4 qv = *reinterpret_cast<const Q4*>(sm.qt + toff<T, kDk>(pos, 32 * w + 8 * i + 4 * g));
+                const Q4 kv = *reinterpret_cast<const Q4*>(sm.kt + toff<T, kDk>(pos, 32 * w + 8 * i + 4 * g));
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            st_rows_lds<T>(sm.qt, dq[rt], rt, g, n, w);
-            st_rows_lds<T>(sm.kt, dk[rt], rt, g, n, w);
+                for (int e = 0; e < 4; ++e) {
+                    pq[4 * i + e] = (float)qv[e] * dq2[4 * i + e];
+                    pk3[4 * i + e] = (float)kv[e] * dk3[4 * i + e];
+                    pk4[4 * i + e] = (float)kv[e] * dk4[4 * i + e];
+                }
+            }
+            col_sums(sm.part[w][1] + 32 * rt, pq, g, n);
+            col_sums(sm.part[w][2] + 32 * rt, pk3, g, n);
+            col_sums(sm.part[w][3] + 32 * rt, pk4, g, n);
+            const size_t row = (((size_t)b * Tn + t0 + pos) * H + h) * kDk + 32 * w;
+            store_row_pieces<T>((T*)prm.dq + row, dqt, g, pos < nv);
+            store_row_pieces<T>((T*)prm.dk + row, dkt, g, pos < nv);
         }
-        lds_barrier();
-        copy_tile_rows<T>((T*)prm.dq + (((size_t)b * Tn + t0) * H + h) * kDk, sm.qt, H, nv, tid);
-        copy_tile_rows<T>((T*)prm.dk + (((size_t)b * Tn + t0) * H + h) * kDk, sm.kt, H, nv, tid);
     }
     // ---- phase 5: <dHn, Hn> for the gradient of gamma_C, this wave's part
     {
