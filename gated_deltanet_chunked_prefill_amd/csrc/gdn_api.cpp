@@ -233,6 +233,29 @@ gdn_status device_cus(int* cus) {
     return GDN_OK;
 }
 
+// Packed sequences: a sequence longer than the per-CU share of all chunks (at
+// least two windows) is cut into segments of about that many chunks, at most 16,
+// each later one warming up over a window (talk summary, paragraphs 4 and 5).
+// The cut is taken on the device from each sequence's length; here only its
+// target length and the segment bound follow from the shapes.
+void varlen_segments(int n_seqs, int T, int H, int cus, gdn::FwdParams& p) {
+    const gdn_options d = resolve(nullptr);
+    const long long nch = num_chunks(T);
+    long long target = (nch * H + cus - 1) / (cus > 0 ? cus : 1);
+    if (target < 2LL * d.window_chunks) target = 2LL * d.window_chunks;
+    long long P = (nch + target - 1) / target;
+    if (P > 16) P = 16;
+    if (P <= 1 || (long long)n_seqs * H * P > (1LL << 30)) {
+        p.vseg = 0;
+        p.P = 1;
+        return;
+    }
+    p.vseg = (int)target;
+    p.P = (int)P;
+    p.w = d.window_chunks;
+    p.log_eps = d.log_eps;
+}
+
 }  // namespace
 
 extern "C" {
@@ -469,6 +492,10 @@ gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.o = o; p.ht = ht;
     p.B = n_seqs; p.T = T; p.H = H; p.N = num_chunks(T); p.P = 1; p.w = 1; p.scale = scale;
     p.cu = cu_seqlens;
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != GDN_OK) return st;
+    varlen_segments(n_seqs, T, H, cus, p);
     const hipError_t e = recorded(GDN_LAUNCH_FWD_SINGLE, s, [&] {
         return gdn::launch_fwd(p, gdn::PHASE_VARLEN, dtype == GDN_BF16, s);
     });

@@ -757,19 +757,73 @@ __device__ __noinline__ void chain_prep(const FwdParams& prm, Smem<T>& sm, const
     }
 }
 
+// Sum of g over tokens [t_lo, t_hi) of row bh of a [B, T, H] gate tensor (token
+// index b*T + t), by the whole workgroup; every thread returns the total.
+template <typename T>
+__device__ float gate_sum(const FwdParams& p, Smem<T>& sm, int bh, int t_lo, int t_hi) {
+    const int b = bh / p.H, h = bh % p.H;
+    float x = 0.f;
+    for (int t = t_lo + (int)threadIdx.x; t < t_hi; t += kThreads)
+        x += p.g[((size_t)b * p.T + t) * p.H + h];
+    x = lane_value(wave_inclusive_scan(x), 63);
+    float* const part = &sm.pscr[0][0][0];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) tot += part[i];
+    __syncthreads();   // the partials are read before the task reuses the scratch
+    return tot;
+}
+
+// First chunk of a later segment's warm-up (window path, talk summary paragraph 5,
+// commentary paragraph 8): starting from the zero state m*w chunks before the
+// segment's first output chunk c_out is within a factor exp(sum of g over those
+// chunks) of the true state, so the shortest of m = 1, 2, 4, 8 whose window sum
+// is at most log eps is taken; with none, the segment runs from the sequence's
+// first chunk (its h0), which is exact.
+template <typename T>
+__device__ int varlen_warmup_start(const FwdParams& p, Smem<T>& sm, int bh, int c_out) {
+    float acc = 0.f;
+    int done = 0;   // chunks summed so far, counted back from c_out
+    for (int m = 1; m <= 8; m *= 2) {
+        const int L = m * p.w;
+        if (c_out - L <= 0) return 0;
+        acc += gate_sum(p, sm, bh, (c_out - L) * kChunk, (c_out - done) * kChunk);
+        done = L;
+        if (acc <= p.log_eps) return c_out - L;
+    }
+    return 0;
+}
+
 template <typename T, int PHASE>
 __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_kernel(FwdParams prm) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     Smem<T>& sm = *reinterpret_cast<Smem<T>*>(smem_raw);
     Task tk;
     if constexpr (PHASE == PHASE_VARLEN || PHASE == PHASE_STATES_VARLEN) {
-        // Packed sequences: sequence s = blockIdx / H holds tokens [t0, t0 + len).
-        // The task runs as sequence s of a batch of sequences of length len, with
-        // every token pointer shifted by t0 - s*len, so that the loops' token
-        // index s*len + t addresses token t0 + t (and, when the states are kept,
-        // the state slot bh*(nch+1) + c addresses the sequence's own slots).
-        const int s = (int)blockIdx.x / prm.H, h = (int)blockIdx.x % prm.H;
+        // Packed sequences: workgroup = (segment p, sequence s, head h), p slowest
+        // and descending (later segments, which carry a warm-up and belong to the
+        // longest sequences, are dispatched first); sequence s holds tokens
+        // [t0, t0 + len).  The task runs as sequence s of
+        // a batch of sequences of length len, with every token pointer shifted by
+        // t0 - s*len, so that the loops' token index s*len + t addresses token
+        // t0 + t (and, when the states are kept, the state slot bh*(nch+1) + c
+        // addresses the sequence's own slots).
+        const int SH = prm.B * prm.H;
+        int pi = (int)blockIdx.x / SH;
+        const int sh = (int)blockIdx.x % SH;
+        if (PHASE == PHASE_VARLEN && prm.vseg > 0) pi = prm.P - 1 - pi;
+        const int s = sh / prm.H, h = sh % prm.H;
         const SeqSpan sp = seq_span(prm.cu, prm.cstart, prm.B, prm.T, s);
+        // a long sequence is cut into segments of about vseg chunks (talk summary,
+        // paragraph 4); every workgroup derives the same cut from the sequence's length
+        int nseg = 1;
+        if (PHASE == PHASE_VARLEN && prm.vseg > 0) {
+            nseg = (sp.nch + prm.vseg - 1) / prm.vseg;
+            nseg = nseg < 1 ? 1 : (nseg > prm.P ? prm.P : nseg);
+        }
+        if (pi >= nseg) return;   // workgroup-uniform, before any barrier
         const long long shift = ((long long)sp.t0 - (long long)s * sp.len) * prm.H;   // token-head rows
         FwdParams p = prm;
         p.q = (const T*)prm.q + shift * kDk;
@@ -782,10 +836,17 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_kernel(FwdParams prm) {
         p.N = sp.nch;
         if constexpr (PHASE == PHASE_STATES_VARLEN) {
             const long long slot = (long long)h * (prm.cmax + prm.B) + sp.c0 + s -
-                                   (long long)blockIdx.x * (sp.nch + 1);
+                                   (long long)sh * (sp.nch + 1);
             p.hstore = prm.hstore + slot * (long long)(kDk * kDv);
         }
-        whole_head_task(p, tk);
+        tk.bh = sh;
+        tk.seg = 0;
+        tk.c_out = (int)((long long)sp.nch * pi / nseg);
+        tk.c_end = (int)((long long)sp.nch * (pi + 1) / nseg);
+        tk.c_begin = pi == 0 ? 0 : varlen_warmup_start(p, sm, sh, tk.c_out);
+        tk.mode = MODE_FULL;
+        tk.init = (tk.c_begin == 0 && prm.h0) ? INIT_H0 : INIT_ZERO;
+        tk.dst = (tk.c_end == sp.nch && prm.ht) ? DST_HT : DST_NONE;
         run_task<T, MODE_FULL, PHASE == PHASE_STATES_VARLEN>(p, sm, tk);
     } else {
         whole_head_task(prm, tk);
@@ -1454,6 +1515,9 @@ hipError_t launch_phase(const FwdParams& p, hipStream_t s) {
     }
     if constexpr (PHASE == PHASE_QUEUE)
         hipLaunchKernelGGL((gdn_fwd_queue_kernel<T>), dim3(p.cus), dim3(kThreads), lds, s, p);
+    else if constexpr (PHASE == PHASE_VARLEN)
+        hipLaunchKernelGGL((gdn_fwd_kernel<T, PHASE>), dim3(p.B * p.H * (p.vseg > 0 ? p.P : 1)),
+                           dim3(kThreads), lds, s, p);
     else
         hipLaunchKernelGGL((gdn_fwd_kernel<T, PHASE>), dim3(p.B * p.H), dim3(kThreads), lds, s, p);
     return hipGetLastError();

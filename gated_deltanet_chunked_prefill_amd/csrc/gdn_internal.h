@@ -81,6 +81,8 @@ struct FwdParams {
                        // chunks of all sequences together)
     const int* cstart; // packed sequences with kept states: chunk prefix [B+1], then the
                        // sequence bounds [B+1] (seq_span)
+    int vseg;          // packed sequences without kept states: target chunks per segment
+                       // (0 = one workgroup per sequence and head); P = segments at most
 };
 
 // Packed sequences: sequence s holds tokens [t0, t0 + len).  Without the chunk

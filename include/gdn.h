@@ -184,8 +184,15 @@ gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, co
  *   ht                final states [n_seqs, H, dk, dv] float32, or NULL (not written)
  *   scale             multiplies every output
  * Chunks never cross a sequence boundary (each sequence's last chunk may be
- * short).  One workgroup per (sequence, head); the intra-GPU sequence split and
- * the window shortcut are not applied here.  No workspace.  Errors as for
+ * short).  A sequence longer than the per-CU share of all chunks
+ * (max(2 * window_chunks, ceil(ceil(T/64) * H / CUs)) chunks, default options) is
+ * cut into up to 16 segments of about that length (talk summary, paragraph 4);
+ * the cut is taken on the device from the sequence's length.  A later segment
+ * starts from the zero state m * window_chunks chunks before its first output
+ * chunk, for the smallest m in 1, 2, 4, 8 whose sum of g over those chunks (this
+ * head, this sequence) is at most log_eps (the window shortcut of paragraph 5,
+ * decided per segment), and otherwise runs from the sequence's start (exact).
+ * One workgroup per (segment, sequence, head).  No workspace.  Errors as for
  * gdn_chunk_fwd; tokens outside every sequence are neither read nor written. */
 gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, const float* h0, void* o, float* ht,

@@ -373,12 +373,12 @@ def test_fp32_split(gdn, opts):
     _check(to_np(o), to_np(ht), oref, href, TOL_F32, label=f"fp32 split {opts}")
 
 
-def _varlen_case(gdn, lens, H, dtype, seed, tol):
+def _varlen_case(gdn, lens, H, dtype, seed, tol, **gen):
     import torch
     T = int(sum(lens))
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     S = len(lens)
-    x = inputs.generate(B=1, T=T, H=H, dtype=dtype, seed=seed)
+    x = inputs.generate(B=1, T=T, H=H, dtype=dtype, seed=seed, **gen)
     h0 = inputs.generate(B=S, T=1, H=H, dtype=dtype, h0_std=0.05, seed=seed + 1).h0
     t = to_gpu(x)
     sq = lambda a: a[0]   # [1, T, ...] -> [T, ...]
@@ -406,6 +406,46 @@ def test_varlen_packed_bf16(gdn):
 def test_varlen_packed_fp32(gdn):
     say("case varlen fp32 lengths 5, 64, 70")
     _varlen_case(gdn, [5, 64, 70], H=2, dtype="f32", seed=43, tol=TOL_F32)
+
+
+def _varlen_segments(lens, H, cus):
+    """Segments per sequence of the packed forward's cut: target chunks per segment
+    = max(2 windows, ceil(total chunks * H / CUs)), at most 16 segments."""
+    nch = -(-int(sum(lens)) // 64)
+    target = max(16, -(-nch * H // cus))
+    pmax = min(16, -(-nch // target))
+    if pmax <= 1:
+        return [1] * len(lens)
+    return [min(pmax, max(1, -(-(-(-n // 64)) // target))) for n in lens]
+
+
+def test_varlen_split_long_prompt(gdn):
+    """A long prompt among short and empty ones is cut into segments, each later
+    segment warming up over its own decay window or running from the sequence
+    start; every sequence is checked against the oracle run on it alone."""
+    import torch
+    lens = [4096, 100, 300, 0, 2500]
+    segs = _varlen_segments(lens, 2, torch.cuda.get_device_properties(0).multi_processor_count)
+    say(f"case varlen split bf16 lengths {lens}, H=2, segments {segs}")
+    assert max(segs) > 1
+    _varlen_case(gdn, lens, H=2, dtype="bf16", seed=61, tol=TOL_BF16)
+
+
+def test_varlen_split_mixed_decay(gdn):
+    """Strongly decaying heads take the window; near-1 heads find no window whose
+    decay reaches eps and run their later segments from the sequence start."""
+    import torch
+    lens = [3000, 64, 5000, 129]
+    segs = _varlen_segments(lens, 4, torch.cuda.get_device_properties(0).multi_processor_count)
+    say(f"case varlen split bf16 lengths {lens}, H=4, mixed gates, segments {segs}")
+    assert max(segs) > 1
+    _varlen_case(gdn, lens, H=4, dtype="bf16", seed=63, tol=TOL_BF16, gate="mixed", strong_frac=0.5)
+
+
+def test_varlen_split_fp32(gdn):
+    say("case varlen split fp32 lengths 2100, 70, 1500")
+    _varlen_case(gdn, [2100, 70, 1500], H=2, dtype="f32", seed=65, tol=TOL_F32, gate="uniform",
+                 gate_lo=-0.3, gate_hi=-0.05)
 
 
 def test_varlen_equals_fixed_length(gdn):
