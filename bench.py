@@ -9,6 +9,9 @@ segment planner and the fused forward launch).
 Prints one JSON line with tokens/s, the roofline of the fused forward kernel
 (algorithmic bytes over its HIP-event-timed launch durations, against the
 8 TB/s HBM peak) and the fp64 CPU oracle timed on the host as a reference.
+A "pattern_ceiling" object gives the bandwidth of the same memory pattern with
+no arithmetic (gdn_stream_probe: K, Q, V tiles streamed per head and segment,
+an output tile written per chunk), the ceiling that layout leaves the kernel.
 A secondary "backward" object times whole gdn_chunk_bwd calls on the training
 shape (B=4, T=8192, H=32, bf16) with per-launch event times, and a "varlen"
 object whole gdn_chunk_fwd_varlen calls on a packed batch of 8 prompts of
@@ -347,6 +350,37 @@ def cpu_baseline(x, tokens):
                       f"{threads} OpenMP threads (one head each at a time), {dt:.2f} s wall"}
 
 
+def pattern_ceiling(torch, gdn, lib, _lib, q, k, v, o, reps=20):
+    """Bandwidth of the forward's memory pattern with no arithmetic
+    (gdn_stream_probe): K, Q, V tiles of every (head, segment) streamed into LDS
+    chunk by chunk and an output tile written per chunk, one workgroup per CU."""
+    B, T, H, _ = q.shape
+    n = T // 64
+    seg = max(1, torch.cuda.get_device_properties(0).multi_processor_count // H)
+    while seg > 1 and n % seg:
+        seg -= 1
+    flat = lambda t: t.reshape(B * T, H, 128)
+    args = (flat(k), flat(q), flat(v), flat(o), seg)
+    for _ in range(3):
+        gdn.gdn_stream_probe(*args)
+    torch.cuda.synchronize()
+    ev = HipEvents(2 * reps)
+    labels = (ctypes.c_int * reps)()
+    lib.gdn_profile_events(ctypes.cast(ev.arr, ctypes.c_void_p), ctypes.cast(labels, ctypes.c_void_p), reps)
+    for _ in range(reps):
+        gdn.gdn_stream_probe(*args)
+    torch.cuda.synchronize()
+    cnt = lib.gdn_profile_events(None, None, 0)
+    ms = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(cnt)]
+    ev.close()
+    cpw = n // seg
+    nbytes = 3 * B * T * H * 256 + B * T * H * 256 * (cpw - 1) // cpw
+    mean = float(np.mean(ms))
+    gbs = nbytes / (mean * 1e-3) / 1e9
+    return {"kernel": "stream_probe", "segments_per_head": seg, "bytes": nbytes, "ms_mean": mean,
+            "ms_min": float(np.min(ms)), "gbs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -429,6 +463,7 @@ def main():
         raise SystemExit("bench.py: the split forward reported a failed wait in a timed call")
     timing = {"plain": rep_stats(torch, step, args.reps),
               "mall_flushed": rep_stats(torch, step, args.reps, flush_bytes=512 * 2 ** 20)}
+    ceiling = pattern_ceiling(torch, gdn, lib, _lib, q, k, v, o)
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tokens_per_s = B * T / (ms_per_step * 1e-3)
@@ -465,6 +500,7 @@ def main():
                      "traffic_gbs": None if tr is None else traffic / (fwd_ms * 1e-3) / 1e9, "kernel_ms": kernel_ms,
                      "call_frac": nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "timing": timing,
+        "pattern_ceiling": dict(ceiling, fwd_kernel_vs_ceiling=achieved / ceiling["gbs"]),
     }
     if args.bwd_steps > 0 or args.varlen_steps > 0 or args.kda_steps > 0:
         del q, k, v, g, beta, o, ht, ws

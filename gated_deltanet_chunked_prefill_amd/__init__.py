@@ -271,6 +271,22 @@ def gdn_kda_fwd(q, k, v, g, beta, h0=None, scale=1.0, *, output_final_state=True
     return o, ht
 
 
+def gdn_stream_probe(k, q, v, o, segments):
+    """Measurement aid: stream k, q, v ([T, H, 128] bf16, T a multiple of
+    64 * segments) into LDS chunk by chunk in the fused forward's layout and write
+    o, with no arithmetic (one workgroup per head and segment).  Returns None."""
+    torch = _torch()
+    lib = _lib.load()
+    for t, nm in ((k, "k"), (q, "q"), (v, "v"), (o, "o")):
+        _dev(t, nm, torch.bfloat16)
+    if k.dim() != 3 or k.shape[-1] != 128:
+        raise ValueError("k, q, v, o must be [T, H, 128]")
+    T, H, _ = k.shape
+    for t, nm in ((q, "q"), (v, "v"), (o, "o")):
+        _shape(t, nm, (T, H, 128), k.device)
+    _lib.check(lib.gdn_stream_probe(_ptr(k), _ptr(q), _ptr(v), _ptr(o), T, H, int(segments), _stream(k.device)))
+
+
 def gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None, scale=1.0, *,
                          output_final_state=True, out=None, out_ht=None):
     """Fused forward over packed variable-length sequences.  q, k, v: [T, H, d]

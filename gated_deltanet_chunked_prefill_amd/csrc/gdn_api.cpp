@@ -468,6 +468,26 @@ gdn_status gdn_kda_fwd(const void* q, const void* k, const void* v, const float*
     return GDN_OK;
 }
 
+gdn_status gdn_stream_probe(const void* k, const void* q, const void* v, void* o, int T, int H, int segments,
+                            void* stream) {
+    g_err[0] = 0;
+    if (!k || !q || !v || !o) return fail(GDN_ERR_INVALID_ARG, "k, q, v and o are required");
+    if (H < 1 || segments < 1 || T < 1) return fail(GDN_ERR_INVALID_ARG, "T, H and segments must be positive");
+    if (T % (64LL * segments) != 0)
+        return fail(GDN_ERR_INVALID_ARG, "T (%d) must be a multiple of 64 * segments (%d)", T, segments);
+    if ((long long)T * H * 128 * 2 >= (1LL << 40) || (long long)H * segments > (1LL << 30))
+        return fail(GDN_ERR_INVALID_ARG, "shape too large");
+    const void* ptrs[] = {k, q, v, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return fail(GDN_ERR_INVALID_ARG, "k, q, v and o must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    const hipError_t e = recorded(GDN_LAUNCH_STREAM_PROBE, s, [&] {
+        return gdn::launch_stream_probe(k, q, v, o, T, H, segments, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "stream probe launch");
+    return GDN_OK;
+}
+
 gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, const float* h0, void* o, float* ht,
                                 const int32_t* cu_seqlens, int n_seqs, int T, int H, int dk, int dv,

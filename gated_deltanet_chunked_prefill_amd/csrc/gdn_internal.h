@@ -184,6 +184,9 @@ struct KdaParams {
     int B, T, H, N;
     float scale;
 };
+// Streaming probe of the forward's memory pattern (gdn_probe.hip).
+hipError_t launch_stream_probe(const void* k, const void* q, const void* v, void* o, int T, int H, int segments,
+                               hipStream_t s);
 hipError_t launch_kda_fwd(const KdaParams& p, hipStream_t s);
 size_t kda_smem_bytes();
 

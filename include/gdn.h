@@ -290,6 +290,20 @@ gdn_status gdn_gate_scan(const float* g, int B, int T, int H, int window_chunks,
                          int32_t* flags, float* max_window_logdecay, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Measurement aid, not part of the operator: the memory pattern of the fused
+ * forward with no arithmetic (the talk summary, paragraph 7, argues the fused
+ * forward is memory-bound; this measures what its layout can stream).  One
+ * workgroup per (head, segment) of T / (64 * segments) chunks copies each
+ * chunk's K, Q, V tiles (rows of 256 bytes, H * 256 bytes apart) into LDS and
+ * writes the previous chunk's V tile to o at that chunk's rows, so every call
+ * reads k, q, v once and writes o except each segment's last chunk.  Its time
+ * bounds the forward's from below for the same bytes.
+ *   k, q, v, o   DEVICE pointers, [T, H, 128] bfloat16, 16-byte aligned
+ *   T            a positive multiple of 64 * segments;  H >= 1;  segments >= 1
+ * GDN_ERR_INVALID_ARG for other shapes or null pointers; no workspace. */
+gdn_status gdn_stream_probe(const void* k, const void* q, const void* v, void* o, int T, int H, int segments,
+                            void* stream);
+
 /* Kinds of kernel launch reported by gdn_profile_events. */
 typedef enum {
     GDN_LAUNCH_GATE_SUMS = 0,   /* gate scan: per-chunk sums of g                     */
@@ -301,7 +315,8 @@ typedef enum {
     GDN_LAUNCH_BWD_DH = 6,      /* backward: state gradient, end to start             */
     GDN_LAUNCH_BWD_LOCAL = 7,   /* backward: local gradients of every chunk           */
     GDN_LAUNCH_FWD_SUMS = 8,    /* split forward: chunk sums of g, planner reset      */
-    GDN_LAUNCH_KDA_FWD = 9      /* KDA forward                                        */
+    GDN_LAUNCH_KDA_FWD = 9,     /* KDA forward                                        */
+    GDN_LAUNCH_STREAM_PROBE = 10 /* measurement aid: the forward's memory pattern     */
 } gdn_launch_kind;
 
 /* Measurement hook (the talk summary, paragraph 7, argues the fused operator

@@ -142,6 +142,24 @@ def test_varlen_validation_before_launch():
     assert call(cu=A + 2) == _lib.GDN_ERR_INVALID_ARG
 
 
+def test_stream_probe_validation_before_launch():
+    """The memory-pattern probe rejects bad shapes before anything is launched."""
+    lib = _lib.load()
+    A = 1 << 20
+    P = lambda a: ctypes.c_void_p(a) if a else None
+
+    def call(k=A, o=A, T=1024, H=2, seg=4):
+        return lib.gdn_stream_probe(P(k), P(A), P(A), P(o), T, H, seg, None)
+    assert call(k=0) == _lib.GDN_ERR_INVALID_ARG
+    assert call(o=0) == _lib.GDN_ERR_INVALID_ARG
+    assert call(T=1000) == _lib.GDN_ERR_INVALID_ARG   # not a multiple of 64 * segments
+    assert "multiple" in _lib.last_error()
+    assert call(T=64 * 3) == _lib.GDN_ERR_INVALID_ARG
+    assert call(seg=0) == _lib.GDN_ERR_INVALID_ARG
+    assert call(H=0) == _lib.GDN_ERR_INVALID_ARG
+    assert call(k=A + 8) == _lib.GDN_ERR_INVALID_ARG
+
+
 def test_bwd_varlen_validation_before_launch():
     lib = _lib.load()
     A = 1 << 20

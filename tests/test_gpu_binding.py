@@ -157,3 +157,23 @@ def test_bwd_varlen_decreasing_cu_seqlens(gdn):
             e = rel_err(got[n][None, a:b], ref[n])
             assert e <= TOL_BF16, (s_, n, e)
         assert rel_err(got["dh0"][s_:s_ + 1], ref["dh0"]) <= TOL_BF16
+
+
+def test_stream_probe_copies_v(gdn):
+    """The memory-pattern probe writes each chunk's V tile to o, except the last
+    chunk of every segment (a copy, bit-exact), and reads k and q in full."""
+    import torch
+    say("case stream probe T=64*12 H=3 segments=4")
+    T, H, seg = 64 * 12, 3, 4
+    gen = torch.Generator().manual_seed(5)
+    k, q, v = (torch.randn((T, H, 128), generator=gen).to(torch.bfloat16).cuda() for _ in range(3))
+    o = torch.zeros_like(v)
+    gdn.gdn_stream_probe(k, q, v, o, seg)
+    torch.cuda.synchronize()
+    cpw = T // 64 // seg
+    written = torch.ones(T, dtype=torch.bool)
+    for p in range(seg):
+        last = (p + 1) * cpw - 1
+        written[last * 64:(last + 1) * 64] = False
+    assert torch.equal(o.cpu()[written], v.cpu()[written])
+    assert torch.count_nonzero(o.cpu()[~written]) == 0
