@@ -44,10 +44,14 @@ namespace gdn {
 namespace {
 
 constexpr int kDhThreads = 512;     // 4 gradient waves + 4 prep waves
-// The reverse sweep runs prep and gradient step back to back (three barriers per
-// chunk).  Its pipelined schedule (prep one chunk ahead, as in the forward) gave
-// run-to-run different state gradients from the second chunk on, and is off.
+// The reverse sweep runs prep and gradient step back to back, two barriers per
+// chunk, with the next chunk's K, Q, dO tiles and gates fetched into a second
+// slot during the prep (kDhLoadAhead; deterministic and bit-identical to the
+// three-barrier sweep without the fetch ahead).  The fully pipelined schedule
+// (prep one chunk ahead of the step, as in the forward) gave run-to-run
+// different state gradients from the second chunk on, and is off.
 constexpr bool kDhPipelined = false;
+constexpr bool kDhLoadAhead = true;
 constexpr int kLocalThreads = 256;  // 4 waves
 // direct state loads per wave in the local-gradient kernel (four 64 x 128 tiles)
 constexpr int kStateLoads = 16;
@@ -143,6 +147,16 @@ __device__ __noinline__ void dh_state_loop(const BwdParams& prm, Smem<T>& sm, in
                              sm.e_vec[vb], sm.gc[vb][0], scale, dH);
             lds_barrier();
         }
+    } else if constexpr (kDhLoadAhead) {
+        for (int i = 0; i < N; ++i) {
+            const int c = N - 1 - i;
+            const int slot = i & 1;
+            lds_barrier();   // A
+            lds_barrier();   // B
+            store_state_bf16t(uni(dst + (size_t)c * SS), L.w, L.lane, dH);
+            dh_chunk_step<T>(L, sm.kt[slot], sm.qt[slot], sm.vt[slot], sm.t32[0], sm.gam_vec[0], sm.e_vec[0],
+                             sm.gc[0][0], scale, dH);
+        }
     } else {
         for (int i = 0; i < N; ++i) {
             const int c = N - 1 - i;
@@ -216,6 +230,30 @@ __device__ __noinline__ void dh_prep_loop(const BwdParams& prm, Smem<T>& sm, int
                 wait_vm();
             }
             lds_barrier();
+        }
+    } else if constexpr (kDhLoadAhead) {
+        // chunk i + 1's tiles and gates are fetched into the other slot while
+        // chunk i is prepped; prep and gradient step stay in sequence
+        if (N > 0) {
+            load_kq(cidx(0), 0);
+            load_do(cidx(0), 0);
+            load_gate_beta(gp, bp, Tn, H, b, h, cidx(0), L.lane, g_nxt, b_nxt);
+            wait_vm();
+        }
+        for (int i = 0; i < N; ++i) {
+            const int slot = i & 1;
+            lds_barrier();   // A: the gradient step of chunk i - 1 is done with the buffers
+            g_cur = g_nxt;
+            b_cur = b_nxt;
+            if (i + 1 < N) {
+                load_kq(cidx(i + 1), slot ^ 1);
+                load_do(cidx(i + 1), slot ^ 1);
+                load_gate_beta(gp, bp, Tn, H, b, h, cidx(i + 1), L.lane, g_nxt, b_nxt);
+            }
+            chunk_prep<T, MODE_FULL>(sm, L, pw, sm.kt[slot], sm.qt[slot], sm.t32[0], sm.gam_vec[0],
+                                     sm.e_vec[0], sm.gc[0], g_cur, b_cur, true, gsum);
+            wait_vm();
+            lds_barrier();   // B: prep of chunk i and the tiles of chunk i + 1 are in LDS
         }
     } else {
         for (int i = 0; i < N; ++i) {
