@@ -190,15 +190,22 @@ __device__ __noinline__ void dh_prep_loop(const BwdParams& prm, Smem<T>& sm, int
     float gsum = 0.f;
     float g_cur = 0.f, b_cur = 0.f, g_nxt = 0.f, b_nxt = 0.f;
     auto cidx = [&](int i) { return N - 1 - i; };
-    TileLoader<T> TL;
-    TL.init(pw, L.lane, H);
+    // with the fetch ahead, prep waves 2 and 3 issue every tile load, so waves 0
+    // and 1 (the diagonal inverses, the longest prep work) never wait on the
+    // memory pipeline; otherwise all four load their quarter
+    constexpr int kLoaders = kDhLoadAhead ? 2 : 4;
+    const bool loader = pw >= 4 - kLoaders;
+    TileLoader<T, kLoaders> TL;
+    if (loader) TL.init(pw - (4 - kLoaders), L.lane, H);
     auto load_kq = [&](int c, int slot) {
+        if (!loader) return;
         const size_t cb = chunk_base(b, h, Tn, H, c);
         const int nv = chunk_len(Tn, c);
         TL.load(sm.kt[slot], k + cb, nv);
         TL.load(sm.qt[slot], q + cb, nv);
     };
     auto load_do = [&](int c, int slot) {
+        if (!loader) return;
         TL.load(sm.vt[slot], dout + chunk_base(b, h, Tn, H, c), chunk_len(Tn, c));
     };
     if constexpr (kPipe) {
