@@ -618,9 +618,11 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
         const size_t e0 = ((size_t)b * Tn + t0) * H + h;
         if (nv == kChunk) {
             __builtin_amdgcn_global_load_lds((const void*)(prm.g + e0 + (size_t)lane * H),
-                                             (__attribute__((address_space(3))) void*)&sm.gst[0][0], 4, 0, 0);
+                                             (__attribute__((address_space(3))) void*)&sm.gst[0][0], 4, 0,
+                                             kCpolStream);
             __builtin_amdgcn_global_load_lds((const void*)(prm.beta + e0 + (size_t)lane * H),
-                                             (__attribute__((address_space(3))) void*)&sm.gst[1][0], 4, 0, 0);
+                                             (__attribute__((address_space(3))) void*)&sm.gst[1][0], 4, 0,
+                                             kCpolStream);
         } else {
             float gv = 0.f, bv = 0.f;
             load_gate_beta(prm.g, prm.beta, Tn, H, b, h, c, lane, gv, bv);

@@ -480,7 +480,7 @@ __device__ __noinline__ void prep_loop(const FwdParams& prm, Smem<T>& sm, const 
         const int nv = chunk_len(Tn, c);
         if (nv == kChunk) {
             __builtin_amdgcn_global_load_lds((const void*)(src + e0 + (size_t)L.lane * H),
-                                             (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+                                             (__attribute__((address_space(3))) void*)dst, 4, 0, kCpolStream);
         } else {
             typedef __attribute__((address_space(1))) const float gfloat;
             dst[L.lane] = L.lane < nv ? ((gfloat*)src)[e0 + (size_t)L.lane * H] : 0.f;
