@@ -676,7 +676,7 @@ __device__ __forceinline__ void local_body(const BwdParams& prm, int bh, int c) 
             // diagonal block p: T_pp = diag(Gamma) T0_pp diag(1/Gamma), T0_pp gate-free
             const int p = ti;
             const f32x16 brow = rows_of(sm.beta, p, g);
-            const f32x16 zt = diag_inverse_t<T>(skk, brow, sm.beta[32 * p + n], n, g);
+            const f32x16 zt = diag_inverse_t<T>(skk, skk, brow, sm.beta[32 * p + n], n, g);
             // zt = acc(T0_pp^T): lane n holds row 32p + n, registers columns 32p + rho
             const float gn = sm.gam[32 * p + n];
 #pragma unroll

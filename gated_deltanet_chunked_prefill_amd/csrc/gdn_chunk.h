@@ -303,30 +303,54 @@ __device__ __forceinline__ f32x16 mm_acc(const f32x16& xt, const f32x16& y, f32x
 }
 
 // Inverse of (I + Nd) for one 32x32 diagonal block, Nd = diag(beta) strict_lower(S),
-// from S = K_p K_p^T (acc form).  Returns acc(T0_pp^T) in zt.
+// from acc(S) and acc(S^T) (the same registers when S is symmetric).  Returns
+// acc(T0^T): lane n holds row n of T0 = (I + Nd)^{-1} at columns rho.
+//
+// Recursive block inversion on MFMA: with Z the inverse of the block-diagonal
+// part of I + Nd at block size b, and No the entries of Nd that join block pairs
+// (rows in block 2m+1, columns in block 2m), the inverse at block size 2b is
+// Z - Z No Z (Z No is strictly block-lower inside each pair, so its square is
+// zero).  Starting from b = 1 (Z = I) this takes four doubling steps to b = 32.
+// Every product forms entries of a true inverse (block forward substitution in
+// matrix form), so no intermediate grows beyond the inverse's own entries and
+// rounding stays at the operands' precision for any keys (a power series in Nd,
+// exact only in exact arithmetic, cancels catastrophically when a chunk's keys
+// are strongly correlated).  With bf16 operands the entries come out within
+// about twice the rounding of storing them as bf16 (which the block solve does
+// with every inverse block); float32 operands give float32 accuracy.
 template <typename T>
-__device__ __forceinline__ f32x16 diag_inverse_t(const f32x16& S, const f32x16& beta_rows,
+__device__ __forceinline__ f32x16 diag_inverse_t(const f32x16& S, const f32x16& St, const f32x16& beta_rows,
                                                  float beta_n, int n, int g) {
-    f32x16 m, mt, z, zt;
+    f32x16 nd, ndt, z, zt;   // acc(Nd), acc(Nd^T), acc(Z), acc(Z^T)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        int row = rho(g, r);
-        m[r] = (n < row) ? -beta_rows[r] * S[r] : 0.f;   // M = -Nd
-        mt[r] = (row < n) ? -beta_n * S[r] : 0.f;        // M^T (S is symmetric)
-        float id = (row == n) ? 1.f : 0.f;
-        z[r] = id + m[r];
-        zt[r] = id + mt[r];
+        const int row = rho(g, r);
+        nd[r] = n < row ? beta_rows[r] * S[r] : 0.f;   // Nd[row][n]
+        ndt[r] = row < n ? beta_n * St[r] : 0.f;       // Nd^T[row][n] = Nd[n][row]
+        const float id = row == n ? 1.f : 0.f;
+        // b = 1 -> 2: Z = I - Nd on the pairs (2m + 1, 2m)
+        z[r] = id - ((row == n + 1 && (row & 1)) ? nd[r] : 0.f);
+        zt[r] = id - ((n == row + 1 && (n & 1)) ? ndt[r] : 0.f);
     }
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        f32x16 m2 = mm_acc<T>(mt, m, zero16());    // M^(2^(it+1))
-        f32x16 m2t = mm_acc<T>(m, mt, zero16());   // its transpose
-        m = m2;
-        mt = m2t;
-        f32x16 zn = (it < 3) ? mm_acc<T>(zt, m, z) : z;   // Z is only needed transposed at the end
-        f32x16 ztn = mm_acc<T>(m, zt, zt);         // Z^T (I + M^(2^(it+1)))^T
-        z = zn;
-        zt = ztn;
+    for (int lev = 1; lev < 5; ++lev) {
+        // acc(No^T): entry (row, n) is No[n][row], present when n's block of size
+        // 2^lev is odd and row's block is the one before it
+        f32x16 not_;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = rho(g, r);
+            const bool in = (n >> lev) == (row >> lev) + 1 && ((n >> lev) & 1);
+            not_[r] = in ? ndt[r] : 0.f;
+        }
+        const f32x16 q = mm_acc<T>(not_, z, zero16());   // Q = No Z
+        const f32x16 p = mm_acc<T>(zt, q, zero16());     // Z Q
+        const f32x16 pt = mm_acc<T>(q, zt, zero16());    // (Z Q)^T = Q^T Z^T
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            z[r] -= p[r];
+            zt[r] -= pt[r];
+        }
     }
     return zt;
 }
@@ -339,24 +363,38 @@ __device__ __forceinline__ float gate_factor(float fr, float fc) {
     else return fr * fc;
 }
 
-// Diagonal block p of the chunk: S = K_p K_p^T, T0_pp by the series, then the
-// gated Tt_pp (and the gate-free T0_pp diag(beta) in pass-1).  p is a template
-// parameter so that every per-lane address-table index is a compile-time constant.
-template <typename T, int MODE, int p, bool PW>
-__device__ __forceinline__ void diag_block(const Lane<T>& L, const T* kt, T (*t32)[kT32],
-                                           const float* s_row, const float* s_col,
-                                           const float* s_beta) {
+// acc(K_p K_p^T) of diagonal block p.  p is a template parameter so that every
+// per-lane address-table index is a compile-time constant.
+template <typename T, int p>
+__device__ __forceinline__ f32x16 diag_gram(const Lane<T>& L, const T* kt) {
     using F = typename FragOf<T>::type;
-    const int n = L.n, g = L.g;
     f32x16 S = zero16();
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
         F kf = L.f128(kt, p, ks);
         S = mma(kf, kf, S);
     }
+    return S;
+}
+
+// T0_pp of diagonal block p = pw (prep waves 0 and 1): one copy of the inverse
+// for both blocks and both gate forms.  Returns acc(T0_pp^T): lane n holds row
+// 32p + n of T0_pp, registers columns 32p + rho.
+template <typename T>
+__device__ __forceinline__ f32x16 diag_t0(const Lane<T>& L, int pw, const T* kt, const float* s_beta) {
+    const f32x16 S = pw == 0 ? diag_gram<T, 0>(L, kt) : diag_gram<T, 1>(L, kt);
+    return diag_inverse_t<T>(S, S, rows_of(s_beta, pw, L.g), s_beta[32 * pw + L.n], L.n, L.g);
+}
+
+// Outputs of diagonal block p from zt = acc(T0_pp^T): the gated Tt_pp (and the
+// gate-free T0_pp diag(beta) in pass-1).
+template <typename T, int MODE, int p, bool PW>
+__device__ __forceinline__ void diag_block(const Lane<T>& L, const f32x16& zt, T (*t32)[kT32],
+                                           const float* s_row, const float* s_col,
+                                           const float* s_beta) {
+    using F = typename FragOf<T>::type;
+    const int n = L.n, g = L.g;
     const f32x16 brow = rows_of(s_beta, p, g);
-    f32x16 zt = diag_inverse_t<T>(S, brow, s_beta[32 * p + n], n, g);
-    // acc(T0^T): lane n holds row 32p+n of T0_pp, registers = columns 32p + rho
     const float fr = s_row[32 * p + n];
     const f32x16 fc = rows_of(s_col, p, g);
 #pragma unroll
@@ -378,16 +416,17 @@ __device__ __forceinline__ void diag_block(const Lane<T>& L, const T* kt, T (*t3
 // the product of the re-centred exponentials (PW = false) or pairwise (PW = true).
 template <typename T, int MODE, bool PW>
 __device__ __forceinline__ void chunk_prep_mats(const Lane<T>& L, int pw, const T* kt, const T* qt,
-                                                T (*t32)[kT32], const float* scr, bool emit) {
+                                                T (*t32)[kT32], const float* scr, bool emit,
+                                                const f32x16& zt) {
     using F = typename FragOf<T>::type;
     const int n = L.n, g = L.g;
     const float* s_row = scr + (PW ? 0 : 1) * kChunk;   // gamma or exp(gamma - gC/2)
     const float* s_col = scr + (PW ? 0 : 2) * kChunk;   // gamma or exp(gC/2 - gamma)
     const float* s_beta = scr + 3 * kChunk;
     if (pw == 0) {
-        diag_block<T, MODE, 0, PW>(L, kt, t32, s_row, s_col, s_beta);
+        diag_block<T, MODE, 0, PW>(L, zt, t32, s_row, s_col, s_beta);
     } else if (pw == 1) {
-        diag_block<T, MODE, 1, PW>(L, kt, t32, s_row, s_col, s_beta);
+        diag_block<T, MODE, 1, PW>(L, zt, t32, s_row, s_col, s_beta);
     } else if (pw == 2) {
         // off-diagonal block: acc(K_0 K_1^T) has lane n = row 32+n, registers = columns rho
         f32x16 x = zero16();
@@ -475,10 +514,12 @@ __device__ __forceinline__ void chunk_prep(Smem<T>& sm, const Lane<T>& L, int pw
         gsum += gC;
     }
     wait_lgkm();
+    f32x16 zt;   // prep waves 0 and 1: the diagonal block's T0, before the gate form splits
+    if (pw < 2) zt = diag_t0<T>(L, pw, kt, scr + 3 * kChunk);
     if (pairwise)
-        chunk_prep_mats<T, MODE, true>(L, pw, kt, qt, t32, scr, emit);
+        chunk_prep_mats<T, MODE, true>(L, pw, kt, qt, t32, scr, emit, zt);
     else
-        chunk_prep_mats<T, MODE, false>(L, pw, kt, qt, t32, scr, emit);
+        chunk_prep_mats<T, MODE, false>(L, pw, kt, qt, t32, scr, emit, zt);
 }
 
 // X = K Hm for the two 32-row position tiles (Hm: the four dk tiles of a state).

@@ -19,8 +19,8 @@
 // 32-row blocks 0 and 1 of the chunk:
 //   prep (paragraph 3 steps 1-2, paragraph 6):
 //     A0 = diag(beta) strict_lower(K K^T); its diagonal blocks are inverted
-//     gate-free, T0_pp = (I + A0_pp)^-1, by the product series
-//     (I+M)(I+M^2)(I+M^4)(I+M^8)(I+M^16), M = -A0_pp (exact: M^32 = 0);
+//     gate-free, T0_pp = (I + A0_pp)^-1, by recursive block doubling on
+//     MFMA (Z <- Z - Z No Z from 1x1 to 32x32 blocks, stable for any keys);
 //     gates enter as the factor Gamma_r/Gamma_s = exp(gamma_r - gamma_C/2) *
 //     exp(gamma_C/2 - gamma_s) (2C+1 exponentials: the diagonal scaling pulled
 //     outside the inverse), giving Tt_pp = T_pp diag(beta) with

@@ -61,32 +61,6 @@ struct KdaSmem {
     float beta[kChunk];
 };
 
-// Inverse of (I + Nd) for one 32 x 32 diagonal block, Nd = diag(beta)
-// strict_lower(S), given acc(S) and acc(S^T) (S is not symmetric here).
-// Returns acc(T0^T): lane n holds row n of T0.  The product series
-// (I + M)(I + M^2)(I + M^4)(I + M^8)(I + M^16), M = -Nd, is exact (M^32 = 0).
-__device__ __forceinline__ f32x16 kda_diag_inverse_t(const f32x16& S, const f32x16& St, const f32x16& beta_rows,
-                                                     float beta_n, int n, int g) {
-    f32x16 m, mt, zt;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = rho(g, r);
-        m[r] = (n < row) ? -beta_rows[r] * S[r] : 0.f;   // M[row][n]
-        mt[r] = (row < n) ? -beta_n * St[r] : 0.f;       // M^T[row][n] = M[n][row]
-        const float id = (row == n) ? 1.f : 0.f;
-        zt[r] = id + mt[r];
-    }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const f32x16 m2 = mm_acc<__bf16>(mt, m, zero16());    // M^(2^(it+1))
-        const f32x16 m2t = mm_acc<__bf16>(m, mt, zero16());   // its transpose
-        m = m2;
-        mt = m2t;
-        zt = mm_acc<__bf16>(m, zt, zt);                       // Z^T (I + M^(2^(it+1)))^T
-    }
-    return zt;
-}
-
 // A 32 x 32 block written as an A-layout tile (lane n = row n): values x[r] at
 // row n, column rho(g, r), times `s` and masked to columns <= n when `lower`.
 __device__ __forceinline__ void put_block(const Lane<__bf16>& L, __bf16* tile, const f32x16& x, float s,
@@ -117,12 +91,13 @@ __device__ __forceinline__ f32x16 rows_product(const Lane<__bf16>& L, const __bf
 __device__ __forceinline__ void kda_prep(const Lane<__bf16>& L, KdaSmem& sm, int pw) {
     const int n = L.n, g = L.g;
     if (pw < 2) {
-        // diagonal block p: S = Kc_p Kd_p^T, T0_pp by the series, Tt_pp = T0_pp diag(beta)
+        // diagonal block p: S = Kc_p Kd_p^T, T0_pp by recursive block inversion,
+        // Tt_pp = T0_pp diag(beta)
         const int p = pw;
         const f32x16 S = rows_product(L, sm.kc, p, sm.kd, p);    // acc(Kc Kd^T): [rho][n] = kc_rho . kd_n
         const f32x16 St = rows_product(L, sm.kd, p, sm.kc, p);   // acc(S^T)
         const f32x16 brow = rows_of(sm.beta, p, g);
-        const f32x16 zt = kda_diag_inverse_t(S, St, brow, sm.beta[32 * p + n], n, g);
+        const f32x16 zt = diag_inverse_t<__bf16>(S, St, brow, sm.beta[32 * p + n], n, g);
         f32x16 tt;
 #pragma unroll
         for (int r = 0; r < 16; ++r) tt[r] = zt[r] * brow[r];

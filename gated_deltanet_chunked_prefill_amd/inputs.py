@@ -19,7 +19,13 @@ Distributions follow the workloads the operator is specified on:
                          strongly decaying U[-0.5,-0.05] per token, the rest
                          near 1, U[-1e-3,-1e-5] per token.
   * h0 ~ N(0, std^2) float32 when requested, dout ~ N(0,1) in the I/O dtype.
-The draw order is fixed: q, k, v, beta, gate parts, h0, dout.
+  * key_corr = rho > 0 (optional): the keys of each head share a direction; a
+    key becomes the normalised sqrt(1 - rho) sqrt(dk) k + sqrt(rho) c_h, with
+    c_h ~ N(0, I) drawn once per head, so that two keys of a head have cosine
+    about rho (projected keys of trained models are far from orthogonal; the
+    default rho = 0 keeps independent keys).
+The draw order is fixed: q, k, v, beta, gate parts, h0, dout, then the shared
+key directions (only when key_corr > 0, so other draws do not move).
 """
 from __future__ import annotations
 
@@ -97,8 +103,21 @@ def _plain_normal(rng, shape, dtype_tag):
     return round_to_bf16(x) if dtype_tag == "bf16" else x
 
 
+def _correlate_keys(rng, k, rho, dtype_tag):
+    B, T, H, dk = k.shape
+    c = rng.standard_normal((H, dk))
+    a, b = np.sqrt((1.0 - rho) * dk), np.sqrt(rho)
+    out = np.empty_like(k)
+    for t0 in range(0, T, 4096):
+        x = a * k[:, t0:t0 + 4096].astype(np.float64) + b * c
+        x /= np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+        out[:, t0:t0 + 4096] = x.astype(np.float32)
+    return round_to_bf16(out) if dtype_tag == "bf16" else out
+
+
 def generate(B, T, H, dk=128, dv=128, dtype="bf16", gate="softplus_head", gate_lo=-0.2,
-             gate_hi=-0.005, h0_std=None, dout=False, seed=0, strong_frac=0.7) -> GDNInputs:
+             gate_hi=-0.005, h0_std=None, dout=False, seed=0, strong_frac=0.7,
+             key_corr=0.0) -> GDNInputs:
     """Draw one seeded input set.  See the module docstring for the distributions."""
     if dtype not in ("bf16", "f32"):
         raise ValueError("dtype must be 'bf16' or 'f32'")
@@ -131,6 +150,9 @@ def generate(B, T, H, dk=128, dv=128, dtype="bf16", gate="softplus_head", gate_l
     if h0_std is not None:
         h0 = (rng.standard_normal((B, H, dk, dv), dtype=np.float32) * np.float32(h0_std))
     do = _plain_normal(rng, (B, T, H, dv), dtype) if dout else None
+    if key_corr > 0.0:
+        k = _correlate_keys(rng, k, key_corr, dtype)
+        meta["key_corr"] = key_corr
     return GDNInputs(q=q, k=k, v=v, g=g, beta=beta, h0=h0, dout=do, dtype=dtype, meta=meta)
 
 
@@ -144,12 +166,13 @@ KDA_WORKLOADS = {
 
 
 def generate_kda(B, T, H, dk=128, dv=128, gate="softplus_channel", gate_lo=-0.3, gate_hi=-0.01,
-                 h0_std=None, seed=0) -> GDNInputs:
+                 h0_std=None, seed=0, key_corr=0.0) -> GDNInputs:
     """Seeded bf16 inputs of the per-key-channel-decay variant: q, k, v, beta as
-    :func:`generate`; g [B,T,H,dk] float32, either -softplus(x) * A_{h,i} with x ~
-    N(0,1) per element and a decay rate A_{h,i} = exp(U[-4,-1]) drawn once per
-    (head, key channel) ("softplus_channel"), or U[gate_lo, gate_hi] per element
-    ("uniform").  Draw order: q, k, v, beta, gate parts, h0."""
+    :func:`generate` (key_corr included); g [B,T,H,dk] float32, either
+    -softplus(x) * A_{h,i} with x ~ N(0,1) per element and a decay rate A_{h,i} =
+    exp(U[-4,-1]) drawn once per (head, key channel) ("softplus_channel"), or
+    U[gate_lo, gate_hi] per element ("uniform").  Draw order: q, k, v, beta, gate
+    parts, h0, then the shared key directions when key_corr > 0."""
     rng = np.random.Generator(np.random.PCG64(seed))
     q = _normal_rows(rng, (B, T, H, dk), "bf16")
     k = _normal_rows(rng, (B, T, H, dk), "bf16")
@@ -168,6 +191,9 @@ def generate_kda(B, T, H, dk=128, dv=128, gate="softplus_channel", gate_lo=-0.3,
     h0 = None
     if h0_std is not None:
         h0 = (rng.standard_normal((B, H, dk, dv), dtype=np.float32) * np.float32(h0_std))
+    if key_corr > 0.0:
+        k = _correlate_keys(rng, k, key_corr, "bf16")
+        meta["key_corr"] = key_corr
     return GDNInputs(q=q, k=k, v=v, g=g, beta=beta, h0=h0, dout=None, dtype="bf16", meta=meta)
 
 

@@ -82,6 +82,17 @@ def test_bwd_strong_decay(gdn):
     _check(got, ref, "strong decay")
 
 
+@pytest.mark.parametrize("rho", [0.5, 0.9])
+def test_bwd_correlated_keys(gdn, rho):
+    """Keys sharing a direction (pairwise cosine about rho) through every
+    gradient: the inverse blocks of the state store, the sweep and the local
+    gradients stay accurate."""
+    say(f"case bwd correlated keys rho={rho}")
+    x = inputs.generate(B=1, T=64 * 5 + 9, H=2, h0_std=0.02, dout=True, seed=320, key_corr=rho)
+    got, ref = _bwd(gdn, x)
+    _check(got, ref, f"rho={rho}")
+
+
 @pytest.mark.parametrize("case", ["no_decay", "beta0", "beta1"])
 def test_bwd_degenerate_gates(gdn, case):
     """alpha = 1 (g = 0), beta = 0 (then dk = dv = 0 exactly: keys and values never

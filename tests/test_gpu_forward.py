@@ -115,6 +115,35 @@ def test_split_mixed_heads_window(gdn):
            label="mixed P=10 w=2")
 
 
+@pytest.mark.parametrize("rho", [0.5, 0.9, 0.99])
+def test_correlated_keys(gdn, rho):
+    """Keys of a head sharing a direction (pairwise cosine about rho): the
+    diagonal-block inverse keeps its accuracy (a power series in the strictly
+    lower part loses every digit at rho = 0.9; see test_inverse_numerics)."""
+    say(f"case correlated keys rho={rho}")
+    x = inputs.generate(B=1, T=64 * 8 + 21, H=3, h0_std=0.02, seed=40, key_corr=rho)
+    _check(*_run(gdn, x), TOL_BF16, label=f"rho={rho}")
+
+
+@pytest.mark.parametrize("window", [0, 1])
+def test_correlated_keys_split(gdn, window):
+    """Correlated keys through the split forward: exact heads' gate-free
+    transitions (pass 1), the chain and pass 3, and window heads."""
+    say(f"case correlated keys rho=0.9, forced split window={window}")
+    x = inputs.generate(B=1, T=64 * 16 + 5, H=4, gate="mixed", strong_frac=0.5, h0_std=0.02, seed=41,
+                        key_corr=0.9)
+    _check(*_run(gdn, x, split_mode=2, n_segments=4, use_window=window), TOL_BF16,
+           label=f"rho=0.9 P=4 w={window}")
+
+
+@pytest.mark.parametrize("opts", [dict(), dict(split_mode=2, n_segments=3)])
+def test_correlated_keys_fp32(gdn, opts):
+    say(f"case correlated keys rho=0.9 fp32 {opts}")
+    x = inputs.generate(B=1, T=64 * 6 + 10, H=2, dtype="f32", gate="uniform", gate_lo=-0.2, gate_hi=-0.005,
+                        h0_std=0.05, seed=42, key_corr=0.9)
+    _check(*_run(gdn, x, **opts), TOL_F32, label=f"fp32 rho=0.9 {opts}")
+
+
 @pytest.mark.parametrize("case", ["no_decay", "beta0", "beta1"])
 @pytest.mark.parametrize("split", [1, 0, 2])
 def test_degenerate_gates(gdn, case, split):

@@ -50,6 +50,13 @@ def test_kda_no_initial_state_uniform_gates(gdn):
     _check(*_run(gdn, x), "uniform gates")
 
 
+def test_kda_correlated_keys(gdn):
+    """Keys sharing a direction (pairwise cosine about 0.9)."""
+    say("case KDA correlated keys rho=0.9")
+    x = inputs.generate_kda(B=1, T=64 * 4 + 7, H=2, h0_std=0.05, seed=213, key_corr=0.9)
+    _check(*_run(gdn, x), "rho=0.9")
+
+
 def test_kda_strong_channel_decay(gdn):
     """Channels that decay by up to e^-3 per token (e^-96 over a 32-token half):
     the re-centred tiles keep every factor finite and the result matches."""

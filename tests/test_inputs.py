@@ -34,3 +34,24 @@ def test_mixed_gate_heads():
     assert strong.sum() == 11
     assert np.all(x.g[..., strong] <= -0.05) and np.all(x.g[..., strong] >= -0.5)
     assert np.all(x.g[..., ~strong] >= -1e-3) and np.all(x.g[..., ~strong] <= -1e-5)
+
+
+def test_correlated_keys():
+    # key_corr = rho: unit keys whose pairwise cosine within a head is about rho;
+    # the other tensors are the draws of the uncorrelated call (drawn first)
+    base = inputs.generate(B=1, T=256, H=3, dtype="bf16", h0_std=0.02, dout=True, seed=11)
+    for rho in (0.5, 0.9):
+        x = inputs.generate(B=1, T=256, H=3, dtype="bf16", h0_std=0.02, dout=True, seed=11,
+                            key_corr=rho)
+        for n in ("q", "v", "g", "beta", "h0", "dout"):
+            np.testing.assert_array_equal(getattr(x, n), getattr(base, n))
+        np.testing.assert_array_equal(inputs.round_to_bf16(x.k.copy()), x.k)
+        for h in range(3):
+            k = x.k[0, :, h].astype(np.float64)
+            c = k @ k.T
+            assert np.all(np.abs(np.diag(c) - 1) < 1e-2)
+            off = c[~np.eye(256, dtype=bool)]
+            assert abs(off.mean() - rho) < 0.05, (rho, off.mean())
+    y = inputs.generate_kda(B=1, T=128, H=2, seed=5, key_corr=0.9)
+    k = y.k[0, :, 1].astype(np.float64)
+    assert abs((k @ k.T)[~np.eye(128, dtype=bool)].mean() - 0.9) < 0.05
