@@ -302,6 +302,34 @@ __device__ __forceinline__ f32x16 mm_acc(const f32x16& xt, const f32x16& y, f32x
     return c;
 }
 
+// Whether entry (row, n), row = rho(g, r), of acc(No^T) at doubling step LEV is
+// an entry of Nd joining two blocks of 2^LEV: No[n][row] with n in an odd block
+// and row in the block before it.  Spelled out per step so that the register
+// part is a compile-time constant and one lane test serves several registers.
+template <int LEV>
+__device__ __forceinline__ bool joins(int r, int n, int g) {
+    if constexpr (LEV == 4) return r < 8 && n >= 16;
+    if constexpr (LEV == 3) return ((r >> 2) & 1) == 0 && (n >> 3) == (r >> 2) + 1;
+    if constexpr (LEV == 2) return g == 0 && (n >> 2) == 2 * (r >> 2) + 1;
+    return ((r & 3) >> 1) == 0 && (n >> 1) == 4 * (r >> 2) + 2 * g + 1;
+}
+
+// One doubling step: block size 2^LEV -> 2^(LEV+1).
+template <typename T, int LEV>
+__device__ __forceinline__ void doubling_step(f32x16& z, f32x16& zt, const f32x16& nnt, int n, int g) {
+    f32x16 not_;   // acc(-No^T)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) not_[r] = joins<LEV>(r, n, g) ? nnt[r] : 0.f;
+    const f32x16 q = mm_acc<T>(not_, z, zero16());   // Q = -No Z
+    if constexpr (LEV < 4) {
+        const f32x16 zn = mm_acc<T>(zt, q, z);         // Z + Z Q = Z - Z No Z
+        zt = mm_acc<T>(q, zt, zt);                     // its transpose, Z^T + Q^T Z^T
+        z = zn;
+    } else {
+        zt = mm_acc<T>(q, zt, zt);                     // the last step needs Z^T only
+    }
+}
+
 // Inverse of (I + Nd) for one 32x32 diagonal block, Nd = diag(beta) strict_lower(S),
 // from acc(S) and acc(S^T) (the same registers when S is symmetric).  Returns
 // acc(T0^T): lane n holds row n of T0 = (I + Nd)^{-1} at columns rho.
@@ -321,37 +349,23 @@ __device__ __forceinline__ f32x16 mm_acc(const f32x16& xt, const f32x16& y, f32x
 template <typename T>
 __device__ __forceinline__ f32x16 diag_inverse_t(const f32x16& S, const f32x16& St, const f32x16& beta_rows,
                                                  float beta_n, int n, int g) {
-    f32x16 nd, ndt, z, zt;   // acc(Nd), acc(Nd^T), acc(Z), acc(Z^T)
+    // row = (8 (r >> 2) + (r & 3)) | 4 g, so comparing u = n ^ 4g with a constant
+    // per register tests row == n (and row == n +- 1 for the pairs below)
+    const int u = n ^ (g << 2);
+    f32x16 z, zt, nnt;   // acc(Z), acc(Z^T), acc(-Nd^T)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int row = rho(g, r);
-        nd[r] = n < row ? beta_rows[r] * S[r] : 0.f;   // Nd[row][n]
-        ndt[r] = row < n ? beta_n * St[r] : 0.f;       // Nd^T[row][n] = Nd[n][row]
-        const float id = row == n ? 1.f : 0.f;
+        const int c = 8 * (r >> 2) + (r & 3), row = rho(g, r);
+        const float nn = n < row ? -beta_rows[r] * S[r] : 0.f;   // -Nd[row][n]
+        nnt[r] = row < n ? -beta_n * St[r] : 0.f;                // -Nd[n][row]
         // b = 1 -> 2: Z = I - Nd on the pairs (2m + 1, 2m)
-        z[r] = id - ((row == n + 1 && (row & 1)) ? nd[r] : 0.f);
-        zt[r] = id - ((n == row + 1 && (n & 1)) ? ndt[r] : 0.f);
+        z[r] = u == c ? 1.f : ((r & 1) && u == c - 1) ? nn : 0.f;
+        zt[r] = u == c ? 1.f : (!(r & 1) && u == c + 1) ? nnt[r] : 0.f;
     }
-#pragma unroll
-    for (int lev = 1; lev < 5; ++lev) {
-        // acc(No^T): entry (row, n) is No[n][row], present when n's block of size
-        // 2^lev is odd and row's block is the one before it
-        f32x16 not_;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = rho(g, r);
-            const bool in = (n >> lev) == (row >> lev) + 1 && ((n >> lev) & 1);
-            not_[r] = in ? ndt[r] : 0.f;
-        }
-        const f32x16 q = mm_acc<T>(not_, z, zero16());   // Q = No Z
-        const f32x16 p = mm_acc<T>(zt, q, zero16());     // Z Q
-        const f32x16 pt = mm_acc<T>(q, zt, zero16());    // (Z Q)^T = Q^T Z^T
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            z[r] -= p[r];
-            zt[r] -= pt[r];
-        }
-    }
+    doubling_step<T, 1>(z, zt, nnt, n, g);
+    doubling_step<T, 2>(z, zt, nnt, n, g);
+    doubling_step<T, 3>(z, zt, nnt, n, g);
+    doubling_step<T, 4>(z, zt, nnt, n, g);
     return zt;
 }
 
