@@ -302,6 +302,24 @@ __device__ __forceinline__ f32x16 mm_acc(const f32x16& xt, const f32x16& y, f32x
     return c;
 }
 
+// c + X Y to about float32 accuracy from bf16 MFMAs: X and Y split into bf16
+// high and low parts, the three products that matter accumulated separately
+// (the low x low term is below float32 rounding); float32 operands need no split.
+template <typename T>
+__device__ __forceinline__ f32x16 mm_acc_split(const f32x16& xt, const f32x16& y, f32x16 c) {
+    if constexpr (sizeof(T) == 2) {
+        f32x16 xl, yl;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            xl[r] = xt[r] - (float)(T)xt[r];
+            yl[r] = y[r] - (float)(T)y[r];
+        }
+        c = mm_acc<T>(xt, yl, c);
+        c = mm_acc<T>(xl, y, c);
+    }
+    return mm_acc<T>(xt, y, c);
+}
+
 // Whether entry (row, n), row = rho(g, r), of acc(No^T) at doubling step LEV is
 // an entry of Nd joining two blocks of 2^LEV: No[n][row] with n in an odd block
 // and row in the block before it.  Spelled out per step so that the register
@@ -315,13 +333,14 @@ __device__ __forceinline__ bool joins(int r, int n, int g) {
 }
 
 // One doubling step: block size 2^LEV -> 2^(LEV+1).
+// LEV = 5 is step 4 forming Z as well as Z^T.
 template <typename T, int LEV>
 __device__ __forceinline__ void doubling_step(f32x16& z, f32x16& zt, const f32x16& nnt, int n, int g) {
     f32x16 not_;   // acc(-No^T)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) not_[r] = joins<LEV>(r, n, g) ? nnt[r] : 0.f;
+    for (int r = 0; r < 16; ++r) not_[r] = joins<(LEV < 5 ? LEV : 4)>(r, n, g) ? nnt[r] : 0.f;
     const f32x16 q = mm_acc<T>(not_, z, zero16());   // Q = -No Z
-    if constexpr (LEV < 4) {
+    if constexpr (LEV != 4) {
         const f32x16 zn = mm_acc<T>(zt, q, z);         // Z + Z Q = Z - Z No Z
         zt = mm_acc<T>(q, zt, zt);                     // its transpose, Z^T + Q^T Z^T
         z = zn;
@@ -346,7 +365,7 @@ __device__ __forceinline__ void doubling_step(f32x16& z, f32x16& zt, const f32x1
 // are strongly correlated).  With bf16 operands the entries come out within
 // about twice the rounding of storing them as bf16 (which the block solve does
 // with every inverse block); float32 operands give float32 accuracy.
-template <typename T>
+template <typename T, bool REFINE = true>
 __device__ __forceinline__ f32x16 diag_inverse_t(const f32x16& S, const f32x16& St, const f32x16& beta_rows,
                                                  float beta_n, int n, int g) {
     // row = (8 (r >> 2) + (r & 3)) | 4 g, so comparing u = n ^ 4g with a constant
@@ -365,6 +384,30 @@ __device__ __forceinline__ f32x16 diag_inverse_t(const f32x16& S, const f32x16& 
     doubling_step<T, 1>(z, zt, nnt, n, g);
     doubling_step<T, 2>(z, zt, nnt, n, g);
     doubling_step<T, 3>(z, zt, nnt, n, g);
+    if constexpr (sizeof(T) == 2) {
+        // With bf16 operands the doubling's error grows with the largest entry of
+        // Nd (about 0.3 % of the inverse's largest entry at 0.5, 1.3 % near 2).
+        // With unit keys and beta <= 1 no entry exceeds 1; a block with a larger
+        // one (beta up to 2, or longer keys) gets one Newton step, Z <- Z + Z R
+        // with R = I - (I + Nd) Z formed in split precision, which brings Z to
+        // about float32 accuracy.  The test is wave-uniform.  REFINE = false
+        // leaves it out where registers are short (the gate-free transition of
+        // pass 1, whose blocks are stored in bf16 in any case).
+        float big = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) big = fmaxf(big, fabsf(nnt[r]));
+        if (REFINE && __builtin_amdgcn_ballot_w64(big > 1.f) != 0) {
+            doubling_step<T, 5>(z, zt, nnt, n, g);   // step 4 forming Z as well
+            const f32x16 ndz = mm_acc_split<T>(nnt, z, zero16());   // -Nd Z
+            f32x16 res;                                            // acc(R)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int c = 8 * (r >> 2) + (r & 3);
+                res[r] = (u == c ? 1.f : 0.f) - z[r] + ndz[r];
+            }
+            return mm_acc<T>(res, zt, zt);   // Z^T + R^T Z^T
+        }
+    }
     doubling_step<T, 4>(z, zt, nnt, n, g);
     return zt;
 }
@@ -394,10 +437,11 @@ __device__ __forceinline__ f32x16 diag_gram(const Lane<T>& L, const T* kt) {
 // T0_pp of diagonal block p = pw (prep waves 0 and 1): one copy of the inverse
 // for both blocks and both gate forms.  Returns acc(T0_pp^T): lane n holds row
 // 32p + n of T0_pp, registers columns 32p + rho.
-template <typename T>
+template <typename T, int MODE>
 __device__ __forceinline__ f32x16 diag_t0(const Lane<T>& L, int pw, const T* kt, const float* s_beta) {
     const f32x16 S = pw == 0 ? diag_gram<T, 0>(L, kt) : diag_gram<T, 1>(L, kt);
-    return diag_inverse_t<T>(S, S, rows_of(s_beta, pw, L.g), s_beta[32 * pw + L.n], L.n, L.g);
+    return diag_inverse_t<T, MODE != MODE_PASS1>(S, S, rows_of(s_beta, pw, L.g), s_beta[32 * pw + L.n], L.n,
+                                                 L.g);
 }
 
 // Outputs of diagonal block p from zt = acc(T0_pp^T): the gated Tt_pp (and the
@@ -529,7 +573,7 @@ __device__ __forceinline__ void chunk_prep(Smem<T>& sm, const Lane<T>& L, int pw
     }
     wait_lgkm();
     f32x16 zt;   // prep waves 0 and 1: the diagonal block's T0, before the gate form splits
-    if (pw < 2) zt = diag_t0<T>(L, pw, kt, scr + 3 * kChunk);
+    if (pw < 2) zt = diag_t0<T, MODE>(L, pw, kt, scr + 3 * kChunk);
     if (pairwise)
         chunk_prep_mats<T, MODE, true>(L, pw, kt, qt, t32, scr, emit, zt);
     else

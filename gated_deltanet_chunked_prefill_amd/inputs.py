@@ -10,7 +10,8 @@ Distributions follow the workloads the operator is specified on:
     summary, paragraph 5, relies on L2-normalised keys; normalisation is done
     here, never inside the op), then rounded to the I/O dtype.
   * v ~ N(0,1), rounded to the I/O dtype.
-  * beta = sigmoid(N(0,1)), float32.
+  * beta = beta_max * sigmoid(N(0,1)), float32 (beta_max = 1 by default; up to 2,
+    the range in which each per-token map I - beta k k^T is still a contraction).
   * g = log(alpha), float32, one of
       - "uniform":       U[lo, hi] per token,
       - "softplus_head": -softplus(x) * A_h with x ~ N(0,1) per (b,t,h) and a
@@ -117,7 +118,7 @@ def _correlate_keys(rng, k, rho, dtype_tag):
 
 def generate(B, T, H, dk=128, dv=128, dtype="bf16", gate="softplus_head", gate_lo=-0.2,
              gate_hi=-0.005, h0_std=None, dout=False, seed=0, strong_frac=0.7,
-             key_corr=0.0) -> GDNInputs:
+             key_corr=0.0, beta_max=1.0) -> GDNInputs:
     """Draw one seeded input set.  See the module docstring for the distributions."""
     if dtype not in ("bf16", "f32"):
         raise ValueError("dtype must be 'bf16' or 'f32'")
@@ -125,7 +126,7 @@ def generate(B, T, H, dk=128, dv=128, dtype="bf16", gate="softplus_head", gate_l
     q = _normal_rows(rng, (B, T, H, dk), dtype)
     k = _normal_rows(rng, (B, T, H, dk), dtype)
     v = _plain_normal(rng, (B, T, H, dv), dtype)
-    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32)
+    beta = (beta_max / (1.0 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32)
     meta = {"gate": gate}
     if gate == "uniform":
         g = rng.uniform(gate_lo, gate_hi, (B, T, H)).astype(np.float32)
@@ -166,9 +167,9 @@ KDA_WORKLOADS = {
 
 
 def generate_kda(B, T, H, dk=128, dv=128, gate="softplus_channel", gate_lo=-0.3, gate_hi=-0.01,
-                 h0_std=None, seed=0, key_corr=0.0) -> GDNInputs:
+                 h0_std=None, seed=0, key_corr=0.0, beta_max=1.0) -> GDNInputs:
     """Seeded bf16 inputs of the per-key-channel-decay variant: q, k, v, beta as
-    :func:`generate` (key_corr included); g [B,T,H,dk] float32, either
+    :func:`generate` (key_corr and beta_max included); g [B,T,H,dk] float32, either
     -softplus(x) * A_{h,i} with x ~ N(0,1) per element and a decay rate A_{h,i} =
     exp(U[-4,-1]) drawn once per (head, key channel) ("softplus_channel"), or
     U[gate_lo, gate_hi] per element ("uniform").  Draw order: q, k, v, beta, gate
@@ -177,7 +178,7 @@ def generate_kda(B, T, H, dk=128, dv=128, gate="softplus_channel", gate_lo=-0.3,
     q = _normal_rows(rng, (B, T, H, dk), "bf16")
     k = _normal_rows(rng, (B, T, H, dk), "bf16")
     v = _plain_normal(rng, (B, T, H, dv), "bf16")
-    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32)
+    beta = (beta_max / (1.0 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32)
     meta = {"gate": gate}
     if gate == "softplus_channel":
         rate = np.exp(rng.uniform(-4.0, -1.0, (H, dk)))

@@ -93,6 +93,14 @@ def test_bwd_correlated_keys(gdn, rho):
     _check(got, ref, f"rho={rho}")
 
 
+def test_bwd_beta_up_to_two(gdn):
+    """beta up to 2 with keys of cosine 0.99 (the inverse blocks' Newton step)."""
+    say("case bwd beta up to 2, key cosine 0.99")
+    x = inputs.generate(B=1, T=64 * 5 + 9, H=2, h0_std=0.02, dout=True, seed=321, key_corr=0.99, beta_max=2.0)
+    got, ref = _bwd(gdn, x)
+    _check(got, ref, "beta<=2 rho=0.99")
+
+
 @pytest.mark.parametrize("case", ["no_decay", "beta0", "beta1"])
 def test_bwd_degenerate_gates(gdn, case):
     """alpha = 1 (g = 0), beta = 0 (then dk = dv = 0 exactly: keys and values never

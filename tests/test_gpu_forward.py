@@ -136,6 +136,16 @@ def test_correlated_keys_split(gdn, window):
            label=f"rho=0.9 P=4 w={window}")
 
 
+@pytest.mark.parametrize("opts", [dict(), dict(split_mode=2, n_segments=3, use_window=0)])
+def test_beta_up_to_two(gdn, opts):
+    """beta up to 2 (each map I - beta k k^T still a contraction) with keys of
+    cosine 0.99: entries of Nd above 1, so the diagonal blocks take the Newton
+    step after the doubling (pass 1 of the split keeps the plain doubling)."""
+    say(f"case beta up to 2, key cosine 0.99 {opts}")
+    x = inputs.generate(B=1, T=64 * 8 + 3, H=3, h0_std=0.02, seed=43, key_corr=0.99, beta_max=2.0)
+    _check(*_run(gdn, x, **opts), TOL_BF16, label=f"beta<=2 rho=0.99 {opts}")
+
+
 @pytest.mark.parametrize("opts", [dict(), dict(split_mode=2, n_segments=3)])
 def test_correlated_keys_fp32(gdn, opts):
     say(f"case correlated keys rho=0.9 fp32 {opts}")

@@ -57,6 +57,13 @@ def test_kda_correlated_keys(gdn):
     _check(*_run(gdn, x), "rho=0.9")
 
 
+def test_kda_beta_up_to_two(gdn):
+    """beta up to 2 with keys of cosine 0.9."""
+    say("case KDA beta up to 2, key cosine 0.9")
+    x = inputs.generate_kda(B=1, T=64 * 4 + 7, H=2, h0_std=0.05, seed=214, key_corr=0.9, beta_max=2.0)
+    _check(*_run(gdn, x), "beta<=2 rho=0.9")
+
+
 def test_kda_strong_channel_decay(gdn):
     """Channels that decay by up to e^-3 per token (e^-96 over a 32-token half):
     the re-centred tiles keep every factor finite and the result matches."""

@@ -10,7 +10,9 @@ definition (np.linalg.inv in float64).  Two ways to build it from 32x32 products
   * recursive block doubling Z <- Z - Z No Z (No: the entries joining block
     pairs), whose every product forms entries of the inverse itself.
 The kernel uses the second; these tests show why, with the keys of the seeded
-generator's key_corr option.  No kernel code is involved: this pins the method,
+generator's key_corr option.  The doubling's error grows with the largest entry
+of Nd; a block with an entry above 1 (beta up to 2) gets one Newton step with a
+split-precision residual, which the last test pins.  No kernel code is involved: this pins the method,
 the GPU parity tests pin the kernels.
 """
 import numpy as np
@@ -51,8 +53,8 @@ def _doubling(nd):
     return z
 
 
-def _blocks(rho, n=12, seed=0):
-    x = inputs.generate(B=1, T=32 * n, H=1, key_corr=rho, seed=seed)
+def _blocks(rho, n=12, seed=0, beta_max=1.0):
+    x = inputs.generate(B=1, T=32 * n, H=1, key_corr=rho, seed=seed, beta_max=beta_max)
     for c in range(n):
         k = x.k[0, 32 * c:32 * c + 32, 0].astype(np.float64)
         beta = x.beta[0, 32 * c:32 * c + 32, 0].astype(np.float64)
@@ -86,3 +88,28 @@ def test_series_fails_for_correlated_keys():
     assert max(_rel(_series(nd), ref) for nd, ref in _blocks(0.0)) < 1e-2
     # keys with pairwise cosine 0.9: the series loses every digit
     assert max(_rel(_series(nd), ref) for nd, ref in _blocks(0.9)) > 1.0
+
+
+def _split(x):
+    hi = _bf(x)
+    return hi, _bf(_f32(x - hi))
+
+
+def _refined(nd):
+    # the doubling through its last step, then Z <- Z + Z R with R = I - Z - Nd Z,
+    # Nd Z from split bf16 operands (hi*hi + hi*lo + lo*hi, float32 accumulation)
+    z = _doubling(nd)
+    nh, nl = _split(nd)
+    zh, zl = _split(z)
+    ndz = _f32(_f32(_f32(nh @ zl) + nl @ zh) + nh @ zh)
+    r = _f32(np.eye(32) - z - ndz)
+    return _f32(z + _mm(z, r))
+
+
+def test_refinement_for_beta_up_to_two():
+    for rho in (0.9, 0.99):
+        blocks = list(_blocks(rho, beta_max=2.0, seed=3))
+        assert max(np.abs(nd).max() for nd, _ in blocks) > 1.0   # the refinement's trigger
+        plain = max(_rel(_doubling(nd), ref) for nd, ref in blocks)
+        refined = max(_rel(_refined(nd), ref) for nd, ref in blocks)
+        assert plain > 5e-3 and refined < 3e-4 and refined < plain / 30, (rho, plain, refined)
