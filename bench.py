@@ -305,7 +305,9 @@ KDA_BYTES_PER_TOKEN_HEAD = 4 * 256 + 128 * 4 + 4
 
 
 def bench_kda(torch, gdn, inputs, steps, warmup):
-    """Whole gdn_kda_fwd calls (per-key-channel decay) on the throughput shape."""
+    """Whole gdn_kda_fwd calls (per-key-channel decay) on the throughput shape:
+    with the automatic sequence split (the default) and unsplit (one workgroup
+    per head)."""
     x = inputs.kda_workload(KDA_WORKLOAD)
     B, T, H, dk, dv = x.shape
     dev = torch.device("cuda:0")
@@ -316,22 +318,31 @@ def bench_kda(torch, gdn, inputs, steps, warmup):
     del x
     o = torch.empty_like(v)
     ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    segs = gdn.gdn_kda_plan_segments(B, T, H, cus)
+    nws = gdn.gdn_kda_fwd_workspace_size(B, T, H, dk, dv, n_segments=0)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
 
-    def step():
-        gdn.gdn_kda_fwd(q, k, v, g, beta, None, out=o, out_ht=ht)
+    def timed(nseg):
+        def step():
+            gdn.gdn_kda_fwd(q, k, v, g, beta, None, out=o, out_ht=ht, n_segments=nseg,
+                            workspace=ws if nseg == 0 else None)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    ms = timed(0)
+    ms1 = timed(1)
     nbytes = B * T * H * KDA_BYTES_PER_TOKEN_HEAD + B * H * STATE_BYTES
-    return {"workload": KDA_WORKLOAD, "B": B, "T": T, "H": H, "steps": steps, "ms_per_call": ms,
-            "tokens_per_s": B * T / (ms * 1e-3), "algorithmic_bytes": nbytes,
-            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return {"workload": KDA_WORKLOAD, "B": B, "T": T, "H": H, "steps": steps, "segments_per_head": segs,
+            "ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3), "algorithmic_bytes": nbytes,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "unsplit_ms_per_call": ms1}
 
 
 def cpu_baseline(x, tokens):

@@ -8,7 +8,7 @@ library's HIP kernels; there is no fallback path.
 
     gdn_chunk_fwd(q, k, v, g, beta, h0=None, scale=1.0, ...) -> (o, ht)
     gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None, ...) -> (o, ht)
-    gdn_kda_fwd(q, k, v, g, beta, h0=None, scale=1.0) -> (o, ht)   (g per key channel)
+    gdn_kda_fwd(q, k, v, g, beta, h0=None, scale=1.0, n_segments=0) -> (o, ht)   (g per key channel)
     gdn_chunk_bwd(q, k, v, g, beta, dout, h0=None, dht=None, scale=1.0) -> dict
     gdn_chunk_bwd_varlen(q, k, v, g, beta, dout, cu_seqlens, h0=None, ...) -> dict
     gdn_gate_scan(g, window_chunks=8, log_eps=log(2^-24)) -> (flags, max_window_logdecay)
@@ -25,7 +25,8 @@ from . import _lib
 
 DEFAULT_LOG_EPS = math.log(2.0 ** -24)
 
-__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_kda_fwd", "gdn_chunk_fwd_varlen", "gdn_chunk_bwd", "gdn_chunk_bwd_varlen", "gdn_gate_scan",
+__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_kda_fwd",
+           "gdn_kda_plan_segments", "gdn_kda_fwd_workspace_size", "gdn_chunk_fwd_varlen", "gdn_chunk_bwd", "gdn_chunk_bwd_varlen", "gdn_gate_scan",
            "gdn_plan_segments",
            "gdn_chunk_fwd_plan_info", "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd_workspace_size",
            "gdn_chunk_bwd_varlen_workspace_size", "options"]
@@ -238,10 +239,24 @@ def gdn_chunk_fwd_noalloc(q, k, v, g, beta, h0=None, scale=1.0, *, out, out_ht=N
     return out, out_ht
 
 
-def gdn_kda_fwd(q, k, v, g, beta, h0=None, scale=1.0, *, output_final_state=True, out=None, out_ht=None):
+def gdn_kda_plan_segments(B, T, H, num_cus, n_segments=0) -> int:
+    """Segments per head gdn_kda_fwd uses for these shapes on num_cus compute units."""
+    return _lib.load().gdn_kda_plan_segments(int(B), int(T), int(H), int(num_cus), int(n_segments))
+
+
+def gdn_kda_fwd_workspace_size(B, T, H, dk=128, dv=128, n_segments=0) -> int:
+    n = _lib.load().gdn_kda_fwd_workspace_size(int(B), int(T), int(H), int(dk), int(dv), int(n_segments))
+    if n == ctypes.c_size_t(-1).value:
+        raise _lib.GDNError(_lib.GDN_ERR_INVALID_ARG, _lib.last_error())
+    return int(n)
+
+
+def gdn_kda_fwd(q, k, v, g, beta, h0=None, scale=1.0, *, output_final_state=True, out=None, out_ht=None,
+                n_segments=0, workspace=None):
     """Chunked forward of the per-key-channel-decay variant (KDA): as
     gdn_chunk_fwd, with g [B, T, H, dk] float32 (one log-decay per key channel)
-    and bf16 q, k, v.  Returns (o, ht)."""
+    and bf16 q, k, v.  n_segments: 0 automatic sequence split, 1 unsplit, k >= 2
+    that many segments per head.  Returns (o, ht)."""
     torch = _torch()
     lib = _lib.load()
     _dev(q, "q", torch.bfloat16)
@@ -266,8 +281,16 @@ def gdn_kda_fwd(q, k, v, g, beta, h0=None, scale=1.0, *, output_final_state=True
         _shape(ht, "out_ht", (B, H, dk, dv), dev)
     else:
         ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
+    _workspace_arg(workspace, dev)
+    if workspace is None:
+        n = lib.gdn_kda_fwd_workspace_size(B, T, H, dk, dv, int(n_segments))
+        if n == ctypes.c_size_t(-1).value:
+            raise _lib.GDNError(_lib.GDN_ERR_INVALID_ARG, _lib.last_error())
+        workspace = _workspace(int(n), dev)
+    wsz = 0 if workspace is None else workspace.numel()
     _lib.check(lib.gdn_kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht),
-                               B, T, H, dk, dv, _lib.GDN_BF16, float(scale), _stream(dev)))
+                               B, T, H, dk, dv, _lib.GDN_BF16, float(scale), int(n_segments), _ptr(workspace),
+                               wsz, _stream(dev)))
     return o, ht
 
 

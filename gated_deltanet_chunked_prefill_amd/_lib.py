@@ -25,13 +25,13 @@ EXPORTS = ("gdn_default_options", "gdn_plan_segments", "gdn_chunk_fwd_workspace_
            "gdn_gate_scan_workspace_size", "gdn_gate_scan", "gdn_profile_events",
            "gdn_last_error", "gdn_chunk_fwd_plan_info", "gdn_chunk_fwd_varlen",
            "gdn_chunk_bwd_varlen_workspace_size", "gdn_chunk_bwd_varlen", "gdn_chunk_fwd_noalloc", "gdn_kda_fwd",
-           "gdn_stream_probe")
+           "gdn_kda_plan_segments", "gdn_kda_fwd_workspace_size", "gdn_stream_probe")
 #: bytes of the fixed scratch array of gdn_chunk_fwd_noalloc (GDN_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 LAUNCH_KINDS = {0: "gate_sums", 1: "gate_flags", 2: "fwd_single", 3: "fwd_windows",
                 4: "fwd_queue", 5: "bwd_states", 6: "bwd_dh", 7: "bwd_local", 8: "fwd_sums",
-                9: "kda_fwd", 10: "stream_probe"}
+                9: "kda_fwd", 10: "stream_probe", 11: "kda_pass1", 12: "kda_chain"}
 
 
 class Options(ctypes.Structure):
@@ -67,8 +67,12 @@ def load():
     lib.gdn_chunk_fwd.restype = _i
     lib.gdn_chunk_fwd_noalloc.argtypes = [_vp] * 8 + [_i] * 6 + [ctypes.c_float, op, _vp]
     lib.gdn_chunk_fwd_noalloc.restype = _i
-    lib.gdn_kda_fwd.argtypes = [_vp] * 8 + [_i] * 6 + [ctypes.c_float, _vp]
+    lib.gdn_kda_fwd.argtypes = [_vp] * 8 + [_i] * 6 + [ctypes.c_float, _i, _vp, _sz, _vp]
     lib.gdn_kda_fwd.restype = _i
+    lib.gdn_kda_plan_segments.argtypes = [_i] * 5
+    lib.gdn_kda_plan_segments.restype = _i
+    lib.gdn_kda_fwd_workspace_size.argtypes = [_i] * 6
+    lib.gdn_kda_fwd_workspace_size.restype = _sz
     lib.gdn_stream_probe.argtypes = [_vp] * 4 + [_i] * 3 + [_vp]
     lib.gdn_stream_probe.restype = _i
     lib.gdn_chunk_fwd_varlen.argtypes = [_vp] * 9 + [_i] * 6 + [ctypes.c_float, _vp]

@@ -224,6 +224,36 @@ BwdVarlenLayout bwd_varlen_layout(int S, int T, int H) {
     return L;
 }
 
+// KDA sequence split: P segments of S chunks per head (the last one shorter).
+// n_segments = 1: unsplit; n_segments >= 2: that many (at most the chunk count);
+// 0: as many as fill the device, cus / (B H), at most 16 and with at least 8
+// chunks each, and unsplit below 3 segments (the transition pass costs about as
+// much as the output pass, so two segments gain nothing).  S = ceil(N / P), then
+// P = ceil(N / S) so that no segment is empty.
+constexpr int kKdaMaxSegments = 1024;
+void kda_plan(int B, int T, int H, int cus, int n_segments, int* P, int* S) {
+    const int N = num_chunks(T);
+    int p = 1;
+    if (n_segments >= 2) {
+        p = n_segments < N ? n_segments : N;
+    } else if (n_segments == 0) {
+        const long bh = (long)B * H;
+        long a = cus / bh;
+        if (a > 16) a = 16;
+        if (a > N / 8) a = N / 8;
+        p = a >= 3 ? (int)a : 1;
+    }
+    if (p < 1) p = 1;
+    const int s = (N + p - 1) / p;
+    *S = s;
+    *P = (N + s - 1) / s;
+}
+
+// Workspace of the KDA split: (P - 1) slots of gdn::kKdaSlot floats per head.
+size_t kda_workspace_bytes(int B, int H, int P) {
+    return P > 1 ? (size_t)B * H * (P - 1) * gdn::kKdaSlot * sizeof(float) : 0;
+}
+
 gdn_status device_cus(int* cus) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -454,18 +484,58 @@ gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, co
 
 gdn_status gdn_kda_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                        const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, gdn_dtype dtype,
-                       float scale, void* stream) {
+                       float scale, int n_segments, void* workspace, size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     gdn_status st = check_fwd_args(q, k, v, g, beta, h0, o, ht, B, T, H, dk, dv, dtype, scale);
     if (st != GDN_OK) return st;
     if (dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "the KDA forward supports bf16 I/O only");
+    if (n_segments < 0 || n_segments > kKdaMaxSegments)
+        return fail(GDN_ERR_INVALID_ARG, "n_segments must be in [0, %d] (got %d)", kKdaMaxSegments, n_segments);
+    int cus = 0;
+    if (n_segments == 0 && (st = device_cus(&cus)) != GDN_OK) return st;
+    int P = 1, S = 1;
+    kda_plan(B, T, H, cus, n_segments, &P, &S);
+    const size_t need = kda_workspace_bytes(B, H, P);
+    if (need > 0) {
+        if (!workspace) return fail(GDN_ERR_WORKSPACE, "%d segments per head need a workspace of %zu bytes", P, need);
+        if (workspace_bytes < need)
+            return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+        if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+            return fail(GDN_ERR_INVALID_ARG, "the workspace must be %zu-byte aligned", kAlign);
+    }
     gdn::KdaParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.o = o; p.ht = ht;
     p.B = B; p.T = T; p.H = H; p.N = num_chunks(T); p.scale = scale;
+    p.P = P; p.S = S; p.ws = (float*)workspace;
     hipStream_t s = (hipStream_t)stream;
-    const hipError_t e = recorded(GDN_LAUNCH_KDA_FWD, s, [&] { return gdn::launch_kda_fwd(p, s); });
+    hipError_t e = hipSuccess;
+    if (P > 1) {
+        e = recorded(GDN_LAUNCH_KDA_PASS1, s, [&] { return gdn::launch_kda_fwd(p, gdn::KDA_PASS1, s); });
+        if (e != hipSuccess) return hip_fail(e, "KDA transition launch");
+        e = recorded(GDN_LAUNCH_KDA_CHAIN, s, [&] { return gdn::launch_kda_chain(p, s); });
+        if (e != hipSuccess) return hip_fail(e, "KDA chain launch");
+    }
+    e = recorded(GDN_LAUNCH_KDA_FWD, s, [&] { return gdn::launch_kda_fwd(p, gdn::KDA_FULL, s); });
     if (e != hipSuccess) return hip_fail(e, "KDA forward launch");
     return GDN_OK;
+}
+
+int gdn_kda_plan_segments(int B, int T, int H, int num_cus, int n_segments) {
+    if (B <= 0 || T <= 0 || H <= 0 || n_segments < 0 || n_segments > kKdaMaxSegments) return 0;
+    if (n_segments == 0 && num_cus <= 0) return 0;
+    int P = 1, S = 1;
+    kda_plan(B, T, H, num_cus, n_segments, &P, &S);
+    return P;
+}
+
+size_t gdn_kda_fwd_workspace_size(int B, int T, int H, int dk, int dv, int n_segments) {
+    if (check_shapes(B, T, H, dk, dv, GDN_BF16) != GDN_OK) return (size_t)-1;
+    if (n_segments < 0 || n_segments > kKdaMaxSegments) return (size_t)-1;
+    int cus = 0;
+    if (n_segments == 0 && device_cus(&cus) != GDN_OK) return (size_t)-1;
+    int P = 1, S = 1;
+    kda_plan(B, T, H, cus, n_segments, &P, &S);
+    return kda_workspace_bytes(B, H, P);
 }
 
 gdn_status gdn_stream_probe(const void* k, const void* q, const void* v, void* o, int T, int H, int segments,

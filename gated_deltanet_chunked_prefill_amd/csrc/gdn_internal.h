@@ -183,11 +183,25 @@ struct KdaParams {
     float* ht;         // nullable
     int B, T, H, N;
     float scale;
+    // sequence split: P segments of S chunks (the last one shorter); P = 1 runs
+    // unsplit.  ws: per batch-head bh and segment p < P - 1, at slot bh (P - 1) + p,
+    // kKdaSlot floats: the segment's transition M (its linear state map, [dk][dk])
+    // and its state b from a zero start ([dk][dv]), which the chain overwrites with
+    // the state entering segment p + 1 (float32, row-major).
+    int P, S;
+    float* ws;
 };
+constexpr size_t kKdaSlot = 2 * 128 * 128;
+enum { KDA_FULL = 0, KDA_PASS1 = 1 };
 // Streaming probe of the forward's memory pattern (gdn_probe.hip).
 hipError_t launch_stream_probe(const void* k, const void* q, const void* v, void* o, int T, int H, int segments,
                                hipStream_t s);
-hipError_t launch_kda_fwd(const KdaParams& p, hipStream_t s);
+// mode KDA_PASS1: the transitions of segments 0 .. P-2; KDA_FULL: every segment
+// with outputs (from h0 for segment 0, else from the state the chain left).
+hipError_t launch_kda_fwd(const KdaParams& p, int mode, hipStream_t s);
+// the states entering segments 1 .. P-1 from the transitions (one workgroup per
+// batch-head, segments in order)
+hipError_t launch_kda_chain(const KdaParams& p, hipStream_t s);
 size_t kda_smem_bytes();
 
 // Packed sequences: the stored states of sequence s, head h sit at per-head slots

@@ -182,29 +182,76 @@ __device__ __forceinline__ void kda_tiles(const KdaParams& prm, KdaSmem& sm, con
     __syncthreads();
 }
 
-// Waves 4-7: per chunk the shared steps, then the inverse and score blocks.
+// Waves 4-7: per chunk the shared steps, then the inverse and score blocks.  In
+// pass 1 of the sequence split (segment p < P - 1, no outputs, so no score
+// blocks) they also carry the segment's transition M from the identity, 32
+// columns each: the chunk step with no values (the chunk map is linear in the
+// state), after the blocks are written; M goes to the segment's slot.
 // Executes exactly the barriers of kda_state_loop.
-__device__ __noinline__ void kda_prep_loop(const KdaParams& prm, KdaSmem& sm) {
-    const int bh = blockIdx.x, H = uni(prm.H), N = uni(prm.N);
+template <bool PASS1>
+__device__ __noinline__ void kda_prep_loop(const KdaParams& prm, KdaSmem& sm, int bh, int p, int c0, int c1) {
+    using F = bf16x8;
+    const int H = uni(prm.H);
     const int b = bh / H, h = bh % H;
+    const int lane = threadIdx.x & 63;
     Lane<__bf16> L;
     L.init(threadIdx.x);
     TileLoader<__bf16, 8> TL;
-    TL.init(wave_id(), threadIdx.x & 63, H);
-    for (int c = 0; c < N; ++c) {
+    TL.init(wave_id(), lane, H);
+    const int n = L.n, gg = L.g, w = L.w;
+    const int pw = wave_id() - 4;
+    f32x16 Ms[4];
+    if (PASS1) {
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Ms[ht][r] = (32 * ht + rho(gg, r) == 32 * w + n) ? 1.f : 0.f;
+    }
+    for (int c = c0; c < c1; ++c) {
         kda_tiles(prm, sm, TL, b, h, c);
-        kda_prep(L, sm, wave_id() - 4);
+        if (!PASS1 || pw < 3) kda_prep(L, sm, pw);
         __syncthreads();   // blocks written
+        if (PASS1) {
+            // X = Kt M (state rows scaled by each half's exp(centre)), U = T (-X)
+            f32x16 X[2] = {zero16(), zero16()};
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const f32x16 s0 = rows_of(sm.ec0, ks >> 1, gg), s1 = rows_of(sm.ec1, ks >> 1, gg);
+                F m0f, m1f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int r = 8 * (ks & 1) + j;
+                    m0f[j] = (__bf16)(-Ms[ks >> 1][r] * s0[r]);
+                    m1f[j] = (__bf16)(-Ms[ks >> 1][r] * s1[r]);
+                }
+                m0f = nat_frag<__bf16>(m0f);
+                m1f = nat_frag<__bf16>(m1f);
+                X[0] = mma(L.f128(sm.kc, 0, ks), m0f, X[0]);
+                X[1] = mma(L.f128(sm.kc, 1, ks), m1f, X[1]);
+            }
+            const F y0f[2] = {acc_frag<__bf16>(X[0], 0), acc_frag<__bf16>(X[0], 1)};
+            f32x16 Vp[2];
+            block_solve<__bf16>(L, sm.t32[0], sm.t32[1], sm.t32[2], y0f, X[1], Vp);
+            F vf[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) vf[ks] = acc_frag<__bf16>(Vp[ks >> 1], ks & 1);
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht) Ms[ht] = Ms[ht] * rows_of(sm.eC, ht, gg);
+            kt_update<__bf16>(L, sm.ku, Ms, 1.f, vf);
+        }
         __syncthreads();   // the state step is done with the tiles
     }
+    if (PASS1) store_state(uni(prm.ws) + ((size_t)bh * (prm.P - 1) + p) * kKdaSlot, w, lane, Ms);
 }
 
 // Waves 0-3: the state (32 columns per wave, in MFMA accumulators) and the
-// serial chunk step.  Executes exactly the barriers of kda_prep_loop.
-__device__ __noinline__ void kda_state_loop(const KdaParams& prm, KdaSmem& sm) {
+// serial chunk step over chunks c0 .. c1-1 of segment p, with outputs; the
+// segment starts from h0 (p = 0) or from the state the chain left for it, and the
+// last segment writes ht.  Executes exactly the barriers of kda_prep_loop.
+template <bool PASS1>
+__device__ __noinline__ void kda_state_loop(const KdaParams& prm, KdaSmem& sm, int bh, int p, int c0, int c1) {
     using F = bf16x8;
-    const int bh = blockIdx.x;
-    const int Tn = uni(prm.T), H = uni(prm.H), N = uni(prm.N);
+    const int Tn = uni(prm.T), H = uni(prm.H);
     const int b = bh / H, h = bh % H;
     const int lane = threadIdx.x & 63;
     const float scale = uni(prm.scale);
@@ -215,13 +262,18 @@ __device__ __noinline__ void kda_state_loop(const KdaParams& prm, KdaSmem& sm) {
     TL.init(wave_id(), lane, H);
     const int n = L.n, gg = L.g, w = L.w;
     f32x16 Hs[4];
-    if (prm.h0) {
+    if (PASS1) {
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) Hs[ht] = zero16();
+    } else if (p > 0) {
+        load_state(uni(prm.ws) + ((size_t)bh * (prm.P - 1) + p - 1) * kKdaSlot + kDk * kDk, w, lane, Hs);
+    } else if (prm.h0) {
         load_state(uni(prm.h0) + (size_t)bh * kDk * kDv, w, lane, Hs);
     } else {
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) Hs[ht] = zero16();
     }
-    for (int c = 0; c < N; ++c) {
+    for (int c = c0; c < c1; ++c) {
         const int nv = chunk_len(Tn, c);
         kda_tiles(prm, sm, TL, b, h, c);
         // Kt H and (Qt H)^T: state rows of each k-step scaled by each half's exp(centre)
@@ -245,8 +297,10 @@ __device__ __noinline__ void kda_state_loop(const KdaParams& prm, KdaSmem& sm) {
             h1f = nat_frag<__bf16>(h1f);
             X[0] = mma(L.f128(sm.kc, 0, ks), h0f, X[0]);
             X[1] = mma(L.f128(sm.kc, 1, ks), h1f, X[1]);
-            OT[0] = mma(h0f, L.f128(sm.qc, 0, ks), OT[0]);
-            OT[1] = mma(h1f, L.f128(sm.qc, 1, ks), OT[1]);
+            if (!PASS1) {
+                OT[0] = mma(h0f, L.f128(sm.qc, 0, ks), OT[0]);
+                OT[1] = mma(h1f, L.f128(sm.qc, 1, ks), OT[1]);
+            }
         }
         __syncthreads();   // blocks written
         // Y = V - Kt H, U by block substitution
@@ -266,6 +320,13 @@ __device__ __noinline__ void kda_state_loop(const KdaParams& prm, KdaSmem& sm) {
         F vf[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) vf[ks] = acc_frag<__bf16>(Vp[ks >> 1], ks & 1);
+        if (PASS1) {
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht) Hs[ht] = Hs[ht] * rows_of(sm.eC, ht, gg);
+            kt_update<__bf16>(L, sm.ku, Hs, 1.f, vf);
+            __syncthreads();   // the tiles are free for the next chunk
+            continue;
+        }
         // O^T = (Qt H)^T + U^T P^T; P^T's B fragments are rows of P
         OT[0] = mma(vf[0], L.f32(sm.t32[3], 0), OT[0]);
         OT[0] = mma(vf[1], L.f32(sm.t32[3], 1), OT[0]);
@@ -311,33 +372,109 @@ __device__ __noinline__ void kda_state_loop(const KdaParams& prm, KdaSmem& sm) {
         }
         __syncthreads();   // the tiles are free for the next chunk
     }
-    if (prm.ht) store_state(uni(prm.ht) + (size_t)bh * kDk * kDv, w, lane, Hs);
+    if (PASS1)
+        store_state(uni(prm.ws) + ((size_t)bh * (prm.P - 1) + p) * kKdaSlot + kDk * kDk, w, lane, Hs);
+    else if (prm.ht && p == prm.P - 1)
+        store_state(uni(prm.ht) + (size_t)bh * kDk * kDv, w, lane, Hs);
 }
 
+template <int MODE>
 __global__ __launch_bounds__(kKdaThreads, 1) void gdn_kda_fwd_kernel(KdaParams prm) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     KdaSmem& sm = *reinterpret_cast<KdaSmem*>(smem_raw);
+    const int segs = MODE == KDA_PASS1 ? prm.P - 1 : prm.P;
+    const int bh = (int)blockIdx.x / segs, p = (int)blockIdx.x % segs;
+    const int c0 = p * prm.S, c1 = min(c0 + prm.S, prm.N);
     // the role branch is wave-uniform: both roles hold barriers
     if (wave_id() < 4)
-        kda_state_loop(prm, sm);
+        kda_state_loop<MODE == KDA_PASS1>(prm, sm, bh, p, c0, c1);
     else
-        kda_prep_loop(prm, sm);
+        kda_prep_loop<MODE == KDA_PASS1>(prm, sm, bh, p, c0, c1);
+}
+
+// The states entering segments 1 .. P-1 of batch-head blockIdx.x: S_{p+1} =
+// M_p S_p + b_p from S_0 = h0 (or zero), in float32 on the vector units (one
+// 128 x 128 x 128 product per segment), written over b_p in segment p's slot.
+// Thread t owns rows 4 (t >> 4) .. +3 and columns 8 (t & 15) .. +7 of the
+// result (it reads exactly those entries of b_p first); M^T and S in LDS (64 KB
+// each).
+__global__ __launch_bounds__(512, 1) void kda_chain_kernel(KdaParams prm) {
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    float* const MT = reinterpret_cast<float*>(smem_raw);   // [k][i]
+    float* const Sl = MT + kDk * kDk;                         // [k][j]
+    const int bh = blockIdx.x, t = threadIdx.x;
+    const int i0 = 4 * (t >> 4), j0 = 8 * (t & 15);
+    const size_t SS = (size_t)kDk * kDv;
+    float* const base = prm.ws + (size_t)bh * (prm.P - 1) * kKdaSlot;
+    for (int e = t; e < (int)SS; e += 512) Sl[e] = prm.h0 ? prm.h0[(size_t)bh * SS + e] : 0.f;
+    for (int p = 0; p + 1 < prm.P; ++p) {
+        const float* const M = base + (size_t)p * kKdaSlot;
+        float* const bp = base + (size_t)p * kKdaSlot + (size_t)kDk * kDk;
+        for (int e = t; e < (int)SS; e += 512) MT[(e & (kDk - 1)) * kDk + (e >> 7)] = M[e];   // M[i][k] -> MT[k][i]
+        __syncthreads();
+        float acc[4][8];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[a][c] = bp[(size_t)(i0 + a) * kDv + j0 + c];
+        for (int k = 0; k < kDk; ++k) {
+            const f32x4 m = *reinterpret_cast<const f32x4*>(MT + k * kDk + i0);
+            const f32x4 s0 = *reinterpret_cast<const f32x4*>(Sl + k * kDv + j0);
+            const f32x4 s1 = *reinterpret_cast<const f32x4*>(Sl + k * kDv + j0 + 4);
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    acc[a][c] = __builtin_fmaf(m[a], s0[c], acc[a][c]);
+                    acc[a][4 + c] = __builtin_fmaf(m[a], s1[c], acc[a][4 + c]);
+                }
+        }
+        __syncthreads();   // every product has read S_p and M^T
+        float* const nxt = bp;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                Sl[(i0 + a) * kDv + j0 + c] = acc[a][c];
+                nxt[(size_t)(i0 + a) * kDv + j0 + c] = acc[a][c];
+            }
+        __syncthreads();
+    }
 }
 
 }  // namespace
 
 size_t kda_smem_bytes() { return sizeof(KdaSmem); }
 
-hipError_t launch_kda_fwd(const KdaParams& p, hipStream_t s) {
+hipError_t launch_kda_fwd(const KdaParams& p, int mode, hipStream_t s) {
     static bool configured = false;
     const size_t lds = sizeof(KdaSmem);
     if (!configured) {
-        const hipError_t e = hipFuncSetAttribute((const void*)gdn_kda_fwd_kernel,
+        hipError_t e = hipFuncSetAttribute((const void*)gdn_kda_fwd_kernel<KDA_FULL>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute((const void*)gdn_kda_fwd_kernel<KDA_PASS1>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        configured = true;
+    }
+    if (mode == KDA_PASS1)
+        hipLaunchKernelGGL(gdn_kda_fwd_kernel<KDA_PASS1>, dim3(p.B * p.H * (p.P - 1)), dim3(kKdaThreads), lds, s, p);
+    else
+        hipLaunchKernelGGL(gdn_kda_fwd_kernel<KDA_FULL>, dim3(p.B * p.H * p.P), dim3(kKdaThreads), lds, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_kda_chain(const KdaParams& p, hipStream_t s) {
+    static bool configured = false;
+    const size_t lds = 2 * (size_t)kDk * kDk * sizeof(float);
+    if (!configured) {
+        const hipError_t e = hipFuncSetAttribute((const void*)kda_chain_kernel,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         configured = true;
     }
-    hipLaunchKernelGGL(gdn_kda_fwd_kernel, dim3(p.B * p.H), dim3(kKdaThreads), lds, s, p);
+    hipLaunchKernelGGL(kda_chain_kernel, dim3(p.B * p.H), dim3(512), lds, s, p);
     return hipGetLastError();
 }
 

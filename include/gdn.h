@@ -209,15 +209,42 @@ gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
  *   q, k, v, o        as for gdn_chunk_fwd, bfloat16 only (GDN_ERR_UNSUPPORTED otherwise)
  *   g                 [B, T, H, dk] float32, log-decays (<= 0) per key channel
  *   beta, h0, ht      as for gdn_chunk_fwd (h0, ht nullable)
+ *   n_segments        sequence split (talk summary, paragraph 4): 1 = one
+ *                     workgroup per (batch, head) over all chunks in order;
+ *                     k >= 2 = k segments of ceil(N / k) chunks (N = ceil(T/64),
+ *                     fewer when the last ones would be empty); 0 = automatic
+ *                     (gdn_kda_plan_segments with the current device's CU count).
+ *                     At most 1024.
+ *   workspace         device memory of gdn_kda_fwd_workspace_size() bytes,
+ *                     256-byte aligned (NULL allowed when that size is 0)
  * The chunk step applies the per-channel decay factors to the K and Q tiles
  * (re-centred per 32-token half, and at the half boundary for the block that
  * couples the halves), so results are finite as long as no key channel decays
- * by more than exp(-176) over 16 consecutive tokens of a 64-token chunk.  One
- * workgroup per (batch, head), chunks in order; no workspace, no sequence split.
- * Errors as for gdn_chunk_fwd. */
+ * by more than exp(-176) over 16 consecutive tokens of a 64-token chunk.
+ * With P > 1 segments the split is exact (no window shortcut): the chunk map is
+ * affine in the state, S_out = M S_in + b, so a first launch runs segments
+ * 0 .. P-2 from the identity and from zero to get each segment's M (dk x dk) and
+ * b (float32, in the workspace), a second composes them in order into the state
+ * entering every segment, and the third runs all segments with outputs from
+ * those states.  Results differ from the unsplit call by rounding only.
+ * Errors as for gdn_chunk_fwd; GDN_ERR_WORKSPACE when the workspace is missing
+ * or too small. */
 gdn_status gdn_kda_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                        const float* h0, void* o, float* ht, int B, int T, int H, int dk, int dv, gdn_dtype dtype,
-                       float scale, void* stream);
+                       float scale, int n_segments, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Segments per head gdn_kda_fwd uses for these shapes on a device with num_cus
+ * compute units (host only): 1 for n_segments = 1; min(n_segments, N) reduced to
+ * ceil(N / ceil(N / n_segments)) for n_segments >= 2; for n_segments = 0,
+ * a = min(16, floor(num_cus / (B H)), floor(N / 8)) reduced the same way when
+ * a >= 3, else 1.  Returns 0 for invalid arguments (num_cus is read only when
+ * n_segments = 0). */
+int gdn_kda_plan_segments(int B, int T, int H, int num_cus, int n_segments);
+
+/* Workspace bytes gdn_kda_fwd needs on the current device: B H (P - 1) x 2 x
+ * 128 x 128 float32 values for P segments per head (0 when P = 1).  Returns
+ * (size_t)-1 for invalid arguments. */
+size_t gdn_kda_fwd_workspace_size(int B, int T, int H, int dk, int dv, int n_segments);
 
 /* Workspace bytes for gdn_chunk_bwd_varlen ((size_t)-1 for invalid arguments):
  * the chunk prefix and bounds of the sequences, and per head (ceil(T/64) + 2 n_seqs)
@@ -315,8 +342,10 @@ typedef enum {
     GDN_LAUNCH_BWD_DH = 6,      /* backward: state gradient, end to start             */
     GDN_LAUNCH_BWD_LOCAL = 7,   /* backward: local gradients of every chunk           */
     GDN_LAUNCH_FWD_SUMS = 8,    /* split forward: chunk sums of g, planner reset      */
-    GDN_LAUNCH_KDA_FWD = 9,     /* KDA forward                                        */
-    GDN_LAUNCH_STREAM_PROBE = 10 /* measurement aid: the forward's memory pattern     */
+    GDN_LAUNCH_KDA_FWD = 9,     /* KDA forward (with outputs)                         */
+    GDN_LAUNCH_STREAM_PROBE = 10, /* measurement aid: the forward's memory pattern    */
+    GDN_LAUNCH_KDA_PASS1 = 11,  /* KDA split: segment transitions and zero-start states */
+    GDN_LAUNCH_KDA_CHAIN = 12   /* KDA split: states entering the segments            */
 } gdn_launch_kind;
 
 /* Measurement hook (the talk summary, paragraph 7, argues the fused operator

@@ -268,13 +268,15 @@ def test_varlen_prefix_spans_stay_in_slots(case):
 
 
 def test_kda_validation_before_launch():
-    """gdn_kda_fwd: bf16 only, the forward's argument checks, nothing launched."""
+    """gdn_kda_fwd: bf16 only, the forward's argument checks, the segment count
+    and the workspace, all checked before anything is launched."""
     lib = _lib.load()
     A = 1 << 20
     P = lambda a: ctypes.c_void_p(a) if a else None
 
-    def call(q=A, g=A, dt=1, T=128, H=1, dk=128):
-        return lib.gdn_kda_fwd(P(q), P(A), P(A), P(g), P(A), None, P(A), None, 1, T, H, dk, 128, dt, 1.0, None)
+    def call(q=A, g=A, dt=1, T=128, H=1, dk=128, nseg=1, ws=0, wsz=0):
+        return lib.gdn_kda_fwd(P(q), P(A), P(A), P(g), P(A), None, P(A), None, 1, T, H, dk, 128, dt, 1.0,
+                               nseg, P(ws), wsz, None)
     assert call(q=0) == _lib.GDN_ERR_INVALID_ARG
     assert call(g=0) == _lib.GDN_ERR_INVALID_ARG
     assert call(dt=0) == _lib.GDN_ERR_UNSUPPORTED
@@ -282,3 +284,36 @@ def test_kda_validation_before_launch():
     assert call(dk=64) == _lib.GDN_ERR_UNSUPPORTED
     assert call(T=0) == _lib.GDN_ERR_INVALID_ARG
     assert call(g=A + 2) == _lib.GDN_ERR_INVALID_ARG
+    assert call(nseg=-1) == _lib.GDN_ERR_INVALID_ARG
+    assert call(nseg=1025) == _lib.GDN_ERR_INVALID_ARG
+    # two segments of one chunk each need (P - 1) slots of 2 x 128 x 128 floats
+    need = 2 * 128 * 128 * 4
+    assert call(nseg=2) == _lib.GDN_ERR_WORKSPACE
+    assert call(nseg=2, ws=A, wsz=need - 1) == _lib.GDN_ERR_WORKSPACE
+    assert call(nseg=2, ws=A + 16, wsz=need) == _lib.GDN_ERR_INVALID_ARG
+
+
+def test_kda_plan_and_workspace():
+    """The KDA split's host planner and workspace size (no device needed for
+    n_segments >= 1; the automatic count reads num_cus)."""
+    lib = _lib.load()
+    plan = lib.gdn_kda_plan_segments
+    assert plan(1, 32768, 32, 256, 0) == 8           # 256 CUs / 32 heads, 512 chunks
+    assert plan(1, 32768, 8, 256, 0) == 16           # capped at 16
+    assert plan(1, 32768, 128, 256, 0) == 1          # two per head would not pay
+    assert plan(1, 32768, 64, 256, 0) == 4
+    assert plan(1, 32768, 80, 256, 0) == 3
+    assert plan(1, 1024, 4, 256, 0) == 1             # 16 chunks: at most 2 of 8 chunks
+    assert plan(1, 3072, 4, 256, 0) == 6             # 48 chunks: 6 segments of 8
+    assert plan(1, 128, 1, 256, 1) == 1
+    assert plan(1, 128, 1, 256, 5) == 2              # at most one segment per chunk
+    assert plan(1, 64 * 10, 1, 0, 4) == 4            # 3, 3, 3, 1 chunks
+    assert plan(1, 64 * 10, 1, 0, 6) == 5            # S = 2: 5 segments, none empty
+    assert plan(1, 64 * 10, 1, 0, 0) == 0            # automatic needs the CU count
+    assert plan(0, 128, 1, 256, 1) == 0
+    assert plan(1, 128, 1, 256, -1) == 0
+    wsz = lib.gdn_kda_fwd_workspace_size
+    assert wsz(2, 64 * 10, 3, 128, 128, 1) == 0
+    assert wsz(2, 64 * 10, 3, 128, 128, 4) == 2 * 3 * 3 * 2 * 128 * 128 * 4
+    assert wsz(2, 64 * 10, 3, 128, 128, -2) == ctypes.c_size_t(-1).value
+    assert wsz(2, 64 * 10, 3, 64, 128, 2) == ctypes.c_size_t(-1).value

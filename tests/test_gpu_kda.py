@@ -20,11 +20,11 @@ def gdn():
     return m
 
 
-def _run(gdn, x, scale=1.0):
+def _run(gdn, x, scale=1.0, n_segments=0):
     import torch
     t = to_gpu(x)
     g = torch.from_numpy(np.ascontiguousarray(x.g)).cuda()
-    o, ht = gdn.gdn_kda_fwd(t["q"], t["k"], t["v"], g, t["beta"], t["h0"], scale=scale)
+    o, ht = gdn.gdn_kda_fwd(t["q"], t["k"], t["v"], g, t["beta"], t["h0"], scale=scale, n_segments=n_segments)
     torch.cuda.synchronize()
     oref, href = oracle.kda_fwd(x.q, x.k, x.v, x.g, x.beta, x.h0, scale=scale)
     return to_np(o), to_np(ht), oref, href
@@ -88,6 +88,81 @@ def test_kda_equal_channels_match_gdn_forward(gdn):
     oref, href = oracle.fwd(x.q, x.k, x.v, x.g, x.beta, x.h0)
     _check(to_np(o1), to_np(h1), oref, href, "KDA kernel vs scalar-gate oracle")
     assert rel_err(to_np(o1), to_np(o2)) <= TOL_BF16 and rel_err(to_np(h1), to_np(h2)) <= TOL_BF16
+
+
+# Sequence split: segments 0 .. P-2 give their transition M and zero-start state
+# b, the chain composes them, every segment then runs from its entering state.
+@pytest.mark.parametrize("nseg", [2, 3, 4, 10])
+def test_kda_split(gdn, nseg):
+    """T = 9 chunks + 13 tokens (10 chunks, the last ragged): 2, 3, 4 and 10
+    segments (one chunk each) with h0, against the oracle and the unsplit call."""
+    say(f"case KDA split n_segments={nseg}")
+    x = inputs.generate_kda(B=2, T=64 * 9 + 13, H=2, h0_std=0.05, seed=220 + nseg)
+    o, ht, oref, href = _run(gdn, x, scale=0.8, n_segments=nseg)
+    _check(o, ht, oref, href, f"split {nseg}")
+    o1, h1, _, _ = _run(gdn, x, scale=0.8, n_segments=1)
+    d = max(rel_err(o, o1), rel_err(ht, h1))
+    say(f"  split {nseg} vs unsplit: {d:.3e}")
+    assert d <= 1e-2, d
+
+
+def test_kda_split_no_h0_correlated_keys(gdn):
+    """Split into 3 segments (4, 4, 3 chunks), no h0, keys of cosine 0.9, beta up to 2."""
+    say("case KDA split 3, no h0, rho=0.9, beta<=2")
+    x = inputs.generate_kda(B=1, T=64 * 11 - 5, H=3, seed=231, key_corr=0.9, beta_max=2.0)
+    _check(*_run(gdn, x, n_segments=3), "split 3 rho=0.9 beta<=2")
+
+
+def test_kda_split_strong_decay(gdn):
+    """Split into 4 segments with channels decaying by up to e^-3 per token: the
+    transitions are near zero in those rows, the composed states still match."""
+    say("case KDA split 4, strong per-channel decay")
+    x = inputs.generate_kda(B=1, T=64 * 8, H=2, gate="uniform", gate_lo=-3.0, gate_hi=-0.0, h0_std=0.05,
+                            seed=232)
+    _check(*_run(gdn, x, n_segments=4), "split 4 strong decay")
+
+
+def test_kda_split_workspace_reuse(gdn):
+    """One caller-owned workspace for two calls in a row, the second smaller and
+    with other segment counts: stale slots from the first call change nothing."""
+    import torch
+    say("case KDA split workspace reuse")
+    xa = inputs.generate_kda(B=1, T=64 * 12, H=3, h0_std=0.05, seed=233)
+    xb = inputs.generate_kda(B=2, T=64 * 5 + 1, H=1, h0_std=0.05, seed=234)
+    n = gdn.gdn_kda_fwd_workspace_size(1, 64 * 12, 3, n_segments=6)
+    assert n == 3 * 5 * 2 * 128 * 128 * 4
+    ws = torch.full((n,), 255, dtype=torch.uint8, device="cuda")   # NaN bit patterns
+    for x, nseg in ((xa, 6), (xb, 3)):
+        t = to_gpu(x)
+        g = torch.from_numpy(np.ascontiguousarray(x.g)).cuda()
+        o, ht = gdn.gdn_kda_fwd(t["q"], t["k"], t["v"], g, t["beta"], t["h0"], n_segments=nseg, workspace=ws)
+        torch.cuda.synchronize()
+        oref, href = oracle.kda_fwd(x.q, x.k, x.v, x.g, x.beta, x.h0)
+        _check(to_np(o), to_np(ht), oref, href, f"reuse n_segments={nseg}")
+
+
+@pytest.mark.slow
+def test_kda_throughput_shape_split_sampled(gdn):
+    """The throughput shape (T = 32768, H = 32) with the automatic split (8
+    segments of 64 chunks on 256 CUs): heads 0 and 31 against the oracle over the
+    whole sequence, every head against the unsplit call."""
+    import torch
+    say("case bf16_kda_t32768_h32 automatic split, heads 0 and 31 vs the oracle")
+    x = inputs.kda_workload("bf16_kda_t32768_h32")
+    t = to_gpu(x)
+    g = torch.from_numpy(np.ascontiguousarray(x.g)).cuda()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    say(f"  {cus} CUs: {gdn.gdn_kda_plan_segments(1, 32768, 32, cus)} segments per head")
+    o, ht = gdn.gdn_kda_fwd(t["q"], t["k"], t["v"], g, t["beta"], None)
+    o1, h1 = gdn.gdn_kda_fwd(t["q"], t["k"], t["v"], g, t["beta"], None, n_segments=1)
+    torch.cuda.synchronize()
+    d = max(rel_err(to_np(o), to_np(o1)), rel_err(to_np(ht), to_np(h1)))
+    say(f"  split vs unsplit, every head: {d:.3e}")
+    assert d <= 1e-2, d
+    for h in (0, 31):
+        sl = slice(h, h + 1)
+        oref, href = oracle.kda_fwd(x.q[:, :, sl], x.k[:, :, sl], x.v[:, :, sl], x.g[:, :, sl], x.beta[:, :, sl])
+        _check(to_np(o[:, :, sl]), to_np(ht[:, sl]), oref, href, f"head {h}")
 
 
 @pytest.mark.slow
