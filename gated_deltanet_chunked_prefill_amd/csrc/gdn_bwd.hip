@@ -55,9 +55,6 @@ constexpr bool kDhLoadAhead = true;
 constexpr int kLocalThreads = 256;  // 4 waves
 // direct state loads per wave in the local-gradient kernel (four 64 x 128 tiles)
 constexpr int kStateLoads = 16;
-// s_waitcnt immediate for vmcnt(n) alone, n < 64 (vmcnt in bits 3:0 and 15:14;
-// expcnt and lgkmcnt at their maxima, as in vmcnt(0) = 0x3f70)
-constexpr int vmcnt_wait(int n) { return 0x3f70 | (n & 15) | (((n >> 4) & 3) << 14); }
 
 // ---------------------------------------------------------------------------
 // Launch 1: reverse sweep of the state gradient.

@@ -50,6 +50,9 @@ struct Smem {
 };
 
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x3f70); }   // vmcnt(0)
+// s_waitcnt immediate for vmcnt(n) alone, n < 64 (vmcnt in bits 3:0 and 15:14;
+// expcnt and lgkmcnt at their maxima, as in vmcnt(0) = 0x3f70)
+constexpr int vmcnt_wait(int n) { return 0x3f70 | (n & 15) | (((n >> 4) & 3) << 14); }
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xc07f); } // lgkmcnt(0)
 
 // Workgroup barrier that orders LDS only: outstanding global stores of the

@@ -59,7 +59,20 @@ struct KdaSmem {
     float eC[kDk];             // exp(G_C)
     float psum[4][kDk];        // per key channel: sums of g over tokens 16p .. 16p + 15
     float beta[kChunk];
+    float gst[kChunk * kDk];   // the next chunk's gates [token][channel], staged by direct loads
+    float bst[kChunk];         // the next chunk's beta, staged likewise
 };
+static_assert(sizeof(KdaSmem) <= 160 * 1024, "KDA LDS exceeds a CU's 160 KB");
+
+// Workgroup barrier ordering LDS only: the prep waves' direct loads into the
+// other buffers stay in flight (a release fence on LDS would wait for them,
+// since they write LDS); their readers wait for them explicitly.
+__device__ __forceinline__ void bar() {
+    wait_lgkm();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // A 32 x 32 block written as an A-layout tile (lane n = row n): values x[r] at
 // row n, column rho(g, r), times `s` and masked to columns <= n when `lower`.
@@ -115,39 +128,116 @@ __device__ __forceinline__ void kda_prep(const Lane<__bf16>& L, KdaSmem& sm, int
     }
 }
 
-// Steps 1 and 2 of chunk c, run by every wave: the raw K, Q, V tiles (zero past
-// the end of the sequence), beta, the cumulative decays per key channel and the
-// re-centred tiles.  Thread (channel ch, quarter part) owns tokens 16 part ..
-// 16 part + 15 of key channel ch.  Ends with a barrier.
-__device__ __forceinline__ void kda_tiles(const KdaParams& prm, KdaSmem& sm, const TileLoader<__bf16, 8>& TL, int b,
-                                          int h, int c) {
-    const int Tn = uni(prm.T), H = uni(prm.H);
-    const int tid = threadIdx.x;
-    const int ch = tid & (kDk - 1), part = tid >> 7;
+// Loads of chunk c, issued by prep wave pw (0..3) as direct buffer loads into
+// LDS, which are waited for only where their data is read.  Each tensor's
+// buffer descriptor starts at the chunk's first row and ends after its last
+// row in the sequence, so rows past the sequence's end read as zero.  The fp32
+// gates and beta go to the staging area; the raw K, Q, V tiles go to kd, kc and
+// bnd (swizzled rows as toff), buffers whose previous contents are dead once
+// the chunk before has written its blocks.  In pass 1 of the sequence split Q
+// is not needed.
+// The launch's input pointers and sizes, read once per workgroup into scalar
+// registers: a read of the parameter block inside the chunk loop is a vector
+// memory load, whose wait would also wait for every prefetch issued before it.
+struct KdaIO {
+    const __bf16 *k, *q, *v;
+    const float *g, *beta;
+    int T, H;
+    __device__ __forceinline__ void init(const KdaParams& prm) {
+        k = uni((const __bf16*)prm.k);
+        q = uni((const __bf16*)prm.q);
+        v = uni((const __bf16*)prm.v);
+        g = uni(prm.g);
+        beta = uni(prm.beta);
+        T = uni(prm.T);
+        H = uni(prm.H);
+    }
+};
+
+constexpr int kKdaGateLoads = kChunk * kDk * 4 / (4 * 1024);   // 1 KB per wave instruction: 8 per wave
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t kda_rows(const void* first_row, int rows, int row_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(first_row), (short)0, rows * row_bytes, 0x00020000);
+}
+__device__ __forceinline__ void kda_stage_gates(const KdaIO& io, KdaSmem& sm, int pw, int lane, int b, int h, int c) {
+    const int Tn = io.T, H = io.H;
+    const int nv = chunk_len(Tn, c);
+    const size_t row0 = ((size_t)b * Tn + (size_t)c * kChunk) * H + h;
+    const __amdgpu_buffer_rsrc_t rg = kda_rows(io.g + row0 * kDk, nv, H * kDk * 4);
+    // rows 2R, 2R + 1 for R = 4 i + pw: 1 KB, lane-contiguous in LDS
+    const int voff = (2 * pw + (lane >> 5)) * H * kDk * 4 + 16 * (lane & 31);
+#pragma unroll
+    for (int i = 0; i < kKdaGateLoads; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (__attribute__((address_space(3))) void*)(sm.gst + 2 * (4 * i + pw) * kDk),
+                                                 16, voff, i * 8 * H * kDk * 4, 0, kCpolStream);
+    // every prep wave writes the same 256 bytes of beta (with the load under a
+    // wave-index branch this compiler's gfx950 back end rejects the kernel)
+    const __amdgpu_buffer_rsrc_t rb = kda_rows(io.beta + row0, nv, H * 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)sm.bst, 4, lane * H * 4, 0, 0,
+                                             kCpolStream);
+}
+template <bool PASS1>
+__device__ __forceinline__ void kda_stage_tiles(const KdaIO& io, KdaSmem& sm, int pw, int lane, int b, int h, int c) {
+    const int Tn = io.T, H = io.H;
     const int nv = chunk_len(Tn, c);
     const size_t cb = chunk_base(b, h, Tn, H, c);
-    TL.load(sm.ku, uni((const __bf16*)prm.k) + cb, nv);
-    TL.load(sm.qc, uni((const __bf16*)prm.q) + cb, nv);
-    TL.load(sm.vt, uni((const __bf16*)prm.v) + cb, nv);
-    typedef __attribute__((address_space(1))) const float gfloat;
-    if (tid < kChunk)
-        sm.beta[tid] = tid < nv ? ((gfloat*)uni(prm.beta))[((size_t)b * Tn + (size_t)c * kChunk + tid) * H + h] : 0.f;
-    const float* const gp = uni(prm.g);
-    float gl[16];
+    const int rb = H * kDk * 2;   // bytes between rows
+    const __amdgpu_buffer_rsrc_t rk = kda_rows(io.k + cb, nv, rb);
+    const __amdgpu_buffer_rsrc_t rq = kda_rows(io.q + cb, nv, rb);
+    const __amdgpu_buffer_rsrc_t rv = kda_rows(io.v + cb, nv, rb);
+    // round i: tile slots (4 i + pw) * 64 + lane, i.e. row 16 i + 4 pw + lane / 16
+    // and 16-byte piece lane % 16 (stored at slot piece ^ swz16(row), which does
+    // not depend on i)
+    const int row = 4 * pw + (lane >> 4);
+    const int voff = row * rb + (((lane & 15) ^ swz16(row)) << 4);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int t = 16 * part + j;
-        gl[j] = t < nv ? ((gfloat*)gp)[(((size_t)b * Tn + (size_t)c * kChunk + t) * H + h) * kDk + ch] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+        const int so = 16 * i * rb, lo = (4 * i + pw) * 64 * 8;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(sm.kd + lo), 16, voff, so,
+                                                 0, kCpolStream);
+        if (!PASS1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(sm.kc + lo), 16, voff,
+                                                     so, 0, kCpolStream);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(sm.bnd + lo), 16, voff,
+                                                 so, 0, kCpolStream);
     }
+}
+// direct loads of kda_stage_tiles per prep wave
+template <bool PASS1>
+constexpr int kda_tile_loads() { return (PASS1 ? 2 : 3) * kChunk * kDk * 2 / (4 * 1024); }
+
+// Step 1 of chunk c, by every wave, from the staged gates: thread (channel ch,
+// quarter part) owns tokens 16 part .. 16 part + 15 of key channel ch and forms
+// their in-chunk cumulative sums; the quarter sums go to LDS, beta to its slot.
+// A barrier follows.
+__device__ __forceinline__ void kda_gates(int Tn, KdaSmem& sm, int c, float (&gl)[16]) {
+    const int nv = chunk_len(Tn, c);
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));   // per-chunk addressing, not hoisted out of the chunk loop
+    const int ch = tid & (kDk - 1), part = tid >> 7;
     float run = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-        run += gl[j];
+        const int t = 16 * part + j;
+        const float x = sm.gst[t * kDk + ch];
+        run += t < nv ? x : 0.f;
         gl[j] = run;
     }
     sm.psum[part][ch] = run;
-    wait_vm();
-    __syncthreads();
+    if (tid < kChunk) {
+        const float x = sm.bst[tid];
+        sm.beta[tid] = tid < nv ? x : 0.f;
+    }
+}
+
+// Step 2 of chunk c, by every wave: the re-centred tiles from the raw K, Q, V
+// tiles (each thread reads and then overwrites only its own elements of kd, kc
+// and bnd, so the in-place reuse is race-free); rows past the sequence's end
+// are zeroed here, whatever the buffer loads left in them.  A barrier follows.
+template <bool PASS1>
+__device__ __forceinline__ void kda_scale(KdaSmem& sm, const float (&gl)[16], int nv) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));   // per-chunk addressing, not hoisted out of the chunk loop
+    const int ch = tid & (kDk - 1), part = tid >> 7;
     float Gend[4];
     Gend[0] = sm.psum[0][ch];
 #pragma unroll
@@ -160,18 +250,22 @@ __device__ __forceinline__ void kda_tiles(const KdaParams& prm, KdaSmem& sm, con
         const int t = 16 * part + j;
         const float G = off + gl[j];
         const int e = toff<__bf16, kDk>(t, ch);
-        const float kv = (float)sm.ku[e], qv = (float)sm.qc[e];
+        const bool in = t < nv;
+        const float kv = in ? (float)sm.kd[e] : 0.f;
+        const float qv = PASS1 || !in ? 0.f : (float)sm.kc[e];
+        const __bf16 vv = sm.bnd[e];
+        sm.vt[e] = in ? vv : (__bf16)0.f;
         const float ec = __expf(G - centre), ed = __expf(centre - G);
         sm.kc[e] = (__bf16)(kv * ec);
         sm.kd[e] = (__bf16)(kv * ed);
-        sm.qc[e] = (__bf16)(qv * ec);
+        if (!PASS1) sm.qc[e] = (__bf16)(qv * ec);
         sm.ku[e] = (__bf16)(kv * __expf(gC - G));
         if (part < 2) {
             sm.bnd[e] = (__bf16)(kv * __expf(gb - G));
         } else {
             const float eb = __expf(G - gb);
             sm.bnd[e] = (__bf16)(kv * eb);
-            sm.bq[toff<__bf16, kDk>(t - 32, ch)] = (__bf16)(qv * eb);
+            if (!PASS1) sm.bq[toff<__bf16, kDk>(t - 32, ch)] = (__bf16)(qv * eb);
         }
     }
     if (part == 0) {
@@ -179,7 +273,6 @@ __device__ __forceinline__ void kda_tiles(const KdaParams& prm, KdaSmem& sm, con
         sm.ec1[ch] = __expf(c1);
         sm.eC[ch] = __expf(gC);
     }
-    __syncthreads();
 }
 
 // Waves 4-7: per chunk the shared steps, then the inverse and score blocks.  In
@@ -190,16 +283,18 @@ __device__ __forceinline__ void kda_tiles(const KdaParams& prm, KdaSmem& sm, con
 // Executes exactly the barriers of kda_state_loop.
 template <bool PASS1>
 __device__ __noinline__ void kda_prep_loop(const KdaParams& prm, KdaSmem& sm, int bh, int p, int c0, int c1) {
+    // arguments arrive in vector registers: make them wave-uniform
+    bh = uni(bh), p = uni(p), c0 = uni(c0), c1 = uni(c1);
     using F = bf16x8;
-    const int H = uni(prm.H);
+    KdaIO io;
+    io.init(prm);
+    const int H = io.H;
     const int b = bh / H, h = bh % H;
     const int lane = threadIdx.x & 63;
     Lane<__bf16> L;
     L.init(threadIdx.x);
-    TileLoader<__bf16, 8> TL;
-    TL.init(wave_id(), lane, H);
-    const int n = L.n, gg = L.g, w = L.w;
     const int pw = wave_id() - 4;
+    const int n = L.n, gg = L.g, w = L.w;
     f32x16 Ms[4];
     if (PASS1) {
 #pragma unroll
@@ -207,10 +302,22 @@ __device__ __noinline__ void kda_prep_loop(const KdaParams& prm, KdaSmem& sm, in
 #pragma unroll
             for (int r = 0; r < 16; ++r) Ms[ht][r] = (32 * ht + rho(gg, r) == 32 * w + n) ? 1.f : 0.f;
     }
+    // the first chunk's loads; later chunks' are issued one chunk ahead
+    kda_stage_gates(io, sm, pw, lane, b, h, c0);
+    kda_stage_tiles<PASS1>(io, sm, pw, lane, b, h, c0);
+    wait_vm();
+    bar();
     for (int c = c0; c < c1; ++c) {
-        kda_tiles(prm, sm, TL, b, h, c);
+        float gl[16];
+        kda_gates(io.T, sm, c, gl);
+        wait_vm();   // this chunk's raw tiles
+        bar();       // gates scanned: the staging area is free
+        if (c + 1 < c1) kda_stage_gates(io, sm, pw, lane, b, h, c + 1);
+        kda_scale<PASS1>(sm, gl, chunk_len(io.T, c));
+        bar();       // tiles formed
         if (!PASS1 || pw < 3) kda_prep(L, sm, pw);
-        __syncthreads();   // blocks written
+        bar();       // blocks written: kd, kc (full pass) and bnd are free
+        if (c + 1 < c1) kda_stage_tiles<PASS1>(io, sm, pw, lane, b, h, c + 1);
         if (PASS1) {
             // X = Kt M (state rows scaled by each half's exp(centre)), U = T (-X)
             f32x16 X[2] = {zero16(), zero16()};
@@ -239,9 +346,11 @@ __device__ __noinline__ void kda_prep_loop(const KdaParams& prm, KdaSmem& sm, in
             for (int ht = 0; ht < 4; ++ht) Ms[ht] = Ms[ht] * rows_of(sm.eC, ht, gg);
             kt_update<__bf16>(L, sm.ku, Ms, 1.f, vf);
         }
-        __syncthreads();   // the state step is done with the tiles
+        // the next chunk's gates (issued before its tiles) have landed
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(kda_tile_loads<PASS1>()));
+        bar();       // the state step is done with the tiles
     }
-    if (PASS1) store_state(uni(prm.ws) + ((size_t)bh * (prm.P - 1) + p) * kKdaSlot, w, lane, Ms);
+    if (PASS1) store_state(uni(prm.ws) + ((size_t)bh * (uni(prm.P) - 1) + p) * kKdaSlot, w, lane, Ms);
 }
 
 // Waves 0-3: the state (32 columns per wave, in MFMA accumulators) and the
@@ -250,6 +359,8 @@ __device__ __noinline__ void kda_prep_loop(const KdaParams& prm, KdaSmem& sm, in
 // last segment writes ht.  Executes exactly the barriers of kda_prep_loop.
 template <bool PASS1>
 __device__ __noinline__ void kda_state_loop(const KdaParams& prm, KdaSmem& sm, int bh, int p, int c0, int c1) {
+    // arguments arrive in vector registers: make them wave-uniform
+    bh = uni(bh), p = uni(p), c0 = uni(c0), c1 = uni(c1);
     using F = bf16x8;
     const int Tn = uni(prm.T), H = uni(prm.H);
     const int b = bh / H, h = bh % H;
@@ -258,8 +369,6 @@ __device__ __noinline__ void kda_state_loop(const KdaParams& prm, KdaSmem& sm, i
     __bf16* const op = uni((__bf16*)prm.o);
     Lane<__bf16> L;
     L.init(threadIdx.x);
-    TileLoader<__bf16, 8> TL;
-    TL.init(wave_id(), lane, H);
     const int n = L.n, gg = L.g, w = L.w;
     f32x16 Hs[4];
     if (PASS1) {
@@ -273,9 +382,16 @@ __device__ __noinline__ void kda_state_loop(const KdaParams& prm, KdaSmem& sm, i
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) Hs[ht] = zero16();
     }
+    bar();   // the first chunk's loads have landed
     for (int c = c0; c < c1; ++c) {
         const int nv = chunk_len(Tn, c);
-        kda_tiles(prm, sm, TL, b, h, c);
+        {
+            float gl[16];
+            kda_gates(Tn, sm, c, gl);
+            bar();
+            kda_scale<PASS1>(sm, gl, nv);
+            bar();
+        }
         // Kt H and (Qt H)^T: state rows of each k-step scaled by each half's exp(centre)
         f32x16 X[2], OT[2];
 #pragma unroll
@@ -302,7 +418,7 @@ __device__ __noinline__ void kda_state_loop(const KdaParams& prm, KdaSmem& sm, i
                 OT[1] = mma(h1f, L.f128(sm.qc, 1, ks), OT[1]);
             }
         }
-        __syncthreads();   // blocks written
+        bar();   // blocks written
         // Y = V - Kt H, U by block substitution
         f32x16 Y[2];
 #pragma unroll
@@ -324,7 +440,7 @@ __device__ __noinline__ void kda_state_loop(const KdaParams& prm, KdaSmem& sm, i
 #pragma unroll
             for (int ht = 0; ht < 4; ++ht) Hs[ht] = Hs[ht] * rows_of(sm.eC, ht, gg);
             kt_update<__bf16>(L, sm.ku, Hs, 1.f, vf);
-            __syncthreads();   // the tiles are free for the next chunk
+            bar();   // the tiles are free for the next chunk
             continue;
         }
         // O^T = (Qt H)^T + U^T P^T; P^T's B fragments are rows of P
@@ -370,7 +486,7 @@ __device__ __noinline__ void kda_state_loop(const KdaParams& prm, KdaSmem& sm, i
                 }
             }
         }
-        __syncthreads();   // the tiles are free for the next chunk
+        bar();   // the tiles are free for the next chunk
     }
     if (PASS1)
         store_state(uni(prm.ws) + ((size_t)bh * (prm.P - 1) + p) * kKdaSlot + kDk * kDk, w, lane, Hs);
@@ -392,52 +508,59 @@ __global__ __launch_bounds__(kKdaThreads, 1) void gdn_kda_fwd_kernel(KdaParams p
         kda_prep_loop<MODE == KDA_PASS1>(prm, sm, bh, p, c0, c1);
 }
 
-// The states entering segments 1 .. P-1 of batch-head blockIdx.x: S_{p+1} =
-// M_p S_p + b_p from S_0 = h0 (or zero), in float32 on the vector units (one
-// 128 x 128 x 128 product per segment), written over b_p in segment p's slot.
-// Thread t owns rows 4 (t >> 4) .. +3 and columns 8 (t & 15) .. +7 of the
-// result (it reads exactly those entries of b_p first); M^T and S in LDS (64 KB
-// each).
-__global__ __launch_bounds__(512, 1) void kda_chain_kernel(KdaParams prm) {
-    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-    float* const MT = reinterpret_cast<float*>(smem_raw);   // [k][i]
-    float* const Sl = MT + kDk * kDk;                         // [k][j]
-    const int bh = blockIdx.x, t = threadIdx.x;
-    const int i0 = 4 * (t >> 4), j0 = 8 * (t & 15);
+// The states entering segments 1 .. P-1: S_{p+1} = M_p S_p + b_p from S_0 = h0
+// (or zero), in float32 on the vector units, written over b_p in segment p's
+// slot.  Columns of S never mix, so workgroup (batch-head, column block cb) owns
+// 16 of the 128 columns: its S block stays in LDS across the segments, and thread
+// t owns row t >> 1, columns 16 cb + 8 (t & 1) .. +7 of every product.  Each
+// thread holds its row of M_p in registers, fetched one segment ahead.
+constexpr int kChainCols = 16;
+constexpr int kChainThreads = 2 * kDk;
+
+__global__ __launch_bounds__(kChainThreads, 1) void kda_chain_kernel(KdaParams prm) {
+    __shared__ __attribute__((aligned(16))) float Sl[kDk * kChainCols];   // [k][16 columns]
+    constexpr int CB = kDv / kChainCols;
+    const int bh = (int)blockIdx.x / CB, cb = (int)blockIdx.x % CB, t = threadIdx.x;
+    const int i = t >> 1, jl = 8 * (t & 1), j0 = kChainCols * cb + jl;
     const size_t SS = (size_t)kDk * kDv;
     float* const base = prm.ws + (size_t)bh * (prm.P - 1) * kKdaSlot;
-    for (int e = t; e < (int)SS; e += 512) Sl[e] = prm.h0 ? prm.h0[(size_t)bh * SS + e] : 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) Sl[i * kChainCols + jl + c] = prm.h0 ? prm.h0[(size_t)bh * SS + (size_t)i * kDv + j0 + c] : 0.f;
+    f32x4 mnext[kDk / 4];
+#pragma unroll
+    for (int q = 0; q < kDk / 4; ++q) mnext[q] = *reinterpret_cast<const f32x4*>(base + (size_t)i * kDk + 4 * q);
+    __syncthreads();
     for (int p = 0; p + 1 < prm.P; ++p) {
-        const float* const M = base + (size_t)p * kKdaSlot;
         float* const bp = base + (size_t)p * kKdaSlot + (size_t)kDk * kDk;
-        for (int e = t; e < (int)SS; e += 512) MT[(e & (kDk - 1)) * kDk + (e >> 7)] = M[e];   // M[i][k] -> MT[k][i]
-        __syncthreads();
-        float acc[4][8];
+        // b_p first: the loads complete in order, so M_{p+1}'s stay in flight
+        float acc[8];
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int c = 0; c < 8; ++c) acc[c] = bp[(size_t)i * kDv + j0 + c];
+        f32x4 m[kDk / 4];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) acc[a][c] = bp[(size_t)(i0 + a) * kDv + j0 + c];
-        for (int k = 0; k < kDk; ++k) {
-            const f32x4 m = *reinterpret_cast<const f32x4*>(MT + k * kDk + i0);
-            const f32x4 s0 = *reinterpret_cast<const f32x4*>(Sl + k * kDv + j0);
-            const f32x4 s1 = *reinterpret_cast<const f32x4*>(Sl + k * kDv + j0 + 4);
+        for (int q = 0; q < kDk / 4; ++q) m[q] = mnext[q];
+        if (p + 2 < prm.P) {
+            const float* const Mn = base + (size_t)(p + 1) * kKdaSlot;
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    acc[a][c] = __builtin_fmaf(m[a], s0[c], acc[a][c]);
-                    acc[a][4 + c] = __builtin_fmaf(m[a], s1[c], acc[a][4 + c]);
-                }
+            for (int q = 0; q < kDk / 4; ++q) mnext[q] = *reinterpret_cast<const f32x4*>(Mn + (size_t)i * kDk + 4 * q);
         }
-        __syncthreads();   // every product has read S_p and M^T
-        float* const nxt = bp;
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int k = 0; k < kDk; ++k) {
+            const float mk = m[k >> 2][k & 3];
+            const f32x4 s0 = *reinterpret_cast<const f32x4*>(Sl + k * kChainCols + jl);
+            const f32x4 s1 = *reinterpret_cast<const f32x4*>(Sl + k * kChainCols + jl + 4);
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                Sl[(i0 + a) * kDv + j0 + c] = acc[a][c];
-                nxt[(size_t)(i0 + a) * kDv + j0 + c] = acc[a][c];
+            for (int c = 0; c < 4; ++c) {
+                acc[c] = __builtin_fmaf(mk, s0[c], acc[c]);
+                acc[4 + c] = __builtin_fmaf(mk, s1[c], acc[4 + c]);
             }
+        }
+        __syncthreads();   // every product has read S_p
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            Sl[i * kChainCols + jl + c] = acc[c];
+            bp[(size_t)i * kDv + j0 + c] = acc[c];
+        }
         __syncthreads();
     }
 }
@@ -466,15 +589,7 @@ hipError_t launch_kda_fwd(const KdaParams& p, int mode, hipStream_t s) {
 }
 
 hipError_t launch_kda_chain(const KdaParams& p, hipStream_t s) {
-    static bool configured = false;
-    const size_t lds = 2 * (size_t)kDk * kDk * sizeof(float);
-    if (!configured) {
-        const hipError_t e = hipFuncSetAttribute((const void*)kda_chain_kernel,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
-    hipLaunchKernelGGL(kda_chain_kernel, dim3(p.B * p.H), dim3(512), lds, s, p);
+    hipLaunchKernelGGL(kda_chain_kernel, dim3(p.B * p.H * (kDv / kChainCols)), dim3(kChainThreads), 0, s, p);
     return hipGetLastError();
 }
 
