@@ -526,23 +526,28 @@ __global__ __launch_bounds__(kChainThreads, 1) void kda_chain_kernel(KdaParams p
     float* const base = prm.ws + (size_t)bh * (prm.P - 1) * kKdaSlot;
 #pragma unroll
     for (int c = 0; c < 8; ++c) Sl[i * kChainCols + jl + c] = prm.h0 ? prm.h0[(size_t)bh * SS + (size_t)i * kDv + j0 + c] : 0.f;
+    // M_p's row and b_p's entries of this thread are fetched one segment ahead
     f32x4 mnext[kDk / 4];
+    float bnext[8];
 #pragma unroll
     for (int q = 0; q < kDk / 4; ++q) mnext[q] = *reinterpret_cast<const f32x4*>(base + (size_t)i * kDk + 4 * q);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) bnext[c] = base[(size_t)kDk * kDk + (size_t)i * kDv + j0 + c];
     __syncthreads();
     for (int p = 0; p + 1 < prm.P; ++p) {
         float* const bp = base + (size_t)p * kKdaSlot + (size_t)kDk * kDk;
-        // b_p first: the loads complete in order, so M_{p+1}'s stay in flight
         float acc[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = bp[(size_t)i * kDv + j0 + c];
         f32x4 m[kDk / 4];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = bnext[c];
 #pragma unroll
         for (int q = 0; q < kDk / 4; ++q) m[q] = mnext[q];
         if (p + 2 < prm.P) {
             const float* const Mn = base + (size_t)(p + 1) * kKdaSlot;
 #pragma unroll
             for (int q = 0; q < kDk / 4; ++q) mnext[q] = *reinterpret_cast<const f32x4*>(Mn + (size_t)i * kDk + 4 * q);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) bnext[c] = Mn[(size_t)kDk * kDk + (size_t)i * kDv + j0 + c];
         }
 #pragma unroll
         for (int k = 0; k < kDk; ++k) {
