@@ -226,10 +226,11 @@ BwdVarlenLayout bwd_varlen_layout(int S, int T, int H) {
 
 // KDA sequence split: P segments of S chunks per head (the last one shorter).
 // n_segments = 1: unsplit; n_segments >= 2: that many (at most the chunk count);
-// 0: as many as fill the device, cus / (B H), at most 16 and with at least 8
-// chunks each, and unsplit below 3 segments (the transition pass costs about as
-// much as the output pass, so two segments gain nothing).  S = ceil(N / P), then
-// P = ceil(N / S) so that no segment is empty.
+// 0: one segment more than the workgroups per head that fill the device, a =
+// min(16, cus / (B H), N / 8 - 1), when a >= 2, else unsplit (both launches with
+// outputs then hold a workgroups per head: segment 0 runs beside the
+// transitions of segments 1 .. P-2, segments 1 .. P-1 after the chain).
+// S = ceil(N / P), then P = ceil(N / S) so that no segment is empty.
 constexpr int kKdaMaxSegments = 1024;
 void kda_plan(int B, int T, int H, int cus, int n_segments, int* P, int* S) {
     const int N = num_chunks(T);
@@ -240,8 +241,8 @@ void kda_plan(int B, int T, int H, int cus, int n_segments, int* P, int* S) {
         const long bh = (long)B * H;
         long a = cus / bh;
         if (a > 16) a = 16;
-        if (a > N / 8) a = N / 8;
-        p = a >= 3 ? (int)a : 1;
+        if (a > N / 8 - 1) a = N / 8 - 1;
+        p = a >= 2 ? (int)a + 1 : 1;
     }
     if (p < 1) p = 1;
     const int s = (N + p - 1) / p;
@@ -509,13 +510,18 @@ gdn_status gdn_kda_fwd(const void* q, const void* k, const void* v, const float*
     p.P = P; p.S = S; p.ws = (float*)workspace;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;
-    if (P > 1) {
-        e = recorded(GDN_LAUNCH_KDA_PASS1, s, [&] { return gdn::launch_kda_fwd(p, gdn::KDA_PASS1, s); });
-        if (e != hipSuccess) return hip_fail(e, "KDA transition launch");
+    if (P == 1) {
+        e = recorded(GDN_LAUNCH_KDA_FWD, s, [&] { return gdn::launch_kda_fwd(p, gdn::KDA_FULL, s); });
+        if (e != hipSuccess) return hip_fail(e, "KDA forward launch");
+        return GDN_OK;
+    }
+    e = recorded(GDN_LAUNCH_KDA_PASS1, s, [&] { return gdn::launch_kda_fwd(p, gdn::KDA_FIRST, s); });
+    if (e != hipSuccess) return hip_fail(e, "KDA first launch");
+    if (P > 2) {
         e = recorded(GDN_LAUNCH_KDA_CHAIN, s, [&] { return gdn::launch_kda_chain(p, s); });
         if (e != hipSuccess) return hip_fail(e, "KDA chain launch");
     }
-    e = recorded(GDN_LAUNCH_KDA_FWD, s, [&] { return gdn::launch_kda_fwd(p, gdn::KDA_FULL, s); });
+    e = recorded(GDN_LAUNCH_KDA_FWD, s, [&] { return gdn::launch_kda_fwd(p, gdn::KDA_REST, s); });
     if (e != hipSuccess) return hip_fail(e, "KDA forward launch");
     return GDN_OK;
 }

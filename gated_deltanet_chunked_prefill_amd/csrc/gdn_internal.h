@@ -184,23 +184,26 @@ struct KdaParams {
     int B, T, H, N;
     float scale;
     // sequence split: P segments of S chunks (the last one shorter); P = 1 runs
-    // unsplit.  ws: per batch-head bh and segment p < P - 1, at slot bh (P - 1) + p,
-    // kKdaSlot floats: the segment's transition M (its linear state map, [dk][dk])
-    // and its state b from a zero start ([dk][dv]), which the chain overwrites with
-    // the state entering segment p + 1 (float32, row-major).
+    // unsplit.  ws: per batch-head bh, P - 1 slots (slot bh (P - 1) + p) of
+    // kKdaSlot floats: for p >= 1 segment p's transition M (its linear state map,
+    // [dk][dk]) and its state b from a zero start ([dk][dv]); the chain overwrites
+    // each b field with the state entering segment p + 1; slot 0's b field
+    // receives the final state of segment 0, which runs from h0 (float32,
+    // row-major).
     int P, S;
     float* ws;
 };
 constexpr size_t kKdaSlot = 2 * 128 * 128;
-enum { KDA_FULL = 0, KDA_PASS1 = 1 };
+// KDA_FULL: one segment per head (P = 1).  KDA_FIRST: segment 0 with outputs
+// beside the transitions of segments 1 .. P-2 (P - 1 workgroups per head).
+// KDA_REST: segments 1 .. P-1 with outputs from the states the chain left.
+enum { KDA_FULL = 0, KDA_FIRST = 1, KDA_REST = 2 };
 // Streaming probe of the forward's memory pattern (gdn_probe.hip).
 hipError_t launch_stream_probe(const void* k, const void* q, const void* v, void* o, int T, int H, int segments,
                                hipStream_t s);
-// mode KDA_PASS1: the transitions of segments 0 .. P-2; KDA_FULL: every segment
-// with outputs (from h0 for segment 0, else from the state the chain left).
 hipError_t launch_kda_fwd(const KdaParams& p, int mode, hipStream_t s);
-// the states entering segments 1 .. P-1 from the transitions (one workgroup per
-// batch-head, segments in order)
+// the states entering segments 2 .. P-1 from segment 0's final state and the
+// transitions (segments in order; 16 state columns per workgroup)
 hipError_t launch_kda_chain(const KdaParams& p, hipStream_t s);
 size_t kda_smem_bytes();
 

@@ -488,9 +488,10 @@ __device__ __noinline__ void kda_state_loop(const KdaParams& prm, KdaSmem& sm, i
         }
         bar();   // the tiles are free for the next chunk
     }
-    if (PASS1)
-        store_state(uni(prm.ws) + ((size_t)bh * (prm.P - 1) + p) * kKdaSlot + kDk * kDk, w, lane, Hs);
-    else if (prm.ht && p == prm.P - 1)
+    const int P = uni(prm.P);
+    if (PASS1 || (p == 0 && P > 1))   // b of segment p, or the state entering segment 1
+        store_state(uni(prm.ws) + ((size_t)bh * (P - 1) + p) * kKdaSlot + kDk * kDk, w, lane, Hs);
+    else if (prm.ht && p == P - 1)
         store_state(uni(prm.ht) + (size_t)bh * kDk * kDv, w, lane, Hs);
 }
 
@@ -498,22 +499,33 @@ template <int MODE>
 __global__ __launch_bounds__(kKdaThreads, 1) void gdn_kda_fwd_kernel(KdaParams prm) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     KdaSmem& sm = *reinterpret_cast<KdaSmem*>(smem_raw);
-    const int segs = MODE == KDA_PASS1 ? prm.P - 1 : prm.P;
-    const int bh = (int)blockIdx.x / segs, p = (int)blockIdx.x % segs;
-    const int c0 = p * prm.S, c1 = min(c0 + prm.S, prm.N);
-    // the role branch is wave-uniform: both roles hold barriers
-    if (wave_id() < 4)
-        kda_state_loop<MODE == KDA_PASS1>(prm, sm, bh, p, c0, c1);
-    else
-        kda_prep_loop<MODE == KDA_PASS1>(prm, sm, bh, p, c0, c1);
+    const int groups = MODE == KDA_FULL ? 1 : prm.P - 1;
+    const int bh = (int)blockIdx.x / groups, j = (int)blockIdx.x % groups;
+    const int p = MODE == KDA_REST ? j + 1 : j;
+    const int c0 = p * prm.S, c1 = MODE == KDA_FULL ? prm.N : min(c0 + prm.S, prm.N);
+    // the role branch is wave-uniform (both roles hold barriers); in KDA_FIRST
+    // workgroup j = 0 runs segment 0 with outputs, the others pass 1
+    const bool pass1 = MODE == KDA_FIRST && j > 0;
+    if (wave_id() < 4) {
+        if (pass1)
+            kda_state_loop<true>(prm, sm, bh, p, c0, c1);
+        else
+            kda_state_loop<false>(prm, sm, bh, p, c0, c1);
+    } else {
+        if (pass1)
+            kda_prep_loop<true>(prm, sm, bh, p, c0, c1);
+        else
+            kda_prep_loop<false>(prm, sm, bh, p, c0, c1);
+    }
 }
 
-// The states entering segments 1 .. P-1: S_{p+1} = M_p S_p + b_p from S_0 = h0
-// (or zero), in float32 on the vector units, written over b_p in segment p's
-// slot.  Columns of S never mix, so workgroup (batch-head, column block cb) owns
-// 16 of the 128 columns: its S block stays in LDS across the segments, and thread
-// t owns row t >> 1, columns 16 cb + 8 (t & 1) .. +7 of every product.  Each
-// thread holds its row of M_p in registers, fetched one segment ahead.
+// The states entering segments 2 .. P-1: S_{p+1} = M_p S_p + b_p for p = 1 ..
+// P-2, from S_1 (the final state of segment 0, which ran from h0), in float32 on
+// the vector units; S_{p+1} is written over b_p in segment p's slot.  Columns of
+// S never mix, so workgroup (batch-head, column block cb) owns 16 of the 128
+// columns: its S block stays in LDS across the segments, and thread t owns row
+// t >> 1, columns 16 cb + 8 (t & 1) .. +7 of every product.  Each thread holds
+// its row of M_p in registers, fetched one segment ahead with its entries of b_p.
 constexpr int kChainCols = 16;
 constexpr int kChainThreads = 2 * kDk;
 
@@ -524,18 +536,19 @@ __global__ __launch_bounds__(kChainThreads, 1) void kda_chain_kernel(KdaParams p
     const int i = t >> 1, jl = 8 * (t & 1), j0 = kChainCols * cb + jl;
     const size_t SS = (size_t)kDk * kDv;
     float* const base = prm.ws + (size_t)bh * (prm.P - 1) * kKdaSlot;
+    const size_t MM = (size_t)kDk * kDk;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) Sl[i * kChainCols + jl + c] = prm.h0 ? prm.h0[(size_t)bh * SS + (size_t)i * kDv + j0 + c] : 0.f;
-    // M_p's row and b_p's entries of this thread are fetched one segment ahead
+    for (int c = 0; c < 8; ++c) Sl[i * kChainCols + jl + c] = base[MM + (size_t)i * kDv + j0 + c];   // S_1
     f32x4 mnext[kDk / 4];
     float bnext[8];
+    const float* const M1 = base + kKdaSlot;
 #pragma unroll
-    for (int q = 0; q < kDk / 4; ++q) mnext[q] = *reinterpret_cast<const f32x4*>(base + (size_t)i * kDk + 4 * q);
+    for (int q = 0; q < kDk / 4; ++q) mnext[q] = *reinterpret_cast<const f32x4*>(M1 + (size_t)i * kDk + 4 * q);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) bnext[c] = base[(size_t)kDk * kDk + (size_t)i * kDv + j0 + c];
+    for (int c = 0; c < 8; ++c) bnext[c] = M1[MM + (size_t)i * kDv + j0 + c];
     __syncthreads();
-    for (int p = 0; p + 1 < prm.P; ++p) {
-        float* const bp = base + (size_t)p * kKdaSlot + (size_t)kDk * kDk;
+    for (int p = 1; p + 1 < prm.P; ++p) {
+        float* const bp = base + (size_t)p * kKdaSlot + MM;
         float acc[8];
         f32x4 m[kDk / 4];
 #pragma unroll
@@ -547,7 +560,7 @@ __global__ __launch_bounds__(kChainThreads, 1) void kda_chain_kernel(KdaParams p
 #pragma unroll
             for (int q = 0; q < kDk / 4; ++q) mnext[q] = *reinterpret_cast<const f32x4*>(Mn + (size_t)i * kDk + 4 * q);
 #pragma unroll
-            for (int c = 0; c < 8; ++c) bnext[c] = Mn[(size_t)kDk * kDk + (size_t)i * kDv + j0 + c];
+            for (int c = 0; c < 8; ++c) bnext[c] = Mn[MM + (size_t)i * kDv + j0 + c];
         }
 #pragma unroll
         for (int k = 0; k < kDk; ++k) {
@@ -581,15 +594,21 @@ hipError_t launch_kda_fwd(const KdaParams& p, int mode, hipStream_t s) {
         hipError_t e = hipFuncSetAttribute((const void*)gdn_kda_fwd_kernel<KDA_FULL>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e == hipSuccess)
-            e = hipFuncSetAttribute((const void*)gdn_kda_fwd_kernel<KDA_PASS1>,
+            e = hipFuncSetAttribute((const void*)gdn_kda_fwd_kernel<KDA_FIRST>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute((const void*)gdn_kda_fwd_kernel<KDA_REST>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         configured = true;
     }
-    if (mode == KDA_PASS1)
-        hipLaunchKernelGGL(gdn_kda_fwd_kernel<KDA_PASS1>, dim3(p.B * p.H * (p.P - 1)), dim3(kKdaThreads), lds, s, p);
+    const unsigned bh = (unsigned)(p.B * p.H);
+    if (mode == KDA_FIRST)
+        hipLaunchKernelGGL(gdn_kda_fwd_kernel<KDA_FIRST>, dim3(bh * (p.P - 1)), dim3(kKdaThreads), lds, s, p);
+    else if (mode == KDA_REST)
+        hipLaunchKernelGGL(gdn_kda_fwd_kernel<KDA_REST>, dim3(bh * (p.P - 1)), dim3(kKdaThreads), lds, s, p);
     else
-        hipLaunchKernelGGL(gdn_kda_fwd_kernel<KDA_FULL>, dim3(p.B * p.H * p.P), dim3(kKdaThreads), lds, s, p);
+        hipLaunchKernelGGL(gdn_kda_fwd_kernel<KDA_FULL>, dim3(bh), dim3(kKdaThreads), lds, s, p);
     return hipGetLastError();
 }
 

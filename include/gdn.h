@@ -222,11 +222,13 @@ gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
  * couples the halves), so results are finite as long as no key channel decays
  * by more than exp(-176) over 16 consecutive tokens of a 64-token chunk.
  * With P > 1 segments the split is exact (no window shortcut): the chunk map is
- * affine in the state, S_out = M S_in + b, so a first launch runs segments
- * 0 .. P-2 from the identity and from zero to get each segment's M (dk x dk) and
- * b (float32, in the workspace), a second composes them in order into the state
- * entering every segment, and the third runs all segments with outputs from
- * those states.  Results differ from the unsplit call by rounding only.
+ * affine in the state, S_out = M S_in + b.  A first launch runs segment 0 with
+ * outputs from h0 (its final state goes to the workspace) beside segments
+ * 1 .. P-2 from the identity and from zero, which give each segment's M (dk x
+ * dk) and b (float32, in the workspace); a second composes them in order into
+ * the state entering every segment; the third runs segments 1 .. P-1 with
+ * outputs from those states.  Results differ from the unsplit call by rounding
+ * only.
  * Errors as for gdn_chunk_fwd; GDN_ERR_WORKSPACE when the workspace is missing
  * or too small. */
 gdn_status gdn_kda_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
@@ -234,11 +236,12 @@ gdn_status gdn_kda_fwd(const void* q, const void* k, const void* v, const float*
                        float scale, int n_segments, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Segments per head gdn_kda_fwd uses for these shapes on a device with num_cus
- * compute units (host only): 1 for n_segments = 1; min(n_segments, N) reduced to
- * ceil(N / ceil(N / n_segments)) for n_segments >= 2; for n_segments = 0,
- * a = min(16, floor(num_cus / (B H)), floor(N / 8)) reduced the same way when
- * a >= 3, else 1.  Returns 0 for invalid arguments (num_cus is read only when
- * n_segments = 0). */
+ * compute units (host only), N = ceil(T/64): 1 for n_segments = 1;
+ * min(n_segments, N) reduced to ceil(N / ceil(N / n_segments)) for
+ * n_segments >= 2; for n_segments = 0, a + 1 reduced the same way, with
+ * a = min(16, floor(num_cus / (B H)), floor(N / 8) - 1), when a >= 2, else 1 (a
+ * workgroups per head then run in each launch with outputs).  Returns 0 for
+ * invalid arguments (num_cus is read only when n_segments = 0). */
 int gdn_kda_plan_segments(int B, int T, int H, int num_cus, int n_segments);
 
 /* Workspace bytes gdn_kda_fwd needs on the current device: B H (P - 1) x 2 x
@@ -344,7 +347,7 @@ typedef enum {
     GDN_LAUNCH_FWD_SUMS = 8,    /* split forward: chunk sums of g, planner reset      */
     GDN_LAUNCH_KDA_FWD = 9,     /* KDA forward (with outputs)                         */
     GDN_LAUNCH_STREAM_PROBE = 10, /* measurement aid: the forward's memory pattern    */
-    GDN_LAUNCH_KDA_PASS1 = 11,  /* KDA split: segment transitions and zero-start states */
+    GDN_LAUNCH_KDA_PASS1 = 11,  /* KDA split: segment 0, and the other segments' transitions */
     GDN_LAUNCH_KDA_CHAIN = 12   /* KDA split: states entering the segments            */
 } gdn_launch_kind;
 

@@ -298,13 +298,14 @@ def test_kda_plan_and_workspace():
     n_segments >= 1; the automatic count reads num_cus)."""
     lib = _lib.load()
     plan = lib.gdn_kda_plan_segments
-    assert plan(1, 32768, 32, 256, 0) == 8           # 256 CUs / 32 heads, 512 chunks
-    assert plan(1, 32768, 8, 256, 0) == 16           # capped at 16
-    assert plan(1, 32768, 128, 256, 0) == 1          # two per head would not pay
-    assert plan(1, 32768, 64, 256, 0) == 4
-    assert plan(1, 32768, 80, 256, 0) == 3
-    assert plan(1, 1024, 4, 256, 0) == 1             # 16 chunks: at most 2 of 8 chunks
-    assert plan(1, 3072, 4, 256, 0) == 6             # 48 chunks: 6 segments of 8
+    assert plan(1, 32768, 32, 256, 0) == 9           # 8 workgroups per head on 256 CUs, one segment more
+    assert plan(1, 32768, 8, 256, 0) == 17           # capped at 16 + 1
+    assert plan(1, 32768, 128, 256, 0) == 3          # two workgroups per head
+    assert plan(1, 32768, 256, 256, 0) == 1          # one workgroup per head: unsplit
+    assert plan(1, 32768, 64, 256, 0) == 5
+    assert plan(1, 32768, 80, 256, 0) == 4
+    assert plan(1, 1024, 4, 256, 0) == 1             # 16 chunks: a = 16/8 - 1 = 1
+    assert plan(1, 3072, 4, 256, 0) == 6             # 48 chunks: a = 5, 6 segments of 8
     assert plan(1, 128, 1, 256, 1) == 1
     assert plan(1, 128, 1, 256, 5) == 2              # at most one segment per chunk
     assert plan(1, 64 * 10, 1, 0, 4) == 4            # 3, 3, 3, 1 chunks

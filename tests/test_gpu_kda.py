@@ -94,8 +94,9 @@ def test_kda_equal_channels_match_gdn_forward(gdn):
 # b, the chain composes them, every segment then runs from its entering state.
 @pytest.mark.parametrize("nseg", [2, 3, 4, 10])
 def test_kda_split(gdn, nseg):
-    """T = 9 chunks + 13 tokens (10 chunks, the last ragged): 2, 3, 4 and 10
-    segments (one chunk each) with h0, against the oracle and the unsplit call."""
+    """T = 9 chunks + 13 tokens (10 chunks, the last ragged): 2 (no chain), 3,
+    4 and 10 segments (one chunk each) with h0, against the oracle and the
+    unsplit call."""
     say(f"case KDA split n_segments={nseg}")
     x = inputs.generate_kda(B=2, T=64 * 9 + 13, H=2, h0_std=0.05, seed=220 + nseg)
     o, ht, oref, href = _run(gdn, x, scale=0.8, n_segments=nseg)
@@ -143,8 +144,8 @@ def test_kda_split_workspace_reuse(gdn):
 
 @pytest.mark.slow
 def test_kda_throughput_shape_split_sampled(gdn):
-    """The throughput shape (T = 32768, H = 32) with the automatic split (8
-    segments of 64 chunks on 256 CUs): heads 0 and 31 against the oracle over the
+    """The throughput shape (T = 32768, H = 32) with the automatic split (9
+    segments of 57 chunks on 256 CUs): heads 0 and 31 against the oracle over the
     whole sequence, every head against the unsplit call."""
     import torch
     say("case bf16_kda_t32768_h32 automatic split, heads 0 and 31 vs the oracle")
