@@ -27,8 +27,10 @@
 // tokens|)), and the off-diagonal block (rows in the second half, columns in the
 // first) at the decay of token 31, the boundary, where both factors are at most
 // 1.  The exact products Kt H and Qt H use the re-centred tiles against state
-// rows scaled by exp(centre) (at most 1).  Results are finite whenever no key
-// channel decays by more than exp(-176) over 16 consecutive tokens of a chunk.
+// rows scaled by exp(centre) (at most 1).  The largest factor is exp(decay over
+// the 16 tokens between a half's centre and its end), so results are finite
+// whenever no key channel decays by more than exp(-88) (the float32 exponent
+// range) over 16 consecutive tokens of a chunk.
 //
 // One workgroup (eight waves) per (batch, head) runs the chunks in order; per
 // chunk: all waves load the K, Q, V tiles and form the re-centred tiles in LDS;

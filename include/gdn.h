@@ -220,7 +220,8 @@ gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
  * The chunk step applies the per-channel decay factors to the K and Q tiles
  * (re-centred per 32-token half, and at the half boundary for the block that
  * couples the halves), so results are finite as long as no key channel decays
- * by more than exp(-176) over 16 consecutive tokens of a 64-token chunk.
+ * by more than exp(-88) (the float32 exponent range) over 16 consecutive tokens
+ * of a 64-token chunk.
  * With P > 1 segments the split is exact (no window shortcut): the chunk map is
  * affine in the state, S_out = M S_in + b.  A first launch runs segment 0 with
  * outputs from h0 (its final state goes to the workspace) beside segments

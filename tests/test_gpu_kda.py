@@ -73,6 +73,33 @@ def test_kda_strong_channel_decay(gdn):
     _check(*_run(gdn, x), "strong decay")
 
 
+@pytest.mark.parametrize("nseg", [1, 2])
+def test_kda_decay_at_range_limit(gdn, nseg):
+    """Every channel decaying by 5.3 to 5.4 per token (up to 86 over 16 tokens,
+    just inside the float32 range that the re-centred factors need): finite and
+    equal to the oracle, unsplit and split."""
+    say(f"case KDA decay at the range limit, n_segments={nseg}")
+    x = inputs.generate_kda(B=1, T=64 * 3 + 5, H=2, gate="uniform", gate_lo=-5.4, gate_hi=-5.3, h0_std=0.05,
+                            seed=215)
+    _check(*_run(gdn, x, n_segments=nseg), f"decay 5.4 per token, n_segments={nseg}")
+
+
+def test_kda_no_final_state_split(gdn):
+    """Split into 3 segments without a final state (ht not written)."""
+    import torch
+    say("case KDA split 3 without ht")
+    x = inputs.generate_kda(B=1, T=64 * 7 + 3, H=2, h0_std=0.05, seed=216)
+    t = to_gpu(x)
+    g = torch.from_numpy(np.ascontiguousarray(x.g)).cuda()
+    o, ht = gdn.gdn_kda_fwd(t["q"], t["k"], t["v"], g, t["beta"], t["h0"], output_final_state=False, n_segments=3)
+    torch.cuda.synchronize()
+    assert ht is None
+    oref, _ = oracle.kda_fwd(x.q, x.k, x.v, x.g, x.beta, x.h0)
+    eo = rel_err(to_np(o), oref)
+    say(f"  o err {eo:.3e}")
+    assert eo <= TOL_BF16, eo
+
+
 def test_kda_equal_channels_match_gdn_forward(gdn):
     """Every key channel with the same gate: the KDA kernel computes the gated
     delta rule, so it agrees with the oracle's scalar-gate recurrence and with
