@@ -59,7 +59,6 @@ struct KdaSmem {
     float ec0[kDk];            // exp(c_0) per key channel (c_0 = G at token 15)
     float ec1[kDk];            // exp(c_1) (c_1 = G at token 47)
     float eC[kDk];             // exp(G_C)
-    float psum[4][kDk];        // per key channel: sums of g over tokens 16p .. 16p + 15
     float beta[kChunk];
     float gst[kChunk * kDk];   // the next chunk's gates [token][channel], staged by direct loads
     float bst[kChunk];         // the next chunk's beta, staged likewise
@@ -207,24 +206,37 @@ __device__ __forceinline__ void kda_stage_tiles(const KdaIO& io, KdaSmem& sm, in
 template <bool PASS1>
 constexpr int kda_tile_loads() { return (PASS1 ? 2 : 3) * kChunk * kDk * 2 / (4 * 1024); }
 
-// Step 1 of chunk c, by every wave, from the staged gates: thread (channel ch,
-// quarter part) owns tokens 16 part .. 16 part + 15 of key channel ch and forms
-// their in-chunk cumulative sums; the quarter sums go to LDS, beta to its slot.
-// A barrier follows.
-__device__ __forceinline__ void kda_gates(int Tn, KdaSmem& sm, int c, float (&gl)[16]) {
+// Steps 1 and 2 run with thread (pair pr = tid % 64, group grp = tid / 64)
+// owning key channels 2 pr, 2 pr + 1 and tokens 8 grp .. 8 grp + 7 (a wave
+// covers one group: whole 256-byte rows, two channels per 4-byte LDS access).
+// Cumulative gates are kept in base-2 units (times log2 e), so each factor is
+// one exp2 of a difference.
+typedef float kf2 __attribute__((ext_vector_type(2)));
+typedef __bf16 kb2 __attribute__((ext_vector_type(2)));
+constexpr float kLog2e = 1.4426950408889634f;
+// the eight group sums per channel pass from step 1 to step 2 through the
+// inverse and score blocks' space, dead from the end of one chunk step until
+// the next chunk's blocks are written
+__device__ __forceinline__ float* kda_group_sums(KdaSmem& sm) { return reinterpret_cast<float*>(&sm.t32[0][0]); }
+static_assert(sizeof(KdaSmem::t32) >= 8 * kDk * sizeof(float), "group sums need 4 KB");
+
+// Step 1 of chunk c, by every wave, from the staged gates: the in-chunk
+// cumulative sums of this thread's 8 tokens for its two channels (base 2); the
+// group sums go to LDS, beta to its slot.  A barrier follows.
+__device__ __forceinline__ void kda_gates(int Tn, KdaSmem& sm, int c, kf2 (&gl)[8]) {
     const int nv = chunk_len(Tn, c);
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));   // per-chunk addressing, not hoisted out of the chunk loop
-    const int ch = tid & (kDk - 1), part = tid >> 7;
-    float run = 0.f;
+    const int pr = tid & 63, grp = tid >> 6;
+    kf2 run = {0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int t = 16 * part + j;
-        const float x = sm.gst[t * kDk + ch];
-        run += t < nv ? x : 0.f;
+    for (int j = 0; j < 8; ++j) {
+        const int t = 8 * grp + j;
+        const kf2 x = *reinterpret_cast<const kf2*>(sm.gst + t * kDk + 2 * pr);
+        run += t < nv ? x * kLog2e : kf2{0.f, 0.f};
         gl[j] = run;
     }
-    sm.psum[part][ch] = run;
+    *reinterpret_cast<kf2*>(kda_group_sums(sm) + grp * kDk + 2 * pr) = run;
     if (tid < kChunk) {
         const float x = sm.bst[tid];
         sm.beta[tid] = tid < nv ? x : 0.f;
@@ -236,44 +248,56 @@ __device__ __forceinline__ void kda_gates(int Tn, KdaSmem& sm, int c, float (&gl
 // and bnd, so the in-place reuse is race-free); rows past the sequence's end
 // are zeroed here, whatever the buffer loads left in them.  A barrier follows.
 template <bool PASS1>
-__device__ __forceinline__ void kda_scale(KdaSmem& sm, const float (&gl)[16], int nv) {
+__device__ __forceinline__ void kda_scale(KdaSmem& sm, const kf2 (&gl)[8], int nv) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));   // per-chunk addressing, not hoisted out of the chunk loop
-    const int ch = tid & (kDk - 1), part = tid >> 7;
-    float Gend[4];
-    Gend[0] = sm.psum[0][ch];
+    const int pr = tid & 63, grp = tid >> 6;
+    const float* const gs = kda_group_sums(sm);
+    kf2 cum[8];   // cumulative group sums: G at tokens 7, 15, .., 63 (base 2)
+    cum[0] = *reinterpret_cast<const kf2*>(gs + 2 * pr);
 #pragma unroll
-    for (int p = 1; p < 4; ++p) Gend[p] = Gend[p - 1] + sm.psum[p][ch];
-    const float off = part == 0 ? 0.f : Gend[part - 1];
-    const float c0 = Gend[0], gb = Gend[1], c1 = Gend[2], gC = Gend[3];
-    const float centre = part < 2 ? c0 : c1;
+    for (int i = 1; i < 8; ++i) cum[i] = cum[i - 1] + *reinterpret_cast<const kf2*>(gs + i * kDk + 2 * pr);
+    kf2 off = {0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int t = 16 * part + j;
-        const float G = off + gl[j];
-        const int e = toff<__bf16, kDk>(t, ch);
+    for (int i = 0; i < 7; ++i)
+        if (i < grp) off = cum[i];
+    const kf2 c0 = cum[1], gb = cum[3], c1 = cum[5], gC = cum[7];
+    const kf2 centre = grp < 4 ? c0 : c1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int t = 8 * grp + j;
+        const int e = toff<__bf16, kDk>(t, 2 * pr);   // channels 2 pr, 2 pr + 1: adjacent
         const bool in = t < nv;
-        const float kv = in ? (float)sm.kd[e] : 0.f;
-        const float qv = PASS1 || !in ? 0.f : (float)sm.kc[e];
-        const __bf16 vv = sm.bnd[e];
-        sm.vt[e] = in ? vv : (__bf16)0.f;
-        const float ec = __expf(G - centre), ed = __expf(centre - G);
-        sm.kc[e] = (__bf16)(kv * ec);
-        sm.kd[e] = (__bf16)(kv * ed);
-        if (!PASS1) sm.qc[e] = (__bf16)(qv * ec);
-        sm.ku[e] = (__bf16)(kv * __expf(gC - G));
-        if (part < 2) {
-            sm.bnd[e] = (__bf16)(kv * __expf(gb - G));
-        } else {
-            const float eb = __expf(G - gb);
-            sm.bnd[e] = (__bf16)(kv * eb);
-            if (!PASS1) sm.bq[toff<__bf16, kDk>(t - 32, ch)] = (__bf16)(qv * eb);
+        const kb2 kr = *reinterpret_cast<const kb2*>(sm.kd + e);
+        const kb2 qr = *reinterpret_cast<const kb2*>(sm.kc + e);
+        const kb2 vr = *reinterpret_cast<const kb2*>(sm.bnd + e);
+        *reinterpret_cast<kb2*>(sm.vt + e) = in ? vr : kb2{(__bf16)0.f, (__bf16)0.f};
+        kb2 okc, okd, oqc, oku, obn, obq;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float G = off[i] + gl[j][i];
+            const float kv = in ? (float)kr[i] : 0.f;
+            const float qv = PASS1 || !in ? 0.f : (float)qr[i];
+            const float ec = __builtin_amdgcn_exp2f(G - centre[i]), ed = __builtin_amdgcn_exp2f(centre[i] - G);
+            okc[i] = (__bf16)(kv * ec);
+            okd[i] = (__bf16)(kv * ed);
+            oqc[i] = (__bf16)(qv * ec);
+            oku[i] = (__bf16)(kv * __builtin_amdgcn_exp2f(gC[i] - G));
+            const float eb = __builtin_amdgcn_exp2f(grp < 4 ? gb[i] - G : G - gb[i]);
+            obn[i] = (__bf16)(kv * eb);
+            obq[i] = (__bf16)(qv * eb);
         }
+        *reinterpret_cast<kb2*>(sm.kc + e) = okc;
+        *reinterpret_cast<kb2*>(sm.kd + e) = okd;
+        if (!PASS1) *reinterpret_cast<kb2*>(sm.qc + e) = oqc;
+        *reinterpret_cast<kb2*>(sm.ku + e) = oku;
+        *reinterpret_cast<kb2*>(sm.bnd + e) = obn;
+        if (!PASS1 && grp >= 4) *reinterpret_cast<kb2*>(sm.bq + toff<__bf16, kDk>(t - 32, 2 * pr)) = obq;
     }
-    if (part == 0) {
-        sm.ec0[ch] = __expf(c0);
-        sm.ec1[ch] = __expf(c1);
-        sm.eC[ch] = __expf(gC);
+    if (grp == 0) {
+        *reinterpret_cast<kf2*>(sm.ec0 + 2 * pr) = kf2{__builtin_amdgcn_exp2f(c0[0]), __builtin_amdgcn_exp2f(c0[1])};
+        *reinterpret_cast<kf2*>(sm.ec1 + 2 * pr) = kf2{__builtin_amdgcn_exp2f(c1[0]), __builtin_amdgcn_exp2f(c1[1])};
+        *reinterpret_cast<kf2*>(sm.eC + 2 * pr) = kf2{__builtin_amdgcn_exp2f(gC[0]), __builtin_amdgcn_exp2f(gC[1])};
     }
 }
 
@@ -310,7 +334,7 @@ __device__ __noinline__ void kda_prep_loop(const KdaParams& prm, KdaSmem& sm, in
     wait_vm();
     bar();
     for (int c = c0; c < c1; ++c) {
-        float gl[16];
+        kf2 gl[8];
         kda_gates(io.T, sm, c, gl);
         wait_vm();   // this chunk's raw tiles
         bar();       // gates scanned: the staging area is free
@@ -388,7 +412,7 @@ __device__ __noinline__ void kda_state_loop(const KdaParams& prm, KdaSmem& sm, i
     for (int c = c0; c < c1; ++c) {
         const int nv = chunk_len(Tn, c);
         {
-            float gl[16];
+            kf2 gl[8];
             kda_gates(Tn, sm, c, gl);
             bar();
             kda_scale<PASS1>(sm, gl, nv);
