@@ -490,6 +490,11 @@ gdn_status gdn_kda_fwd(const void* q, const void* k, const void* v, const float*
     gdn_status st = check_fwd_args(q, k, v, g, beta, h0, o, ht, B, T, H, dk, dv, dtype, scale);
     if (st != GDN_OK) return st;
     if (dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "the KDA forward supports bf16 I/O only");
+    // the per-channel gates (128 float32 per token-head) are addressed like a
+    // float32 tile: 64 rows of H * 512 bytes within 32-bit offsets
+    if ((long long)kChunkRows * H * 128 * 4 > (long long)INT32_MAX)
+        return fail(GDN_ERR_INVALID_ARG, "H = %d too large for the KDA gates (at most %lld heads)", H,
+                    (long long)INT32_MAX / (kChunkRows * 128 * 4));
     if (n_segments < 0 || n_segments > kKdaMaxSegments)
         return fail(GDN_ERR_INVALID_ARG, "n_segments must be in [0, %d] (got %d)", kKdaMaxSegments, n_segments);
     int cus = 0;

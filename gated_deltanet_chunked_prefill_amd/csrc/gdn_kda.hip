@@ -157,6 +157,7 @@ struct KdaIO {
 
 constexpr int kKdaGateLoads = kChunk * kDk * 4 / (4 * 1024);   // 1 KB per wave instruction: 8 per wave
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t kda_rows(const void* first_row, int rows, int row_bytes) {
+    // at most 64 rows of at most 2^31 / 64 bytes (the entry point bounds H)
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(first_row), (short)0, rows * row_bytes, 0x00020000);
 }
 __device__ __forceinline__ void kda_stage_gates(const KdaIO& io, KdaSmem& sm, int pw, int lane, int b, int h, int c) {

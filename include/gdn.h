@@ -207,7 +207,9 @@ gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
  * with one log-decay per key channel, g_t in R^dk, applied to the state before
  * the delta correction; with equal channels it is gdn_chunk_fwd's operator.
  *   q, k, v, o        as for gdn_chunk_fwd, bfloat16 only (GDN_ERR_UNSUPPORTED otherwise)
- *   g                 [B, T, H, dk] float32, log-decays (<= 0) per key channel
+ *   g                 [B, T, H, dk] float32, log-decays (<= 0) per key channel;
+ *                     H at most 65535 (GDN_ERR_INVALID_ARG beyond: 64 rows of
+ *                     gates are addressed with 32-bit byte offsets)
  *   beta, h0, ht      as for gdn_chunk_fwd (h0, ht nullable)
  *   n_segments        sequence split (talk summary, paragraph 4): 1 = one
  *                     workgroup per (batch, head) over all chunks in order;

@@ -284,6 +284,8 @@ def test_kda_validation_before_launch():
     assert call(dk=64) == _lib.GDN_ERR_UNSUPPORTED
     assert call(T=0) == _lib.GDN_ERR_INVALID_ARG
     assert call(g=A + 2) == _lib.GDN_ERR_INVALID_ARG
+    assert call(H=65536) == _lib.GDN_ERR_INVALID_ARG   # 64 rows of 65536 * 512 bytes of gates: past 2^31
+    assert "KDA gates" in _lib.last_error()
     assert call(nseg=-1) == _lib.GDN_ERR_INVALID_ARG
     assert call(nseg=1025) == _lib.GDN_ERR_INVALID_ARG
     # two segments of one chunk each need (P - 1) slots of 2 x 128 x 128 floats
