@@ -16,7 +16,9 @@ A secondary "backward" object times whole gdn_chunk_bwd calls on the training
 shape (B=4, T=8192, H=32, bf16) with per-launch event times, and a "varlen"
 object whole gdn_chunk_fwd_varlen calls on a packed batch of 8 prompts of
 mixed lengths (32768 tokens, H=32), and a "kda" object whole gdn_kda_fwd calls
-(per-key-channel decay) at B=1, T=32768, H=32.
+(per-key-channel decay) at B=1, T=32768, H=32.  These run before the headline
+forward loop, which is timed on a GPU under sustained load; during that loop
+only the forward kernel's launches carry HIP events.
 """
 from __future__ import annotations
 
@@ -429,10 +431,23 @@ def main():
     import gated_deltanet_chunked_prefill_amd as gdn
     from gated_deltanet_chunked_prefill_amd import _lib, inputs
 
-    x = inputs.workload(WORKLOAD)
-    B, T, H, dk, dv = x.shape
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    # The secondary workloads run first and the headline forward loop last, on a
+    # GPU under sustained load: in the first ~10 ms of full load after an idle
+    # period the power controller overshoots (forward calls ~0.37-0.41 ms instead
+    # of the ~0.32 ms it settles at), and the headline is the sustained rate.
+    extra = {}
+    if args.bwd_steps > 0:
+        extra["backward"] = bench_backward(torch, gdn, _lib, inputs, args.bwd_steps, 2)
+    if args.varlen_steps > 0:
+        extra["varlen"] = bench_varlen(torch, gdn, inputs, args.varlen_steps, 2)
+    if args.kda_steps > 0:
+        extra["kda"] = bench_kda(torch, gdn, inputs, args.kda_steps, 1)
+    torch.cuda.empty_cache()
+
+    x = inputs.workload(WORKLOAD)
+    B, T, H, dk, dv = x.shape
     q = torch.from_numpy(x.q).to(dev).to(torch.bfloat16)
     k = torch.from_numpy(x.k).to(dev).to(torch.bfloat16)
     v = torch.from_numpy(x.v).to(dev).to(torch.bfloat16)
@@ -453,30 +468,48 @@ def main():
         raise SystemExit("bench.py: the split forward reported a failed wait; outputs are invalid")
 
     lib = _lib.load()
-    cap = 8 * args.steps
-    ev = HipEvents(2 * cap)
-    labels = (ctypes.c_int * cap)()
-    lib.gdn_profile_events(ctypes.cast(ev.arr, ctypes.c_void_p), ctypes.cast(labels, ctypes.c_void_p), cap)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
+
+    def record(nsteps, mask):
+        # HIP events around the launches of the kinds in mask (each record costs
+        # the stream a few microseconds, so the timed loop brackets only the
+        # forward kernel); returns the wall time per step and the per-kind times
+        cap = 8 * nsteps
+        ev = HipEvents(2 * cap)
+        labels = (ctypes.c_int * cap)()
+        prev = lib.gdn_profile_kinds(mask)
+        lib.gdn_profile_events(ctypes.cast(ev.arr, ctypes.c_void_p), ctypes.cast(labels, ctypes.c_void_p), cap)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(nsteps):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        n = lib.gdn_profile_events(None, None, 0)
+        lib.gdn_profile_kinds(prev)
+        kinds = {}
+        for i in range(n):
+            kinds.setdefault(_lib.LAUNCH_KINDS[labels[i]], []).append(ev.elapsed_ms(2 * i, 2 * i + 1))
+        ev.close()
+        return (t1 - t0) * 1e3 / nsteps, kinds
+
+    # single-call latencies and the memory pattern's ceiling, before the
+    # throughput loop (so that it runs on a GPU under this workload's load)
+    timing = {"plain": rep_stats(torch, step, args.reps),
+              "mall_flushed": rep_stats(torch, step, args.reps, flush_bytes=512 * 2 ** 20)}
+    ceiling = pattern_ceiling(torch, gdn, lib, _lib, q, k, v, o)
+    for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    n = lib.gdn_profile_events(None, None, 0)
-    per_kind = {}
-    for i in range(n):
-        per_kind.setdefault(_lib.LAUNCH_KINDS[labels[i]], []).append(ev.elapsed_ms(2 * i, 2 * i + 1))
-    ev.close()
+
+    FWD_MASK = (1 << 2) | (1 << 4)   # GDN_LAUNCH_FWD_SINGLE, GDN_LAUNCH_FWD_QUEUE
+    ms_per_step, per_kind = record(args.steps, FWD_MASK)
     # a wait that ran out inside a timed call would leave invalid outputs
     plan_after = gdn.gdn_chunk_fwd_plan_info(B, T, H, workspace=ws)
     if plan_after["error"]:
         raise SystemExit("bench.py: the split forward reported a failed wait in a timed call")
-    timing = {"plain": rep_stats(torch, step, args.reps),
-              "mall_flushed": rep_stats(torch, step, args.reps, flush_bytes=512 * 2 ** 20)}
-    ceiling = pattern_ceiling(torch, gdn, lib, _lib, q, k, v, o)
+    # every launch of a call, bracketed, after the timed loop (informational)
+    _, all_kinds = record(5, 0xFFFFFFFF)
 
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
     tokens_per_s = B * T / (ms_per_step * 1e-3)
     nbytes = algorithmic_bytes(B, T, H, False, True)
     # the fused forward kernel reads every input and writes every output (the gate
@@ -485,6 +518,7 @@ def main():
     fwd_ms = sum(float(np.mean(per_kind[kd])) for kd in fwd_kinds)
     achieved = nbytes / (fwd_ms * 1e-3) / 1e9
     kernel_ms = {kd: round(float(np.mean(t)), 4) for kd, t in per_kind.items()}
+    launch_ms = {kd: round(float(np.mean(t)), 4) for kd, t in all_kinds.items()}
     tr = load_traffic()
     traffic = None if tr is None else tr["traffic_bytes"]
 
@@ -510,18 +544,10 @@ def main():
                      "algorithmic_bytes": nbytes,
                      "traffic_gbs": None if tr is None else traffic / (fwd_ms * 1e-3) / 1e9, "kernel_ms": kernel_ms,
                      "call_frac": nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "timing": timing,
+        "timing": dict(timing, launches_ms=launch_ms),
         "pattern_ceiling": dict(ceiling, fwd_kernel_vs_ceiling=achieved / ceiling["gbs"]),
     }
-    if args.bwd_steps > 0 or args.varlen_steps > 0 or args.kda_steps > 0:
-        del q, k, v, g, beta, o, ht, ws
-        torch.cuda.empty_cache()
-    if args.bwd_steps > 0:
-        res["backward"] = bench_backward(torch, gdn, _lib, inputs, args.bwd_steps, 2)
-    if args.varlen_steps > 0:
-        res["varlen"] = bench_varlen(torch, gdn, inputs, args.varlen_steps, 2)
-    if args.kda_steps > 0:
-        res["kda"] = bench_kda(torch, gdn, inputs, args.kda_steps, 1)
+    res.update(extra)
     if args.calib_copy_mib > 0:
         src = torch.randn(args.calib_copy_mib * 2 ** 18, device=dev)
         dst = torch.empty_like(src)

@@ -25,12 +25,13 @@ struct Profile {
     int used = 0;
 };
 thread_local Profile g_prof;
+thread_local uint32_t g_prof_kinds = 0xffffffffu;   // gdn_profile_kinds
 
 // Run one launcher, bracketed by profiling events when the hook is set.
 template <typename F>
 hipError_t recorded(int label, hipStream_t s, F&& launch) {
     Profile& p = g_prof;
-    const bool rec = p.events && p.used < p.capacity;
+    const bool rec = p.events && p.used < p.capacity && ((g_prof_kinds >> label) & 1u);
     if (rec) {
         hipError_t e = hipEventRecord(p.events[2 * p.used], s);
         if (e != hipSuccess) return e;
@@ -302,6 +303,12 @@ void gdn_default_options(gdn_options* opt) {
 }
 
 const char* gdn_last_error(void) { return g_err; }
+
+uint32_t gdn_profile_kinds(uint32_t mask) {
+    const uint32_t prev = g_prof_kinds;
+    g_prof_kinds = mask;
+    return prev;
+}
 
 int gdn_profile_events(void** events, int* labels, int capacity) {
     const int used = g_prof.used;

@@ -365,6 +365,13 @@ typedef enum {
  * device memory is touched. */
 int gdn_profile_events(void** events, int* labels, int capacity);
 
+/* Restrict the hook to the launch kinds whose bit (1u << gdn_launch_kind) is set
+ * in mask (all kinds by default); launches of other kinds are neither bracketed
+ * nor counted.  Each event record costs the stream a few microseconds, so a
+ * caller timing one kernel keeps the others unbracketed.  Thread-local; returns
+ * the previous mask. */
+uint32_t gdn_profile_kinds(uint32_t mask);
+
 /* Thread-local text describing the last non-OK status on this thread ("" if none). */
 const char* gdn_last_error(void);
 

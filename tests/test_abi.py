@@ -320,3 +320,13 @@ def test_kda_plan_and_workspace():
     assert wsz(2, 64 * 10, 3, 128, 128, 4) == 2 * 3 * 3 * 2 * 128 * 128 * 4
     assert wsz(2, 64 * 10, 3, 128, 128, -2) == ctypes.c_size_t(-1).value
     assert wsz(2, 64 * 10, 3, 64, 128, 2) == ctypes.c_size_t(-1).value
+
+
+def test_profile_kinds_mask_is_thread_local_bookkeeping():
+    """gdn_profile_kinds sets the launch kinds the profiling hook brackets and
+    returns the previous mask (all kinds by default); host-only."""
+    lib = _lib.load()
+    prev = lib.gdn_profile_kinds(1 << 4)
+    assert prev == 0xFFFFFFFF
+    assert lib.gdn_profile_kinds(prev) == 1 << 4
+    assert lib.gdn_profile_kinds(0xFFFFFFFF) == 0xFFFFFFFF

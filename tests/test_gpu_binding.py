@@ -177,3 +177,26 @@ def test_stream_probe_copies_v(gdn):
         written[last * 64:(last + 1) * 64] = False
     assert torch.equal(o.cpu()[written], v.cpu()[written])
     assert torch.count_nonzero(o.cpu()[~written]) == 0
+
+
+def test_profile_kinds_mask_brackets_only_the_selected_launches(gdn):
+    """With the mask set to the persistent forward launch, a split forward call
+    records exactly that launch (its two preparation launches go unbracketed)."""
+    import torch
+    say("case profiling hook restricted to the persistent forward launch")
+    x = inputs.generate(B=1, T=64 * 40, H=2, seed=72)
+    t = to_gpu(x)
+    kind_queue = 4   # GDN_LAUNCH_FWD_QUEUE
+    with _Launches() as all_kinds:
+        gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], None, split_mode=2, n_segments=4)
+    assert all_kinds.count >= 2
+    prev = all_kinds.lib.gdn_profile_kinds(1 << kind_queue)
+    try:
+        with _Launches() as only:
+            o, ht = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], None, split_mode=2, n_segments=4)
+    finally:
+        all_kinds.lib.gdn_profile_kinds(prev)
+    torch.cuda.synchronize()
+    assert only.count == 1 and only.labels[0] == kind_queue, (only.count, list(only.labels)[:only.count])
+    oref, href = oracle.fwd(x.q, x.k, x.v, x.g, x.beta, None)
+    assert rel_err(to_np(o), oref) <= TOL_BF16 and rel_err(to_np(ht), href) <= TOL_BF16
