@@ -31,7 +31,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 
 LAUNCH_KINDS = {0: "gate_sums", 1: "gate_flags", 2: "fwd_single", 3: "fwd_windows",
                 4: "fwd_queue", 5: "bwd_states", 6: "bwd_dh", 7: "bwd_local", 8: "fwd_sums",
-                9: "kda_fwd", 10: "stream_probe", 11: "kda_pass1", 12: "kda_chain"}
+                9: "kda_fwd", 10: "stream_probe", 11: "kda_pass1", 12: "kda_chain", 13: "bwd_chain"}
 
 
 class Options(ctypes.Structure):

@@ -204,6 +204,45 @@ BwdLayout bwd_layout(int B, int T, int H) {
     return L;
 }
 
+// Backward for few heads (talk summary, paragraph 4, applied to both serial
+// passes): when 2 B H < CUs, the state store runs through the split forward on
+// every CU (P_f segment slots per head, its workspace after the unsplit layout)
+// and the state-gradient sweep is split into P_s segments (their maps in P_s
+// slots per head after that): a = min(16, CUs / (B H), N / 8 - 1) workgroups per
+// head, P_s = a + 1 when a >= 2 (as for KDA: segment P_s - 1 runs beside the maps
+// of the others).  P_s = 1 means the unsplit backward.
+struct BwdSplit {
+    int pf, ps, ss;          // forward segment slots, sweep segments, chunks per sweep segment
+    size_t fwd, slots, total;   // offsets of the forward's workspace and the sweep slots; total bytes
+};
+BwdSplit bwd_split(int B, int T, int H, int cus) {
+    BwdSplit sp{};
+    sp.ps = 1;
+    const int N = num_chunks(T);
+    const long long bh = (long long)B * H;
+    if (cus > 0 && 2 * bh < cus) {
+        long long a = cus / bh;
+        if (a > 16) a = 16;
+        if (a > N / 8 - 1) a = N / 8 - 1;
+        if (a >= 2) {
+            const int p = (int)a + 1;
+            sp.ss = (N + p - 1) / p;
+            sp.ps = (N + sp.ss - 1) / sp.ss;
+        }
+    }
+    if (sp.ps == 1) return sp;
+    gdn_options o;
+    gdn_default_options(&o);
+    sp.pf = plan(B, T, H, cus, o);
+    size_t off = bwd_layout(B, T, H).total;
+    sp.fwd = off;
+    if (sp.pf > 1) off += align_up(fwd_layout(B, T, H, sp.pf).total);
+    sp.slots = off;
+    off += align_up((size_t)bh * sp.ps * gdn::kStateSlot * sizeof(float));
+    sp.total = off;
+    return sp;
+}
+
 // Packed-sequence backward workspace: the chunk prefix and the sequence bounds
 // (cu_seqlens clamped to [0, T] and made non-decreasing), then states and state
 // gradients in per-head slots (cmax = ceil(T/64) + S bounds the chunks of all
@@ -366,17 +405,22 @@ gdn_status check_fwd_args(const void* q, const void* k, const void* v, const flo
 // least fwd_layout(B, T, H, P).total bytes (unused when P = 1).
 gdn_status fwd_launch(const void* q, const void* k, const void* v, const float* g, const float* beta,
                       const float* h0, void* o, float* ht, int B, int T, int H, gdn_dtype dtype, float scale,
-                      const gdn_options& op, int cus, int P, void* workspace, hipStream_t s) {
+                      const gdn_options& op, int cus, int P, void* workspace, hipStream_t s,
+                      __bf16* hstore = nullptr) {
     const int N = num_chunks(T);
     const FwdLayout L = fwd_layout(B, T, H, P);
     gdn::FwdParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.o = o; p.ht = ht;
     p.B = B; p.T = T; p.H = H; p.N = N; p.P = P; p.w = op.window_chunks; p.scale = scale;
     p.wmax = nullptr;
+    p.hstore = hstore;   // keep the state entering every chunk (the backward's state store)
     const bool bf16 = dtype == GDN_BF16;
     hipError_t e;
     if (P == 1) {
-        e = recorded(GDN_LAUNCH_FWD_SINGLE, s, [&] { return gdn::launch_fwd(p, gdn::PHASE_SINGLE, bf16, s); });
+        if (hstore)
+            e = recorded(GDN_LAUNCH_BWD_STATES, s, [&] { return gdn::launch_fwd(p, gdn::PHASE_STATES, bf16, s); });
+        else
+            e = recorded(GDN_LAUNCH_FWD_SINGLE, s, [&] { return gdn::launch_fwd(p, gdn::PHASE_SINGLE, bf16, s); });
         if (e != hipSuccess) return hip_fail(e, "forward launch");
         return GDN_OK;
     }
@@ -420,7 +464,11 @@ gdn_status fwd_launch(const void* q, const void* k, const void* v, const float* 
         });
         if (e != hipSuccess) return hip_fail(e, "forward window launch");
     }
-    e = recorded(GDN_LAUNCH_FWD_QUEUE, s, [&] { return gdn::launch_fwd(p, gdn::PHASE_QUEUE, bf16, s); });
+    if (hstore)
+        e = recorded(GDN_LAUNCH_BWD_STATES, s,
+                     [&] { return gdn::launch_fwd(p, gdn::PHASE_QUEUE_STATES, bf16, s); });
+    else
+        e = recorded(GDN_LAUNCH_FWD_QUEUE, s, [&] { return gdn::launch_fwd(p, gdn::PHASE_QUEUE, bf16, s); });
     if (e != hipSuccess) return hip_fail(e, "forward launch");
     return GDN_OK;
 }
@@ -752,7 +800,13 @@ gdn_status gdn_gate_scan(const float* g, int B, int T, int H, int window_chunks,
 
 size_t gdn_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, gdn_dtype dtype) {
     if (check_shapes(B, T, H, dk, dv, dtype) != GDN_OK) return (size_t)-1;
-    return bwd_layout(B, T, H).total;
+    int cus = 0;
+    if (device_cus(&cus) != GDN_OK) {   // no device: the unsplit backward's size
+        g_err[0] = 0;
+        return bwd_layout(B, T, H).total;
+    }
+    const BwdSplit sp = bwd_split(B, T, H, cus);
+    return sp.ps > 1 ? sp.total : bwd_layout(B, T, H).total;
 }
 
 gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
@@ -785,13 +839,46 @@ gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const floa
         return fail(GDN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
 
     hipStream_t s = (hipStream_t)stream;
-    hipStream_t s2 = nullptr;
-    hipError_t e = side_stream(&s2);
-    if (e != hipSuccess) return hip_fail(e, "backward side stream");
     const int N = num_chunks(T);
     char* ws = (char*)workspace;
     __bf16* hstore = (__bf16*)(ws + L.hstore);
     __bf16* dhstore = (__bf16*)(ws + L.dhstore);
+    int cus = 0;
+    if ((st = device_cus(&cus)) != GDN_OK) return st;
+    const BwdSplit sp = bwd_split(B, T, H, cus);
+    if (sp.ps > 1 && workspace_bytes >= sp.total) {
+        // few heads: the state store through the split forward on every CU, then
+        // the sweep in segments (first launch: the last segment and the others'
+        // maps; the chain; the remaining segments), then the local gradients
+        gdn_options o;
+        gdn_default_options(&o);
+        st = fwd_launch(q, k, v, g, beta, h0, nullptr, nullptr, B, T, H, dtype, scale, o, cus, sp.pf,
+                        ws + sp.fwd, s, hstore);
+        if (st != GDN_OK) return st;
+        gdn::BwdParams p{};
+        p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.dout = dout; p.dht = dht;
+        p.dq = grad_q; p.dk = grad_k; p.dv = grad_v; p.dg = grad_g; p.dbeta = grad_beta; p.dh0 = grad_h0;
+        p.B = B; p.T = T; p.H = H; p.N = N; p.scale = scale;
+        p.hstore = hstore;
+        p.dhstore = dhstore;
+        p.P = sp.ps; p.S = sp.ss; p.ws = (float*)(ws + sp.slots);
+        hipError_t e = recorded(GDN_LAUNCH_BWD_DH, s, [&] { return gdn::launch_bwd_dh(p, true, s, gdn::DH_FIRST); });
+        if (e != hipSuccess) return hip_fail(e, "backward state-gradient launch");
+        if (sp.ps > 2) {
+            // from the gradient at the start of segment P-1 down to segment 1
+            gdn::ChainParams c{p.ws, sp.ps, sp.ps - 1, -1, sp.ps - 2};
+            e = recorded(GDN_LAUNCH_BWD_CHAIN, s, [&] { return gdn::launch_state_chain(c, B * H, s); });
+            if (e != hipSuccess) return hip_fail(e, "backward chain launch");
+        }
+        e = recorded(GDN_LAUNCH_BWD_DH, s, [&] { return gdn::launch_bwd_dh(p, true, s, gdn::DH_REST); });
+        if (e != hipSuccess) return hip_fail(e, "backward state-gradient launch");
+        e = recorded(GDN_LAUNCH_BWD_LOCAL, s, [&] { return gdn::launch_bwd_local(p, true, s); });
+        if (e != hipSuccess) return hip_fail(e, "backward local-gradient launch");
+        return GDN_OK;
+    }
+    hipStream_t s2 = nullptr;
+    hipError_t e = side_stream(&s2);
+    if (e != hipSuccess) return hip_fail(e, "backward side stream");
     gdn::FwdParams f{};
     f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.h0 = h0; f.o = nullptr; f.ht = nullptr;
     f.B = B; f.T = T; f.H = H; f.N = N; f.P = 1; f.w = 1; f.scale = scale;

@@ -113,21 +113,72 @@ __device__ __forceinline__ void dh_chunk_step(const Lane<T>& L, const T* kt, con
     kt_update<T>(L, qt, dH, 1.f, bq);
 }
 
-// Gradient waves: carry dH from the end of the sequence to its start.  Executes
-// exactly the same barriers as dh_prep_loop.
+// The linear part of one chunk's step, for the segment maps of the split sweep:
+// dH <- Gamma_C dH - K^T diag(Gamma) dY with dY from dV' = diag(E) K dH alone
+// (the chunk map of dh_chunk_step with dO = 0).
 template <typename T>
-__device__ __noinline__ void dh_state_loop(const BwdParams& prm, Smem<T>& sm, int bh) {
+__device__ __forceinline__ void dh_map_step(const Lane<T>& L, const T* kt, const T (*t32)[kT32],
+                                            const float* gam_vec, const float* e_vec, float GC, f32x16* M) {
+    using F = typename FragOf<T>::type;
+    const int g = L.g, lane = L.lane;
+    f32x16 X[2];
+    k_times<T>(L, kt, M, X);   // K M
+    const f32x16 e0 = rows_of(e_vec, 0, g), e1 = rows_of(e_vec, 1, g);
+    f32x16 dvp0, dvp1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        dvp0[r] = e0[r] * X[0][r];
+        dvp1[r] = e1[r] * X[1][r];
+    }
+    f32x16 dy1 = zero16();
+    dy1 = mma(tfrag<T, 32>(t32[1], 0, 0, lane), acc_frag<T>(dvp1, 0), dy1);
+    dy1 = mma(tfrag<T, 32>(t32[1], 0, 1, lane), acc_frag<T>(dvp1, 1), dy1);
+    f32x16 z0 = dvp0;
+    z0 = mma(tfrag<T, 32>(t32[2], 0, 0, lane), acc_frag<T>(dy1, 0), z0);
+    z0 = mma(tfrag<T, 32>(t32[2], 0, 1, lane), acc_frag<T>(dy1, 1), z0);
+    f32x16 dy0 = zero16();
+    dy0 = mma(tfrag<T, 32>(t32[0], 0, 0, lane), acc_frag<T>(z0, 0), dy0);
+    dy0 = mma(tfrag<T, 32>(t32[0], 0, 1, lane), acc_frag<T>(z0, 1), dy0);
+    F bk[4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const f32x16 gr = rows_of(gam_vec, rt, g);
+        const f32x16& dy = rt ? dy1 : dy0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            bk[2 * rt][j] = (T)(-gr[j] * dy[j]);
+            bk[2 * rt + 1][j] = (T)(-gr[8 + j] * dy[8 + j]);
+        }
+    }
+    kt_update<T>(L, kt, M, GC, bk);
+}
+
+// Gradient waves: carry dH over chunks c1 - 1 down to c0 of head bh.  The start
+// is dht (in_slot < 0) or the b field of workspace slot in_slot; PASS1 starts
+// from zero and stores no per-chunk gradients (the segment's b).  At the end the
+// gradient goes to the b field of slot out_slot (>= 0), to dh0 (-1) or nowhere
+// (-2).  Executes exactly the same barriers as dh_prep_loop.
+template <typename T, bool PASS1 = false>
+__device__ __noinline__ void dh_state_loop(const BwdParams& prm, Smem<T>& sm, int bh, int c0, int c1, int in_slot,
+                                           int out_slot) {
+    static_assert(!PASS1 || kDhLoadAhead, "segment maps are built with the fetch-ahead sweep only");
+    bh = uni(bh), c0 = uni(c0), c1 = uni(c1), in_slot = uni(in_slot), out_slot = uni(out_slot);
     constexpr bool kPipe = kDhPipelined;
     const size_t SS = (size_t)kDk * kDv;
     const int N = uni(prm.N);
+    const int n = c1 - c0;
     const float scale = uni(prm.scale);
     __bf16* const dst = uni(prm.dhstore) + (size_t)bh * N * SS;
     const float* const dht = uni(prm.dht);
     float* const dh0 = uni(prm.dh0);
+    float* const ws = uni(prm.ws);
+    const int P = uni(prm.P);
     Lane<T> L;
     L.init(threadIdx.x);
     f32x16 dH[4];
-    if (dht) {
+    if (!PASS1 && in_slot >= 0) {
+        load_state(ws + ((size_t)bh * P + in_slot) * kStateSlot + kDk * kDk, L.w, L.lane, dH);
+    } else if (!PASS1 && dht) {
         load_state(dht + (size_t)bh * SS, L.w, L.lane, dH);
     } else {
 #pragma unroll
@@ -136,8 +187,8 @@ __device__ __noinline__ void dh_state_loop(const BwdParams& prm, Smem<T>& sm, in
     if constexpr (kPipe) {
         lds_barrier();
         lds_barrier();
-        for (int i = 0; i < N; ++i) {
-            const int c = N - 1 - i;
+        for (int i = 0; i < n; ++i) {
+            const int c = c1 - 1 - i;
             const int slot = i % 3, vb = i & 1;
             store_state_bf16t(uni(dst + (size_t)c * SS), L.w, L.lane, dH);
             dh_chunk_step<T>(L, sm.kt[slot], sm.qt[slot], sm.vt[vb], sm.t32[vb], sm.gam_vec[vb],
@@ -145,18 +196,18 @@ __device__ __noinline__ void dh_state_loop(const BwdParams& prm, Smem<T>& sm, in
             lds_barrier();
         }
     } else if constexpr (kDhLoadAhead) {
-        for (int i = 0; i < N; ++i) {
-            const int c = N - 1 - i;
+        for (int i = 0; i < n; ++i) {
+            const int c = c1 - 1 - i;
             const int slot = i & 1;
             lds_barrier();   // A
             lds_barrier();   // B
-            store_state_bf16t(uni(dst + (size_t)c * SS), L.w, L.lane, dH);
+            if (!PASS1) store_state_bf16t(uni(dst + (size_t)c * SS), L.w, L.lane, dH);
             dh_chunk_step<T>(L, sm.kt[slot], sm.qt[slot], sm.vt[slot], sm.t32[0], sm.gam_vec[0], sm.e_vec[0],
                              sm.gc[0][0], scale, dH);
         }
     } else {
-        for (int i = 0; i < N; ++i) {
-            const int c = N - 1 - i;
+        for (int i = 0; i < n; ++i) {
+            const int c = c1 - 1 - i;
             lds_barrier();
             lds_barrier();
             lds_barrier();
@@ -165,17 +216,24 @@ __device__ __noinline__ void dh_state_loop(const BwdParams& prm, Smem<T>& sm, in
                              sm.gc[0][0], scale, dH);
         }
     }
-    if (dh0) store_state(uni(dh0 + (size_t)bh * SS), L.w, L.lane, dH);
+    if (out_slot >= 0)
+        store_state(ws + ((size_t)bh * P + out_slot) * kStateSlot + kDk * kDk, L.w, L.lane, dH);
+    else if (out_slot == -1 && dh0)
+        store_state(uni(dh0 + (size_t)bh * SS), L.w, L.lane, dH);
 }
 
-// Prep waves: stream K, Q, dO of the chunks in reverse order and prep each one a
-// step ahead of the gradient waves.  Executes exactly the same barriers as
-// dh_state_loop.
-template <typename T>
-__device__ __noinline__ void dh_prep_loop(const BwdParams& prm, Smem<T>& sm, int bh) {
+// Prep waves: stream K, Q, dO of chunks c1 - 1 down to c0 and prep each one
+// ahead of the gradient waves.  In PASS1 they also carry the segment's map M
+// from the identity, 32 columns each, after the blocks of a chunk are written
+// (the gradient waves' step reads the same buffers), and store it in the M
+// field of slot out_slot.  Executes exactly the same barriers as dh_state_loop.
+template <typename T, bool PASS1 = false>
+__device__ __noinline__ void dh_prep_loop(const BwdParams& prm, Smem<T>& sm, int bh, int c0, int c1, int out_slot) {
+    bh = uni(bh), c0 = uni(c0), c1 = uni(c1), out_slot = uni(out_slot);
     constexpr bool kPipe = kDhPipelined;
     const int pw = wave_id() - 4;
-    const int H = uni(prm.H), Tn = uni(prm.T), N = uni(prm.N);
+    const int H = uni(prm.H), Tn = uni(prm.T);
+    const int N = c1 - c0;   // chunks of this range
     const int b = bh / H, h = bh % H;
     const T* const q = uni((const T*)prm.q);
     const T* const k = uni((const T*)prm.k);
@@ -186,7 +244,14 @@ __device__ __noinline__ void dh_prep_loop(const BwdParams& prm, Smem<T>& sm, int
     L.init(threadIdx.x);
     float gsum = 0.f;
     float g_cur = 0.f, b_cur = 0.f, g_nxt = 0.f, b_nxt = 0.f;
-    auto cidx = [&](int i) { return N - 1 - i; };
+    auto cidx = [&](int i) { return c1 - 1 - i; };
+    f32x16 Ms[4];
+    if (PASS1) {
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Ms[ht][r] = (32 * ht + rho(L.g, r) == 32 * L.w + L.n) ? 1.f : 0.f;
+    }
     // with the fetch ahead, prep waves 2 and 3 issue every tile load, so waves 0
     // and 1 (the diagonal inverses, the longest prep work) never wait on the
     // memory pipeline; otherwise all four load their quarter
@@ -258,6 +323,7 @@ __device__ __noinline__ void dh_prep_loop(const BwdParams& prm, Smem<T>& sm, int
                                      sm.e_vec[0], sm.gc[0], g_cur, b_cur, true, gsum);
             wait_vm();
             lds_barrier();   // B: prep of chunk i and the tiles of chunk i + 1 are in LDS
+            if (PASS1) dh_map_step<T>(L, sm.kt[slot], sm.t32[0], sm.gam_vec[0], sm.e_vec[0], sm.gc[0][0], Ms);
         }
     } else {
         for (int i = 0; i < N; ++i) {
@@ -273,18 +339,45 @@ __device__ __noinline__ void dh_prep_loop(const BwdParams& prm, Smem<T>& sm, int
             lds_barrier();
         }
     }
+    if (PASS1) store_state(uni(prm.ws) + ((size_t)bh * uni(prm.P) + out_slot) * kStateSlot, L.w, L.lane, Ms);
 }
 
-template <typename T>
+// DH_FULL: workgroup = head, all chunks.  DH_FIRST: per head P - 1 workgroups;
+// j = 0 runs segment P-1 from dht (its gradients stored, the gradient at its
+// start to slot P-1), j >= 1 builds the map of segment P-1-j.  DH_REST: per head
+// P - 1 workgroups; j runs segment j from the gradient at its end (slot j + 1).
+template <typename T, int MODE>
 __global__ __launch_bounds__(kDhThreads, 1) void gdn_bwd_dh_kernel(BwdParams prm) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     Smem<T>& sm = *reinterpret_cast<Smem<T>*>(smem_raw);
-    const int bh = blockIdx.x;
+    const int groups = MODE == DH_FULL ? 1 : prm.P - 1;
+    const int bh = (int)blockIdx.x / groups, j = (int)blockIdx.x % groups;
+    int seg = 0, c0 = 0, c1 = prm.N, in_slot = -1, out_slot = -1;
+    if (MODE == DH_FIRST) {
+        seg = prm.P - 1 - j;
+        out_slot = seg;
+    } else if (MODE == DH_REST) {
+        seg = j;
+        in_slot = seg + 1;
+        out_slot = seg == 0 ? -1 : -2;
+    }
+    if (MODE != DH_FULL) {
+        c0 = seg * prm.S;
+        c1 = min(c0 + prm.S, prm.N);
+    }
+    const bool map = MODE == DH_FIRST && j > 0;
     // wave-uniform role branch: both roles hold barriers
-    if (wave_id() < 4)
-        dh_state_loop<T>(prm, sm, bh);
-    else
-        dh_prep_loop<T>(prm, sm, bh);
+    if (wave_id() < 4) {
+        if (map)
+            dh_state_loop<T, true>(prm, sm, bh, c0, c1, in_slot, out_slot);
+        else
+            dh_state_loop<T>(prm, sm, bh, c0, c1, in_slot, out_slot);
+    } else {
+        if (map)
+            dh_prep_loop<T, true>(prm, sm, bh, c0, c1, out_slot);
+        else
+            dh_prep_loop<T>(prm, sm, bh, c0, c1, out_slot);
+    }
 }
 
 // Packed sequences: parameters of sequence s, head h as one sequence of a batch
@@ -323,9 +416,9 @@ __global__ __launch_bounds__(kDhThreads, 1) void gdn_bwd_dh_varlen_kernel(BwdPar
     BwdParams prm = prm_in;
     varlen_bwd_params(prm, bh / prm_in.H, bh % prm_in.H, sizeof(T));
     if (wave_id() < 4)
-        dh_state_loop<T>(prm, sm, bh);
+        dh_state_loop<T>(prm, sm, bh, 0, prm.N, -1, -1);
     else
-        dh_prep_loop<T>(prm, sm, bh);
+        dh_prep_loop<T>(prm, sm, bh, 0, prm.N, -1);
 }
 
 // Packed sequences, one workgroup, 256 bounds per round with running carries:
@@ -958,19 +1051,26 @@ hipError_t set_lds(K kernel, size_t bytes) {
 }
 
 template <typename T>
-hipError_t launch_dh_t(const BwdParams& p, hipStream_t s) {
+hipError_t launch_dh_t(const BwdParams& p, hipStream_t s, int mode) {
     static bool configured = false;
     const size_t lds = sizeof(Smem<T>);
     if (!configured) {
-        hipError_t e = set_lds(gdn_bwd_dh_kernel<T>, lds);
+        hipError_t e = set_lds(gdn_bwd_dh_kernel<T, DH_FULL>, lds);
+        if (e == hipSuccess) e = set_lds(gdn_bwd_dh_kernel<T, DH_FIRST>, lds);
+        if (e == hipSuccess) e = set_lds(gdn_bwd_dh_kernel<T, DH_REST>, lds);
         if (e == hipSuccess) e = set_lds(gdn_bwd_dh_varlen_kernel<T>, lds);
         if (e != hipSuccess) return e;
         configured = true;
     }
+    const unsigned nbh = (unsigned)(p.B * p.H);
     if (p.cu)
-        hipLaunchKernelGGL((gdn_bwd_dh_varlen_kernel<T>), dim3(p.B * p.H), dim3(kDhThreads), lds, s, p);
+        hipLaunchKernelGGL((gdn_bwd_dh_varlen_kernel<T>), dim3(nbh), dim3(kDhThreads), lds, s, p);
+    else if (mode == DH_FIRST)
+        hipLaunchKernelGGL((gdn_bwd_dh_kernel<T, DH_FIRST>), dim3(nbh * (p.P - 1)), dim3(kDhThreads), lds, s, p);
+    else if (mode == DH_REST)
+        hipLaunchKernelGGL((gdn_bwd_dh_kernel<T, DH_REST>), dim3(nbh * (p.P - 1)), dim3(kDhThreads), lds, s, p);
     else
-        hipLaunchKernelGGL((gdn_bwd_dh_kernel<T>), dim3(p.B * p.H), dim3(kDhThreads), lds, s, p);
+        hipLaunchKernelGGL((gdn_bwd_dh_kernel<T, DH_FULL>), dim3(nbh), dim3(kDhThreads), lds, s, p);
     return hipGetLastError();
 }
 
@@ -994,8 +1094,8 @@ hipError_t launch_local_t(const BwdParams& p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_bwd_dh(const BwdParams& p, bool bf16, hipStream_t s) {
-    return bf16 ? launch_dh_t<__bf16>(p, s) : hipErrorNotSupported;
+hipError_t launch_bwd_dh(const BwdParams& p, bool bf16, hipStream_t s, int mode) {
+    return bf16 ? launch_dh_t<__bf16>(p, s, mode) : hipErrorNotSupported;
 }
 
 hipError_t launch_bwd_local(const BwdParams& p, bool bf16, hipStream_t s) {

@@ -875,7 +875,9 @@ template <typename T>
 __device__ __forceinline__ void plan_wg(const FwdParams& prm, Smem<T>& sm, bool publish);
 
 // Persistent workgroups of the split forward: take jobs until the list is empty.
-template <typename T>
+// KEEP: every job with outputs also stores the state entering each of its output
+// chunks (the backward's state store for few heads).
+template <typename T, bool KEEP>
 __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_queue_kernel(FwdParams prm) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     Smem<T>& sm = *reinterpret_cast<Smem<T>*>(smem_raw);
@@ -936,7 +938,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_queue_kernel(FwdParams pr
         } else if (tk.mode == MODE_PASS1) {
             run_task<T, MODE_PASS1>(prm, sm, tk);
         } else {
-            run_task<T, MODE_FULL>(prm, sm, tk);
+            run_task<T, MODE_FULL, KEEP>(prm, sm, tk);
         }
         if (threadIdx.x == 0) sm.islot[0] = (int)gridDim.x + atomicAdd(&prm.plan->next, 1);
         __syncthreads();
@@ -1507,14 +1509,18 @@ hipError_t launch_phase(const FwdParams& p, hipStream_t s) {
     if (!configured) {
         hipError_t e;
         if constexpr (PHASE == PHASE_QUEUE)
-            e = set_lds(gdn_fwd_queue_kernel<T>, lds);
+            e = set_lds(gdn_fwd_queue_kernel<T, false>, lds);
+        else if constexpr (PHASE == PHASE_QUEUE_STATES)
+            e = set_lds(gdn_fwd_queue_kernel<T, true>, lds);
         else
             e = set_lds(gdn_fwd_kernel<T, PHASE>, lds);
         if (e != hipSuccess) return e;
         configured = true;
     }
     if constexpr (PHASE == PHASE_QUEUE)
-        hipLaunchKernelGGL((gdn_fwd_queue_kernel<T>), dim3(p.cus), dim3(kThreads), lds, s, p);
+        hipLaunchKernelGGL((gdn_fwd_queue_kernel<T, false>), dim3(p.cus), dim3(kThreads), lds, s, p);
+    else if constexpr (PHASE == PHASE_QUEUE_STATES)
+        hipLaunchKernelGGL((gdn_fwd_queue_kernel<T, true>), dim3(p.cus), dim3(kThreads), lds, s, p);
     else if constexpr (PHASE == PHASE_VARLEN)
         hipLaunchKernelGGL((gdn_fwd_kernel<T, PHASE>), dim3(p.B * p.H * (p.vseg > 0 ? p.P : 1)),
                            dim3(kThreads), lds, s, p);
@@ -1529,6 +1535,7 @@ hipError_t launch_fwd_t(const FwdParams& p, int phase, hipStream_t s) {
     if (phase == PHASE_STATES) return launch_phase<T, PHASE_STATES>(p, s);
     if (phase == PHASE_VARLEN) return launch_phase<T, PHASE_VARLEN>(p, s);
     if (phase == PHASE_STATES_VARLEN) return launch_phase<T, PHASE_STATES_VARLEN>(p, s);
+    if (phase == PHASE_QUEUE_STATES) return launch_phase<T, PHASE_QUEUE_STATES>(p, s);
     return launch_phase<T, PHASE_QUEUE>(p, s);
 }
 

@@ -116,11 +116,14 @@ __device__ inline SeqSpan seq_span(const int* cu, const int* cstart, int nseq, i
 
 // PHASE_SINGLE: one workgroup per head, the whole sequence.
 // PHASE_QUEUE: persistent workgroups running the jobs of the split forward.
+// PHASE_QUEUE_STATES: the same, keeping the state entering every chunk (hstore,
+// as PHASE_STATES) from the jobs that own the chunk's output.
 // PHASE_STATES: the unsplit forward that only stores the state entering every
 // chunk (into hstore), for the backward.
 // PHASE_VARLEN: one workgroup per (sequence, head) of a packed batch (cu).
 // PHASE_STATES_VARLEN: PHASE_STATES over a packed batch.
-enum FwdPhase { PHASE_SINGLE = 0, PHASE_QUEUE = 1, PHASE_STATES = 2, PHASE_VARLEN = 3, PHASE_STATES_VARLEN = 4 };
+enum FwdPhase { PHASE_SINGLE = 0, PHASE_QUEUE = 1, PHASE_STATES = 2, PHASE_VARLEN = 3, PHASE_STATES_VARLEN = 4,
+                PHASE_QUEUE_STATES = 5 };
 
 hipError_t launch_fwd(const FwdParams& p, int phase, bool bf16, hipStream_t s);
 // The forward's fixed scratch array (gdn_chunk_fwd_noalloc): its size, and its
@@ -169,7 +172,19 @@ struct BwdParams {
     const int* cu;         // packed sequences: token offsets [B+1] (null: B sequences of length T)
     int cmax;              // packed sequences: chunk slots per head (see FwdParams)
     const int* cstart;     // packed sequences: chunk prefix [B+1], then the sequence bounds [B+1]
+    // split state-gradient sweep: P segments of S chunks (the last shorter); ws:
+    // per batch-head P slots of kStateSlot floats: slot s (1 <= s <= P-2) holds
+    // segment s's map from the gradient at its end to the gradient at its start
+    // (M, then b), and after the chain its b field holds the gradient at the end
+    // of segment s - 1; slot P-1's b field receives the gradient at the start of
+    // segment P-1, which runs from dht
+    int P, S;
+    float* ws;
 };
+// sweep launches: DH_FULL one workgroup per head over all chunks; DH_FIRST
+// segment P-1 (from dht) beside the maps of segments 1 .. P-2; DH_REST segments
+// 0 .. P-2 from the gradients the chain left
+enum { DH_FULL = 0, DH_FIRST = 1, DH_REST = 2 };
 // Per-key-channel-decay variant (KDA): g is [B, T, H, dk] float32 (one log-decay
 // per key channel), q, k, v, o bf16; one workgroup per (batch, head).
 struct KdaParams {
@@ -193,7 +208,17 @@ struct KdaParams {
     int P, S;
     float* ws;
 };
-constexpr size_t kKdaSlot = 2 * 128 * 128;
+// one segment map of an exact split: M ([dk][dk]) then b ([dk][dv]), float32
+constexpr size_t kStateSlot = 2 * 128 * 128;
+constexpr size_t kKdaSlot = kStateSlot;
+// The chain of segment maps (gdn_chain.hip): per batch-head `slots` slots; from
+// the b field of slot `start`, for i = 1 .. count, slot cur = start + i * step:
+// S = M_cur S + b_cur, written over b_cur.
+struct ChainParams {
+    float* ws;
+    int slots, start, step, count;
+};
+hipError_t launch_state_chain(const ChainParams& p, int nbh, hipStream_t s);
 // KDA_FULL: one segment per head (P = 1).  KDA_FIRST: segment 0 with outputs
 // beside the transitions of segments 1 .. P-2 (P - 1 workgroups per head).
 // KDA_REST: segments 1 .. P-1 with outputs from the states the chain left.
@@ -210,7 +235,7 @@ size_t kda_smem_bytes();
 // Packed sequences: the stored states of sequence s, head h sit at per-head slots
 // h * (cmax + B) + c0 + s + c (c = 0 .. nch, the last being its final state) and
 // the state gradients at h * cmax + c0 + c (c < nch).
-hipError_t launch_bwd_dh(const BwdParams& p, bool bf16, hipStream_t s);
+hipError_t launch_bwd_dh(const BwdParams& p, bool bf16, hipStream_t s, int mode = DH_FULL);
 // Packed sequences: cstart[s] = chunks of sequences 0 .. s-1, s = 0 .. B, then
 // the bounds cstart[B + 1 + s] = max(0, clamp(cu[0]), .., clamp(cu[s])), s = 0 .. B.
 hipError_t launch_seq_chunk_prefix(const int* cu, int B, int T, int* cstart, hipStream_t s);

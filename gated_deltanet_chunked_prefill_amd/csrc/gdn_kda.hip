@@ -546,70 +546,6 @@ __global__ __launch_bounds__(kKdaThreads, 1) void gdn_kda_fwd_kernel(KdaParams p
     }
 }
 
-// The states entering segments 2 .. P-1: S_{p+1} = M_p S_p + b_p for p = 1 ..
-// P-2, from S_1 (the final state of segment 0, which ran from h0), in float32 on
-// the vector units; S_{p+1} is written over b_p in segment p's slot.  Columns of
-// S never mix, so workgroup (batch-head, column block cb) owns 16 of the 128
-// columns: its S block stays in LDS across the segments, and thread t owns row
-// t >> 1, columns 16 cb + 8 (t & 1) .. +7 of every product.  Each thread holds
-// its row of M_p in registers, fetched one segment ahead with its entries of b_p.
-constexpr int kChainCols = 16;
-constexpr int kChainThreads = 2 * kDk;
-
-__global__ __launch_bounds__(kChainThreads, 1) void kda_chain_kernel(KdaParams prm) {
-    __shared__ __attribute__((aligned(16))) float Sl[kDk * kChainCols];   // [k][16 columns]
-    constexpr int CB = kDv / kChainCols;
-    const int bh = (int)blockIdx.x / CB, cb = (int)blockIdx.x % CB, t = threadIdx.x;
-    const int i = t >> 1, jl = 8 * (t & 1), j0 = kChainCols * cb + jl;
-    const size_t SS = (size_t)kDk * kDv;
-    float* const base = prm.ws + (size_t)bh * (prm.P - 1) * kKdaSlot;
-    const size_t MM = (size_t)kDk * kDk;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) Sl[i * kChainCols + jl + c] = base[MM + (size_t)i * kDv + j0 + c];   // S_1
-    f32x4 mnext[kDk / 4];
-    float bnext[8];
-    const float* const M1 = base + kKdaSlot;
-#pragma unroll
-    for (int q = 0; q < kDk / 4; ++q) mnext[q] = *reinterpret_cast<const f32x4*>(M1 + (size_t)i * kDk + 4 * q);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) bnext[c] = M1[MM + (size_t)i * kDv + j0 + c];
-    __syncthreads();
-    for (int p = 1; p + 1 < prm.P; ++p) {
-        float* const bp = base + (size_t)p * kKdaSlot + MM;
-        float acc[8];
-        f32x4 m[kDk / 4];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = bnext[c];
-#pragma unroll
-        for (int q = 0; q < kDk / 4; ++q) m[q] = mnext[q];
-        if (p + 2 < prm.P) {
-            const float* const Mn = base + (size_t)(p + 1) * kKdaSlot;
-#pragma unroll
-            for (int q = 0; q < kDk / 4; ++q) mnext[q] = *reinterpret_cast<const f32x4*>(Mn + (size_t)i * kDk + 4 * q);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) bnext[c] = Mn[MM + (size_t)i * kDv + j0 + c];
-        }
-#pragma unroll
-        for (int k = 0; k < kDk; ++k) {
-            const float mk = m[k >> 2][k & 3];
-            const f32x4 s0 = *reinterpret_cast<const f32x4*>(Sl + k * kChainCols + jl);
-            const f32x4 s1 = *reinterpret_cast<const f32x4*>(Sl + k * kChainCols + jl + 4);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                acc[c] = __builtin_fmaf(mk, s0[c], acc[c]);
-                acc[4 + c] = __builtin_fmaf(mk, s1[c], acc[4 + c]);
-            }
-        }
-        __syncthreads();   // every product has read S_p
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            Sl[i * kChainCols + jl + c] = acc[c];
-            bp[(size_t)i * kDv + j0 + c] = acc[c];
-        }
-        __syncthreads();
-    }
-}
-
 }  // namespace
 
 size_t kda_smem_bytes() { return sizeof(KdaSmem); }
@@ -640,8 +576,9 @@ hipError_t launch_kda_fwd(const KdaParams& p, int mode, hipStream_t s) {
 }
 
 hipError_t launch_kda_chain(const KdaParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(kda_chain_kernel, dim3(p.B * p.H * (kDv / kChainCols)), dim3(kChainThreads), 0, s, p);
-    return hipGetLastError();
+    // S_1 in slot 0 (segment 0's final state), then slots 1 .. P-2 in order
+    ChainParams c{p.ws, p.P - 1, 0, 1, p.P - 2};
+    return launch_state_chain(c, p.B * p.H, s);
 }
 
 }  // namespace gdn

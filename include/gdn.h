@@ -351,7 +351,8 @@ typedef enum {
     GDN_LAUNCH_KDA_FWD = 9,     /* KDA forward (with outputs)                         */
     GDN_LAUNCH_STREAM_PROBE = 10, /* measurement aid: the forward's memory pattern    */
     GDN_LAUNCH_KDA_PASS1 = 11,  /* KDA split: segment 0, and the other segments' transitions */
-    GDN_LAUNCH_KDA_CHAIN = 12   /* KDA split: states entering the segments            */
+    GDN_LAUNCH_KDA_CHAIN = 12,  /* KDA split: states entering the segments            */
+    GDN_LAUNCH_BWD_CHAIN = 13   /* backward, few heads: gradients entering the sweep's segments */
 } gdn_launch_kind;
 
 /* Measurement hook (the talk summary, paragraph 7, argues the fused operator

@@ -120,6 +120,53 @@ def test_bwd_degenerate_gates(gdn, case):
     _check(got, ref, case)
 
 
+def _bwd_both(gdn, x, dht=None, scale=1.0):
+    """The same call twice: with the library's workspace query (the few-heads
+    path: split state store and split sweep) and with a workspace of the unsplit
+    backward's size (the unsplit path)."""
+    import torch
+    from gated_deltanet_chunked_prefill_amd import _lib
+    t = to_gpu(x)
+    B, T, H = x.beta.shape
+    dht_t = None if dht is None else torch.from_numpy(dht).float().cuda()
+    SS = 128 * 128
+    N = -(-T // 64)
+    small = torch.empty(B * H * (2 * N + 1) * SS * 2 + 4096, dtype=torch.uint8, device="cuda")
+    outs = []
+    for ws in (None, small):
+        out = gdn.gdn_chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["dout"], h0=t["h0"],
+                                dht=dht_t, scale=scale, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append({n: to_np(out[n]) for n in NAMES})
+    ref = oracle.bwd(x.q, x.k, x.v, x.g, x.beta, x.dout, x.h0, dht, scale=scale)
+    return outs[0], outs[1], ref
+
+
+# Few heads (2 B H below the CU count) with enough chunks: the state store runs
+# through the split forward and the state-gradient sweep in segments (segment
+# P-1 from dht beside the other segments' maps, the chain, then segments 0..P-2).
+@pytest.mark.parametrize("T,H", [(64 * 40 + 17, 2), (64 * 24, 3), (64 * 97, 1)])
+def test_bwd_few_heads_split(gdn, T, H):
+    say(f"case bwd few heads split T={T} H={H}")
+    x = inputs.generate(B=1, T=T, H=H, h0_std=0.05, dout=True, seed=400 + H)
+    dht = np.random.default_rng(401).standard_normal((1, H, 128, 128)).astype(np.float32) * 0.05
+    split, unsplit, ref = _bwd_both(gdn, x, dht=dht, scale=0.75)
+    _check(split, ref, f"split T={T} H={H}")
+    _check(unsplit, ref, f"unsplit T={T} H={H}")
+    d = max(rel_err(split[n], unsplit[n]) for n in NAMES)
+    say(f"  split vs unsplit: {d:.2e}")
+    assert d <= 1e-2, d
+
+
+def test_bwd_few_heads_split_correlated_keys(gdn):
+    """Split path with keys of cosine 0.9, beta up to 2, no h0, window and
+    exact heads mixed in the state store (one slowly decaying head)."""
+    say("case bwd few heads split, correlated keys, beta<=2")
+    x = inputs.generate(B=2, T=64 * 33 + 5, H=2, h0_std=None, dout=True, seed=410, key_corr=0.9, beta_max=2.0)
+    split, _, ref = _bwd_both(gdn, x)
+    _check(split, ref, "split rho=0.9 beta<=2")
+
+
 @pytest.mark.slow
 def test_bwd_train_workload_all_heads(gdn):
     """The training shape (B=4, T=8192, H=32, h0 given, dO ~ N(0,1)) at full size:
