@@ -153,6 +153,43 @@ __device__ __forceinline__ void dh_map_step(const Lane<T>& L, const T* kt, const
     kt_update<T>(L, kt, M, GC, bk);
 }
 
+// Chunk tile for loader wave lw (0, 1) of the sweep's segment maps, by buffer
+// loads into LDS with the lane offsets formed per call: no offset registers stay
+// live across the chunk loop, where the prep waves also hold their 32 columns of
+// M (the fetch-ahead loader's offsets were spilled there).  The same slots as
+// TileLoader<T, 2>; a short chunk goes through registers, zero past its end.
+template <typename T>
+__device__ __forceinline__ void dh_load_tile(T* tile, const T* chunk, int nv, int H, int lw) {
+    static_assert(sizeof(T) == 2, "bf16 tiles");
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));   // offsets per call, not hoisted out of the chunk loop
+    const int rb = H * kDk * (int)sizeof(T);   // bytes between rows
+    if (nv == kChunk) {
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(chunk), (short)0, kChunk * rb, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            // slots (2 i + lw) * 64 + lane: row 8 i + 4 lw + lane / 16, piece lane % 16
+            const int row = 8 * i + 4 * lw + (lane >> 4);
+            const int voff = (4 * lw + (lane >> 4)) * rb + (((lane & 15) ^ swz16(row)) << 4);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)(tile + (2 * i + lw) * 64 * 8), 16, voff, 8 * i * rb, 0,
+                kCpolStream);
+        }
+    } else {
+        typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int L = (2 * i + lw) * 64 + lane, row = L >> 4, slot = L & 15;
+            u4 v = {0u, 0u, 0u, 0u};
+            if (row < nv)
+                v = *(const __attribute__((address_space(1))) u4*)((const char*)chunk + (size_t)row * rb +
+                                                                    ((slot ^ swz16(row)) << 4));
+            *(u4*)(tile + L * 8) = v;
+        }
+    }
+}
+
 // Gradient waves: carry dH over chunks c1 - 1 down to c0 of head bh.  The start
 // is dht (in_slot < 0) or the b field of workspace slot in_slot; PASS1 starts
 // from zero and stores no per-chunk gradients (the segment's b).  At the end the
@@ -229,6 +266,7 @@ __device__ __noinline__ void dh_state_loop(const BwdParams& prm, Smem<T>& sm, in
 // field of slot out_slot.  Executes exactly the same barriers as dh_state_loop.
 template <typename T, bool PASS1 = false>
 __device__ __noinline__ void dh_prep_loop(const BwdParams& prm, Smem<T>& sm, int bh, int c0, int c1, int out_slot) {
+    static_assert(!PASS1 || kDhLoadAhead, "segment maps are built with the fetch-ahead sweep only");
     bh = uni(bh), c0 = uni(c0), c1 = uni(c1), out_slot = uni(out_slot);
     constexpr bool kPipe = kDhPipelined;
     const int pw = wave_id() - 4;
@@ -258,17 +296,25 @@ __device__ __noinline__ void dh_prep_loop(const BwdParams& prm, Smem<T>& sm, int
     constexpr int kLoaders = kDhLoadAhead ? 2 : 4;
     const bool loader = pw >= 4 - kLoaders;
     TileLoader<T, kLoaders> TL;
-    if (loader) TL.init(pw - (4 - kLoaders), L.lane, H);
+    if (!PASS1 && loader) TL.init(pw - (4 - kLoaders), L.lane, H);
     auto load_kq = [&](int c, int slot) {
         if (!loader) return;
         const size_t cb = chunk_base(b, h, Tn, H, c);
         const int nv = chunk_len(Tn, c);
-        TL.load(sm.kt[slot], k + cb, nv);
-        TL.load(sm.qt[slot], q + cb, nv);
+        if constexpr (PASS1) {
+            dh_load_tile<T>(sm.kt[slot], k + cb, nv, H, pw - 2);
+            dh_load_tile<T>(sm.qt[slot], q + cb, nv, H, pw - 2);
+        } else {
+            TL.load(sm.kt[slot], k + cb, nv);
+            TL.load(sm.qt[slot], q + cb, nv);
+        }
     };
     auto load_do = [&](int c, int slot) {
         if (!loader) return;
-        TL.load(sm.vt[slot], dout + chunk_base(b, h, Tn, H, c), chunk_len(Tn, c));
+        if constexpr (PASS1)
+            dh_load_tile<T>(sm.vt[slot], dout + chunk_base(b, h, Tn, H, c), chunk_len(Tn, c), H, pw - 2);
+        else
+            TL.load(sm.vt[slot], dout + chunk_base(b, h, Tn, H, c), chunk_len(Tn, c));
     };
     if constexpr (kPipe) {
         load_kq(cidx(0), 0);
