@@ -157,9 +157,16 @@ BWD_WORKLOAD = "bf16_b4_t8192_h32_train"
 BWD_BYTES_PER_TOKEN_HEAD = 4 * 256 + 8 + 3 * 256 + 8
 
 
-def bench_backward(torch, gdn, _lib, inputs, steps, warmup):
-    """Whole gdn_chunk_bwd calls on the training shape, with per-launch event times."""
-    x = inputs.workload(BWD_WORKLOAD)
+def bench_backward(torch, gdn, _lib, inputs, steps, warmup, few_heads=False):
+    """Whole gdn_chunk_bwd calls on the training shape, with per-launch event
+    times; few_heads: at B=1, T=32768, H=32 instead (the split backward: state
+    store through the split forward, state-gradient sweep in segments)."""
+    if few_heads:
+        x = inputs.generate(B=1, T=32768, H=32, h0_std=0.02, dout=True, seed=12)
+        name = "bf16_b1_t32768_h32_bwd"
+    else:
+        x = inputs.workload(BWD_WORKLOAD)
+        name = BWD_WORKLOAD
     B, T, H, dk, dv = x.shape
     dev = torch.device("cuda:0")
     bf = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)
@@ -194,7 +201,7 @@ def bench_backward(torch, gdn, _lib, inputs, steps, warmup):
     ev.close()
     ms = (t1 - t0) * 1e3 / steps
     nbytes = B * T * H * BWD_BYTES_PER_TOKEN_HEAD + B * H * STATE_BYTES * 2
-    res = {"workload": BWD_WORKLOAD, "B": B, "T": T, "H": H, "steps": steps, "warmup": warmup,
+    res = {"workload": name, "B": B, "T": T, "H": H, "steps": steps, "warmup": warmup,
            "ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3),
            "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
            "kernel_ms": {kd: round(float(np.mean(t)), 4) for kd, t in per_kind.items()}}
@@ -440,6 +447,9 @@ def main():
     extra = {}
     if args.bwd_steps > 0:
         extra["backward"] = bench_backward(torch, gdn, _lib, inputs, args.bwd_steps, 2)
+        torch.cuda.empty_cache()
+        extra["backward_few_heads"] = bench_backward(torch, gdn, _lib, inputs, args.bwd_steps, 2, few_heads=True)
+        torch.cuda.empty_cache()
     if args.varlen_steps > 0:
         extra["varlen"] = bench_varlen(torch, gdn, inputs, args.varlen_steps, 2)
     if args.kda_steps > 0:
