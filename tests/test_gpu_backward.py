@@ -145,14 +145,17 @@ def _bwd_both(gdn, x, dht=None, scale=1.0):
 # Few heads (2 B H below the CU count) with enough chunks: the state store runs
 # through the split forward and the state-gradient sweep in segments (segment
 # P-1 from dht beside the other segments' maps, the chain, then segments 0..P-2).
-@pytest.mark.parametrize("T,H", [(64 * 40 + 17, 2), (64 * 24, 3), (64 * 97, 1)])
-def test_bwd_few_heads_split(gdn, T, H):
-    say(f"case bwd few heads split T={T} H={H}")
-    x = inputs.generate(B=1, T=T, H=H, h0_std=0.05, dout=True, seed=400 + H)
-    dht = np.random.default_rng(401).standard_normal((1, H, 128, 128)).astype(np.float32) * 0.05
+@pytest.mark.parametrize("B,T,H", [(1, 64 * 40 + 17, 2), (1, 64 * 24, 3), (1, 64 * 97, 1),
+                                   (2, 64 * 30 + 5, 3), (3, 64 * 150 + 40, 1)])
+def test_bwd_few_heads_split(gdn, B, T, H):
+    # (2, 1925, 3): three segments per head over two batch entries; (3, 9640, 1):
+    # the largest segment count (17) with a ragged tail
+    say(f"case bwd few heads split B={B} T={T} H={H}")
+    x = inputs.generate(B=B, T=T, H=H, h0_std=0.05, dout=True, seed=400 + H + 10 * (B - 1))
+    dht = np.random.default_rng(401).standard_normal((B, H, 128, 128)).astype(np.float32) * 0.05
     split, unsplit, ref = _bwd_both(gdn, x, dht=dht, scale=0.75)
-    _check(split, ref, f"split T={T} H={H}")
-    _check(unsplit, ref, f"unsplit T={T} H={H}")
+    _check(split, ref, f"split B={B} T={T} H={H}")
+    _check(unsplit, ref, f"unsplit B={B} T={T} H={H}")
     d = max(rel_err(split[n], unsplit[n]) for n in NAMES)
     say(f"  split vs unsplit: {d:.2e}")
     assert d <= 1e-2, d
