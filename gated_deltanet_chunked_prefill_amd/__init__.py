@@ -26,7 +26,7 @@ from . import _lib
 DEFAULT_LOG_EPS = math.log(2.0 ** -24)
 
 __all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_kda_fwd",
-           "gdn_kda_plan_segments", "gdn_kda_fwd_workspace_size", "gdn_chunk_fwd_varlen", "gdn_chunk_bwd", "gdn_chunk_bwd_varlen", "gdn_gate_scan",
+           "gdn_kda_plan_segments", "gdn_kda_fwd_workspace_size", "gdn_chunk_bwd_plan_segments", "gdn_chunk_fwd_varlen", "gdn_chunk_bwd", "gdn_chunk_bwd_varlen", "gdn_gate_scan",
            "gdn_plan_segments",
            "gdn_chunk_fwd_plan_info", "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd_workspace_size",
            "gdn_chunk_bwd_varlen_workspace_size", "options"]
@@ -237,6 +237,12 @@ def gdn_chunk_fwd_noalloc(q, k, v, g, beta, h0=None, scale=1.0, *, out, out_ht=N
                                          _ptr(out), _ptr(out_ht), B, T, H, dk, dv, _dtype_code(q), float(scale),
                                          ctypes.byref(opt), _stream(dev)))
     return out, out_ht
+
+
+def gdn_chunk_bwd_plan_segments(B, T, H, num_cus) -> int:
+    """Segments per head of gdn_chunk_bwd's state-gradient sweep on a device with
+    num_cus compute units (1 = unsplit, 0 = invalid arguments)."""
+    return _lib.load().gdn_chunk_bwd_plan_segments(int(B), int(T), int(H), int(num_cus))
 
 
 def gdn_kda_plan_segments(B, T, H, num_cus, n_segments=0) -> int:

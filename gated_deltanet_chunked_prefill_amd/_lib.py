@@ -25,7 +25,7 @@ EXPORTS = ("gdn_default_options", "gdn_plan_segments", "gdn_chunk_fwd_workspace_
            "gdn_gate_scan_workspace_size", "gdn_gate_scan", "gdn_profile_events",
            "gdn_last_error", "gdn_chunk_fwd_plan_info", "gdn_chunk_fwd_varlen",
            "gdn_chunk_bwd_varlen_workspace_size", "gdn_chunk_bwd_varlen", "gdn_chunk_fwd_noalloc", "gdn_kda_fwd",
-           "gdn_kda_plan_segments", "gdn_kda_fwd_workspace_size", "gdn_stream_probe", "gdn_profile_kinds")
+           "gdn_kda_plan_segments", "gdn_kda_fwd_workspace_size", "gdn_chunk_bwd_plan_segments", "gdn_stream_probe", "gdn_profile_kinds")
 #: bytes of the fixed scratch array of gdn_chunk_fwd_noalloc (GDN_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -73,6 +73,8 @@ def load():
     lib.gdn_profile_kinds.restype = ctypes.c_uint32
     lib.gdn_kda_plan_segments.argtypes = [_i] * 5
     lib.gdn_kda_plan_segments.restype = _i
+    lib.gdn_chunk_bwd_plan_segments.argtypes = [_i] * 4
+    lib.gdn_chunk_bwd_plan_segments.restype = _i
     lib.gdn_kda_fwd_workspace_size.argtypes = [_i] * 6
     lib.gdn_kda_fwd_workspace_size.restype = _sz
     lib.gdn_stream_probe.argtypes = [_vp] * 4 + [_i] * 3 + [_vp]

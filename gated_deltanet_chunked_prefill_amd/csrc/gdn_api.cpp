@@ -798,6 +798,11 @@ gdn_status gdn_gate_scan(const float* g, int B, int T, int H, int window_chunks,
     return GDN_OK;
 }
 
+int gdn_chunk_bwd_plan_segments(int B, int T, int H, int num_cus) {
+    if (B <= 0 || T <= 0 || H <= 0 || (long long)B * H > (1LL << 30)) return 0;
+    return bwd_split(B, T, H, num_cus).ps;
+}
+
 size_t gdn_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, gdn_dtype dtype) {
     if (check_shapes(B, T, H, dk, dv, dtype) != GDN_OK) return (size_t)-1;
     int cus = 0;

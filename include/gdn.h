@@ -279,11 +279,24 @@ gdn_status gdn_chunk_bwd_varlen(const void* q, const void* k, const void* v, con
                                 int T, int H, int dk, int dv, gdn_dtype dtype, float scale,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes for gdn_chunk_bwd ((size_t)-1 for invalid arguments):
- * B*H*(2N+1) bfloat16 128 x 128 matrices (N = number of 64-token chunks), the
- * state entering every chunk plus the final state, and the state gradient
- * reaching the end of every chunk. */
+/* Workspace bytes for gdn_chunk_bwd on the current device ((size_t)-1 for
+ * invalid arguments): B*H*(2N+1) bfloat16 128 x 128 matrices (N = number of
+ * 64-token chunks), the state entering every chunk plus the final state, and the
+ * state gradient reaching the end of every chunk; when the sweep is split
+ * (gdn_chunk_bwd_plan_segments > 1) also the split forward's workspace and
+ * B*H*P slots of 2 x 128 x 128 float32 values.  Without a device: the unsplit
+ * size. */
 size_t gdn_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, gdn_dtype dtype);
+
+/* Segments per head of gdn_chunk_bwd's state-gradient sweep on a device with
+ * num_cus compute units (the same rule as the forward's sequence split, talk
+ * summary paragraph 4, applied to the reverse recurrence, whose chunk map is the
+ * transposed forward map): with few heads, 2 B H < num_cus, the sweep is cut
+ * into P = a + 1 segments, a = min(16, floor(num_cus / (B H)), floor(N / 8) - 1),
+ * when a >= 2 (then S = ceil(N / P) chunks each and P = ceil(N / S)); else 1
+ * (unsplit).  A split sweep also stores the states through the split forward.
+ * Returns 0 for invalid arguments, 1 when num_cus <= 0. */
+int gdn_chunk_bwd_plan_segments(int B, int T, int H, int num_cus);
 
 /* Fused chunked backward (page 1 lede and talk summary paragraph 6: the
  * backward of GDN chunked prefill; the gradient of the K K^T term is formed as
@@ -300,6 +313,12 @@ size_t gdn_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, gdn_dty
  * last chunk to the first (on a library-owned side stream of the current
  * device, created on first use with default priority, joined back through an
  * event); then the local gradients of all chunks in parallel on `stream`.
+ * With few heads (gdn_chunk_bwd_plan_segments > 1) and a workspace of the
+ * size gdn_chunk_bwd_workspace_size reports, everything runs on `stream`: the
+ * states through the split forward, then the sweep's last segment from dht
+ * beside the other segments' maps (dH_in = M dH_out + b), a chain composing
+ * the gradients entering the segments, the other segments from those, and the
+ * local gradients; with the unsplit size the call runs unsplit.
  * The call is ordered after earlier work on `stream` and later work on
  * `stream` is ordered after it, as with a single stream. */
 gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g,

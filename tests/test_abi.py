@@ -322,6 +322,38 @@ def test_kda_plan_and_workspace():
     assert wsz(2, 64 * 10, 3, 64, 128, 2) == ctypes.c_size_t(-1).value
 
 
+def test_bwd_plan_segments():
+    """The backward's host rule for splitting the state-gradient sweep (few heads:
+    2 B H below the CU count), written out here from its documented form."""
+    lib = _lib.load()
+    plan = lib.gdn_chunk_bwd_plan_segments
+    assert plan(1, 32768, 32, 256) == 9             # 8 workgroups per head, one segment more
+    assert plan(4, 8192, 32, 256) == 1              # 2 B H = 256 CUs: unsplit
+    assert plan(1, 32768, 127, 256) == 3            # 2 B H = 254: a = 2
+    assert plan(1, 32768, 128, 256) == 1            # 2 B H = 256: unsplit
+    assert plan(1, 64 * 97, 1, 256) == 11           # a = 97 // 8 - 1 = 11: 12 -> S = 9, P = 11
+    assert plan(3, 64 * 150 + 40, 1, 256) == 17     # a capped at 16
+    assert plan(2, 64 * 30 + 5, 3, 256) == 3        # 31 chunks: a = 2, S = 11
+    assert plan(1, 64 * 23, 2, 256) == 1            # 23 chunks: a = 1
+    assert plan(1, 64 * 24, 2, 256) == 3            # 24 chunks: a = 2
+    assert plan(1, 32768, 32, 0) == 1               # no CU count: unsplit
+    assert plan(0, 128, 1, 256) == 0
+    assert plan(1, 0, 1, 256) == 0
+
+    def rule(B, T, H, cus):
+        N = -(-T // 64)
+        if cus <= 0 or 2 * B * H >= cus:
+            return 1
+        a = min(16, cus // (B * H), N // 8 - 1)
+        if a < 2:
+            return 1
+        S = -(-N // (a + 1))
+        return -(-N // S)
+    for B, T, H, cus in [(1, 4096, 1, 304), (2, 100000, 5, 256), (1, 640, 1, 80), (7, 65536, 3, 256),
+                         (1, 262144, 16, 256), (1, 513, 1, 256)]:
+        assert plan(B, T, H, cus) == rule(B, T, H, cus), (B, T, H, cus)
+
+
 def test_profile_kinds_mask_is_thread_local_bookkeeping():
     """gdn_profile_kinds sets the launch kinds the profiling hook brackets and
     returns the previous mask (all kinds by default); host-only."""
